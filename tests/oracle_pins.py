@@ -1,0 +1,433 @@
+"""Pins for the fp64 oracle: each check compares the oracle with something
+other than itself — a library routine, a closed form, an invariant of the
+definition, or brute force on inputs whose dot products are exact.
+
+Each ``check_*`` raises AssertionError on failure.  They are collected as
+tests by ``test_oracle_pins.py`` and re-run against deliberately broken
+builds of the oracle by ``test_oracle_mutants.py`` (which asserts that every
+planted mistake trips at least one of them).
+
+Where a pin follows a statement of the pages it names the page and section:
+  [P1] "NeurIPS'26：注意力也是FFN？…", section "用少量地标查询，同时构造全局概括与细节专家"
+  [P2] "NeurIPS 2026 | Mixture-of-Top-k 注意力…", section "MiTA：用少量地标查询，同时完成压缩与专家构造"
+  [P3] "And attention is also FFN? …", Figure 3 and Algorithm 1
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+import oracle as O
+
+# ---------------------------------------------------------------------------
+# helpers (no MiTA arithmetic: only data construction)
+# ---------------------------------------------------------------------------
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _int_data(rng, shape, lo=-3, hi=3):
+    """Small integers: every dot product of such vectors is exact in fp64 in
+    any summation order, so equal scores are real ties."""
+    return rng.integers(lo, hi + 1, size=shape).astype(np.float64)
+
+
+def _bf16_bits(x: float) -> int:
+    f = np.array([x], dtype=np.float32)
+    u = int(f.view(np.uint32)[0])
+    assert float(f[0]) == x, "result is not an fp32 value"
+    assert u & 0xFFFF == 0, "result has more than 8 significant bits"
+    return u >> 16
+
+
+def _bf16_value(bits: int) -> float:
+    return float(np.array([bits << 16], dtype=np.uint32).view(np.float32)[0])
+
+
+# ---------------------------------------------------------------------------
+# rounding into bfloat16 (the landmark queries are stored in the input type)
+# ---------------------------------------------------------------------------
+
+
+def check_round_bf16_definition():
+    """Round-to-nearest, ties-to-even into bf16, checked against the IEEE
+    definition with exact rational arithmetic: the result is a bf16 value and
+    no neighbouring bf16 value is closer (on a tie the result is even)."""
+    rng = _rng(11)
+    xs = list(rng.standard_normal(3000) * np.exp2(rng.integers(-20, 20, 3000)))
+    # exact midpoints between neighbouring bf16 values, and points just off them
+    for b in rng.integers(0x3C00, 0x4400, 300):
+        lo, hi = _bf16_value(int(b)), _bf16_value(int(b) + 1)
+        mid = (lo + hi) / 2
+        xs += [mid, np.nextafter(mid, np.inf), np.nextafter(mid, -np.inf), -mid]
+    for x in xs:
+        r = O.round_bf16(float(x))
+        bits = _bf16_bits(r)
+        dist = abs(Fraction(x) - Fraction(r))
+        for nb in (bits - 1, bits + 1):
+            if (nb & 0x7F80) == 0x7F80:  # infinities / NaN are not neighbours
+                continue
+            dn = abs(Fraction(x) - Fraction(_bf16_value(nb)))
+            assert dist <= dn, (x, r)
+            if dist == dn:
+                assert bits % 2 == 0, ("tie not to even", x, r)
+
+
+def check_round_bf16_cases():
+    """Hand-derived cases.  1 + 2^-8 lies halfway between the bf16 values 1
+    and 1 + 2^-7, so ties-to-even gives 1; 1 + 3*2^-8 lies halfway between
+    1 + 2^-7 and 1 + 2^-6 and goes to the even 1 + 2^-6.  1 + 2^-8 + 2^-40
+    is above the midpoint and must round up to 1 + 2^-7 — rounding first to
+    fp32 would drop the 2^-40 and then tie down to 1 (double rounding)."""
+    assert O.round_bf16(1 + 2.0**-8) == 1.0
+    assert O.round_bf16(1 + 3 * 2.0**-8) == 1 + 2.0**-6
+    assert O.round_bf16(1 + 2.0**-8 + 2.0**-40) == 1 + 2.0**-7
+    assert O.round_bf16(-(1 + 2.0**-8 + 2.0**-40)) == -(1 + 2.0**-7)
+    assert O.round_bf16(2.0**-133) == 2.0**-133  # smallest subnormal
+    assert O.round_bf16(2.0**-135) == 0.0  # below half of it
+    assert O.round_bf16(3 * 2.0**-135) == 2.0**-133  # above half of it
+    assert O.round_bf16(2.0**128) == float("inf")
+
+
+# ---------------------------------------------------------------------------
+# step 1: landmark queries by local average pooling [P1][P2]
+# ---------------------------------------------------------------------------
+
+
+def check_pool_bins_14_to_5():
+    """Adaptive bins of a 14-token side into 5: start = floor(i*14/5),
+    end = ceil((i+1)*14/5): 0..3, 2..6, 5..9, 8..12, 11..14 (they overlap)."""
+    want = [(0, 3), (2, 6), (5, 9), (8, 12), (11, 14)]
+    for a in range(5):
+        for c in range(5):
+            r0, r1, c0, c1 = O.window(14, 14, 5, 5, a * 5 + c)
+            assert (r0, r1) == want[a] and (c0, c1) == want[c]
+    # 1D: gh = mh = 1; windows of N/m tokens when m divides N
+    for i in range(64):
+        assert O.window(1, 4096, 1, 64, i) == (0, 1, 64 * i, 64 * (i + 1))
+
+
+def check_pool_vs_adaptive_avg_pool():
+    """Before rounding, the pooled landmarks equal torch's adaptive average
+    pooling in fp64 (a library routine with the same bin rule)."""
+    rng = _rng(12)
+    for gh, gw, mh, mw in [(14, 14, 5, 5), (40, 40, 7, 7), (32, 32, 7, 7), (9, 13, 4, 3),
+                           (1, 100, 1, 7), (1, 4096, 1, 64)]:
+        N, d = gh * gw, 8
+        Q = rng.standard_normal((N, d))
+        got = O.pool(Q, gh, gw, mh, mw, O.ROUND_NONE)
+        img = torch.from_numpy(Q.T.reshape(d, gh, gw).copy())
+        ref = F.adaptive_avg_pool2d(img, (mh, mw)).reshape(d, mh * mw).T.numpy()
+        np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-14)
+
+
+def check_pool_special_cases():
+    rng = _rng(13)
+    # constant tokens give constant landmarks
+    Q = np.full((196, 4), 0.75)
+    assert np.all(O.pool(Q, 14, 14, 5, 5) == 0.75)
+    # one landmark per token: identity
+    Q = rng.standard_normal((12, 5))
+    assert np.array_equal(O.pool(Q, 3, 4, 3, 4), Q)
+    # a single landmark: the global mean
+    Q = rng.standard_normal((60, 6))
+    np.testing.assert_allclose(O.pool(Q, 6, 10, 1, 1)[0], Q.mean(0), rtol=1e-13, atol=1e-15)
+    # 1D windows of N/m contiguous tokens
+    Q = rng.standard_normal((512, 3))
+    np.testing.assert_allclose(O.pool(Q, 1, 512, 1, 16), Q.reshape(16, 32, 3).mean(1),
+                               rtol=1e-13, atol=1e-15)
+
+
+def check_pool_rounding_modes():
+    """Rounded landmarks are exactly representable in the target type and are
+    the nearest such value to the fp64 mean."""
+    rng = _rng(14)
+    Qf = torch.randn(196, 16, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    Q = Qf.to(torch.float64).numpy()
+    exact = O.pool(Q, 14, 14, 5, 5, O.ROUND_NONE)
+    rb = O.pool(Q, 14, 14, 5, 5, O.ROUND_BF16)
+    assert np.array_equal(torch.from_numpy(rb).to(torch.bfloat16).to(torch.float64).numpy(), rb)
+    for x, r in zip(exact.ravel()[:200], rb.ravel()[:200]):
+        bits = _bf16_bits(float(r))
+        for nb in (bits - 1, bits + 1):
+            assert abs(Fraction(float(x)) - Fraction(float(r))) <= abs(
+                Fraction(float(x)) - Fraction(_bf16_value(nb)))
+    Q = rng.standard_normal((196, 16)).astype(np.float32).astype(np.float64)
+    r32 = O.pool(Q, 14, 14, 5, 5, O.ROUND_F32)
+    e64 = O.pool(Q, 14, 14, 5, 5, O.ROUND_NONE)
+    assert np.array_equal(r32, e64.astype(np.float32).astype(np.float64))
+
+
+# ---------------------------------------------------------------------------
+# step 2a: routed experts = per-landmark top-k keys [P1][P2]
+# ---------------------------------------------------------------------------
+
+
+def _bruteforce_topk(S, k):
+    """Full sort of every row by (larger score, then lower index)."""
+    m, N = S.shape
+    out = np.empty((m, k), np.int64)
+    for i in range(m):
+        order = np.lexsort((np.arange(N), -S[i]))  # last key is primary
+        out[i] = np.sort(order[:k])
+    return out
+
+
+def check_topk_bruteforce_with_ties():
+    rng = _rng(21)
+    for N, d, m, k in [(37, 4, 5, 6), (64, 8, 3, 64), (100, 3, 7, 1), (23, 2, 4, 11)]:
+        Ql = _int_data(rng, (m, d))
+        K = _int_data(rng, (N, d))
+        got = O.topk(Ql, K, k)
+        S = Ql @ K.T  # exact: small integers
+        assert np.array_equal(got, _bruteforce_topk(S, k)), (N, d, m, k)
+        assert np.all(np.diff(got, axis=1) > 0)  # ascending, distinct
+
+
+def check_topk_gaussian_vs_torch():
+    rng = _rng(22)
+    Ql = rng.standard_normal((9, 16))
+    K = rng.standard_normal((300, 16))
+    got = O.topk(Ql, K, 17)
+    ref = torch.topk(torch.from_numpy(Ql @ K.T), 17, dim=1).indices.numpy()
+    for i in range(9):
+        assert set(got[i].tolist()) == set(ref[i].tolist())
+
+
+def check_topk_k_equals_n_and_duplicates():
+    rng = _rng(23)
+    Ql = rng.standard_normal((4, 8))
+    K = rng.standard_normal((50, 8))
+    assert np.array_equal(O.topk(Ql, K, 50), np.tile(np.arange(50), (4, 1)))
+    # two identical key rows that beat every other key: with k = 1 the lower
+    # index wins
+    K[17] = K[31] = 10.0 * Ql[0]
+    got = O.topk(Ql[:1], K, 1)
+    assert got[0, 0] == 17
+    got = O.topk(Ql[:1], K, 2)
+    assert got[0].tolist() == [17, 31]
+
+
+def check_topk_permutation_equivariance():
+    rng = _rng(24)
+    Ql = rng.standard_normal((6, 8))
+    K = rng.standard_normal((120, 8))
+    p = rng.permutation(120)
+    a = O.topk(Ql, K, 13)
+    b = O.topk(Ql, K[p], 13)
+    for i in range(6):
+        assert set(p[b[i]].tolist()) == set(a[i].tolist())
+
+
+def check_topk_gap_report():
+    rng = _rng(25)
+    Ql = rng.standard_normal((5, 8))
+    K = rng.standard_normal((90, 8))
+    _, gap = O.topk(Ql, K, 10, with_gap=True)
+    S = Ql @ K.T
+    srt = -np.sort(-S, axis=1)
+    np.testing.assert_allclose(gap[:, 0], srt[:, 9], rtol=1e-12)
+    np.testing.assert_allclose(gap[:, 1], srt[:, 10], rtol=1e-12)
+    assert np.all(gap[:, 2] >= np.abs(gap[:, 0]) - 1e-12)
+
+
+# ---------------------------------------------------------------------------
+# step 2b: landmark values = cross-attention of landmarks over all keys [P1][P2]
+# ---------------------------------------------------------------------------
+
+
+def check_landmark_values_vs_torch_softmax():
+    rng = _rng(31)
+    for N, d, m, scale in [(196, 16, 25, 0.25), (1000, 8, 3, 1.0), (7, 4, 2, 0.125)]:
+        Ql = rng.standard_normal((m, d))
+        K = rng.standard_normal((N, d))
+        V = rng.standard_normal((N, d))
+        got = O.landmark_values(Ql, K, V, scale)
+        A = torch.softmax(torch.from_numpy(scale * (Ql @ K.T)), dim=-1)
+        ref = (A @ torch.from_numpy(V)).numpy()
+        np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-13)
+
+
+def check_landmark_values_invariants():
+    rng = _rng(32)
+    N, d, m = 150, 8, 6
+    Ql = rng.standard_normal((m, d))
+    K = rng.standard_normal((N, d))
+    V = rng.standard_normal((N, d))
+    Vl = O.landmark_values(Ql, K, V, 0.3)
+    # convex combination of value rows
+    assert np.all(Vl <= V.max(0) + 1e-12) and np.all(Vl >= V.min(0) - 1e-12)
+    # equal keys: uniform weights, the mean value
+    Ke = np.tile(K[:1], (N, 1))
+    np.testing.assert_allclose(O.landmark_values(Ql, Ke, V, 0.3), np.tile(V.mean(0), (m, 1)),
+                               rtol=1e-12, atol=1e-13)
+    # weights sum to one: affine maps of V carry through
+    c = rng.standard_normal(d)
+    np.testing.assert_allclose(O.landmark_values(Ql, K, 2.5 * V + c, 0.3), 2.5 * Vl + c,
+                               rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# step 3: routing to the best-matching landmark [P1][P2]
+# ---------------------------------------------------------------------------
+
+
+def check_route_vs_argmax_with_ties():
+    rng = _rng(41)
+    Q = _int_data(rng, (400, 4), -2, 2)
+    Ql = _int_data(rng, (9, 4), -1, 1)
+    got = O.route(Q, Ql)
+    ref = np.argmax(Q @ Ql.T, axis=1)  # first occurrence of the maximum
+    assert np.array_equal(got, ref)
+    # a single landmark takes every query
+    assert np.all(O.route(Q, Ql[:1]) == 0)
+    # routing a subset gives the same answers
+    sel = rng.choice(400, 37, replace=False)
+    assert np.array_equal(O.route(Q, Ql, qsel=sel), ref[sel])
+
+
+def check_route_top2_report():
+    rng = _rng(42)
+    Q = rng.standard_normal((50, 8))
+    Ql = rng.standard_normal((6, 8))
+    r, top2 = O.route(Q, Ql, with_top2=True)
+    R = Q @ Ql.T
+    srt = -np.sort(-R, axis=1)
+    np.testing.assert_allclose(top2[:, 0], srt[:, 0], rtol=1e-12)
+    np.testing.assert_allclose(top2[:, 1], srt[:, 1], rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# step 4: grouping queries by expert [P1][P2]
+# ---------------------------------------------------------------------------
+
+
+def check_bucket_vs_stable_argsort():
+    rng = _rng(51)
+    for N, m in [(1000, 7), (5, 9), (64, 1)]:
+        r = rng.integers(0, m, N).astype(np.int32)
+        off, perm = O.bucket(r, m)
+        assert np.array_equal(perm, np.argsort(r, kind="stable"))
+        assert np.array_equal(off, np.concatenate([[0], np.cumsum(np.bincount(r, minlength=m))]))
+
+
+# ---------------------------------------------------------------------------
+# step 5: one softmax over m compressed + k raw pairs [P1][P2][P3]
+# ---------------------------------------------------------------------------
+
+
+def check_output_k_equals_n_is_dense_attention():
+    """With k = N every expert holds all keys, so each query attends densely
+    over the m compressed pairs plus all N raw pairs: fp64 scaled dot-product
+    attention over the concatenated keys [Ql; K] and values [Vl; V]."""
+    rng = _rng(61)
+    for N, d, m, scale in [(60, 8, 5, 0.35), (196, 16, 25, 0.25)]:
+        Q = rng.standard_normal((N, d))
+        K = rng.standard_normal((N, d))
+        V = rng.standard_normal((N, d))
+        Ql = rng.standard_normal((m, d))
+        Vl = rng.standard_normal((m, d))
+        idx = np.tile(np.arange(N, dtype=np.int32), (m, 1))
+        r = rng.integers(0, m, N).astype(np.int32)
+        got = O.output(Q, K, V, Ql, Vl, idx, r, scale)
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a))[None, None]
+        ref = F.scaled_dot_product_attention(t(Q), t(np.vstack([Ql, K])), t(np.vstack([Vl, V])),
+                                             scale=scale)[0, 0].numpy()
+        np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-13)
+
+
+def check_output_pair_count_closed_form():
+    """With all logits equal, every one of the m + k pairs gets weight
+    1/(m+k): 25 + 25 = 50 pairs at m = k = 25 (the pages' ImageNet count),
+    none merged or dropped, even when the expert's keys repeat."""
+    rng = _rng(62)
+    N, d, m, k = 196, 8, 25, 25
+    Q = np.zeros((N, d))
+    K = rng.standard_normal((N, d))
+    V = rng.standard_normal((N, d))
+    Ql = rng.standard_normal((m, d))
+    Vl = rng.standard_normal((m, d))
+    idx = np.tile(np.arange(k, dtype=np.int32), (m, 1))
+    r = rng.integers(0, m, N).astype(np.int32)
+    got = O.output(Q, K, V, Ql, Vl, idx, r, 0.125)
+    want = (Vl.sum(0) + V[:k].sum(0)) / (m + k)
+    np.testing.assert_allclose(got, np.tile(want, (N, 1)), rtol=1e-12, atol=1e-14)
+
+
+def check_output_uses_routed_expert():
+    """Each query reads exactly the expert it is routed to: compare against
+    dense attention over [Ql; K[idx[route[q]]]] computed per query with
+    torch."""
+    rng = _rng(63)
+    N, d, m, k, scale = 80, 8, 4, 9, 0.4
+    Q, K, V = (rng.standard_normal((N, d)) for _ in range(3))
+    Ql, Vl = rng.standard_normal((m, d)), rng.standard_normal((m, d))
+    idx = np.sort(np.stack([rng.choice(N, k, replace=False) for _ in range(m)]), 1).astype(
+        np.int32)
+    r = rng.integers(0, m, N).astype(np.int32)
+    got = O.output(Q, K, V, Ql, Vl, idx, r, scale)
+    for q in range(N):
+        kk = torch.from_numpy(np.vstack([Ql, K[idx[r[q]]]]))
+        vv = torch.from_numpy(np.vstack([Vl, V[idx[r[q]]]]))
+        w = torch.softmax(scale * (kk @ torch.from_numpy(Q[q])), 0)
+        np.testing.assert_allclose(got[q], (w @ vv).numpy(), rtol=1e-11, atol=1e-13)
+    # a query subset gives the same rows
+    sel = np.array([3, 77, 0, 41])
+    np.testing.assert_array_equal(O.output(Q, K, V, Ql, Vl, idx, r, scale, qsel=sel), got[sel])
+
+
+def check_output_invariants():
+    rng = _rng(64)
+    N, d, m, k = 100, 8, 5, 12
+    Q, K, V = (rng.standard_normal((N, d)) for _ in range(3))
+    Ql, Vl = rng.standard_normal((m, d)), rng.standard_normal((m, d))
+    idx = np.sort(np.stack([rng.choice(N, k, replace=False) for _ in range(m)]), 1).astype(
+        np.int32)
+    r = rng.integers(0, m, N).astype(np.int32)
+    out = O.output(Q, K, V, Ql, Vl, idx, r, 0.3)
+    for q in range(N):
+        pool_v = np.vstack([Vl, V[idx[r[q]]]])
+        assert np.all(out[q] <= pool_v.max(0) + 1e-12)
+        assert np.all(out[q] >= pool_v.min(0) - 1e-12)
+    # relabelling the keys (K, V rows and the expert indices) changes nothing
+    p = rng.permutation(N)
+    inv = np.argsort(p)
+    idx2 = np.sort(inv[idx], 1).astype(np.int32)
+    out2 = O.output(Q, K[p], V[p], Ql, Vl, idx2, r, 0.3)
+    np.testing.assert_allclose(out2, out, rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# whole pipeline
+# ---------------------------------------------------------------------------
+
+
+def check_forward_composes_steps():
+    rng = _rng(71)
+    B, H, N, d, grid, k = 2, 2, 196, 16, (14, 14, 5, 5), 25
+    Q, K, V = (torch.from_numpy(rng.standard_normal((B, H, N, d)).astype(np.float32))
+               .to(torch.bfloat16).to(torch.float64).numpy() for _ in range(3))
+    res = O.forward(Q, K, V, grid, k, 0.125, O.ROUND_BF16)
+    for b in range(B):
+        for h in range(H):
+            ql = O.pool(Q[b, h], *grid, O.ROUND_BF16)
+            assert np.array_equal(res["ql"][b, h], ql)
+            idx = O.topk(ql, K[b, h], k)
+            assert np.array_equal(res["idx"][b, h], idx)
+            vl = O.landmark_values(ql, K[b, h], V[b, h], 0.125)
+            np.testing.assert_array_equal(res["vl"][b, h], vl)
+            r = O.route(Q[b, h], ql)
+            assert np.array_equal(res["route"][b, h], r)
+            off, perm = O.bucket(r, 25)
+            assert np.array_equal(res["offsets"][b, h], off)
+            assert np.array_equal(res["perm"][b, h], perm)
+            out = O.output(Q[b, h], K[b, h], V[b, h], ql, vl, idx, r, 0.125)
+            np.testing.assert_array_equal(res["out"][b, h], out)
+
+
+ALL_CHECKS = [v for k_, v in sorted(globals().items()) if k_.startswith("check_")]

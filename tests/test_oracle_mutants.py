@@ -1,0 +1,66 @@
+"""Planted mistakes: each mutant is a copy of the oracle source with one
+plausible error (a dropped term, a wrong tie rule, a swapped operand, ...),
+built on the CPU.  Every mutant must fail at least one pin; a mutant that
+passes all of them would mean the pins cannot see that class of mistake.
+The real oracle is never modified."""
+import os
+import subprocess
+
+import pytest
+
+import oracle as O
+import oracle_pins as P
+
+SRC = os.path.join(os.path.dirname(O.oracle.__file__), "mita_oracle.c")
+
+MUTANTS = {
+    "pool_bin_end_floor": ("*r1 = ceil_div((a + 1) * gh, mh);", "*r1 = floor_div((a + 1) * gh, mh);"),
+    "pool_count_off_by_one": ("(double)((r1 - r0) * (c1 - c0));",
+                              "(double)((r1 - r0) * (c1 - c0) + 1);"),
+    "bf16_double_rounding": ("ldexp(nearbyint(ldexp(x, -q)), q);",
+                             "ldexp(nearbyint(ldexp((double)(float)x, -q)), q);"),
+    "bf16_ties_away": ("ldexp(nearbyint(ldexp(x, -q)), q);", "ldexp(round(ldexp(x, -q)), q);"),
+    "bf16_seven_bits": ("int q = e - 8;", "int q = e - 7;"),
+    "topk_ties_to_high_index": ("return (a->t < b->t) ? -1 : (a->t > b->t);",
+                                "return (a->t > b->t) ? -1 : (a->t < b->t);"),
+    "topk_smallest_scores": ("if (a->s > b->s) return -1;\n  if (a->s < b->s) return 1;",
+                             "if (a->s < b->s) return -1;\n  if (a->s > b->s) return 1;"),
+    "topk_skips_best": ("dst[j] = (int32_t)row[j].t;", "dst[j] = (int32_t)row[(j + 1) % N].t;"),
+    "landmark_values_unscaled": ("logit[t] = scale * dot(Ql + i * d, K + t * d, d);",
+                                 "logit[t] = dot(Ql + i * d, K + t * d, d);"),
+    "landmark_values_unnormalised": ("Vl[i * d + j] = acc / z;", "Vl[i * d + j] = acc;"),
+    "route_ties_to_last": ("if (v > best_v) { /* strict", "if (v >= best_v) { /* strict"),
+    "route_argmin": ("if (v > best_v) { /* strict", "if (v < best_v) { /* strict"),
+    "bucket_unstable": ("for (int64_t q = 0; q < N; ++q) perm[fill[route[q]]++] = (int32_t)q;",
+                        "for (int64_t q = N - 1; q >= 0; --q) perm[fill[route[q]]++] = (int32_t)q;"),
+    "output_drops_compressed_values": ("for (int64_t i = 0; i < m; ++i) acc += w[i] * Vl[i * d + c];",
+                                       "for (int64_t i = 0; i < m; ++i) acc += 0.0 * Vl[i * d + c];"),
+    "output_raw_logits_unscaled": ("w[m + j] = scale * dot(", "w[m + j] = dot("),
+    "output_wrong_expert": ("const int32_t* ex = idx + (int64_t)route[q] * k;",
+                            "const int32_t* ex = idx + (int64_t)((route[q] + 1) % m) * k;"),
+    "output_keys_as_values": ("acc += w[m + j] * V[(int64_t)ex[j] * d + c];",
+                              "acc += w[m + j] * K[(int64_t)ex[j] * d + c];"),
+    "output_compressed_keys_from_k": ("w[i] = scale * dot(Q + q * d, Ql + i * d, d);",
+                                      "w[i] = scale * dot(Q + q * d, K + i * d, d);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, name):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mut = tmp_path / "mutant.c"
+    mut.write_text(src.replace(old, new))
+    (tmp_path / "mita_oracle.h").write_text(open(SRC[:-1] + "h").read())
+    so = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-std=c11", "-O1", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+                    "-w", "-o", str(so), str(mut), "-lm"], check=True)
+    caught = []
+    with O.use_library(str(so)):
+        for check in P.ALL_CHECKS:
+            try:
+                check()
+            except Exception:  # any failure of a pin counts as detection
+                caught.append(check.__name__)
+    assert caught, f"no pin detects mutant {name}"

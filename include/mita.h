@@ -1,0 +1,157 @@
+/*
+ * mita.h — C ABI of libmita.so: the Mixture-of-Top-k Attention (MiTA)
+ * forward pass on one AMD Instinct MI355X (gfx950) GPU.
+ *
+ * What is computed (per batch b and head h; Q, K, V are [N][d]):
+ *   1. m landmark queries Ql by local average pooling of Q, stored in the
+ *      input type (fp64 sum and division, one round-to-nearest-even into the
+ *      input type).
+ *      [P1 "NeurIPS'26：注意力也是FFN？从快权重出发，重新理解高效注意力",
+ *       section "用少量地标查询，同时构造全局概括与细节专家";
+ *       P2 "NeurIPS 2026 | Mixture-of-Top-k 注意力：从快权重统一高效注意力，
+ *       让 Top-k 专家灵活又可复用", section "MiTA：用少量地标查询，同时完成
+ *       压缩与专家构造"]
+ *   2. One pass over the keys scores S = Ql K^T and feeds two results:
+ *      (a) expert i = the k keys with the largest S[i][t] (ties: lower key
+ *          index), returned ascending in idx_out — the routed experts;
+ *      (b) Vl = softmax(scale * S) V — the landmark values; (Ql, Vl) are the
+ *          m compressed key/value pairs of the shared expert.  [P1, P2, same
+ *          sections]
+ *   3. Query q goes to expert argmax_i q . Ql[i] (ties: lower landmark
+ *      index); these dot products are also the compressed-branch logits.
+ *      [P1, P2, same sections]
+ *   4. Queries are grouped by expert, stably (ascending query index within
+ *      each group).  [P1 same section; P2 same section, implementation note]
+ *   5. out[q] = softmax over the m + k logits scale*[q.Ql[0..m), q.K[t] for
+ *      t in expert(q)] applied to the values [Vl[0..m), V[t] ...]; exactly
+ *      m + k pairs, none merged or masked.  [P1, P2 same sections; P3 "And
+ *      attention is also FFN? Starting with fast weighting, re-understanding
+ *      efficient attention", Figure 3 and Algorithm 1]
+ *
+ * Memory: every tensor argument is a DEVICE pointer owned by the caller.
+ * The library never frees them and keeps none after the call returns,
+ * except inside the work it enqueued on `stream` (ordinary stream
+ * semantics: keep buffers alive until the stream has passed the call).
+ * Inputs are read-only; outputs are fully overwritten; inputs and outputs
+ * must not overlap.  Layouts are dense, row-major, [B][H][...] with the
+ * innermost dimension contiguous; every pointer must be 16-byte aligned.
+ *
+ * Work space: allocated stream-ordered on `stream` (hipMallocAsync /
+ * hipFreeAsync) for the duration of the call.  There is no host
+ * synchronisation and no global state besides the per-device attribute
+ * cache and the optional stage profiler, so calls on different streams may
+ * run concurrently.
+ *
+ * Errors: every function returns a status.  Arguments are validated on the
+ * host before any HIP call; nothing is enqueued when validation fails.  A
+ * failed launch returns MITA_ERR_HIP.  Faults during kernel execution show
+ * up at the caller's next synchronisation (HIP semantics).  NaN or infinite
+ * inputs give unspecified values, not an error.  mita_last_error() returns a
+ * human-readable reason for the calling thread's last failure.
+ */
+#ifndef MITA_H
+#define MITA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MITA_VERSION 1
+
+typedef enum {
+  MITA_OK = 0,
+  MITA_ERR_INVALID_ARG = -1, /* a pointer, size or value breaks the rules below */
+  MITA_ERR_UNSUPPORTED = -2, /* valid MiTA, but outside this build's limits */
+  MITA_ERR_OOM = -3,         /* work-space allocation failed */
+  MITA_ERR_HIP = -4,         /* a HIP call or kernel launch failed */
+  MITA_ERR_INTERNAL = -5     /* unexpected internal condition */
+} mita_status;
+
+typedef enum {
+  MITA_F32 = 0, /* Q, K, V and Ql in fp32; fp32 MFMA and arithmetic */
+  MITA_BF16 = 1 /* Q, K, V and Ql in bfloat16; bf16 MFMA, fp32 accumulation */
+} mita_dtype;
+
+/* Token grid gh x gw (tokens numbered row-major, gh*gw == N) and landmark
+ * grid mh x mw (mh*mw == m).  Landmark i = a*mw + c pools rows
+ * [floor(a*gh/mh), ceil((a+1)*gh/mh)) x columns [floor(c*gw/mw),
+ * ceil((c+1)*gw/mw)).  A 1D sequence is {1, N, 1, m}: contiguous windows of
+ * N/m tokens when m divides N. */
+typedef struct {
+  int32_t gh, gw, mh, mw;
+} mita_grid;
+
+/* Optional intermediate outputs (each pointer may be NULL): device buffers
+ * owned by the caller.
+ *   ql      [B][H][m][d]  landmark queries, input type
+ *   vl      [B][H][m][d]  landmark values, fp32
+ *   perm    [B][H][N]     queries ordered by (route, query index)
+ *   offsets [B][H][m+1]   start of each expert's group in perm; offsets[m]=N */
+typedef struct {
+  void* ql;
+  float* vl;
+  int32_t* perm;
+  int32_t* offsets;
+} mita_intermediates;
+
+/*
+ * mita_forward — the whole forward pass, enqueued on `stream`.
+ *
+ *   Q, K, V    [B][H][N][d] in `dtype`
+ *   dtype      a mita_dtype value
+ *   B, H, N    >= 1, N < 2^31, B*H*N*d < 2^40
+ *   d          head dimension; this build supports d == 64 only
+ *              (others: MITA_ERR_UNSUPPORTED)
+ *   grid       pooling geometry; NULL means the 1D grid {1, N, 1, m}
+ *   m          number of landmarks/experts, 1 <= m <= N, m <= 64 in this build
+ *   k          keys per expert, 1 <= k <= N, k <= 64 in this build
+ *   scale      softmax temperature (usually 1/sqrt(d)); finite and > 0.
+ *              Selection (step 2a) and routing (step 3) use unscaled dots.
+ *   out        [B][H][N][d] fp32
+ *   idx_out    [B][H][m][k] int32, ascending key indices of each expert
+ *   route_out  [B][H][N] int32 in [0, m)
+ *   stream     a hipStream_t (NULL = the default stream)
+ *
+ * Returns MITA_OK once the work is enqueued.
+ */
+int mita_forward(const void* Q, const void* K, const void* V, int dtype, int64_t B, int64_t H,
+                 int64_t N, int64_t d, const mita_grid* grid, int64_t m, int64_t k, float scale,
+                 float* out, int32_t* idx_out, int32_t* route_out, void* stream);
+
+/* mita_forward_ex — mita_forward plus the intermediates of steps 1, 2b and 4
+ * (dbg may be NULL, and so may each of its members). */
+int mita_forward_ex(const void* Q, const void* K, const void* V, int dtype, int64_t B,
+                    int64_t H, int64_t N, int64_t d, const mita_grid* grid, int64_t m,
+                    int64_t k, float scale, float* out, int32_t* idx_out, int32_t* route_out,
+                    void* stream, const mita_intermediates* dbg);
+
+/* Static description of a status code (never NULL). */
+const char* mita_status_string(int status);
+
+/* Detail of the calling thread's last failed call ("" if none). */
+const char* mita_last_error(void);
+
+/* MITA_VERSION of the loaded library. */
+int mita_version(void);
+
+/*
+ * Stage profiler (for measurement; off by default).  While enabled, each
+ * forward call records a pair of HIP events around every stage on the
+ * call's stream.  mita_profile_read() waits for the recorded events and
+ * returns, per stage, the summed milliseconds and the number of calls since
+ * the last mita_profile_enable().  Not thread-safe: profile from one thread.
+ *   mita_profile_enable(1) clears the sums and starts recording;
+ *   mita_profile_enable(0) stops recording (the sums stay readable).
+ */
+int mita_profile_enable(int enabled);
+int mita_profile_stage_count(void);
+const char* mita_profile_stage_name(int stage);
+int mita_profile_read(double* ms_per_stage, int64_t* calls, int n_stages);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MITA_H */

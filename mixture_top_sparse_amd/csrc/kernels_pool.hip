@@ -1,0 +1,121 @@
+// kernels_pool.hip — step 1: landmark queries by local average pooling of Q.
+//
+// Landmark i averages Q over its window of the token grid (the pages pool
+// landmark queries locally from Q: "NeurIPS'26：注意力也是FFN？…", section
+// "用少量地标查询，同时构造全局概括与细节专家"; "Mixture-of-Top-k 注意力…",
+// section "MiTA：用少量地标查询，同时完成压缩与专家构造").  Windows are the
+// adaptive-pooling bins rows [floor(a*gh/mh), ceil((a+1)*gh/mh)) x columns
+// [floor(c*gw/mw), ceil((c+1)*gw/mw)).
+//
+// Precision: window sums are accumulated in fp64 and divided once in fp64,
+// then rounded to the input type directly from fp64.  For bf16 inputs
+// (8-bit significands) these fp64 sums are exact, hence independent of the
+// order in which the partial sums below are combined.
+//
+// Roofline: HBM-bound streaming read of Q (N*d*e bytes per head), m*d*e
+// bytes written.
+#include "mita_device.hpp"
+#include "mita_internal.hpp"
+
+namespace mita {
+
+__device__ __forceinline__ void window_bounds(int gh, int gw, int mh, int mw, int i, int64_t& r0,
+                                              int64_t& r1, int64_t& c0, int64_t& c1) {
+  const int64_t a = i / mw, c = i % mw;
+  r0 = (a * gh) / mh;
+  r1 = ((a + 1) * gh + mh - 1) / mh;
+  c0 = (c * gw) / mw;
+  c1 = ((c + 1) * gw + mw - 1) / mw;
+}
+
+// load 8 consecutive elements as float
+__device__ __forceinline__ void load8(const uint16_t* p, float (&v)[8]) {
+  const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[2 * j] = __uint_as_float(w[j] << 16);
+    v[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[j] = a[j];
+    v[4 + j] = b[j];
+  }
+}
+
+// grid (pool_splits, m, BH), 256 threads: 32 token rows x 8 column groups
+template <class T>
+__global__ __launch_bounds__(256) void k_pool_partial(const typename T::elem* __restrict__ Q,
+                                                     int64_t N, int gh, int gw, int mh, int mw,
+                                                     int splits, double* __restrict__ part) {
+  __shared__ double red[32][kD + 1];
+  const int split = blockIdx.x, i = blockIdx.y, m = mh * mw;
+  const int64_t bh = blockIdx.z;
+  int64_t r0, r1, c0, c1;
+  window_bounds(gh, gw, mh, mw, i, r0, r1, c0, c1);
+  const int64_t wc = c1 - c0, W = (r1 - r0) * wc;
+  const int64_t t_beg = static_cast<int64_t>(split) * kPoolChunk;
+  const int64_t t_end = t_beg + kPoolChunk < W ? t_beg + kPoolChunk : W;
+  const int col = threadIdx.x & 7, row = threadIdx.x >> 3;
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const typename T::elem* Qh = Q + bh * N * kD;
+  for (int64_t t = t_beg + row; t < t_end; t += 32) {
+    const int64_t tok = (r0 + t / wc) * gw + (c0 + t % wc);
+    float v[8];
+    load8(Qh + tok * kD + col * 8, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] += static_cast<double>(v[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) red[row][col * 8 + j] = acc[j];
+  __syncthreads();
+  if (threadIdx.x < kD) {
+    double s = 0.0;
+    for (int r = 0; r < 32; ++r) s += red[r][threadIdx.x];
+    part[((bh * m + i) * splits + split) * kD + threadIdx.x] = s;
+  }
+}
+
+// grid (m, BH), 64 threads: combine partial sums, divide, round
+template <class T>
+__global__ __launch_bounds__(64) void k_pool_final(const double* __restrict__ part, int gh, int gw,
+                                                  int mh, int mw, int splits,
+                                                  typename T::elem* __restrict__ ql,
+                                                  typename T::elem* __restrict__ ql_copy) {
+  const int i = blockIdx.x, m = mh * mw, j = threadIdx.x;
+  const int64_t bh = blockIdx.y;
+  int64_t r0, r1, c0, c1;
+  window_bounds(gh, gw, mh, mw, i, r0, r1, c0, c1);
+  const double W = static_cast<double>((r1 - r0) * (c1 - c0));
+  double s = 0.0;
+  for (int p = 0; p < splits; ++p) s += part[((bh * m + i) * splits + p) * kD + j];
+  const typename T::elem v = T::from_f64(s / W);
+  ql[(bh * m + i) * kD + j] = v;
+  if (ql_copy) ql_copy[(bh * m + i) * kD + j] = v;
+}
+
+template <class T>
+static hipError_t launch_pool_t(const Shape& s, const void* Q, const Workspace& ws, void* ql_copy,
+                                hipStream_t st) {
+  using E = typename T::elem;
+  hipLaunchKernelGGL(k_pool_partial<T>, dim3(s.pool_splits, s.m, s.BH), dim3(256), 0, st,
+                     static_cast<const E*>(Q), s.N, s.gh, s.gw, s.mh, s.mw, s.pool_splits,
+                     ws.pool_part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_pool_final<T>, dim3(s.m, s.BH), dim3(64), 0, st, ws.pool_part, s.gh, s.gw,
+                     s.mh, s.mw, s.pool_splits, static_cast<E*>(ws.ql), static_cast<E*>(ql_copy));
+  return hipGetLastError();
+}
+
+hipError_t launch_pool(const Shape& s, const void* Q, const Workspace& ws, void* ql_copy,
+                       hipStream_t st) {
+  return s.dtype == 1 ? launch_pool_t<BF16>(s, Q, ws, ql_copy, st)
+                      : launch_pool_t<F32>(s, Q, ws, ql_copy, st);
+}
+
+}  // namespace mita

@@ -1,0 +1,373 @@
+// mita_api.hip — the C ABI (include/mita.h): host-side validation, work-space
+// planning and the launch sequence of the MiTA forward pass.  No device code
+// here; every step of the computation runs in the kernels of the other
+// translation units.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "mita.h"
+#include "mita_internal.hpp"
+
+namespace mita {
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const std::string& why) {
+  g_last_error = why;
+  return status;
+}
+
+int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------------------
+// stage profiler
+// ---------------------------------------------------------------------------
+
+enum Stage { kStagePool = 0, kStageScan, kStageMerge, kStageRoute, kStageBucket, kStageAttend,
+             kStageCount };
+const char* kStageNames[kStageCount] = {"pool", "landmark_scan", "landmark_merge", "route",
+                                        "bucket", "expert_attend"};
+
+struct Profiler {
+  bool enabled = false;
+  std::vector<hipEvent_t> free_events;
+  struct Pending {
+    int stage;
+    hipEvent_t a, b;
+  };
+  std::vector<Pending> pending;
+  double ms[kStageCount] = {};
+  int64_t calls = 0;
+
+  hipEvent_t get() {
+    if (!free_events.empty()) {
+      hipEvent_t e = free_events.back();
+      free_events.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+  void drain() {
+    for (auto& p : pending) {
+      float t = 0.f;
+      if (hipEventSynchronize(p.b) == hipSuccess && hipEventElapsedTime(&t, p.a, p.b) == hipSuccess)
+        ms[p.stage] += t;
+      free_events.push_back(p.a);
+      free_events.push_back(p.b);
+    }
+    pending.clear();
+  }
+};
+Profiler g_prof;
+
+struct StageTimer {
+  int stage;
+  hipStream_t st;
+  hipEvent_t a = nullptr, b = nullptr;
+  StageTimer(int s, hipStream_t stream) : stage(s), st(stream) {
+    if (g_prof.enabled) {
+      a = g_prof.get();
+      b = g_prof.get();
+      if (a && b) hipEventRecord(a, st);
+    }
+  }
+  ~StageTimer() {
+    if (a && b) {
+      hipEventRecord(b, st);
+      g_prof.pending.push_back({stage, a, b});
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// device attributes (cached per device)
+// ---------------------------------------------------------------------------
+
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ---------------------------------------------------------------------------
+// validation (host only, before any HIP call)
+// ---------------------------------------------------------------------------
+
+int validate(const void* Q, const void* K, const void* V, int dtype, int64_t B, int64_t H,
+             int64_t N, int64_t d, const mita_grid* grid, int64_t m, int64_t k, float scale,
+             const float* out, const int32_t* idx_out, const int32_t* route_out,
+             const mita_intermediates* dbg, Shape* s) {
+  if (!Q || !K || !V) return fail(MITA_ERR_INVALID_ARG, "Q, K and V must be non-null");
+  if (!out || !idx_out || !route_out)
+    return fail(MITA_ERR_INVALID_ARG, "out, idx_out and route_out must be non-null");
+  if (dtype != MITA_F32 && dtype != MITA_BF16)
+    return fail(MITA_ERR_INVALID_ARG, "dtype must be MITA_F32 or MITA_BF16");
+  if (B < 1 || H < 1 || N < 1) return fail(MITA_ERR_INVALID_ARG, "B, H and N must be >= 1");
+  if (d < 1) return fail(MITA_ERR_INVALID_ARG, "d must be >= 1");
+  if (N >= (int64_t(1) << 31)) return fail(MITA_ERR_INVALID_ARG, "N must be < 2^31");
+  if (B > (int64_t(1) << 30) || H > (int64_t(1) << 30) || B * H > 65535)
+    return fail(MITA_ERR_UNSUPPORTED, "B*H must be <= 65535 in this build");
+  if (d != kD) return fail(MITA_ERR_UNSUPPORTED, "only d == 64 is supported in this build");
+  if ((B * H) > (int64_t(1) << 40) / (N * d))
+    return fail(MITA_ERR_INVALID_ARG, "B*H*N*d must be < 2^40");
+  if (m < 1 || m > N) return fail(MITA_ERR_INVALID_ARG, "m must satisfy 1 <= m <= N");
+  if (k < 1 || k > N) return fail(MITA_ERR_INVALID_ARG, "k must satisfy 1 <= k <= N");
+  if (m > kMaxM) return fail(MITA_ERR_UNSUPPORTED, "m must be <= 64 in this build");
+  if (k > kMaxK) return fail(MITA_ERR_UNSUPPORTED, "k must be <= 64 in this build");
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(MITA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  mita_grid gr = grid ? *grid : mita_grid{1, static_cast<int32_t>(N), 1, static_cast<int32_t>(m)};
+  if (gr.gh < 1 || gr.gw < 1 || gr.mh < 1 || gr.mw < 1)
+    return fail(MITA_ERR_INVALID_ARG, "grid sizes must be >= 1");
+  if (int64_t(gr.gh) * gr.gw != N) return fail(MITA_ERR_INVALID_ARG, "grid gh*gw must equal N");
+  if (int64_t(gr.mh) * gr.mw != m) return fail(MITA_ERR_INVALID_ARG, "grid mh*mw must equal m");
+  if (gr.mh > gr.gh || gr.mw > gr.gw)
+    return fail(MITA_ERR_INVALID_ARG, "landmark grid must not exceed the token grid");
+  const void* ptrs[] = {Q, K, V, out, idx_out, route_out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(MITA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (dbg) {
+    const void* dp[] = {dbg->ql, dbg->vl, dbg->perm, dbg->offsets};
+    for (const void* p : dp)
+      if (p && !aligned16(p))
+        return fail(MITA_ERR_INVALID_ARG, "intermediate pointers must be 16-byte aligned");
+  }
+  s->B = B;
+  s->H = H;
+  s->BH = B * H;
+  s->N = N;
+  s->m = static_cast<int>(m);
+  s->k = static_cast<int>(k);
+  s->gh = gr.gh;
+  s->gw = gr.gw;
+  s->mh = gr.mh;
+  s->mw = gr.mw;
+  s->scale = scale;
+  s->dtype = dtype;
+  return MITA_OK;
+}
+
+// largest pooling window of the grid (same bin rule as the kernels)
+int64_t max_window(const Shape& s) {
+  int64_t best = 0;
+  for (int i = 0; i < s.m; ++i) {
+    const int64_t a = i / s.mw, c = i % s.mw;
+    const int64_t r0 = (a * s.gh) / s.mh, r1 = ((a + 1) * s.gh + s.mh - 1) / s.mh;
+    const int64_t c0 = (c * s.gw) / s.mw, c1 = ((c + 1) * s.gw + s.mw - 1) / s.mw;
+    const int64_t w = (r1 - r0) * (c1 - c0);
+    if (w > best) best = w;
+  }
+  return best;
+}
+
+void derive(Shape& s, int cus) {
+  s.mpad = static_cast<int>(round_up(s.m, 32));
+  s.kpad = static_cast<int>(round_up(s.k, 32));
+  s.scan_waves = s.m <= 16 ? 1 : (s.m <= 32 ? 2 : 4);
+  s.mrows = s.scan_waves * 16;
+  // landmark scan: about two blocks per CU, chunks of at least 512 keys
+  const int64_t target = 2 * static_cast<int64_t>(cus);
+  int64_t chunk = round_up(cdiv(s.N * s.BH, target), kTileKeys);
+  if (chunk < 512) chunk = 512;
+  if (chunk > round_up(s.N, kTileKeys)) chunk = round_up(s.N, kTileKeys);
+  s.scan_chunk = static_cast<int>(chunk);
+  s.scan_splits = static_cast<int>(cdiv(s.N, chunk));
+  s.pool_splits = static_cast<int>(cdiv(max_window(s), kPoolChunk));
+  s.nseg = static_cast<int>(cdiv(s.N, kRouteSeg));
+  s.attend_tiles = static_cast<int>(cdiv(s.N, kAttendTile) + s.m);
+}
+
+}  // namespace
+
+size_t plan_workspace(const Shape& s, Workspace* ws, char* base) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char* {
+    char* p = base ? base + off : nullptr;
+    off += (bytes + 255) / 256 * 256;
+    return p;
+  };
+  const size_t BH = static_cast<size_t>(s.BH), es = s.dtype == MITA_BF16 ? 2 : 4;
+  ws->pool_part = reinterpret_cast<double*>(take(BH * s.m * s.pool_splits * kD * sizeof(double)));
+  ws->ql = take(BH * s.m * kD * es);
+  ws->theta = nullptr;
+  const size_t parts = BH * s.scan_splits * s.mrows;
+  ws->part_keys = reinterpret_cast<uint64_t*>(take(parts * kTopCap * sizeof(uint64_t)));
+  ws->part_stats = reinterpret_cast<float*>(take(parts * 2 * sizeof(float)));
+  ws->part_acc = reinterpret_cast<float*>(take(parts * kD * sizeof(float)));
+  ws->vl = reinterpret_cast<float*>(take(BH * s.m * kD * sizeof(float)));
+  if (s.dtype == MITA_BF16) {
+    ws->vlt_hi = reinterpret_cast<uint16_t*>(take(BH * kD * s.mpad * 2));
+    ws->vlt_lo = reinterpret_cast<uint16_t*>(take(BH * kD * s.mpad * 2));
+  } else {
+    ws->vlt_hi = ws->vlt_lo = nullptr;
+  }
+  ws->counts = reinterpret_cast<int32_t*>(take(BH * s.nseg * s.m * 4));
+  ws->seg_base = reinterpret_cast<int32_t*>(take(BH * s.nseg * s.m * 4));
+  ws->offsets = reinterpret_cast<int32_t*>(take(BH * (s.m + 1) * 4));
+  ws->tile_start = reinterpret_cast<int32_t*>(take(BH * (s.m + 1) * 4));
+  ws->perm = reinterpret_cast<int32_t*>(take(BH * s.N * 4));
+  return off;
+}
+
+}  // namespace mita
+
+using namespace mita;
+
+extern "C" {
+
+int mita_version(void) { return MITA_VERSION; }
+
+const char* mita_status_string(int status) {
+  switch (status) {
+    case MITA_OK: return "success";
+    case MITA_ERR_INVALID_ARG: return "invalid argument";
+    case MITA_ERR_UNSUPPORTED: return "unsupported by this build";
+    case MITA_ERR_OOM: return "work-space allocation failed";
+    case MITA_ERR_HIP: return "HIP runtime or launch error";
+    case MITA_ERR_INTERNAL: return "internal error";
+    default: return "unknown status";
+  }
+}
+
+const char* mita_last_error(void) { return g_last_error.c_str(); }
+
+int mita_forward_ex(const void* Q, const void* K, const void* V, int dtype, int64_t B, int64_t H,
+                    int64_t N, int64_t d, const mita_grid* grid, int64_t m, int64_t k,
+                    float scale, float* out, int32_t* idx_out, int32_t* route_out, void* stream,
+                    const mita_intermediates* dbg) {
+  try {
+    g_last_error.clear();
+    Shape s;
+    int rc = validate(Q, K, V, dtype, B, H, N, d, grid, m, k, scale, out, idx_out, route_out, dbg,
+                      &s);
+    if (rc != MITA_OK) return rc;
+    const char* inject = std::getenv("MITA_FAULT_INJECT");
+    if (inject && std::strcmp(inject, "alloc") == 0)
+      return fail(MITA_ERR_OOM, "work-space allocation failed (injected by MITA_FAULT_INJECT)");
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    derive(s, device_cus());
+    Workspace ws;
+    const size_t bytes = plan_workspace(s, &ws, nullptr);
+    void* base = nullptr;
+    hipError_t e = hipMallocAsync(&base, bytes, st);
+    if (e != hipSuccess || base == nullptr) {
+      (void)hipGetLastError();
+      return fail(MITA_ERR_OOM, std::string("hipMallocAsync of work space failed: ") +
+                                    hipGetErrorString(e));
+    }
+    plan_workspace(s, &ws, static_cast<char*>(base));
+
+    void* ql_copy = dbg ? dbg->ql : nullptr;
+    float* vl_copy = dbg ? dbg->vl : nullptr;
+    int32_t* perm_copy = dbg ? dbg->perm : nullptr;
+    int32_t* off_copy = dbg ? dbg->offsets : nullptr;
+    const bool inject_launch = inject && std::strcmp(inject, "launch") == 0;
+
+    const char* where = "pool";
+    if (inject_launch) e = hipErrorLaunchFailure;
+    if (e == hipSuccess) {
+      StageTimer t(kStagePool, st);
+      e = launch_pool(s, Q, ws, ql_copy, st);
+    }
+    if (e == hipSuccess) {
+      where = "landmark_scan";
+      StageTimer t(kStageScan, st);
+      e = launch_scan(s, K, V, ws, st);
+    }
+    if (e == hipSuccess) {
+      where = "landmark_merge";
+      StageTimer t(kStageMerge, st);
+      e = launch_merge(s, ws, idx_out, vl_copy, st);
+    }
+    if (e == hipSuccess) {
+      where = "route";
+      StageTimer t(kStageRoute, st);
+      e = launch_route(s, Q, ws, route_out, st);
+    }
+    if (e == hipSuccess) {
+      where = "bucket";
+      StageTimer t(kStageBucket, st);
+      e = launch_bucket(s, route_out, ws, off_copy, perm_copy, st);
+    }
+    if (e == hipSuccess) {
+      where = "expert_attend";
+      StageTimer t(kStageAttend, st);
+      e = launch_attend(s, Q, K, V, idx_out, ws, out, st);
+    }
+    if (g_prof.enabled && e == hipSuccess) g_prof.calls += 1;
+    const hipError_t ef = hipFreeAsync(base, st);
+    if (e != hipSuccess)
+      return fail(MITA_ERR_HIP, std::string("launch of stage ") + where +
+                                    " failed: " + hipGetErrorString(e));
+    if (ef != hipSuccess)
+      return fail(MITA_ERR_HIP, std::string("hipFreeAsync failed: ") + hipGetErrorString(ef));
+    return MITA_OK;
+  } catch (...) {
+    return fail(MITA_ERR_INTERNAL, "unexpected exception inside mita_forward");
+  }
+}
+
+int mita_forward(const void* Q, const void* K, const void* V, int dtype, int64_t B, int64_t H,
+                 int64_t N, int64_t d, const mita_grid* grid, int64_t m, int64_t k, float scale,
+                 float* out, int32_t* idx_out, int32_t* route_out, void* stream) {
+  return mita_forward_ex(Q, K, V, dtype, B, H, N, d, grid, m, k, scale, out, idx_out, route_out,
+                         stream, nullptr);
+}
+
+int mita_profile_enable(int enabled) {
+  try {
+    if (enabled) {
+      g_prof.drain();
+      for (double& v : g_prof.ms) v = 0.0;
+      g_prof.calls = 0;
+      g_prof.enabled = true;
+    } else {
+      g_prof.enabled = false;
+    }
+    return MITA_OK;
+  } catch (...) {
+    return fail(MITA_ERR_INTERNAL, "profiler failure");
+  }
+}
+
+int mita_profile_stage_count(void) { return kStageCount; }
+
+const char* mita_profile_stage_name(int stage) {
+  return (stage >= 0 && stage < kStageCount) ? kStageNames[stage] : "";
+}
+
+int mita_profile_read(double* ms_per_stage, int64_t* calls, int n_stages) {
+  try {
+    if (!ms_per_stage || !calls || n_stages < 1)
+      return fail(MITA_ERR_INVALID_ARG, "profile_read needs output arrays");
+    g_prof.drain();
+    for (int i = 0; i < n_stages && i < kStageCount; ++i) ms_per_stage[i] = g_prof.ms[i];
+    *calls = g_prof.calls;
+    return MITA_OK;
+  } catch (...) {
+    return fail(MITA_ERR_INTERNAL, "profiler failure");
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// mita_internal.hpp — shapes, work-space layout and kernel launchers of the
+// MiTA forward pass (host side; no device code here).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mita {
+
+constexpr int kD = 64;           // head dimension supported by this build
+constexpr int kMaxM = 64;        // landmarks (= experts)
+constexpr int kMaxK = 64;        // keys per expert
+constexpr int kTopCap = 64;      // per-split top list length (one key per lane)
+constexpr int kTileKeys = 64;    // keys per landmark-scan tile
+constexpr int kRouteSeg = 1024;  // queries per routing/bucketing segment
+constexpr int kAttendTile = 64;  // queries per expert-attention tile
+constexpr int kPoolChunk = 2048; // tokens per pooling partial sum
+
+struct Shape {
+  int64_t B = 0, H = 0, BH = 0, N = 0;
+  int m = 0, k = 0;
+  int gh = 0, gw = 0, mh = 0, mw = 0;
+  float scale = 0.f;
+  int dtype = 0;  // mita_dtype
+  // derived
+  int mpad = 0;        // m rounded up to 32 (attention pair blocks)
+  int kpad = 0;        // k rounded up to 32
+  int scan_waves = 0;  // 1, 2 or 4 waves of 16 landmarks
+  int mrows = 0;       // scan_waves * 16
+  int scan_chunk = 0;  // keys per landmark-scan block
+  int scan_splits = 0;
+  int pool_splits = 0; // partial sums per landmark window
+  int nseg = 0;        // routing segments per head
+  int attend_tiles = 0;// upper bound of expert tiles per head
+};
+
+// Work space carved from one stream-ordered allocation.
+struct Workspace {
+  double* pool_part = nullptr;   // [BH][m][pool_splits][64] fp64 partial window sums
+  void* ql = nullptr;            // [BH][m][64] landmark queries (input type)
+  float* theta = nullptr;        // [BH][mrows] top-k pre-filter scores (unused: -inf)
+  uint64_t* part_keys = nullptr; // [BH][splits][mrows][64] per-split top lists
+  float* part_stats = nullptr;   // [BH][splits][mrows][2] (max in log2 units, sum)
+  float* part_acc = nullptr;     // [BH][splits][mrows][64] unnormalised P.V
+  float* vl = nullptr;           // [BH][m][64] landmark values fp32
+  uint16_t* vlt_hi = nullptr;    // [BH][64][mpad] bf16 hi part of Vl^T (bf16 path)
+  uint16_t* vlt_lo = nullptr;    // [BH][64][mpad] bf16 lo part of Vl^T
+  int32_t* counts = nullptr;     // [BH][nseg][m] routed queries per segment and expert
+  int32_t* seg_base = nullptr;   // [BH][nseg][m] first perm slot of each (segment, expert)
+  int32_t* offsets = nullptr;    // [BH][m+1]
+  int32_t* tile_start = nullptr; // [BH][m+1] first attention tile of each expert
+  int32_t* perm = nullptr;       // [BH][N]
+};
+
+size_t plan_workspace(const Shape& s, Workspace* ws, char* base);
+
+// Kernel launchers; each returns the launch status.
+hipError_t launch_pool(const Shape& s, const void* Q, const Workspace& ws, void* ql_copy,
+                       hipStream_t st);
+hipError_t launch_scan(const Shape& s, const void* K, const void* V, const Workspace& ws,
+                       hipStream_t st);
+hipError_t launch_merge(const Shape& s, const Workspace& ws, int32_t* idx_out, float* vl_copy,
+                        hipStream_t st);
+hipError_t launch_route(const Shape& s, const void* Q, const Workspace& ws, int32_t* route_out,
+                        hipStream_t st);
+hipError_t launch_bucket(const Shape& s, const int32_t* route, const Workspace& ws,
+                         int32_t* offsets_copy, int32_t* perm_copy, hipStream_t st);
+hipError_t launch_attend(const Shape& s, const void* Q, const void* K, const void* V,
+                         const int32_t* idx, const Workspace& ws, float* out, hipStream_t st);
+
+}  // namespace mita

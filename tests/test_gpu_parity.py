@@ -1,0 +1,165 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Every test prints the case it is about to run before touching the GPU."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+from mixture_top_sparse_amd.inputs import WORKLOADS, Workload, generate, to_torch
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _say(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mixture_top_sparse_amd as mts
+
+    mts.lib()  # fail loudly if the library is missing
+
+
+def _run(w: Workload, Q, K, V):
+    import mixture_top_sparse_amd as mts
+    from parity import gpu_results_to_numpy
+
+    Qt, Kt, Vt = to_torch((Q, K, V), w.dtype, "cuda")
+    res = mts.mita_forward_ex(Qt, Kt, Vt, m=w.m, k=w.k, grid=w.grid, scale=w.scale)
+    g = gpu_results_to_numpy(res)
+    exact = [t.to("cpu").to(torch.float64).numpy() for t in (Qt, Kt, Vt)]
+    return g, exact
+
+
+def _check(w, g, exact, heads=None, qsel=None, exact_ties=False):
+    from parity import Report, check_head
+
+    rep = Report()
+    Qd, Kd, Vd = exact
+    pairs = heads if heads is not None else [(b, h) for b in range(w.B) for h in range(w.H)]
+    for b, h in pairs:
+        gh = {key: val[b, h] for key, val in g.items()}
+        check_head(w, Qd[b, h], Kd[b, h], Vd[b, h], gh, rep, qsel=qsel, exact_ties=exact_ties)
+    _say(f"{w.name}: {rep.summary()}")
+    assert rep.ok(), rep.failures
+
+
+# ---------------------------------------------------------------------------
+# the workloads: whole outputs where the oracle is quick, samples at full size
+# ---------------------------------------------------------------------------
+
+FULL = ["tiny_f32_14x14", "deit_s_14x14", "seg_40x40", "seg_32x32", "long1d_16k"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_workload_full(name):
+    w = WORKLOADS[name]
+    _say(f"case {name} B={w.B} H={w.H} N={w.N} m={w.m} k={w.k} {w.dtype}")
+    Q, K, V = generate(w)
+    g, exact = _run(w, Q, K, V)
+    heads = None
+    if name == "long1d_16k":
+        heads = [(0, 0), (1, 3), (3, 7)]
+    _check(w, g, exact, heads=heads)
+
+
+SAMPLED = ["long1d_32k", "long1d_64k", "len_64k", "len_256k", "len_1m"]
+
+
+@pytest.mark.parametrize("name", SAMPLED)
+def test_workload_sampled(name):
+    w = WORKLOADS[name]
+    _say(f"case {name} B={w.B} H={w.H} N={w.N} m={w.m} k={w.k} {w.dtype} (sampled)")
+    Q, K, V = generate(w)
+    g, exact = _run(w, Q, K, V)
+    rng = np.random.default_rng(123)
+    qsel = np.unique(np.concatenate([np.arange(64), np.arange(w.N - 64, w.N),
+                                     rng.choice(w.N, 1500, replace=False)]))
+    heads = [(0, 0), (w.B - 1, w.H - 1)]
+    _check(w, g, exact, heads=heads, qsel=qsel)
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+
+
+def _edge(name, B, H, N, grid, k, dtype="bf16", values="iid", seed=100, centres=0):
+    return Workload(name, B, H, N, 64, dtype, grid, k, values, centres, 0.5 if centres else 0.0,
+                    seed)
+
+
+EDGES = {
+    # N not a multiple of the 64-key tile, m does not divide N (overlapping
+    # adaptive 1D windows), k not a multiple of 16
+    "ragged_1d": _edge("ragged_1d", 2, 2, 1000, (1, 1000, 1, 10), 7),
+    "single_landmark_k1": _edge("single_landmark_k1", 1, 2, 300, (1, 300, 1, 1), 1),
+    "k_equals_n": _edge("k_equals_n", 1, 1, 48, (1, 48, 1, 3), 48),
+    "m_equals_n": _edge("m_equals_n", 1, 1, 64, (8, 8, 8, 8), 64),
+    "grid_12x20": _edge("grid_12x20", 2, 1, 240, (12, 20, 3, 5), 33, values="mixture", centres=16),
+    "f32_ragged": _edge("f32_ragged", 1, 3, 777, (1, 777, 1, 40), 50, dtype="f32"),
+    "m17_k63": _edge("m17_k63", 1, 2, 5000, (1, 5000, 1, 17), 63, values="mixture", centres=32),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EDGES))
+def test_edge_case(name):
+    w = EDGES[name]
+    _say(f"case {name} B={w.B} H={w.H} N={w.N} grid={w.grid} k={w.k} {w.dtype}")
+    Q, K, V = generate(w)
+    g, exact = _run(w, Q, K, V)
+    _check(w, g, exact)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_exact_ties_resolve_to_lowest_index(dtype):
+    """Small-integer inputs: every dot product is exact in fp32 and fp64, so
+    equal scores are true ties on both sides and must resolve to the lower
+    key (top-k) and the lower landmark (routing) exactly."""
+    w = _edge(f"ties_{dtype}", 1, 2, 640, (1, 640, 1, 16), 20, dtype=dtype)
+    rng = np.random.default_rng(7)
+    Q = rng.integers(-2, 3, size=(1, 2, 640, 64)).astype(np.float32)
+    K = rng.integers(-1, 2, size=(1, 2, 640, 64)).astype(np.float32)
+    V = rng.integers(-3, 4, size=(1, 2, 640, 64)).astype(np.float32)
+    K[:, :, 100:110] = K[:, :, 5:15]  # duplicated keys: equal scores at different indices
+    # windows of 40 tokens: make the landmark means exact small values
+    Q[:, :, :, :] = np.repeat(Q[:, :, ::40, :], 40, axis=2)
+    _say(f"case exact ties {dtype}")
+    g, exact = _run(w, Q, K, V)
+    _check(w, g, exact, exact_ties=True)
+
+
+def test_all_queries_one_expert():
+    """Constant queries: every landmark is the same vector, every routing
+    logit ties, so all N queries go to expert 0 (many tiles of one expert,
+    m-1 empty experts)."""
+    w = _edge("one_expert", 1, 1, 4000, (1, 4000, 1, 8), 16)
+    rng = np.random.default_rng(8)
+    Q = np.full((1, 1, 4000, 64), 0.5, np.float32)
+    K = rng.standard_normal((1, 1, 4000, 64)).astype(np.float32)
+    V = rng.standard_normal((1, 1, 4000, 64)).astype(np.float32)
+    _say("case all queries to one expert")
+    g, exact = _run(w, Q, K, V)
+    assert np.all(g["route"] == 0)
+    assert g["offsets"][0, 0].tolist() == [0] + [4000] * 8
+    _check(w, g, exact, exact_ties=False)
+
+
+def test_deterministic():
+    """Two runs give bitwise-identical results (no races in merges or scatter)."""
+    w = WORKLOADS["len_64k"]
+    _say("case determinism len_64k")
+    Q, K, V = generate(w)
+    g1, _ = _run(w, Q, K, V)
+    g2, _ = _run(w, Q, K, V)
+    for key in g1:
+        assert np.array_equal(g1[key], g2[key]), key

@@ -95,6 +95,27 @@ def cpu_baseline(w, Qt, Kt, Vt, g_out, g_idx, g_route):
     }
 
 
+def copy_probe(nbytes: int = 1 << 30, reps: int = 10) -> dict:
+    """A plain elementwise copy (torch.neg of 1 GiB of fp32 into another
+    buffer): nbytes read + nbytes written per launch."""
+    import torch
+
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.neg(x, out=y)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "ms": round(ms, 4),
+            "GBs": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,6 +123,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="len_1m")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also time a plain 1 GiB device copy kernel (bandwidth context and the "
+                         "calibration kernel for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the MiTA forward here runs on a single MI355X "
@@ -197,6 +221,8 @@ def main() -> int:
                       "bucket_size_min_med_max": [int(sizes.min()), float(np.median(sizes)),
                                                   int(sizes.max())]},
     }
+    if args.copy_probe:
+        line["copy_probe"] = copy_probe()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, Qt, Kt, Vt, out, idx, route)
     print(json.dumps(line), flush=True)

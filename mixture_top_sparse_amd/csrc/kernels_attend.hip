@@ -47,19 +47,24 @@ struct AttendLds<F32, MPAD, KPAD> {
 };
 
 struct TileInfo {
-  int e, qb, qe;
+  int e;      // expert
+  int qb;     // first perm slot of this work item
+  int qe;     // one past its last perm slot
 };
 
-__device__ __forceinline__ bool find_tile(const int32_t* __restrict__ tile_start,
-                                          const int32_t* __restrict__ offsets, int m, int t,
-                                          TileInfo& ti) {
-  if (t >= tile_start[m]) return false;
+// Work item t of a head covers up to `tpb` consecutive 64-query tiles of one
+// expert; item_start[e] is the first item of expert e (exclusive scan of
+// ceil(tiles_e / tpb)).
+__device__ __forceinline__ bool find_item(const int32_t* __restrict__ item_start,
+                                          const int32_t* __restrict__ offsets, int m, int tpb,
+                                          int t, TileInfo& ti) {
+  if (t >= item_start[m]) return false;
   int e = 0;
-  while (e < m - 1 && tile_start[e + 1] <= t) ++e;
-  const int j = t - tile_start[e];
+  while (e < m - 1 && item_start[e + 1] <= t) ++e;
+  const int j0 = (t - item_start[e]) * tpb;
   ti.e = e;
-  ti.qb = offsets[e] + kAttendTile * j;
-  ti.qe = min(ti.qb + kAttendTile, static_cast<int>(offsets[e + 1]));
+  ti.qb = offsets[e] + kAttendTile * j0;
+  ti.qe = min(ti.qb + kAttendTile * tpb, static_cast<int>(offsets[e + 1]));
   return true;
 }
 
@@ -70,18 +75,14 @@ __device__ __forceinline__ int64_t clamp_index(int64_t v, int64_t n) {
 // ---- bf16 ----------------------------------------------------------------
 
 template <int MPAD, int KPAD>
-__device__ void attend_bf16(AttendLds<BF16, MPAD, KPAD>& S, const uint16_t* __restrict__ Q,
-                            const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-                            const uint16_t* __restrict__ Ql, const uint16_t* __restrict__ vlt_hi,
-                            const uint16_t* __restrict__ vlt_lo, const int32_t* __restrict__ idx,
-                            const int32_t* __restrict__ perm, int64_t N, int m, int k, float c2,
-                            float* __restrict__ out, int64_t bh, const TileInfo& ti) {
+__device__ void stage_bf16(AttendLds<BF16, MPAD, KPAD>& S, const uint16_t* __restrict__ K,
+                           const uint16_t* __restrict__ V, const uint16_t* __restrict__ Ql,
+                           const uint16_t* __restrict__ vlt_hi, const uint16_t* __restrict__ vlt_lo,
+                           const int32_t* __restrict__ ex, int64_t N, int m, int k, int64_t bh) {
   using L = AttendLds<BF16, MPAD, KPAD>;
   constexpr int NP = MPAD + KPAD;
-  const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
-  const int32_t* ex = idx + (bh * m + ti.e) * k;
+  const int tid = threadIdx.x;
   const u32x4 z = {0, 0, 0, 0};
-
   // pair keys: Ql rows then the expert's K rows (zero rows for padding)
   for (int c = tid; c < NP * 8; c += 256) {
     const int row = c >> 3, col = c & 7;
@@ -114,23 +115,22 @@ __device__ void attend_bf16(AttendLds<BF16, MPAD, KPAD>& S, const uint16_t* __re
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint32_t wa = a[i >> 1], wb = b[i >> 1];
-      const uint32_t word = (i & 1) ? ((wa >> 16) | (wb & 0xFFFF0000u)) : ((wa & 0xFFFFu) | (wb << 16));
+      const uint32_t word =
+          (i & 1) ? ((wa >> 16) | (wb & 0xFFFF0000u)) : ((wa & 0xFFFFu) | (wb << 16));
       *reinterpret_cast<uint32_t*>(S.vr + (col * 8 + i) * L::VRST + 2 * rp) = word;
     }
   }
-  __syncthreads();
+}
 
-  // this lane's query
-  const int pos = ti.qb + 16 * w + c16;
-  const bool qok = pos < ti.qe && pos >= 0 && pos < N;
-  const int64_t q = qok ? clamp_index(perm[bh * N + pos], N) : 0;
-  bf16x8 qb[2];
-#pragma unroll
-  for (int s = 0; s < 2; ++s)
-    qb[s] = as_bf16x8(qok ? *reinterpret_cast<const u32x4*>(Q + (bh * N + q) * kD + 32 * s + 8 * g)
-                          : z);
-
-  constexpr int NPB = NP / 16;
+// 16 queries of one wave (lane column c16 = query) against the staged expert
+template <int MPAD, int KPAD>
+__device__ __forceinline__ void attend_queries_bf16(const AttendLds<BF16, MPAD, KPAD>& S,
+                                                    const bf16x8 (&qb)[2], bool qok, int64_t q,
+                                                    int m, int k, float c2,
+                                                    float* __restrict__ out_h) {
+  using L = AttendLds<BF16, MPAD, KPAD>;
+  constexpr int NPB = (MPAD + KPAD) / 16;
+  const int l = lane_id(), g = l >> 4, c16 = l & 15;
   float x[NPB][4];
   float mx = -INFINITY;
 #pragma unroll
@@ -138,26 +138,26 @@ __device__ void attend_bf16(AttendLds<BF16, MPAD, KPAD>& S, const uint16_t* __re
     f32x4 a = {0, 0, 0, 0};
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const bf16x8 kk =
-          as_bf16x8(*reinterpret_cast<const u32x4*>(S.pk + (16 * pb + c16) * L::PKST + 32 * s + 8 * g));
+      const bf16x8 kk = as_bf16x8(
+          *reinterpret_cast<const u32x4*>(S.pk + (16 * pb + c16) * L::PKST + 32 * s + 8 * g));
       a = mfma_bf16(kk, qb[s], a);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int p = 16 * pb + 4 * g + r;
       const bool valid = (p < MPAD) ? (p < m) : (p - MPAD < k);
-      x[pb][r] = valid ? a[r] * c2 : -INFINITY;
+      x[pb][r] = valid ? a[r] : -INFINITY;
       mx = fmaxf(mx, x[pb][r]);
     }
   }
   mx = xor_max(mx, 16);
-  mx = xor_max(mx, 32);
+  mx = xor_max(mx, 32) * c2;
   float lsum = 0.f;
 #pragma unroll
   for (int pb = 0; pb < NPB; ++pb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      x[pb][r] = exp2f(x[pb][r] - mx);
+      x[pb][r] = fast_exp2(fmaf(x[pb][r], c2, -mx));
       lsum += x[pb][r];
     }
   lsum = xor_sum(lsum, 16);
@@ -214,7 +214,53 @@ __device__ void attend_bf16(AttendLds<BF16, MPAD, KPAD>& S, const uint16_t* __re
     const float inv = 1.0f / lsum;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
-      *reinterpret_cast<f32x4*>(out + (bh * N + q) * kD + 16 * dt + 4 * g) = acc[dt] * inv;
+      *reinterpret_cast<f32x4*>(out_h + q * kD + 16 * dt + 4 * g) = acc[dt] * inv;
+  }
+}
+
+template <int MPAD, int KPAD>
+__device__ void attend_bf16(AttendLds<BF16, MPAD, KPAD>& S, const uint16_t* __restrict__ Q,
+                            const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                            const uint16_t* __restrict__ Ql, const uint16_t* __restrict__ vlt_hi,
+                            const uint16_t* __restrict__ vlt_lo, const int32_t* __restrict__ idx,
+                            const int32_t* __restrict__ perm, int64_t N, int m, int k, float c2,
+                            float* __restrict__ out, int64_t bh, const TileInfo& ti) {
+  const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
+  const uint16_t* Qh = Q + bh * N * kD;
+  const int32_t* ph = perm + bh * N;
+  float* out_h = out + bh * N * kD;
+  const u32x4 z = {0, 0, 0, 0};
+
+  // wave w handles the 16-query sub-tiles w, w+4, w+8, ... of the item;
+  // the query index runs two sub-tiles ahead and the Q rows one ahead
+  auto qpos = [&](int i) { return ti.qb + 16 * (w + 4 * i) + c16; };
+  auto load_perm = [&](int i) -> int64_t {
+    const int pos = qpos(i);
+    return (pos < ti.qe && pos >= 0 && pos < N) ? clamp_index(ph[pos], N) : -1;
+  };
+  auto load_q = [&](int64_t q, bf16x8 (&qb)[2]) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      qb[s] = as_bf16x8(q >= 0 ? *reinterpret_cast<const u32x4*>(Qh + q * kD + 32 * s + 8 * g) : z);
+  };
+  const int nsub = (ti.qe - ti.qb + 15) / 16;  // sub-tiles in this item
+  int64_t q_cur = load_perm(0);
+  int64_t q_nxt = load_perm(1);
+  bf16x8 qb[2];
+  load_q(q_cur, qb);
+
+  stage_bf16<MPAD, KPAD>(S, K, V, Ql, vlt_hi, vlt_lo, idx + (bh * m + ti.e) * k, N, m, k, bh);
+  __syncthreads();
+
+  for (int i = 0; w + 4 * i < nsub; ++i) {
+    bf16x8 qn[2];
+    load_q(q_nxt, qn);  // next sub-tile's rows (q = -1 loads nothing)
+    const int64_t q_nn = load_perm(i + 2);
+    attend_queries_bf16<MPAD, KPAD>(S, qb, q_cur >= 0, q_cur, m, k, c2, out_h);
+    q_cur = q_nxt;
+    q_nxt = q_nn;
+    qb[0] = qn[0];
+    qb[1] = qn[1];
   }
 }
 
@@ -229,6 +275,7 @@ __device__ void attend_f32(AttendLds<F32, MPAD, KPAD>& S, const float* __restric
                            const TileInfo& ti) {
   using L = AttendLds<F32, MPAD, KPAD>;
   constexpr int NP = MPAD + KPAD;
+  constexpr int NPB = NP / 16;
   const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
   const int32_t* ex = idx + (bh * m + ti.e) * k;
   const f32x4 z = {0, 0, 0, 0};
@@ -250,60 +297,63 @@ __device__ void attend_f32(AttendLds<F32, MPAD, KPAD>& S, const float* __restric
   }
   __syncthreads();
 
-  const int pos = ti.qb + 16 * w + c16;
-  const bool qok = pos < ti.qe && pos >= 0 && pos < N;
-  const int64_t q = qok ? clamp_index(perm[bh * N + pos], N) : 0;
-  float qv[16];
+  const int nsub = (ti.qe - ti.qb + 15) / 16;
+  for (int i = 0; w + 4 * i < nsub; ++i) {
+    const int pos = ti.qb + 16 * (w + 4 * i) + c16;
+    const bool qok = pos < ti.qe && pos >= 0 && pos < N;
+    const int64_t q = qok ? clamp_index(perm[bh * N + pos], N) : 0;
+    float qv[16];
 #pragma unroll
-  for (int s = 0; s < 16; ++s) qv[s] = qok ? Q[(bh * N + q) * kD + 4 * s + g] : 0.f;
-
-  constexpr int NPB = NP / 16;
-  float x[NPB][4];
-  float mx = -INFINITY;
+    for (int s = 0; s < 16; ++s) qv[s] = qok ? Q[(bh * N + q) * kD + 4 * s + g] : 0.f;
+    float x[NPB][4];
+    float mx = -INFINITY;
 #pragma unroll
-  for (int pb = 0; pb < NPB; ++pb) {
-    f32x4 a = {0, 0, 0, 0};
+    for (int pb = 0; pb < NPB; ++pb) {
+      f32x4 a = {0, 0, 0, 0};
 #pragma unroll
-    for (int s = 0; s < 16; ++s) a = mfma_f32(S.pk[(16 * pb + c16) * L::PKST + 4 * s + g], qv[s], a);
+      for (int s = 0; s < 16; ++s)
+        a = mfma_f32(S.pk[(16 * pb + c16) * L::PKST + 4 * s + g], qv[s], a);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int p = 16 * pb + 4 * g + r;
-      const bool valid = (p < MPAD) ? (p < m) : (p - MPAD < k);
-      x[pb][r] = valid ? a[r] * c2 : -INFINITY;
-      mx = fmaxf(mx, x[pb][r]);
+      for (int r = 0; r < 4; ++r) {
+        const int p = 16 * pb + 4 * g + r;
+        const bool valid = (p < MPAD) ? (p < m) : (p - MPAD < k);
+        x[pb][r] = valid ? a[r] * c2 : -INFINITY;
+        mx = fmaxf(mx, x[pb][r]);
+      }
     }
-  }
-  mx = xor_max(mx, 16);
-  mx = xor_max(mx, 32);
-  float lsum = 0.f;
+    mx = xor_max(mx, 16);
+    mx = xor_max(mx, 32);
+    float lsum = 0.f;
 #pragma unroll
-  for (int pb = 0; pb < NPB; ++pb)
+    for (int pb = 0; pb < NPB; ++pb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      x[pb][r] = exp2f(x[pb][r] - mx);
-      lsum += x[pb][r];
-    }
-  lsum = xor_sum(lsum, 16);
-  lsum = xor_sum(lsum, 32);
-  f32x4 acc[4];
+      for (int r = 0; r < 4; ++r) {
+        x[pb][r] = fast_exp2(x[pb][r] - mx);
+        lsum += x[pb][r];
+      }
+    lsum = xor_sum(lsum, 16);
+    lsum = xor_sum(lsum, 32);
+    f32x4 acc[4];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x4{0, 0, 0, 0};
+    for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x4{0, 0, 0, 0};
 #pragma unroll
-  for (int pb = 0; pb < NPB; ++pb)
+    for (int pb = 0; pb < NPB; ++pb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+          acc[dt] =
+              mfma_f32(S.val[(16 * pb + 4 * g + r) * L::VST + 16 * dt + c16], x[pb][r], acc[dt]);
+    if (qok) {
+      const float inv = 1.0f / lsum;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
-        acc[dt] = mfma_f32(S.val[(16 * pb + 4 * g + r) * L::VST + 16 * dt + c16], x[pb][r], acc[dt]);
-  if (qok) {
-    const float inv = 1.0f / lsum;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-      *reinterpret_cast<f32x4*>(out + (bh * N + q) * kD + 16 * dt + 4 * g) = acc[dt] * inv;
+        *reinterpret_cast<f32x4*>(out + (bh * N + q) * kD + 16 * dt + 4 * g) = acc[dt] * inv;
+    }
   }
 }
 
-// grid (tiles, BH), 256 threads
+// grid (work items, BH), 256 threads
 template <class T, int MPAD, int KPAD>
 __global__ __launch_bounds__(256) void k_attend(
     const typename T::elem* __restrict__ Q, const typename T::elem* __restrict__ K,
@@ -311,12 +361,13 @@ __global__ __launch_bounds__(256) void k_attend(
     const float* __restrict__ vl, const uint16_t* __restrict__ vlt_hi,
     const uint16_t* __restrict__ vlt_lo, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ tile_start, int64_t N, int m, int k, float c2,
+    const int32_t* __restrict__ item_start, int tpb, int64_t N, int m, int k, float c2,
     float* __restrict__ out) {
   __shared__ AttendLds<T, MPAD, KPAD> S;
   const int64_t bh = blockIdx.y;
   TileInfo ti;
-  if (!find_tile(tile_start + bh * (m + 1), offsets + bh * (m + 1), m, blockIdx.x, ti)) return;
+  if (!find_item(item_start + bh * (m + 1), offsets + bh * (m + 1), m, tpb, blockIdx.x, ti))
+    return;
   if constexpr (sizeof(typename T::elem) == 2)
     attend_bf16<MPAD, KPAD>(S, Q, K, V, Ql, vlt_hi, vlt_lo, idx, perm, N, m, k, c2, out, bh, ti);
   else
@@ -328,10 +379,11 @@ static hipError_t launch_attend_t(const Shape& s, const void* Q, const void* K, 
                                   const int32_t* idx, const Workspace& ws, float* out,
                                   hipStream_t st) {
   using E = typename T::elem;
-  hipLaunchKernelGGL((k_attend<T, MPAD, KPAD>), dim3(s.attend_tiles, s.BH), dim3(256), 0, st,
+  hipLaunchKernelGGL((k_attend<T, MPAD, KPAD>), dim3(s.attend_items, s.BH), dim3(256), 0, st,
                      static_cast<const E*>(Q), static_cast<const E*>(K), static_cast<const E*>(V),
                      static_cast<const E*>(ws.ql), ws.vl, ws.vlt_hi, ws.vlt_lo, idx, ws.perm,
-                     ws.offsets, ws.tile_start, s.N, s.m, s.k, s.scale * kLog2e, out);
+                     ws.offsets, ws.item_start, s.attend_tpb, s.N, s.m, s.k, s.scale * kLog2e,
+                     out);
   return hipGetLastError();
 }
 

@@ -12,7 +12,7 @@
 //                    query columns), argmax with ties to the lower landmark,
 //                    route_out, and the segment's per-expert counts.
 //   k_bucket_scan    (head): expert totals -> offsets, per-(segment, expert)
-//                    bases, and the first attention tile of each expert.
+//                    bases, and the first attention work item of each expert.
 //   k_bucket_scatter (segment, head), one wave: stable counting-sort scatter;
 //                    a query's rank among equal routes inside a group of 64
 //                    comes from 6 ballots over the route bits.
@@ -161,11 +161,11 @@ __global__ __launch_bounds__(256) void k_route(const typename T::elem* __restric
 // grid (BH), 1024 threads: thread (e = t % 64, part = t / 64) handles expert
 // e over segments [part*nseg/16, (part+1)*nseg/16)
 __global__ __launch_bounds__(1024) void k_bucket_scan(const int32_t* __restrict__ counts, int m,
-                                                     int nseg, int64_t N, int tile,
+                                                     int nseg, int64_t N, int tile, int tpb,
                                                      int32_t* __restrict__ seg_base,
                                                      int32_t* __restrict__ offsets,
                                                      int32_t* __restrict__ offsets_copy,
-                                                     int32_t* __restrict__ tile_start) {
+                                                     int32_t* __restrict__ item_start) {
   __shared__ int psum[16][kMaxM];
   __shared__ int off[kMaxM + 1];
   __shared__ int tst[kMaxM + 1];
@@ -184,7 +184,8 @@ __global__ __launch_bounds__(1024) void k_bucket_scan(const int32_t* __restrict_
     if (e < m)
       for (int p = 0; p < 16; ++p) total += psum[p][e];
     // exclusive scans over experts of totals and of tile counts (one wave)
-    int ex = total, tl = (total + tile - 1) / tile;
+    const int tiles_e = (total + tile - 1) / tile;
+    int ex = total, tl = (tiles_e + tpb - 1) / tpb;  // work items of expert e
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
       const int a = static_cast<int>(lane_read(static_cast<uint32_t>(ex), t >= d ? t - d : t));
@@ -206,7 +207,7 @@ __global__ __launch_bounds__(1024) void k_bucket_scan(const int32_t* __restrict_
   if (t <= m) {
     offsets[bh * (m + 1) + t] = off[t];
     if (offsets_copy) offsets_copy[bh * (m + 1) + t] = off[t];
-    tile_start[bh * (m + 1) + t] = tst[t];
+    item_start[bh * (m + 1) + t] = tst[t];
   }
   if (e < m) {
     int run = off[e];
@@ -275,7 +276,8 @@ hipError_t launch_route(const Shape& s, const void* Q, const Workspace& ws, int3
 hipError_t launch_bucket(const Shape& s, const int32_t* route, const Workspace& ws,
                          int32_t* offsets_copy, int32_t* perm_copy, hipStream_t st) {
   hipLaunchKernelGGL(k_bucket_scan, dim3(s.BH), dim3(1024), 0, st, ws.counts, s.m, s.nseg, s.N,
-                     kAttendTile, ws.seg_base, ws.offsets, offsets_copy, ws.tile_start);
+                     kAttendTile, s.attend_tpb, ws.seg_base, ws.offsets, offsets_copy,
+                     ws.item_start);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_bucket_scatter, dim3(s.nseg, s.BH), dim3(64), 0, st, route, s.m, s.nseg,

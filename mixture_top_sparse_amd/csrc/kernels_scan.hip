@@ -207,25 +207,28 @@ struct ScanTraits<F32> {
 // the scan kernel
 // ---------------------------------------------------------------------------
 
+// Block: 256 threads stage each 64-key tile (double-buffered LDS, two tiles
+// of global loads in flight); waves 0..NW-1 each own 16 landmarks.
 template <class T, int NW>
-__global__ __launch_bounds__(NW * 64) void k_scan(
+__global__ __launch_bounds__(256) void k_scan(
     const typename T::elem* __restrict__ K, const typename T::elem* __restrict__ V,
     const typename T::elem* __restrict__ Ql, const float* __restrict__ theta, int64_t N, int m,
     int k, int chunk, int splits, float c2, uint64_t* __restrict__ part_keys,
     float* __restrict__ part_stats, float* __restrict__ part_acc) {
   using TR = ScanTraits<T>;
   using E = typename T::elem;
-  constexpr int NT = NW * 64;
+  constexpr int NT = 256;
   constexpr int MROWS = NW * 16;
-  __shared__ __attribute__((aligned(16))) E klds[64 * TR::KST];
-  __shared__ __attribute__((aligned(16))) E vlds[64 * TR::VST];
+  __shared__ __attribute__((aligned(16))) E klds[2][64 * TR::KST];
+  __shared__ __attribute__((aligned(16))) E vlds[2][64 * TR::VST];
   __shared__ uint64_t cand[MROWS][kTopCap];
 
   const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
+  const bool computes = w < NW;
   const int split = blockIdx.x;
   const int64_t bh = blockIdx.y;
   const int lm = w * 16 + c16;
-  const bool lm_ok = lm < m;
+  const bool lm_ok = computes && lm < m;
   const int64_t kbeg = static_cast<int64_t>(split) * chunk;
   const int64_t kend = (kbeg + chunk < N) ? kbeg + chunk : N;
   const int ntiles = static_cast<int>((kend - kbeg + kTileKeys - 1) / kTileKeys);
@@ -246,7 +249,7 @@ __global__ __launch_bounds__(NW * 64) void k_scan(
   int cnt = 0;
 
   // merge landmark slot L's candidate buffer into its top list (whole wave)
-  auto merge_slot = [&](int L) {
+  auto merge_slot = [&](int L) __attribute__((always_inline)) {
     const int cL = static_cast<int>(uniform_read(static_cast<uint32_t>(cnt), L));
     uint64_t c = (l < cL) ? cand[w * 16 + L][l] : 0ull;
     c = wave_sort_desc(c);
@@ -258,89 +261,109 @@ __global__ __launch_bounds__(NW * 64) void k_scan(
     }
   };
 
-  typename TR::template Tile<NT> pf;
-  TR::template load_tile<NT>(pf, Kh, Vh, kbeg, kend, tid);
-
-  for (int it = 0; it < ntiles; ++it) {
-    __syncthreads();
-    TR::template store_tile<NT>(pf, klds, vlds, tid);
-    __syncthreads();
-    const int64_t t0 = kbeg + static_cast<int64_t>(it) * kTileKeys;
-    if (it + 1 < ntiles) TR::template load_tile<NT>(pf, Kh, Vh, t0 + kTileKeys, kend, tid);
-
+  auto compute_tile = [&](const E* kl, const E* vl, int64_t t0) __attribute__((always_inline)) {
     float sc[4][4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const f32x4 a = TR::score(klds, kb, q, c16, g);
+      const f32x4 a = TR::score(kl, kb, q, c16, g);
 #pragma unroll
       for (int r = 0; r < 4; ++r) sc[kb][r] = a[r];
     }
-
-    // ---- streaming top-k ----
-    uint32_t passbits = 0;
-    int npass = 0;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool ok = lm_ok && (t0 + 16 * kb + 4 * g + r < kend) && (sc[kb][r] > th);
-        passbits |= static_cast<uint32_t>(ok) << (4 * kb + r);
-        npass += ok;
-      }
-    const int n0 = static_cast<int>(lane_read(static_cast<uint32_t>(npass), c16));
-    const int n1 = static_cast<int>(lane_read(static_cast<uint32_t>(npass), 16 + c16));
-    const int n2 = static_cast<int>(lane_read(static_cast<uint32_t>(npass), 32 + c16));
-    const int n3 = static_cast<int>(lane_read(static_cast<uint32_t>(npass), 48 + c16));
-    const int tot = n0 + n1 + n2 + n3;
-    const int pre = (g > 0 ? n0 : 0) + (g > 1 ? n1 : 0) + (g > 2 ? n2 : 0);
-    const uint32_t need = static_cast<uint32_t>(ballot(cnt + tot > kTopCap)) & 0xFFFFu;
-    if (need) {
-#pragma unroll
-      for (int L = 0; L < 16; ++L)
-        if ((need >> L) & 1u) merge_slot(L);
-    }
-    if (passbits) {
-      int pos = cnt + pre;
+    if (t0 + kTileKeys > kend) {  // ragged last tile: drop keys past the chunk
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if ((passbits >> (4 * kb + r)) & 1u)
-            cand[lm][pos++] = make_key(sc[kb][r], static_cast<uint32_t>(t0 + 16 * kb + 4 * g + r));
+          if (t0 + 16 * kb + 4 * g + r >= kend) sc[kb][r] = -INFINITY;
     }
-    cnt += tot;
-
-    // ---- online softmax and P.V ----
-    float x[4][4];
-    float mx = -INFINITY;
+    float smax = sc[0][0];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        x[kb][r] = (t0 + 16 * kb + 4 * g + r < kend) ? sc[kb][r] * c2 : -INFINITY;
-        mx = fmaxf(mx, x[kb][r]);
-      }
-    mx = xor_max(mx, 16);
-    mx = xor_max(mx, 32);
-    const float Mn = fmaxf(M, mx);
-    const float alpha = exp2f(M - Mn);
-    Lsum *= alpha;
+      for (int r = 0; r < 4; ++r) smax = fmaxf(smax, sc[kb][r]);
+
+    // ---- streaming top-k: only when some score beats its landmark's k-th best
+    if (ballot(lm_ok && smax > th)) {
+      uint32_t passbits = 0;
+      int npass = 0;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool ok = lm_ok && (sc[kb][r] > th);
+          passbits |= static_cast<uint32_t>(ok) << (4 * kb + r);
+          npass += ok;
+        }
+      const int n0 = static_cast<int>(lane_read(static_cast<uint32_t>(npass), c16));
+      const int n1 = static_cast<int>(lane_read(static_cast<uint32_t>(npass), 16 + c16));
+      const int n2 = static_cast<int>(lane_read(static_cast<uint32_t>(npass), 32 + c16));
+      const int n3 = static_cast<int>(lane_read(static_cast<uint32_t>(npass), 48 + c16));
+      const int tot = n0 + n1 + n2 + n3;
+      const int pre = (g > 0 ? n0 : 0) + (g > 1 ? n1 : 0) + (g > 2 ? n2 : 0);
+      const uint32_t need = static_cast<uint32_t>(ballot(cnt + tot > kTopCap)) & 0xFFFFu;
+      if (need) {
+#pragma unroll
+        for (int L = 0; L < 16; ++L)
+          if ((need >> L) & 1u) merge_slot(L);
+      }
+      if (passbits) {
+        int pos = cnt + pre;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if ((passbits >> (4 * kb + r)) & 1u)
+              cand[lm][pos++] =
+                  make_key(sc[kb][r], static_cast<uint32_t>(t0 + 16 * kb + 4 * g + r));
+      }
+      cnt += tot;
+    }
+
+    // ---- online softmax (log2 domain, lazy rescale) and P.V ----
+    float mx = xor_max(smax, 16);
+    mx = xor_max(mx, 32) * c2;
+    if (ballot(mx > M)) {
+      const float Mn = fmaxf(M, mx);
+      const float alpha = fast_exp2(M - Mn);
+      Lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
+      M = Mn;
+    }
     float p[4][4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p[kb][r] = exp2f(x[kb][r] - Mn);
+        p[kb][r] = fast_exp2(fmaf(sc[kb][r], c2, -M));
         Lsum += p[kb][r];
       }
-    M = Mn;
-    TR::pv(acc, vlds, p, c16, g);
+    TR::pv(acc, vl, p, c16, g);
+  };
+
+  // prologue: tile 0 into LDS buffer 0, tiles 1 and 2 in flight
+  typename TR::template Tile<NT> ra, rb;
+  TR::template load_tile<NT>(ra, Kh, Vh, kbeg, kend, tid);
+  TR::template store_tile<NT>(ra, klds[0], vlds[0], tid);
+  if (ntiles > 1) TR::template load_tile<NT>(ra, Kh, Vh, kbeg + kTileKeys, kend, tid);
+  if (ntiles > 2) TR::template load_tile<NT>(rb, Kh, Vh, kbeg + 2 * kTileKeys, kend, tid);
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; it += 2) {
+    const int64_t t0 = kbeg + static_cast<int64_t>(it) * kTileKeys;
+    if (computes) compute_tile(klds[0], vlds[0], t0);
+    if (it + 1 < ntiles) TR::template store_tile<NT>(ra, klds[1], vlds[1], tid);
+    if (it + 3 < ntiles) TR::template load_tile<NT>(ra, Kh, Vh, t0 + 3 * kTileKeys, kend, tid);
+    __syncthreads();
+    if (it + 1 >= ntiles) break;
+    if (computes) compute_tile(klds[1], vlds[1], t0 + kTileKeys);
+    if (it + 2 < ntiles) TR::template store_tile<NT>(rb, klds[0], vlds[0], tid);
+    if (it + 4 < ntiles) TR::template load_tile<NT>(rb, Kh, Vh, t0 + 4 * kTileKeys, kend, tid);
+    __syncthreads();
   }
+  if (!computes) return;
 
   // flush the candidate buffers
-  __syncthreads();
   const uint32_t need = static_cast<uint32_t>(ballot(cnt > 0)) & 0xFFFFu;
   if (need) {
 #pragma unroll
@@ -401,7 +424,7 @@ __global__ __launch_bounds__(256) void k_merge(
     const int64_t b = (bh * splits + s) * mrows + lm;
     const float Ms = part_stats[b * 2], Ls = part_stats[b * 2 + 1], as = part_acc[b * kD + l];
     const float Mn = fmaxf(Mw, Ms);
-    const float f0 = exp2f(Mw - Mn), f1 = exp2f(Ms - Mn);
+    const float f0 = fast_exp2(Mw - Mn), f1 = fast_exp2(Ms - Mn);
     Lw = Lw * f0 + Ls * f1;
     aw = aw * f0 + as * f1;
     Mw = Mn;
@@ -428,7 +451,7 @@ __global__ __launch_bounds__(256) void k_merge(
   float Lt = 0.f, at = 0.f;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    const float f = exp2f(sM[v] - Mt);
+    const float f = fast_exp2(sM[v] - Mt);
     Lt += sL[v] * f;
     at += sacc[v][l] * f;
   }
@@ -449,7 +472,7 @@ static hipError_t launch_scan_t(const Shape& s, const void* K, const void* V, co
                                 hipStream_t st) {
   using E = typename T::elem;
   const float c2 = s.scale * kLog2e;
-  hipLaunchKernelGGL((k_scan<T, NW>), dim3(s.scan_splits, s.BH), dim3(NW * 64), 0, st,
+  hipLaunchKernelGGL((k_scan<T, NW>), dim3(s.scan_splits, s.BH), dim3(256), 0, st,
                      static_cast<const E*>(K), static_cast<const E*>(V),
                      static_cast<const E*>(ws.ql), ws.theta, s.N, s.m, s.k, s.scan_chunk,
                      s.scan_splits, c2, ws.part_keys, ws.part_stats, ws.part_acc);

@@ -194,7 +194,12 @@ void derive(Shape& s, int cus) {
   s.scan_splits = static_cast<int>(cdiv(s.N, chunk));
   s.pool_splits = static_cast<int>(cdiv(max_window(s), kPoolChunk));
   s.nseg = static_cast<int>(cdiv(s.N, kRouteSeg));
-  s.attend_tiles = static_cast<int>(cdiv(s.N, kAttendTile) + s.m);
+  // expert attention: work items of up to 16 tiles, keeping >= 4 items per CU
+  const int64_t tiles = cdiv(s.N, kAttendTile);
+  int64_t tpb = (tiles * s.BH) / (4 * static_cast<int64_t>(cus));
+  tpb = tpb < 1 ? 1 : (tpb > 16 ? 16 : tpb);
+  s.attend_tpb = static_cast<int>(tpb);
+  s.attend_items = static_cast<int>(cdiv(tiles + s.m, tpb) + s.m);
 }
 
 }  // namespace
@@ -224,7 +229,7 @@ size_t plan_workspace(const Shape& s, Workspace* ws, char* base) {
   ws->counts = reinterpret_cast<int32_t*>(take(BH * s.nseg * s.m * 4));
   ws->seg_base = reinterpret_cast<int32_t*>(take(BH * s.nseg * s.m * 4));
   ws->offsets = reinterpret_cast<int32_t*>(take(BH * (s.m + 1) * 4));
-  ws->tile_start = reinterpret_cast<int32_t*>(take(BH * (s.m + 1) * 4));
+  ws->item_start = reinterpret_cast<int32_t*>(take(BH * (s.m + 1) * 4));
   ws->perm = reinterpret_cast<int32_t*>(take(BH * s.N * 4));
   return off;
 }

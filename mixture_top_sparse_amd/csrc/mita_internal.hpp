@@ -31,7 +31,8 @@ struct Shape {
   int scan_splits = 0;
   int pool_splits = 0; // partial sums per landmark window
   int nseg = 0;        // routing segments per head
-  int attend_tiles = 0;// upper bound of expert tiles per head
+  int attend_tpb = 0;   // 64-query tiles per expert-attention work item
+  int attend_items = 0; // upper bound of work items per head
 };
 
 // Work space carved from one stream-ordered allocation.
@@ -48,7 +49,7 @@ struct Workspace {
   int32_t* counts = nullptr;     // [BH][nseg][m] routed queries per segment and expert
   int32_t* seg_base = nullptr;   // [BH][nseg][m] first perm slot of each (segment, expert)
   int32_t* offsets = nullptr;    // [BH][m+1]
-  int32_t* tile_start = nullptr; // [BH][m+1] first attention tile of each expert
+  int32_t* item_start = nullptr; // [BH][m+1] first attention work item of each expert
   int32_t* perm = nullptr;       // [BH][N]
 };
 

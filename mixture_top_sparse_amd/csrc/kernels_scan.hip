@@ -117,6 +117,19 @@ struct ScanTraits<BF16> {
     return acc;
   }
 
+  // the same block straight from global memory (key row `row` of this lane)
+  __device__ static f32x4 score_global(const E* Kh, int64_t row, int64_t N, const QReg& q, int g) {
+    f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const u32x4 z = {0, 0, 0, 0};
+      const bf16x8 a = as_bf16x8(
+          row < N ? *reinterpret_cast<const u32x4*>(Kh + row * kD + 32 * s + 8 * g) : z);
+      acc = mfma_bf16(a, q.v[s], acc);
+    }
+    return acc;
+  }
+
   // O^T[d][lm] += V^T[d][keys] P^T[keys][lm] for the tile's 64 keys
   __device__ static void pv(f32x4 (&acc)[4], const E* vlds, const float (&p)[4][4], int c16, int g) {
 #pragma unroll
@@ -189,6 +202,13 @@ struct ScanTraits<F32> {
     f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
     for (int s = 0; s < 16; ++s) acc = mfma_f32(klds[(16 * kb + c16) * KST + 4 * s + g], q.v[s], acc);
+    return acc;
+  }
+
+  __device__ static f32x4 score_global(const E* Kh, int64_t row, int64_t N, const QReg& q, int g) {
+    f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < 16; ++s) acc = mfma_f32(row < N ? Kh[row * kD + 4 * s + g] : 0.f, q.v[s], acc);
     return acc;
   }
 
@@ -386,6 +406,86 @@ __global__ __launch_bounds__(256) void k_scan(
 }
 
 // ---------------------------------------------------------------------------
+// top-k pre-threshold from a key sample
+// ---------------------------------------------------------------------------
+//
+// For each landmark, the k-th largest of G group maxima (G sample tiles of 64
+// keys spread evenly over N) is the key of some real key t, and the k keys
+// behind those maxima are distinct, so the global k-th best key is >= it.
+// The scan may therefore drop every score below that sample key's score
+// without changing the exact top-k.
+
+// grid (G / kThetaTilesPerBlock, BH), 256 threads; wave w: landmarks 16w..16w+15
+template <class T>
+__global__ __launch_bounds__(256) void k_theta_sample(const typename T::elem* __restrict__ K,
+                                                     const typename T::elem* __restrict__ Ql,
+                                                     int64_t N, int m, int groups,
+                                                     uint64_t* __restrict__ gmax) {
+  using TR = ScanTraits<T>;
+  using E = typename T::elem;
+  const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
+  const int64_t bh = blockIdx.y;
+  const int lm = w * 16 + c16;
+  const bool lm_ok = lm < m;
+  if (w * 16 >= m) return;  // whole wave beyond the landmarks
+  typename TR::QReg q;
+  TR::load_q(q, Ql + (bh * m + (lm_ok ? lm : 0)) * kD, lm_ok, g);
+  const int64_t ntiles = (N + kTileKeys - 1) / kTileKeys;
+  const E* Kh = K + bh * N * kD;
+  for (int j = 0; j < kThetaTilesPerBlock; ++j) {
+    const int gi = blockIdx.x * kThetaTilesPerBlock + j;
+    const int64_t t0 = ((static_cast<int64_t>(gi) * ntiles) / groups) * kTileKeys;
+    uint64_t best = 0;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const f32x4 a = TR::score_global(Kh, t0 + 16 * kb + c16, N, q, g);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t t = t0 + 16 * kb + 4 * g + r;
+        if (t < N) {
+          const uint64_t key = make_key(a[r], static_cast<uint32_t>(t));
+          best = key > best ? key : best;
+        }
+      }
+    }
+#pragma unroll
+    for (int mask = 16; mask <= 32; mask <<= 1) {
+      const uint64_t o = lane_read(best, l ^ mask);
+      best = o > best ? o : best;
+    }
+    if (g == 0 && lm_ok) gmax[(bh * m + lm) * groups + gi] = best;
+  }
+}
+
+// grid (m, BH), 256 threads: theta[bh][lm] = score of the k-th largest group
+// maximum, lowered by one ulp so that the scan's strict test (s > theta)
+// keeps every score equal to it; -inf when fewer than k maxima exist.
+__global__ __launch_bounds__(256) void k_theta_select(const uint64_t* __restrict__ gmax, int m,
+                                                     int k, int groups, int mrows,
+                                                     float* __restrict__ theta) {
+  __shared__ uint64_t tops[4][64];
+  const int l = lane_id(), w = wave_id(), lm = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const uint64_t* G = gmax + (bh * m + lm) * groups;
+  uint64_t top = 0;
+  for (int c = w; c * 64 < groups; c += 4) {
+    const int i = c * 64 + l;
+    uint64_t v = i < groups ? G[i] : 0ull;
+    v = wave_sort_desc(v);
+    top = wave_merge_top(top, v);
+  }
+  tops[w][l] = top;
+  __syncthreads();
+  if (w != 0) return;
+  uint64_t t = tops[0][l];
+#pragma unroll
+  for (int v = 1; v < 4; ++v) t = wave_merge_top(t, tops[v][l]);
+  const uint64_t kth = uniform_read(t, k - 1);
+  if (l == 0)
+    theta[bh * mrows + lm] = kth != 0ull ? nextafterf(key_score(kth), -INFINITY) : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
 // merge of the per-split partials
 // ---------------------------------------------------------------------------
 
@@ -489,8 +589,27 @@ static hipError_t launch_scan_w(const Shape& s, const void* K, const void* V, co
   }
 }
 
+template <class T>
+static hipError_t launch_theta_t(const Shape& s, const void* K, const Workspace& ws,
+                                 hipStream_t st) {
+  using E = typename T::elem;
+  hipLaunchKernelGGL(k_theta_sample<T>, dim3(s.theta_groups / kThetaTilesPerBlock, s.BH), dim3(256),
+                     0, st, static_cast<const E*>(K), static_cast<const E*>(ws.ql), s.N, s.m,
+                     s.theta_groups, ws.gmax);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_theta_select, dim3(s.m, s.BH), dim3(256), 0, st, ws.gmax, s.m, s.k,
+                     s.theta_groups, s.mrows, ws.theta);
+  return hipGetLastError();
+}
+
 hipError_t launch_scan(const Shape& s, const void* K, const void* V, const Workspace& ws,
                        hipStream_t st) {
+  if (s.theta_groups > 0) {
+    const hipError_t e = s.dtype == 1 ? launch_theta_t<BF16>(s, K, ws, st)
+                                      : launch_theta_t<F32>(s, K, ws, st);
+    if (e != hipSuccess) return e;
+  }
   return s.dtype == 1 ? launch_scan_w<BF16>(s, K, V, ws, st) : launch_scan_w<F32>(s, K, V, ws, st);
 }
 

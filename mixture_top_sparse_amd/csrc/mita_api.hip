@@ -193,6 +193,13 @@ void derive(Shape& s, int cus) {
   s.scan_chunk = static_cast<int>(chunk);
   s.scan_splits = static_cast<int>(cdiv(s.N, chunk));
   s.pool_splits = static_cast<int>(cdiv(max_window(s), kPoolChunk));
+  // top-k pre-threshold: sample up to a quarter of the key tiles (at most
+  // 1024 per head), only when there are at least max(k, 64) of them
+  const int64_t ktiles = cdiv(s.N, kTileKeys);
+  int64_t groups = ktiles / 4;
+  if (groups > 1024) groups = 1024;
+  groups = groups / kThetaTilesPerBlock * kThetaTilesPerBlock;
+  s.theta_groups = (groups >= 64 && groups >= s.k) ? static_cast<int>(groups) : 0;
   s.nseg = static_cast<int>(cdiv(s.N, kRouteSeg));
   // expert attention: work items of up to 16 tiles, keeping >= 4 items per CU
   const int64_t tiles = cdiv(s.N, kAttendTile);
@@ -214,7 +221,13 @@ size_t plan_workspace(const Shape& s, Workspace* ws, char* base) {
   const size_t BH = static_cast<size_t>(s.BH), es = s.dtype == MITA_BF16 ? 2 : 4;
   ws->pool_part = reinterpret_cast<double*>(take(BH * s.m * s.pool_splits * kD * sizeof(double)));
   ws->ql = take(BH * s.m * kD * es);
-  ws->theta = nullptr;
+  if (s.theta_groups > 0) {
+    ws->gmax = reinterpret_cast<uint64_t*>(take(BH * s.m * s.theta_groups * sizeof(uint64_t)));
+    ws->theta = reinterpret_cast<float*>(take(BH * s.mrows * sizeof(float)));
+  } else {
+    ws->gmax = nullptr;
+    ws->theta = nullptr;
+  }
   const size_t parts = BH * s.scan_splits * s.mrows;
   ws->part_keys = reinterpret_cast<uint64_t*>(take(parts * kTopCap * sizeof(uint64_t)));
   ws->part_stats = reinterpret_cast<float*>(take(parts * 2 * sizeof(float)));

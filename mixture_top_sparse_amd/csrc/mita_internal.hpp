@@ -15,6 +15,7 @@ constexpr int kTileKeys = 64;    // keys per landmark-scan tile
 constexpr int kRouteSeg = 1024;  // queries per routing/bucketing segment
 constexpr int kAttendTile = 64;  // queries per expert-attention tile
 constexpr int kPoolChunk = 2048; // tokens per pooling partial sum
+constexpr int kThetaTilesPerBlock = 4;  // sample tiles per top-k pre-threshold block
 
 struct Shape {
   int64_t B = 0, H = 0, BH = 0, N = 0;
@@ -30,6 +31,7 @@ struct Shape {
   int scan_chunk = 0;  // keys per landmark-scan block
   int scan_splits = 0;
   int pool_splits = 0; // partial sums per landmark window
+  int theta_groups = 0;// sample tiles for the top-k pre-threshold (0: off)
   int nseg = 0;        // routing segments per head
   int attend_tpb = 0;   // 64-query tiles per expert-attention work item
   int attend_items = 0; // upper bound of work items per head
@@ -39,7 +41,8 @@ struct Shape {
 struct Workspace {
   double* pool_part = nullptr;   // [BH][m][pool_splits][64] fp64 partial window sums
   void* ql = nullptr;            // [BH][m][64] landmark queries (input type)
-  float* theta = nullptr;        // [BH][mrows] top-k pre-filter scores (unused: -inf)
+  uint64_t* gmax = nullptr;      // [BH][m][theta_groups] per-sample-tile maximum keys
+  float* theta = nullptr;        // [BH][mrows] top-k pre-threshold (nullptr: off)
   uint64_t* part_keys = nullptr; // [BH][splits][mrows][64] per-split top lists
   float* part_stats = nullptr;   // [BH][splits][mrows][2] (max in log2 units, sum)
   float* part_acc = nullptr;     // [BH][splits][mrows][64] unnormalised P.V

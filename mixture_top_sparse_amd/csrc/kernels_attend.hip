@@ -13,7 +13,7 @@
 // 64 queries reuse it.  Queries are gathered in expert order (perm) straight
 // into MFMA operand registers; output rows are scattered back.
 //   logits^T = [Ql; K_e] Q_tile^T   (pair rows x query columns, MFMA)
-//   out^T    = [Vl; V_e]^T P^T       (MFMA; P and Vl as bf16 hi + lo parts)
+//   out^T    = [Vl; V_e]^T P^T       (fp16 MFMA on 2^-s scaled values)
 // Every per-query quantity (max, sum, rescale) stays in the 4 lanes that hold
 // that query's column.
 //
@@ -29,21 +29,22 @@ struct AttendLds;
 
 template <int MPAD, int KPAD>
 struct AttendLds<BF16, MPAD, KPAD> {
-  static constexpr int PKST = 72;        // pair-key rows (elements)
-  static constexpr int VCST = MPAD + 4;  // compressed Vl^T rows
-  static constexpr int VRST = KPAD + 4;  // raw V^T rows
-  uint16_t pk[(MPAD + KPAD) * PKST];
-  uint16_t vch[kD * VCST];
-  uint16_t vcl[kD * VCST];
-  uint16_t vr[kD * VRST];
+  static constexpr int PKST = 72;        // pair-key rows (bf16 elements)
+  static constexpr int VCST = MPAD + 4;  // compressed Vl^T rows (fp16)
+  static constexpr int VRST = KPAD + 4;  // raw V^T rows (fp16)
+  alignas(16) uint16_t pk[(MPAD + KPAD) * PKST];
+  alignas(16) uint16_t vc[kD * VCST];  // fp16 2^-s * Vl^T
+  alignas(16) uint16_t vr[kD * VRST];  // fp16 2^-s * V^T of the expert's rows
+  alignas(16) int32_t perm[kAttendTile * kAttendMaxTpb];  // the work item's query indices
+  uint32_t vmax;            // bits of the largest |value| staged (>= 0)
 };
 
 template <int MPAD, int KPAD>
 struct AttendLds<F32, MPAD, KPAD> {
   static constexpr int PKST = 68;
   static constexpr int VST = 68;
-  float pk[(MPAD + KPAD) * PKST];
-  float val[(MPAD + KPAD) * VST];
+  alignas(16) float pk[(MPAD + KPAD) * PKST];
+  alignas(16) float val[(MPAD + KPAD) * VST];
 };
 
 struct TileInfo {
@@ -73,60 +74,114 @@ __device__ __forceinline__ int64_t clamp_index(int64_t v, int64_t n) {
 }
 
 // ---- bf16 ----------------------------------------------------------------
+//
+// Logits run on bf16 MFMA (Q, Ql and K are exact bf16).  P.V runs on fp16
+// MFMA: P in [0, 1] rounds to fp16 with relative error <= 2^-11; the values
+// are scaled by 2^-s (s >= 0 chosen from the largest |value| of the item, so
+// that every scaled value stays below 2^15) and then convert to fp16 — exactly
+// for the raw bf16 values, with relative error <= 2^-11 for the fp32 landmark
+// values (convex combinations of V rows, so that error is <= 2^-11 max|V|).
+// The output multiplies the 2^s back.
 
+// Stage the expert of this work item; returns the value scale exponent s.
 template <int MPAD, int KPAD>
-__device__ void stage_bf16(AttendLds<BF16, MPAD, KPAD>& S, const uint16_t* __restrict__ K,
-                           const uint16_t* __restrict__ V, const uint16_t* __restrict__ Ql,
-                           const uint16_t* __restrict__ vlt_hi, const uint16_t* __restrict__ vlt_lo,
-                           const int32_t* __restrict__ ex, int64_t N, int m, int k, int64_t bh) {
+__device__ int stage_bf16(AttendLds<BF16, MPAD, KPAD>& S, const uint16_t* __restrict__ K,
+                          const uint16_t* __restrict__ V, const uint16_t* __restrict__ Ql,
+                          const float* __restrict__ vl, const int32_t* __restrict__ ex, int64_t N,
+                          int m, int k, int64_t bh) {
   using L = AttendLds<BF16, MPAD, KPAD>;
   constexpr int NP = MPAD + KPAD;
   const int tid = threadIdx.x;
   const u32x4 z = {0, 0, 0, 0};
+  if (tid == 0) S.vmax = 0u;
+  __syncthreads();
+
+  // raw values: rows 2rp, 2rp+1 of the expert, 8 features from 8*col
+  const bool vr_ok = tid < (KPAD / 2) * 8;
+  const int rp = tid >> 3, col = tid & 7;
+  u32x4 va = z, vb = z;
+  uint32_t mbits = 0;  // largest |bf16| bit pattern seen
+  if (vr_ok) {
+    if (2 * rp < k)
+      va = *reinterpret_cast<const u32x4*>(V + (bh * N + clamp_index(ex[2 * rp], N)) * kD + col * 8);
+    if (2 * rp + 1 < k)
+      vb = *reinterpret_cast<const u32x4*>(V + (bh * N + clamp_index(ex[2 * rp + 1], N)) * kD +
+                                           col * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      mbits = max(mbits, max(va[i] & 0x7FFFu, (va[i] >> 16) & 0x7FFFu));
+      mbits = max(mbits, max(vb[i] & 0x7FFFu, (vb[i] >> 16) & 0x7FFFu));
+    }
+  }
+  float vmax = __uint_as_float(mbits << 16);
+  // landmark values: rows 2lp, 2lp+1, 8 features from 8*dc
+  constexpr int LP = MPAD / 2;
+  const bool vl_ok = tid < LP * 8;
+  const int lp = tid % LP, dc = tid / LP;
+  float la[8], lb[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) la[i] = lb[i] = 0.f;
+  if (vl_ok) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 2 * lp + h;
+      if (row < m) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(vl + (bh * m + row) * kD + dc * 8);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(vl + (bh * m + row) * kD + dc * 8 + 4);
+        float* dst = h ? lb : la;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          dst[i] = a[i];
+          dst[4 + i] = b[i];
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vmax = fmaxf(vmax, fmaxf(fabsf(la[i]), fabsf(lb[i])));
+  }
+  atomicMax(&S.vmax, __float_as_uint(vmax));
+
   // pair keys: Ql rows then the expert's K rows (zero rows for padding)
   for (int c = tid; c < NP * 8; c += 256) {
-    const int row = c >> 3, col = c & 7;
+    const int row = c >> 3, cc = c & 7;
     u32x4 v = z;
     if (row < MPAD) {
-      if (row < m) v = *reinterpret_cast<const u32x4*>(Ql + (bh * m + row) * kD + col * 8);
+      if (row < m) v = *reinterpret_cast<const u32x4*>(Ql + (bh * m + row) * kD + cc * 8);
     } else if (row - MPAD < k) {
       const int64_t t = clamp_index(ex[row - MPAD], N);
-      v = *reinterpret_cast<const u32x4*>(K + (bh * N + t) * kD + col * 8);
+      v = *reinterpret_cast<const u32x4*>(K + (bh * N + t) * kD + cc * 8);
     }
-    *reinterpret_cast<u32x4*>(S.pk + row * L::PKST + col * 8) = v;
+    *reinterpret_cast<u32x4*>(S.pk + row * L::PKST + cc * 8) = v;
   }
-  // compressed values, already transposed and split (rows d, columns pairs)
-  for (int c = tid; c < kD * (MPAD / 8); c += 256) {
-    const int d = c / (MPAD / 8), col = c % (MPAD / 8);
-    *reinterpret_cast<u32x4*>(S.vch + d * L::VCST + col * 8) =
-        *reinterpret_cast<const u32x4*>(vlt_hi + (bh * kD + d) * MPAD + col * 8);
-    *reinterpret_cast<u32x4*>(S.vcl + d * L::VCST + col * 8) =
-        *reinterpret_cast<const u32x4*>(vlt_lo + (bh * kD + d) * MPAD + col * 8);
-  }
-  // raw values transposed: V^T[d][pair], two gathered rows per thread
-  for (int c = tid; c < (KPAD / 2) * 8; c += 256) {
-    const int rp = c >> 3, col = c & 7;
-    u32x4 a = z, b = z;
-    if (2 * rp < k)
-      a = *reinterpret_cast<const u32x4*>(V + (bh * N + clamp_index(ex[2 * rp], N)) * kD + col * 8);
-    if (2 * rp + 1 < k)
-      b = *reinterpret_cast<const u32x4*>(V + (bh * N + clamp_index(ex[2 * rp + 1], N)) * kD +
-                                          col * 8);
+  __syncthreads();
+
+  const int e = static_cast<int>((S.vmax >> 23) & 0xFF) - 127;
+  const int sh = e > 14 ? e - 14 : 0;  // 2^-sh * max|value| < 2^15
+  const float sc = exp2i(-sh);
+  if (vr_ok) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint32_t wa = a[i >> 1], wb = b[i >> 1];
-      const uint32_t word =
-          (i & 1) ? ((wa >> 16) | (wb & 0xFFFF0000u)) : ((wa & 0xFFFFu) | (wb << 16));
-      *reinterpret_cast<uint32_t*>(S.vr + (col * 8 + i) * L::VRST + 2 * rp) = word;
+      const uint32_t wa = va[i >> 1], wb = vb[i >> 1];
+      const float a = __uint_as_float((i & 1) ? (wa & 0xFFFF0000u) : (wa << 16));
+      const float b = __uint_as_float((i & 1) ? (wb & 0xFFFF0000u) : (wb << 16));
+      *reinterpret_cast<uint32_t*>(S.vr + (col * 8 + i) * L::VRST + 2 * rp) = pack_f16(a * sc, b * sc);
     }
   }
+  if (vl_ok) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      *reinterpret_cast<uint32_t*>(S.vc + (dc * 8 + i) * L::VCST + 2 * lp) =
+          pack_f16(la[i] * sc, lb[i] * sc);
+    }
+  }
+  return sh;
 }
 
 // 16 queries of one wave (lane column c16 = query) against the staged expert
-template <int MPAD, int KPAD>
+template <int MPAD, int KPAD, bool FULL>
 __device__ __forceinline__ void attend_queries_bf16(const AttendLds<BF16, MPAD, KPAD>& S,
                                                     const bf16x8 (&qb)[2], bool qok, int64_t q,
-                                                    int m, int k, float c2,
+                                                    int m, int k, float c2, float oscale,
                                                     float* __restrict__ out_h) {
   using L = AttendLds<BF16, MPAD, KPAD>;
   constexpr int NPB = (MPAD + KPAD) / 16;
@@ -144,9 +199,13 @@ __device__ __forceinline__ void attend_queries_bf16(const AttendLds<BF16, MPAD, 
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int p = 16 * pb + 4 * g + r;
-      const bool valid = (p < MPAD) ? (p < m) : (p - MPAD < k);
-      x[pb][r] = valid ? a[r] : -INFINITY;
+      if constexpr (FULL) {
+        x[pb][r] = a[r];
+      } else {
+        const int p = 16 * pb + 4 * g + r;
+        const bool valid = (p < MPAD) ? (p < m) : (p - MPAD < k);
+        x[pb][r] = valid ? a[r] : -INFINITY;
+      }
       mx = fmaxf(mx, x[pb][r]);
     }
   }
@@ -166,101 +225,89 @@ __device__ __forceinline__ void attend_queries_bf16(const AttendLds<BF16, MPAD, 
   f32x4 acc[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x4{0, 0, 0, 0};
-  // compressed pairs: Vl (hi + lo) x P (hi + lo), dropping lo x lo
+  // 32 pairs per step: pair blocks 2*s2 and 2*s2+1 give this lane's 8 P values
+  auto p_f16 = [&](int pb0) {
+    u32x4 w = {pack_f16(x[pb0][0], x[pb0][1]), pack_f16(x[pb0][2], x[pb0][3]),
+               pack_f16(x[pb0 + 1][0], x[pb0 + 1][1]), pack_f16(x[pb0 + 1][2], x[pb0 + 1][3])};
+    return __builtin_bit_cast(f16x8, w);
+  };
 #pragma unroll
   for (int s2 = 0; s2 < MPAD / 32; ++s2) {
-    float pp[8];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      pp[r] = x[2 * s2][r];
-      pp[4 + r] = x[2 * s2 + 1][r];
-    }
-    bf16x8 ph, pl;
-    split_hi_lo(pp, ph, pl);
+    const f16x8 pf = p_f16(2 * s2);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      const uint16_t* rh = S.vch + (16 * dt + c16) * L::VCST + 32 * s2 + 4 * g;
-      const uint16_t* rl = S.vcl + (16 * dt + c16) * L::VCST + 32 * s2 + 4 * g;
-      const bf16x8 ah = join_bf16x8(*reinterpret_cast<const u32x2*>(rh),
-                                    *reinterpret_cast<const u32x2*>(rh + 16));
-      const bf16x8 al = join_bf16x8(*reinterpret_cast<const u32x2*>(rl),
-                                    *reinterpret_cast<const u32x2*>(rl + 16));
-      acc[dt] = mfma_bf16(ah, ph, acc[dt]);
-      acc[dt] = mfma_bf16(ah, pl, acc[dt]);
-      acc[dt] = mfma_bf16(al, ph, acc[dt]);
+      const uint16_t* rc = S.vc + (16 * dt + c16) * L::VCST + 32 * s2 + 4 * g;
+      acc[dt] = mfma_f16(join_f16x8(*reinterpret_cast<const u32x2*>(rc),
+                                    *reinterpret_cast<const u32x2*>(rc + 16)), pf, acc[dt]);
     }
   }
-  // raw pairs: V (exact bf16) x P (hi + lo)
 #pragma unroll
   for (int s2 = 0; s2 < KPAD / 32; ++s2) {
-    float pp[8];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      pp[r] = x[MPAD / 16 + 2 * s2][r];
-      pp[4 + r] = x[MPAD / 16 + 2 * s2 + 1][r];
-    }
-    bf16x8 ph, pl;
-    split_hi_lo(pp, ph, pl);
+    const f16x8 pf = p_f16(MPAD / 16 + 2 * s2);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       const uint16_t* rv = S.vr + (16 * dt + c16) * L::VRST + 32 * s2 + 4 * g;
-      const bf16x8 a = join_bf16x8(*reinterpret_cast<const u32x2*>(rv),
-                                   *reinterpret_cast<const u32x2*>(rv + 16));
-      acc[dt] = mfma_bf16(a, ph, acc[dt]);
-      acc[dt] = mfma_bf16(a, pl, acc[dt]);
+      acc[dt] = mfma_f16(join_f16x8(*reinterpret_cast<const u32x2*>(rv),
+                                    *reinterpret_cast<const u32x2*>(rv + 16)), pf, acc[dt]);
     }
   }
   if (qok) {
-    const float inv = 1.0f / lsum;
+    const float f = oscale * __builtin_amdgcn_rcpf(lsum);  // lsum >= 1
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
-      *reinterpret_cast<f32x4*>(out_h + q * kD + 16 * dt + 4 * g) = acc[dt] * inv;
+      *reinterpret_cast<f32x4*>(out_h + q * kD + 16 * dt + 4 * g) = acc[dt] * f;
   }
 }
 
-template <int MPAD, int KPAD>
+template <int MPAD, int KPAD, bool FULL>
 __device__ void attend_bf16(AttendLds<BF16, MPAD, KPAD>& S, const uint16_t* __restrict__ Q,
                             const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-                            const uint16_t* __restrict__ Ql, const uint16_t* __restrict__ vlt_hi,
-                            const uint16_t* __restrict__ vlt_lo, const int32_t* __restrict__ idx,
-                            const int32_t* __restrict__ perm, int64_t N, int m, int k, float c2,
-                            float* __restrict__ out, int64_t bh, const TileInfo& ti) {
-  const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
+                            const uint16_t* __restrict__ Ql, const float* __restrict__ vl,
+                            const int32_t* __restrict__ idx, const int32_t* __restrict__ perm,
+                            int64_t N, int m, int k, float c2, float* __restrict__ out, int64_t bh,
+                            const TileInfo& ti) {
+  constexpr int D = 4;  // Q gathers in flight per wave (sub-tiles ahead)
+  const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
   const uint16_t* Qh = Q + bh * N * kD;
   const int32_t* ph = perm + bh * N;
   float* out_h = out + bh * N * kD;
   const u32x4 z = {0, 0, 0, 0};
-
-  // wave w handles the 16-query sub-tiles w, w+4, w+8, ... of the item;
-  // the query index runs two sub-tiles ahead and the Q rows one ahead
-  auto qpos = [&](int i) { return ti.qb + 16 * (w + 4 * i) + c16; };
-  auto load_perm = [&](int i) -> int64_t {
-    const int pos = qpos(i);
-    return (pos < ti.qe && pos >= 0 && pos < N) ? clamp_index(ph[pos], N) : -1;
-  };
+  const int nq = ti.qe - ti.qb;                // queries in this item (<= 64 * tpb)
+  const int nsub = (nq + 15) / 16;             // 16-query sub-tiles
+  // wave w handles sub-tiles w, w+4, w+8, ...; slot of sub-tile i in the item
+  auto slot = [&](int i) { return 16 * (w + 4 * i) + c16; };
   auto load_q = [&](int64_t q, bf16x8 (&qb)[2]) {
 #pragma unroll
     for (int s = 0; s < 2; ++s)
       qb[s] = as_bf16x8(q >= 0 ? *reinterpret_cast<const u32x4*>(Qh + q * kD + 32 * s + 8 * g) : z);
   };
-  const int nsub = (ti.qe - ti.qb + 15) / 16;  // sub-tiles in this item
-  int64_t q_cur = load_perm(0);
-  int64_t q_nxt = load_perm(1);
-  bf16x8 qb[2];
-  load_q(q_cur, qb);
-
-  stage_bf16<MPAD, KPAD>(S, K, V, Ql, vlt_hi, vlt_lo, idx + (bh * m + ti.e) * k, N, m, k, bh);
+  // the first D sub-tiles' rows are requested before staging (perm from global)
+  bf16x8 ring[D][2];
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    const int sl = slot(j);
+    const int64_t q = (sl < nq && ti.qb + sl < N) ? clamp_index(ph[ti.qb + sl], N) : -1;
+    load_q(q, ring[j]);
+  }
+  for (int c = tid; c < nq; c += 256) S.perm[c] = static_cast<int32_t>(clamp_index(ph[ti.qb + c], N));
+  const int sh = stage_bf16<MPAD, KPAD>(S, K, V, Ql, vl, idx + (bh * m + ti.e) * k, N, m, k, bh);
+  const float oscale = exp2i(sh);
   __syncthreads();
 
-  for (int i = 0; w + 4 * i < nsub; ++i) {
-    bf16x8 qn[2];
-    load_q(q_nxt, qn);  // next sub-tile's rows (q = -1 loads nothing)
-    const int64_t q_nn = load_perm(i + 2);
-    attend_queries_bf16<MPAD, KPAD>(S, qb, q_cur >= 0, q_cur, m, k, c2, out_h);
-    q_cur = q_nxt;
-    q_nxt = q_nn;
-    qb[0] = qn[0];
-    qb[1] = qn[1];
+  for (int i0 = 0; w + 4 * i0 < nsub; i0 += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int i = i0 + j;
+      if (w + 4 * i >= nsub) break;
+      // re-read the staged operands from LDS for every sub-tile instead of
+      // pinning all of them in registers across the loop (keeps occupancy)
+      __asm__ volatile("" ::: "memory");
+      const int sl = slot(i);
+      const int64_t q = sl < nq ? static_cast<int64_t>(S.perm[sl]) : -1;
+      attend_queries_bf16<MPAD, KPAD, FULL>(S, ring[j], q >= 0, q, m, k, c2, oscale, out_h);
+      const int sn = slot(i + D);  // refill this slot with sub-tile i + D
+      load_q(sn < nq ? static_cast<int64_t>(S.perm[sn]) : -1, ring[j]);
+    }
   }
 }
 
@@ -353,35 +400,59 @@ __device__ void attend_f32(AttendLds<F32, MPAD, KPAD>& S, const float* __restric
   }
 }
 
-// grid (work items, BH), 256 threads
-template <class T, int MPAD, int KPAD>
-__global__ __launch_bounds__(256) void k_attend(
-    const typename T::elem* __restrict__ Q, const typename T::elem* __restrict__ K,
-    const typename T::elem* __restrict__ V, const typename T::elem* __restrict__ Ql,
-    const float* __restrict__ vl, const uint16_t* __restrict__ vlt_hi,
-    const uint16_t* __restrict__ vlt_lo, const int32_t* __restrict__ idx,
+// grid (work items, BH), 256 threads.  bf16: register budget for 4 waves per
+// SIMD (LDS allows 4 blocks per CU); fp32 (small problems): default budget.
+template <int MPAD, int KPAD, bool FULL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_attend_bf16(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ Ql, const float* __restrict__ vl, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ item_start, int tpb, int64_t N, int m, int k, float c2,
     float* __restrict__ out) {
-  __shared__ AttendLds<T, MPAD, KPAD> S;
+  __shared__ AttendLds<BF16, MPAD, KPAD> S;
   const int64_t bh = blockIdx.y;
   TileInfo ti;
   if (!find_item(item_start + bh * (m + 1), offsets + bh * (m + 1), m, tpb, blockIdx.x, ti))
     return;
-  if constexpr (sizeof(typename T::elem) == 2)
-    attend_bf16<MPAD, KPAD>(S, Q, K, V, Ql, vlt_hi, vlt_lo, idx, perm, N, m, k, c2, out, bh, ti);
-  else
-    attend_f32<MPAD, KPAD>(S, Q, K, V, Ql, vl, idx, perm, N, m, k, c2, out, bh, ti);
+  attend_bf16<MPAD, KPAD, FULL>(S, Q, K, V, Ql, vl, idx, perm, N, m, k, c2, out, bh, ti);
 }
+
+template <int MPAD, int KPAD, bool FULL>
+__global__ __launch_bounds__(256) void k_attend_f32(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    const float* __restrict__ Ql, const float* __restrict__ vl, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ item_start, int tpb, int64_t N, int m, int k, float c2,
+    float* __restrict__ out) {
+  __shared__ AttendLds<F32, MPAD, KPAD> S;
+  const int64_t bh = blockIdx.y;
+  TileInfo ti;
+  if (!find_item(item_start + bh * (m + 1), offsets + bh * (m + 1), m, tpb, blockIdx.x, ti))
+    return;
+  attend_f32<MPAD, KPAD>(S, Q, K, V, Ql, vl, idx, perm, N, m, k, c2, out, bh, ti);
+}
+
+template <class T, int MPAD, int KPAD, bool FULL>
+struct AttendKernel;
+template <int MPAD, int KPAD, bool FULL>
+struct AttendKernel<BF16, MPAD, KPAD, FULL> {
+  static constexpr auto fn = k_attend_bf16<MPAD, KPAD, FULL>;
+};
+template <int MPAD, int KPAD, bool FULL>
+struct AttendKernel<F32, MPAD, KPAD, FULL> {
+  static constexpr auto fn = k_attend_f32<MPAD, KPAD, FULL>;
+};
 
 template <class T, int MPAD, int KPAD>
 static hipError_t launch_attend_t(const Shape& s, const void* Q, const void* K, const void* V,
                                   const int32_t* idx, const Workspace& ws, float* out,
                                   hipStream_t st) {
   using E = typename T::elem;
-  hipLaunchKernelGGL((k_attend<T, MPAD, KPAD>), dim3(s.attend_items, s.BH), dim3(256), 0, st,
+  auto kern = (s.m == MPAD && s.k == KPAD) ? AttendKernel<T, MPAD, KPAD, true>::fn
+                                           : AttendKernel<T, MPAD, KPAD, false>::fn;
+  hipLaunchKernelGGL(kern, dim3(s.attend_items, s.BH), dim3(256), 0, st,
                      static_cast<const E*>(Q), static_cast<const E*>(K), static_cast<const E*>(V),
-                     static_cast<const E*>(ws.ql), ws.vl, ws.vlt_hi, ws.vlt_lo, idx, ws.perm,
+                     static_cast<const E*>(ws.ql), ws.vl, idx, ws.perm,
                      ws.offsets, ws.item_start, s.attend_tpb, s.N, s.m, s.k, s.scale * kLog2e,
                      out);
   return hipGetLastError();

@@ -51,10 +51,11 @@ __device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
 template <class T>
 __global__ __launch_bounds__(256) void k_pool_partial(const typename T::elem* __restrict__ Q,
                                                      int64_t N, int gh, int gw, int mh, int mw,
-                                                     int splits, double* __restrict__ part) {
+                                                     int splits, int64_t bh0,
+                                                     double* __restrict__ part) {
   __shared__ double red[32][kD + 1];
   const int split = blockIdx.x, i = blockIdx.y, m = mh * mw;
-  const int64_t bh = blockIdx.z;
+  const int64_t bh = bh0 + blockIdx.z;
   int64_t r0, r1, c0, c1;
   window_bounds(gh, gw, mh, mw, i, r0, r1, c0, c1);
   const int64_t wc = c1 - c0, W = (r1 - r0) * wc;
@@ -63,6 +64,7 @@ __global__ __launch_bounds__(256) void k_pool_partial(const typename T::elem* __
   const int col = threadIdx.x & 7, row = threadIdx.x >> 3;
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   const typename T::elem* Qh = Q + bh * N * kD;
+#pragma unroll 8
   for (int64_t t = t_beg + row; t < t_end; t += 32) {
     const int64_t tok = (r0 + t / wc) * gw + (c0 + t % wc);
     float v[8];
@@ -83,11 +85,11 @@ __global__ __launch_bounds__(256) void k_pool_partial(const typename T::elem* __
 // grid (m, BH), 64 threads: combine partial sums, divide, round
 template <class T>
 __global__ __launch_bounds__(64) void k_pool_final(const double* __restrict__ part, int gh, int gw,
-                                                  int mh, int mw, int splits,
+                                                  int mh, int mw, int splits, int64_t bh0,
                                                   typename T::elem* __restrict__ ql,
                                                   typename T::elem* __restrict__ ql_copy) {
   const int i = blockIdx.x, m = mh * mw, j = threadIdx.x;
-  const int64_t bh = blockIdx.y;
+  const int64_t bh = bh0 + blockIdx.y;
   int64_t r0, r1, c0, c1;
   window_bounds(gh, gw, mh, mw, i, r0, r1, c0, c1);
   const double W = static_cast<double>((r1 - r0) * (c1 - c0));
@@ -100,22 +102,23 @@ __global__ __launch_bounds__(64) void k_pool_final(const double* __restrict__ pa
 
 template <class T>
 static hipError_t launch_pool_t(const Shape& s, const void* Q, const Workspace& ws, void* ql_copy,
-                                hipStream_t st) {
+                                int64_t bh0, int64_t nbh, hipStream_t st) {
   using E = typename T::elem;
-  hipLaunchKernelGGL(k_pool_partial<T>, dim3(s.pool_splits, s.m, s.BH), dim3(256), 0, st,
-                     static_cast<const E*>(Q), s.N, s.gh, s.gw, s.mh, s.mw, s.pool_splits,
+  hipLaunchKernelGGL(k_pool_partial<T>, dim3(s.pool_splits, s.m, nbh), dim3(256), 0, st,
+                     static_cast<const E*>(Q), s.N, s.gh, s.gw, s.mh, s.mw, s.pool_splits, bh0,
                      ws.pool_part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_pool_final<T>, dim3(s.m, s.BH), dim3(64), 0, st, ws.pool_part, s.gh, s.gw,
-                     s.mh, s.mw, s.pool_splits, static_cast<E*>(ws.ql), static_cast<E*>(ql_copy));
+  hipLaunchKernelGGL(k_pool_final<T>, dim3(s.m, nbh), dim3(64), 0, st, ws.pool_part, s.gh, s.gw,
+                     s.mh, s.mw, s.pool_splits, bh0, static_cast<E*>(ws.ql),
+                     static_cast<E*>(ql_copy));
   return hipGetLastError();
 }
 
 hipError_t launch_pool(const Shape& s, const void* Q, const Workspace& ws, void* ql_copy,
-                       hipStream_t st) {
-  return s.dtype == 1 ? launch_pool_t<BF16>(s, Q, ws, ql_copy, st)
-                      : launch_pool_t<F32>(s, Q, ws, ql_copy, st);
+                       int64_t bh0, int64_t nbh, hipStream_t st) {
+  return s.dtype == 1 ? launch_pool_t<BF16>(s, Q, ws, ql_copy, bh0, nbh, st)
+                      : launch_pool_t<F32>(s, Q, ws, ql_copy, bh0, nbh, st);
 }
 
 }  // namespace mita

@@ -11,11 +11,13 @@
 //   k_route          (segment, head): R^T = Ql Q^T on MFMA (landmark rows x
 //                    query columns), argmax with ties to the lower landmark,
 //                    route_out, and the segment's per-expert counts.
-//   k_bucket_scan    (head): expert totals -> offsets, per-(segment, expert)
-//                    bases, and the first attention work item of each expert.
-//   k_bucket_scatter (segment, head), one wave: stable counting-sort scatter;
-//                    a query's rank among equal routes inside a group of 64
-//                    comes from 6 ballots over the route bits.
+//   k_bucket_scan    (expert, head): prefix of the expert's per-segment counts
+//                    over the segments, and the expert's total.
+//   k_bucket_scatter (segment, head), one wave: expert offsets from the
+//                    totals, then a stable counting-sort scatter; a query's
+//                    rank among equal routes inside a group of 64 comes from
+//                    6 ballots over the route bits.  Segment 0 publishes the
+//                    offsets and the first attention work item of each expert.
 //
 // Roofline: k_route streams Q (N*d*e bytes per head) — HBM-bound; the
 // bucket kernels move ~16 bytes per query.
@@ -23,6 +25,9 @@
 #include "mita_internal.hpp"
 
 namespace mita {
+
+// row stride (elements) of the block's LDS copy of the landmark queries
+constexpr int kQlStride = kD + 8;
 
 template <class T>
 struct RouteTraits;
@@ -36,17 +41,14 @@ struct RouteTraits<BF16> {
   struct QReg {
     bf16x8 v[2];
   };
-  __device__ static void load_ql(QlReg& a, const E* Qlh, int m, int c16, int g) {
+  // Ql rows from the block's LDS copy (rows >= m are zero there)
+  __device__ static void load_ql(QlReg& a, const E* qls, int c16, int g) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const int lm = 16 * mt + c16;
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const u32x4 z = {0, 0, 0, 0};
+      for (int s = 0; s < 2; ++s)
         a.v[mt][s] = as_bf16x8(
-            lm < m ? *reinterpret_cast<const u32x4*>(Qlh + lm * kD + 32 * s + 8 * g) : z);
-      }
-    }
+            *reinterpret_cast<const u32x4*>(qls + (16 * mt + c16) * kQlStride + 32 * s + 8 * g));
   }
   __device__ static void load_q(QReg& b, const E* row, bool ok, int g) {
 #pragma unroll
@@ -72,13 +74,11 @@ struct RouteTraits<F32> {
   struct QReg {
     float v[16];
   };
-  __device__ static void load_ql(QlReg& a, const E* Qlh, int m, int c16, int g) {
+  __device__ static void load_ql(QlReg& a, const E* qls, int c16, int g) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const int lm = 16 * mt + c16;
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int s = 0; s < 16; ++s) a.v[mt][s] = lm < m ? Qlh[lm * kD + 4 * s + g] : 0.f;
-    }
+      for (int s = 0; s < 16; ++s) a.v[mt][s] = qls[(16 * mt + c16) * kQlStride + 4 * s + g];
   }
   __device__ static void load_q(QReg& b, const E* row, bool ok, int g) {
 #pragma unroll
@@ -93,38 +93,71 @@ struct RouteTraits<F32> {
 };
 
 // grid (nseg, BH), 256 threads; wave w routes queries seg*1024 + 256w + [0, 256)
+// in four steps of 64 (groups of 16 queries); the next step's Q rows are in
+// flight while the current step computes
 template <class T>
 __global__ __launch_bounds__(256) void k_route(const typename T::elem* __restrict__ Q,
                                               const typename T::elem* __restrict__ Ql, int64_t N,
-                                              int m, int nseg, int32_t* __restrict__ route_out,
+                                              int m, int nseg, int64_t bh0,
+                                              int32_t* __restrict__ route_out,
                                               int32_t* __restrict__ counts) {
   using TR = RouteTraits<T>;
+  using E = typename T::elem;
   __shared__ int cnt[kMaxM];
+  __shared__ __attribute__((aligned(16))) E qls[kMaxM * kQlStride];
   const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
   const int seg = blockIdx.x;
-  const int64_t bh = blockIdx.y;
+  const int64_t bh = bh0 + blockIdx.y;
   if (threadIdx.x < kMaxM) cnt[threadIdx.x] = 0;
-  typename TR::QlReg a;
-  TR::load_ql(a, Ql + bh * m * kD, m, c16, g);
-  const int mtiles = (m + 15) >> 4;
+  {  // the landmark queries once per block, zero rows past m
+    constexpr int CH = 16 / sizeof(E);  // elements per 16-byte chunk
+    for (int c = threadIdx.x; c < kMaxM * (kD / CH); c += 256) {
+      const int row = c / (kD / CH), col = c % (kD / CH);
+      const u32x4 z = {0, 0, 0, 0};
+      *reinterpret_cast<u32x4*>(qls + row * kQlStride + col * CH) =
+          row < m ? *reinterpret_cast<const u32x4*>(Ql + (bh * m + row) * kD + col * CH) : z;
+    }
+  }
+  const E* Qh = Q + bh * N * kD;
+  const int64_t qw = static_cast<int64_t>(seg) * kRouteSeg + 256 * w;
+  // bf16: the whole next step's rows in flight; fp32 operands are 4x larger,
+  // so they are loaded group by group (register budget)
+  constexpr bool kPrefetch = sizeof(E) == 2;
+  constexpr int NB = kPrefetch ? 4 : 1;
+  auto load_group = [&](int it, int G, typename TR::QReg& dst) {
+    const int64_t qq = qw + 64 * it + 16 * G + c16;
+    TR::load_q(dst, Qh + (qq < N ? qq : 0) * kD, qq < N, g);
+  };
+  typename TR::QReg b[NB];
+  if constexpr (kPrefetch) {
+#pragma unroll
+    for (int G = 0; G < 4; ++G) load_group(0, G, b[G]);
+  }
   __syncthreads();
+  typename TR::QlReg a;
+  TR::load_ql(a, qls, c16, g);
+  const int mtiles = (m + 15) >> 4;
 
-  const typename T::elem* Qh = Q + bh * N * kD;
   for (int it = 0; it < 4; ++it) {
-    const int64_t q0 = static_cast<int64_t>(seg) * kRouteSeg + 256 * w + 64 * it;
-    if (q0 >= N) break;
+    if (qw + 64 * it >= N) break;
+    typename TR::QReg bn[NB];
+    if constexpr (kPrefetch) {
+      if (it + 1 < 4) {
+#pragma unroll
+        for (int G = 0; G < 4; ++G) load_group(it + 1, G, bn[G]);
+      }
+    }
     int rsel = 0;
 #pragma unroll
     for (int G = 0; G < 4; ++G) {
-      const int64_t qq = q0 + 16 * G + c16;
-      typename TR::QReg b;
-      TR::load_q(b, Qh + (qq < N ? qq : 0) * kD, qq < N, g);
+      if constexpr (!kPrefetch) load_group(it, G, b[0]);
+      const typename TR::QReg& bq = b[kPrefetch ? G : 0];
       float best = -INFINITY;
       int bi = 0;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         if (mt < mtiles) {
-          const f32x4 r4 = TR::logits(a, mt, b);
+          const f32x4 r4 = TR::logits(a, mt, bq);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int lmi = 16 * mt + 4 * g + r;  // increasing within the lane
@@ -146,90 +179,90 @@ __global__ __launch_bounds__(256) void k_route(const typename T::elem* __restric
           bi = oi;
         }
       }
-      if (G == g) rsel = bi;  // lane l = 16G + c16 keeps query q0 + l
+      if (G == g) rsel = bi;  // lane l = 16G + c16 keeps query qw + 64 it + l
     }
-    const int64_t q = q0 + l;
+    const int64_t q = qw + 64 * it + l;
     if (q < N) {
       route_out[bh * N + q] = rsel;
       atomicAdd(&cnt[rsel], 1);
     }
-  }
-  __syncthreads();
-  if (threadIdx.x < m) counts[(bh * nseg + seg) * m + threadIdx.x] = cnt[threadIdx.x];
-}
-
-// grid (BH), 1024 threads: thread (e = t % 64, part = t / 64) handles expert
-// e over segments [part*nseg/16, (part+1)*nseg/16)
-__global__ __launch_bounds__(1024) void k_bucket_scan(const int32_t* __restrict__ counts, int m,
-                                                     int nseg, int64_t N, int tile, int tpb,
-                                                     int32_t* __restrict__ seg_base,
-                                                     int32_t* __restrict__ offsets,
-                                                     int32_t* __restrict__ offsets_copy,
-                                                     int32_t* __restrict__ item_start) {
-  __shared__ int psum[16][kMaxM];
-  __shared__ int off[kMaxM + 1];
-  __shared__ int tst[kMaxM + 1];
-  const int t = threadIdx.x, e = t & 63, part = t >> 6;
-  const int64_t bh = blockIdx.x;
-  const int s0 = static_cast<int>((static_cast<int64_t>(part) * nseg) / 16);
-  const int s1 = static_cast<int>((static_cast<int64_t>(part + 1) * nseg) / 16);
-  const int32_t* C = counts + bh * nseg * m;
-  int sum = 0;
-  if (e < m)
-    for (int s = s0; s < s1; ++s) sum += C[s * m + e];
-  psum[part][e] = sum;
-  __syncthreads();
-  if (t < 64) {
-    int total = 0;
-    if (e < m)
-      for (int p = 0; p < 16; ++p) total += psum[p][e];
-    // exclusive scans over experts of totals and of tile counts (one wave)
-    const int tiles_e = (total + tile - 1) / tile;
-    int ex = total, tl = (tiles_e + tpb - 1) / tpb;  // work items of expert e
+    if constexpr (kPrefetch) {
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int a = static_cast<int>(lane_read(static_cast<uint32_t>(ex), t >= d ? t - d : t));
-      const int b = static_cast<int>(lane_read(static_cast<uint32_t>(tl), t >= d ? t - d : t));
-      if (t >= d) {
-        ex += a;
-        tl += b;
-      }
-    }
-    // ex, tl are inclusive; shift to exclusive
-    off[t + 1] = ex;
-    tst[t + 1] = tl;
-    if (t == 0) {
-      off[0] = 0;
-      tst[0] = 0;
+      for (int G = 0; G < 4; ++G) b[G] = bn[G];
     }
   }
   __syncthreads();
-  if (t <= m) {
-    offsets[bh * (m + 1) + t] = off[t];
-    if (offsets_copy) offsets_copy[bh * (m + 1) + t] = off[t];
-    item_start[bh * (m + 1) + t] = tst[t];
-  }
-  if (e < m) {
-    int run = off[e];
-    for (int p = 0; p < part; ++p) run += psum[p][e];
-    int32_t* SB = seg_base + bh * nseg * m;
-    for (int s = s0; s < s1; ++s) {
-      SB[s * m + e] = run;
-      run += C[s * m + e];
-    }
-  }
+  if (threadIdx.x < m) counts[(bh * m + threadIdx.x) * nseg + seg] = cnt[threadIdx.x];  // expert-major
 }
 
-// grid (nseg, BH), 64 threads: stable scatter of one segment's queries
-__global__ __launch_bounds__(64) void k_bucket_scatter(const int32_t* __restrict__ route, int m,
-                                                      int nseg, int64_t N,
-                                                      const int32_t* __restrict__ seg_base,
-                                                      int32_t* __restrict__ perm,
-                                                      int32_t* __restrict__ perm_copy) {
+// inclusive prefix sum over the 64 lanes of a wave
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = static_cast<int>(lane_read(static_cast<uint32_t>(v), l >= d ? l - d : l));
+    if (l >= d) v += o;
+  }
+  return v;
+}
+
+// grid (m, BH), 256 threads: for expert e, the exclusive prefix of its
+// per-segment counts over the segments (colpre) and its total
+__global__ __launch_bounds__(256) void k_bucket_scan(const int32_t* __restrict__ counts, int m,
+                                                     int nseg, int32_t* __restrict__ colpre,
+                                                     int32_t* __restrict__ totals) {
+  __shared__ int wsum[4];
+  const int e = blockIdx.x, t = threadIdx.x, l = lane_id(), w = wave_id();
+  const int64_t bh = blockIdx.y;
+  const int32_t* C = counts + (bh * m + e) * nseg;
+  int32_t* P = colpre + (bh * m + e) * nseg;
+  const int per = (nseg + 255) / 256;  // contiguous segments per thread
+  const int s0 = t * per, s1 = min(s0 + per, nseg);
+  int sum = 0;
+  for (int s = s0; s < s1; ++s) sum += C[s];
+  const int incl = wave_inclusive_sum(sum);
+  if (l == 63) wsum[w] = incl;
+  __syncthreads();
+  int run = incl - sum;
+  for (int v = 0; v < w; ++v) run += wsum[v];
+  for (int s = s0; s < s1; ++s) {
+    const int c = C[s];
+    P[s] = run;
+    run += c;
+  }
+  if (t == 255) totals[bh * m + e] = run;
+}
+
+// grid (nseg, BH), 64 threads: stable scatter of one segment's queries.
+// Expert offsets come from the per-expert totals (exclusive scan over the m
+// experts); segment 0 also publishes offsets and the attention work items.
+__global__ __launch_bounds__(64) void k_bucket_scatter(
+    const int32_t* __restrict__ route, int m, int nseg, int64_t N, int tile, int tpb,
+    const int32_t* __restrict__ totals, const int32_t* __restrict__ colpre,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ offsets_copy,
+    int32_t* __restrict__ item_start, int32_t* __restrict__ perm, int32_t* __restrict__ perm_copy) {
   __shared__ int base[kMaxM];
   const int l = threadIdx.x, seg = blockIdx.x;
   const int64_t bh = blockIdx.y;
-  if (l < m) base[l] = seg_base[(bh * nseg + seg) * m + l];
+  const int c = l < m ? totals[bh * m + l] : 0;
+  const int incl = wave_inclusive_sum(c);
+  if (seg == 0) {
+    const int items = ((c + tile - 1) / tile + tpb - 1) / tpb;
+    const int incl_items = wave_inclusive_sum(items);
+    int32_t* O = offsets + bh * (m + 1);
+    int32_t* I = item_start + bh * (m + 1);
+    if (l < m) {
+      O[l] = incl - c;
+      I[l] = incl_items - items;
+      if (offsets_copy) offsets_copy[bh * (m + 1) + l] = incl - c;
+    }
+    if (l == m - 1) {
+      O[m] = incl;
+      I[m] = incl_items;
+      if (offsets_copy) offsets_copy[bh * (m + 1) + m] = incl;
+    }
+  }
+  if (l < m) base[l] = (incl - c) + colpre[(bh * m + l) * nseg + seg];
   __syncthreads();
   const uint64_t below = (l == 0) ? 0ull : (~0ull >> (64 - l));
   for (int it = 0; it < kRouteSeg / 64; ++it) {
@@ -260,28 +293,28 @@ __global__ __launch_bounds__(64) void k_bucket_scatter(const int32_t* __restrict
 
 template <class T>
 static hipError_t launch_route_t(const Shape& s, const void* Q, const Workspace& ws,
-                                 int32_t* route_out, hipStream_t st) {
+                                 int32_t* route_out, int64_t bh0, int64_t nbh, hipStream_t st) {
   using E = typename T::elem;
-  hipLaunchKernelGGL(k_route<T>, dim3(s.nseg, s.BH), dim3(256), 0, st, static_cast<const E*>(Q),
-                     static_cast<const E*>(ws.ql), s.N, s.m, s.nseg, route_out, ws.counts);
+  hipLaunchKernelGGL(k_route<T>, dim3(s.nseg, nbh), dim3(256), 0, st, static_cast<const E*>(Q),
+                     static_cast<const E*>(ws.ql), s.N, s.m, s.nseg, bh0, route_out, ws.counts);
   return hipGetLastError();
 }
 
 hipError_t launch_route(const Shape& s, const void* Q, const Workspace& ws, int32_t* route_out,
-                        hipStream_t st) {
-  return s.dtype == 1 ? launch_route_t<BF16>(s, Q, ws, route_out, st)
-                      : launch_route_t<F32>(s, Q, ws, route_out, st);
+                        int64_t bh0, int64_t nbh, hipStream_t st) {
+  return s.dtype == 1 ? launch_route_t<BF16>(s, Q, ws, route_out, bh0, nbh, st)
+                      : launch_route_t<F32>(s, Q, ws, route_out, bh0, nbh, st);
 }
 
 hipError_t launch_bucket(const Shape& s, const int32_t* route, const Workspace& ws,
                          int32_t* offsets_copy, int32_t* perm_copy, hipStream_t st) {
-  hipLaunchKernelGGL(k_bucket_scan, dim3(s.BH), dim3(1024), 0, st, ws.counts, s.m, s.nseg, s.N,
-                     kAttendTile, s.attend_tpb, ws.seg_base, ws.offsets, offsets_copy,
-                     ws.item_start);
+  hipLaunchKernelGGL(k_bucket_scan, dim3(s.m, s.BH), dim3(256), 0, st, ws.counts, s.m, s.nseg,
+                     ws.colpre, ws.totals);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_bucket_scatter, dim3(s.nseg, s.BH), dim3(64), 0, st, route, s.m, s.nseg,
-                     s.N, ws.seg_base, ws.perm, perm_copy);
+                     s.N, kAttendTile, s.attend_tpb, ws.totals, ws.colpre, ws.offsets,
+                     offsets_copy, ws.item_start, ws.perm, perm_copy);
   return hipGetLastError();
 }
 

@@ -489,25 +489,16 @@ __global__ __launch_bounds__(256) void k_theta_select(const uint64_t* __restrict
 // merge of the per-split partials
 // ---------------------------------------------------------------------------
 
-// grid (landmark rows, BH), 256 threads.  Rows m..mpad-1 only clear the
-// padding columns of Vl^T.
+// grid (m, BH), 256 threads
 __global__ __launch_bounds__(256) void k_merge(
     const uint64_t* __restrict__ part_keys, const float* __restrict__ part_stats,
-    const float* __restrict__ part_acc, int m, int k, int mrows, int splits, int mpad,
-    int32_t* __restrict__ idx_out, float* __restrict__ vl, float* __restrict__ vl_copy,
-    uint16_t* __restrict__ vlt_hi, uint16_t* __restrict__ vlt_lo) {
+    const float* __restrict__ part_acc, int m, int k, int mrows, int splits,
+    int32_t* __restrict__ idx_out, float* __restrict__ vl, float* __restrict__ vl_copy) {
   __shared__ uint64_t tops[4][64];
   __shared__ float sacc[4][64];
   __shared__ float sM[4], sL[4];
   const int l = lane_id(), w = wave_id(), lm = blockIdx.x;
   const int64_t bh = blockIdx.y;
-  if (lm >= m) {
-    if (vlt_hi != nullptr && threadIdx.x < kD) {
-      vlt_hi[(bh * kD + threadIdx.x) * mpad + lm] = 0;
-      vlt_lo[(bh * kD + threadIdx.x) * mpad + lm] = 0;
-    }
-    return;
-  }
 
   // top lists of splits w, w+4, ...
   uint64_t top = 0;
@@ -558,11 +549,6 @@ __global__ __launch_bounds__(256) void k_merge(
   const float val = at / Lt;
   vl[(bh * m + lm) * kD + l] = val;
   if (vl_copy != nullptr) vl_copy[(bh * m + lm) * kD + l] = val;
-  if (vlt_hi != nullptr) {
-    const __bf16 h = f32_to_bf16(val);
-    vlt_hi[(bh * kD + l) * mpad + lm] = __builtin_bit_cast(uint16_t, h);
-    vlt_lo[(bh * kD + l) * mpad + lm] = f32_to_bf16_bits(val - static_cast<float>(h));
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -615,10 +601,8 @@ hipError_t launch_scan(const Shape& s, const void* K, const void* V, const Works
 
 hipError_t launch_merge(const Shape& s, const Workspace& ws, int32_t* idx_out, float* vl_copy,
                         hipStream_t st) {
-  const bool bf = s.dtype == 1;
-  hipLaunchKernelGGL(k_merge, dim3(bf ? s.mpad : s.m, s.BH), dim3(256), 0, st, ws.part_keys,
-                     ws.part_stats, ws.part_acc, s.m, s.k, s.mrows, s.scan_splits, s.mpad, idx_out,
-                     ws.vl, vl_copy, bf ? ws.vlt_hi : nullptr, bf ? ws.vlt_lo : nullptr);
+  hipLaunchKernelGGL(k_merge, dim3(s.m, s.BH), dim3(256), 0, st, ws.part_keys, ws.part_stats,
+                     ws.part_acc, s.m, s.k, s.mrows, s.scan_splits, idx_out, ws.vl, vl_copy);
   return hipGetLastError();
 }
 

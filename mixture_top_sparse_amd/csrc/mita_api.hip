@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -110,6 +111,37 @@ int device_cus() {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // ---------------------------------------------------------------------------
+// per-device side stream: the routing branch (route + bucket) depends only on
+// the pooled landmarks, like the landmark branch (pre-threshold, scan,
+// merge), so the two run concurrently: fork after pooling, join before the
+// expert attention.  Default priority, non-blocking; one mutex per device
+// keeps each call's fork/record/wait sequence from interleaving with another
+// host thread's.
+// ---------------------------------------------------------------------------
+
+struct SideStream {
+  std::mutex mu;
+  bool ready = false;
+  hipStream_t aux = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+SideStream g_side[64];
+
+SideStream* side_stream() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  SideStream& ss = g_side[dev];
+  std::lock_guard<std::mutex> lk(ss.mu);
+  if (!ss.ready) {
+    if (hipStreamCreateWithFlags(&ss.aux, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) return nullptr;
+    ss.ready = true;
+  }
+  return &ss;
+}
+
+// ---------------------------------------------------------------------------
 // validation (host only, before any HIP call)
 // ---------------------------------------------------------------------------
 
@@ -204,9 +236,10 @@ void derive(Shape& s, int cus) {
   // expert attention: work items of up to 16 tiles, keeping >= 4 items per CU
   const int64_t tiles = cdiv(s.N, kAttendTile);
   int64_t tpb = (tiles * s.BH) / (4 * static_cast<int64_t>(cus));
-  tpb = tpb < 1 ? 1 : (tpb > 16 ? 16 : tpb);
+  tpb = tpb < 1 ? 1 : (tpb > kAttendMaxTpb ? kAttendMaxTpb : tpb);
   s.attend_tpb = static_cast<int>(tpb);
   s.attend_items = static_cast<int>(cdiv(tiles + s.m, tpb) + s.m);
+
 }
 
 }  // namespace
@@ -233,14 +266,9 @@ size_t plan_workspace(const Shape& s, Workspace* ws, char* base) {
   ws->part_stats = reinterpret_cast<float*>(take(parts * 2 * sizeof(float)));
   ws->part_acc = reinterpret_cast<float*>(take(parts * kD * sizeof(float)));
   ws->vl = reinterpret_cast<float*>(take(BH * s.m * kD * sizeof(float)));
-  if (s.dtype == MITA_BF16) {
-    ws->vlt_hi = reinterpret_cast<uint16_t*>(take(BH * kD * s.mpad * 2));
-    ws->vlt_lo = reinterpret_cast<uint16_t*>(take(BH * kD * s.mpad * 2));
-  } else {
-    ws->vlt_hi = ws->vlt_lo = nullptr;
-  }
   ws->counts = reinterpret_cast<int32_t*>(take(BH * s.nseg * s.m * 4));
-  ws->seg_base = reinterpret_cast<int32_t*>(take(BH * s.nseg * s.m * 4));
+  ws->colpre = reinterpret_cast<int32_t*>(take(BH * s.nseg * s.m * 4));
+  ws->totals = reinterpret_cast<int32_t*>(take(BH * s.m * 4));
   ws->offsets = reinterpret_cast<int32_t*>(take(BH * (s.m + 1) * 4));
   ws->item_start = reinterpret_cast<int32_t*>(take(BH * (s.m + 1) * 4));
   ws->perm = reinterpret_cast<int32_t*>(take(BH * s.N * 4));
@@ -306,27 +334,52 @@ int mita_forward_ex(const void* Q, const void* K, const void* V, int dtype, int6
     if (inject_launch) e = hipErrorLaunchFailure;
     if (e == hipSuccess) {
       StageTimer t(kStagePool, st);
-      e = launch_pool(s, Q, ws, ql_copy, st);
+      e = launch_pool(s, Q, ws, ql_copy, 0, s.BH, st);
+    }
+    // routing branch on the side stream, landmark branch on the caller's
+    SideStream* ss = (e == hipSuccess) ? side_stream() : nullptr;
+    if (e == hipSuccess && ss == nullptr) {
+      e = hipErrorInvalidResourceHandle;
+      where = "side stream";
     }
     if (e == hipSuccess) {
-      where = "landmark_scan";
-      StageTimer t(kStageScan, st);
-      e = launch_scan(s, K, V, ws, st);
-    }
-    if (e == hipSuccess) {
-      where = "landmark_merge";
-      StageTimer t(kStageMerge, st);
-      e = launch_merge(s, ws, idx_out, vl_copy, st);
-    }
-    if (e == hipSuccess) {
-      where = "route";
-      StageTimer t(kStageRoute, st);
-      e = launch_route(s, Q, ws, route_out, st);
-    }
-    if (e == hipSuccess) {
-      where = "bucket";
-      StageTimer t(kStageBucket, st);
-      e = launch_bucket(s, route_out, ws, off_copy, perm_copy, st);
+      std::lock_guard<std::mutex> lk(ss->mu);
+      hipError_t ea = hipEventRecord(ss->fork, st);
+      if (ea == hipSuccess) ea = hipStreamWaitEvent(ss->aux, ss->fork, 0);
+      const bool forked = ea == hipSuccess;
+      const char* where_aux = "fork";
+      if (forked) {
+        where_aux = "route";
+        {
+          StageTimer t(kStageRoute, ss->aux);
+          ea = launch_route(s, Q, ws, route_out, 0, s.BH, ss->aux);
+        }
+        if (ea == hipSuccess) {
+          where_aux = "bucket";
+          StageTimer t(kStageBucket, ss->aux);
+          ea = launch_bucket(s, route_out, ws, off_copy, perm_copy, ss->aux);
+        }
+      }
+      if (e == hipSuccess) {
+        where = "landmark_scan";
+        StageTimer t(kStageScan, st);
+        e = launch_scan(s, K, V, ws, st);
+      }
+      if (e == hipSuccess) {
+        where = "landmark_merge";
+        StageTimer t(kStageMerge, st);
+        e = launch_merge(s, ws, idx_out, vl_copy, st);
+      }
+      if (forked) {  // join, also on failure, before the work space is freed
+        hipError_t ej = hipEventRecord(ss->join, ss->aux);
+        if (ej == hipSuccess) ej = hipStreamWaitEvent(st, ss->join, 0);
+        if (ea == hipSuccess) ea = ej;
+        if (ej != hipSuccess) (void)hipStreamSynchronize(ss->aux);
+      }
+      if (e == hipSuccess && ea != hipSuccess) {
+        e = ea;
+        where = where_aux;
+      }
     }
     if (e == hipSuccess) {
       where = "expert_attend";

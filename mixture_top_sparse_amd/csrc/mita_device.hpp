@@ -19,6 +19,7 @@
 namespace mita {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -206,11 +207,32 @@ __device__ __forceinline__ int32_t wave_sort_asc_i32(int32_t v) {
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ f16x8 join_f16x8(u32x2 lo, u32x2 hi) {
+  u32x4 v = {lo.x, lo.y, hi.x, hi.y};
+  return __builtin_bit_cast(f16x8, v);
+}
+// two fp32 values -> one dword of two fp16 (round to nearest even)
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  f16x2 v = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w)));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+}
+// 2^e as a float for -126 <= e <= 127
+__device__ __forceinline__ float exp2i(int e) { return __uint_as_float(static_cast<uint32_t>(e + 127) << 23); }
 __device__ __forceinline__ bf16x8 join_bf16x8(u32x2 lo, u32x2 hi) {
   u32x4 v = {lo.x, lo.y, hi.x, hi.y};
   return __builtin_bit_cast(bf16x8, v);

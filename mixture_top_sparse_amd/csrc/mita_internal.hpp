@@ -14,6 +14,7 @@ constexpr int kTopCap = 64;      // per-split top list length (one key per lane)
 constexpr int kTileKeys = 64;    // keys per landmark-scan tile
 constexpr int kRouteSeg = 1024;  // queries per routing/bucketing segment
 constexpr int kAttendTile = 64;  // queries per expert-attention tile
+constexpr int kAttendMaxTpb = 16;  // tiles per expert-attention work item, at most
 constexpr int kPoolChunk = 2048; // tokens per pooling partial sum
 constexpr int kThetaTilesPerBlock = 4;  // sample tiles per top-k pre-threshold block
 
@@ -47,10 +48,9 @@ struct Workspace {
   float* part_stats = nullptr;   // [BH][splits][mrows][2] (max in log2 units, sum)
   float* part_acc = nullptr;     // [BH][splits][mrows][64] unnormalised P.V
   float* vl = nullptr;           // [BH][m][64] landmark values fp32
-  uint16_t* vlt_hi = nullptr;    // [BH][64][mpad] bf16 hi part of Vl^T (bf16 path)
-  uint16_t* vlt_lo = nullptr;    // [BH][64][mpad] bf16 lo part of Vl^T
-  int32_t* counts = nullptr;     // [BH][nseg][m] routed queries per segment and expert
-  int32_t* seg_base = nullptr;   // [BH][nseg][m] first perm slot of each (segment, expert)
+  int32_t* counts = nullptr;     // [BH][m][nseg] routed queries per expert and segment
+  int32_t* colpre = nullptr;     // [BH][m][nseg] exclusive prefix of counts over segments
+  int32_t* totals = nullptr;     // [BH][m] routed queries per expert
   int32_t* offsets = nullptr;    // [BH][m+1]
   int32_t* item_start = nullptr; // [BH][m+1] first attention work item of each expert
   int32_t* perm = nullptr;       // [BH][N]
@@ -60,13 +60,13 @@ size_t plan_workspace(const Shape& s, Workspace* ws, char* base);
 
 // Kernel launchers; each returns the launch status.
 hipError_t launch_pool(const Shape& s, const void* Q, const Workspace& ws, void* ql_copy,
-                       hipStream_t st);
+                       int64_t bh0, int64_t nbh, hipStream_t st);
 hipError_t launch_scan(const Shape& s, const void* K, const void* V, const Workspace& ws,
                        hipStream_t st);
 hipError_t launch_merge(const Shape& s, const Workspace& ws, int32_t* idx_out, float* vl_copy,
                         hipStream_t st);
 hipError_t launch_route(const Shape& s, const void* Q, const Workspace& ws, int32_t* route_out,
-                        hipStream_t st);
+                        int64_t bh0, int64_t nbh, hipStream_t st);
 hipError_t launch_bucket(const Shape& s, const int32_t* route, const Workspace& ws,
                          int32_t* offsets_copy, int32_t* perm_copy, hipStream_t st);
 hipError_t launch_attend(const Shape& s, const void* Q, const void* K, const void* V,

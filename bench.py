@@ -21,10 +21,53 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MiTA fwd Mtokens·heads/s at N=64K–1M; % of HBM roofline (gather-bound)"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+# profiler stages that are exactly one kernel launch, with that kernel's name
+SINGLE_KERNEL_STAGES = {"landmark_scan": "k_scan", "route": "k_route",
+                        "expert_attend": "k_attend"}
+KERNEL_SOURCES = {"k_scan": "kernels_scan.hip", "k_route": "kernels_route.hip",
+                  "k_attend": "kernels_attend.hip"}
+# HBM bytes per launch on the 1M-token workload from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE (scaled by 2.0 and 1.0, the factors a 1 GiB copy kernel gives),
+# with the sha1 of the kernel's sources when the counters were taken: a
+# kernel whose sources changed since reports traffic null.
+COUNTED_TRAFFIC = {
+    "len_1m": {
+        "k_scan": {"sha": "015f662fb73d", "bytes": 1100567579},
+        "k_route": {"sha": "5b596e380fa2", "bytes": 562964875},
+        "k_attend": {"sha": "1581a5ea8364", "bytes": 1648485944},
+    },
+}
+
+
+def kernel_sha(symbol: str) -> str:
+    """sha1 (12 hex digits) of a kernel's source file and the shared headers."""
+    import hashlib
+
+    h = hashlib.sha1()
+    csrc = os.path.join(ROOT, "mixture_top_sparse_amd", "csrc")
+    for f in (KERNEL_SOURCES[symbol], "mita_device.hpp", "mita_internal.hpp"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:12]
+
+
+def counted_traffic(workload: str, symbol: str):
+    rec = COUNTED_TRAFFIC.get(workload, {}).get(symbol)
+    if rec is None or rec["sha"] != kernel_sha(symbol):
+        return None
+    return rec["bytes"]
 
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def threshold_tiles(w) -> int:
+    """Key tiles of 64 sampled per head by the top-k pre-threshold (the
+    library's rule: a quarter of the tiles, at most 1024, a multiple of 4,
+    and only when there are at least max(k, 64) of them)."""
+    g = min(-(-w.N // 64) // 4, 1024) // 4 * 4
+    return g if g >= 64 and g >= w.k else 0
 
 
 def stage_bytes(w) -> dict[str, float]:
@@ -36,6 +79,7 @@ def stage_bytes(w) -> dict[str, float]:
     rows = min(m * k, N)
     return {
         "pool": BH * (N * d * e + m * d * e),
+        "landmark_threshold": BH * (threshold_tiles(w) * 64 * d * e + m * d * e),
         "landmark_scan": BH * (2 * N * d * e),
         "landmark_merge": BH * (4 * m * k + 4 * m * d),
         "route": BH * (N * d * e + 4 * N),
@@ -175,7 +219,8 @@ def main() -> int:
 
     avg_stage = {k: v / max(calls, 1) for k, v in stage_ms.items()}
     sbytes = stage_bytes(w)
-    dominant = max(avg_stage, key=avg_stage.get)
+    # the dominant kernel: the slowest of the single-launch stages
+    dominant = max(SINGLE_KERNEL_STAGES, key=lambda st: avg_stage[st])
     ach = sbytes[dominant] / (avg_stage[dominant] * 1e-3) / 1e9
     pbytes = path_bytes(w)
     path_gbs = pbytes / (ms_per_step * 1e-3) / 1e9
@@ -206,11 +251,13 @@ def main() -> int:
         "roofline": {
             "bound": "hbm",
             "kernel": dominant,
+            "symbol": SINGLE_KERNEL_STAGES[dominant],
+            "launch_ms": round(avg_stage[dominant], 4),
             "achieved": round(ach, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": counted_traffic(w.name, SINGLE_KERNEL_STAGES[dominant]),
         },
         "path_roofline": {"algorithmic_bytes": pbytes, "achieved_GBs": round(path_gbs, 1),
                           "frac": round(path_gbs / HBM_PEAK_GBS, 4)},

@@ -139,7 +139,11 @@ int mita_version(void);
 /*
  * Stage profiler (for measurement; off by default).  While enabled, each
  * forward call records a pair of HIP events around every stage on the
- * call's stream.  mita_profile_read() waits for the recorded events and
+ * stream the stage runs on (routing and bucketing run on a library-owned
+ * side stream).  Stages, in order: pool, landmark_threshold (the sampled
+ * top-k pre-threshold), landmark_scan, landmark_merge, route, bucket,
+ * expert_attend; each of landmark_scan, route and expert_attend is a single
+ * kernel launch.  mita_profile_read() waits for the recorded events and
  * returns, per stage, the summed milliseconds and the number of calls since
  * the last mita_profile_enable().  Not thread-safe: profile from one thread.
  *   mita_profile_enable(1) clears the sums and starts recording;

@@ -589,13 +589,14 @@ static hipError_t launch_theta_t(const Shape& s, const void* K, const Workspace&
   return hipGetLastError();
 }
 
+hipError_t launch_threshold(const Shape& s, const void* K, const Workspace& ws,
+                            hipStream_t st) {
+  if (s.theta_groups == 0) return hipSuccess;
+  return s.dtype == 1 ? launch_theta_t<BF16>(s, K, ws, st) : launch_theta_t<F32>(s, K, ws, st);
+}
+
 hipError_t launch_scan(const Shape& s, const void* K, const void* V, const Workspace& ws,
                        hipStream_t st) {
-  if (s.theta_groups > 0) {
-    const hipError_t e = s.dtype == 1 ? launch_theta_t<BF16>(s, K, ws, st)
-                                      : launch_theta_t<F32>(s, K, ws, st);
-    if (e != hipSuccess) return e;
-  }
   return s.dtype == 1 ? launch_scan_w<BF16>(s, K, V, ws, st) : launch_scan_w<F32>(s, K, V, ws, st);
 }
 

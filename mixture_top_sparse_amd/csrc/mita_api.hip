@@ -32,10 +32,19 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // stage profiler
 // ---------------------------------------------------------------------------
 
-enum Stage { kStagePool = 0, kStageScan, kStageMerge, kStageRoute, kStageBucket, kStageAttend,
-             kStageCount };
-const char* kStageNames[kStageCount] = {"pool", "landmark_scan", "landmark_merge", "route",
-                                        "bucket", "expert_attend"};
+enum Stage {
+  kStagePool = 0,
+  kStageThreshold,
+  kStageScan,
+  kStageMerge,
+  kStageRoute,
+  kStageBucket,
+  kStageAttend,
+  kStageCount
+};
+const char* kStageNames[kStageCount] = {"pool",           "landmark_threshold", "landmark_scan",
+                                        "landmark_merge", "route",              "bucket",
+                                        "expert_attend"};
 
 struct Profiler {
   bool enabled = false;
@@ -359,6 +368,11 @@ int mita_forward_ex(const void* Q, const void* K, const void* V, int dtype, int6
           StageTimer t(kStageBucket, ss->aux);
           ea = launch_bucket(s, route_out, ws, off_copy, perm_copy, ss->aux);
         }
+      }
+      if (e == hipSuccess) {
+        where = "landmark_threshold";
+        StageTimer t(kStageThreshold, st);
+        e = launch_threshold(s, K, ws, st);
       }
       if (e == hipSuccess) {
         where = "landmark_scan";

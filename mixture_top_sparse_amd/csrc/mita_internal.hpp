@@ -61,6 +61,8 @@ size_t plan_workspace(const Shape& s, Workspace* ws, char* base);
 // Kernel launchers; each returns the launch status.
 hipError_t launch_pool(const Shape& s, const void* Q, const Workspace& ws, void* ql_copy,
                        int64_t bh0, int64_t nbh, hipStream_t st);
+hipError_t launch_threshold(const Shape& s, const void* K, const Workspace& ws,
+                            hipStream_t st);  // no-op when theta_groups == 0
 hipError_t launch_scan(const Shape& s, const void* K, const void* V, const Workspace& ws,
                        hipStream_t st);
 hipError_t launch_merge(const Shape& s, const Workspace& ws, int32_t* idx_out, float* vl_copy,

@@ -37,10 +37,14 @@
  * innermost dimension contiguous; every pointer must be 16-byte aligned.
  *
  * Work space: allocated stream-ordered on `stream` (hipMallocAsync /
- * hipFreeAsync) for the duration of the call.  There is no host
- * synchronisation and no global state besides the per-device attribute
- * cache and the optional stage profiler, so calls on different streams may
- * run concurrently.
+ * hipFreeAsync) for the duration of the call.  Steps 3-4 run on a
+ * library-owned side stream of the current device (created on first use,
+ * default priority, never destroyed), forked from and joined back to
+ * `stream` with events, so they overlap step 2; the call returns with all
+ * its work ordered on `stream`.  There is no host synchronisation and no
+ * global state besides that side stream, the per-device attribute cache
+ * and the optional stage profiler; calls on different streams may run
+ * concurrently (their routing steps share the side stream).
  *
  * Errors: every function returns a status.  Arguments are validated on the
  * host before any HIP call; nothing is enqueued when validation fails.  A

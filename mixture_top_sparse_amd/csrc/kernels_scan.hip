@@ -9,13 +9,16 @@
 // FlashAttention-style pass (same page, implementation remark).  Here one
 // kernel streams K and V once:
 //
-//   k_scan  (split, head) blocks; wave w owns landmarks 16w..16w+15.
-//     per 64-key tile: S^T = K_tile Ql^T on MFMA (key rows x landmark
-//     columns), online softmax of scale*S with P.V on MFMA (P split into
-//     bf16 hi + lo parts), and an exact streaming top-k: scores above the
-//     landmark's current k-th best are appended to an LDS candidate buffer;
-//     a full buffer is sorted (wave bitonic network) and merged into the
-//     landmark's top list, which lives in registers (lane i = i-th best).
+//   k_scan_bf16 / k_scan_f32  (split, head) blocks; wave w owns landmarks
+//     16w..16w+15.  Per 64-key tile: S^T = K_tile Ql^T on MFMA (key rows x
+//     landmark columns), online softmax of scale*S with P.V on MFMA (bf16: P
+//     split into bf16 hi + lo parts), and an exact streaming top-k: scores
+//     above the landmark's current k-th best are appended to an LDS
+//     candidate buffer; a full buffer is sorted (wave bitonic network) and
+//     merged into the landmark's top list, which lives in registers (lane i
+//     = i-th best).  The bf16 kernel stages K and V tiles straight into LDS
+//     with the global-load-to-LDS DMA (no register staging, no transposing
+//     stores) and reads V^T operands with the LDS transpose read.
 //   k_merge (landmark, head) blocks: merges the per-split top lists and the
 //     per-split softmax states (log-sum-exp) into idx_out and Vl.
 //
@@ -23,7 +26,8 @@
 // so "higher score, then lower index" is a plain unsigned comparison.
 //
 // Roofline: HBM-bound; K and V are read once (2*N*d*e bytes per head); the
-// per-split partials add splits*mrows*(64*8 + 8 + 64*4) bytes per head.
+// per-split partials add about splits*mrows*(64*4 + 12) bytes per head plus
+// the (few) surviving top-list entries.
 #include "mita_device.hpp"
 #include "mita_internal.hpp"
 
@@ -36,23 +40,13 @@ namespace mita {
 template <class T>
 struct ScanTraits;
 
-// bf16: K rows in LDS (row stride 72 elements); V transposed in LDS
-// (V^T[d][key], row stride 68) so that P.V's A operand (8 keys of one d)
-// is two 8-byte reads.
+// bf16: the landmark query operand and the global-memory score (the
+// pre-threshold sample); the scan's tile staging is in k_scan_bf16.
 template <>
 struct ScanTraits<BF16> {
   using E = uint16_t;
-  static constexpr int KST = 72;
-  static constexpr int VST = 68;
   struct QReg {
     bf16x8 v[2];
-  };
-  template <int NT>
-  struct Tile {
-    static constexpr int CK = 512 / NT;  // 16-byte K chunks per thread
-    static constexpr int CV = 256 / NT;  // V row pairs per thread
-    u32x4 k[CK];
-    u32x4 v[CV][2];
   };
 
   __device__ static void load_q(QReg& q, const E* ql_row, bool ok, int g) {
@@ -63,61 +57,7 @@ struct ScanTraits<BF16> {
     }
   }
 
-  template <int NT>
-  __device__ static void load_tile(Tile<NT>& t, const E* Kh, const E* Vh, int64_t t0, int64_t kend,
-                                   int tid) {
-#pragma unroll
-    for (int j = 0; j < Tile<NT>::CK; ++j) {
-      const int c = tid + NT * j, row = c >> 3, col = c & 7;
-      const u32x4 z = {0, 0, 0, 0};
-      t.k[j] = (t0 + row < kend) ? *reinterpret_cast<const u32x4*>(Kh + (t0 + row) * kD + col * 8)
-                                 : z;
-    }
-#pragma unroll
-    for (int j = 0; j < Tile<NT>::CV; ++j) {
-      const int p = tid + NT * j, rp = p >> 3, col = p & 7;
-      const u32x4 z = {0, 0, 0, 0};
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int64_t row = t0 + 2 * rp + h;
-        t.v[j][h] = (row < kend) ? *reinterpret_cast<const u32x4*>(Vh + row * kD + col * 8) : z;
-      }
-    }
-  }
-
-  template <int NT>
-  __device__ static void store_tile(const Tile<NT>& t, E* klds, E* vlds, int tid) {
-#pragma unroll
-    for (int j = 0; j < Tile<NT>::CK; ++j) {
-      const int c = tid + NT * j, row = c >> 3, col = c & 7;
-      *reinterpret_cast<u32x4*>(klds + row * KST + col * 8) = t.k[j];
-    }
-#pragma unroll
-    for (int j = 0; j < Tile<NT>::CV; ++j) {
-      const int p = tid + NT * j, rp = p >> 3, col = p & 7;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t a = t.v[j][0][i >> 1], b = t.v[j][1][i >> 1];
-        const uint32_t word = (i & 1) ? ((a >> 16) | (b & 0xFFFF0000u))
-                                      : ((a & 0xFFFFu) | (b << 16));
-        *reinterpret_cast<uint32_t*>(vlds + (col * 8 + i) * VST + 2 * rp) = word;
-      }
-    }
-  }
-
-  // S^T block: keys 16kb..16kb+15 (rows) x the wave's 16 landmarks (columns)
-  __device__ static f32x4 score(const E* klds, int kb, const QReg& q, int c16, int g) {
-    f32x4 acc = {0, 0, 0, 0};
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const bf16x8 a =
-          as_bf16x8(*reinterpret_cast<const u32x4*>(klds + (16 * kb + c16) * KST + 32 * s + 8 * g));
-      acc = mfma_bf16(a, q.v[s], acc);
-    }
-    return acc;
-  }
-
-  // the same block straight from global memory (key row `row` of this lane)
+  // S^T block for key row `row` of this lane (columns: the wave's landmarks)
   __device__ static f32x4 score_global(const E* Kh, int64_t row, int64_t N, const QReg& q, int g) {
     f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
@@ -128,29 +68,6 @@ struct ScanTraits<BF16> {
       acc = mfma_bf16(a, q.v[s], acc);
     }
     return acc;
-  }
-
-  // O^T[d][lm] += V^T[d][keys] P^T[keys][lm] for the tile's 64 keys
-  __device__ static void pv(f32x4 (&acc)[4], const E* vlds, const float (&p)[4][4], int c16, int g) {
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      float pp[8];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pp[r] = p[2 * s2][r];
-        pp[4 + r] = p[2 * s2 + 1][r];
-      }
-      bf16x8 hi, lo;
-      split_hi_lo(pp, hi, lo);
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const E* row = vlds + (16 * dt + c16) * VST + 32 * s2 + 4 * g;
-        const bf16x8 a = join_bf16x8(*reinterpret_cast<const u32x2*>(row),
-                                     *reinterpret_cast<const u32x2*>(row + 16));
-        acc[dt] = mfma_bf16(a, hi, acc[dt]);
-        acc[dt] = mfma_bf16(a, lo, acc[dt]);
-      }
-    }
   }
 };
 
@@ -224,17 +141,47 @@ struct ScanTraits<F32> {
 };
 
 // ---------------------------------------------------------------------------
-// the scan kernel
+// the scan kernels
 // ---------------------------------------------------------------------------
 
-// Block: 256 threads stage each 64-key tile (double-buffered LDS, two tiles
-// of global loads in flight); waves 0..NW-1 each own 16 landmarks.
-template <class T, int NW>
-__global__ __launch_bounds__(256) void k_scan(
-    const typename T::elem* __restrict__ K, const typename T::elem* __restrict__ V,
-    const typename T::elem* __restrict__ Ql, const float* __restrict__ theta, int64_t N, int m,
-    int k, int chunk, int splits, float c2, uint64_t* __restrict__ part_keys,
+// Per-split partial results of one wave (16 landmarks): the top lists
+// (descending; only the nonzero entries are written, their number goes to
+// part_cnt), the softmax state (max in log2 units, sum) and the unnormalised
+// P.V accumulators O^T (lane: landmark column c16, rows d = 16dt + 4g + r).
+template <int NW>
+__device__ __forceinline__ void write_partials(const uint64_t (&top)[16], float M, float Lsum,
+                                               const f32x4 (&acc)[4], int64_t pbase, int w, int l,
+                                               int g, int lm, uint64_t* __restrict__ part_keys,
+                                               int32_t* __restrict__ part_cnt,
+                                               float* __restrict__ part_stats,
+                                               float* __restrict__ part_acc) {
+#pragma unroll
+  for (int L = 0; L < 16; ++L) {
+    const uint64_t nz = ballot(top[L] != 0ull);
+    if (top[L] != 0ull) part_keys[(pbase + w * 16 + L) * kTopCap + l] = top[L];
+    if (l == 0) part_cnt[pbase + w * 16 + L] = __popcll(nz);
+  }
+  Lsum = xor_sum(Lsum, 16);
+  Lsum = xor_sum(Lsum, 32);
+  if (g == 0) {
+    part_stats[(pbase + lm) * 2 + 0] = M;
+    part_stats[(pbase + lm) * 2 + 1] = Lsum;
+  }
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+    *reinterpret_cast<f32x4*>(part_acc + (pbase + lm) * kD + 16 * dt + 4 * g) = acc[dt];
+}
+
+// fp32 scan.  Block: 256 threads stage each 64-key tile through registers
+// (double-buffered LDS, two tiles of global loads in flight); waves
+// 0..NW-1 each own 16 landmarks.
+template <int NW>
+__global__ __launch_bounds__(256) void k_scan_f32(
+    const float* __restrict__ K, const float* __restrict__ V, const float* __restrict__ Ql,
+    const float* __restrict__ theta, int64_t N, int m, int k, int chunk, int splits, float c2,
+    uint64_t* __restrict__ part_keys, int32_t* __restrict__ part_cnt,
     float* __restrict__ part_stats, float* __restrict__ part_acc) {
+  using T = F32;
   using TR = ScanTraits<T>;
   using E = typename T::elem;
   constexpr int NT = 256;
@@ -391,18 +338,362 @@ __global__ __launch_bounds__(256) void k_scan(
       if ((need >> L) & 1u) merge_slot(L);
   }
 
-  const int64_t pbase = (bh * splits + split) * MROWS;
-#pragma unroll
-  for (int L = 0; L < 16; ++L) part_keys[(pbase + w * 16 + L) * kTopCap + l] = top[L];
-  Lsum = xor_sum(Lsum, 16);
-  Lsum = xor_sum(Lsum, 32);
-  if (g == 0) {
-    part_stats[(pbase + lm) * 2 + 0] = M;
-    part_stats[(pbase + lm) * 2 + 1] = Lsum;
+  write_partials<NW>(top, M, Lsum, acc, (bh * splits + split) * MROWS, w, l, g, lm, part_keys,
+                     part_cnt, part_stats, part_acc);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 scan: K and V tiles go straight from HBM into LDS (global-load-to-LDS
+// DMA, 16 bytes per lane into a fixed lane*16 slot of each 1 KiB piece).
+// Tile layout: 64 key rows of 128 bytes, 16-byte chunk c of row r stored at
+// chunk c ^ ((r >> 1) & 7), so that the 16 rows read by one MFMA operand
+// fetch fall on distinct banks.  V stays row-major; the P.V operand (8 keys
+// of one feature per lane) comes from the LDS transpose read, which hands
+// lane i of each 16-lane group element i of four 8-byte row pieces.
+// ---------------------------------------------------------------------------
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// s_waitcnt immediates (gfx9 encoding): vmcnt <= n, expcnt and lgkmcnt not
+// waited on.  Each staged tile is four requests per lane.
+constexpr int kWaitVm0 = 0x0F70, kWaitVm4 = 0x0F74;
+
+__device__ __forceinline__ int tile_off(int r, int c) {
+  return (r << 7) | ((c ^ ((r >> 1) & 7)) << 4);
+}
+
+// Byte offset, inside a tile of 64 rows, of the global 16-byte chunk that
+// lane l of wave w fetches for the wave's piece j (rows 16w + 8j .. +7):
+// the chunk that lands at the lane's fixed LDS slot under the swizzle.
+__device__ __forceinline__ uint32_t stage_src_off(int w, int j, int l) {
+  const int r = 16 * w + 8 * j + (l >> 3);
+  const int c = (l & 7) ^ ((r >> 1) & 7);
+  return static_cast<uint32_t>(r * 128 + c * 16);
+}
+
+// LDS accesses of the candidate path, written as assembly: the compiler
+// cannot tell these locations from the tile buffers that the in-flight DMA
+// writes, and would otherwise wait for every outstanding tile first.  They
+// complete before returning (explicit lgkmcnt wait).
+template <class P>
+__device__ __forceinline__ uint32_t lds_address(P* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)(p)));
+}
+__device__ __forceinline__ int lds_fetch_add1(uint32_t addr) {
+  int old;
+  const int one = 1;
+  __asm__ volatile("ds_add_rtn_u32 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)"
+                   : "=v"(old)
+                   : "v"(addr), "v"(one)
+                   : "memory");
+  return old;
+}
+__device__ __forceinline__ void lds_store_u64(uint32_t addr, uint64_t v) {
+  __asm__ volatile("ds_write_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(addr), "v"(v) : "memory");
+}
+
+// One global-load-to-LDS request: each lane's 16 bytes at gaddr land at
+// LDS address lds_base + 16 * lane (lds_base wave-uniform, in M0).  Written
+// as assembly so that the compiler inserts no waits of its own for it: the
+// scan orders every tile with explicit vmcnt waits and block barriers.
+__device__ __forceinline__ void dma16_to_lds(const void* gaddr, uint32_t lds_base) {
+  __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                   :
+                   : "v"(gaddr), "s"(lds_base)
+                   : "memory", "m0");
+}
+
+// Wave `w` (wave-uniform) requests its two 1 KiB pieces (rows 16w..16w+15)
+// of the K and V tiles starting at key t0 (LDS byte addresses kbuf, vbuf).
+// Full tiles use the tile base plus the lane's 32-bit offset; a tile that
+// runs past the head's last key re-reads key N-1 for the missing rows (their
+// scores are masked and their probabilities are 0).
+__device__ __forceinline__ void stage_tile_bf16(const uint16_t* __restrict__ Kh,
+                                                const uint16_t* __restrict__ Vh, int64_t t0,
+                                                int64_t N, uint32_t kbuf, uint32_t vbuf, int w,
+                                                uint32_t off0, uint32_t off1) {
+  const char* kt = reinterpret_cast<const char*>(Kh + t0 * kD);
+  const char* vt = reinterpret_cast<const char*>(Vh + t0 * kD);
+  uint32_t o0 = off0, o1 = off1;
+  if (t0 + kTileKeys > N) {
+    __asm__ volatile("" ::: "memory");  // keep this a branch
+    const uint32_t last = static_cast<uint32_t>((N - 1 - t0) * 128);  // byte offset of key N-1
+    if ((o0 & ~127u) > last) o0 = last + (o0 & 127u);
+    if ((o1 & ~127u) > last) o1 = last + (o1 & 127u);
   }
+  const uint32_t p0 = 2048u * static_cast<uint32_t>(w), p1 = p0 + 1024u;
+  dma16_to_lds(kt + o0, kbuf + p0);
+  dma16_to_lds(vt + o0, vbuf + p0);
+  dma16_to_lds(kt + o1, kbuf + p1);
+  dma16_to_lds(vt + o1, vbuf + p1);
+}
+
+// Block: 4 waves; waves 0..NW-1 each own 16 landmarks, all 4 stage tiles.
+// A ring of three LDS tile buffers: while one tile is scored, the next two
+// are in flight.  52 KiB of LDS and at most 168 VGPRs: three blocks per CU.
+template <int NW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_scan_bf16(
+    const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ Ql, const float* __restrict__ theta, int64_t N, int m, int k,
+    int splits, float c2, uint64_t* __restrict__ part_keys,
+    int32_t* __restrict__ part_cnt, float* __restrict__ part_stats,
+    float* __restrict__ part_acc) {
+  using TR = ScanTraits<BF16>;
+  constexpr int MROWS = NW * 16;
+  // ring slots: K tile (8 KiB), then V tile (8 KiB)
+  __shared__ __attribute__((aligned(16))) uint8_t b0[16384];
+  __shared__ __attribute__((aligned(16))) uint8_t b1[16384];
+  __shared__ __attribute__((aligned(16))) uint8_t b2[16384];
+  __shared__ uint64_t cand[MROWS][kCandCap];
+  __shared__ int lcnt[MROWS];  // candidates buffered per landmark (may overshoot kCandCap)
+
+  const int l = lane_id(), g = l >> 4, c16 = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(wave_id());
+  const bool computes = w < NW;
+  const int split = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int lm = w * 16 + c16;
+  const bool lm_ok = computes && lm < m;
+  // this block's tiles: split, split + splits, ... (all blocks of a head
+  // sweep the keys together, which keeps the DRAM access streams adjacent)
+  const int64_t ktiles = (N + kTileKeys - 1) / kTileKeys;
+  const int ntiles = static_cast<int>((ktiles - split + splits - 1) / splits);
+  const int64_t tstride = static_cast<int64_t>(splits) * kTileKeys;  // keys between my tiles
+  const int64_t kbeg = static_cast<int64_t>(split) * kTileKeys;
+  const uint16_t* Kh = K + bh * N * kD;
+  const uint16_t* Vh = V + bh * N * kD;
+
+  TR::QReg q;
+  TR::load_q(q, Ql + (bh * m + (lm_ok ? lm : 0)) * kD, lm_ok, g);
+  float th = (theta != nullptr && lm_ok) ? theta[bh * MROWS + lm] : -INFINITY;
+  // these loads complete before the first tile request: inside the loop the
+  // only outstanding requests are tiles, which the explicit waits below count
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __asm__ volatile("" ::: "memory");
+
+  // prologue: tiles 0 and 1 in flight (ring of three LDS tile buffers)
+  const uint32_t soff0 = stage_src_off(w, 0, l), soff1 = stage_src_off(w, 1, l);
+  const uint32_t a0 = lds_address(b0), a1 = lds_address(b1), a2 = lds_address(b2);
+  stage_tile_bf16(Kh, Vh, kbeg, N, a0, a0 + 8192, w, soff0, soff1);
+  if (ntiles > 1) stage_tile_bf16(Kh, Vh, kbeg + tstride, N, a1, a1 + 8192, w, soff0, soff1);
+  if (threadIdx.x < MROWS) lcnt[threadIdx.x] = 0;  // visible after the first barrier
+
+  float M = -INFINITY, Lsum = 0.f;
+  f32x4 acc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x4{0, 0, 0, 0};
+  uint64_t top[16];
+#pragma unroll
+  for (int L = 0; L < 16; ++L) top[L] = 0;
+  const uint32_t lcnt_addr = lds_address(&lcnt[lm < MROWS ? lm : 0]);
+  const uint32_t cand_addr = lds_address(&cand[lm < MROWS ? lm : 0][0]);
+
+  // lane-constant LDS offsets of the MFMA operands (the swizzle term of the
+  // rows an operand touches depends on the lane only)
+  const int kq0 = tile_off(c16, g), kq1 = tile_off(c16, 4 + g);  // + 2048 kb
+  int voff[4];  // + 4096 s2 + 2048 h
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
-    *reinterpret_cast<f32x4*>(part_acc + (pbase + lm) * kD + 16 * dt + 4 * g) = acc[dt];
+    voff[dt] = tile_off(4 * g + (c16 >> 2), 2 * dt + ((c16 & 3) >> 1)) + ((c16 & 1) << 3);
+
+  // merge landmark slot L's candidate buffer into its top list (whole wave)
+  auto merge_slot = [&](int L) __attribute__((always_inline)) {
+    const int n = min(lcnt[w * 16 + L], kCandCap);
+    uint64_t c = (l < n) ? cand[w * 16 + L][l] : 0ull;
+    c = wave_sort_desc_first<kCandCap>(c);
+    top[L] = wave_merge_top(top[L], c);
+    const uint64_t kth = uniform_read(top[L], k - 1);
+    if (l == 0) lcnt[w * 16 + L] = 0;
+    if (c16 == L && kth != 0ull) th = fmaxf(th, key_score(kth));
+  };
+
+  auto compute_tile = [&](const uint8_t* kl, const uint8_t* vl, int64_t t0)
+      __attribute__((always_inline)) {
+    float sc[4][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      f32x4 a = {0, 0, 0, 0};
+      a = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(kl + kq0 + 2048 * kb)), q.v[0], a);
+      a = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(kl + kq1 + 2048 * kb)), q.v[1], a);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[kb][r] = a[r];
+    }
+    if (t0 + kTileKeys > N) {  // ragged last tile of the head: drop keys past N
+      __asm__ volatile("" ::: "memory");  // keep this a branch (no if-conversion)
+      const int rel = static_cast<int>(N - t0) - 4 * g;  // key 16kb+4g+r valid iff 16kb+r < rel
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (16 * kb + r >= rel) sc[kb][r] = -INFINITY;
+    }
+    float kbmax[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      kbmax[kb] = fmaxf(fmaxf(sc[kb][0], sc[kb][1]), fmaxf(sc[kb][2], sc[kb][3]));
+    const float smax = fmaxf(fmaxf(kbmax[0], kbmax[1]), fmaxf(kbmax[2], kbmax[3]));
+
+    // ---- streaming top-k: only when some score beats its landmark's k-th best.
+    // One ballot per score position (uniform branches, rarely taken); lanes
+    // with a passing score take a buffer slot with an LDS atomic.  Entries
+    // that find their landmark's buffer full wait in `pend` for its merge.
+    if (ballot(lm_ok && smax > th)) {
+      uint32_t pend = 0;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        if (ballot(lm_ok && kbmax[kb] > th)) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const bool pass = lm_ok && sc[kb][r] > th;
+            if (ballot(pass)) {
+              if (pass) {
+                const int slot = lds_fetch_add1(lcnt_addr);
+                if (slot < kCandCap)
+                  lds_store_u64(cand_addr + 8 * slot,
+                                make_key(sc[kb][r], static_cast<uint32_t>(t0 + 16 * kb + 4 * g + r)));
+                else
+                  pend |= 1u << (4 * kb + r);
+              }
+            }
+          }
+        }
+      }
+      while (true) {  // rare: merge the full buffers, then place the pending entries
+        const uint64_t full = ballot(pend != 0u);
+        if (full == 0ull) break;
+        const uint32_t need =
+            static_cast<uint32_t>((full | (full >> 16) | (full >> 32) | (full >> 48)) & 0xFFFFull);
+#pragma unroll
+        for (int L = 0; L < 16; ++L)
+          if ((need >> L) & 1u) merge_slot(L);
+        if (pend) {
+          uint32_t left = 0;
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const uint32_t bit = 1u << (4 * kb + r);
+              if (pend & bit) {
+                float v = sc[kb][r];
+                __asm__ volatile("" : "+v"(v));  // keep the key work in this rare path
+                const int slot = lds_fetch_add1(lcnt_addr);
+                if (slot < kCandCap)
+                  lds_store_u64(cand_addr + 8 * slot,
+                                make_key(v, static_cast<uint32_t>(t0 + 16 * kb + 4 * g + r)));
+                else
+                  left |= bit;
+              }
+            }
+          pend = left;
+        }
+      }
+    }
+
+    // ---- online softmax (log2 domain, lazy rescale) and P.V ----
+    float mx = xor_max(smax, 16);
+    mx = xor_max(mx, 32) * c2;
+    if (ballot(mx > M)) {
+      const float Mn = fmaxf(M, mx);
+      const float alpha = fast_exp2(M - Mn);
+      Lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
+      M = Mn;
+    }
+    float p[4][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[kb][r] = fast_exp2(fmaf(sc[kb][r], c2, -M));
+        Lsum += p[kb][r];
+      }
+    // O^T[d][lm] += V^T[d][keys] P^T[keys][lm]; K-position 8g + j is key
+    // 32 s2 + 4g + j (j < 4) or 32 s2 + 16 + 4g + (j - 4)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      float pp[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pp[r] = p[2 * s2][r];
+        pp[4 + r] = p[2 * s2 + 1][r];
+      }
+      bf16x8 hi, lo;
+      split_hi_lo_pk(pp, hi, lo);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16*)(vl + voff[dt] + 4096 * s2));
+        const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16*)(vl + voff[dt] + 4096 * s2 + 2048));
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[dt] = mfma_bf16(a, hi, acc[dt]);
+        acc[dt] = mfma_bf16(a, lo, acc[dt]);
+      }
+    }
+  };
+
+  // Tile `it` sits in buffer it % 3.  Before using it, wait until at most
+  // the requests of the (up to one) younger tile are outstanding; the block
+  // barrier then makes every wave's pieces visible and frees buffer
+  // (it + 2) % 3, whose tile was used one step earlier, for tile it + 2.
+  auto step = [&](int it, const uint8_t* cur, uint32_t nxt) __attribute__((always_inline)) {
+    if (it + 1 < ntiles) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm4);
+    } else {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    }
+    // a plain barrier: __syncthreads() would add a workgroup release fence,
+    // i.e. a wait for every outstanding request, the younger tile's included
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    const int64_t t0 = kbeg + static_cast<int64_t>(it) * tstride;
+    if (it + 2 < ntiles)
+      stage_tile_bf16(Kh, Vh, t0 + 2 * tstride, N, nxt, nxt + 8192, w, soff0, soff1);
+    if (computes) compute_tile(cur, cur + 8192, t0);
+  };
+  for (int it = 0; it < ntiles; it += 3) {
+    step(it, b0, a2);
+    if (it + 1 >= ntiles) break;
+    step(it + 1, b1, a0);
+    if (it + 2 >= ntiles) break;
+    step(it + 2, b2, a1);
+  }
+  if (!computes) return;
+
+  // flush the candidate buffers: all 16 slots at once, network stage by
+  // network stage, so that the 16 independent cross-lane chains overlap
+  {
+    uint64_t c[16];
+#pragma unroll
+    for (int L = 0; L < 16; ++L) {
+      const int n = min(lcnt[w * 16 + L], kCandCap);
+      c[L] = (l < n) ? cand[w * 16 + L][l] : 0ull;
+    }
+#pragma unroll
+    for (int size = 2; size <= kCandCap; size <<= 1) {
+      const bool desc_block = (l & size) == 0;
+#pragma unroll
+      for (int stride = size >> 1; stride >= 1; stride >>= 1)
+#pragma unroll
+        for (int L = 0; L < 16; ++L) c[L] = cmpx_desc(c[L], stride, desc_block);
+    }
+#pragma unroll
+    for (int L = 0; L < 16; ++L) {
+      const uint64_t rev = lane_read(c[L], 63 - l);
+      top[L] = top[L] > rev ? top[L] : rev;
+    }
+#pragma unroll
+    for (int stride = 32; stride >= 1; stride >>= 1)
+#pragma unroll
+      for (int L = 0; L < 16; ++L) top[L] = cmpx_desc(top[L], stride, true);
+  }
+  write_partials<NW>(top, M, Lsum, acc, (bh * splits + split) * MROWS, w, l, g, lm, part_keys,
+                     part_cnt, part_stats, part_acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -489,36 +780,58 @@ __global__ __launch_bounds__(256) void k_theta_select(const uint64_t* __restrict
 // merge of the per-split partials
 // ---------------------------------------------------------------------------
 
-// grid (m, BH), 256 threads
+// grid (m, BH), 256 threads; wave w takes splits w, w+4, ... in batches of
+// 8 (loads first, then the arithmetic).  A split's top list only enters the
+// merge network when its best key beats the wave's current k-th best.
 __global__ __launch_bounds__(256) void k_merge(
-    const uint64_t* __restrict__ part_keys, const float* __restrict__ part_stats,
-    const float* __restrict__ part_acc, int m, int k, int mrows, int splits,
-    int32_t* __restrict__ idx_out, float* __restrict__ vl, float* __restrict__ vl_copy) {
+    const uint64_t* __restrict__ part_keys, const int32_t* __restrict__ part_cnt,
+    const float* __restrict__ part_stats, const float* __restrict__ part_acc, int m, int k,
+    int mrows, int splits, int32_t* __restrict__ idx_out, float* __restrict__ vl,
+    float* __restrict__ vl_copy) {
+  constexpr int kBatch = 8;
   __shared__ uint64_t tops[4][64];
   __shared__ float sacc[4][64];
   __shared__ float sM[4], sL[4];
-  const int l = lane_id(), w = wave_id(), lm = blockIdx.x;
+  const int l = lane_id(), lm = blockIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(wave_id());
   const int64_t bh = blockIdx.y;
+  const int64_t row0 = bh * splits * mrows + lm;  // partial row of split s: row0 + s * mrows
 
-  // top lists of splits w, w+4, ...
   uint64_t top = 0;
-  auto list_at = [&](int s) { return part_keys[((bh * splits + s) * mrows + lm) * kTopCap + l]; };
-  uint64_t nxt = (w < splits) ? list_at(w) : 0ull;
-  for (int s = w; s < splits; s += 4) {
-    const uint64_t cur = nxt;
-    if (s + 4 < splits) nxt = list_at(s + 4);
-    top = wave_merge_top(top, cur);
-  }
-  // softmax states of the same splits (lane = feature d)
   float Mw = -INFINITY, Lw = 0.f, aw = 0.f;
-  for (int s = w; s < splits; s += 4) {
-    const int64_t b = (bh * splits + s) * mrows + lm;
-    const float Ms = part_stats[b * 2], Ls = part_stats[b * 2 + 1], as = part_acc[b * kD + l];
-    const float Mn = fmaxf(Mw, Ms);
-    const float f0 = fast_exp2(Mw - Mn), f1 = fast_exp2(Ms - Mn);
-    Lw = Lw * f0 + Ls * f1;
-    aw = aw * f0 + as * f1;
-    Mw = Mn;
+  for (int s0 = w; s0 < splits; s0 += 4 * kBatch) {
+    int cnt[kBatch];
+    float Ms[kBatch], Ls[kBatch], as[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int s = s0 + 4 * u;
+      const int64_t r = row0 + static_cast<int64_t>(s) * mrows;
+      const bool ok = s < splits;
+      cnt[u] = ok ? part_cnt[r] : 0;
+      Ms[u] = ok ? part_stats[r * 2] : 0.f;
+      Ls[u] = ok ? part_stats[r * 2 + 1] : 0.f;
+      as[u] = ok ? part_acc[r * kD + l] : 0.f;
+    }
+    uint64_t lst[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {  // issued with the loads above; masked once cnt is in
+      const int s = s0 + 4 * u;
+      const int64_t r = row0 + static_cast<int64_t>(s < splits ? s : 0) * mrows;
+      lst[u] = part_keys[r * kTopCap + l];
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) lst[u] = (l < cnt[u]) ? lst[u] : 0ull;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (s0 + 4 * u >= splits) break;
+      const float Mn = fmaxf(Mw, Ms[u]);
+      const float f0 = fast_exp2(Mw - Mn), f1 = fast_exp2(Ms[u] - Mn);
+      Lw = Lw * f0 + Ls[u] * f1;
+      aw = aw * f0 + as[u] * f1;
+      Mw = Mn;
+      if (cnt[u] > 0 && uniform_read(lst[u], 0) > uniform_read(top, k - 1))
+        top = wave_merge_top(top, lst[u]);
+    }
   }
   tops[w][l] = top;
   sacc[w][l] = aw;
@@ -531,17 +844,21 @@ __global__ __launch_bounds__(256) void k_merge(
 
   uint64_t t = tops[0][l];
 #pragma unroll
-  for (int v = 1; v < 4; ++v) t = wave_merge_top(t, tops[v][l]);
+  for (int v = 1; v < 4; ++v) {
+    const uint64_t o = tops[v][l];
+    if (uniform_read(o, 0) > uniform_read(t, k - 1)) t = wave_merge_top(t, o);
+  }
   int32_t ix = (l < k) ? static_cast<int32_t>(key_index(t)) : INT32_MAX;
   ix = wave_sort_asc_i32(ix);
   if (l < k) idx_out[(bh * m + lm) * k + l] = ix;
 
-  float Mt = sM[0];
+  float Mt = -INFINITY;
 #pragma unroll
-  for (int v = 1; v < 4; ++v) Mt = fmaxf(Mt, sM[v]);
+  for (int v = 0; v < 4; ++v) Mt = fmaxf(Mt, sM[v]);
   float Lt = 0.f, at = 0.f;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
+    if (sM[v] == -INFINITY) continue;  // a wave that had no split
     const float f = fast_exp2(sM[v] - Mt);
     Lt += sL[v] * f;
     at += sacc[v][l] * f;
@@ -553,26 +870,22 @@ __global__ __launch_bounds__(256) void k_merge(
 
 // ---------------------------------------------------------------------------
 
-template <class T, int NW>
-static hipError_t launch_scan_t(const Shape& s, const void* K, const void* V, const Workspace& ws,
-                                hipStream_t st) {
-  using E = typename T::elem;
+template <int NW>
+static hipError_t launch_scan_nw(const Shape& s, const void* K, const void* V, const Workspace& ws,
+                                 hipStream_t st) {
   const float c2 = s.scale * kLog2e;
-  hipLaunchKernelGGL((k_scan<T, NW>), dim3(s.scan_splits, s.BH), dim3(256), 0, st,
-                     static_cast<const E*>(K), static_cast<const E*>(V),
-                     static_cast<const E*>(ws.ql), ws.theta, s.N, s.m, s.k, s.scan_chunk,
-                     s.scan_splits, c2, ws.part_keys, ws.part_stats, ws.part_acc);
-  return hipGetLastError();
-}
-
-template <class T>
-static hipError_t launch_scan_w(const Shape& s, const void* K, const void* V, const Workspace& ws,
-                                hipStream_t st) {
-  switch (s.scan_waves) {
-    case 1: return launch_scan_t<T, 1>(s, K, V, ws, st);
-    case 2: return launch_scan_t<T, 2>(s, K, V, ws, st);
-    default: return launch_scan_t<T, 4>(s, K, V, ws, st);
+  if (s.dtype == 1) {
+    hipLaunchKernelGGL((k_scan_bf16<NW>), dim3(s.scan_splits, s.BH), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V),
+                       static_cast<const uint16_t*>(ws.ql), ws.theta, s.N, s.m, s.k,
+                       s.scan_splits, c2, ws.part_keys, ws.part_cnt, ws.part_stats, ws.part_acc);
+  } else {
+    hipLaunchKernelGGL((k_scan_f32<NW>), dim3(s.scan_splits, s.BH), dim3(256), 0, st,
+                       static_cast<const float*>(K), static_cast<const float*>(V),
+                       static_cast<const float*>(ws.ql), ws.theta, s.N, s.m, s.k, s.scan_chunk,
+                       s.scan_splits, c2, ws.part_keys, ws.part_cnt, ws.part_stats, ws.part_acc);
   }
+  return hipGetLastError();
 }
 
 template <class T>
@@ -597,13 +910,18 @@ hipError_t launch_threshold(const Shape& s, const void* K, const Workspace& ws,
 
 hipError_t launch_scan(const Shape& s, const void* K, const void* V, const Workspace& ws,
                        hipStream_t st) {
-  return s.dtype == 1 ? launch_scan_w<BF16>(s, K, V, ws, st) : launch_scan_w<F32>(s, K, V, ws, st);
+  switch (s.scan_waves) {
+    case 1: return launch_scan_nw<1>(s, K, V, ws, st);
+    case 2: return launch_scan_nw<2>(s, K, V, ws, st);
+    default: return launch_scan_nw<4>(s, K, V, ws, st);
+  }
 }
 
 hipError_t launch_merge(const Shape& s, const Workspace& ws, int32_t* idx_out, float* vl_copy,
                         hipStream_t st) {
-  hipLaunchKernelGGL(k_merge, dim3(s.m, s.BH), dim3(256), 0, st, ws.part_keys, ws.part_stats,
-                     ws.part_acc, s.m, s.k, s.mrows, s.scan_splits, idx_out, ws.vl, vl_copy);
+  hipLaunchKernelGGL(k_merge, dim3(s.m, s.BH), dim3(256), 0, st, ws.part_keys, ws.part_cnt,
+                     ws.part_stats, ws.part_acc, s.m, s.k, s.mrows, s.scan_splits, idx_out, ws.vl,
+                     vl_copy);
   return hipGetLastError();
 }
 

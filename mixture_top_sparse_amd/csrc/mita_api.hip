@@ -120,12 +120,12 @@ int device_cus() {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // ---------------------------------------------------------------------------
-// per-device side stream: the routing branch (route + bucket) depends only on
-// the pooled landmarks, like the landmark branch (pre-threshold, scan,
-// merge), so the two run concurrently: fork after pooling, join before the
-// expert attention.  Default priority, non-blocking; one mutex per device
-// keeps each call's fork/record/wait sequence from interleaving with another
-// host thread's.
+// per-device side stream: bucketing depends only on the routes, and the
+// landmark branch (pre-threshold, scan, merge) only on the pooled landmarks,
+// so the two run concurrently: fork after routing, join before the expert
+// attention.  Default priority, non-blocking; one mutex per device keeps
+// each call's fork/record/wait sequence from interleaving with another host
+// thread's.
 // ---------------------------------------------------------------------------
 
 struct SideStream {
@@ -226,17 +226,27 @@ void derive(Shape& s, int cus) {
   s.kpad = static_cast<int>(round_up(s.k, 32));
   s.scan_waves = s.m <= 16 ? 1 : (s.m <= 32 ? 2 : 4);
   s.mrows = s.scan_waves * 16;
-  // landmark scan: about two blocks per CU, chunks of at least 512 keys
-  const int64_t target = 2 * static_cast<int64_t>(cus);
-  int64_t chunk = round_up(cdiv(s.N * s.BH, target), kTileKeys);
-  if (chunk < 512) chunk = 512;
-  if (chunk > round_up(s.N, kTileKeys)) chunk = round_up(s.N, kTileKeys);
-  s.scan_chunk = static_cast<int>(chunk);
-  s.scan_splits = static_cast<int>(cdiv(s.N, chunk));
+  // landmark scan.  bf16: three blocks per CU (the kernel's register and LDS
+  // budget), each taking every splits-th 64-key tile of its head, at least 8
+  // tiles per block.  fp32: one block per CU, contiguous chunks of at least
+  // 512 keys.
+  const int64_t ktiles = cdiv(s.N, kTileKeys);
+  if (s.dtype == MITA_BF16) {
+    int64_t splits = cdiv(3 * static_cast<int64_t>(cus), s.BH);
+    if (splits > ktiles / 8) splits = ktiles / 8;
+    if (splits < 1) splits = 1;
+    s.scan_splits = static_cast<int>(splits);
+    s.scan_chunk = 0;
+  } else {
+    int64_t chunk = round_up(cdiv(s.N * s.BH, static_cast<int64_t>(cus)), kTileKeys);
+    if (chunk < 512) chunk = 512;
+    if (chunk > round_up(s.N, kTileKeys)) chunk = round_up(s.N, kTileKeys);
+    s.scan_chunk = static_cast<int>(chunk);
+    s.scan_splits = static_cast<int>(cdiv(s.N, chunk));
+  }
   s.pool_splits = static_cast<int>(cdiv(max_window(s), kPoolChunk));
   // top-k pre-threshold: sample up to a quarter of the key tiles (at most
   // 1024 per head), only when there are at least max(k, 64) of them
-  const int64_t ktiles = cdiv(s.N, kTileKeys);
   int64_t groups = ktiles / 4;
   if (groups > 1024) groups = 1024;
   groups = groups / kThetaTilesPerBlock * kThetaTilesPerBlock;
@@ -272,6 +282,7 @@ size_t plan_workspace(const Shape& s, Workspace* ws, char* base) {
   }
   const size_t parts = BH * s.scan_splits * s.mrows;
   ws->part_keys = reinterpret_cast<uint64_t*>(take(parts * kTopCap * sizeof(uint64_t)));
+  ws->part_cnt = reinterpret_cast<int32_t*>(take(parts * sizeof(int32_t)));
   ws->part_stats = reinterpret_cast<float*>(take(parts * 2 * sizeof(float)));
   ws->part_acc = reinterpret_cast<float*>(take(parts * kD * sizeof(float)));
   ws->vl = reinterpret_cast<float*>(take(BH * s.m * kD * sizeof(float)));
@@ -345,7 +356,14 @@ int mita_forward_ex(const void* Q, const void* K, const void* V, int dtype, int6
       StageTimer t(kStagePool, st);
       e = launch_pool(s, Q, ws, ql_copy, 0, s.BH, st);
     }
-    // routing branch on the side stream, landmark branch on the caller's
+    // routing on the caller's stream (run beside the landmark scan it would
+    // compete for bandwidth and CUs), then bucketing on the side stream, which
+    // overlaps the latency-bound bucketing with the landmark branch
+    if (e == hipSuccess) {
+      where = "route";
+      StageTimer t(kStageRoute, st);
+      e = launch_route(s, Q, ws, route_out, 0, s.BH, st);
+    }
     SideStream* ss = (e == hipSuccess) ? side_stream() : nullptr;
     if (e == hipSuccess && ss == nullptr) {
       e = hipErrorInvalidResourceHandle;
@@ -358,16 +376,9 @@ int mita_forward_ex(const void* Q, const void* K, const void* V, int dtype, int6
       const bool forked = ea == hipSuccess;
       const char* where_aux = "fork";
       if (forked) {
-        where_aux = "route";
-        {
-          StageTimer t(kStageRoute, ss->aux);
-          ea = launch_route(s, Q, ws, route_out, 0, s.BH, ss->aux);
-        }
-        if (ea == hipSuccess) {
-          where_aux = "bucket";
-          StageTimer t(kStageBucket, ss->aux);
-          ea = launch_bucket(s, route_out, ws, off_copy, perm_copy, ss->aux);
-        }
+        where_aux = "bucket";
+        StageTimer t(kStageBucket, ss->aux);
+        ea = launch_bucket(s, route_out, ws, off_copy, perm_copy, ss->aux);
       }
       if (e == hipSuccess) {
         where = "landmark_threshold";

@@ -118,11 +118,36 @@ __device__ __forceinline__ uint64_t lane_read(uint64_t v, int src_lane) {
   uint32_t hi = lane_read(static_cast<uint32_t>(v >> 32), src_lane);
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
+// Lanes l and l^16 (l^32) exchanged on the VALU with the gfx950 row/half
+// swaps: v_permlane16_swap leaves each lane with its own value and that of
+// lane l^16 (one in each result), v_permlane32_swap the same for l^32.  The
+// max or sum of the pair is then the same number in both lanes.
+__device__ __forceinline__ void xor_pair(float v, int mask, float& a, float& b) {
+  const uint32_t u = __float_as_uint(v);
+  if (mask == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  } else if (mask == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  } else {
+    const bool lower = (lane_id() & mask) == 0;
+    const float o = lane_read(v, lane_id() ^ mask);
+    a = lower ? v : o;
+    b = lower ? o : v;
+  }
+}
 __device__ __forceinline__ float xor_max(float v, int mask) {
-  return fmaxf(v, lane_read(v, lane_id() ^ mask));
+  float a, b;
+  xor_pair(v, mask, a, b);
+  return fmaxf(a, b);
 }
 __device__ __forceinline__ float xor_sum(float v, int mask) {
-  return v + lane_read(v, lane_id() ^ mask);
+  float a, b;
+  xor_pair(v, mask, a, b);
+  return a + b;
 }
 
 // wave-uniform read of lane `l`'s value
@@ -135,7 +160,7 @@ __device__ __forceinline__ uint64_t uniform_read(uint64_t v, int l) {
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
-__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+__device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
 // number of set bits of `mask` in lanes below the calling lane
 __device__ __forceinline__ uint32_t count_below(uint64_t mask) {
@@ -160,6 +185,21 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v) {
   const int l = lane_id();
 #pragma unroll
   for (int size = 2; size <= 64; size <<= 1) {
+    const bool desc_block = (l & size) == 0;
+#pragma unroll
+    for (int stride = size >> 1; stride >= 1; stride >>= 1) v = cmpx_desc(v, stride, desc_block);
+  }
+  return v;
+}
+
+// sort 64 keys of which only lanes 0..W-1 may be nonzero (W a power of two):
+// the network's stages up to size W sort lanes 0..W-1 descending and leave
+// the zero lanes zero, so the whole wave is then in descending order
+template <int W>
+__device__ __forceinline__ uint64_t wave_sort_desc_first(uint64_t v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int size = 2; size <= W; size <<= 1) {
     const bool desc_block = (l & size) == 0;
 #pragma unroll
     for (int stride = size >> 1; stride >= 1; stride >>= 1) v = cmpx_desc(v, stride, desc_block);
@@ -246,6 +286,23 @@ __device__ __forceinline__ void split_hi_lo(const float (&p)[8], bf16x8& hi, bf1
     const __bf16 h = f32_to_bf16(p[i]);
     hi[i] = h;
     lo[i] = f32_to_bf16(p[i] - static_cast<float>(h));
+  }
+}
+
+// the same split with pairwise conversions (one v_cvt_pk_bf16_f32 per two
+// values); hi and lo are identical to split_hi_lo's
+__device__ __forceinline__ void split_hi_lo_pk(const float (&p)[8], bf16x8& hi, bf16x8& lo) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const bf16x2 h = __builtin_convertvector(f32x2{p[i], p[i + 1]}, bf16x2);
+    const f32x2 hf = __builtin_convertvector(h, f32x2);
+    const bf16x2 r = __builtin_convertvector(f32x2{p[i] - hf[0], p[i + 1] - hf[1]}, bf16x2);
+    hi[i] = h[0];
+    hi[i + 1] = h[1];
+    lo[i] = r[0];
+    lo[i + 1] = r[1];
   }
 }
 

@@ -11,12 +11,13 @@ constexpr int kD = 64;           // head dimension supported by this build
 constexpr int kMaxM = 64;        // landmarks (= experts)
 constexpr int kMaxK = 64;        // keys per expert
 constexpr int kTopCap = 64;      // per-split top list length (one key per lane)
+constexpr int kCandCap = 8;      // candidate buffer per landmark (bf16 landmark scan)
 constexpr int kTileKeys = 64;    // keys per landmark-scan tile
 constexpr int kRouteSeg = 1024;  // queries per routing/bucketing segment
 constexpr int kAttendTile = 64;  // queries per expert-attention tile
 constexpr int kAttendMaxTpb = 16;  // tiles per expert-attention work item, at most
 constexpr int kPoolChunk = 2048; // tokens per pooling partial sum
-constexpr int kThetaTilesPerBlock = 4;  // sample tiles per top-k pre-threshold block
+constexpr int kThetaTilesPerBlock = 1;  // sample tiles per top-k pre-threshold block
 
 struct Shape {
   int64_t B = 0, H = 0, BH = 0, N = 0;
@@ -29,7 +30,7 @@ struct Shape {
   int kpad = 0;        // k rounded up to 32
   int scan_waves = 0;  // 1, 2 or 4 waves of 16 landmarks
   int mrows = 0;       // scan_waves * 16
-  int scan_chunk = 0;  // keys per landmark-scan block
+  int scan_chunk = 0;  // keys per landmark-scan block (fp32; the bf16 scan interleaves tiles)
   int scan_splits = 0;
   int pool_splits = 0; // partial sums per landmark window
   int theta_groups = 0;// sample tiles for the top-k pre-threshold (0: off)
@@ -44,7 +45,9 @@ struct Workspace {
   void* ql = nullptr;            // [BH][m][64] landmark queries (input type)
   uint64_t* gmax = nullptr;      // [BH][m][theta_groups] per-sample-tile maximum keys
   float* theta = nullptr;        // [BH][mrows] top-k pre-threshold (nullptr: off)
-  uint64_t* part_keys = nullptr; // [BH][splits][mrows][64] per-split top lists
+  uint64_t* part_keys = nullptr; // [BH][splits][mrows][64] per-split top lists (first
+                                 //   part_cnt entries valid, descending)
+  int32_t* part_cnt = nullptr;   // [BH][splits][mrows] entries in each per-split top list
   float* part_stats = nullptr;   // [BH][splits][mrows][2] (max in log2 units, sum)
   float* part_acc = nullptr;     // [BH][splits][mrows][64] unnormalised P.V
   float* vl = nullptr;           // [BH][m][64] landmark values fp32

@@ -24,6 +24,10 @@
 
 namespace mita {
 
+constexpr int kAttendWaves = 8;       // bf16 expert attention: waves per block
+constexpr int kAttendThreads = 64 * kAttendWaves;
+constexpr int kOStageStride = 68;     // floats per staged output row (bank spread)
+
 template <class T, int MPAD, int KPAD>
 struct AttendLds;
 
@@ -36,6 +40,7 @@ struct AttendLds<BF16, MPAD, KPAD> {
   alignas(16) uint16_t vc[kD * VCST];  // fp16 2^-s * Vl^T
   alignas(16) uint16_t vr[kD * VRST];  // fp16 2^-s * V^T of the expert's rows
   alignas(16) int32_t perm[kAttendTile * kAttendMaxTpb];  // the work item's query indices
+  alignas(16) float ostage[kAttendWaves][16 * kOStageStride];  // per-wave output rows
   uint32_t vmax;            // bits of the largest |value| staged (>= 0)
 };
 
@@ -142,7 +147,7 @@ __device__ int stage_bf16(AttendLds<BF16, MPAD, KPAD>& S, const uint16_t* __rest
   atomicMax(&S.vmax, __float_as_uint(vmax));
 
   // pair keys: Ql rows then the expert's K rows (zero rows for padding)
-  for (int c = tid; c < NP * 8; c += 256) {
+  for (int c = tid; c < NP * 8; c += kAttendThreads) {
     const int row = c >> 3, cc = c & 7;
     u32x4 v = z;
     if (row < MPAD) {
@@ -179,8 +184,8 @@ __device__ int stage_bf16(AttendLds<BF16, MPAD, KPAD>& S, const uint16_t* __rest
 
 // 16 queries of one wave (lane column c16 = query) against the staged expert
 template <int MPAD, int KPAD, bool FULL>
-__device__ __forceinline__ void attend_queries_bf16(const AttendLds<BF16, MPAD, KPAD>& S,
-                                                    const bf16x8 (&qb)[2], bool qok, int64_t q,
+__device__ __forceinline__ void attend_queries_bf16(AttendLds<BF16, MPAD, KPAD>& S,
+                                                    const bf16x8 (&qb)[2], int sl0, int nq,
                                                     int m, int k, float c2, float oscale,
                                                     float* __restrict__ out_h) {
   using L = AttendLds<BF16, MPAD, KPAD>;
@@ -251,11 +256,22 @@ __device__ __forceinline__ void attend_queries_bf16(const AttendLds<BF16, MPAD, 
                                     *reinterpret_cast<const u32x2*>(rv + 16)), pf, acc[dt]);
     }
   }
-  if (qok) {
-    const float f = oscale * __builtin_amdgcn_rcpf(lsum);  // lsum >= 1
+  // Output rows go through this wave's LDS stage: lane (query c16, g) holds
+  // features 16dt + 4g .. +3; read back, 16 lanes cover one 256-byte row, so
+  // each store instruction writes four complete rows.
+  float* st = S.ostage[wave_id()];
+  const float f = oscale * __builtin_amdgcn_rcpf(lsum);  // lsum >= 1
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-      *reinterpret_cast<f32x4*>(out_h + q * kD + 16 * dt + 4 * g) = acc[dt] * f;
+  for (int dt = 0; dt < 4; ++dt)
+    *reinterpret_cast<f32x4*>(st + c16 * kOStageStride + 16 * dt + 4 * g) = acc[dt] * f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = 4 * j + (l >> 4);
+    if (sl0 + row < nq) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(st + row * kOStageStride + 4 * (l & 15));
+      const int64_t q = S.perm[sl0 + row];
+      *reinterpret_cast<f32x4*>(out_h + q * kD + 4 * (l & 15)) = v;
+    }
   }
 }
 
@@ -274,8 +290,9 @@ __device__ void attend_bf16(AttendLds<BF16, MPAD, KPAD>& S, const uint16_t* __re
   const u32x4 z = {0, 0, 0, 0};
   const int nq = ti.qe - ti.qb;                // queries in this item (<= 64 * tpb)
   const int nsub = (nq + 15) / 16;             // 16-query sub-tiles
-  // wave w handles sub-tiles w, w+4, w+8, ...; slot of sub-tile i in the item
-  auto slot = [&](int i) { return 16 * (w + 4 * i) + c16; };
+  // wave w handles sub-tiles w, w+W, w+2W, ...; slot of sub-tile i in the item
+  constexpr int W = kAttendWaves;
+  auto slot = [&](int i) { return 16 * (w + W * i) + c16; };
   auto load_q = [&](int64_t q, bf16x8 (&qb)[2]) {
 #pragma unroll
     for (int s = 0; s < 2; ++s)
@@ -289,22 +306,22 @@ __device__ void attend_bf16(AttendLds<BF16, MPAD, KPAD>& S, const uint16_t* __re
     const int64_t q = (sl < nq && ti.qb + sl < N) ? clamp_index(ph[ti.qb + sl], N) : -1;
     load_q(q, ring[j]);
   }
-  for (int c = tid; c < nq; c += 256) S.perm[c] = static_cast<int32_t>(clamp_index(ph[ti.qb + c], N));
+  for (int c = tid; c < nq; c += kAttendThreads)
+    S.perm[c] = static_cast<int32_t>(clamp_index(ph[ti.qb + c], N));
   const int sh = stage_bf16<MPAD, KPAD>(S, K, V, Ql, vl, idx + (bh * m + ti.e) * k, N, m, k, bh);
   const float oscale = exp2i(sh);
   __syncthreads();
 
-  for (int i0 = 0; w + 4 * i0 < nsub; i0 += D) {
+  for (int i0 = 0; w + W * i0 < nsub; i0 += D) {
 #pragma unroll
     for (int j = 0; j < D; ++j) {
       const int i = i0 + j;
-      if (w + 4 * i >= nsub) break;
+      if (w + W * i >= nsub) break;
       // re-read the staged operands from LDS for every sub-tile instead of
       // pinning all of them in registers across the loop (keeps occupancy)
       __asm__ volatile("" ::: "memory");
-      const int sl = slot(i);
-      const int64_t q = sl < nq ? static_cast<int64_t>(S.perm[sl]) : -1;
-      attend_queries_bf16<MPAD, KPAD, FULL>(S, ring[j], q >= 0, q, m, k, c2, oscale, out_h);
+      attend_queries_bf16<MPAD, KPAD, FULL>(S, ring[j], 16 * (w + W * i), nq, m, k, c2, oscale,
+                                            out_h);
       const int sn = slot(i + D);  // refill this slot with sub-tile i + D
       load_q(sn < nq ? static_cast<int64_t>(S.perm[sn]) : -1, ring[j]);
     }
@@ -400,10 +417,11 @@ __device__ void attend_f32(AttendLds<F32, MPAD, KPAD>& S, const float* __restric
   }
 }
 
-// grid (work items, BH), 256 threads.  bf16: register budget for 4 waves per
-// SIMD (LDS allows 4 blocks per CU); fp32 (small problems): default budget.
+// grid (work items, BH).  bf16: 512 threads, register budget for 4 waves
+// per SIMD (LDS allows 2 blocks per CU); fp32 (small problems): 256 threads,
+// default budget.
 template <int MPAD, int KPAD, bool FULL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_attend_bf16(
+__global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_attend_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ Ql, const float* __restrict__ vl, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets,
@@ -437,10 +455,12 @@ struct AttendKernel;
 template <int MPAD, int KPAD, bool FULL>
 struct AttendKernel<BF16, MPAD, KPAD, FULL> {
   static constexpr auto fn = k_attend_bf16<MPAD, KPAD, FULL>;
+  static constexpr int threads = kAttendThreads;
 };
 template <int MPAD, int KPAD, bool FULL>
 struct AttendKernel<F32, MPAD, KPAD, FULL> {
   static constexpr auto fn = k_attend_f32<MPAD, KPAD, FULL>;
+  static constexpr int threads = 256;
 };
 
 template <class T, int MPAD, int KPAD>
@@ -450,7 +470,7 @@ static hipError_t launch_attend_t(const Shape& s, const void* Q, const void* K, 
   using E = typename T::elem;
   auto kern = (s.m == MPAD && s.k == KPAD) ? AttendKernel<T, MPAD, KPAD, true>::fn
                                            : AttendKernel<T, MPAD, KPAD, false>::fn;
-  hipLaunchKernelGGL(kern, dim3(s.attend_items, s.BH), dim3(256), 0, st,
+  hipLaunchKernelGGL(kern, dim3(s.attend_items, s.BH), dim3(AttendKernel<T, MPAD, KPAD, true>::threads), 0, st,
                      static_cast<const E*>(Q), static_cast<const E*>(K), static_cast<const E*>(V),
                      static_cast<const E*>(ws.ql), ws.vl, idx, ws.perm,
                      ws.offsets, ws.item_start, s.attend_tpb, s.N, s.m, s.k, s.scale * kLog2e,

@@ -37,14 +37,15 @@
  * innermost dimension contiguous; every pointer must be 16-byte aligned.
  *
  * Work space: allocated stream-ordered on `stream` (hipMallocAsync /
- * hipFreeAsync) for the duration of the call.  Step 4 runs on a
- * library-owned side stream of the current device (created on first use,
- * default priority, never destroyed), forked from and joined back to
- * `stream` with events, so it overlaps step 2; the call returns with all
- * its work ordered on `stream`.  There is no host synchronisation and no
+ * hipFreeAsync) for the duration of the call.  The sampled top-k
+ * pre-threshold of step 2 and step 4 run on a library-owned side stream of
+ * the current device (created on first use, default priority, never
+ * destroyed), forked from and joined back to `stream` with events, so they
+ * overlap steps 3 and 2; the call returns with all its work ordered on
+ * `stream`.  There is no host synchronisation and no
  * global state besides that side stream, the per-device attribute cache
  * and the optional stage profiler; calls on different streams may run
- * concurrently (their bucketing steps share the side stream).
+ * concurrently (their side-stream steps share the side stream).
  *
  * Errors: every function returns a status.  Arguments are validated on the
  * host before any HIP call; nothing is enqueued when validation fails.  A
@@ -143,8 +144,8 @@ int mita_version(void);
 /*
  * Stage profiler (for measurement; off by default).  While enabled, each
  * forward call records a pair of HIP events around every stage on the
- * stream the stage runs on (bucketing runs on a library-owned side
- * stream).  Stages, in order: pool, landmark_threshold (the sampled
+ * stream the stage runs on (landmark_threshold and bucket run on a
+ * library-owned side stream).  Stages, in order: pool, landmark_threshold (the sampled
  * top-k pre-threshold), landmark_scan, landmark_merge, route, bucket,
  * expert_attend; each of landmark_scan, route and expert_attend is a single
  * kernel launch.  mita_profile_read() waits for the recorded events and

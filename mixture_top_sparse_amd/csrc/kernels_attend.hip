@@ -270,7 +270,9 @@ __device__ __forceinline__ void attend_queries_bf16(AttendLds<BF16, MPAD, KPAD>&
     if (sl0 + row < nq) {
       const f32x4 v = *reinterpret_cast<const f32x4*>(st + row * kOStageStride + 4 * (l & 15));
       const int64_t q = S.perm[sl0 + row];
-      *reinterpret_cast<f32x4*>(out_h + q * kD + 4 * (l & 15)) = v;
+      // non-temporal: the rows are not read again here, and written-through
+      // lines do not leave dirty cache lines for the next kernel to flush
+      __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(out_h + q * kD + 4 * (l & 15)));
     }
   }
 }

@@ -64,13 +64,36 @@ __global__ __launch_bounds__(256) void k_pool_partial(const typename T::elem* __
   const int col = threadIdx.x & 7, row = threadIdx.x >> 3;
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   const typename T::elem* Qh = Q + bh * N * kD;
-#pragma unroll 8
-  for (int64_t t = t_beg + row; t < t_end; t += 32) {
-    const int64_t tok = (r0 + t / wc) * gw + (c0 + t % wc);
-    float v[8];
-    load8(Qh + tok * kD + col * 8, v);
+  if (r1 - r0 == 1) {
+    // one row segment (every 1D window): tokens are contiguous, 4 loads in
+    // flight per thread
+    const typename T::elem* p = Qh + (r0 * gw + c0 + t_beg + row) * kD + col * 8;
+    const int n = t_beg + row < t_end ? static_cast<int>((t_end - t_beg - row + 31) / 32) : 0;
+    int j = 0;
+    for (; j + 4 <= n; j += 4) {
+      float v[4][8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] += static_cast<double>(v[j]);
+      for (int u = 0; u < 4; ++u) load8(p + static_cast<int64_t>(j + u) * 32 * kD, v[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += static_cast<double>(v[u][e]);
+    }
+    for (; j < n; ++j) {
+      float v[8];
+      load8(p + static_cast<int64_t>(j) * 32 * kD, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += static_cast<double>(v[e]);
+    }
+  } else {
+    // 2D window (few tokens): token position from the window-local index
+    for (int64_t t = t_beg + row; t < t_end; t += 32) {
+      const int64_t tok = (r0 + t / wc) * gw + (c0 + t % wc);
+      float v[8];
+      load8(Qh + tok * kD + col * 8, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += static_cast<double>(v[e]);
+    }
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) red[row][col * 8 + j] = acc[j];

@@ -106,8 +106,11 @@ __global__ __launch_bounds__(256) void k_route(const typename T::elem* __restric
   __shared__ int cnt[kMaxM];
   __shared__ __attribute__((aligned(16))) E qls[kMaxM * kQlStride];
   const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
-  const int seg = blockIdx.x;
-  const int64_t bh = bh0 + blockIdx.y;
+  // blocks run from the end of the heads' queries backwards: pooling has just
+  // read Q front to back, so the first rows routed are still in the last-level
+  // cache
+  const int seg = nseg - 1 - static_cast<int>(blockIdx.x);
+  const int64_t bh = bh0 + (gridDim.y - 1 - blockIdx.y);
   if (threadIdx.x < kMaxM) cnt[threadIdx.x] = 0;
   {  // the landmark queries once per block, zero rows past m
     constexpr int CH = 16 / sizeof(E);  // elements per 16-byte chunk
@@ -170,15 +173,8 @@ __global__ __launch_bounds__(256) void k_route(const typename T::elem* __restric
       }
       // combine the 4 lane groups holding this query: larger value, then
       // lower landmark index
-#pragma unroll
-      for (int mask = 16; mask <= 32; mask <<= 1) {
-        const float ob = lane_read(best, l ^ mask);
-        const int oi = static_cast<int>(lane_read(static_cast<uint32_t>(bi), l ^ mask));
-        if (ob > best || (ob == best && oi < bi)) {
-          best = ob;
-          bi = oi;
-        }
-      }
+      xor_argmax(best, bi, 16);
+      xor_argmax(best, bi, 32);
       if (G == g) rsel = bi;  // lane l = 16G + c16 keeps query qw + 64 it + l
     }
     const int64_t q = qw + 64 * it + l;
@@ -262,14 +258,23 @@ __global__ __launch_bounds__(64) void k_bucket_scatter(
       if (offsets_copy) offsets_copy[bh * (m + 1) + m] = incl;
     }
   }
+  // all of the segment's routes in flight at once
+  constexpr int NG = kRouteSeg / 64;
+  int rr[NG];
+#pragma unroll
+  for (int it = 0; it < NG; ++it) {
+    const int64_t q = static_cast<int64_t>(seg) * kRouteSeg + 64 * it + l;
+    rr[it] = q < N ? route[bh * N + q] : 0;
+  }
   if (l < m) base[l] = (incl - c) + colpre[(bh * m + l) * nseg + seg];
-  __syncthreads();
+  // one wave: its LDS accesses complete in program order, no barriers needed
   const uint64_t below = (l == 0) ? 0ull : (~0ull >> (64 - l));
-  for (int it = 0; it < kRouteSeg / 64; ++it) {
+#pragma unroll
+  for (int it = 0; it < NG; ++it) {
     const int64_t q = static_cast<int64_t>(seg) * kRouteSeg + 64 * it + l;
     if (static_cast<int64_t>(seg) * kRouteSeg + 64 * it >= N) break;
     const bool ok = q < N;
-    int r = ok ? route[bh * N + q] : 0;
+    int r = rr[it];
     r = r < 0 ? 0 : (r >= m ? m - 1 : r);  // routes come from k_route; clamp defensively
     uint64_t same = ballot(ok);
 #pragma unroll
@@ -285,9 +290,7 @@ __global__ __launch_bounds__(64) void k_bucket_scatter(
       perm[bh * N + pos] = static_cast<int32_t>(q);
       if (perm_copy) perm_copy[bh * N + pos] = static_cast<int32_t>(q);
     }
-    __syncthreads();  // the reads of base[] above complete before the update
-    if (ok && rank == total - 1) base[r] += total;
-    __syncthreads();
+    if (ok && rank == total - 1) base[r] += total;  // after every lane's read of base[r]
   }
 }
 

@@ -132,7 +132,7 @@ struct SideStream {
   std::mutex mu;
   bool ready = false;
   hipStream_t aux = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr, routed = nullptr, thr_done = nullptr;
 };
 SideStream g_side[64];
 
@@ -142,9 +142,16 @@ SideStream* side_stream() {
   SideStream& ss = g_side[dev];
   std::lock_guard<std::mutex> lk(ss.mu);
   if (!ss.ready) {
-    if (hipStreamCreateWithFlags(&ss.aux, hipStreamNonBlocking) != hipSuccess) return nullptr;
-    if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess) return nullptr;
-    if (hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) return nullptr;
+    if (ss.aux == nullptr && hipStreamCreateWithFlags(&ss.aux, hipStreamNonBlocking) != hipSuccess) {
+      ss.aux = nullptr;
+      return nullptr;
+    }
+    for (hipEvent_t* ev : {&ss.fork, &ss.join, &ss.routed, &ss.thr_done}) {
+      if (*ev == nullptr && hipEventCreateWithFlags(ev, hipEventDisableTiming) != hipSuccess) {
+        *ev = nullptr;  // kept for the next attempt; the rest stay created
+        return nullptr;
+      }
+    }
     ss.ready = true;
   }
   return &ss;
@@ -356,14 +363,12 @@ int mita_forward_ex(const void* Q, const void* K, const void* V, int dtype, int6
       StageTimer t(kStagePool, st);
       e = launch_pool(s, Q, ws, ql_copy, 0, s.BH, st);
     }
-    // routing on the caller's stream (run beside the landmark scan it would
-    // compete for bandwidth and CUs), then bucketing on the side stream, which
-    // overlaps the latency-bound bucketing with the landmark branch
-    if (e == hipSuccess) {
-      where = "route";
-      StageTimer t(kStageRoute, st);
-      e = launch_route(s, Q, ws, route_out, 0, s.BH, st);
-    }
+    // Two branches after pooling.  Caller's stream: route, landmark scan,
+    // merge.  Side stream: the sampled top-k pre-threshold (beside routing;
+    // the scan waits for it), then bucketing (after routing, beside the
+    // scan).  The routing kernel does not run beside the scan: the two would
+    // compete for bandwidth and CUs, and the scan's long blocks would start
+    // late.
     SideStream* ss = (e == hipSuccess) ? side_stream() : nullptr;
     if (e == hipSuccess && ss == nullptr) {
       e = hipErrorInvalidResourceHandle;
@@ -376,14 +381,41 @@ int mita_forward_ex(const void* Q, const void* K, const void* V, int dtype, int6
       const bool forked = ea == hipSuccess;
       const char* where_aux = "fork";
       if (forked) {
+        where_aux = "landmark_threshold";
+        StageTimer t(kStageThreshold, ss->aux);
+        ea = launch_threshold(s, K, ws, ss->aux);
+      }
+      bool thr_recorded = false;
+      if (forked && ea == hipSuccess) {
+        ea = hipEventRecord(ss->thr_done, ss->aux);
+        thr_recorded = ea == hipSuccess;
+      }
+      if (e == hipSuccess) {
+        where = "route";
+        StageTimer t(kStageRoute, st);
+        e = launch_route(s, Q, ws, route_out, 0, s.BH, st);
+      }
+      if (forked) {  // bucketing follows routing (recorded also on failure)
+        hipError_t er = hipEventRecord(ss->routed, st);
+        if (er == hipSuccess) er = hipStreamWaitEvent(ss->aux, ss->routed, 0);
+        if (ea == hipSuccess && er != hipSuccess) {
+          ea = er;
+          where_aux = "route event";
+        }
+      }
+      if (forked && ea == hipSuccess && e == hipSuccess) {
         where_aux = "bucket";
         StageTimer t(kStageBucket, ss->aux);
         ea = launch_bucket(s, route_out, ws, off_copy, perm_copy, ss->aux);
       }
-      if (e == hipSuccess) {
-        where = "landmark_threshold";
-        StageTimer t(kStageThreshold, st);
-        e = launch_threshold(s, K, ws, st);
+      if (e == hipSuccess) {  // the scan needs the pre-threshold
+        if (thr_recorded) {
+          e = hipStreamWaitEvent(st, ss->thr_done, 0);
+          if (e != hipSuccess) where = "threshold event";
+        } else if (!forked || ea != hipSuccess) {
+          e = ea != hipSuccess ? ea : hipErrorInvalidResourceHandle;
+          where = where_aux;
+        }
       }
       if (e == hipSuccess) {
         where = "landmark_scan";

@@ -139,6 +139,32 @@ __device__ __forceinline__ void xor_pair(float v, int mask, float& a, float& b) 
     b = lower ? o : v;
   }
 }
+// (value, index) of lanes l and l^mask combined: the larger value, on equal
+// values the lower index.  Symmetric, so both lanes get the same pair.
+__device__ __forceinline__ void xor_argmax(float& v, int& i, int mask) {
+  float a, b;
+  xor_pair(v, mask, a, b);
+  const uint32_t u = static_cast<uint32_t>(i);
+  uint32_t ia, ib;
+  if (mask == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    ia = r[0];
+    ib = r[1];
+  } else if (mask == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    ia = r[0];
+    ib = r[1];
+  } else {
+    const bool lower = (lane_id() & mask) == 0;
+    const uint32_t o = lane_read(u, lane_id() ^ mask);
+    ia = lower ? u : o;
+    ib = lower ? o : u;
+  }
+  const bool take_b = b > a || (b == a && static_cast<int>(ib) < static_cast<int>(ia));
+  v = take_b ? b : a;
+  i = static_cast<int>(take_b ? ib : ia);
+}
+
 __device__ __forceinline__ float xor_max(float v, int mask) {
   float a, b;
   xor_pair(v, mask, a, b);

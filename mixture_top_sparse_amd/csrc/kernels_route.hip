@@ -35,21 +35,9 @@ struct RouteTraits;
 template <>
 struct RouteTraits<BF16> {
   using E = uint16_t;
-  struct QlReg {
-    bf16x8 v[4][2];
-  };
   struct QReg {
     bf16x8 v[2];
   };
-  // Ql rows from the block's LDS copy (rows >= m are zero there)
-  __device__ static void load_ql(QlReg& a, const E* qls, int c16, int g) {
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-        a.v[mt][s] = as_bf16x8(
-            *reinterpret_cast<const u32x4*>(qls + (16 * mt + c16) * kQlStride + 32 * s + 8 * g));
-  }
   __device__ static void load_q(QReg& b, const E* row, bool ok, int g) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -57,10 +45,14 @@ struct RouteTraits<BF16> {
       b.v[s] = as_bf16x8(ok ? *reinterpret_cast<const u32x4*>(row + 32 * s + 8 * g) : z);
     }
   }
-  __device__ static f32x4 logits(const QlReg& a, int mt, const QReg& b) {
+  // landmark rows 16mt.. from LDS straight into one MFMA: R^T block mt
+  __device__ static f32x4 logits_lds(const E* qls, int mt, const QReg& b, int c16, int g) {
     f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-    for (int s = 0; s < 2; ++s) acc = mfma_bf16(a.v[mt][s], b.v[s], acc);
+    for (int s = 0; s < 2; ++s)
+      acc = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(
+                          qls + (16 * mt + c16) * kQlStride + 32 * s + 8 * g)),
+                      b.v[s], acc);
     return acc;
   }
 };
@@ -68,33 +60,24 @@ struct RouteTraits<BF16> {
 template <>
 struct RouteTraits<F32> {
   using E = float;
-  struct QlReg {
-    float v[4][16];
-  };
   struct QReg {
     float v[16];
   };
-  __device__ static void load_ql(QlReg& a, const E* qls, int c16, int g) {
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int s = 0; s < 16; ++s) a.v[mt][s] = qls[(16 * mt + c16) * kQlStride + 4 * s + g];
-  }
   __device__ static void load_q(QReg& b, const E* row, bool ok, int g) {
 #pragma unroll
     for (int s = 0; s < 16; ++s) b.v[s] = ok ? row[4 * s + g] : 0.f;
   }
-  __device__ static f32x4 logits(const QlReg& a, int mt, const QReg& b) {
+  __device__ static f32x4 logits_lds(const E* qls, int mt, const QReg& b, int c16, int g) {
     f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-    for (int s = 0; s < 16; ++s) acc = mfma_f32(a.v[mt][s], b.v[s], acc);
+    for (int s = 0; s < 16; ++s)
+      acc = mfma_f32(qls[(16 * mt + c16) * kQlStride + 4 * s + g], b.v[s], acc);
     return acc;
   }
 };
 
 // grid (nseg, BH), 256 threads; wave w routes queries seg*1024 + 256w + [0, 256)
-// in four steps of 64 (groups of 16 queries); the next step's Q rows are in
-// flight while the current step computes
+// in 16 groups of 16 queries, four groups of Q rows in flight
 template <class T>
 __global__ __launch_bounds__(256) void k_route(const typename T::elem* __restrict__ Q,
                                               const typename T::elem* __restrict__ Ql, int64_t N,
@@ -123,44 +106,30 @@ __global__ __launch_bounds__(256) void k_route(const typename T::elem* __restric
   }
   const E* Qh = Q + bh * N * kD;
   const int64_t qw = static_cast<int64_t>(seg) * kRouteSeg + 256 * w;
-  // bf16: the whole next step's rows in flight; fp32 operands are 4x larger,
-  // so they are loaded group by group (register budget)
-  constexpr bool kPrefetch = sizeof(E) == 2;
-  constexpr int NB = kPrefetch ? 4 : 1;
-  auto load_group = [&](int it, int G, typename TR::QReg& dst) {
-    const int64_t qq = qw + 64 * it + 16 * G + c16;
+  // a ring of D groups of 16 queries in flight; the landmark operands are
+  // read from LDS for every group (not pinned in registers: occupancy)
+  constexpr int D = 4, NG = 16;
+  auto load_group = [&](int G, typename TR::QReg& dst) {
+    const int64_t qq = qw + 16 * G + c16;
     TR::load_q(dst, Qh + (qq < N ? qq : 0) * kD, qq < N, g);
   };
-  typename TR::QReg b[NB];
-  if constexpr (kPrefetch) {
+  typename TR::QReg ring[D];
 #pragma unroll
-    for (int G = 0; G < 4; ++G) load_group(0, G, b[G]);
-  }
-  __syncthreads();
-  typename TR::QlReg a;
-  TR::load_ql(a, qls, c16, g);
+  for (int j = 0; j < D; ++j) load_group(j, ring[j]);
+  __syncthreads();  // landmark rows and counters staged
   const int mtiles = (m + 15) >> 4;
-
-  for (int it = 0; it < 4; ++it) {
-    if (qw + 64 * it >= N) break;
-    typename TR::QReg bn[NB];
-    if constexpr (kPrefetch) {
-      if (it + 1 < 4) {
+  for (int G0 = 0; G0 < NG; G0 += D) {
+    if (qw + 16 * G0 >= N) break;
 #pragma unroll
-        for (int G = 0; G < 4; ++G) load_group(it + 1, G, bn[G]);
-      }
-    }
-    int rsel = 0;
-#pragma unroll
-    for (int G = 0; G < 4; ++G) {
-      if constexpr (!kPrefetch) load_group(it, G, b[0]);
-      const typename TR::QReg& bq = b[kPrefetch ? G : 0];
+    for (int j = 0; j < D; ++j) {
+      const int G = G0 + j;
+      __asm__ volatile("" ::: "memory");  // re-read the landmark operands
       float best = -INFINITY;
       int bi = 0;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         if (mt < mtiles) {
-          const f32x4 r4 = TR::logits(a, mt, bq);
+          const f32x4 r4 = TR::logits_lds(qls, mt, ring[j], c16, g);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int lmi = 16 * mt + 4 * g + r;  // increasing within the lane
@@ -175,16 +144,12 @@ __global__ __launch_bounds__(256) void k_route(const typename T::elem* __restric
       // lower landmark index
       xor_argmax(best, bi, 16);
       xor_argmax(best, bi, 32);
-      if (G == g) rsel = bi;  // lane l = 16G + c16 keeps query qw + 64 it + l
-    }
-    const int64_t q = qw + 64 * it + l;
-    if (q < N) {
-      route_out[bh * N + q] = rsel;
-      atomicAdd(&cnt[rsel], 1);
-    }
-    if constexpr (kPrefetch) {
-#pragma unroll
-      for (int G = 0; G < 4; ++G) b[G] = bn[G];
+      if (G + D < NG) load_group(G + D, ring[j]);
+      const int64_t q = qw + 16 * G + c16;
+      if (g == 0 && q < N) {
+        route_out[bh * N + q] = bi;
+        atomicAdd(&cnt[bi], 1);
+      }
     }
   }
   __syncthreads();

@@ -780,14 +780,20 @@ __global__ __launch_bounds__(256) void k_theta_select(const uint64_t* __restrict
 // merge of the per-split partials
 // ---------------------------------------------------------------------------
 
-// grid (m, BH), 256 threads; wave w takes splits w, w+4, ... in batches of
-// 8 (loads first, then the arithmetic).  A split's top list only enters the
-// merge network when its best key beats the wave's current k-th best.
+// grid (m, BH, P), 256 threads.  Block (lm, bh, p) combines the splits
+// s = p, p + P, p + 2P, ...; wave w takes the w-th, (w+4)-th, ... of them in
+// batches of 8 (loads first, then the arithmetic).  A split's top list only
+// enters the merge network when its best key beats the wave's current k-th
+// best.  FINAL (P = 1): writes idx_out (ascending) and Vl.  Otherwise the
+// block's combined top list and softmax state go to the out_* arrays in the
+// layout of the scan's partials with P "splits", for a FINAL pass.
+template <bool FINAL>
 __global__ __launch_bounds__(256) void k_merge(
     const uint64_t* __restrict__ part_keys, const int32_t* __restrict__ part_cnt,
     const float* __restrict__ part_stats, const float* __restrict__ part_acc, int m, int k,
     int mrows, int splits, int32_t* __restrict__ idx_out, float* __restrict__ vl,
-    float* __restrict__ vl_copy) {
+    float* __restrict__ vl_copy, uint64_t* __restrict__ out_keys, int32_t* __restrict__ out_cnt,
+    float* __restrict__ out_stats, float* __restrict__ out_acc) {
   constexpr int kBatch = 8;
   __shared__ uint64_t tops[4][64];
   __shared__ float sacc[4][64];
@@ -795,18 +801,20 @@ __global__ __launch_bounds__(256) void k_merge(
   const int l = lane_id(), lm = blockIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(wave_id());
   const int64_t bh = blockIdx.y;
+  const int P = gridDim.z, p = blockIdx.z;
   const int64_t row0 = bh * splits * mrows + lm;  // partial row of split s: row0 + s * mrows
+  const int nmine = splits > p ? (splits - p + P - 1) / P : 0;  // splits of this block
 
   uint64_t top = 0;
   float Mw = -INFINITY, Lw = 0.f, aw = 0.f;
-  for (int s0 = w; s0 < splits; s0 += 4 * kBatch) {
+  for (int i0 = w; i0 < nmine; i0 += 4 * kBatch) {
     int cnt[kBatch];
     float Ms[kBatch], Ls[kBatch], as[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const int s = s0 + 4 * u;
-      const int64_t r = row0 + static_cast<int64_t>(s) * mrows;
-      const bool ok = s < splits;
+      const int i = i0 + 4 * u;
+      const int64_t r = row0 + static_cast<int64_t>(p + P * i) * mrows;
+      const bool ok = i < nmine;
       cnt[u] = ok ? part_cnt[r] : 0;
       Ms[u] = ok ? part_stats[r * 2] : 0.f;
       Ls[u] = ok ? part_stats[r * 2 + 1] : 0.f;
@@ -815,15 +823,15 @@ __global__ __launch_bounds__(256) void k_merge(
     uint64_t lst[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {  // issued with the loads above; masked once cnt is in
-      const int s = s0 + 4 * u;
-      const int64_t r = row0 + static_cast<int64_t>(s < splits ? s : 0) * mrows;
+      const int i = i0 + 4 * u;
+      const int64_t r = row0 + static_cast<int64_t>(i < nmine ? p + P * i : p) * mrows;
       lst[u] = part_keys[r * kTopCap + l];
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) lst[u] = (l < cnt[u]) ? lst[u] : 0ull;
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      if (s0 + 4 * u >= splits) break;
+      if (i0 + 4 * u >= nmine) break;
       const float Mn = fmaxf(Mw, Ms[u]);
       const float f0 = fast_exp2(Mw - Mn), f1 = fast_exp2(Ms[u] - Mn);
       Lw = Lw * f0 + Ls[u] * f1;
@@ -848,9 +856,6 @@ __global__ __launch_bounds__(256) void k_merge(
     const uint64_t o = tops[v][l];
     if (uniform_read(o, 0) > uniform_read(t, k - 1)) t = wave_merge_top(t, o);
   }
-  int32_t ix = (l < k) ? static_cast<int32_t>(key_index(t)) : INT32_MAX;
-  ix = wave_sort_asc_i32(ix);
-  if (l < k) idx_out[(bh * m + lm) * k + l] = ix;
 
   float Mt = -INFINITY;
 #pragma unroll
@@ -863,9 +868,26 @@ __global__ __launch_bounds__(256) void k_merge(
     Lt += sL[v] * f;
     at += sacc[v][l] * f;
   }
-  const float val = at / Lt;
-  vl[(bh * m + lm) * kD + l] = val;
-  if (vl_copy != nullptr) vl_copy[(bh * m + lm) * kD + l] = val;
+  if constexpr (FINAL) {
+    int32_t ix = (l < k) ? static_cast<int32_t>(key_index(t)) : INT32_MAX;
+    ix = wave_sort_asc_i32(ix);
+    if (l < k) idx_out[(bh * m + lm) * k + l] = ix;
+    const float val = at / Lt;
+    vl[(bh * m + lm) * kD + l] = val;
+    if (vl_copy != nullptr) vl_copy[(bh * m + lm) * kD + l] = val;
+  } else {
+    // this block's combination, as partial number p of P (every block of
+    // the grid had at least one split, so Mt is finite)
+    const int64_t r = (bh * P + p) * mrows + lm;
+    const uint64_t nz = ballot(t != 0ull);
+    if (t != 0ull) out_keys[r * kTopCap + l] = t;
+    if (l == 0) {
+      out_cnt[r] = __popcll(nz);
+      out_stats[r * 2] = Mt;
+      out_stats[r * 2 + 1] = Lt;
+    }
+    out_acc[r * kD + l] = at;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -919,9 +941,21 @@ hipError_t launch_scan(const Shape& s, const void* K, const void* V, const Works
 
 hipError_t launch_merge(const Shape& s, const Workspace& ws, int32_t* idx_out, float* vl_copy,
                         hipStream_t st) {
-  hipLaunchKernelGGL(k_merge, dim3(s.m, s.BH), dim3(256), 0, st, ws.part_keys, ws.part_cnt,
-                     ws.part_stats, ws.part_acc, s.m, s.k, s.mrows, s.scan_splits, idx_out, ws.vl,
-                     vl_copy);
+  if (s.merge_parts > 1) {  // first level: merge_parts partial combinations per landmark
+    hipLaunchKernelGGL(k_merge<false>, dim3(s.m, s.BH, s.merge_parts), dim3(256), 0, st,
+                       ws.part_keys, ws.part_cnt, ws.part_stats, ws.part_acc, s.m, s.k, s.mrows,
+                       s.scan_splits, nullptr, nullptr, nullptr, ws.part2_keys, ws.part2_cnt,
+                       ws.part2_stats, ws.part2_acc);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_merge<true>, dim3(s.m, s.BH, 1), dim3(256), 0, st, ws.part2_keys,
+                       ws.part2_cnt, ws.part2_stats, ws.part2_acc, s.m, s.k, s.mrows,
+                       s.merge_parts, idx_out, ws.vl, vl_copy, nullptr, nullptr, nullptr, nullptr);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(k_merge<true>, dim3(s.m, s.BH, 1), dim3(256), 0, st, ws.part_keys,
+                     ws.part_cnt, ws.part_stats, ws.part_acc, s.m, s.k, s.mrows, s.scan_splits,
+                     idx_out, ws.vl, vl_copy, nullptr, nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
 

@@ -251,6 +251,8 @@ void derive(Shape& s, int cus) {
     s.scan_chunk = static_cast<int>(chunk);
     s.scan_splits = static_cast<int>(cdiv(s.N, chunk));
   }
+  // merge of the scan partials in two levels when there are many splits
+  s.merge_parts = s.scan_splits > 32 ? 8 : 1;
   s.pool_splits = static_cast<int>(cdiv(max_window(s), kPoolChunk));
   // top-k pre-threshold: sample up to a quarter of the key tiles (at most
   // 1024 per head), only when there are at least max(k, 64) of them
@@ -292,6 +294,13 @@ size_t plan_workspace(const Shape& s, Workspace* ws, char* base) {
   ws->part_cnt = reinterpret_cast<int32_t*>(take(parts * sizeof(int32_t)));
   ws->part_stats = reinterpret_cast<float*>(take(parts * 2 * sizeof(float)));
   ws->part_acc = reinterpret_cast<float*>(take(parts * kD * sizeof(float)));
+  if (s.merge_parts > 1) {
+    const size_t parts2 = BH * s.merge_parts * s.mrows;
+    ws->part2_keys = reinterpret_cast<uint64_t*>(take(parts2 * kTopCap * sizeof(uint64_t)));
+    ws->part2_cnt = reinterpret_cast<int32_t*>(take(parts2 * sizeof(int32_t)));
+    ws->part2_stats = reinterpret_cast<float*>(take(parts2 * 2 * sizeof(float)));
+    ws->part2_acc = reinterpret_cast<float*>(take(parts2 * kD * sizeof(float)));
+  }
   ws->vl = reinterpret_cast<float*>(take(BH * s.m * kD * sizeof(float)));
   ws->counts = reinterpret_cast<int32_t*>(take(BH * s.nseg * s.m * 4));
   ws->colpre = reinterpret_cast<int32_t*>(take(BH * s.nseg * s.m * 4));

@@ -32,6 +32,7 @@ struct Shape {
   int mrows = 0;       // scan_waves * 16
   int scan_chunk = 0;  // keys per landmark-scan block (fp32; the bf16 scan interleaves tiles)
   int scan_splits = 0;
+  int merge_parts = 0; // first-level merge partitions per landmark (1: single pass)
   int pool_splits = 0; // partial sums per landmark window
   int theta_groups = 0;// sample tiles for the top-k pre-threshold (0: off)
   int nseg = 0;        // routing segments per head
@@ -50,6 +51,10 @@ struct Workspace {
   int32_t* part_cnt = nullptr;   // [BH][splits][mrows] entries in each per-split top list
   float* part_stats = nullptr;   // [BH][splits][mrows][2] (max in log2 units, sum)
   float* part_acc = nullptr;     // [BH][splits][mrows][64] unnormalised P.V
+  uint64_t* part2_keys = nullptr; // the same four arrays with merge_parts in place of splits
+  int32_t* part2_cnt = nullptr;
+  float* part2_stats = nullptr;
+  float* part2_acc = nullptr;
   float* vl = nullptr;           // [BH][m][64] landmark values fp32
   int32_t* counts = nullptr;     // [BH][m][nseg] routed queries per expert and segment
   int32_t* colpre = nullptr;     // [BH][m][nseg] exclusive prefix of counts over segments

@@ -32,9 +32,9 @@ KERNEL_SOURCES = {"k_scan": "kernels_scan.hip", "k_route": "kernels_route.hip",
 # kernel whose sources changed since reports traffic null.
 COUNTED_TRAFFIC = {
     "len_1m": {
-        "k_scan": {"sha": "015f662fb73d", "bytes": 1100567579},
-        "k_route": {"sha": "5b596e380fa2", "bytes": 562964875},
-        "k_attend": {"sha": "1581a5ea8364", "bytes": 1648485944},
+        "k_scan": {"sha": "f73ac051c435", "bytes": 1096191301},
+        "k_route": {"sha": "cd4bc04bf2a7", "bytes": 564126350},
+        "k_attend": {"sha": "0c1633766ba0", "bytes": 1636630319},
     },
 }
 

@@ -183,11 +183,14 @@ __device__ int stage_bf16(AttendLds<BF16, MPAD, KPAD>& S, const uint16_t* __rest
 }
 
 // 16 queries of one wave (lane column c16 = query) against the staged expert
-template <int MPAD, int KPAD, bool FULL>
+// `after_scores` runs once the logits have been formed (the Q operand is then
+// free, so the caller can refill it while the rest of the sub-tile runs).
+template <int MPAD, int KPAD, bool FULL, class AfterScores>
 __device__ __forceinline__ void attend_queries_bf16(AttendLds<BF16, MPAD, KPAD>& S,
-                                                    const bf16x8 (&qb)[2], int sl0, int nq,
-                                                    int m, int k, float c2, float oscale,
-                                                    float* __restrict__ out_h) {
+                                                    bf16x8 (&qb)[2], int sl0, int nq, int m,
+                                                    int k, float c2, float oscale,
+                                                    float* __restrict__ out_h,
+                                                    AfterScores&& after_scores) {
   using L = AttendLds<BF16, MPAD, KPAD>;
   constexpr int NPB = (MPAD + KPAD) / 16;
   const int l = lane_id(), g = l >> 4, c16 = l & 15;
@@ -214,6 +217,7 @@ __device__ __forceinline__ void attend_queries_bf16(AttendLds<BF16, MPAD, KPAD>&
       mx = fmaxf(mx, x[pb][r]);
     }
   }
+  after_scores(qb);
   mx = xor_max(mx, 16);
   mx = xor_max(mx, 32) * c2;
   float lsum = 0.f;
@@ -267,13 +271,14 @@ __device__ __forceinline__ void attend_queries_bf16(AttendLds<BF16, MPAD, KPAD>&
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = 4 * j + (l >> 4);
-    if (sl0 + row < nq) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(st + row * kOStageStride + 4 * (l & 15));
-      const int64_t q = S.perm[sl0 + row];
-      // non-temporal: the rows are not read again here, and written-through
-      // lines do not leave dirty cache lines for the next kernel to flush
-      __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(out_h + q * kD + 4 * (l & 15)));
-    }
+    // slots past the item repeat its last query: those lanes computed that
+    // query's row from the same operands, so they store identical bits
+    const int sl = min(sl0 + row, nq - 1);
+    const f32x4 v = *reinterpret_cast<const f32x4*>(st + row * kOStageStride + 4 * (l & 15));
+    const int64_t q = S.perm[sl];
+    // non-temporal: the rows are not read again here, and written-through
+    // lines do not leave dirty cache lines for the next kernel to flush
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(out_h + q * kD + 4 * (l & 15)));
   }
 }
 
@@ -289,44 +294,58 @@ __device__ void attend_bf16(AttendLds<BF16, MPAD, KPAD>& S, const uint16_t* __re
   const uint16_t* Qh = Q + bh * N * kD;
   const int32_t* ph = perm + bh * N;
   float* out_h = out + bh * N * kD;
-  const u32x4 z = {0, 0, 0, 0};
-  const int nq = ti.qe - ti.qb;                // queries in this item (<= 64 * tpb)
-  const int nsub = (nq + 15) / 16;             // 16-query sub-tiles
-  // wave w handles sub-tiles w, w+W, w+2W, ...; slot of sub-tile i in the item
+  const int nq = ti.qe - ti.qb;  // queries in this item, 1 .. 64 * tpb
+  if (nq <= 0) return;           // (items are never empty; uniform per block)
+  const int nsub = (nq + 15) / 16;  // 16-query sub-tiles
+  // wave w handles sub-tiles w, w+W, w+2W, ...; every slot index is clamped
+  // to the item's last query, so each Q gather reads a valid row and needs no
+  // branch (the wait counters then stay exact across the ring)
   constexpr int W = kAttendWaves;
-  auto slot = [&](int i) { return 16 * (w + W * i) + c16; };
+  auto slot = [&](int i) { return min(16 * (w + W * i) + c16, nq - 1); };
   auto load_q = [&](int64_t q, bf16x8 (&qb)[2]) {
 #pragma unroll
     for (int s = 0; s < 2; ++s)
-      qb[s] = as_bf16x8(q >= 0 ? *reinterpret_cast<const u32x4*>(Qh + q * kD + 32 * s + 8 * g) : z);
+      qb[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(Qh + q * kD + 32 * s + 8 * g));
   };
   // the first D sub-tiles' rows are requested before staging (perm from global)
+  int32_t p0[D];
+#pragma unroll
+  for (int j = 0; j < D; ++j) p0[j] = ph[ti.qb + slot(j)];
   bf16x8 ring[D][2];
 #pragma unroll
-  for (int j = 0; j < D; ++j) {
-    const int sl = slot(j);
-    const int64_t q = (sl < nq && ti.qb + sl < N) ? clamp_index(ph[ti.qb + sl], N) : -1;
-    load_q(q, ring[j]);
-  }
+  for (int j = 0; j < D; ++j) load_q(clamp_index(p0[j], N), ring[j]);
   for (int c = tid; c < nq; c += kAttendThreads)
     S.perm[c] = static_cast<int32_t>(clamp_index(ph[ti.qb + c], N));
   const int sh = stage_bf16<MPAD, KPAD>(S, K, V, Ql, vl, idx + (bh * m + ti.e) * k, N, m, k, bh);
   const float oscale = exp2i(sh);
   __syncthreads();
 
-  for (int i0 = 0; w + W * i0 < nsub; i0 += D) {
+  const int nw = nsub > w ? (nsub - w + W - 1) / W : 0;  // this wave's sub-tiles
+  if (nw >= D) {
+    // whole ring rounds: the last round's extra sub-tiles repeat the item's
+    // last query (same values stored again); refills past the end re-read it
+    const int rounds = (nw + D - 1) / D;
+    for (int r = 0; r < rounds; ++r) {
 #pragma unroll
-    for (int j = 0; j < D; ++j) {
-      const int i = i0 + j;
-      if (w + W * i >= nsub) break;
-      // re-read the staged operands from LDS for every sub-tile instead of
-      // pinning all of them in registers across the loop (keeps occupancy)
-      __asm__ volatile("" ::: "memory");
-      attend_queries_bf16<MPAD, KPAD, FULL>(S, ring[j], 16 * (w + W * i), nq, m, k, c2, oscale,
-                                            out_h);
-      const int sn = slot(i + D);  // refill this slot with sub-tile i + D
-      load_q(sn < nq ? static_cast<int64_t>(S.perm[sn]) : -1, ring[j]);
+      for (int j = 0; j < D; ++j) {
+        const int i = r * D + j;
+        // re-read the staged operands from LDS for every sub-tile instead of
+        // pinning all of them in registers across the loop, and keep the
+        // scheduler from interleaving sub-tiles (both keep occupancy)
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        attend_queries_bf16<MPAD, KPAD, FULL>(
+            S, ring[j], 16 * (w + W * i), nq, m, k, c2, oscale, out_h,
+            [&](bf16x8(&qb)[2]) { load_q(S.perm[slot(i + D)], qb); });  // sub-tile i + D
+      }
     }
+  } else {
+    // fewer sub-tiles than ring slots: all were requested before staging
+#pragma unroll
+    for (int j = 0; j < D; ++j)
+      if (j < nw)
+        attend_queries_bf16<MPAD, KPAD, FULL>(S, ring[j], 16 * (w + W * j), nq, m, k, c2,
+                                              oscale, out_h, [](bf16x8(&)[2]) {});
   }
 }
 

@@ -109,20 +109,24 @@ __global__ __launch_bounds__(256) void k_route(const typename T::elem* __restric
   // a ring of D groups of 16 queries in flight; the landmark operands are
   // read from LDS for every group (not pinned in registers: occupancy)
   constexpr int D = 4, NG = 16;
+  // unconditional loads of a clamped row (results past N are never used):
+  // branch-free, so the compiler's wait counts stay exact
   auto load_group = [&](int G, typename TR::QReg& dst) {
     const int64_t qq = qw + 16 * G + c16;
-    TR::load_q(dst, Qh + (qq < N ? qq : 0) * kD, qq < N, g);
+    TR::load_q(dst, Qh + (qq < N ? qq : N - 1) * kD, true, g);
   };
   typename TR::QReg ring[D];
 #pragma unroll
   for (int j = 0; j < D; ++j) load_group(j, ring[j]);
   __syncthreads();  // landmark rows and counters staged
   const int mtiles = (m + 15) >> 4;
-  for (int G0 = 0; G0 < NG; G0 += D) {
-    if (qw + 16 * G0 >= N) break;
+  // fully unrolled, so that each group's wait covers exactly its own rows
+  // (a rolled ring loop makes the compiler wait for every group in flight)
 #pragma unroll
-    for (int j = 0; j < D; ++j) {
-      const int G = G0 + j;
+  for (int G = 0; G < NG; ++G) {
+    if (qw + 16 * G >= N) break;
+    {
+      const int j = G % D;
       __asm__ volatile("" ::: "memory");  // re-read the landmark operands
       float best = -INFINITY;
       int bi = 0;
@@ -133,10 +137,9 @@ __global__ __launch_bounds__(256) void k_route(const typename T::elem* __restric
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int lmi = 16 * mt + 4 * g + r;  // increasing within the lane
-            if (lmi < m && r4[r] > best) {
-              best = r4[r];
-              bi = lmi;
-            }
+            const bool better = lmi < m && r4[r] > best;
+            best = better ? r4[r] : best;
+            bi = better ? lmi : bi;
           }
         }
       }

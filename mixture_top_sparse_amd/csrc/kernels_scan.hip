@@ -357,7 +357,7 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 // s_waitcnt immediates (gfx9 encoding): vmcnt <= n, expcnt and lgkmcnt not
 // waited on.  Each staged tile is four requests per lane.
-constexpr int kWaitVm0 = 0x0F70, kWaitVm4 = 0x0F74;
+constexpr int kWaitVm0 = 0x0F70;
 
 __device__ __forceinline__ int tile_off(int r, int c) {
   return (r << 7) | ((c ^ ((r >> 1) & 7)) << 4);
@@ -431,8 +431,10 @@ __device__ __forceinline__ void stage_tile_bf16(const uint16_t* __restrict__ Kh,
 }
 
 // Block: 4 waves; waves 0..NW-1 each own 16 landmarks, all 4 stage tiles.
-// A ring of three LDS tile buffers: while one tile is scored, the next two
-// are in flight.  52 KiB of LDS and at most 168 VGPRs: three blocks per CU.
+// Two LDS tile buffers: while one tile is scored, the next is in flight.
+// With three blocks per CU (at most 168 VGPRs) that keeps 48 KiB of tile
+// requests in flight per CU; deeper rings (96 KiB per CU) measured slower,
+// the DMA path losing bandwidth when that many requests queue up.
 template <int NW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_scan_bf16(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -445,7 +447,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   // ring slots: K tile (8 KiB), then V tile (8 KiB)
   __shared__ __attribute__((aligned(16))) uint8_t b0[16384];
   __shared__ __attribute__((aligned(16))) uint8_t b1[16384];
-  __shared__ __attribute__((aligned(16))) uint8_t b2[16384];
   __shared__ uint64_t cand[MROWS][kCandCap];
   __shared__ int lcnt[MROWS];  // candidates buffered per landmark (may overshoot kCandCap)
 
@@ -473,11 +474,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __asm__ volatile("" ::: "memory");
 
-  // prologue: tiles 0 and 1 in flight (ring of three LDS tile buffers)
+  // prologue: tile 0 in flight
   const uint32_t soff0 = stage_src_off(w, 0, l), soff1 = stage_src_off(w, 1, l);
-  const uint32_t a0 = lds_address(b0), a1 = lds_address(b1), a2 = lds_address(b2);
+  const uint32_t a0 = lds_address(b0), a1 = lds_address(b1);
   stage_tile_bf16(Kh, Vh, kbeg, N, a0, a0 + 8192, w, soff0, soff1);
-  if (ntiles > 1) stage_tile_bf16(Kh, Vh, kbeg + tstride, N, a1, a1 + 8192, w, soff0, soff1);
   if (threadIdx.x < MROWS) lcnt[threadIdx.x] = 0;  // visible after the first barrier
 
   float M = -INFINITY, Lsum = 0.f;
@@ -532,8 +532,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     float kbmax[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
-      kbmax[kb] = fmaxf(fmaxf(sc[kb][0], sc[kb][1]), fmaxf(sc[kb][2], sc[kb][3]));
-    const float smax = fmaxf(fmaxf(kbmax[0], kbmax[1]), fmaxf(kbmax[2], kbmax[3]));
+      kbmax[kb] = fmax_nc(fmax_nc(sc[kb][0], sc[kb][1]), fmax_nc(sc[kb][2], sc[kb][3]));
+    const float smax = fmax_nc(fmax_nc(kbmax[0], kbmax[1]), fmax_nc(kbmax[2], kbmax[3]));
 
     // ---- streaming top-k: only when some score beats its landmark's k-th best.
     // One ballot per score position (uniform branches, rarely taken); lanes
@@ -636,32 +636,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     }
   };
 
-  // Tile `it` sits in buffer it % 3.  Before using it, wait until at most
-  // the requests of the (up to one) younger tile are outstanding; the block
-  // barrier then makes every wave's pieces visible and frees buffer
-  // (it + 2) % 3, whose tile was used one step earlier, for tile it + 2.
+  // Tile `it` sits in buffer it % 2.  Before using it, wait for this wave's
+  // requests (the only ones outstanding); the block barrier then makes every
+  // wave's pieces visible and frees the other buffer, whose tile every wave
+  // finished one step earlier, for tile it + 1.
   auto step = [&](int it, const uint8_t* cur, uint32_t nxt) __attribute__((always_inline)) {
-    if (it + 1 < ntiles) {
-      __builtin_amdgcn_s_waitcnt(kWaitVm4);
-    } else {
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    }
-    // a plain barrier: __syncthreads() would add a workgroup release fence,
-    // i.e. a wait for every outstanding request, the younger tile's included
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    // a plain barrier: __syncthreads() would add a workgroup release fence
     __asm__ volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
     const int64_t t0 = kbeg + static_cast<int64_t>(it) * tstride;
-    if (it + 2 < ntiles)
-      stage_tile_bf16(Kh, Vh, t0 + 2 * tstride, N, nxt, nxt + 8192, w, soff0, soff1);
+    if (it + 1 < ntiles)
+      stage_tile_bf16(Kh, Vh, t0 + tstride, N, nxt, nxt + 8192, w, soff0, soff1);
     if (computes) compute_tile(cur, cur + 8192, t0);
   };
-  for (int it = 0; it < ntiles; it += 3) {
-    step(it, b0, a2);
+  for (int it = 0; it < ntiles; it += 2) {
+    step(it, b0, a1);
     if (it + 1 >= ntiles) break;
     step(it + 1, b1, a0);
-    if (it + 2 >= ntiles) break;
-    step(it + 2, b2, a1);
   }
   if (!computes) return;
 

@@ -165,10 +165,15 @@ __device__ __forceinline__ void xor_argmax(float& v, int& i, int mask) {
   i = static_cast<int>(take_b ? ib : ia);
 }
 
+// max that propagates NaN (IEEE maximum): one v_maximum3 instruction, where
+// fmaxf first has to quiet both operands; equal to fmaxf for non-NaN input
+__device__ __forceinline__ float fmax_nc(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
 __device__ __forceinline__ float xor_max(float v, int mask) {
   float a, b;
   xor_pair(v, mask, a, b);
-  return fmaxf(a, b);
+  return fmax_nc(a, b);
 }
 __device__ __forceinline__ float xor_sum(float v, int mask) {
   float a, b;

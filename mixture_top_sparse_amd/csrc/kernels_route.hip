@@ -14,9 +14,10 @@
 //   k_bucket_scan    (expert, head): prefix of the expert's per-segment counts
 //                    over the segments, and the expert's total.
 //   k_bucket_scatter (segment, head), one wave: expert offsets from the
-//                    totals, then a stable counting-sort scatter; a query's
-//                    rank among equal routes inside a group of 64 comes from
-//                    6 ballots over the route bits.  Segment 0 publishes the
+//                    totals, then a stable counting sort of the segment in
+//                    LDS (a query's rank among equal routes inside a group
+//                    of 64 comes from 6 ballots over the route bits), copied
+//                    out one expert run at a time.  Segment 0 publishes the
 //                    offsets and the first attention work item of each expert.
 //
 // Roofline: k_route streams Q (N*d*e bytes per head) — HBM-bound; the
@@ -200,13 +201,29 @@ __global__ __launch_bounds__(256) void k_bucket_scan(const int32_t* __restrict__
 // grid (nseg, BH), 64 threads: stable scatter of one segment's queries.
 // Expert offsets come from the per-expert totals (exclusive scan over the m
 // experts); segment 0 also publishes offsets and the attention work items.
+// The segment is first sorted by route in LDS (ranks from ballots, bases
+// from the routing kernel's per-segment counts); the sorted list is then
+// copied out run by run, so consecutive lanes store consecutive positions of
+// an expert's range instead of one lane per expert region.  Consecutive
+// segments are taken by blocks on one XCD (groups of four), so the partial
+// lines they leave at the ends of each run meet in one L2.
 __global__ __launch_bounds__(64) void k_bucket_scatter(
-    const int32_t* __restrict__ route, int m, int nseg, int64_t N, int tile, int tpb,
-    const int32_t* __restrict__ totals, const int32_t* __restrict__ colpre,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ offsets_copy,
-    int32_t* __restrict__ item_start, int32_t* __restrict__ perm, int32_t* __restrict__ perm_copy) {
-  __shared__ int base[kMaxM];
-  const int l = threadIdx.x, seg = blockIdx.x;
+    const int32_t* __restrict__ route, const int32_t* __restrict__ counts, int m, int nseg,
+    int64_t N, int tile, int tpb, const int32_t* __restrict__ totals,
+    const int32_t* __restrict__ colpre, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ offsets_copy, int32_t* __restrict__ item_start,
+    int32_t* __restrict__ perm, int32_t* __restrict__ perm_copy) {
+  constexpr int R = 4;  // consecutive segments per XCD
+  __shared__ int lbase[kMaxM];   // next local slot of each expert
+  __shared__ int gshift[kMaxM];  // global position minus local slot, per expert
+  __shared__ int32_t sq[kRouteSeg];
+  __shared__ uint8_t se[kRouteSeg];
+  const int l = threadIdx.x;
+  int seg = blockIdx.x;
+  {  // blocks are dispatched to the XCDs round-robin: b -> XCD b % 8
+    const int n = gridDim.x, full = n / (8 * R) * (8 * R), b = blockIdx.x;
+    if (b < full) seg = ((b / 8 / R) * 8 + b % 8) * R + (b / 8) % R;
+  }
   const int64_t bh = blockIdx.y;
   const int c = l < m ? totals[bh * m + l] : 0;
   const int incl = wave_inclusive_sum(c);
@@ -228,20 +245,28 @@ __global__ __launch_bounds__(64) void k_bucket_scatter(
   }
   // all of the segment's routes in flight at once
   constexpr int NG = kRouteSeg / 64;
+  const int64_t q0 = static_cast<int64_t>(seg) * kRouteSeg;
+  const int nq = static_cast<int>(N - q0 < kRouteSeg ? N - q0 : kRouteSeg);
   int rr[NG];
 #pragma unroll
   for (int it = 0; it < NG; ++it) {
-    const int64_t q = static_cast<int64_t>(seg) * kRouteSeg + 64 * it + l;
+    const int64_t q = q0 + 64 * it + l;
     rr[it] = q < N ? route[bh * N + q] : 0;
   }
-  if (l < m) base[l] = (incl - c) + colpre[(bh * m + l) * nseg + seg];
+  {
+    const int cl = l < m ? counts[(bh * m + l) * nseg + seg] : 0;
+    const int lex = wave_inclusive_sum(cl) - cl;  // local start of expert l
+    if (l < m) {
+      lbase[l] = lex;
+      gshift[l] = (incl - c) + colpre[(bh * m + l) * nseg + seg] - lex;
+    }
+  }
   // one wave: its LDS accesses complete in program order, no barriers needed
   const uint64_t below = (l == 0) ? 0ull : (~0ull >> (64 - l));
 #pragma unroll
   for (int it = 0; it < NG; ++it) {
-    const int64_t q = static_cast<int64_t>(seg) * kRouteSeg + 64 * it + l;
-    if (static_cast<int64_t>(seg) * kRouteSeg + 64 * it >= N) break;
-    const bool ok = q < N;
+    if (64 * it >= nq) break;
+    const bool ok = 64 * it + l < nq;
     int r = rr[it];
     r = r < 0 ? 0 : (r >= m ? m - 1 : r);  // routes come from k_route; clamp defensively
     uint64_t same = ballot(ok);
@@ -253,12 +278,22 @@ __global__ __launch_bounds__(64) void k_bucket_scatter(
     }
     const int rank = __popcll(same & below);
     const int total = __popcll(same);
-    const int pos = ok ? base[r] + rank : 0;
-    if (ok && pos >= 0 && pos < N) {
-      perm[bh * N + pos] = static_cast<int32_t>(q);
-      if (perm_copy) perm_copy[bh * N + pos] = static_cast<int32_t>(q);
+    const int pos = ok ? lbase[r] + rank : -1;
+    if (pos >= 0 && pos < kRouteSeg) {
+      sq[pos] = static_cast<int32_t>(q0 + 64 * it + l);
+      se[pos] = static_cast<uint8_t>(r);
     }
-    if (ok && rank == total - 1) base[r] += total;  // after every lane's read of base[r]
+    if (ok && rank == total - 1) lbase[r] += total;  // after every lane's read of lbase[r]
+  }
+  // copy out in sorted order: lanes l, l+1 of one expert run store adjacent
+  // positions
+  for (int i = l; i < nq; i += 64) {
+    const int e = se[i];
+    const int pos = e < m ? gshift[e] + i : -1;
+    if (pos >= 0 && pos < N) {
+      perm[bh * N + pos] = sq[i];
+      if (perm_copy) perm_copy[bh * N + pos] = sq[i];
+    }
   }
 }
 
@@ -283,8 +318,8 @@ hipError_t launch_bucket(const Shape& s, const int32_t* route, const Workspace& 
                      ws.colpre, ws.totals);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_bucket_scatter, dim3(s.nseg, s.BH), dim3(64), 0, st, route, s.m, s.nseg,
-                     s.N, kAttendTile, s.attend_tpb, ws.totals, ws.colpre, ws.offsets,
+  hipLaunchKernelGGL(k_bucket_scatter, dim3(s.nseg, s.BH), dim3(64), 0, st, route, ws.counts,
+                     s.m, s.nseg, s.N, kAttendTile, s.attend_tpb, ws.totals, ws.colpre, ws.offsets,
                      offsets_copy, ws.item_start, ws.perm, perm_copy);
   return hipGetLastError();
 }

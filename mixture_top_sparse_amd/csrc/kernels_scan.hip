@@ -57,17 +57,24 @@ struct ScanTraits<BF16> {
     }
   }
 
-  // S^T block for key row `row` of this lane (columns: the wave's landmarks)
-  __device__ static f32x4 score_global(const E* Kh, int64_t row, int64_t N, const QReg& q, int g) {
-    f32x4 acc = {0, 0, 0, 0};
+  // S^T blocks of the 64-key tile at t0 (block kb: key rows t0 + 16kb ..;
+  // columns: the wave's landmarks).  Rows past N read row N - 1 (the caller
+  // drops those scores): all eight loads are issued before the first product.
+  __device__ static void score_tile_global(const E* Kh, int64_t t0, int64_t N, const QReg& q,
+                                           int c16, int g, f32x4 (&sc)[4]) {
+    u32x4 ko[4][2];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const u32x4 z = {0, 0, 0, 0};
-      const bf16x8 a = as_bf16x8(
-          row < N ? *reinterpret_cast<const u32x4*>(Kh + row * kD + 32 * s + 8 * g) : z);
-      acc = mfma_bf16(a, q.v[s], acc);
+    for (int kb = 0; kb < 4; ++kb) {
+      const int64_t row = t0 + 16 * kb + c16;
+      const int64_t rr = row < N ? row : N - 1;
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        ko[kb][s] = *reinterpret_cast<const u32x4*>(Kh + rr * kD + 32 * s + 8 * g);
     }
-    return acc;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) sc[kb] = mfma_bf16(as_bf16x8(ko[kb][0]), q.v[0], f32x4{0, 0, 0, 0});
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) sc[kb] = mfma_bf16(as_bf16x8(ko[kb][1]), q.v[1], sc[kb]);
   }
 };
 
@@ -122,11 +129,17 @@ struct ScanTraits<F32> {
     return acc;
   }
 
-  __device__ static f32x4 score_global(const E* Kh, int64_t row, int64_t N, const QReg& q, int g) {
-    f32x4 acc = {0, 0, 0, 0};
+  __device__ static void score_tile_global(const E* Kh, int64_t t0, int64_t N, const QReg& q,
+                                           int c16, int g, f32x4 (&sc)[4]) {
 #pragma unroll
-    for (int s = 0; s < 16; ++s) acc = mfma_f32(row < N ? Kh[row * kD + 4 * s + g] : 0.f, q.v[s], acc);
-    return acc;
+    for (int kb = 0; kb < 4; ++kb) {
+      const int64_t row = t0 + 16 * kb + c16;
+      const int64_t rr = row < N ? row : N - 1;
+      f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+      for (int s = 0; s < 16; ++s) acc = mfma_f32(Kh[rr * kD + 4 * s + g], q.v[s], acc);
+      sc[kb] = acc;
+    }
   }
 
   __device__ static void pv(f32x4 (&acc)[4], const E* vlds, const float (&p)[4][4], int c16, int g) {
@@ -713,16 +726,20 @@ __global__ __launch_bounds__(256) void k_theta_sample(const typename T::elem* __
   const bool lm_ok = lm < m;
   if (w * 16 >= m) return;  // whole wave beyond the landmarks
   typename TR::QReg q;
-  TR::load_q(q, Ql + (bh * m + (lm_ok ? lm : 0)) * kD, lm_ok, g);
+  // lanes past m read landmark m - 1 (their maxima are not stored): the
+  // loads stay unconditional, so the compiler's wait counts stay exact
+  TR::load_q(q, Ql + (bh * m + (lm_ok ? lm : m - 1)) * kD, true, g);
   const int64_t ntiles = (N + kTileKeys - 1) / kTileKeys;
   const E* Kh = K + bh * N * kD;
   for (int j = 0; j < kThetaTilesPerBlock; ++j) {
     const int gi = blockIdx.x * kThetaTilesPerBlock + j;
     const int64_t t0 = ((static_cast<int64_t>(gi) * ntiles) / groups) * kTileKeys;
     uint64_t best = 0;
+    f32x4 sc[4];
+    TR::score_tile_global(Kh, t0, N, q, c16, g, sc);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const f32x4 a = TR::score_global(Kh, t0 + 16 * kb + c16, N, q, g);
+      const f32x4 a = sc[kb];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t t = t0 + 16 * kb + 4 * g + r;
@@ -738,6 +755,70 @@ __global__ __launch_bounds__(256) void k_theta_sample(const typename T::elem* __
       best = o > best ? o : best;
     }
     if (g == 0 && lm_ok) gmax[(bh * m + lm) * groups + gi] = best;
+  }
+}
+
+// bf16: grid (ceil(G / 4), BH), 256 threads; wave w scores sample tile
+// 4 * blockIdx.x + w against all landmarks (up to four blocks of 16), so each
+// sampled tile is read once.  Rows past N read row N - 1 and landmarks past
+// m read landmark m - 1: every load is unconditional (exact wait counts);
+// those scores are dropped and those maxima not stored.
+__global__ __launch_bounds__(256) void k_theta_sample_bf16(const uint16_t* __restrict__ K,
+                                                          const uint16_t* __restrict__ Ql,
+                                                          int64_t N, int m, int groups,
+                                                          uint64_t* __restrict__ gmax) {
+  const int l = lane_id(), g = l >> 4, c16 = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(wave_id());
+  const int gi = static_cast<int>(blockIdx.x) * 4 + w;
+  if (gi >= groups) return;  // whole wave
+  const int64_t bh = blockIdx.y;
+  const int64_t ntiles = (N + kTileKeys - 1) / kTileKeys;
+  const int64_t t0 = ((static_cast<int64_t>(gi) * ntiles) / groups) * kTileKeys;
+  const uint16_t* Kh = K + bh * N * kD;
+  u32x4 ko[4][2], qo[4][2];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const int64_t row = t0 + 16 * kb + c16;
+    const int64_t rr = row < N ? row : N - 1;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      ko[kb][s] = *reinterpret_cast<const u32x4*>(Kh + rr * kD + 32 * s + 8 * g);
+  }
+#pragma unroll
+  for (int lb = 0; lb < 4; ++lb) {
+    const int lr = min(16 * lb + c16, m - 1);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      qo[lb][s] = *reinterpret_cast<const u32x4*>(Ql + (bh * m + lr) * kD + 32 * s + 8 * g);
+  }
+#pragma unroll
+  for (int lb = 0; lb < 4; ++lb) {
+    if (16 * lb >= m) break;  // uniform
+    f32x4 sc[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      sc[kb] = mfma_bf16(as_bf16x8(ko[kb][0]), as_bf16x8(qo[lb][0]), f32x4{0, 0, 0, 0});
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      sc[kb] = mfma_bf16(as_bf16x8(ko[kb][1]), as_bf16x8(qo[lb][1]), sc[kb]);
+    uint64_t best = 0;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t t = t0 + 16 * kb + 4 * g + r;
+        if (t < N) {
+          const uint64_t key = make_key(sc[kb][r], static_cast<uint32_t>(t));
+          best = key > best ? key : best;
+        }
+      }
+#pragma unroll
+    for (int mask = 16; mask <= 32; mask <<= 1) {
+      const uint64_t o = lane_read(best, l ^ mask);
+      best = o > best ? o : best;
+    }
+    const int lm = 16 * lb + c16;
+    if (g == 0 && lm < m) gmax[(bh * m + lm) * groups + gi] = best;
   }
 }
 
@@ -907,9 +988,15 @@ template <class T>
 static hipError_t launch_theta_t(const Shape& s, const void* K, const Workspace& ws,
                                  hipStream_t st) {
   using E = typename T::elem;
-  hipLaunchKernelGGL(k_theta_sample<T>, dim3(s.theta_groups / kThetaTilesPerBlock, s.BH), dim3(256),
-                     0, st, static_cast<const E*>(K), static_cast<const E*>(ws.ql), s.N, s.m,
-                     s.theta_groups, ws.gmax);
+  if constexpr (std::is_same<T, BF16>::value) {
+    hipLaunchKernelGGL(k_theta_sample_bf16, dim3((s.theta_groups + 3) / 4, s.BH), dim3(256), 0,
+                       st, static_cast<const E*>(K), static_cast<const E*>(ws.ql), s.N, s.m,
+                       s.theta_groups, ws.gmax);
+  } else {
+    hipLaunchKernelGGL(k_theta_sample<T>, dim3(s.theta_groups / kThetaTilesPerBlock, s.BH),
+                       dim3(256), 0, st, static_cast<const E*>(K), static_cast<const E*>(ws.ql),
+                       s.N, s.m, s.theta_groups, ws.gmax);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_theta_select, dim3(s.m, s.BH), dim3(256), 0, st, ws.gmax, s.m, s.k,

@@ -16,7 +16,7 @@ constexpr int kTileKeys = 64;    // keys per landmark-scan tile
 constexpr int kRouteSeg = 1024;  // queries per routing/bucketing segment
 constexpr int kAttendTile = 64;  // queries per expert-attention tile
 constexpr int kAttendMaxTpb = 16;  // tiles per expert-attention work item, at most
-constexpr int kPoolChunk = 2048; // tokens per pooling partial sum
+constexpr int kPoolChunk = 4096; // tokens per pooling partial sum (fewer, longer blocks stream faster)
 constexpr int kThetaTilesPerBlock = 1;  // sample tiles per top-k pre-threshold block
 
 struct Shape {

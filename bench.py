@@ -32,9 +32,9 @@ KERNEL_SOURCES = {"k_scan": "kernels_scan.hip", "k_route": "kernels_route.hip",
 # kernel whose sources changed since reports traffic null.
 COUNTED_TRAFFIC = {
     "len_1m": {
-        "k_scan": {"sha": "f73ac051c435", "bytes": 1096191301},
-        "k_route": {"sha": "cd4bc04bf2a7", "bytes": 564126350},
-        "k_attend": {"sha": "0c1633766ba0", "bytes": 1636630319},
+        "k_scan": {"sha": "c8b4458f6cbb", "bytes": 1094160531},
+        "k_route": {"sha": "7ad89cdef050", "bytes": 565860716},
+        "k_attend": {"sha": "e8c5e1249f41", "bytes": 1637647671},
     },
 }
 

@@ -822,32 +822,99 @@ __global__ __launch_bounds__(256) void k_theta_sample_bf16(const uint16_t* __res
   }
 }
 
-// grid (m, BH), 256 threads: theta[bh][lm] = score of the k-th largest group
-// maximum, lowered by one ulp so that the scan's strict test (s > theta)
-// keeps every score equal to it; -inf when fewer than k maxima exist.
+// Below the size where tile sampling applies: groups of GS consecutive keys
+// (GS = 1: every key is its own group, so the threshold is the exact k-th
+// largest score; GS = 16: the maximum of each 16-key block).  grid (key
+// tiles, BH), 256 threads; wave w: landmarks 16w..16w+15.  Scores use the
+// scan's operand layout and accumulation order, so they are bitwise the
+// scores the scan computes.
+template <class T, int GS>
+__global__ __launch_bounds__(256) void k_theta_fine(const typename T::elem* __restrict__ K,
+                                                   const typename T::elem* __restrict__ Ql,
+                                                   int64_t N, int m, int groups,
+                                                   uint64_t* __restrict__ gmax) {
+  static_assert(GS == 1 || GS == 16, "groups of 1 or 16 keys");
+  using TR = ScanTraits<T>;
+  const int l = lane_id(), g = l >> 4, c16 = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(wave_id());
+  if (w * 16 >= m) return;  // whole wave beyond the landmarks
+  const int64_t bh = blockIdx.y;
+  const int lm = w * 16 + c16;
+  const bool lm_ok = lm < m;
+  typename TR::QReg q;
+  TR::load_q(q, Ql + (bh * m + (lm_ok ? lm : m - 1)) * kD, true, g);
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTileKeys;
+  f32x4 sc[4];
+  TR::score_tile_global(K + bh * N * kD, t0, N, q, c16, g, sc);
+  uint64_t* G = gmax + (bh * m + (lm_ok ? lm : 0)) * groups;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    uint64_t key[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t t = t0 + 16 * kb + 4 * g + r;
+      key[r] = t < N ? make_key(sc[kb][r], static_cast<uint32_t>(t)) : 0ull;
+    }
+    if constexpr (GS == 1) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t t = t0 + 16 * kb + 4 * g + r;
+        if (lm_ok && t < N) G[t] = key[r];
+      }
+    } else {
+      uint64_t best = key[0];
+#pragma unroll
+      for (int r = 1; r < 4; ++r) best = key[r] > best ? key[r] : best;
+#pragma unroll
+      for (int mask = 16; mask <= 32; mask <<= 1) {
+        const uint64_t o = lane_read(best, l ^ mask);
+        best = o > best ? o : best;
+      }
+      const int64_t gi = (t0 >> 4) + kb;
+      if (g == 0 && lm_ok && gi < groups) G[gi] = best;
+    }
+  }
+}
+
+// grid (ceil(m / 4), BH), 256 threads; wave w: landmark 4 * blockIdx.x + w.
+// theta[bh][lm] = the k-th largest group maximum's score, lowered by one ulp
+// so that the scan's strict test (s > theta) keeps every score equal to it;
+// -inf when fewer than k maxima exist.  The k-th largest score comes from a
+// bisection over the scores' 32-bit order (the upper half of the keys): the
+// largest T with at least k maxima at or above T.  Each step counts with one
+// ballot per register, so the search stays uniform across the wave.  KPL:
+// maxima per lane (groups <= 64 * KPL).
+template <int KPL>
 __global__ __launch_bounds__(256) void k_theta_select(const uint64_t* __restrict__ gmax, int m,
                                                      int k, int groups, int mrows,
                                                      float* __restrict__ theta) {
-  __shared__ uint64_t tops[4][64];
-  const int l = lane_id(), w = wave_id(), lm = blockIdx.x;
+  const int l = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(wave_id());
+  const int lm = static_cast<int>(blockIdx.x) * 4 + w;
+  if (lm >= m) return;  // whole wave
   const int64_t bh = blockIdx.y;
   const uint64_t* G = gmax + (bh * m + lm) * groups;
-  uint64_t top = 0;
-  for (int c = w; c * 64 < groups; c += 4) {
-    const int i = c * 64 + l;
-    uint64_t v = i < groups ? G[i] : 0ull;
-    v = wave_sort_desc(v);
-    top = wave_merge_top(top, v);
-  }
-  tops[w][l] = top;
-  __syncthreads();
-  if (w != 0) return;
-  uint64_t t = tops[0][l];
+  uint32_t v[KPL];  // 0: no maximum (below every real key's order bits)
 #pragma unroll
-  for (int v = 1; v < 4; ++v) t = wave_merge_top(t, tops[v][l]);
-  const uint64_t kth = uniform_read(t, k - 1);
+  for (int j = 0; j < KPL; ++j) {
+    const int i = 64 * j + l;
+    v[j] = i < groups ? static_cast<uint32_t>(G[i] >> 32) : 0u;
+  }
+  // invariant: at least k values >= lo (lo = 0 holds: 64 * KPL >= groups >= k)
+  uint32_t lo = 0u, hi = 0xFFFFFFFFu;
+  while (lo < hi) {
+    const uint32_t mid = lo + ((hi - lo) >> 1) + 1u;
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) cnt += __popcll(ballot(v[j] >= mid));
+    if (cnt >= k)
+      lo = mid;
+    else
+      hi = mid - 1u;
+  }
   if (l == 0)
-    theta[bh * mrows + lm] = kth != 0ull ? nextafterf(key_score(kth), -INFINITY) : -INFINITY;
+    theta[bh * mrows + lm] =
+        lo != 0u ? nextafterf(key_score(static_cast<uint64_t>(lo) << 32), -INFINITY) : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -988,7 +1055,17 @@ template <class T>
 static hipError_t launch_theta_t(const Shape& s, const void* K, const Workspace& ws,
                                  hipStream_t st) {
   using E = typename T::elem;
-  if constexpr (std::is_same<T, BF16>::value) {
+  const int64_t ktiles = (s.N + kTileKeys - 1) / kTileKeys;
+  if (s.theta_gs == 1 || s.theta_gs == 16) {
+    if (s.theta_gs == 1)
+      hipLaunchKernelGGL((k_theta_fine<T, 1>), dim3(ktiles, s.BH), dim3(256), 0, st,
+                         static_cast<const E*>(K), static_cast<const E*>(ws.ql), s.N, s.m,
+                         s.theta_groups, ws.gmax);
+    else
+      hipLaunchKernelGGL((k_theta_fine<T, 16>), dim3(ktiles, s.BH), dim3(256), 0, st,
+                         static_cast<const E*>(K), static_cast<const E*>(ws.ql), s.N, s.m,
+                         s.theta_groups, ws.gmax);
+  } else if constexpr (std::is_same<T, BF16>::value) {
     hipLaunchKernelGGL(k_theta_sample_bf16, dim3((s.theta_groups + 3) / 4, s.BH), dim3(256), 0,
                        st, static_cast<const E*>(K), static_cast<const E*>(ws.ql), s.N, s.m,
                        s.theta_groups, ws.gmax);
@@ -999,8 +1076,13 @@ static hipError_t launch_theta_t(const Shape& s, const void* K, const Workspace&
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_theta_select, dim3(s.m, s.BH), dim3(256), 0, st, ws.gmax, s.m, s.k,
-                     s.theta_groups, s.mrows, ws.theta);
+  if (s.theta_groups > 64 * 64) return hipErrorInvalidValue;  // beyond the selection's registers
+  if (s.theta_groups <= 64 * 16)
+    hipLaunchKernelGGL(k_theta_select<16>, dim3((s.m + 3) / 4, s.BH), dim3(256), 0, st, ws.gmax,
+                       s.m, s.k, s.theta_groups, s.mrows, ws.theta);
+  else
+    hipLaunchKernelGGL(k_theta_select<64>, dim3((s.m + 3) / 4, s.BH), dim3(256), 0, st, ws.gmax,
+                       s.m, s.k, s.theta_groups, s.mrows, ws.theta);
   return hipGetLastError();
 }
 

@@ -260,6 +260,18 @@ void derive(Shape& s, int cus) {
   if (groups > 1024) groups = 1024;
   groups = groups / kThetaTilesPerBlock * kThetaTilesPerBlock;
   s.theta_groups = (groups >= 64 && groups >= s.k) ? static_cast<int>(groups) : 0;
+  s.theta_gs = 64;
+  if (s.theta_groups == 0 && s.N >= s.k) {
+    // too few tiles to sample: every key (exact k-th largest score) up to
+    // kThetaExactKeys keys, else the maxima of 16-key blocks
+    if (s.N <= kThetaExactKeys) {
+      s.theta_gs = 1;
+      s.theta_groups = static_cast<int>(s.N);
+    } else if (cdiv(s.N, 16) >= (s.k > 64 ? s.k : 64)) {
+      s.theta_gs = 16;
+      s.theta_groups = static_cast<int>(cdiv(s.N, 16));
+    }
+  }
   s.nseg = static_cast<int>(cdiv(s.N, kRouteSeg));
   // expert attention: work items of up to 16 tiles, keeping >= 4 items per CU
   const int64_t tiles = cdiv(s.N, kAttendTile);

@@ -18,6 +18,7 @@ constexpr int kAttendTile = 64;  // queries per expert-attention tile
 constexpr int kAttendMaxTpb = 16;  // tiles per expert-attention work item, at most
 constexpr int kPoolChunk = 4096; // tokens per pooling partial sum (fewer, longer blocks stream faster)
 constexpr int kThetaTilesPerBlock = 1;  // sample tiles per top-k pre-threshold block
+constexpr int kThetaExactKeys = 4096;  // up to this many keys the pre-threshold uses every key
 
 struct Shape {
   int64_t B = 0, H = 0, BH = 0, N = 0;
@@ -34,7 +35,8 @@ struct Shape {
   int scan_splits = 0;
   int merge_parts = 0; // first-level merge partitions per landmark (1: single pass)
   int pool_splits = 0; // partial sums per landmark window
-  int theta_groups = 0;// sample tiles for the top-k pre-threshold (0: off)
+  int theta_groups = 0;// sample groups for the top-k pre-threshold (0: off)
+  int theta_gs = 64;    // keys per group: 64 (sampled tiles), 16 or 1 (every key)
   int nseg = 0;        // routing segments per head
   int attend_tpb = 0;   // 64-query tiles per expert-attention work item
   int attend_items = 0; // upper bound of work items per head
@@ -44,7 +46,7 @@ struct Shape {
 struct Workspace {
   double* pool_part = nullptr;   // [BH][m][pool_splits][64] fp64 partial window sums
   void* ql = nullptr;            // [BH][m][64] landmark queries (input type)
-  uint64_t* gmax = nullptr;      // [BH][m][theta_groups] per-sample-tile maximum keys
+  uint64_t* gmax = nullptr;      // [BH][m][theta_groups] per-group maximum keys
   float* theta = nullptr;        // [BH][mrows] top-k pre-threshold (nullptr: off)
   uint64_t* part_keys = nullptr; // [BH][splits][mrows][64] per-split top lists (first
                                  //   part_cnt entries valid, descending)

@@ -928,19 +928,25 @@ __global__ __launch_bounds__(256) void k_theta_select(const uint64_t* __restrict
 // best.  FINAL (P = 1): writes idx_out (ascending) and Vl.  Otherwise the
 // block's combined top list and softmax state go to the out_* arrays in the
 // layout of the scan's partials with P "splits", for a FINAL pass.
-template <bool FINAL>
+template <bool FINAL, int NWM>
 __global__ __launch_bounds__(256) void k_merge(
     const uint64_t* __restrict__ part_keys, const int32_t* __restrict__ part_cnt,
     const float* __restrict__ part_stats, const float* __restrict__ part_acc, int m, int k,
     int mrows, int splits, int32_t* __restrict__ idx_out, float* __restrict__ vl,
     float* __restrict__ vl_copy, uint64_t* __restrict__ out_keys, int32_t* __restrict__ out_cnt,
     float* __restrict__ out_stats, float* __restrict__ out_acc) {
+  static_assert(NWM == 1 || NWM == 4, "one or four waves per landmark");
   constexpr int kBatch = 8;
-  __shared__ uint64_t tops[4][64];
-  __shared__ float sacc[4][64];
-  __shared__ float sM[4], sL[4];
-  const int l = lane_id(), lm = blockIdx.x;
+  __shared__ uint64_t tops[NWM][64];
+  __shared__ float sacc[NWM][64];
+  __shared__ float sM[NWM], sL[NWM];
+  const int l = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(wave_id());
+  // NWM = 4: the block's four waves share landmark blockIdx.x.  NWM = 1: each
+  // wave takes a landmark of its own (4 * blockIdx.x + w) and all of its splits.
+  const int lm = NWM == 4 ? static_cast<int>(blockIdx.x) : static_cast<int>(blockIdx.x) * 4 + w;
+  const int wi = NWM == 4 ? w : 0;  // the wave's index among its landmark's waves
+  if (lm >= m) return;  // whole wave (NWM = 1 only)
   const int64_t bh = blockIdx.y;
   const int P = gridDim.z, p = blockIdx.z;
   const int64_t row0 = bh * splits * mrows + lm;  // partial row of split s: row0 + s * mrows
@@ -948,12 +954,12 @@ __global__ __launch_bounds__(256) void k_merge(
 
   uint64_t top = 0;
   float Mw = -INFINITY, Lw = 0.f, aw = 0.f;
-  for (int i0 = w; i0 < nmine; i0 += 4 * kBatch) {
+  for (int i0 = wi; i0 < nmine; i0 += NWM * kBatch) {
     int cnt[kBatch];
     float Ms[kBatch], Ls[kBatch], as[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const int i = i0 + 4 * u;
+      const int i = i0 + NWM * u;
       const int64_t r = row0 + static_cast<int64_t>(p + P * i) * mrows;
       const bool ok = i < nmine;
       cnt[u] = ok ? part_cnt[r] : 0;
@@ -964,7 +970,7 @@ __global__ __launch_bounds__(256) void k_merge(
     uint64_t lst[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {  // issued with the loads above; masked once cnt is in
-      const int i = i0 + 4 * u;
+      const int i = i0 + NWM * u;
       const int64_t r = row0 + static_cast<int64_t>(i < nmine ? p + P * i : p) * mrows;
       lst[u] = part_keys[r * kTopCap + l];
     }
@@ -972,7 +978,7 @@ __global__ __launch_bounds__(256) void k_merge(
     for (int u = 0; u < kBatch; ++u) lst[u] = (l < cnt[u]) ? lst[u] : 0ull;
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      if (i0 + 4 * u >= nmine) break;
+      if (i0 + NWM * u >= nmine) break;
       const float Mn = fmaxf(Mw, Ms[u]);
       const float f0 = fast_exp2(Mw - Mn), f1 = fast_exp2(Ms[u] - Mn);
       Lw = Lw * f0 + Ls[u] * f1;
@@ -982,32 +988,36 @@ __global__ __launch_bounds__(256) void k_merge(
         top = wave_merge_top(top, lst[u]);
     }
   }
-  tops[w][l] = top;
-  sacc[w][l] = aw;
-  if (l == 0) {
-    sM[w] = Mw;
-    sL[w] = Lw;
-  }
-  __syncthreads();
-  if (w != 0) return;
+  uint64_t t = top;
+  float Mt = Mw, Lt = Lw, at = aw;
+  if constexpr (NWM == 4) {
+    tops[w][l] = top;
+    sacc[w][l] = aw;
+    if (l == 0) {
+      sM[w] = Mw;
+      sL[w] = Lw;
+    }
+    __syncthreads();
+    if (w != 0) return;
 
-  uint64_t t = tops[0][l];
+    t = tops[0][l];
 #pragma unroll
-  for (int v = 1; v < 4; ++v) {
-    const uint64_t o = tops[v][l];
-    if (uniform_read(o, 0) > uniform_read(t, k - 1)) t = wave_merge_top(t, o);
-  }
-
-  float Mt = -INFINITY;
+    for (int v = 1; v < 4; ++v) {
+      const uint64_t o = tops[v][l];
+      if (uniform_read(o, 0) > uniform_read(t, k - 1)) t = wave_merge_top(t, o);
+    }
+    Mt = -INFINITY;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) Mt = fmaxf(Mt, sM[v]);
-  float Lt = 0.f, at = 0.f;
+    for (int v = 0; v < 4; ++v) Mt = fmaxf(Mt, sM[v]);
+    Lt = 0.f;
+    at = 0.f;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    if (sM[v] == -INFINITY) continue;  // a wave that had no split
-    const float f = fast_exp2(sM[v] - Mt);
-    Lt += sL[v] * f;
-    at += sacc[v][l] * f;
+    for (int v = 0; v < 4; ++v) {
+      if (sM[v] == -INFINITY) continue;  // a wave that had no split
+      const float f = fast_exp2(sM[v] - Mt);
+      Lt += sL[v] * f;
+      at += sacc[v][l] * f;
+    }
   }
   if constexpr (FINAL) {
     int32_t ix = (l < k) ? static_cast<int32_t>(key_index(t)) : INT32_MAX;
@@ -1103,21 +1113,42 @@ hipError_t launch_scan(const Shape& s, const void* K, const void* V, const Works
 
 hipError_t launch_merge(const Shape& s, const Workspace& ws, int32_t* idx_out, float* vl_copy,
                         hipStream_t st) {
+  // one wave per landmark (four landmarks per block) when a landmark has at
+  // most 4 partials, else four waves per landmark (the one wave merges its
+  // partials one after another: shorter only for a few)
+  const dim3 g1(s.m, s.BH, 1), g4((s.m + 3) / 4, s.BH, 1);
   if (s.merge_parts > 1) {  // first level: merge_parts partial combinations per landmark
-    hipLaunchKernelGGL(k_merge<false>, dim3(s.m, s.BH, s.merge_parts), dim3(256), 0, st,
-                       ws.part_keys, ws.part_cnt, ws.part_stats, ws.part_acc, s.m, s.k, s.mrows,
-                       s.scan_splits, nullptr, nullptr, nullptr, ws.part2_keys, ws.part2_cnt,
-                       ws.part2_stats, ws.part2_acc);
+    const int per = (s.scan_splits + s.merge_parts - 1) / s.merge_parts;
+    if (per <= 4)
+      hipLaunchKernelGGL((k_merge<false, 1>), dim3(g4.x, s.BH, s.merge_parts), dim3(256), 0, st,
+                         ws.part_keys, ws.part_cnt, ws.part_stats, ws.part_acc, s.m, s.k, s.mrows,
+                         s.scan_splits, nullptr, nullptr, nullptr, ws.part2_keys, ws.part2_cnt,
+                         ws.part2_stats, ws.part2_acc);
+    else
+      hipLaunchKernelGGL((k_merge<false, 4>), dim3(s.m, s.BH, s.merge_parts), dim3(256), 0, st,
+                         ws.part_keys, ws.part_cnt, ws.part_stats, ws.part_acc, s.m, s.k, s.mrows,
+                         s.scan_splits, nullptr, nullptr, nullptr, ws.part2_keys, ws.part2_cnt,
+                         ws.part2_stats, ws.part2_acc);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_merge<true>, dim3(s.m, s.BH, 1), dim3(256), 0, st, ws.part2_keys,
-                       ws.part2_cnt, ws.part2_stats, ws.part2_acc, s.m, s.k, s.mrows,
-                       s.merge_parts, idx_out, ws.vl, vl_copy, nullptr, nullptr, nullptr, nullptr);
+    if (s.merge_parts <= 4)
+      hipLaunchKernelGGL((k_merge<true, 1>), g4, dim3(256), 0, st, ws.part2_keys, ws.part2_cnt,
+                         ws.part2_stats, ws.part2_acc, s.m, s.k, s.mrows, s.merge_parts, idx_out,
+                         ws.vl, vl_copy, nullptr, nullptr, nullptr, nullptr);
+    else
+      hipLaunchKernelGGL((k_merge<true, 4>), g1, dim3(256), 0, st, ws.part2_keys, ws.part2_cnt,
+                         ws.part2_stats, ws.part2_acc, s.m, s.k, s.mrows, s.merge_parts, idx_out,
+                         ws.vl, vl_copy, nullptr, nullptr, nullptr, nullptr);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(k_merge<true>, dim3(s.m, s.BH, 1), dim3(256), 0, st, ws.part_keys,
-                     ws.part_cnt, ws.part_stats, ws.part_acc, s.m, s.k, s.mrows, s.scan_splits,
-                     idx_out, ws.vl, vl_copy, nullptr, nullptr, nullptr, nullptr);
+  if (s.scan_splits <= 4)
+    hipLaunchKernelGGL((k_merge<true, 1>), g4, dim3(256), 0, st, ws.part_keys, ws.part_cnt,
+                       ws.part_stats, ws.part_acc, s.m, s.k, s.mrows, s.scan_splits, idx_out,
+                       ws.vl, vl_copy, nullptr, nullptr, nullptr, nullptr);
+  else
+    hipLaunchKernelGGL((k_merge<true, 4>), g1, dim3(256), 0, st, ws.part_keys, ws.part_cnt,
+                       ws.part_stats, ws.part_acc, s.m, s.k, s.mrows, s.scan_splits, idx_out,
+                       ws.vl, vl_copy, nullptr, nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
 

@@ -25,14 +25,15 @@
 namespace mita {
 
 constexpr int kAttendWaves = 8;       // bf16 expert attention: waves per block
-constexpr int kAttendThreads = 64 * kAttendWaves;
+constexpr int kAttendShortItems = 256;  // below this many queries per expert (mean): 2 waves
 constexpr int kOStageStride = 68;     // floats per staged output row (bank spread)
 
-template <class T, int MPAD, int KPAD>
+template <class T, int MPAD, int KPAD, int NW = kAttendWaves>
 struct AttendLds;
 
-template <int MPAD, int KPAD>
-struct AttendLds<BF16, MPAD, KPAD> {
+// NW: waves per block (each stages its own output rows)
+template <int MPAD, int KPAD, int NW>
+struct AttendLds<BF16, MPAD, KPAD, NW> {
   static constexpr int PKST = 72;        // pair-key rows (bf16 elements)
   static constexpr int VCST = MPAD + 4;  // compressed Vl^T rows (fp16)
   static constexpr int VRST = KPAD + 4;  // raw V^T rows (fp16)
@@ -40,12 +41,12 @@ struct AttendLds<BF16, MPAD, KPAD> {
   alignas(16) uint16_t vc[kD * VCST];  // fp16 2^-s * Vl^T
   alignas(16) uint16_t vr[kD * VRST];  // fp16 2^-s * V^T of the expert's rows
   alignas(16) int32_t perm[kAttendTile * kAttendMaxTpb];  // the work item's query indices
-  alignas(16) float ostage[kAttendWaves][16 * kOStageStride];  // per-wave output rows
+  alignas(16) float ostage[NW][16 * kOStageStride];  // per-wave output rows
   uint32_t vmax;            // bits of the largest |value| staged (>= 0)
 };
 
-template <int MPAD, int KPAD>
-struct AttendLds<F32, MPAD, KPAD> {
+template <int MPAD, int KPAD, int NW>
+struct AttendLds<F32, MPAD, KPAD, NW> {
   static constexpr int PKST = 68;
   static constexpr int VST = 68;
   alignas(16) float pk[(MPAD + KPAD) * PKST];
@@ -89,65 +90,75 @@ __device__ __forceinline__ int64_t clamp_index(int64_t v, int64_t n) {
 // The output multiplies the 2^s back.
 
 // Stage the expert of this work item; returns the value scale exponent s.
-template <int MPAD, int KPAD>
-__device__ int stage_bf16(AttendLds<BF16, MPAD, KPAD>& S, const uint16_t* __restrict__ K,
+template <int MPAD, int KPAD, int NW>
+__device__ int stage_bf16(AttendLds<BF16, MPAD, KPAD, NW>& S, const uint16_t* __restrict__ K,
                           const uint16_t* __restrict__ V, const uint16_t* __restrict__ Ql,
                           const float* __restrict__ vl, const int32_t* __restrict__ ex, int64_t N,
                           int m, int k, int64_t bh) {
-  using L = AttendLds<BF16, MPAD, KPAD>;
+  using L = AttendLds<BF16, MPAD, KPAD, NW>;
   constexpr int NP = MPAD + KPAD;
+  constexpr int NT = 64 * NW;
   const int tid = threadIdx.x;
   const u32x4 z = {0, 0, 0, 0};
   if (tid == 0) S.vmax = 0u;
   __syncthreads();
 
-  // raw values: rows 2rp, 2rp+1 of the expert, 8 features from 8*col
-  const bool vr_ok = tid < (KPAD / 2) * 8;
-  const int rp = tid >> 3, col = tid & 7;
-  u32x4 va = z, vb = z;
+  // raw values: unit u = rows 2rp, 2rp+1 of the expert, 8 features from 8*col
+  constexpr int RU = (KPAD / 2) * 8, RN = (RU + NT - 1) / NT;
+  u32x4 va[RN], vb[RN];
   uint32_t mbits = 0;  // largest |bf16| bit pattern seen
-  if (vr_ok) {
-    if (2 * rp < k)
-      va = *reinterpret_cast<const u32x4*>(V + (bh * N + clamp_index(ex[2 * rp], N)) * kD + col * 8);
-    if (2 * rp + 1 < k)
-      vb = *reinterpret_cast<const u32x4*>(V + (bh * N + clamp_index(ex[2 * rp + 1], N)) * kD +
-                                           col * 8);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      mbits = max(mbits, max(va[i] & 0x7FFFu, (va[i] >> 16) & 0x7FFFu));
-      mbits = max(mbits, max(vb[i] & 0x7FFFu, (vb[i] >> 16) & 0x7FFFu));
+  for (int j = 0; j < RN; ++j) {
+    const int u = tid + NT * j, rp = u >> 3, col = u & 7;
+    va[j] = z;
+    vb[j] = z;
+    if (u < RU) {
+      if (2 * rp < k)
+        va[j] = *reinterpret_cast<const u32x4*>(V + (bh * N + clamp_index(ex[2 * rp], N)) * kD +
+                                                col * 8);
+      if (2 * rp + 1 < k)
+        vb[j] = *reinterpret_cast<const u32x4*>(V + (bh * N + clamp_index(ex[2 * rp + 1], N)) * kD +
+                                                col * 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        mbits = max(mbits, max(va[j][i] & 0x7FFFu, (va[j][i] >> 16) & 0x7FFFu));
+        mbits = max(mbits, max(vb[j][i] & 0x7FFFu, (vb[j][i] >> 16) & 0x7FFFu));
+      }
     }
   }
   float vmax = __uint_as_float(mbits << 16);
-  // landmark values: rows 2lp, 2lp+1, 8 features from 8*dc
+  // landmark values: unit u = rows 2lp, 2lp+1, 8 features from 8*dc
   constexpr int LP = MPAD / 2;
-  const bool vl_ok = tid < LP * 8;
-  const int lp = tid % LP, dc = tid / LP;
-  float la[8], lb[8];
+  constexpr int LU = LP * 8, LN = (LU + NT - 1) / NT;
+  float la[LN][8], lb[LN][8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) la[i] = lb[i] = 0.f;
-  if (vl_ok) {
+  for (int j = 0; j < LN; ++j) {
+    const int u = tid + NT * j, lp = u % LP, dc = u / LP;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int row = 2 * lp + h;
-      if (row < m) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(vl + (bh * m + row) * kD + dc * 8);
-        const f32x4 b = *reinterpret_cast<const f32x4*>(vl + (bh * m + row) * kD + dc * 8 + 4);
-        float* dst = h ? lb : la;
+    for (int i = 0; i < 8; ++i) la[j][i] = lb[j][i] = 0.f;
+    if (u < LU) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          dst[i] = a[i];
-          dst[4 + i] = b[i];
+      for (int h = 0; h < 2; ++h) {
+        const int row = 2 * lp + h;
+        if (row < m) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(vl + (bh * m + row) * kD + dc * 8);
+          const f32x4 b = *reinterpret_cast<const f32x4*>(vl + (bh * m + row) * kD + dc * 8 + 4);
+          float* dst = h ? lb[j] : la[j];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            dst[i] = a[i];
+            dst[4 + i] = b[i];
+          }
         }
       }
-    }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) vmax = fmaxf(vmax, fmaxf(fabsf(la[i]), fabsf(lb[i])));
+      for (int i = 0; i < 8; ++i) vmax = fmaxf(vmax, fmaxf(fabsf(la[j][i]), fabsf(lb[j][i])));
+    }
   }
   atomicMax(&S.vmax, __float_as_uint(vmax));
 
   // pair keys: Ql rows then the expert's K rows (zero rows for padding)
-  for (int c = tid; c < NP * 8; c += kAttendThreads) {
+  for (int c = tid; c < NP * 8; c += NT) {
     const int row = c >> 3, cc = c & 7;
     u32x4 v = z;
     if (row < MPAD) {
@@ -163,20 +174,28 @@ __device__ int stage_bf16(AttendLds<BF16, MPAD, KPAD>& S, const uint16_t* __rest
   const int e = static_cast<int>((S.vmax >> 23) & 0xFF) - 127;
   const int sh = e > 14 ? e - 14 : 0;  // 2^-sh * max|value| < 2^15
   const float sc = exp2i(-sh);
-  if (vr_ok) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t wa = va[i >> 1], wb = vb[i >> 1];
-      const float a = __uint_as_float((i & 1) ? (wa & 0xFFFF0000u) : (wa << 16));
-      const float b = __uint_as_float((i & 1) ? (wb & 0xFFFF0000u) : (wb << 16));
-      *reinterpret_cast<uint32_t*>(S.vr + (col * 8 + i) * L::VRST + 2 * rp) = pack_f16(a * sc, b * sc);
+  for (int j = 0; j < RN; ++j) {
+    const int u = tid + NT * j, rp = u >> 3, col = u & 7;
+    if (u < RU) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t wa = va[j][i >> 1], wb = vb[j][i >> 1];
+        const float a = __uint_as_float((i & 1) ? (wa & 0xFFFF0000u) : (wa << 16));
+        const float b = __uint_as_float((i & 1) ? (wb & 0xFFFF0000u) : (wb << 16));
+        *reinterpret_cast<uint32_t*>(S.vr + (col * 8 + i) * L::VRST + 2 * rp) =
+            pack_f16(a * sc, b * sc);
+      }
     }
   }
-  if (vl_ok) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      *reinterpret_cast<uint32_t*>(S.vc + (dc * 8 + i) * L::VCST + 2 * lp) =
-          pack_f16(la[i] * sc, lb[i] * sc);
+  for (int j = 0; j < LN; ++j) {
+    const int u = tid + NT * j, lp = u % LP, dc = u / LP;
+    if (u < LU) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<uint32_t*>(S.vc + (dc * 8 + i) * L::VCST + 2 * lp) =
+            pack_f16(la[j][i] * sc, lb[j][i] * sc);
     }
   }
   return sh;
@@ -185,13 +204,13 @@ __device__ int stage_bf16(AttendLds<BF16, MPAD, KPAD>& S, const uint16_t* __rest
 // 16 queries of one wave (lane column c16 = query) against the staged expert
 // `after_scores` runs once the logits have been formed (the Q operand is then
 // free, so the caller can refill it while the rest of the sub-tile runs).
-template <int MPAD, int KPAD, bool FULL, class AfterScores>
-__device__ __forceinline__ void attend_queries_bf16(AttendLds<BF16, MPAD, KPAD>& S,
+template <int MPAD, int KPAD, int NW, bool FULL, class AfterScores>
+__device__ __forceinline__ void attend_queries_bf16(AttendLds<BF16, MPAD, KPAD, NW>& S,
                                                     bf16x8 (&qb)[2], int sl0, int nq, int m,
                                                     int k, float c2, float oscale,
                                                     float* __restrict__ out_h,
                                                     AfterScores&& after_scores) {
-  using L = AttendLds<BF16, MPAD, KPAD>;
+  using L = AttendLds<BF16, MPAD, KPAD, NW>;
   constexpr int NPB = (MPAD + KPAD) / 16;
   const int l = lane_id(), g = l >> 4, c16 = l & 15;
   float x[NPB][4];
@@ -282,8 +301,8 @@ __device__ __forceinline__ void attend_queries_bf16(AttendLds<BF16, MPAD, KPAD>&
   }
 }
 
-template <int MPAD, int KPAD, bool FULL>
-__device__ void attend_bf16(AttendLds<BF16, MPAD, KPAD>& S, const uint16_t* __restrict__ Q,
+template <int MPAD, int KPAD, bool FULL, int NW>
+__device__ void attend_bf16(AttendLds<BF16, MPAD, KPAD, NW>& S, const uint16_t* __restrict__ Q,
                             const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                             const uint16_t* __restrict__ Ql, const float* __restrict__ vl,
                             const int32_t* __restrict__ idx, const int32_t* __restrict__ perm,
@@ -300,7 +319,7 @@ __device__ void attend_bf16(AttendLds<BF16, MPAD, KPAD>& S, const uint16_t* __re
   // wave w handles sub-tiles w, w+W, w+2W, ...; every slot index is clamped
   // to the item's last query, so each Q gather reads a valid row and needs no
   // branch (the wait counters then stay exact across the ring)
-  constexpr int W = kAttendWaves;
+  constexpr int W = NW;
   auto slot = [&](int i) { return min(16 * (w + W * i) + c16, nq - 1); };
   auto load_q = [&](int64_t q, bf16x8 (&qb)[2]) {
 #pragma unroll
@@ -314,9 +333,9 @@ __device__ void attend_bf16(AttendLds<BF16, MPAD, KPAD>& S, const uint16_t* __re
   bf16x8 ring[D][2];
 #pragma unroll
   for (int j = 0; j < D; ++j) load_q(clamp_index(p0[j], N), ring[j]);
-  for (int c = tid; c < nq; c += kAttendThreads)
+  for (int c = tid; c < nq; c += 64 * NW)
     S.perm[c] = static_cast<int32_t>(clamp_index(ph[ti.qb + c], N));
-  const int sh = stage_bf16<MPAD, KPAD>(S, K, V, Ql, vl, idx + (bh * m + ti.e) * k, N, m, k, bh);
+  const int sh = stage_bf16<MPAD, KPAD, NW>(S, K, V, Ql, vl, idx + (bh * m + ti.e) * k, N, m, k, bh);
   const float oscale = exp2i(sh);
   __syncthreads();
 
@@ -334,7 +353,7 @@ __device__ void attend_bf16(AttendLds<BF16, MPAD, KPAD>& S, const uint16_t* __re
         // scheduler from interleaving sub-tiles (both keep occupancy)
         __asm__ volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
-        attend_queries_bf16<MPAD, KPAD, FULL>(
+        attend_queries_bf16<MPAD, KPAD, NW, FULL>(
             S, ring[j], 16 * (w + W * i), nq, m, k, c2, oscale, out_h,
             [&](bf16x8(&qb)[2]) { load_q(S.perm[slot(i + D)], qb); });  // sub-tile i + D
       }
@@ -344,8 +363,8 @@ __device__ void attend_bf16(AttendLds<BF16, MPAD, KPAD>& S, const uint16_t* __re
 #pragma unroll
     for (int j = 0; j < D; ++j)
       if (j < nw)
-        attend_queries_bf16<MPAD, KPAD, FULL>(S, ring[j], 16 * (w + W * j), nq, m, k, c2,
-                                              oscale, out_h, [](bf16x8(&)[2]) {});
+        attend_queries_bf16<MPAD, KPAD, NW, FULL>(S, ring[j], 16 * (w + W * j), nq, m, k, c2,
+                                                  oscale, out_h, [](bf16x8(&)[2]) {});
   }
 }
 
@@ -438,22 +457,25 @@ __device__ void attend_f32(AttendLds<F32, MPAD, KPAD>& S, const float* __restric
   }
 }
 
-// grid (work items, BH).  bf16: 512 threads, register budget for 4 waves
-// per SIMD (LDS allows 2 blocks per CU); fp32 (small problems): 256 threads,
-// default budget.
-template <int MPAD, int KPAD, bool FULL>
-__global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_attend_bf16(
+// grid (work items, BH).  bf16: 64 * NW threads.  NW = 8 for items of many
+// sub-tiles: register budget for 4 waves per SIMD (LDS allows 2 blocks per
+// CU).  NW = 2 for short items (a few queries per expert), whose smaller
+// blocks fit several to a CU: budget for 2 waves per SIMD (LDS allows no
+// more at m, k > 32; staging holds twice the values per thread).  fp32
+// (small problems): 256 threads, default budget.
+template <int MPAD, int KPAD, bool FULL, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 8 ? 4 : 2))) void k_attend_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ Ql, const float* __restrict__ vl, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ item_start, int tpb, int64_t N, int m, int k, float c2,
     float* __restrict__ out) {
-  __shared__ AttendLds<BF16, MPAD, KPAD> S;
+  __shared__ AttendLds<BF16, MPAD, KPAD, NW> S;
   const int64_t bh = blockIdx.y;
   TileInfo ti;
   if (!find_item(item_start + bh * (m + 1), offsets + bh * (m + 1), m, tpb, blockIdx.x, ti))
     return;
-  attend_bf16<MPAD, KPAD, FULL>(S, Q, K, V, Ql, vl, idx, perm, N, m, k, c2, out, bh, ti);
+  attend_bf16<MPAD, KPAD, FULL, NW>(S, Q, K, V, Ql, vl, idx, perm, N, m, k, c2, out, bh, ti);
 }
 
 template <int MPAD, int KPAD, bool FULL>
@@ -471,32 +493,43 @@ __global__ __launch_bounds__(256) void k_attend_f32(
   attend_f32<MPAD, KPAD>(S, Q, K, V, Ql, vl, idx, perm, N, m, k, c2, out, bh, ti);
 }
 
-template <class T, int MPAD, int KPAD, bool FULL>
+template <class T, int MPAD, int KPAD, bool FULL, int NW>
 struct AttendKernel;
-template <int MPAD, int KPAD, bool FULL>
-struct AttendKernel<BF16, MPAD, KPAD, FULL> {
-  static constexpr auto fn = k_attend_bf16<MPAD, KPAD, FULL>;
-  static constexpr int threads = kAttendThreads;
+template <int MPAD, int KPAD, bool FULL, int NW>
+struct AttendKernel<BF16, MPAD, KPAD, FULL, NW> {
+  static constexpr auto fn = k_attend_bf16<MPAD, KPAD, FULL, NW>;
+  static constexpr int threads = 64 * NW;
 };
-template <int MPAD, int KPAD, bool FULL>
-struct AttendKernel<F32, MPAD, KPAD, FULL> {
+template <int MPAD, int KPAD, bool FULL, int NW>
+struct AttendKernel<F32, MPAD, KPAD, FULL, NW> {
   static constexpr auto fn = k_attend_f32<MPAD, KPAD, FULL>;
   static constexpr int threads = 256;
 };
 
-template <class T, int MPAD, int KPAD>
-static hipError_t launch_attend_t(const Shape& s, const void* Q, const void* K, const void* V,
+template <class T, int MPAD, int KPAD, int NW>
+static hipError_t launch_attend_w(const Shape& s, const void* Q, const void* K, const void* V,
                                   const int32_t* idx, const Workspace& ws, float* out,
                                   hipStream_t st) {
   using E = typename T::elem;
-  auto kern = (s.m == MPAD && s.k == KPAD) ? AttendKernel<T, MPAD, KPAD, true>::fn
-                                           : AttendKernel<T, MPAD, KPAD, false>::fn;
-  hipLaunchKernelGGL(kern, dim3(s.attend_items, s.BH), dim3(AttendKernel<T, MPAD, KPAD, true>::threads), 0, st,
+  auto kern = (s.m == MPAD && s.k == KPAD) ? AttendKernel<T, MPAD, KPAD, true, NW>::fn
+                                           : AttendKernel<T, MPAD, KPAD, false, NW>::fn;
+  hipLaunchKernelGGL(kern, dim3(s.attend_items, s.BH),
+                     dim3(AttendKernel<T, MPAD, KPAD, true, NW>::threads), 0, st,
                      static_cast<const E*>(Q), static_cast<const E*>(K), static_cast<const E*>(V),
                      static_cast<const E*>(ws.ql), ws.vl, idx, ws.perm,
                      ws.offsets, ws.item_start, s.attend_tpb, s.N, s.m, s.k, s.scale * kLog2e,
                      out);
   return hipGetLastError();
+}
+
+// short work items (few queries per expert on average) take 2-wave blocks
+template <class T, int MPAD, int KPAD>
+static hipError_t launch_attend_t(const Shape& s, const void* Q, const void* K, const void* V,
+                                  const int32_t* idx, const Workspace& ws, float* out,
+                                  hipStream_t st) {
+  if (std::is_same<T, BF16>::value && s.N < kAttendShortItems * static_cast<int64_t>(s.m))
+    return launch_attend_w<T, MPAD, KPAD, 2>(s, Q, K, V, idx, ws, out, st);
+  return launch_attend_w<T, MPAD, KPAD, kAttendWaves>(s, Q, K, V, idx, ws, out, st);
 }
 
 template <class T>

@@ -254,22 +254,31 @@ void derive(Shape& s, int cus) {
   // merge of the scan partials in two levels when there are many splits
   s.merge_parts = s.scan_splits > 32 ? 8 : 1;
   s.pool_splits = static_cast<int>(cdiv(max_window(s), kPoolChunk));
-  // top-k pre-threshold: sample up to a quarter of the key tiles (at most
-  // 1024 per head), only when there are at least max(k, 64) of them
-  int64_t groups = ktiles / 4;
-  if (groups > 1024) groups = 1024;
-  groups = groups / kThetaTilesPerBlock * kThetaTilesPerBlock;
-  s.theta_groups = (groups >= 64 && groups >= s.k) ? static_cast<int>(groups) : 0;
+  // top-k pre-threshold from group maxima (a group = gs consecutive keys;
+  // the threshold is the k-th largest maximum).  Large N: a quarter of the
+  // 64-key tiles (at most 1024 per head) when that gives at least 256
+  // samples, a cheap pass whose threshold keeps candidates few.  Below that,
+  // every key: singly up to kThetaMaxGroups keys (exact k-th largest score),
+  // else in 16-key groups.  Off when there are fewer than k keys.
+  s.theta_groups = 0;
   s.theta_gs = 64;
-  if (s.theta_groups == 0 && s.N >= s.k) {
-    // too few tiles to sample: every key (exact k-th largest score) up to
-    // kThetaExactKeys keys, else the maxima of 16-key blocks
-    if (s.N <= kThetaExactKeys) {
+  s.theta_sampled = false;
+  if (s.N >= s.k) {
+    if (ktiles / 4 >= 256) {
+      int64_t groups = ktiles / 4;
+      if (groups > 1024) groups = 1024;
+      groups = groups / kThetaTilesPerBlock * kThetaTilesPerBlock;
+      s.theta_sampled = true;
+      s.theta_groups = static_cast<int>(groups);
+    } else if (s.N <= kThetaMaxGroups) {
       s.theta_gs = 1;
       s.theta_groups = static_cast<int>(s.N);
-    } else if (cdiv(s.N, 16) >= (s.k > 64 ? s.k : 64)) {
+    } else if (cdiv(s.N, 16) <= kThetaMaxGroups) {
       s.theta_gs = 16;
       s.theta_groups = static_cast<int>(cdiv(s.N, 16));
+    } else {
+      s.theta_gs = 64;
+      s.theta_groups = static_cast<int>(ktiles);
     }
   }
   s.nseg = static_cast<int>(cdiv(s.N, kRouteSeg));

@@ -18,7 +18,7 @@ constexpr int kAttendTile = 64;  // queries per expert-attention tile
 constexpr int kAttendMaxTpb = 16;  // tiles per expert-attention work item, at most
 constexpr int kPoolChunk = 4096; // tokens per pooling partial sum (fewer, longer blocks stream faster)
 constexpr int kThetaTilesPerBlock = 1;  // sample tiles per top-k pre-threshold block
-constexpr int kThetaExactKeys = 4096;  // up to this many keys the pre-threshold uses every key
+constexpr int kThetaMaxGroups = 4096;  // group maxima the pre-threshold selection holds (64 per lane)
 
 struct Shape {
   int64_t B = 0, H = 0, BH = 0, N = 0;
@@ -36,7 +36,8 @@ struct Shape {
   int merge_parts = 0; // first-level merge partitions per landmark (1: single pass)
   int pool_splits = 0; // partial sums per landmark window
   int theta_groups = 0;// sample groups for the top-k pre-threshold (0: off)
-  int theta_gs = 64;    // keys per group: 64 (sampled tiles), 16 or 1 (every key)
+  int theta_gs = 64;    // keys per pre-threshold group: 1, 16 or 64
+  bool theta_sampled = false;  // groups are a sample of the 64-key tiles
   int nseg = 0;        // routing segments per head
   int attend_tpb = 0;   // 64-query tiles per expert-attention work item
   int attend_items = 0; // upper bound of work items per head

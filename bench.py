@@ -45,7 +45,7 @@ def kernel_sha(symbol: str) -> str:
 
     h = hashlib.sha1()
     csrc = os.path.join(ROOT, "mixture_top_sparse_amd", "csrc")
-    for f in (KERNEL_SOURCES[symbol], "mita_device.hpp", "mita_internal.hpp"):
+    for f in (KERNEL_SOURCES[symbol], "mita_device.hpp", "mita_internal.hpp", "tile_dma.hpp"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:12]
@@ -160,6 +160,37 @@ def copy_probe(nbytes: int = 1 << 30, reps: int = 10) -> dict:
             "GBs": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
+def dense_baseline(w, Qt, Kt, Vt, mita_ms: float) -> dict:
+    """Dense (full) attention on the same inputs with the library's own
+    flash-attention kernel: time per forward, MFMA throughput, and MiTA's
+    speedup over it (the ratio the pages report against full attention)."""
+    import torch
+
+    import mixture_top_sparse_amd as mts
+
+    step = lambda: mts.mita_dense_attention(Qt, Kt, Vt, scale=w.scale)
+    t0 = time.perf_counter()
+    step()
+    torch.cuda.synchronize()
+    once = time.perf_counter() - t0
+    reps = max(1, min(5, int(2.0 / max(once, 1e-3))))  # about 2 s of timed work at most
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = 4.0 * w.B * w.H * float(w.N) ** 2 * w.d
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"dense attention: {ms:.3f} ms/forward ({reps} timed), {tflops:.0f} TFLOP/s, "
+        f"MiTA speedup {ms / mita_ms:.1f}x")
+    return {"kernel": "k_dense_bf16", "ms_per_step": round(ms, 4), "steps": reps,
+            "flops": flops, "achieved": round(tflops, 1), "peak": 2500.0, "unit": "TFLOP/s",
+            "frac": round(tflops / 2500.0, 4), "speedup": round(ms / mita_ms, 2)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,6 +198,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="len_1m")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dense", choices=["auto", "on", "off"], default="auto",
+                    help="also time the hand-written dense (full) attention kernel on the same "
+                         "inputs and report the speedup (auto: bf16 workloads with N >= 65536)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also time a plain 1 GiB device copy kernel (bandwidth context and the "
                          "calibration kernel for HBM byte counters)")
@@ -281,6 +315,8 @@ def main() -> int:
                       "bucket_size_min_med_max": [int(sizes.min()), float(np.median(sizes)),
                                                   int(sizes.max())]},
     }
+    if args.dense == "on" or (args.dense == "auto" and w.dtype == "bf16" and w.N >= 65536):
+        line["dense_baseline"] = dense_baseline(w, Qt, Kt, Vt, ms_per_step)
     if args.copy_probe:
         line["copy_probe"] = copy_probe()
     if not args.no_cpu_baseline:

@@ -132,6 +132,28 @@ int mita_forward_ex(const void* Q, const void* K, const void* V, int dtype, int6
                     int64_t k, float scale, float* out, int32_t* idx_out, int32_t* route_out,
                     void* stream, const mita_intermediates* dbg);
 
+/*
+ * mita_dense_attention — dense (full) attention, the baseline the pages time
+ * MiTA against ["NeurIPS 2026 | Mixture-of-Top-k 注意力…", section
+ * "长序列建模：实际运行时间也能明显缩短"; P1, section "长序列建模：训练时间从
+ * 10.6小时降至2.4小时"]: out[q] = softmax over all N logits scale*q.K[t],
+ * applied to V.  A flash-attention kernel (one pass over K and V per tile of
+ * 64 queries, online softmax, bf16 MFMA with fp32 accumulation; the softmax
+ * weights are rounded to bf16 once before the P.V product, as flash-attention
+ * kernels do).  Enqueued on `stream`; no work space, no side stream.
+ *
+ *   Q, K, V    [B][H][N][d] bfloat16 (MITA_BF16 only in this build;
+ *              MITA_F32 gives MITA_ERR_UNSUPPORTED)
+ *   B, H, N    >= 1, N < 2^31, B*H <= 65535, B*H*N*d < 2^40
+ *   d          64 only in this build
+ *   scale      finite and > 0
+ *   out        [B][H][N][d] fp32, fully overwritten
+ *
+ * Same pointer rules and error behaviour as mita_forward.
+ */
+int mita_dense_attention(const void* Q, const void* K, const void* V, int dtype, int64_t B,
+                         int64_t H, int64_t N, int64_t d, float scale, float* out, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* mita_status_string(int status);
 

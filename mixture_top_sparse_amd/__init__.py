@@ -15,6 +15,7 @@ import os
 __all__ = [
     "mita_forward",
     "mita_forward_ex",
+    "mita_dense_attention",
     "mita_status_string",
     "mita_last_error",
     "mita_version",
@@ -70,6 +71,11 @@ def lib() -> ctypes.CDLL:
         L.mita_forward.restype = ctypes.c_int
         L.mita_forward_ex.argtypes = _FWD_ARGS + [ctypes.POINTER(MitaIntermediates)]
         L.mita_forward_ex.restype = ctypes.c_int
+        L.mita_dense_attention.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                           ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+                                           ctypes.c_void_p, ctypes.c_void_p]
+        L.mita_dense_attention.restype = ctypes.c_int
         L.mita_status_string.argtypes = [ctypes.c_int]
         L.mita_status_string.restype = ctypes.c_char_p
         L.mita_last_error.argtypes = []
@@ -173,6 +179,25 @@ def mita_forward_ex(Q, K, V, *, m: int, k: int, grid=None, scale=None):
     """Like mita_forward, plus a dict of intermediates: ql (landmark queries),
     vl (landmark values, fp32), perm (queries grouped by expert) and offsets."""
     return _call(Q, K, V, m, k, grid, scale, want_dbg=True)
+
+
+def mita_dense_attention(Q, K, V, *, scale=None):
+    """Dense attention of [B, H, N, d] bf16 GPU tensors over all N keys (the
+    full-attention baseline).  Returns out [B, H, N, d] fp32, enqueued on
+    torch's current stream."""
+    import torch
+
+    dt = _check_inputs(Q, K, V)
+    B, H, N, d = Q.shape
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    out = torch.empty((B, H, N, d), dtype=torch.float32, device=Q.device)
+    with torch.cuda.device(Q.device):
+        stream = torch.cuda.current_stream(Q.device).cuda_stream
+        _raise(lib().mita_dense_attention(Q.data_ptr(), K.data_ptr(), V.data_ptr(), dt, B, H, N, d,
+                                          float(scale), out.data_ptr(), stream),
+               "mita_dense_attention")
+    return out
 
 
 def mita_profile_enable(enabled: bool) -> None:

@@ -493,6 +493,36 @@ int mita_forward(const void* Q, const void* K, const void* V, int dtype, int64_t
                          stream, nullptr);
 }
 
+int mita_dense_attention(const void* Q, const void* K, const void* V, int dtype, int64_t B,
+                         int64_t H, int64_t N, int64_t d, float scale, float* out, void* stream) {
+  try {
+    if (!Q || !K || !V || !out) return fail(MITA_ERR_INVALID_ARG, "Q, K, V and out must be non-null");
+    if (dtype != MITA_F32 && dtype != MITA_BF16)
+      return fail(MITA_ERR_INVALID_ARG, "dtype must be MITA_F32 or MITA_BF16");
+    if (B < 1 || H < 1 || N < 1) return fail(MITA_ERR_INVALID_ARG, "B, H and N must be >= 1");
+    if (d < 1) return fail(MITA_ERR_INVALID_ARG, "d must be >= 1");
+    if (N >= (int64_t(1) << 31)) return fail(MITA_ERR_INVALID_ARG, "N must be < 2^31");
+    if (B * H > 65535) return fail(MITA_ERR_UNSUPPORTED, "B*H must be <= 65535 in this build");
+    if (dtype != MITA_BF16)
+      return fail(MITA_ERR_UNSUPPORTED, "the dense baseline supports bf16 inputs only");
+    if (d != kD) return fail(MITA_ERR_UNSUPPORTED, "only d == 64 is supported in this build");
+    if (B * H * N > (int64_t(1) << 40) / kD)
+      return fail(MITA_ERR_INVALID_ARG, "B*H*N*d must be < 2^40");
+    if (!(scale > 0.0f) || !std::isfinite(scale))
+      return fail(MITA_ERR_INVALID_ARG, "scale must be finite and > 0");
+    for (const void* p : {Q, K, V, static_cast<const void*>(out)})
+      if (!aligned16(p)) return fail(MITA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    const hipError_t e = launch_dense(dtype, Q, K, V, B * H, N, scale, out,
+                                      static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+      return fail(MITA_ERR_HIP, std::string("launch of the dense kernel failed: ") +
+                                    hipGetErrorString(e));
+    return MITA_OK;
+  } catch (...) {
+    return fail(MITA_ERR_INTERNAL, "unexpected exception inside mita_dense_attention");
+  }
+}
+
 int mita_profile_enable(int enabled) {
   try {
     if (enabled) {

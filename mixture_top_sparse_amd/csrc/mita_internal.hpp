@@ -84,5 +84,8 @@ hipError_t launch_bucket(const Shape& s, const int32_t* route, const Workspace& 
                          int32_t* offsets_copy, int32_t* perm_copy, hipStream_t st);
 hipError_t launch_attend(const Shape& s, const void* Q, const void* K, const void* V,
                          const int32_t* idx, const Workspace& ws, float* out, hipStream_t st);
+// dense attention over all N pairs (the baseline); bf16 only
+hipError_t launch_dense(int dtype, const void* Q, const void* K, const void* V, int64_t BH,
+                        int64_t N, float scale, float* out, hipStream_t st);
 
 }  // namespace mita

@@ -22,4 +22,5 @@ from .oracle import (  # noqa: F401
     bucket,
     output,
     forward,
+    dense,
 )

@@ -355,6 +355,56 @@ int mita_oracle_output(const double* Q, const double* K, const double* V, const 
 }
 
 /* ------------------------------------------------------------------------ */
+/* Dense attention (the baseline)                                           */
+/* ------------------------------------------------------------------------ */
+
+int mita_oracle_dense(const double* Q, const double* K, const double* V, int64_t N, int64_t d,
+                      double scale, const int64_t* qsel, int64_t nq, double* out) {
+  if (!Q || !K || !V || !out) return -1;
+  if (N < 1 || d < 1) return -1;
+  if (!(scale > 0.0) || isinf(scale)) return -1;
+  if (!qsel && nq != N) return -1;
+  if (nq < 0) return -1;
+  int bad = 0;
+#pragma omp parallel
+  {
+    double* w = (double*)malloc((size_t)N * sizeof(double));
+    if (!w) {
+#pragma omp atomic write
+      bad = 2;
+    }
+#pragma omp for schedule(static)
+    for (int64_t p = 0; p < nq; ++p) {
+      if (!w) continue;
+      const int64_t q = qsel ? qsel[p] : p;
+      if (q < 0 || q >= N) {
+#pragma omp atomic write
+        bad = 1;
+        continue;
+      }
+      /* logits over every key, then one softmax */
+      double top = -INFINITY;
+      for (int64_t t = 0; t < N; ++t) {
+        w[t] = scale * dot(Q + q * d, K + t * d, d);
+        if (w[t] > top) top = w[t];
+      }
+      double total = 0.0;
+      for (int64_t t = 0; t < N; ++t) {
+        w[t] = exp(w[t] - top);
+        total += w[t];
+      }
+      for (int64_t c = 0; c < d; ++c) {
+        double sum = 0.0;
+        for (int64_t t = 0; t < N; ++t) sum += w[t] * V[t * d + c];
+        out[p * d + c] = sum / total;
+      }
+    }
+    free(w);
+  }
+  return bad == 2 ? -2 : (bad ? -1 : 0);
+}
+
+/* ------------------------------------------------------------------------ */
 /* All steps over B*H slices                                                 */
 /* ------------------------------------------------------------------------ */
 

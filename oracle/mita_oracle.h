@@ -119,6 +119,14 @@ int mita_oracle_forward(const double* Q, const double* K, const double* V, int64
                         int32_t* idx, int32_t* route, double* Ql, double* Vl,
                         int32_t* offsets, int32_t* perm);
 
+/* Dense attention, the baseline the pages time MiTA against (page 2,
+ * section on wall-clock time in long-sequence modelling; page 1, section on
+ * long-sequence training time): query q attends over all N key/value pairs
+ * with one softmax, out[q] = sum_t softmax_t(scale * Q[q].K[t]) V[t].
+ * qsel (nullable) selects nq queries; out is [nq][d] (or [N][d]). */
+int mita_oracle_dense(const double* Q, const double* K, const double* V, int64_t N, int64_t d,
+                      double scale, const int64_t* qsel, int64_t nq, double* out);
+
 /* Number of OpenMP threads the oracle uses (for reporting). */
 int mita_oracle_threads(void);
 

@@ -58,6 +58,8 @@ def _load(path: str) -> ctypes.CDLL:
     L.mita_oracle_forward.argtypes = [_f64p, _f64p, _f64p, _i64, _i64, _i64, _i64, _i64, _i64,
                                       _i64, _i64, _i64, ctypes.c_double, ctypes.c_int, _f64p,
                                       _i32p, _i32p, _f64p, _f64p, _i32p, _i32p]
+    L.mita_oracle_dense.argtypes = [_f64p, _f64p, _f64p, _i64, _i64, ctypes.c_double, _i64p,
+                                    _i64, _f64p]
     L.mita_oracle_threads.restype = ctypes.c_int
     return L
 
@@ -183,6 +185,18 @@ def output(Q, K, V, Ql, Vl, idx, route_, scale: float, qsel=None) -> np.ndarray:
     _check(lib().mita_oracle_output(_p(Q, _f64p), _p(K, _f64p), _p(V, _f64p), _p(Ql, _f64p),
                                     _p(Vl, _f64p), _p(idx, _i32p), _p(r, _i32p), N, d, m, k,
                                     float(scale), _p(sel, _i64p), nq, _p(out, _f64p)), "output")
+    return out
+
+
+def dense(Q, K, V, scale: float, qsel=None) -> np.ndarray:
+    """Dense attention over all N pairs (the pages' full-attention baseline)."""
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    N, d = Q.shape
+    sel = None if qsel is None else np.ascontiguousarray(np.asarray(qsel, dtype=np.int64))
+    nq = N if sel is None else sel.shape[0]
+    out = np.empty((nq, d), np.float64)
+    _check(lib().mita_oracle_dense(_p(Q, _f64p), _p(K, _f64p), _p(V, _f64p), N, d, float(scale),
+                                   _p(sel, _i64p), nq, _p(out, _f64p)), "dense")
     return out
 
 

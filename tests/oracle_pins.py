@@ -403,6 +403,60 @@ def check_output_invariants():
 
 
 # ---------------------------------------------------------------------------
+# the dense-attention baseline (the full attention the pages time MiTA
+# against: "NeurIPS 2026 | Mixture-of-Top-k 注意力…", section
+# "长序列建模：实际运行时间也能明显缩短")
+# ---------------------------------------------------------------------------
+
+
+def check_dense_vs_torch_sdpa():
+    """fp64 dense attention equals torch's scaled_dot_product_attention in
+    float64 on the CPU (a library routine of the same definition)."""
+    rng = _rng(71)
+    for N, d, scale in [(1, 4, 0.5), (37, 8, 0.3), (200, 16, 0.125)]:
+        Q, K, V = (rng.standard_normal((N, d)) for _ in range(3))
+        got = O.dense(Q, K, V, scale)
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a))[None, None]
+        ref = F.scaled_dot_product_attention(t(Q), t(K), t(V), scale=scale)[0, 0].numpy()
+        np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-13)
+
+
+def check_dense_is_output_over_every_key():
+    """Step 5 with k = N attends over [Ql; K] and [Vl; V]: exactly dense
+    attention over those concatenated pairs (queries taken from a padded
+    array through the query selection)."""
+    rng = _rng(72)
+    N, d, m, scale = 90, 8, 6, 0.3
+    Q, K, V = (rng.standard_normal((N, d)) for _ in range(3))
+    Ql, Vl = rng.standard_normal((m, d)), rng.standard_normal((m, d))
+    idx = np.tile(np.arange(N, dtype=np.int32), (m, 1))
+    r = rng.integers(0, m, N).astype(np.int32)
+    want = O.output(Q, K, V, Ql, Vl, idx, r, scale)
+    Qpad = np.vstack([np.zeros((m, d)), Q])
+    got = O.dense(Qpad, np.vstack([Ql, K]), np.vstack([Vl, V]), scale, qsel=np.arange(m, m + N))
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-14)
+
+
+def check_dense_invariants():
+    rng = _rng(73)
+    N, d = 120, 8
+    Q, K, V = (rng.standard_normal((N, d)) for _ in range(3))
+    out = O.dense(Q, K, V, 0.4)
+    # a convex combination of the value rows
+    assert np.all(out <= V.max(0) + 1e-12) and np.all(out >= V.min(0) - 1e-12)
+    # zero queries see equal logits: the plain mean of the values (closed form)
+    np.testing.assert_allclose(O.dense(np.zeros((N, d)), K, V, 0.4), np.tile(V.mean(0), (N, 1)),
+                               rtol=1e-12, atol=1e-14)
+    # relabelling keys and values together changes nothing
+    p = rng.permutation(N)
+    np.testing.assert_allclose(O.dense(Q, K[p], V[p], 0.4), out, rtol=1e-12, atol=1e-13)
+    # one key far above the rest takes all the weight
+    K2 = K.copy()
+    K2[17] = 50.0 * Q[3] / np.linalg.norm(Q[3])
+    np.testing.assert_allclose(O.dense(Q, K2, V, 1.0, qsel=[3])[0], V[17], rtol=0, atol=1e-9)
+
+
+# ---------------------------------------------------------------------------
 # whole pipeline
 # ---------------------------------------------------------------------------
 

@@ -126,3 +126,43 @@ def test_profiler_without_calls(L):
     assert calls == 0 and set(ms) == {"pool", "landmark_threshold", "landmark_scan",
                                       "landmark_merge", "route", "bucket", "expert_attend"}
     mts.mita_profile_enable(False)
+
+
+# ---- mita_dense_attention (the full-attention baseline) ------------------
+
+
+def dense_call(L, **over):
+    a = dict(Q=A, K=A, V=A, dtype=1, B=2, H=3, N=4096, d=64, scale=0.125, out=A, stream=None)
+    a.update(over)
+    return L.mita_dense_attention(a["Q"], a["K"], a["V"], a["dtype"], a["B"], a["H"], a["N"],
+                                  a["d"], a["scale"], a["out"], a["stream"])
+
+
+DENSE_INVALID = {
+    "null_q": dict(Q=None),
+    "null_out": dict(out=None),
+    "bad_dtype": dict(dtype=7),
+    "zero_tokens": dict(N=0),
+    "huge_n": dict(N=1 << 31),
+    "scale_zero": dict(scale=0.0),
+    "scale_nan": dict(scale=math.nan),
+    "misaligned_k": dict(K=A + 8),
+}
+
+DENSE_UNSUPPORTED = {
+    "f32": dict(dtype=0),
+    "d_128": dict(d=128),
+    "too_many_heads": dict(B=300, H=300),
+}
+
+
+@pytest.mark.parametrize("case", sorted(DENSE_INVALID))
+def test_dense_invalid_arguments(L, case):
+    assert dense_call(L, **DENSE_INVALID[case]) == mts.MITA_ERR_INVALID_ARG
+    assert mts.mita_last_error() != ""
+
+
+@pytest.mark.parametrize("case", sorted(DENSE_UNSUPPORTED))
+def test_dense_unsupported(L, case):
+    assert dense_call(L, **DENSE_UNSUPPORTED[case]) == mts.MITA_ERR_UNSUPPORTED
+    assert mts.mita_last_error() != ""

@@ -42,6 +42,11 @@ MUTANTS = {
                               "acc += w[m + j] * K[(int64_t)ex[j] * d + c];"),
     "output_compressed_keys_from_k": ("w[i] = scale * dot(Q + q * d, Ql + i * d, d);",
                                       "w[i] = scale * dot(Q + q * d, K + i * d, d);"),
+    "dense_unscaled": ("w[t] = scale * dot(Q + q * d, K + t * d, d);",
+                       "w[t] = dot(Q + q * d, K + t * d, d);"),
+    "dense_unnormalised": ("out[p * d + c] = sum / total;", "out[p * d + c] = sum;"),
+    "dense_keys_as_values": ("sum += w[t] * V[t * d + c];", "sum += w[t] * K[t * d + c];"),
+    "dense_drops_last_key": ("        total += w[t];\n", "        total += (t + 1 < N) ? w[t] : 0.0;\n"),
 }
 
 

@@ -32,9 +32,9 @@ KERNEL_SOURCES = {"k_scan": "kernels_scan.hip", "k_route": "kernels_route.hip",
 # kernel whose sources changed since reports traffic null.
 COUNTED_TRAFFIC = {
     "len_1m": {
-        "k_scan": {"sha": "c8b4458f6cbb", "bytes": 1094160531},
-        "k_route": {"sha": "7ad89cdef050", "bytes": 565860716},
-        "k_attend": {"sha": "e8c5e1249f41", "bytes": 1637647671},
+        "k_scan": {"sha": "665fdd43eda9", "bytes": 1094161068},
+        "k_route": {"sha": "59512122da2e", "bytes": 565831852},
+        "k_attend": {"sha": "5ee62b6b4462", "bytes": 1637664597},
     },
 }
 

@@ -63,11 +63,13 @@ def log(msg: str) -> None:
 
 
 def threshold_tiles(w) -> int:
-    """Key tiles of 64 sampled per head by the top-k pre-threshold (the
-    library's rule: a quarter of the tiles, at most 1024, a multiple of 4,
-    and only when there are at least max(k, 64) of them)."""
-    g = min(-(-w.N // 64) // 4, 1024) // 4 * 4
-    return g if g >= 64 and g >= w.k else 0
+    """Key tiles of 64 the top-k pre-threshold reads per head (the library's
+    rule: with at least 256 samples, a quarter of the tiles, at most 1024;
+    below that every tile; none when there are fewer than k keys)."""
+    ktiles = -(-w.N // 64)
+    if w.N < w.k:
+        return 0
+    return min(ktiles // 4, 1024) if ktiles // 4 >= 256 else ktiles
 
 
 def stage_bytes(w) -> dict[str, float]:
@@ -77,12 +79,14 @@ def stage_bytes(w) -> dict[str, float]:
     e = 2 if w.dtype == "bf16" else 4
     BH, N, d, m, k = w.B * w.H, w.N, w.d, w.m, w.k
     rows = min(m * k, N)
+    thr = BH * (threshold_tiles(w) * 64 * d * e + m * d * e)
+    route = BH * (N * d * e + 4 * N)
     return {
         "pool": BH * (N * d * e + m * d * e),
-        "landmark_threshold": BH * (threshold_tiles(w) * 64 * d * e + m * d * e),
+        "landmark_threshold": thr,
         "landmark_scan": BH * (2 * N * d * e),
         "landmark_merge": BH * (4 * m * k + 4 * m * d),
-        "route": BH * (N * d * e + 4 * N),
+        "route": route,
         "bucket": BH * (4 * N + 4 * N),
         "expert_attend": BH * (N * d * e + 4 * N * d + 4 * N + rows * 2 * d * e),
     }
@@ -239,8 +243,10 @@ def main() -> int:
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record()
+    h0 = time.perf_counter()
     for _ in range(args.steps):
         res = step()
+    host_ms = (time.perf_counter() - h0) * 1e3 / args.steps  # host time to enqueue one step
     ev1.record()
     torch.cuda.synchronize()
     ms_total = ev0.elapsed_time(ev1)
@@ -308,6 +314,7 @@ def main() -> int:
         "path_roofline": {"algorithmic_bytes": pbytes, "achieved_GBs": round(path_gbs, 1),
                           "frac": round(path_gbs / HBM_PEAK_GBS, 4)},
         "ms_per_step_profiled": round(ms_profiled, 4),
+        "host_enqueue_ms_per_step": round(host_ms, 4),
         "stages_ms": {k: round(v, 4) for k, v in avg_stage.items()},
         "stages_GBs": {k: round(sbytes[k] / (avg_stage[k] * 1e-3) / 1e9, 1) for k in avg_stage
                        if avg_stage[k] > 0},

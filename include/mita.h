@@ -36,16 +36,22 @@
  * must not overlap.  Layouts are dense, row-major, [B][H][...] with the
  * innermost dimension contiguous; every pointer must be 16-byte aligned.
  *
- * Work space: allocated stream-ordered on `stream` (hipMallocAsync /
- * hipFreeAsync) for the duration of the call.  The sampled top-k
- * pre-threshold of step 2 and step 4 run on a library-owned side stream of
- * the current device (created on first use, default priority, never
- * destroyed), forked from and joined back to `stream` with events, so they
- * overlap steps 3 and 2; the call returns with all its work ordered on
- * `stream`.  There is no host synchronisation and no
- * global state besides that side stream, the per-device attribute cache
- * and the optional stage profiler; calls on different streams may run
- * concurrently (their side-stream steps share the side stream).
+ * Work space: one device block per calling stream (up to 8 streams per
+ * device), allocated stream-ordered on `stream` (hipMallocAsync) by the
+ * first call that needs it and kept for later calls on that stream, which
+ * are ordered after it by the stream itself.  A block that is too small for
+ * a call is released with hipFreeAsync on its stream and replaced; a new
+ * stream beyond the eighth takes over the least recently used block.  At
+ * 2^20 tokens x 4 heads the block is about 54 MB.  Step 4 runs on a
+ * library-owned side stream of the current device (created on first use,
+ * default priority, never destroyed), forked from `stream` after step 3 and
+ * joined back before step 5, so it overlaps step 2; the call returns with
+ * all its work ordered on `stream`.  There is no host synchronisation and no
+ * global state besides that side stream, the cached work-space blocks, the
+ * per-device attribute cache and the optional stage profiler.  A per-device
+ * mutex serialises the enqueue sequences of concurrent host calls; calls on
+ * different streams may run concurrently on the GPU (their step-4 kernels
+ * share the side stream).
  *
  * Errors: every function returns a status.  Arguments are validated on the
  * host before any HIP call; nothing is enqueued when validation fails.  A

@@ -77,34 +77,77 @@ struct RouteTraits<F32> {
   }
 };
 
-// grid (nseg, BH), 256 threads; wave w routes queries seg*1024 + 256w + [0, 256)
-// in 16 groups of 16 queries, four groups of Q rows in flight
+// The top-k pre-threshold's selection, one wave per landmark lm of head bh:
+// theta[bh][lm] = the k-th largest group maximum's score, lowered by one ulp
+// so that the scan's strict test (s > theta) keeps every score equal to it;
+// -inf when fewer than k maxima exist.  The k-th largest score comes from a
+// bisection over the scores' 32-bit order (the upper half of the keys): the
+// largest T with at least k maxima at or above T.  Each step counts per lane
+// and sums the counts with one ballot per count bit, so the search stays
+// uniform across the wave.  KPL: maxima per lane (groups <= 64 * KPL).
+template <int KPL>
+__device__ __forceinline__ void theta_select_wave(const uint64_t* __restrict__ gmax, int m, int k,
+                                                  int groups, int mrows, int lm, int64_t bh,
+                                                  float* __restrict__ theta) {
+  const int l = lane_id();
+  const uint64_t* G = gmax + (bh * m + lm) * groups;
+  uint32_t v[KPL];  // 0: no maximum (below every real key's order bits)
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const int i = 64 * j + l;
+    v[j] = i < groups ? static_cast<uint32_t>(G[i] >> 32) : 0u;
+  }
+  // invariant: at least k values >= lo (lo = 0 holds: 64 * KPL >= groups >= k)
+  uint32_t lo = 0u, hi = 0xFFFFFFFFu;
+  while (lo < hi) {
+    const uint32_t mid = lo + ((hi - lo) >> 1) + 1u;
+    // per-lane count (vector registers), then the wave total bit by bit:
+    // one ballot per bit of the count instead of one per register
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) c += v[j] >= mid ? 1u : 0u;
+    int cnt = 0;
+#pragma unroll
+    for (int b = 0; (1 << b) <= KPL; ++b) cnt += __popcll(ballot((c >> b) & 1u)) << b;
+    if (cnt >= k)
+      lo = mid;
+    else
+      hi = mid - 1u;
+  }
+  if (l == 0)
+    theta[bh * mrows + lm] =
+        lo != 0u ? nextafterf(key_score(static_cast<uint64_t>(lo) << 32), -INFINITY) : -INFINITY;
+}
+
+// the landmark queries of head bh into LDS (row stride kQlStride), rows past
+// m zeroed; the caller's barrier publishes them
+template <class E>
+__device__ __forceinline__ void stage_landmarks(const E* __restrict__ Ql, int m, int64_t bh,
+                                                E* __restrict__ qls) {
+  constexpr int CH = 16 / sizeof(E);  // elements per 16-byte chunk
+  for (int c = threadIdx.x; c < kMaxM * (kD / CH); c += 256) {
+    const int row = c / (kD / CH), col = c % (kD / CH);
+    const u32x4 z = {0, 0, 0, 0};
+    *reinterpret_cast<u32x4*>(qls + row * kQlStride + col * CH) =
+        row < m ? *reinterpret_cast<const u32x4*>(Ql + (bh * m + row) * kD + col * CH) : z;
+  }
+}
+
+// One routing block (256 threads): wave w routes queries seg*1024 + 256w +
+// [0, 256) of head bh in 16 groups of 16 queries, four groups of Q rows in
+// flight, and the block stores the segment's per-expert counts.
 template <class T>
-__global__ __launch_bounds__(256) void k_route(const typename T::elem* __restrict__ Q,
-                                              const typename T::elem* __restrict__ Ql, int64_t N,
-                                              int m, int nseg, int64_t bh0,
+__device__ __forceinline__ void route_segment(const typename T::elem* __restrict__ Q,
+                                              const typename T::elem* __restrict__ Ql,
+                                              int64_t N, int m, int nseg, int seg, int64_t bh,
                                               int32_t* __restrict__ route_out,
-                                              int32_t* __restrict__ counts) {
+                                              int32_t* __restrict__ counts, int* cnt,
+                                              typename T::elem* qls) {
   using TR = RouteTraits<T>;
   using E = typename T::elem;
-  __shared__ int cnt[kMaxM];
-  __shared__ __attribute__((aligned(16))) E qls[kMaxM * kQlStride];
   const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
-  // blocks run from the end of the heads' queries backwards: pooling has just
-  // read Q front to back, so the first rows routed are still in the last-level
-  // cache
-  const int seg = nseg - 1 - static_cast<int>(blockIdx.x);
-  const int64_t bh = bh0 + (gridDim.y - 1 - blockIdx.y);
   if (threadIdx.x < kMaxM) cnt[threadIdx.x] = 0;
-  {  // the landmark queries once per block, zero rows past m
-    constexpr int CH = 16 / sizeof(E);  // elements per 16-byte chunk
-    for (int c = threadIdx.x; c < kMaxM * (kD / CH); c += 256) {
-      const int row = c / (kD / CH), col = c % (kD / CH);
-      const u32x4 z = {0, 0, 0, 0};
-      *reinterpret_cast<u32x4*>(qls + row * kQlStride + col * CH) =
-          row < m ? *reinterpret_cast<const u32x4*>(Ql + (bh * m + row) * kD + col * CH) : z;
-    }
-  }
+  stage_landmarks(Ql, m, bh, qls);
   const E* Qh = Q + bh * N * kD;
   const int64_t qw = static_cast<int64_t>(seg) * kRouteSeg + 256 * w;
   // a ring of D groups of 16 queries in flight; the landmark operands are
@@ -158,6 +201,133 @@ __global__ __launch_bounds__(256) void k_route(const typename T::elem* __restric
   }
   __syncthreads();
   if (threadIdx.x < m) counts[(bh * m + threadIdx.x) * nseg + seg] = cnt[threadIdx.x];  // expert-major
+}
+
+// grid (nsel + nseg, BH), 256 threads (fp32 inputs, or no pre-threshold).
+//  - blocks x < nsel (KPL > 0): the pre-threshold selection over the group
+//    maxima of the separate group kernel, wave w of block x for landmark
+//    4x + w (nsel = ceil(m / 4)).  They come first in the grid, so they are
+//    dispatched before the routing blocks, and the scan, which follows on
+//    the same stream, finds theta ready.
+//  - the other blocks route; they run from the end of the heads' queries
+//    backwards: pooling has just read Q front to back, so the first rows
+//    routed are still in the last-level cache.
+template <class T, int KPL>
+__global__ __launch_bounds__(256) void k_route(const typename T::elem* __restrict__ Q,
+                                              const typename T::elem* __restrict__ Ql, int64_t N,
+                                              int m, int nseg, int32_t* __restrict__ route_out,
+                                              int32_t* __restrict__ counts, int nsel,
+                                              const uint64_t* __restrict__ gmax, int k,
+                                              int groups, int mrows,
+                                              float* __restrict__ theta) {
+  using E = typename T::elem;
+  __shared__ int cnt[kMaxM];
+  __shared__ __attribute__((aligned(16))) E qls[kMaxM * kQlStride];
+  if constexpr (KPL > 0) {
+    if (static_cast<int>(blockIdx.x) < nsel) {  // whole block
+      const int lm = static_cast<int>(blockIdx.x) * 4 +
+                     __builtin_amdgcn_readfirstlane(wave_id());
+      if (lm < m) theta_select_wave<KPL>(gmax, m, k, groups, mrows, lm, blockIdx.y, theta);
+      return;
+    }
+  }
+  const int seg = nseg - 1 - (static_cast<int>(blockIdx.x) - (KPL > 0 ? nsel : 0));
+  route_segment<T>(Q, Ql, N, m, nseg, seg, gridDim.y - 1 - blockIdx.y, route_out, counts, cnt,
+                   qls);
+}
+
+// The pre-threshold's group maxima of one 64-key tile of head bh (bf16), one
+// wave: the tile is scored against every landmark (operands from the LDS
+// copy of the landmark queries), and the maximum key of each group of GS
+// keys is stored.  SAMPLED: tile ti of `groups` evenly spaced sample tiles,
+// one group per tile.  Else tile ti of the head in groups of GS keys (1:
+// every key its own group; 16: 16-key blocks; 64: the tile).  Rows past N
+// read row N - 1: every load is unconditional; those scores are dropped.
+// The scores use the scan's operand layout and accumulation order, so they
+// are bitwise the scores the scan computes.
+template <int GS, bool SAMPLED>
+__device__ __forceinline__ void theta_tile_wave(const uint16_t* __restrict__ K,
+                                                const uint16_t* qls, int64_t N, int m,
+                                                int groups, int ti, int64_t bh,
+                                                uint64_t* __restrict__ gmax) {
+  static_assert(GS == 1 || GS == 16 || GS == 64, "groups of 1, 16 or 64 keys");
+  static_assert(!SAMPLED || GS == 64, "samples are whole tiles");
+  const int l = lane_id(), g = l >> 4, c16 = l & 15;
+  const int64_t ntiles = (N + kTileKeys - 1) / kTileKeys;
+  const int64_t t0 = SAMPLED ? ((static_cast<int64_t>(ti) * ntiles) / groups) * kTileKeys
+                             : static_cast<int64_t>(ti) * kTileKeys;
+  const uint16_t* Kh = K + bh * N * kD;
+  u32x4 ko[4][2];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const int64_t row = t0 + 16 * kb + c16;
+    const int64_t rr = row < N ? row : N - 1;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      ko[kb][s] = *reinterpret_cast<const u32x4*>(Kh + rr * kD + 32 * s + 8 * g);
+  }
+#pragma unroll
+  for (int lb = 0; lb < 4; ++lb) {
+    if (16 * lb >= m) break;  // uniform
+    const uint16_t* qrow = qls + (16 * lb + c16) * kQlStride + 8 * g;
+    const u32x4 q0 = *reinterpret_cast<const u32x4*>(qrow);
+    const u32x4 q1 = *reinterpret_cast<const u32x4*>(qrow + 32);
+    f32x4 sc[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      sc[kb] = mfma_bf16(as_bf16x8(ko[kb][0]), as_bf16x8(q0), f32x4{0, 0, 0, 0});
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) sc[kb] = mfma_bf16(as_bf16x8(ko[kb][1]), as_bf16x8(q1), sc[kb]);
+    const int lm = 16 * lb + c16;
+    uint64_t* G = gmax + (bh * m + (lm < m ? lm : 0)) * groups;
+    uint64_t best = 0;  // running group maximum (GS = 16, 64)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t t = t0 + 16 * kb + 4 * g + r;
+        const uint64_t key = t < N ? make_key(sc[kb][r], static_cast<uint32_t>(t)) : 0ull;
+        if constexpr (GS == 1) {
+          if (lm < m && t < N) G[t] = key;
+        } else {
+          best = key > best ? key : best;
+        }
+      }
+      if constexpr (GS != 1) {
+        if (GS == 16 || kb == 3) {  // end of a group: combine the 4 lane groups
+#pragma unroll
+          for (int mask = 16; mask <= 32; mask <<= 1) {
+            const uint64_t o = lane_read(best, l ^ mask);
+            best = o > best ? o : best;
+          }
+          const int64_t gi = GS == 16 ? (t0 >> 4) + kb : static_cast<int64_t>(ti);
+          if (g == 0 && lm < m && gi < groups) G[gi] = best;
+          best = 0;
+        }
+      }
+    }
+  }
+}
+
+// The pre-threshold's group maxima (bf16): grid (ceil(tiles / 4), BH), 256
+// threads, wave w: tile 4x + w, scored against the block's LDS copy of the
+// landmark queries.  Its own launch before routing: inside the routing
+// launch, the selection would have to wait across blocks for every tile of
+// the head, and the device-scope fences and polls that takes cost routing
+// more than this launch does.
+template <int GS, bool SAMPLED>
+__global__ __launch_bounds__(256) void k_theta_groups(const uint16_t* __restrict__ K,
+                                                     const uint16_t* __restrict__ Ql, int64_t N,
+                                                     int m, int groups,
+                                                     uint64_t* __restrict__ gmax) {
+  __shared__ __attribute__((aligned(16))) uint16_t qls[kMaxM * kQlStride];
+  const int64_t bh = blockIdx.y;
+  const int ti = static_cast<int>(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(wave_id());
+  const int64_t ntiles = (N + kTileKeys - 1) / kTileKeys;
+  stage_landmarks(Ql, m, bh, qls);
+  __syncthreads();
+  if (ti < (SAMPLED ? groups : ntiles))
+    theta_tile_wave<GS, SAMPLED>(K, qls, N, m, groups, ti, bh, gmax);
 }
 
 // inclusive prefix sum over the 64 lanes of a wave
@@ -299,17 +469,53 @@ __global__ __launch_bounds__(64) void k_bucket_scatter(
 
 template <class T>
 static hipError_t launch_route_t(const Shape& s, const void* Q, const Workspace& ws,
-                                 int32_t* route_out, int64_t bh0, int64_t nbh, hipStream_t st) {
+                                 int32_t* route_out, hipStream_t st) {
   using E = typename T::elem;
-  hipLaunchKernelGGL(k_route<T>, dim3(s.nseg, nbh), dim3(256), 0, st, static_cast<const E*>(Q),
-                     static_cast<const E*>(ws.ql), s.N, s.m, s.nseg, bh0, route_out, ws.counts);
+  const E* Qp = static_cast<const E*>(Q);
+  const E* Qlp = static_cast<const E*>(ws.ql);
+  if (s.theta_groups > 64 * 64) return hipErrorInvalidValue;  // beyond the selection's registers
+  const int nsel = s.theta_groups > 0 ? (s.m + 3) / 4 : 0;
+  const dim3 grid(nsel + s.nseg, s.BH);
+  if (nsel == 0)
+    hipLaunchKernelGGL((k_route<T, 0>), grid, dim3(256), 0, st, Qp, Qlp, s.N, s.m, s.nseg,
+                       route_out, ws.counts, 0, nullptr, s.k, 0, s.mrows, nullptr);
+  else if (s.theta_groups <= 64 * 16)
+    hipLaunchKernelGGL((k_route<T, 16>), grid, dim3(256), 0, st, Qp, Qlp, s.N, s.m, s.nseg,
+                       route_out, ws.counts, nsel, ws.gmax, s.k, s.theta_groups, s.mrows,
+                       ws.theta);
+  else
+    hipLaunchKernelGGL((k_route<T, 64>), grid, dim3(256), 0, st, Qp, Qlp, s.N, s.m, s.nseg,
+                       route_out, ws.counts, nsel, ws.gmax, s.k, s.theta_groups, s.mrows,
+                       ws.theta);
+  return hipGetLastError();
+}
+
+template <int GS, bool SAMPLED>
+static void launch_groups_gs(const Shape& s, const void* K, const Workspace& ws, int nth,
+                             hipStream_t st) {
+  hipLaunchKernelGGL((k_theta_groups<GS, SAMPLED>), dim3(nth, s.BH), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(ws.ql), s.N,
+                     s.m, s.theta_groups, ws.gmax);
+}
+
+hipError_t launch_groups_bf16(const Shape& s, const void* K, const Workspace& ws, hipStream_t st) {
+  const int64_t ktiles = (s.N + kTileKeys - 1) / kTileKeys;
+  const int nth = static_cast<int>(((s.theta_sampled ? s.theta_groups : ktiles) + 3) / 4);
+  if (s.theta_sampled)
+    launch_groups_gs<64, true>(s, K, ws, nth, st);
+  else if (s.theta_gs == 1)
+    launch_groups_gs<1, false>(s, K, ws, nth, st);
+  else if (s.theta_gs == 16)
+    launch_groups_gs<16, false>(s, K, ws, nth, st);
+  else
+    launch_groups_gs<64, false>(s, K, ws, nth, st);
   return hipGetLastError();
 }
 
 hipError_t launch_route(const Shape& s, const void* Q, const Workspace& ws, int32_t* route_out,
-                        int64_t bh0, int64_t nbh, hipStream_t st) {
-  return s.dtype == 1 ? launch_route_t<BF16>(s, Q, ws, route_out, bh0, nbh, st)
-                      : launch_route_t<F32>(s, Q, ws, route_out, bh0, nbh, st);
+                        hipStream_t st) {
+  return s.dtype == 1 ? launch_route_t<BF16>(s, Q, ws, route_out, st)
+                      : launch_route_t<F32>(s, Q, ws, route_out, st);
 }
 
 hipError_t launch_bucket(const Shape& s, const int32_t* route, const Workspace& ws,

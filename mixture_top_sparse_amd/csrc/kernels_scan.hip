@@ -671,88 +671,6 @@ __global__ __launch_bounds__(256) void k_theta_sample(const typename T::elem* __
   }
 }
 
-// bf16: grid (ceil(T / 4), BH), 256 threads; wave w scores tile 4 *
-// blockIdx.x + w against all landmarks (up to four blocks of 16), so each
-// tile is read once.  SAMPLED: tile i of G evenly spaced sample tiles, one
-// group per tile.  Else tile i of the head, in groups of GS keys (1: every key
-// its own group; 16: 16-key blocks; 64: the tile).  Rows past N read row
-// N - 1 and landmarks past m read landmark m - 1: every load is unconditional
-// (exact wait counts); those scores are dropped and those maxima not stored.
-// Scores use the scan's operand layout and accumulation order, so they are
-// bitwise the scores the scan computes.
-template <int GS, bool SAMPLED>
-__global__ __launch_bounds__(256) void k_theta_groups_bf16(const uint16_t* __restrict__ K,
-                                                          const uint16_t* __restrict__ Ql,
-                                                          int64_t N, int m, int groups,
-                                                          uint64_t* __restrict__ gmax) {
-  static_assert(GS == 1 || GS == 16 || GS == 64, "groups of 1, 16 or 64 keys");
-  static_assert(!SAMPLED || GS == 64, "samples are whole tiles");
-  const int l = lane_id(), g = l >> 4, c16 = l & 15;
-  const int w = __builtin_amdgcn_readfirstlane(wave_id());
-  const int ti = static_cast<int>(blockIdx.x) * 4 + w;
-  const int64_t ntiles = (N + kTileKeys - 1) / kTileKeys;
-  if (ti >= (SAMPLED ? groups : ntiles)) return;  // whole wave
-  const int64_t bh = blockIdx.y;
-  const int64_t t0 = SAMPLED ? ((static_cast<int64_t>(ti) * ntiles) / groups) * kTileKeys
-                             : static_cast<int64_t>(ti) * kTileKeys;
-  const uint16_t* Kh = K + bh * N * kD;
-  u32x4 ko[4][2], qo[4][2];
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    const int64_t row = t0 + 16 * kb + c16;
-    const int64_t rr = row < N ? row : N - 1;
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-      ko[kb][s] = *reinterpret_cast<const u32x4*>(Kh + rr * kD + 32 * s + 8 * g);
-  }
-#pragma unroll
-  for (int lb = 0; lb < 4; ++lb) {
-    const int lr = min(16 * lb + c16, m - 1);
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-      qo[lb][s] = *reinterpret_cast<const u32x4*>(Ql + (bh * m + lr) * kD + 32 * s + 8 * g);
-  }
-#pragma unroll
-  for (int lb = 0; lb < 4; ++lb) {
-    if (16 * lb >= m) break;  // uniform
-    f32x4 sc[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      sc[kb] = mfma_bf16(as_bf16x8(ko[kb][0]), as_bf16x8(qo[lb][0]), f32x4{0, 0, 0, 0});
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      sc[kb] = mfma_bf16(as_bf16x8(ko[kb][1]), as_bf16x8(qo[lb][1]), sc[kb]);
-    const int lm = 16 * lb + c16;
-    uint64_t* G = gmax + (bh * m + (lm < m ? lm : 0)) * groups;
-    uint64_t best = 0;  // running group maximum (GS = 16, 64)
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t t = t0 + 16 * kb + 4 * g + r;
-        const uint64_t key = t < N ? make_key(sc[kb][r], static_cast<uint32_t>(t)) : 0ull;
-        if constexpr (GS == 1) {
-          if (lm < m && t < N) G[t] = key;
-        } else {
-          best = key > best ? key : best;
-        }
-      }
-      if constexpr (GS != 1) {
-        if (GS == 16 || kb == 3) {  // end of a group: combine the 4 lane groups
-#pragma unroll
-          for (int mask = 16; mask <= 32; mask <<= 1) {
-            const uint64_t o = lane_read(best, l ^ mask);
-            best = o > best ? o : best;
-          }
-          const int64_t gi = GS == 16 ? (t0 >> 4) + kb : static_cast<int64_t>(ti);
-          if (g == 0 && lm < m && gi < groups) G[gi] = best;
-          best = 0;
-        }
-      }
-    }
-  }
-}
-
 // Every key in groups of GS consecutive keys (GS = 1: each key is a group,
 // so the threshold is the exact k-th largest score; GS = 16 or 64: the
 // maximum of each 16-key block or 64-key tile).  grid (key tiles, BH), 256
@@ -808,52 +726,6 @@ __global__ __launch_bounds__(256) void k_theta_fine(const typename T::elem* __re
       }
     }
   }
-}
-
-// grid (ceil(m / 4), BH), 256 threads; wave w: landmark 4 * blockIdx.x + w.
-// theta[bh][lm] = the k-th largest group maximum's score, lowered by one ulp
-// so that the scan's strict test (s > theta) keeps every score equal to it;
-// -inf when fewer than k maxima exist.  The k-th largest score comes from a
-// bisection over the scores' 32-bit order (the upper half of the keys): the
-// largest T with at least k maxima at or above T.  Each step counts per lane
-// and sums the counts with one ballot per count bit, so the search stays
-// uniform across the wave.  KPL: maxima per lane (groups <= 64 * KPL).
-template <int KPL>
-__global__ __launch_bounds__(256) void k_theta_select(const uint64_t* __restrict__ gmax, int m,
-                                                     int k, int groups, int mrows,
-                                                     float* __restrict__ theta) {
-  const int l = lane_id();
-  const int w = __builtin_amdgcn_readfirstlane(wave_id());
-  const int lm = static_cast<int>(blockIdx.x) * 4 + w;
-  if (lm >= m) return;  // whole wave
-  const int64_t bh = blockIdx.y;
-  const uint64_t* G = gmax + (bh * m + lm) * groups;
-  uint32_t v[KPL];  // 0: no maximum (below every real key's order bits)
-#pragma unroll
-  for (int j = 0; j < KPL; ++j) {
-    const int i = 64 * j + l;
-    v[j] = i < groups ? static_cast<uint32_t>(G[i] >> 32) : 0u;
-  }
-  // invariant: at least k values >= lo (lo = 0 holds: 64 * KPL >= groups >= k)
-  uint32_t lo = 0u, hi = 0xFFFFFFFFu;
-  while (lo < hi) {
-    const uint32_t mid = lo + ((hi - lo) >> 1) + 1u;
-    // per-lane count (vector registers), then the wave total bit by bit:
-    // one ballot per bit of the count instead of one per register
-    uint32_t c = 0;
-#pragma unroll
-    for (int j = 0; j < KPL; ++j) c += v[j] >= mid ? 1u : 0u;
-    int cnt = 0;
-#pragma unroll
-    for (int b = 0; (1 << b) <= KPL; ++b) cnt += __popcll(ballot((c >> b) & 1u)) << b;
-    if (cnt >= k)
-      lo = mid;
-    else
-      hi = mid - 1u;
-  }
-  if (l == 0)
-    theta[bh * mrows + lm] =
-        lo != 0u ? nextafterf(key_score(static_cast<uint64_t>(lo) << 32), -INFINITY) : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -1005,23 +877,7 @@ static hipError_t launch_theta_t(const Shape& s, const void* K, const Workspace&
                                  hipStream_t st) {
   using E = typename T::elem;
   const int64_t ktiles = (s.N + kTileKeys - 1) / kTileKeys;
-  if constexpr (std::is_same<T, BF16>::value) {
-    const auto* Kp = static_cast<const uint16_t*>(K);
-    const auto* Qp = static_cast<const uint16_t*>(ws.ql);
-    const dim3 gt((ktiles + 3) / 4, s.BH);
-    if (s.theta_sampled)
-      hipLaunchKernelGGL((k_theta_groups_bf16<64, true>), dim3((s.theta_groups + 3) / 4, s.BH),
-                         dim3(256), 0, st, Kp, Qp, s.N, s.m, s.theta_groups, ws.gmax);
-    else if (s.theta_gs == 1)
-      hipLaunchKernelGGL((k_theta_groups_bf16<1, false>), gt, dim3(256), 0, st, Kp, Qp, s.N, s.m,
-                         s.theta_groups, ws.gmax);
-    else if (s.theta_gs == 16)
-      hipLaunchKernelGGL((k_theta_groups_bf16<16, false>), gt, dim3(256), 0, st, Kp, Qp, s.N,
-                         s.m, s.theta_groups, ws.gmax);
-    else
-      hipLaunchKernelGGL((k_theta_groups_bf16<64, false>), gt, dim3(256), 0, st, Kp, Qp, s.N,
-                         s.m, s.theta_groups, ws.gmax);
-  } else if (!s.theta_sampled && s.theta_gs == 1) {
+  if (!s.theta_sampled && s.theta_gs == 1) {
     hipLaunchKernelGGL((k_theta_fine<T, 1>), dim3(ktiles, s.BH), dim3(256), 0, st,
                        static_cast<const E*>(K), static_cast<const E*>(ws.ql), s.N, s.m,
                        s.theta_groups, ws.gmax);
@@ -1038,22 +894,13 @@ static hipError_t launch_theta_t(const Shape& s, const void* K, const Workspace&
                        dim3(256), 0, st, static_cast<const E*>(K), static_cast<const E*>(ws.ql),
                        s.N, s.m, s.theta_groups, ws.gmax);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (s.theta_groups > 64 * 64) return hipErrorInvalidValue;  // beyond the selection's registers
-  if (s.theta_groups <= 64 * 16)
-    hipLaunchKernelGGL(k_theta_select<16>, dim3((s.m + 3) / 4, s.BH), dim3(256), 0, st, ws.gmax,
-                       s.m, s.k, s.theta_groups, s.mrows, ws.theta);
-  else
-    hipLaunchKernelGGL(k_theta_select<64>, dim3((s.m + 3) / 4, s.BH), dim3(256), 0, st, ws.gmax,
-                       s.m, s.k, s.theta_groups, s.mrows, ws.theta);
   return hipGetLastError();
 }
 
 hipError_t launch_threshold(const Shape& s, const void* K, const Workspace& ws,
                             hipStream_t st) {
   if (s.theta_groups == 0) return hipSuccess;
-  return s.dtype == 1 ? launch_theta_t<BF16>(s, K, ws, st) : launch_theta_t<F32>(s, K, ws, st);
+  return s.dtype == 1 ? launch_groups_bf16(s, K, ws, st) : launch_theta_t<F32>(s, K, ws, st);
 }
 
 hipError_t launch_scan(const Shape& s, const void* K, const void* V, const Workspace& ws,

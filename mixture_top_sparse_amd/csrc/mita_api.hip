@@ -120,41 +120,101 @@ int device_cus() {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // ---------------------------------------------------------------------------
-// per-device side stream: bucketing depends only on the routes, and the
-// landmark branch (pre-threshold, scan, merge) only on the pooled landmarks,
-// so the two run concurrently: fork after routing, join before the expert
-// attention.  Default priority, non-blocking; one mutex per device keeps
-// each call's fork/record/wait sequence from interleaving with another host
-// thread's.
+// per-device state: the side stream and the cached work spaces
+//
+// Bucketing depends only on the routes, and the landmark branch (scan,
+// merge) only on the pooled landmarks and the pre-threshold, so the two run
+// concurrently: fork after routing, join before the expert attention.  The
+// side stream has default priority and is non-blocking.
+//
+// Work space: one block per calling stream (up to kWsStreams per device),
+// kept between calls and reused while it is large enough.  Calls on one
+// stream are ordered by that stream, so a call's kernels never overlap the
+// previous call's use of the block.  A block that is too small is released
+// with hipFreeAsync on its stream and replaced by a larger hipMallocAsync
+// block; the least recently used entry makes room for a new stream.  The
+// device mutex is held for the whole enqueue sequence of a call, so calls
+// from several host threads on one stream do not interleave their kernels.
 // ---------------------------------------------------------------------------
 
-struct SideStream {
+constexpr int kWsStreams = 8;
+
+struct DeviceState {
   std::mutex mu;
   bool ready = false;
   hipStream_t aux = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr, routed = nullptr, thr_done = nullptr;
+  hipEvent_t routed = nullptr, join = nullptr;
+  struct Ws {
+    hipStream_t st = nullptr;
+    void* p = nullptr;
+    size_t bytes = 0;
+    uint64_t used = 0;
+  } ws[kWsStreams];
+  uint64_t clock = 0;
 };
-SideStream g_side[64];
+DeviceState g_dev[64];
 
-SideStream* side_stream() {
+// the current device's state (side stream and events created on first use);
+// the caller holds ds->mu
+DeviceState* device_state() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  SideStream& ss = g_side[dev];
-  std::lock_guard<std::mutex> lk(ss.mu);
-  if (!ss.ready) {
-    if (ss.aux == nullptr && hipStreamCreateWithFlags(&ss.aux, hipStreamNonBlocking) != hipSuccess) {
-      ss.aux = nullptr;
-      return nullptr;
+  return &g_dev[dev];
+}
+
+bool side_stream_ready(DeviceState& ds) {
+  if (!ds.ready) {
+    if (ds.aux == nullptr && hipStreamCreateWithFlags(&ds.aux, hipStreamNonBlocking) != hipSuccess) {
+      ds.aux = nullptr;
+      return false;
     }
-    for (hipEvent_t* ev : {&ss.fork, &ss.join, &ss.routed, &ss.thr_done}) {
+    for (hipEvent_t* ev : {&ds.routed, &ds.join}) {
       if (*ev == nullptr && hipEventCreateWithFlags(ev, hipEventDisableTiming) != hipSuccess) {
         *ev = nullptr;  // kept for the next attempt; the rest stay created
-        return nullptr;
+        return false;
       }
     }
-    ss.ready = true;
+    ds.ready = true;
   }
-  return &ss;
+  return true;
+}
+
+// a work-space block of at least `bytes` for calls on stream st
+hipError_t workspace_for(DeviceState& ds, hipStream_t st, size_t bytes, void** out) {
+  ++ds.clock;
+  DeviceState::Ws* e = nullptr;
+  for (auto& w : ds.ws)
+    if (w.p != nullptr && w.st == st) e = &w;
+  if (e == nullptr) {  // a free entry, else the least recently used one
+    for (auto& w : ds.ws)
+      if (w.p == nullptr) {
+        e = &w;
+        break;
+      }
+    if (e == nullptr) {
+      e = &ds.ws[0];
+      for (auto& w : ds.ws)
+        if (w.used < e->used) e = &w;
+    }
+  }
+  if (e->p != nullptr && (e->st != st || e->bytes < bytes)) {
+    const hipError_t ef = hipFreeAsync(e->p, e->st);
+    e->p = nullptr;
+    e->bytes = 0;
+    if (ef != hipSuccess) return ef;
+  }
+  if (e->p == nullptr) {
+    const size_t want = bytes + bytes / 4;  // room for somewhat larger calls
+    void* p = nullptr;
+    const hipError_t ea = hipMallocAsync(&p, want, st);
+    if (ea != hipSuccess || p == nullptr) return ea != hipSuccess ? ea : hipErrorOutOfMemory;
+    e->p = p;
+    e->bytes = want;
+  }
+  e->st = st;
+  e->used = ds.clock;
+  *out = e->p;
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------
@@ -370,13 +430,20 @@ int mita_forward_ex(const void* Q, const void* K, const void* V, int dtype, int6
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     derive(s, device_cus());
+    DeviceState* ds = device_state();
+    if (ds == nullptr) return fail(MITA_ERR_HIP, "no current HIP device");
+    std::lock_guard<std::mutex> lk(ds->mu);  // the whole enqueue sequence
+    if (!side_stream_ready(*ds)) {
+      (void)hipGetLastError();
+      return fail(MITA_ERR_HIP, "creating the side stream or its events failed");
+    }
     Workspace ws;
     const size_t bytes = plan_workspace(s, &ws, nullptr);
     void* base = nullptr;
-    hipError_t e = hipMallocAsync(&base, bytes, st);
+    hipError_t e = workspace_for(*ds, st, bytes, &base);
     if (e != hipSuccess || base == nullptr) {
       (void)hipGetLastError();
-      return fail(MITA_ERR_OOM, std::string("hipMallocAsync of work space failed: ") +
+      return fail(MITA_ERR_OOM, std::string("work-space allocation failed: ") +
                                     hipGetErrorString(e));
     }
     plan_workspace(s, &ws, static_cast<char*>(base));
@@ -393,59 +460,38 @@ int mita_forward_ex(const void* Q, const void* K, const void* V, int dtype, int6
       StageTimer t(kStagePool, st);
       e = launch_pool(s, Q, ws, ql_copy, 0, s.BH, st);
     }
-    // Two branches after pooling.  Caller's stream: route, landmark scan,
-    // merge.  Side stream: the sampled top-k pre-threshold (beside routing;
-    // the scan waits for it), then bucketing (after routing, beside the
-    // scan).  The routing kernel does not run beside the scan: the two would
-    // compete for bandwidth and CUs, and the scan's long blocks would start
-    // late.
-    SideStream* ss = (e == hipSuccess) ? side_stream() : nullptr;
-    if (e == hipSuccess && ss == nullptr) {
-      e = hipErrorInvalidResourceHandle;
-      where = "side stream";
+    // Caller's stream: pool, the top-k pre-threshold's group maxima, routing
+    // (the pre-threshold's selection as its leading blocks), landmark scan,
+    // merge, expert attention.  Side stream:
+    // bucketing, forked after routing and joined before the expert
+    // attention, beside the scan and merge.  The pre-threshold does not run
+    // on the side stream beside routing: there its short blocks would queue
+    // behind routing's many blocks, and the scan would wait for them across
+    // streams.
+    if (e == hipSuccess && s.theta_groups > 0) {
+      where = "landmark_threshold";
+      StageTimer t(kStageThreshold, st);
+      e = launch_threshold(s, K, ws, st);
     }
     if (e == hipSuccess) {
-      std::lock_guard<std::mutex> lk(ss->mu);
-      hipError_t ea = hipEventRecord(ss->fork, st);
-      if (ea == hipSuccess) ea = hipStreamWaitEvent(ss->aux, ss->fork, 0);
+      where = "route";
+      StageTimer t(kStageRoute, st);
+      e = launch_route(s, Q, ws, route_out, st);
+    }
+    DeviceState* ss = ds;
+    if (e == hipSuccess) {
+      hipError_t ea = hipEventRecord(ss->routed, st);
+      if (ea == hipSuccess) ea = hipStreamWaitEvent(ss->aux, ss->routed, 0);
       const bool forked = ea == hipSuccess;
-      const char* where_aux = "fork";
+      const char* where_aux = "route event";
       if (forked) {
-        where_aux = "landmark_threshold";
-        StageTimer t(kStageThreshold, ss->aux);
-        ea = launch_threshold(s, K, ws, ss->aux);
-      }
-      bool thr_recorded = false;
-      if (forked && ea == hipSuccess) {
-        ea = hipEventRecord(ss->thr_done, ss->aux);
-        thr_recorded = ea == hipSuccess;
-      }
-      if (e == hipSuccess) {
-        where = "route";
-        StageTimer t(kStageRoute, st);
-        e = launch_route(s, Q, ws, route_out, 0, s.BH, st);
-      }
-      if (forked) {  // bucketing follows routing (recorded also on failure)
-        hipError_t er = hipEventRecord(ss->routed, st);
-        if (er == hipSuccess) er = hipStreamWaitEvent(ss->aux, ss->routed, 0);
-        if (ea == hipSuccess && er != hipSuccess) {
-          ea = er;
-          where_aux = "route event";
-        }
-      }
-      if (forked && ea == hipSuccess && e == hipSuccess) {
         where_aux = "bucket";
         StageTimer t(kStageBucket, ss->aux);
         ea = launch_bucket(s, route_out, ws, off_copy, perm_copy, ss->aux);
       }
-      if (e == hipSuccess) {  // the scan needs the pre-threshold
-        if (thr_recorded) {
-          e = hipStreamWaitEvent(st, ss->thr_done, 0);
-          if (e != hipSuccess) where = "threshold event";
-        } else if (!forked || ea != hipSuccess) {
-          e = ea != hipSuccess ? ea : hipErrorInvalidResourceHandle;
-          where = where_aux;
-        }
+      if (!forked) {
+        e = ea;
+        where = where_aux;
       }
       if (e == hipSuccess) {
         where = "landmark_scan";
@@ -457,7 +503,7 @@ int mita_forward_ex(const void* Q, const void* K, const void* V, int dtype, int6
         StageTimer t(kStageMerge, st);
         e = launch_merge(s, ws, idx_out, vl_copy, st);
       }
-      if (forked) {  // join, also on failure, before the work space is freed
+      if (forked) {  // join, also on failure, before the work space is reused
         hipError_t ej = hipEventRecord(ss->join, ss->aux);
         if (ej == hipSuccess) ej = hipStreamWaitEvent(st, ss->join, 0);
         if (ea == hipSuccess) ea = ej;
@@ -474,12 +520,9 @@ int mita_forward_ex(const void* Q, const void* K, const void* V, int dtype, int6
       e = launch_attend(s, Q, K, V, idx_out, ws, out, st);
     }
     if (g_prof.enabled && e == hipSuccess) g_prof.calls += 1;
-    const hipError_t ef = hipFreeAsync(base, st);
     if (e != hipSuccess)
       return fail(MITA_ERR_HIP, std::string("launch of stage ") + where +
                                     " failed: " + hipGetErrorString(e));
-    if (ef != hipSuccess)
-      return fail(MITA_ERR_HIP, std::string("hipFreeAsync failed: ") + hipGetErrorString(ef));
     return MITA_OK;
   } catch (...) {
     return fail(MITA_ERR_INTERNAL, "unexpected exception inside mita_forward");

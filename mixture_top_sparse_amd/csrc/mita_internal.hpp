@@ -72,14 +72,18 @@ size_t plan_workspace(const Shape& s, Workspace* ws, char* base);
 // Kernel launchers; each returns the launch status.
 hipError_t launch_pool(const Shape& s, const void* Q, const Workspace& ws, void* ql_copy,
                        int64_t bh0, int64_t nbh, hipStream_t st);
+// the pre-threshold's group maxima (the selection runs in the routing
+// launch); no-op when theta_groups == 0
 hipError_t launch_threshold(const Shape& s, const void* K, const Workspace& ws,
-                            hipStream_t st);  // no-op when theta_groups == 0
+                            hipStream_t st);
+hipError_t launch_groups_bf16(const Shape& s, const void* K, const Workspace& ws, hipStream_t st);
 hipError_t launch_scan(const Shape& s, const void* K, const void* V, const Workspace& ws,
                        hipStream_t st);
 hipError_t launch_merge(const Shape& s, const Workspace& ws, int32_t* idx_out, float* vl_copy,
                         hipStream_t st);
+// routing, with the pre-threshold's selection as its leading blocks
 hipError_t launch_route(const Shape& s, const void* Q, const Workspace& ws, int32_t* route_out,
-                        int64_t bh0, int64_t nbh, hipStream_t st);
+                        hipStream_t st);
 hipError_t launch_bucket(const Shape& s, const int32_t* route, const Workspace& ws,
                          int32_t* offsets_copy, int32_t* perm_copy, hipStream_t st);
 hipError_t launch_attend(const Shape& s, const void* Q, const void* K, const void* V,

@@ -172,9 +172,10 @@ int mita_version(void);
 /*
  * Stage profiler (for measurement; off by default).  While enabled, each
  * forward call records a pair of HIP events around every stage on the
- * stream the stage runs on (landmark_threshold and bucket run on a
- * library-owned side stream).  Stages, in order: pool, landmark_threshold (the sampled
- * top-k pre-threshold), landmark_scan, landmark_merge, route, bucket,
+ * stream the stage runs on (bucket runs on a library-owned side stream).
+ * Stages (the array order of mita_profile_read): pool, landmark_threshold
+ * (the top-k pre-threshold's group maxima), landmark_scan, landmark_merge,
+ * route (with the pre-threshold's selection as leading blocks), bucket,
  * expert_attend; each of landmark_scan, route and expert_attend is a single
  * kernel launch.  mita_profile_read() waits for the recorded events and
  * returns, per stage, the summed milliseconds and the number of calls since

@@ -79,15 +79,15 @@ def stage_bytes(w) -> dict[str, float]:
     e = 2 if w.dtype == "bf16" else 4
     BH, N, d, m, k = w.B * w.H, w.N, w.d, w.m, w.k
     rows = min(m * k, N)
-    thr = BH * (threshold_tiles(w) * 64 * d * e + m * d * e)
-    route = BH * (N * d * e + 4 * N)
+    # step 4 (bucketing: read the routes, write perm) rides in the merge
+    # launch; its prefix over the routing counts in the scan launch moves
+    # no per-token bytes
     return {
         "pool": BH * (N * d * e + m * d * e),
-        "landmark_threshold": thr,
+        "landmark_threshold": BH * (threshold_tiles(w) * 64 * d * e + m * d * e),
+        "route": BH * (N * d * e + 4 * N),
         "landmark_scan": BH * (2 * N * d * e),
-        "landmark_merge": BH * (4 * m * k + 4 * m * d),
-        "route": route,
-        "bucket": BH * (4 * N + 4 * N),
+        "landmark_merge": BH * (4 * m * k + 4 * m * d + 4 * N + 4 * N),
         "expert_attend": BH * (N * d * e + 4 * N * d + 4 * N + rows * 2 * d * e),
     }
 
@@ -198,8 +198,8 @@ def dense_baseline(w, Qt, Kt, Vt, mita_ms: float) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="len_1m")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dense", choices=["auto", "on", "off"], default="auto",

@@ -42,16 +42,12 @@
  * are ordered after it by the stream itself.  A block that is too small for
  * a call is released with hipFreeAsync on its stream and replaced; a new
  * stream beyond the eighth takes over the least recently used block.  At
- * 2^20 tokens x 4 heads the block is about 54 MB.  Step 4 runs on a
- * library-owned side stream of the current device (created on first use,
- * default priority, never destroyed), forked from `stream` after step 3 and
- * joined back before step 5, so it overlaps step 2; the call returns with
- * all its work ordered on `stream`.  There is no host synchronisation and no
- * global state besides that side stream, the cached work-space blocks, the
- * per-device attribute cache and the optional stage profiler.  A per-device
- * mutex serialises the enqueue sequences of concurrent host calls; calls on
- * different streams may run concurrently on the GPU (their step-4 kernels
- * share the side stream).
+ * 2^20 tokens x 4 heads the block is about 54 MB.  Every kernel of a call
+ * runs on `stream`; there is no host synchronisation and no global state
+ * besides the cached work-space blocks, the per-device attribute cache and
+ * the optional stage profiler.  A per-device mutex serialises the enqueue
+ * sequences of concurrent host calls; calls on different streams may run
+ * concurrently on the GPU.
  *
  * Errors: every function returns a status.  Arguments are validated on the
  * host before any HIP call; nothing is enqueued when validation fails.  A
@@ -146,7 +142,7 @@ int mita_forward_ex(const void* Q, const void* K, const void* V, int dtype, int6
  * applied to V.  A flash-attention kernel (one pass over K and V per tile of
  * 64 queries, online softmax, bf16 MFMA with fp32 accumulation; the softmax
  * weights are rounded to bf16 once before the P.V product, as flash-attention
- * kernels do).  Enqueued on `stream`; no work space, no side stream.
+ * kernels do).  Enqueued on `stream`; no work space.
  *
  *   Q, K, V    [B][H][N][d] bfloat16 (MITA_BF16 only in this build;
  *              MITA_F32 gives MITA_ERR_UNSUPPORTED)
@@ -171,13 +167,14 @@ int mita_version(void);
 
 /*
  * Stage profiler (for measurement; off by default).  While enabled, each
- * forward call records a pair of HIP events around every stage on the
- * stream the stage runs on (bucket runs on a library-owned side stream).
- * Stages (the array order of mita_profile_read): pool, landmark_threshold
- * (the top-k pre-threshold's group maxima), landmark_scan, landmark_merge,
- * route (with the pre-threshold's selection as leading blocks), bucket,
- * expert_attend; each of landmark_scan, route and expert_attend is a single
- * kernel launch.  mita_profile_read() waits for the recorded events and
+ * forward call records a pair of HIP events around every stage on
+ * `stream`.  Stages, in launch order (the array order of
+ * mita_profile_read): pool, landmark_threshold (the top-k pre-threshold's
+ * group maxima), route (with the pre-threshold's selection as leading
+ * blocks), landmark_scan (with step 4's prefix over the routing counts as
+ * leading blocks), landmark_merge (its first pass carries step 4's
+ * scatter), expert_attend; each of route, landmark_scan and expert_attend
+ * is a single kernel launch.  mita_profile_read() waits for the recorded events and
  * returns, per stage, the summed milliseconds and the number of calls since
  * the last mita_profile_enable().  Not thread-safe: profile from one thread.
  *   mita_profile_enable(1) clears the sums and starts recording;

@@ -11,17 +11,12 @@
 //   k_route          (segment, head): R^T = Ql Q^T on MFMA (landmark rows x
 //                    query columns), argmax with ties to the lower landmark,
 //                    route_out, and the segment's per-expert counts.
-//   k_bucket_scan    (expert, head): prefix of the expert's per-segment counts
-//                    over the segments, and the expert's total.
-//   k_bucket_scatter (segment, head), one wave: expert offsets from the
-//                    totals, then a stable counting sort of the segment in
-//                    LDS (a query's rank among equal routes inside a group
-//                    of 64 comes from 6 ballots over the route bits), copied
-//                    out one expert run at a time.  Segment 0 publishes the
-//                    offsets and the first attention work item of each expert.
+//   k_theta_groups   (tiles, head): the top-k pre-threshold's group maxima
+//                    (its selection runs as k_route's leading blocks).
+// The counting sort that groups queries by expert is finished by the block
+// bodies in mita_bucket.hpp, inside the landmark-scan and merge launches.
 //
-// Roofline: k_route streams Q (N*d*e bytes per head) — HBM-bound; the
-// bucket kernels move ~16 bytes per query.
+// Roofline: k_route streams Q (N*d*e bytes per head) — HBM-bound.
 #include "mita_device.hpp"
 #include "mita_internal.hpp"
 
@@ -330,143 +325,6 @@ __global__ __launch_bounds__(256) void k_theta_groups(const uint16_t* __restrict
     theta_tile_wave<GS, SAMPLED>(K, qls, N, m, groups, ti, bh, gmax);
 }
 
-// inclusive prefix sum over the 64 lanes of a wave
-__device__ __forceinline__ int wave_inclusive_sum(int v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = static_cast<int>(lane_read(static_cast<uint32_t>(v), l >= d ? l - d : l));
-    if (l >= d) v += o;
-  }
-  return v;
-}
-
-// grid (m, BH), 256 threads: for expert e, the exclusive prefix of its
-// per-segment counts over the segments (colpre) and its total
-__global__ __launch_bounds__(256) void k_bucket_scan(const int32_t* __restrict__ counts, int m,
-                                                     int nseg, int32_t* __restrict__ colpre,
-                                                     int32_t* __restrict__ totals) {
-  __shared__ int wsum[4];
-  const int e = blockIdx.x, t = threadIdx.x, l = lane_id(), w = wave_id();
-  const int64_t bh = blockIdx.y;
-  const int32_t* C = counts + (bh * m + e) * nseg;
-  int32_t* P = colpre + (bh * m + e) * nseg;
-  const int per = (nseg + 255) / 256;  // contiguous segments per thread
-  const int s0 = t * per, s1 = min(s0 + per, nseg);
-  int sum = 0;
-  for (int s = s0; s < s1; ++s) sum += C[s];
-  const int incl = wave_inclusive_sum(sum);
-  if (l == 63) wsum[w] = incl;
-  __syncthreads();
-  int run = incl - sum;
-  for (int v = 0; v < w; ++v) run += wsum[v];
-  for (int s = s0; s < s1; ++s) {
-    const int c = C[s];
-    P[s] = run;
-    run += c;
-  }
-  if (t == 255) totals[bh * m + e] = run;
-}
-
-// grid (nseg, BH), 64 threads: stable scatter of one segment's queries.
-// Expert offsets come from the per-expert totals (exclusive scan over the m
-// experts); segment 0 also publishes offsets and the attention work items.
-// The segment is first sorted by route in LDS (ranks from ballots, bases
-// from the routing kernel's per-segment counts); the sorted list is then
-// copied out run by run, so consecutive lanes store consecutive positions of
-// an expert's range instead of one lane per expert region.  Consecutive
-// segments are taken by blocks on one XCD (groups of four), so the partial
-// lines they leave at the ends of each run meet in one L2.
-__global__ __launch_bounds__(64) void k_bucket_scatter(
-    const int32_t* __restrict__ route, const int32_t* __restrict__ counts, int m, int nseg,
-    int64_t N, int tile, int tpb, const int32_t* __restrict__ totals,
-    const int32_t* __restrict__ colpre, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ offsets_copy, int32_t* __restrict__ item_start,
-    int32_t* __restrict__ perm, int32_t* __restrict__ perm_copy) {
-  constexpr int R = 4;  // consecutive segments per XCD
-  __shared__ int lbase[kMaxM];   // next local slot of each expert
-  __shared__ int gshift[kMaxM];  // global position minus local slot, per expert
-  __shared__ int32_t sq[kRouteSeg];
-  __shared__ uint8_t se[kRouteSeg];
-  const int l = threadIdx.x;
-  int seg = blockIdx.x;
-  {  // blocks are dispatched to the XCDs round-robin: b -> XCD b % 8
-    const int n = gridDim.x, full = n / (8 * R) * (8 * R), b = blockIdx.x;
-    if (b < full) seg = ((b / 8 / R) * 8 + b % 8) * R + (b / 8) % R;
-  }
-  const int64_t bh = blockIdx.y;
-  const int c = l < m ? totals[bh * m + l] : 0;
-  const int incl = wave_inclusive_sum(c);
-  if (seg == 0) {
-    const int items = ((c + tile - 1) / tile + tpb - 1) / tpb;
-    const int incl_items = wave_inclusive_sum(items);
-    int32_t* O = offsets + bh * (m + 1);
-    int32_t* I = item_start + bh * (m + 1);
-    if (l < m) {
-      O[l] = incl - c;
-      I[l] = incl_items - items;
-      if (offsets_copy) offsets_copy[bh * (m + 1) + l] = incl - c;
-    }
-    if (l == m - 1) {
-      O[m] = incl;
-      I[m] = incl_items;
-      if (offsets_copy) offsets_copy[bh * (m + 1) + m] = incl;
-    }
-  }
-  // all of the segment's routes in flight at once
-  constexpr int NG = kRouteSeg / 64;
-  const int64_t q0 = static_cast<int64_t>(seg) * kRouteSeg;
-  const int nq = static_cast<int>(N - q0 < kRouteSeg ? N - q0 : kRouteSeg);
-  int rr[NG];
-#pragma unroll
-  for (int it = 0; it < NG; ++it) {
-    const int64_t q = q0 + 64 * it + l;
-    rr[it] = q < N ? route[bh * N + q] : 0;
-  }
-  {
-    const int cl = l < m ? counts[(bh * m + l) * nseg + seg] : 0;
-    const int lex = wave_inclusive_sum(cl) - cl;  // local start of expert l
-    if (l < m) {
-      lbase[l] = lex;
-      gshift[l] = (incl - c) + colpre[(bh * m + l) * nseg + seg] - lex;
-    }
-  }
-  // one wave: its LDS accesses complete in program order, no barriers needed
-  const uint64_t below = (l == 0) ? 0ull : (~0ull >> (64 - l));
-#pragma unroll
-  for (int it = 0; it < NG; ++it) {
-    if (64 * it >= nq) break;
-    const bool ok = 64 * it + l < nq;
-    int r = rr[it];
-    r = r < 0 ? 0 : (r >= m ? m - 1 : r);  // routes come from k_route; clamp defensively
-    uint64_t same = ballot(ok);
-#pragma unroll
-    for (int b = 0; b < 6; ++b) {  // m <= 64: routes fit in 6 bits
-      const bool bit = (r >> b) & 1;
-      const uint64_t bb = ballot(bit);
-      same &= bit ? bb : ~bb;
-    }
-    const int rank = __popcll(same & below);
-    const int total = __popcll(same);
-    const int pos = ok ? lbase[r] + rank : -1;
-    if (pos >= 0 && pos < kRouteSeg) {
-      sq[pos] = static_cast<int32_t>(q0 + 64 * it + l);
-      se[pos] = static_cast<uint8_t>(r);
-    }
-    if (ok && rank == total - 1) lbase[r] += total;  // after every lane's read of lbase[r]
-  }
-  // copy out in sorted order: lanes l, l+1 of one expert run store adjacent
-  // positions
-  for (int i = l; i < nq; i += 64) {
-    const int e = se[i];
-    const int pos = e < m ? gshift[e] + i : -1;
-    if (pos >= 0 && pos < N) {
-      perm[bh * N + pos] = sq[i];
-      if (perm_copy) perm_copy[bh * N + pos] = sq[i];
-    }
-  }
-}
-
 template <class T>
 static hipError_t launch_route_t(const Shape& s, const void* Q, const Workspace& ws,
                                  int32_t* route_out, hipStream_t st) {
@@ -516,18 +374,6 @@ hipError_t launch_route(const Shape& s, const void* Q, const Workspace& ws, int3
                         hipStream_t st) {
   return s.dtype == 1 ? launch_route_t<BF16>(s, Q, ws, route_out, st)
                       : launch_route_t<F32>(s, Q, ws, route_out, st);
-}
-
-hipError_t launch_bucket(const Shape& s, const int32_t* route, const Workspace& ws,
-                         int32_t* offsets_copy, int32_t* perm_copy, hipStream_t st) {
-  hipLaunchKernelGGL(k_bucket_scan, dim3(s.m, s.BH), dim3(256), 0, st, ws.counts, s.m, s.nseg,
-                     ws.colpre, ws.totals);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_bucket_scatter, dim3(s.nseg, s.BH), dim3(64), 0, st, route, ws.counts,
-                     s.m, s.nseg, s.N, kAttendTile, s.attend_tpb, ws.totals, ws.colpre, ws.offsets,
-                     offsets_copy, ws.item_start, ws.perm, perm_copy);
-  return hipGetLastError();
 }
 
 }  // namespace mita

@@ -28,6 +28,7 @@
 // Roofline: HBM-bound; K and V are read once (2*N*d*e bytes per head); the
 // per-split partials add about splits*mrows*(64*4 + 12) bytes per head plus
 // the (few) surviving top-list entries.
+#include "mita_bucket.hpp"
 #include "mita_device.hpp"
 #include "mita_internal.hpp"
 #include "tile_dma.hpp"
@@ -194,7 +195,16 @@ __global__ __launch_bounds__(256) void k_scan_f32(
     const float* __restrict__ K, const float* __restrict__ V, const float* __restrict__ Ql,
     const float* __restrict__ theta, int64_t N, int m, int k, int chunk, int splits, float c2,
     uint64_t* __restrict__ part_keys, int32_t* __restrict__ part_cnt,
-    float* __restrict__ part_stats, float* __restrict__ part_acc) {
+    float* __restrict__ part_stats, float* __restrict__ part_acc, int nbh, BucketArgs ba) {
+  // 1D grid: splits * nbh scan blocks (split-fastest), then m * nbh blocks
+  // for step 4's prefix (one per expert and head), which run in the scan's
+  // tail
+  if (static_cast<int>(blockIdx.x) >= splits * nbh) {  // whole block
+    __shared__ int wsum[4];
+    const int i = static_cast<int>(blockIdx.x) - splits * nbh;
+    bucket_prefix(ba.counts, ba.m, ba.nseg, i % ba.m, i / ba.m, ba.colpre, ba.totals, wsum);
+    return;
+  }
   using T = F32;
   using TR = ScanTraits<T>;
   using E = typename T::elem;
@@ -206,8 +216,8 @@ __global__ __launch_bounds__(256) void k_scan_f32(
 
   const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
   const bool computes = w < NW;
-  const int split = blockIdx.x;
-  const int64_t bh = blockIdx.y;
+  const int split = static_cast<int>(blockIdx.x) % splits;
+  const int64_t bh = static_cast<int>(blockIdx.x) / splits;
   const int lm = w * 16 + c16;
   const bool lm_ok = computes && lm < m;
   const int64_t kbeg = static_cast<int64_t>(split) * chunk;
@@ -367,7 +377,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     const uint16_t* __restrict__ Ql, const float* __restrict__ theta, int64_t N, int m, int k,
     int splits, float c2, uint64_t* __restrict__ part_keys,
     int32_t* __restrict__ part_cnt, float* __restrict__ part_stats,
-    float* __restrict__ part_acc) {
+    float* __restrict__ part_acc, int nbh, BucketArgs ba) {
+  // 1D grid: splits * nbh scan blocks (split-fastest), then m * nbh blocks
+  // for step 4's prefix (one per expert and head), which run in the scan's
+  // tail
+  if (static_cast<int>(blockIdx.x) >= splits * nbh) {  // whole block
+    __shared__ int wsum[4];
+    const int i = static_cast<int>(blockIdx.x) - splits * nbh;
+    bucket_prefix(ba.counts, ba.m, ba.nseg, i % ba.m, i / ba.m, ba.colpre, ba.totals, wsum);
+    return;
+  }
   using TR = ScanTraits<BF16>;
   constexpr int MROWS = NW * 16;
   // ring slots: K tile (8 KiB), then V tile (8 KiB)
@@ -379,8 +398,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   const int l = lane_id(), g = l >> 4, c16 = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(wave_id());
   const bool computes = w < NW;
-  const int split = blockIdx.x;
-  const int64_t bh = blockIdx.y;
+  const int split = static_cast<int>(blockIdx.x) % splits;
+  const int64_t bh = static_cast<int>(blockIdx.x) / splits;
   const int lm = w * 16 + c16;
   const bool lm_ok = computes && lm < m;
   // this block's tiles: split, split + splits, ... (all blocks of a head
@@ -739,27 +758,46 @@ __global__ __launch_bounds__(256) void k_theta_fine(const typename T::elem* __re
 // best.  FINAL (P = 1): writes idx_out (ascending) and Vl.  Otherwise the
 // block's combined top list and softmax state go to the out_* arrays in the
 // layout of the scan's partials with P "splits", for a FINAL pass.
+//
+// Leading blocks (x < nsb) of the launch do step 4's scatter instead: wave w
+// of block x sorts segment 4x + w (mita_bucket.hpp).  The merge blocks
+// follow: block nsb + j is landmark block j % mx of part j / mx (P parts).
 template <bool FINAL, int NWM>
 __global__ __launch_bounds__(256) void k_merge(
     const uint64_t* __restrict__ part_keys, const int32_t* __restrict__ part_cnt,
     const float* __restrict__ part_stats, const float* __restrict__ part_acc, int m, int k,
     int mrows, int splits, int32_t* __restrict__ idx_out, float* __restrict__ vl,
     float* __restrict__ vl_copy, uint64_t* __restrict__ out_keys, int32_t* __restrict__ out_cnt,
-    float* __restrict__ out_stats, float* __restrict__ out_acc) {
+    float* __restrict__ out_stats, float* __restrict__ out_acc, int nsb, int mx, int P,
+    BucketArgs ba) {
   static_assert(NWM == 1 || NWM == 4, "one or four waves per landmark");
   constexpr int kBatch = 8;
-  __shared__ uint64_t tops[NWM][64];
-  __shared__ float sacc[NWM][64];
-  __shared__ float sM[NWM], sL[NWM];
+  // one LDS area: four scatter waves, or the merge's cross-wave exchange
+  constexpr int kMergeLds = NWM * 64 * 12 + NWM * 8;
+  constexpr int kLds = 4 * sizeof(ScatterLds) > kMergeLds ? 4 * sizeof(ScatterLds) : kMergeLds;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
   const int l = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(wave_id());
-  // NWM = 4: the block's four waves share landmark blockIdx.x.  NWM = 1: each
-  // wave takes a landmark of its own (4 * blockIdx.x + w) and all of its splits.
-  const int lm = NWM == 4 ? static_cast<int>(blockIdx.x) : static_cast<int>(blockIdx.x) * 4 + w;
+  const int64_t bh = blockIdx.y;
+  if (static_cast<int>(blockIdx.x) < nsb) {  // whole block: step 4's scatter
+    const int seg = static_cast<int>(blockIdx.x) * 4 + w;
+    if (seg < ba.nseg)
+      scatter_segment(ba.route, ba.counts, ba.m, ba.nseg, ba.N, ba.tile, ba.tpb, ba.totals,
+                      ba.colpre, ba.offsets, ba.offsets_copy, ba.item_start, ba.perm,
+                      ba.perm_copy, seg, bh, reinterpret_cast<ScatterLds*>(smem)[w]);
+    return;
+  }
+  auto tops = reinterpret_cast<uint64_t(*)[64]>(smem);                   // [NWM][64]
+  auto sacc = reinterpret_cast<float(*)[64]>(smem + NWM * 64 * 8);       // [NWM][64]
+  float* sM = reinterpret_cast<float*>(smem + NWM * 64 * 12);            // [NWM]
+  float* sL = sM + NWM;                                                  // [NWM]
+  const int j = static_cast<int>(blockIdx.x) - nsb;
+  const int bx = j % mx, p = j / mx;
+  // NWM = 4: the block's four waves share landmark bx.  NWM = 1: each wave
+  // takes a landmark of its own (4 * bx + w) and all of its splits.
+  const int lm = NWM == 4 ? bx : bx * 4 + w;
   const int wi = NWM == 4 ? w : 0;  // the wave's index among its landmark's waves
   if (lm >= m) return;  // whole wave (NWM = 1 only)
-  const int64_t bh = blockIdx.y;
-  const int P = gridDim.z, p = blockIdx.z;
   const int64_t row0 = bh * splits * mrows + lm;  // partial row of split s: row0 + s * mrows
   const int nmine = splits > p ? (splits - p + P - 1) / P : 0;  // splits of this block
 
@@ -854,20 +892,45 @@ __global__ __launch_bounds__(256) void k_merge(
 
 // ---------------------------------------------------------------------------
 
+// the bucket bodies' arguments for this call
+static BucketArgs bucket_args(const Shape& s, const int32_t* route, const Workspace& ws,
+                              int32_t* offsets_copy, int32_t* perm_copy) {
+  BucketArgs a;
+  a.route = route;
+  a.counts = ws.counts;
+  a.colpre = ws.colpre;
+  a.totals = ws.totals;
+  a.offsets = ws.offsets;
+  a.offsets_copy = offsets_copy;
+  a.item_start = ws.item_start;
+  a.perm = ws.perm;
+  a.perm_copy = perm_copy;
+  a.m = s.m;
+  a.nseg = s.nseg;
+  a.tile = kAttendTile;
+  a.tpb = s.attend_tpb;
+  a.N = s.N;
+  return a;
+}
+
+// 1D grid: splits * BH scan blocks, then m * BH blocks for step 4's prefix
 template <int NW>
 static hipError_t launch_scan_nw(const Shape& s, const void* K, const void* V, const Workspace& ws,
-                                 hipStream_t st) {
+                                 const BucketArgs& ba, hipStream_t st) {
   const float c2 = s.scale * kLog2e;
+  const dim3 grid(static_cast<unsigned>((s.scan_splits + s.m) * s.BH));
   if (s.dtype == 1) {
-    hipLaunchKernelGGL((k_scan_bf16<NW>), dim3(s.scan_splits, s.BH), dim3(256), 0, st,
+    hipLaunchKernelGGL((k_scan_bf16<NW>), grid, dim3(256), 0, st,
                        static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V),
                        static_cast<const uint16_t*>(ws.ql), ws.theta, s.N, s.m, s.k,
-                       s.scan_splits, c2, ws.part_keys, ws.part_cnt, ws.part_stats, ws.part_acc);
+                       s.scan_splits, c2, ws.part_keys, ws.part_cnt, ws.part_stats, ws.part_acc,
+                       static_cast<int>(s.BH), ba);
   } else {
-    hipLaunchKernelGGL((k_scan_f32<NW>), dim3(s.scan_splits, s.BH), dim3(256), 0, st,
+    hipLaunchKernelGGL((k_scan_f32<NW>), grid, dim3(256), 0, st,
                        static_cast<const float*>(K), static_cast<const float*>(V),
                        static_cast<const float*>(ws.ql), ws.theta, s.N, s.m, s.k, s.scan_chunk,
-                       s.scan_splits, c2, ws.part_keys, ws.part_cnt, ws.part_stats, ws.part_acc);
+                       s.scan_splits, c2, ws.part_keys, ws.part_cnt, ws.part_stats, ws.part_acc,
+                       static_cast<int>(s.BH), ba);
   }
   return hipGetLastError();
 }
@@ -904,52 +967,67 @@ hipError_t launch_threshold(const Shape& s, const void* K, const Workspace& ws,
 }
 
 hipError_t launch_scan(const Shape& s, const void* K, const void* V, const Workspace& ws,
-                       hipStream_t st) {
+                       const int32_t* route, hipStream_t st) {
+  const BucketArgs ba = bucket_args(s, route, ws, nullptr, nullptr);
   switch (s.scan_waves) {
-    case 1: return launch_scan_nw<1>(s, K, V, ws, st);
-    case 2: return launch_scan_nw<2>(s, K, V, ws, st);
-    default: return launch_scan_nw<4>(s, K, V, ws, st);
+    case 1: return launch_scan_nw<1>(s, K, V, ws, ba, st);
+    case 2: return launch_scan_nw<2>(s, K, V, ws, ba, st);
+    default: return launch_scan_nw<4>(s, K, V, ws, ba, st);
   }
 }
 
+// one merge pass: nsb scatter blocks (step 4) ahead of the merge blocks
+template <bool FINAL, int NWM>
+static void merge_pass(const Shape& s, const uint64_t* keys, const int32_t* cnt,
+                       const float* stats, const float* acc, int splits, int P, int nsb,
+                       const BucketArgs& ba, int32_t* idx_out, float* vl, float* vl_copy,
+                       uint64_t* out_keys, int32_t* out_cnt, float* out_stats, float* out_acc,
+                       hipStream_t st) {
+  const int mx = NWM == 4 ? s.m : (s.m + 3) / 4;
+  hipLaunchKernelGGL((k_merge<FINAL, NWM>), dim3(nsb + mx * P, s.BH), dim3(256), 0, st, keys, cnt,
+                     stats, acc, s.m, s.k, s.mrows, splits, idx_out, vl, vl_copy, out_keys,
+                     out_cnt, out_stats, out_acc, nsb, mx, P, ba);
+}
+
 hipError_t launch_merge(const Shape& s, const Workspace& ws, int32_t* idx_out, float* vl_copy,
+                        const int32_t* route, int32_t* offsets_copy, int32_t* perm_copy,
                         hipStream_t st) {
   // one wave per landmark (four landmarks per block) when a landmark has at
   // most 4 partials, else four waves per landmark (the one wave merges its
-  // partials one after another: shorter only for a few)
-  const dim3 g1(s.m, s.BH, 1), g4((s.m + 3) / 4, s.BH, 1);
+  // partials one after another: shorter only for a few).  The first pass
+  // also carries step 4's scatter, a wave per route segment.
+  const BucketArgs ba = bucket_args(s, route, ws, offsets_copy, perm_copy);
+  const int nsb = (s.nseg + 3) / 4;
   if (s.merge_parts > 1) {  // first level: merge_parts partial combinations per landmark
     const int per = (s.scan_splits + s.merge_parts - 1) / s.merge_parts;
     if (per <= 4)
-      hipLaunchKernelGGL((k_merge<false, 1>), dim3(g4.x, s.BH, s.merge_parts), dim3(256), 0, st,
-                         ws.part_keys, ws.part_cnt, ws.part_stats, ws.part_acc, s.m, s.k, s.mrows,
-                         s.scan_splits, nullptr, nullptr, nullptr, ws.part2_keys, ws.part2_cnt,
-                         ws.part2_stats, ws.part2_acc);
+      merge_pass<false, 1>(s, ws.part_keys, ws.part_cnt, ws.part_stats, ws.part_acc,
+                           s.scan_splits, s.merge_parts, nsb, ba, nullptr, nullptr, nullptr,
+                           ws.part2_keys, ws.part2_cnt, ws.part2_stats, ws.part2_acc, st);
     else
-      hipLaunchKernelGGL((k_merge<false, 4>), dim3(s.m, s.BH, s.merge_parts), dim3(256), 0, st,
-                         ws.part_keys, ws.part_cnt, ws.part_stats, ws.part_acc, s.m, s.k, s.mrows,
-                         s.scan_splits, nullptr, nullptr, nullptr, ws.part2_keys, ws.part2_cnt,
-                         ws.part2_stats, ws.part2_acc);
+      merge_pass<false, 4>(s, ws.part_keys, ws.part_cnt, ws.part_stats, ws.part_acc,
+                           s.scan_splits, s.merge_parts, nsb, ba, nullptr, nullptr, nullptr,
+                           ws.part2_keys, ws.part2_cnt, ws.part2_stats, ws.part2_acc, st);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (s.merge_parts <= 4)
-      hipLaunchKernelGGL((k_merge<true, 1>), g4, dim3(256), 0, st, ws.part2_keys, ws.part2_cnt,
-                         ws.part2_stats, ws.part2_acc, s.m, s.k, s.mrows, s.merge_parts, idx_out,
-                         ws.vl, vl_copy, nullptr, nullptr, nullptr, nullptr);
+      merge_pass<true, 1>(s, ws.part2_keys, ws.part2_cnt, ws.part2_stats, ws.part2_acc,
+                          s.merge_parts, 1, 0, ba, idx_out, ws.vl, vl_copy, nullptr, nullptr,
+                          nullptr, nullptr, st);
     else
-      hipLaunchKernelGGL((k_merge<true, 4>), g1, dim3(256), 0, st, ws.part2_keys, ws.part2_cnt,
-                         ws.part2_stats, ws.part2_acc, s.m, s.k, s.mrows, s.merge_parts, idx_out,
-                         ws.vl, vl_copy, nullptr, nullptr, nullptr, nullptr);
+      merge_pass<true, 4>(s, ws.part2_keys, ws.part2_cnt, ws.part2_stats, ws.part2_acc,
+                          s.merge_parts, 1, 0, ba, idx_out, ws.vl, vl_copy, nullptr, nullptr,
+                          nullptr, nullptr, st);
     return hipGetLastError();
   }
   if (s.scan_splits <= 4)
-    hipLaunchKernelGGL((k_merge<true, 1>), g4, dim3(256), 0, st, ws.part_keys, ws.part_cnt,
-                       ws.part_stats, ws.part_acc, s.m, s.k, s.mrows, s.scan_splits, idx_out,
-                       ws.vl, vl_copy, nullptr, nullptr, nullptr, nullptr);
+    merge_pass<true, 1>(s, ws.part_keys, ws.part_cnt, ws.part_stats, ws.part_acc, s.scan_splits,
+                        1, nsb, ba, idx_out, ws.vl, vl_copy, nullptr, nullptr, nullptr, nullptr,
+                        st);
   else
-    hipLaunchKernelGGL((k_merge<true, 4>), g1, dim3(256), 0, st, ws.part_keys, ws.part_cnt,
-                       ws.part_stats, ws.part_acc, s.m, s.k, s.mrows, s.scan_splits, idx_out,
-                       ws.vl, vl_copy, nullptr, nullptr, nullptr, nullptr);
+    merge_pass<true, 4>(s, ws.part_keys, ws.part_cnt, ws.part_stats, ws.part_acc, s.scan_splits,
+                        1, nsb, ba, idx_out, ws.vl, vl_copy, nullptr, nullptr, nullptr, nullptr,
+                        st);
   return hipGetLastError();
 }
 

@@ -32,19 +32,18 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // stage profiler
 // ---------------------------------------------------------------------------
 
+// in launch order; step 4 (bucketing) runs inside the scan and merge stages
 enum Stage {
   kStagePool = 0,
   kStageThreshold,
+  kStageRoute,
   kStageScan,
   kStageMerge,
-  kStageRoute,
-  kStageBucket,
   kStageAttend,
   kStageCount
 };
-const char* kStageNames[kStageCount] = {"pool",           "landmark_threshold", "landmark_scan",
-                                        "landmark_merge", "route",              "bucket",
-                                        "expert_attend"};
+const char* kStageNames[kStageCount] = {"pool",          "landmark_threshold", "route",
+                                        "landmark_scan", "landmark_merge",     "expert_attend"};
 
 struct Profiler {
   bool enabled = false;
@@ -120,30 +119,22 @@ int device_cus() {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // ---------------------------------------------------------------------------
-// per-device state: the side stream and the cached work spaces
+// per-device state: the cached work spaces
 //
-// Bucketing depends only on the routes, and the landmark branch (scan,
-// merge) only on the pooled landmarks and the pre-threshold, so the two run
-// concurrently: fork after routing, join before the expert attention.  The
-// side stream has default priority and is non-blocking.
-//
-// Work space: one block per calling stream (up to kWsStreams per device),
-// kept between calls and reused while it is large enough.  Calls on one
-// stream are ordered by that stream, so a call's kernels never overlap the
-// previous call's use of the block.  A block that is too small is released
-// with hipFreeAsync on its stream and replaced by a larger hipMallocAsync
-// block; the least recently used entry makes room for a new stream.  The
-// device mutex is held for the whole enqueue sequence of a call, so calls
-// from several host threads on one stream do not interleave their kernels.
+// One block per calling stream (up to kWsStreams per device), kept between
+// calls and reused while it is large enough.  Calls on one stream are
+// ordered by that stream, so a call's kernels never overlap the previous
+// call's use of the block.  A block that is too small is released with
+// hipFreeAsync on its stream and replaced by a larger hipMallocAsync block;
+// the least recently used entry makes room for a new stream.  The device
+// mutex is held for the whole enqueue sequence of a call, so calls from
+// several host threads on one stream do not interleave their kernels.
 // ---------------------------------------------------------------------------
 
 constexpr int kWsStreams = 8;
 
 struct DeviceState {
   std::mutex mu;
-  bool ready = false;
-  hipStream_t aux = nullptr;
-  hipEvent_t routed = nullptr, join = nullptr;
   struct Ws {
     hipStream_t st = nullptr;
     void* p = nullptr;
@@ -154,29 +145,11 @@ struct DeviceState {
 };
 DeviceState g_dev[64];
 
-// the current device's state (side stream and events created on first use);
-// the caller holds ds->mu
+// the current device's state; the caller holds its mutex while using it
 DeviceState* device_state() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
   return &g_dev[dev];
-}
-
-bool side_stream_ready(DeviceState& ds) {
-  if (!ds.ready) {
-    if (ds.aux == nullptr && hipStreamCreateWithFlags(&ds.aux, hipStreamNonBlocking) != hipSuccess) {
-      ds.aux = nullptr;
-      return false;
-    }
-    for (hipEvent_t* ev : {&ds.routed, &ds.join}) {
-      if (*ev == nullptr && hipEventCreateWithFlags(ev, hipEventDisableTiming) != hipSuccess) {
-        *ev = nullptr;  // kept for the next attempt; the rest stay created
-        return false;
-      }
-    }
-    ds.ready = true;
-  }
-  return true;
 }
 
 // a work-space block of at least `bytes` for calls on stream st
@@ -433,10 +406,6 @@ int mita_forward_ex(const void* Q, const void* K, const void* V, int dtype, int6
     DeviceState* ds = device_state();
     if (ds == nullptr) return fail(MITA_ERR_HIP, "no current HIP device");
     std::lock_guard<std::mutex> lk(ds->mu);  // the whole enqueue sequence
-    if (!side_stream_ready(*ds)) {
-      (void)hipGetLastError();
-      return fail(MITA_ERR_HIP, "creating the side stream or its events failed");
-    }
     Workspace ws;
     const size_t bytes = plan_workspace(s, &ws, nullptr);
     void* base = nullptr;
@@ -460,14 +429,13 @@ int mita_forward_ex(const void* Q, const void* K, const void* V, int dtype, int6
       StageTimer t(kStagePool, st);
       e = launch_pool(s, Q, ws, ql_copy, 0, s.BH, st);
     }
-    // Caller's stream: pool, the top-k pre-threshold's group maxima, routing
-    // (the pre-threshold's selection as its leading blocks), landmark scan,
-    // merge, expert attention.  Side stream:
-    // bucketing, forked after routing and joined before the expert
-    // attention, beside the scan and merge.  The pre-threshold does not run
-    // on the side stream beside routing: there its short blocks would queue
-    // behind routing's many blocks, and the scan would wait for them across
-    // streams.
+    // All on the caller's stream, in this order: pool; the top-k
+    // pre-threshold's group maxima; routing (the pre-threshold's selection as
+    // its leading blocks); the landmark scan (step 4's prefix over the
+    // routing counts as its leading blocks); the merge (step 4's scatter as
+    // leading blocks of its first pass); the expert attention.  Bucketing
+    // rides in launches that follow routing anyway, so the call needs no
+    // second stream and no events.
     if (e == hipSuccess && s.theta_groups > 0) {
       where = "landmark_threshold";
       StageTimer t(kStageThreshold, st);
@@ -478,41 +446,15 @@ int mita_forward_ex(const void* Q, const void* K, const void* V, int dtype, int6
       StageTimer t(kStageRoute, st);
       e = launch_route(s, Q, ws, route_out, st);
     }
-    DeviceState* ss = ds;
     if (e == hipSuccess) {
-      hipError_t ea = hipEventRecord(ss->routed, st);
-      if (ea == hipSuccess) ea = hipStreamWaitEvent(ss->aux, ss->routed, 0);
-      const bool forked = ea == hipSuccess;
-      const char* where_aux = "route event";
-      if (forked) {
-        where_aux = "bucket";
-        StageTimer t(kStageBucket, ss->aux);
-        ea = launch_bucket(s, route_out, ws, off_copy, perm_copy, ss->aux);
-      }
-      if (!forked) {
-        e = ea;
-        where = where_aux;
-      }
-      if (e == hipSuccess) {
-        where = "landmark_scan";
-        StageTimer t(kStageScan, st);
-        e = launch_scan(s, K, V, ws, st);
-      }
-      if (e == hipSuccess) {
-        where = "landmark_merge";
-        StageTimer t(kStageMerge, st);
-        e = launch_merge(s, ws, idx_out, vl_copy, st);
-      }
-      if (forked) {  // join, also on failure, before the work space is reused
-        hipError_t ej = hipEventRecord(ss->join, ss->aux);
-        if (ej == hipSuccess) ej = hipStreamWaitEvent(st, ss->join, 0);
-        if (ea == hipSuccess) ea = ej;
-        if (ej != hipSuccess) (void)hipStreamSynchronize(ss->aux);
-      }
-      if (e == hipSuccess && ea != hipSuccess) {
-        e = ea;
-        where = where_aux;
-      }
+      where = "landmark_scan";
+      StageTimer t(kStageScan, st);
+      e = launch_scan(s, K, V, ws, route_out, st);
+    }
+    if (e == hipSuccess) {
+      where = "landmark_merge";
+      StageTimer t(kStageMerge, st);
+      e = launch_merge(s, ws, idx_out, vl_copy, route_out, off_copy, perm_copy, st);
     }
     if (e == hipSuccess) {
       where = "expert_attend";

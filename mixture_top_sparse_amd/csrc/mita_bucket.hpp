@@ -1,0 +1,179 @@
+// mita_bucket.hpp — step 4's device work: group the queries by expert with a
+// stable counting sort ("Mixture-of-Top-k 注意力…", section "MiTA：用少量地标
+// 查询，同时完成压缩与专家构造", the implementation remark that queries are
+// processed grouped by expert; "And attention is also FFN? …", Algorithm 1
+// caption: each expert handles the subset of queries routed to it).
+//
+// The routing kernel leaves per-segment expert counts (segments of kRouteSeg
+// queries, stored expert-major).  Two block bodies finish the sort; neither
+// has a launch of its own:
+//   bucket_prefix   (one 256-thread block per expert and head): exclusive
+//                   prefix of the expert's counts over the segments, and the
+//                   expert's total.  Leading blocks of the landmark-scan
+//                   launch, which follows routing on the same stream.
+//   scatter_segment (one wave per segment): expert offsets from the totals,
+//                   then a stable sort of the segment in LDS (a query's rank
+//                   among equal routes inside a group of 64 comes from 6
+//                   ballots over the route bits), copied out one expert run
+//                   at a time.  Segment 0 publishes the offsets and the first
+//                   attention work item of each expert.  Leading blocks of the
+//                   first landmark-merge launch, four segments per block.
+// Both depend only on the routes and the counts; the expert attention that
+// reads their results is the next launch after the merge.
+#pragma once
+
+#include "mita_device.hpp"
+#include "mita_internal.hpp"
+
+namespace mita {
+
+// inclusive prefix sum over the 64 lanes of a wave
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = static_cast<int>(lane_read(static_cast<uint32_t>(v), l >= d ? l - d : l));
+    if (l >= d) v += o;
+  }
+  return v;
+}
+
+// Whole 256-thread block: for expert e of head bh, the exclusive prefix of
+// its per-segment counts over the segments (colpre) and its total.  wsum:
+// 4 ints of LDS.
+__device__ __forceinline__ void bucket_prefix(const int32_t* __restrict__ counts, int m, int nseg,
+                                              int e, int64_t bh, int32_t* __restrict__ colpre,
+                                              int32_t* __restrict__ totals, int* wsum) {
+  const int t = threadIdx.x, l = lane_id(), w = wave_id();
+  const int32_t* C = counts + (bh * m + e) * nseg;
+  int32_t* P = colpre + (bh * m + e) * nseg;
+  const int per = (nseg + 255) / 256;  // contiguous segments per thread
+  const int s0 = t * per, s1 = min(s0 + per, nseg);
+  int sum = 0;
+  for (int s = s0; s < s1; ++s) sum += C[s];
+  const int incl = wave_inclusive_sum(sum);
+  if (l == 63) wsum[w] = incl;
+  __syncthreads();
+  int run = incl - sum;
+  for (int v = 0; v < w; ++v) run += wsum[v];
+  for (int s = s0; s < s1; ++s) {
+    const int c = C[s];
+    P[s] = run;
+    run += c;
+  }
+  if (t == 255) totals[bh * m + e] = run;
+}
+
+// LDS of one scatter wave
+struct ScatterLds {
+  int lbase[kMaxM];   // next local slot of each expert
+  int gshift[kMaxM];  // global position minus local slot, per expert
+  int32_t sq[kRouteSeg];
+  uint8_t se[kRouteSeg];
+};
+
+// One wave: stable scatter of segment seg of head bh.  Expert offsets come
+// from the per-expert totals (exclusive scan over the m experts); segment 0
+// also publishes offsets and the attention work items.  The segment is
+// first sorted by route in LDS (ranks from ballots, bases from the routing
+// kernel's per-segment counts); the sorted list is then copied out run by
+// run, so consecutive lanes store consecutive positions of an expert's
+// range instead of one lane per expert region.  The caller gives the four
+// waves of a block four consecutive segments: one CU, one XCD, so the
+// partial lines they leave at the ends of each run meet in one L2.
+__device__ __forceinline__ void scatter_segment(
+    const int32_t* __restrict__ route, const int32_t* __restrict__ counts, int m, int nseg,
+    int64_t N, int tile, int tpb, const int32_t* __restrict__ totals,
+    const int32_t* __restrict__ colpre, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ offsets_copy, int32_t* __restrict__ item_start,
+    int32_t* __restrict__ perm, int32_t* __restrict__ perm_copy, int seg, int64_t bh,
+    ScatterLds& L) {
+  const int l = lane_id();
+  const int c = l < m ? totals[bh * m + l] : 0;
+  const int incl = wave_inclusive_sum(c);
+  if (seg == 0) {
+    const int items = ((c + tile - 1) / tile + tpb - 1) / tpb;
+    const int incl_items = wave_inclusive_sum(items);
+    int32_t* O = offsets + bh * (m + 1);
+    int32_t* I = item_start + bh * (m + 1);
+    if (l < m) {
+      O[l] = incl - c;
+      I[l] = incl_items - items;
+      if (offsets_copy) offsets_copy[bh * (m + 1) + l] = incl - c;
+    }
+    if (l == m - 1) {
+      O[m] = incl;
+      I[m] = incl_items;
+      if (offsets_copy) offsets_copy[bh * (m + 1) + m] = incl;
+    }
+  }
+  // all of the segment's routes in flight at once
+  constexpr int NG = kRouteSeg / 64;
+  const int64_t q0 = static_cast<int64_t>(seg) * kRouteSeg;
+  const int nq = static_cast<int>(N - q0 < kRouteSeg ? N - q0 : kRouteSeg);
+  int rr[NG];
+#pragma unroll
+  for (int it = 0; it < NG; ++it) {
+    const int64_t q = q0 + 64 * it + l;
+    rr[it] = q < N ? route[bh * N + q] : 0;
+  }
+  {
+    const int cl = l < m ? counts[(bh * m + l) * nseg + seg] : 0;
+    const int lex = wave_inclusive_sum(cl) - cl;  // local start of expert l
+    if (l < m) {
+      L.lbase[l] = lex;
+      L.gshift[l] = (incl - c) + colpre[(bh * m + l) * nseg + seg] - lex;
+    }
+  }
+  // one wave: its LDS accesses complete in program order, no barriers needed
+  const uint64_t below = (l == 0) ? 0ull : (~0ull >> (64 - l));
+#pragma unroll
+  for (int it = 0; it < NG; ++it) {
+    if (64 * it >= nq) break;
+    const bool ok = 64 * it + l < nq;
+    int r = rr[it];
+    r = r < 0 ? 0 : (r >= m ? m - 1 : r);  // routes come from k_route; clamp defensively
+    uint64_t same = ballot(ok);
+#pragma unroll
+    for (int b = 0; b < 6; ++b) {  // m <= 64: routes fit in 6 bits
+      const bool bit = (r >> b) & 1;
+      const uint64_t bb = ballot(bit);
+      same &= bit ? bb : ~bb;
+    }
+    const int rank = __popcll(same & below);
+    const int total = __popcll(same);
+    const int pos = ok ? L.lbase[r] + rank : -1;
+    if (pos >= 0 && pos < kRouteSeg) {
+      L.sq[pos] = static_cast<int32_t>(q0 + 64 * it + l);
+      L.se[pos] = static_cast<uint8_t>(r);
+    }
+    if (ok && rank == total - 1) L.lbase[r] += total;  // after every lane's read of lbase[r]
+  }
+  // copy out in sorted order: lanes l, l+1 of one expert run store adjacent
+  // positions
+  for (int i = l; i < nq; i += 64) {
+    const int e = L.se[i];
+    const int pos = e < m ? L.gshift[e] + i : -1;
+    if (pos >= 0 && pos < N) {
+      perm[bh * N + pos] = L.sq[i];
+      if (perm_copy) perm_copy[bh * N + pos] = L.sq[i];
+    }
+  }
+}
+
+// Arguments of the bucket bodies, passed through the scan and merge launches.
+struct BucketArgs {
+  const int32_t* route;
+  const int32_t* counts;
+  int32_t* colpre;
+  int32_t* totals;
+  int32_t* offsets;
+  int32_t* offsets_copy;
+  int32_t* item_start;
+  int32_t* perm;
+  int32_t* perm_copy;
+  int m, nseg, tile, tpb;
+  int64_t N;
+};
+
+}  // namespace mita

@@ -77,15 +77,18 @@ hipError_t launch_pool(const Shape& s, const void* Q, const Workspace& ws, void*
 hipError_t launch_threshold(const Shape& s, const void* K, const Workspace& ws,
                             hipStream_t st);
 hipError_t launch_groups_bf16(const Shape& s, const void* K, const Workspace& ws, hipStream_t st);
+// landmark scan, with step 4's prefix over the routing counts as leading
+// blocks (needs the routes' counts: after launch_route)
 hipError_t launch_scan(const Shape& s, const void* K, const void* V, const Workspace& ws,
-                       hipStream_t st);
+                       const int32_t* route, hipStream_t st);
+// merge of the scan partials, with step 4's scatter as leading blocks of
+// its first pass (perm, offsets and the attention work items)
 hipError_t launch_merge(const Shape& s, const Workspace& ws, int32_t* idx_out, float* vl_copy,
+                        const int32_t* route, int32_t* offsets_copy, int32_t* perm_copy,
                         hipStream_t st);
 // routing, with the pre-threshold's selection as its leading blocks
 hipError_t launch_route(const Shape& s, const void* Q, const Workspace& ws, int32_t* route_out,
                         hipStream_t st);
-hipError_t launch_bucket(const Shape& s, const int32_t* route, const Workspace& ws,
-                         int32_t* offsets_copy, int32_t* perm_copy, hipStream_t st);
 hipError_t launch_attend(const Shape& s, const void* Q, const void* K, const void* V,
                          const int32_t* idx, const Workspace& ws, float* out, hipStream_t st);
 // dense attention over all N pairs (the baseline); bf16 only

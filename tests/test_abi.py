@@ -123,8 +123,8 @@ def test_python_binding_rejects_cpu_tensors():
 def test_profiler_without_calls(L):
     mts.mita_profile_enable(True)
     ms, calls = mts.mita_profile_read()
-    assert calls == 0 and set(ms) == {"pool", "landmark_threshold", "landmark_scan",
-                                      "landmark_merge", "route", "bucket", "expert_attend"}
+    assert calls == 0 and list(ms) == ["pool", "landmark_threshold", "route", "landmark_scan",
+                                       "landmark_merge", "expert_attend"]
     mts.mita_profile_enable(False)
 
 

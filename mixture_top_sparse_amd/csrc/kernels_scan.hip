@@ -371,7 +371,11 @@ __global__ __launch_bounds__(256) void k_scan_f32(
 // With three blocks per CU (at most 168 VGPRs) that keeps 48 KiB of tile
 // requests in flight per CU; deeper rings (96 KiB per CU) measured slower,
 // the DMA path losing bandwidth when that many requests queue up.
-template <int NW>
+// CAP: candidate buffer entries per landmark.  8 in general; 64 where the
+// pre-threshold is the exact k-th score (N <= 4096 keys): then about k keys
+// per landmark pass it, and a 64-entry buffer takes them all without a
+// sort-and-merge per 8 candidates (the end-of-block flush sorts each once).
+template <int NW, int CAP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_scan_bf16(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ Ql, const float* __restrict__ theta, int64_t N, int m, int k,
@@ -392,8 +396,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   // ring slots: K tile (8 KiB), then V tile (8 KiB)
   __shared__ __attribute__((aligned(16))) uint8_t b0[16384];
   __shared__ __attribute__((aligned(16))) uint8_t b1[16384];
-  __shared__ uint64_t cand[MROWS][kCandCap];
-  __shared__ int lcnt[MROWS];  // candidates buffered per landmark (may overshoot kCandCap)
+  __shared__ uint64_t cand[MROWS][CAP];
+  __shared__ int lcnt[MROWS];  // candidates buffered per landmark (may overshoot CAP)
 
   const int l = lane_id(), g = l >> 4, c16 = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(wave_id());
@@ -445,9 +449,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 
   // merge landmark slot L's candidate buffer into its top list (whole wave)
   auto merge_slot = [&](int L) __attribute__((always_inline)) {
-    const int n = min(lcnt[w * 16 + L], kCandCap);
+    const int n = min(lcnt[w * 16 + L], CAP);
     uint64_t c = (l < n) ? cand[w * 16 + L][l] : 0ull;
-    c = wave_sort_desc_first<kCandCap>(c);
+    c = wave_sort_desc_first<CAP>(c);
     top[L] = wave_merge_top(top[L], c);
     const uint64_t kth = uniform_read(top[L], k - 1);
     if (l == 0) lcnt[w * 16 + L] = 0;
@@ -495,7 +499,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
             if (ballot(pass)) {
               if (pass) {
                 const int slot = lds_fetch_add1(lcnt_addr);
-                if (slot < kCandCap)
+                if (slot < CAP)
                   lds_store_u64(cand_addr + 8 * slot,
                                 make_key(sc[kb][r], static_cast<uint32_t>(t0 + 16 * kb + 4 * g + r)));
                 else
@@ -524,7 +528,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
                 float v = sc[kb][r];
                 __asm__ volatile("" : "+v"(v));  // keep the key work in this rare path
                 const int slot = lds_fetch_add1(lcnt_addr);
-                if (slot < kCandCap)
+                if (slot < CAP)
                   lds_store_u64(cand_addr + 8 * slot,
                                 make_key(v, static_cast<uint32_t>(t0 + 16 * kb + 4 * g + r)));
                 else
@@ -609,11 +613,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     uint64_t c[16];
 #pragma unroll
     for (int L = 0; L < 16; ++L) {
-      const int n = min(lcnt[w * 16 + L], kCandCap);
+      const int n = min(lcnt[w * 16 + L], CAP);
       c[L] = (l < n) ? cand[w * 16 + L][l] : 0ull;
     }
 #pragma unroll
-    for (int size = 2; size <= kCandCap; size <<= 1) {
+    for (int size = 2; size <= CAP; size <<= 1) {
       const bool desc_block = (l & size) == 0;
 #pragma unroll
       for (int stride = size >> 1; stride >= 1; stride >>= 1)
@@ -920,11 +924,19 @@ static hipError_t launch_scan_nw(const Shape& s, const void* K, const void* V, c
   const float c2 = s.scale * kLog2e;
   const dim3 grid(static_cast<unsigned>((s.scan_splits + s.m) * s.BH));
   if (s.dtype == 1) {
-    hipLaunchKernelGGL((k_scan_bf16<NW>), grid, dim3(256), 0, st,
-                       static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V),
-                       static_cast<const uint16_t*>(ws.ql), ws.theta, s.N, s.m, s.k,
-                       s.scan_splits, c2, ws.part_keys, ws.part_cnt, ws.part_stats, ws.part_acc,
-                       static_cast<int>(s.BH), ba);
+    const bool exact = s.theta_groups > 0 && !s.theta_sampled && s.theta_gs == 1;
+    if (exact)
+      hipLaunchKernelGGL((k_scan_bf16<NW, 64>), grid, dim3(256), 0, st,
+                         static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V),
+                         static_cast<const uint16_t*>(ws.ql), ws.theta, s.N, s.m, s.k,
+                         s.scan_splits, c2, ws.part_keys, ws.part_cnt, ws.part_stats,
+                         ws.part_acc, static_cast<int>(s.BH), ba);
+    else
+      hipLaunchKernelGGL((k_scan_bf16<NW, kCandCap>), grid, dim3(256), 0, st,
+                         static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V),
+                         static_cast<const uint16_t*>(ws.ql), ws.theta, s.N, s.m, s.k,
+                         s.scan_splits, c2, ws.part_keys, ws.part_cnt, ws.part_stats,
+                         ws.part_acc, static_cast<int>(s.BH), ba);
   } else {
     hipLaunchKernelGGL((k_scan_f32<NW>), grid, dim3(256), 0, st,
                        static_cast<const float*>(K), static_cast<const float*>(V),

@@ -123,10 +123,72 @@ __global__ __launch_bounds__(64) void k_pool_final(const double* __restrict__ pa
   if (ql_copy) ql_copy[(bh * m + i) * kD + j] = v;
 }
 
+// Small windows (at most kPoolDirectMax tokens, the 2D image grids): grid
+// (ceil(m / 8), BH), 256 threads; 32 lanes per landmark = 8 groups of 8
+// columns x 4 token phases.  Each lane sums every fourth token of its
+// landmark's window for its 8 columns in fp64 (loads unrolled by 4), the
+// four phases combine by lane swaps, and phase 0 divides once and rounds:
+// one launch instead of a partial-sum and a final launch.  The fp64 sums are
+// exact for bf16 inputs, so the order of the additions does not matter.
+template <class T>
+__global__ __launch_bounds__(256) void k_pool_direct(const typename T::elem* __restrict__ Q,
+                                                    int64_t N, int gh, int gw, int mh, int mw,
+                                                    typename T::elem* __restrict__ ql,
+                                                    typename T::elem* __restrict__ ql_copy) {
+  const int m = mh * mw;
+  const int u = static_cast<int>(blockIdx.x) * 256 + threadIdx.x;
+  const int i = u >> 5, col = (u >> 2) & 7, ph = u & 3;
+  const int64_t bh = blockIdx.y;
+  int64_t r0, r1, c0, c1;
+  window_bounds(gh, gw, mh, mw, i < m ? i : m - 1, r0, r1, c0, c1);
+  const int64_t wc = c1 - c0, W = (r1 - r0) * wc;
+  const typename T::elem* Qh = Q + bh * N * kD + col * 8;
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  auto tok = [&](int64_t t) { return (r0 + t / wc) * gw + (c0 + t % wc); };
+  int64_t t = ph;
+  for (; t + 12 < W; t += 16) {  // four tokens of this phase in flight
+    float v[4][8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) load8(Qh + tok(t + 4 * j) * kD, v[j]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += static_cast<double>(v[j][e]);
+  }
+  for (; t < W; t += 4) {
+    float v[8];
+    load8(Qh + tok(t) * kD, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += static_cast<double>(v[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    acc[e] += __shfl_xor(acc[e], 1);
+    acc[e] += __shfl_xor(acc[e], 2);
+  }
+  if (ph == 0 && i < m) {
+    const double Wd = static_cast<double>(W);
+    typename T::elem* dst = ql + (bh * m + i) * kD + col * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const typename T::elem v = T::from_f64(acc[e] / Wd);
+      dst[e] = v;
+      if (ql_copy) ql_copy[(bh * m + i) * kD + col * 8 + e] = v;
+    }
+  }
+}
+
 template <class T>
 static hipError_t launch_pool_t(const Shape& s, const void* Q, const Workspace& ws, void* ql_copy,
                                 int64_t bh0, int64_t nbh, hipStream_t st) {
   using E = typename T::elem;
+  if (s.pool_direct) {
+    hipLaunchKernelGGL(k_pool_direct<T>, dim3((s.m + 7) / 8, nbh), dim3(256), 0, st,
+                       static_cast<const E*>(Q) + bh0 * s.N * kD, s.N, s.gh, s.gw, s.mh, s.mw,
+                       static_cast<E*>(ws.ql) + bh0 * s.m * kD,
+                       ql_copy ? static_cast<E*>(ql_copy) + bh0 * s.m * kD : nullptr);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_pool_partial<T>, dim3(s.pool_splits, s.m, nbh), dim3(256), 0, st,
                      static_cast<const E*>(Q), s.N, s.gh, s.gw, s.mh, s.mw, s.pool_splits, bh0,
                      ws.pool_part);

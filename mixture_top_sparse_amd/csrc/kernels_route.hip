@@ -128,9 +128,10 @@ __device__ __forceinline__ void stage_landmarks(const E* __restrict__ Ql, int m,
   }
 }
 
-// One routing block (256 threads): wave w routes queries seg*1024 + 256w +
-// [0, 256) of head bh in 16 groups of 16 queries, four groups of Q rows in
-// flight, and the block stores the segment's per-expert counts.
+// One routing block (256 threads) routes queries seg*1024 + [0, 1024) of
+// head bh in 64 groups of 16; wave w takes groups w, w + 4, w + 8, ... (so a
+// short head keeps all four waves busy), four groups of Q rows in flight,
+// and the block stores the segment's per-expert counts.
 template <class T>
 __device__ __forceinline__ void route_segment(const typename T::elem* __restrict__ Q,
                                               const typename T::elem* __restrict__ Ql,
@@ -144,14 +145,15 @@ __device__ __forceinline__ void route_segment(const typename T::elem* __restrict
   if (threadIdx.x < kMaxM) cnt[threadIdx.x] = 0;
   stage_landmarks(Ql, m, bh, qls);
   const E* Qh = Q + bh * N * kD;
-  const int64_t qw = static_cast<int64_t>(seg) * kRouteSeg + 256 * w;
+  // group G of this wave: queries qw + 64 G + [0, 16)
+  const int64_t qw = static_cast<int64_t>(seg) * kRouteSeg + 16 * w;
   // a ring of D groups of 16 queries in flight; the landmark operands are
   // read from LDS for every group (not pinned in registers: occupancy)
   constexpr int D = 4, NG = 16;
   // unconditional loads of a clamped row (results past N are never used):
   // branch-free, so the compiler's wait counts stay exact
   auto load_group = [&](int G, typename TR::QReg& dst) {
-    const int64_t qq = qw + 16 * G + c16;
+    const int64_t qq = qw + 64 * G + c16;
     TR::load_q(dst, Qh + (qq < N ? qq : N - 1) * kD, true, g);
   };
   typename TR::QReg ring[D];
@@ -163,7 +165,7 @@ __device__ __forceinline__ void route_segment(const typename T::elem* __restrict
   // (a rolled ring loop makes the compiler wait for every group in flight)
 #pragma unroll
   for (int G = 0; G < NG; ++G) {
-    if (qw + 16 * G >= N) break;
+    if (qw + 64 * G >= N) break;
     {
       const int j = G % D;
       __asm__ volatile("" ::: "memory");  // re-read the landmark operands
@@ -187,7 +189,7 @@ __device__ __forceinline__ void route_segment(const typename T::elem* __restrict
       xor_argmax(best, bi, 16);
       xor_argmax(best, bi, 32);
       if (G + D < NG) load_group(G + D, ring[j]);
-      const int64_t q = qw + 16 * G + c16;
+      const int64_t q = qw + 64 * G + c16;
       if (g == 0 && q < N) {
         route_out[bh * N + q] = bi;
         atomicAdd(&cnt[bi], 1);

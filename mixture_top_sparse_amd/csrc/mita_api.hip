@@ -287,6 +287,7 @@ void derive(Shape& s, int cus) {
   // merge of the scan partials in two levels when there are many splits
   s.merge_parts = s.scan_splits > 32 ? 8 : 1;
   s.pool_splits = static_cast<int>(cdiv(max_window(s), kPoolChunk));
+  s.pool_direct = max_window(s) <= kPoolDirectMax;
   // top-k pre-threshold from group maxima (a group = gs consecutive keys;
   // the threshold is the k-th largest maximum).  Large N: a quarter of the
   // 64-key tiles (at most 1024 per head) when that gives at least 256

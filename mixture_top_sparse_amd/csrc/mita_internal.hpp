@@ -17,6 +17,7 @@ constexpr int kRouteSeg = 1024;  // queries per routing/bucketing segment
 constexpr int kAttendTile = 64;  // queries per expert-attention tile
 constexpr int kAttendMaxTpb = 16;  // tiles per expert-attention work item, at most
 constexpr int kPoolChunk = 4096; // tokens per pooling partial sum (fewer, longer blocks stream faster)
+constexpr int kPoolDirectMax = 128;  // windows up to this many tokens: one-launch pooling
 constexpr int kThetaTilesPerBlock = 1;  // sample tiles per top-k pre-threshold block
 constexpr int kThetaMaxGroups = 4096;  // group maxima the pre-threshold selection holds (64 per lane)
 
@@ -35,6 +36,7 @@ struct Shape {
   int scan_splits = 0;
   int merge_parts = 0; // first-level merge partitions per landmark (1: single pass)
   int pool_splits = 0; // partial sums per landmark window
+  bool pool_direct = false;  // small windows: one-launch pooling (k_pool_direct)
   int theta_groups = 0;// sample groups for the top-k pre-threshold (0: off)
   int theta_gs = 64;    // keys per pre-threshold group: 1, 16 or 64
   bool theta_sampled = false;  // groups are a sample of the 64-key tiles

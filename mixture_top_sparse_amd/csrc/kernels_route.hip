@@ -337,11 +337,20 @@ static hipError_t launch_route_t(const Shape& s, const void* Q, const Workspace&
   if (s.theta_groups > 64 * 64) return hipErrorInvalidValue;  // beyond the selection's registers
   const int nsel = s.theta_groups > 0 ? (s.m + 3) / 4 : 0;
   const dim3 grid(nsel + s.nseg, s.BH);
+  // maxima per lane in the selection: the fewest that hold every group
   if (nsel == 0)
     hipLaunchKernelGGL((k_route<T, 0>), grid, dim3(256), 0, st, Qp, Qlp, s.N, s.m, s.nseg,
                        route_out, ws.counts, 0, nullptr, s.k, 0, s.mrows, nullptr);
+  else if (s.theta_groups <= 64 * 4)
+    hipLaunchKernelGGL((k_route<T, 4>), grid, dim3(256), 0, st, Qp, Qlp, s.N, s.m, s.nseg,
+                       route_out, ws.counts, nsel, ws.gmax, s.k, s.theta_groups, s.mrows,
+                       ws.theta);
   else if (s.theta_groups <= 64 * 16)
     hipLaunchKernelGGL((k_route<T, 16>), grid, dim3(256), 0, st, Qp, Qlp, s.N, s.m, s.nseg,
+                       route_out, ws.counts, nsel, ws.gmax, s.k, s.theta_groups, s.mrows,
+                       ws.theta);
+  else if (s.theta_groups <= 64 * 32)
+    hipLaunchKernelGGL((k_route<T, 32>), grid, dim3(256), 0, st, Qp, Qlp, s.N, s.m, s.nseg,
                        route_out, ws.counts, nsel, ws.gmax, s.k, s.theta_groups, s.mrows,
                        ws.theta);
   else

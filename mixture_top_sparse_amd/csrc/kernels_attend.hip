@@ -61,13 +61,17 @@ struct TileInfo {
 
 // Work item t of a head covers up to `tpb` consecutive 64-query tiles of one
 // expert; item_start[e] is the first item of expert e (exclusive scan of
-// ceil(tiles_e / tpb)).
+// ceil(tiles_e / tpb)).  item_start is non-decreasing, so t's expert is the
+// number of experts e < m - 1 whose successor starts at or before t: one
+// load per lane (m <= 64) and a ballot, instead of a chain of m dependent
+// loads.
 __device__ __forceinline__ bool find_item(const int32_t* __restrict__ item_start,
                                           const int32_t* __restrict__ offsets, int m, int tpb,
                                           int t, TileInfo& ti) {
+  const int l = lane_id();
+  const int next = l < m - 1 ? item_start[l + 1] : INT32_MAX;
   if (t >= item_start[m]) return false;
-  int e = 0;
-  while (e < m - 1 && item_start[e + 1] <= t) ++e;
+  const int e = __popcll(ballot(next <= t));
   const int j0 = (t - item_start[e]) * tpb;
   ti.e = e;
   ti.qb = offsets[e] + kAttendTile * j0;

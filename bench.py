@@ -64,12 +64,15 @@ def log(msg: str) -> None:
 
 def threshold_tiles(w) -> int:
     """Key tiles of 64 the top-k pre-threshold reads per head (the library's
-    rule: with at least 256 samples, a quarter of the tiles, at most 1024;
-    below that every tile; none when there are fewer than k keys)."""
+    rule: a quarter of the tiles, at most 1024, when that gives at least 256
+    samples, else half of them when that does; below that every tile; none
+    when there are fewer than k keys)."""
     ktiles = -(-w.N // 64)
     if w.N < w.k:
         return 0
-    return min(ktiles // 4, 1024) if ktiles // 4 >= 256 else ktiles
+    if ktiles // 4 >= 256:
+        return min(ktiles // 4, 1024)
+    return ktiles // 2 if ktiles // 2 >= 256 else ktiles
 
 
 def stage_bytes(w) -> dict[str, float]:

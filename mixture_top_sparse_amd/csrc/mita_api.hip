@@ -289,17 +289,19 @@ void derive(Shape& s, int cus) {
   s.pool_splits = static_cast<int>(cdiv(max_window(s), kPoolChunk));
   s.pool_direct = max_window(s) <= kPoolDirectMax;
   // top-k pre-threshold from group maxima (a group = gs consecutive keys;
-  // the threshold is the k-th largest maximum).  Large N: a quarter of the
-  // 64-key tiles (at most 1024 per head) when that gives at least 256
-  // samples, a cheap pass whose threshold keeps candidates few.  Below that,
-  // every key: singly up to kThetaMaxGroups keys (exact k-th largest score),
-  // else in 16-key groups.  Off when there are fewer than k keys.
+  // the threshold is the k-th largest maximum).  Large N: a sample of the
+  // 64-key tiles, a quarter of them (at most 1024 per head) when that gives
+  // at least 256 samples, else half of them when that does (32K-64K keys: a
+  // pass over every key cost more than the extra candidates a half sample
+  // lets through).  Below that, every key: singly up to kThetaMaxGroups keys
+  // (exact k-th largest score), else in 16-key groups.  Off when there are
+  // fewer than k keys.
   s.theta_groups = 0;
   s.theta_gs = 64;
   s.theta_sampled = false;
   if (s.N >= s.k) {
-    if (ktiles / 4 >= 256) {
-      int64_t groups = ktiles / 4;
+    if (ktiles / 2 >= 256) {
+      int64_t groups = ktiles / 4 >= 256 ? ktiles / 4 : ktiles / 2;
       if (groups > 1024) groups = 1024;
       groups = groups / kThetaTilesPerBlock * kThetaTilesPerBlock;
       s.theta_sampled = true;

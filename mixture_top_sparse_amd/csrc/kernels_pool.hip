@@ -47,12 +47,17 @@ __device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
   }
 }
 
-// grid (pool_splits, m, BH), 256 threads: 32 token rows x 8 column groups
+// grid (pool_splits, m, BH), 256 threads: 32 token rows x 8 column groups.
+// With one split per window the block divides and rounds itself (ql, and
+// ql_copy when non-null) and no final launch follows; otherwise it stores
+// its fp64 partial sum.
 template <class T>
 __global__ __launch_bounds__(256) void k_pool_partial(const typename T::elem* __restrict__ Q,
                                                      int64_t N, int gh, int gw, int mh, int mw,
                                                      int splits, int64_t bh0,
-                                                     double* __restrict__ part) {
+                                                     double* __restrict__ part,
+                                                     typename T::elem* __restrict__ ql,
+                                                     typename T::elem* __restrict__ ql_copy) {
   __shared__ double red[32][kD + 1];
   const int split = blockIdx.x, i = blockIdx.y, m = mh * mw;
   const int64_t bh = bh0 + blockIdx.z;
@@ -101,7 +106,13 @@ __global__ __launch_bounds__(256) void k_pool_partial(const typename T::elem* __
   if (threadIdx.x < kD) {
     double s = 0.0;
     for (int r = 0; r < 32; ++r) s += red[r][threadIdx.x];
-    part[((bh * m + i) * splits + split) * kD + threadIdx.x] = s;
+    if (splits == 1) {
+      const typename T::elem v = T::from_f64(s / static_cast<double>(W));
+      ql[(bh * m + i) * kD + threadIdx.x] = v;
+      if (ql_copy) ql_copy[(bh * m + i) * kD + threadIdx.x] = v;
+    } else {
+      part[((bh * m + i) * splits + split) * kD + threadIdx.x] = s;
+    }
   }
 }
 
@@ -191,9 +202,9 @@ static hipError_t launch_pool_t(const Shape& s, const void* Q, const Workspace& 
   }
   hipLaunchKernelGGL(k_pool_partial<T>, dim3(s.pool_splits, s.m, nbh), dim3(256), 0, st,
                      static_cast<const E*>(Q), s.N, s.gh, s.gw, s.mh, s.mw, s.pool_splits, bh0,
-                     ws.pool_part);
+                     ws.pool_part, static_cast<E*>(ws.ql), static_cast<E*>(ql_copy));
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || s.pool_splits == 1) return e;  // one split: already final
   hipLaunchKernelGGL(k_pool_final<T>, dim3(s.m, nbh), dim3(64), 0, st, ws.pool_part, s.gh, s.gw,
                      s.mh, s.mw, s.pool_splits, bh0, static_cast<E*>(ws.ql),
                      static_cast<E*>(ql_copy));

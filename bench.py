@@ -32,9 +32,9 @@ KERNEL_SOURCES = {"k_scan": "kernels_scan.hip", "k_route": "kernels_route.hip",
 # kernel whose sources changed since reports traffic null.
 COUNTED_TRAFFIC = {
     "len_1m": {
-        "k_scan": {"sha": "c61bfa919473", "bytes": 1096340317},
-        "k_route": {"sha": "9ad4fc893769", "bytes": 568060325},
-        "k_attend": {"sha": "9afd0452b522", "bytes": 1637647689},
+        "k_scan": {"sha": "c78168433fe0", "bytes": 1096204909},
+        "k_route": {"sha": "b4c6debdfdee", "bytes": 566923872},
+        "k_attend": {"sha": "487bdd8c2df1", "bytes": 1637786029},
     },
 }
 

@@ -163,3 +163,47 @@ def test_deterministic():
     g2, _ = _run(w, Q, K, V)
     for key in g1:
         assert np.array_equal(g1[key], g2[key]), key
+
+
+def test_streams_and_workspace_growth():
+    """Calls on two streams at once, and a stream whose cached work space
+    must grow and then serves a smaller call again, give the bitwise results
+    of the same calls made one at a time on the default stream."""
+    import mixture_top_sparse_amd as mts
+
+    small = WORKLOADS["seg_32x32"].with_(B=2, H=2)
+    large = WORKLOADS["long1d_16k"].with_(B=1, H=2)
+    cases = []
+    for w in (small, large):
+        Qt, Kt, Vt = to_torch(generate(w), w.dtype, "cuda")
+        cases.append((w, Qt, Kt, Vt))
+
+    def fwd(c):
+        w, Qt, Kt, Vt = c
+        return mts.mita_forward(Qt, Kt, Vt, m=w.m, k=w.k, grid=w.grid, scale=w.scale)
+
+    def host(res):
+        torch.cuda.synchronize()
+        return [t.cpu().numpy() for t in res]
+
+    _say("case streams: references on the default stream")
+    ref = [host(fwd(c)) for c in cases]
+
+    _say("case streams: small and large on two streams at once")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s1):
+        r1 = fwd(cases[0])
+    with torch.cuda.stream(s2):
+        r2 = fwd(cases[1])
+    for got, want in ((host(r1), ref[0]), (host(r2), ref[1])):
+        for a, b in zip(got, want):
+            assert np.array_equal(a, b)
+
+    _say("case streams: small, large, small on a fresh stream (work space grows)")
+    s3 = torch.cuda.Stream()
+    with torch.cuda.stream(s3):
+        seq = [fwd(cases[0]), fwd(cases[1]), fwd(cases[0])]
+    for got, want in zip([host(r) for r in seq], [ref[0], ref[1], ref[0]]):
+        for a, b in zip(got, want):
+            assert np.array_equal(a, b)

@@ -323,7 +323,10 @@ void derive(Shape& s, int cus) {
   int64_t tpb = (tiles * s.BH) / (4 * static_cast<int64_t>(cus));
   tpb = tpb < 1 ? 1 : (tpb > kAttendMaxTpb ? kAttendMaxTpb : tpb);
   s.attend_tpb = static_cast<int>(tpb);
-  s.attend_items = static_cast<int>(cdiv(tiles + s.m, tpb) + s.m);
+  // items: sum over experts of ceil(t_e / tpb) with t_e = ceil(c_e / 64);
+  // the t_e add up to at most tiles + m - 1, and each ceil adds at most
+  // (tpb - 1) / tpb, so tiles / tpb + m bounds them
+  s.attend_items = static_cast<int>(cdiv(tiles, tpb) + s.m);
 
 }
 

@@ -81,16 +81,16 @@ struct RouteTraits<F32> {
 // and sums the counts with one ballot per count bit, so the search stays
 // uniform across the wave.  KPL: maxima per lane (groups <= 64 * KPL).
 template <int KPL>
-__device__ __forceinline__ void theta_select_wave(const uint64_t* __restrict__ gmax, int m, int k,
+__device__ __forceinline__ void theta_select_wave(const uint32_t* __restrict__ gmax, int m, int k,
                                                   int groups, int mrows, int lm, int64_t bh,
                                                   float* __restrict__ theta) {
   const int l = lane_id();
-  const uint64_t* G = gmax + (bh * m + lm) * groups;
+  const uint32_t* G = gmax + (bh * m + lm) * groups;
   uint32_t v[KPL];  // 0: no maximum (below every real key's order bits)
 #pragma unroll
   for (int j = 0; j < KPL; ++j) {
     const int i = 64 * j + l;
-    v[j] = i < groups ? static_cast<uint32_t>(G[i] >> 32) : 0u;
+    v[j] = i < groups ? G[i] : 0u;
   }
   // invariant: at least k values >= lo (lo = 0 holds: 64 * KPL >= groups >= k)
   uint32_t lo = 0u, hi = 0xFFFFFFFFu;
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(256) void k_route(const typename T::elem* __restric
                                               const typename T::elem* __restrict__ Ql, int64_t N,
                                               int m, int nseg, int32_t* __restrict__ route_out,
                                               int32_t* __restrict__ counts, int nsel,
-                                              const uint64_t* __restrict__ gmax, int k,
+                                              const uint32_t* __restrict__ gmax, int k,
                                               int groups, int mrows,
                                               float* __restrict__ theta) {
   using E = typename T::elem;
@@ -247,7 +247,7 @@ template <int GS, bool SAMPLED>
 __device__ __forceinline__ void theta_tile_wave(const uint16_t* __restrict__ K,
                                                 const uint16_t* qls, int64_t N, int m,
                                                 int groups, int ti, int64_t bh,
-                                                uint64_t* __restrict__ gmax) {
+                                                uint32_t* __restrict__ gmax) {
   static_assert(GS == 1 || GS == 16 || GS == 64, "groups of 1, 16 or 64 keys");
   static_assert(!SAMPLED || GS == 64, "samples are whole tiles");
   const int l = lane_id(), g = l >> 4, c16 = l & 15;
@@ -277,7 +277,7 @@ __device__ __forceinline__ void theta_tile_wave(const uint16_t* __restrict__ K,
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) sc[kb] = mfma_bf16(as_bf16x8(ko[kb][1]), as_bf16x8(q1), sc[kb]);
     const int lm = 16 * lb + c16;
-    uint64_t* G = gmax + (bh * m + (lm < m ? lm : 0)) * groups;
+    uint32_t* G = gmax + (bh * m + (lm < m ? lm : 0)) * groups;
     uint64_t best = 0;  // running group maximum (GS = 16, 64)
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -286,7 +286,7 @@ __device__ __forceinline__ void theta_tile_wave(const uint16_t* __restrict__ K,
         const int64_t t = t0 + 16 * kb + 4 * g + r;
         const uint64_t key = t < N ? make_key(sc[kb][r], static_cast<uint32_t>(t)) : 0ull;
         if constexpr (GS == 1) {
-          if (lm < m && t < N) G[t] = key;
+          if (lm < m && t < N) G[t] = static_cast<uint32_t>(key >> 32);
         } else {
           best = key > best ? key : best;
         }
@@ -299,7 +299,7 @@ __device__ __forceinline__ void theta_tile_wave(const uint16_t* __restrict__ K,
             best = o > best ? o : best;
           }
           const int64_t gi = GS == 16 ? (t0 >> 4) + kb : static_cast<int64_t>(ti);
-          if (g == 0 && lm < m && gi < groups) G[gi] = best;
+          if (g == 0 && lm < m && gi < groups) G[gi] = static_cast<uint32_t>(best >> 32);
           best = 0;
         }
       }
@@ -317,7 +317,7 @@ template <int GS, bool SAMPLED>
 __global__ __launch_bounds__(256) void k_theta_groups(const uint16_t* __restrict__ K,
                                                      const uint16_t* __restrict__ Ql, int64_t N,
                                                      int m, int groups,
-                                                     uint64_t* __restrict__ gmax) {
+                                                     uint32_t* __restrict__ gmax) {
   __shared__ __attribute__((aligned(16))) uint16_t qls[kMaxM * kQlStride];
   const int64_t bh = blockIdx.y;
   const int ti = static_cast<int>(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(wave_id());

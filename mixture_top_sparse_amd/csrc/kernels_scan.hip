@@ -653,7 +653,7 @@ template <class T>
 __global__ __launch_bounds__(256) void k_theta_sample(const typename T::elem* __restrict__ K,
                                                      const typename T::elem* __restrict__ Ql,
                                                      int64_t N, int m, int groups,
-                                                     uint64_t* __restrict__ gmax) {
+                                                     uint32_t* __restrict__ gmax) {
   using TR = ScanTraits<T>;
   using E = typename T::elem;
   const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
@@ -690,7 +690,7 @@ __global__ __launch_bounds__(256) void k_theta_sample(const typename T::elem* __
       const uint64_t o = lane_read(best, l ^ mask);
       best = o > best ? o : best;
     }
-    if (g == 0 && lm_ok) gmax[(bh * m + lm) * groups + gi] = best;
+    if (g == 0 && lm_ok) gmax[(bh * m + lm) * groups + gi] = static_cast<uint32_t>(best >> 32);
   }
 }
 
@@ -704,7 +704,7 @@ template <class T, int GS>
 __global__ __launch_bounds__(256) void k_theta_fine(const typename T::elem* __restrict__ K,
                                                    const typename T::elem* __restrict__ Ql,
                                                    int64_t N, int m, int groups,
-                                                   uint64_t* __restrict__ gmax) {
+                                                   uint32_t* __restrict__ gmax) {
   static_assert(GS == 1 || GS == 16 || GS == 64, "groups of 1, 16 or 64 keys");
   using TR = ScanTraits<T>;
   const int l = lane_id(), g = l >> 4, c16 = l & 15;
@@ -718,7 +718,7 @@ __global__ __launch_bounds__(256) void k_theta_fine(const typename T::elem* __re
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTileKeys;
   f32x4 sc[4];
   TR::score_tile_global(K + bh * N * kD, t0, N, q, c16, g, sc);
-  uint64_t* G = gmax + (bh * m + (lm_ok ? lm : 0)) * groups;
+  uint32_t* G = gmax + (bh * m + (lm_ok ? lm : 0)) * groups;
   uint64_t tbest = 0;  // running group maximum (GS = 16, 64)
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
@@ -732,7 +732,7 @@ __global__ __launch_bounds__(256) void k_theta_fine(const typename T::elem* __re
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t t = t0 + 16 * kb + 4 * g + r;
-        if (lm_ok && t < N) G[t] = key[r];
+        if (lm_ok && t < N) G[t] = static_cast<uint32_t>(key[r] >> 32);
       }
     } else {
 #pragma unroll
@@ -744,7 +744,7 @@ __global__ __launch_bounds__(256) void k_theta_fine(const typename T::elem* __re
           tbest = o > tbest ? o : tbest;
         }
         const int64_t gi = GS == 16 ? (t0 >> 4) + kb : static_cast<int64_t>(blockIdx.x);
-        if (g == 0 && lm_ok && gi < groups) G[gi] = tbest;
+        if (g == 0 && lm_ok && gi < groups) G[gi] = static_cast<uint32_t>(tbest >> 32);
         tbest = 0;
       }
     }

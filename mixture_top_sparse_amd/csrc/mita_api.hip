@@ -343,7 +343,7 @@ size_t plan_workspace(const Shape& s, Workspace* ws, char* base) {
   ws->pool_part = reinterpret_cast<double*>(take(BH * s.m * s.pool_splits * kD * sizeof(double)));
   ws->ql = take(BH * s.m * kD * es);
   if (s.theta_groups > 0) {
-    ws->gmax = reinterpret_cast<uint64_t*>(take(BH * s.m * s.theta_groups * sizeof(uint64_t)));
+    ws->gmax = reinterpret_cast<uint32_t*>(take(BH * s.m * s.theta_groups * sizeof(uint32_t)));
     ws->theta = reinterpret_cast<float*>(take(BH * s.mrows * sizeof(float)));
   } else {
     ws->gmax = nullptr;

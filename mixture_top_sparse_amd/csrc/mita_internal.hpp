@@ -49,7 +49,7 @@ struct Shape {
 struct Workspace {
   double* pool_part = nullptr;   // [BH][m][pool_splits][64] fp64 partial window sums
   void* ql = nullptr;            // [BH][m][64] landmark queries (input type)
-  uint64_t* gmax = nullptr;      // [BH][m][theta_groups] per-group maximum keys
+  uint32_t* gmax = nullptr;      // [BH][m][theta_groups] order bits of each group's maximum score
   float* theta = nullptr;        // [BH][mrows] top-k pre-threshold (nullptr: off)
   uint64_t* part_keys = nullptr; // [BH][splits][mrows][64] per-split top lists (first
                                  //   part_cnt entries valid, descending)

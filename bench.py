@@ -32,9 +32,9 @@ KERNEL_SOURCES = {"k_scan": "kernels_scan.hip", "k_route": "kernels_route.hip",
 # kernel whose sources changed since reports traffic null.
 COUNTED_TRAFFIC = {
     "len_1m": {
-        "k_scan": {"sha": "c78168433fe0", "bytes": 1096204909},
-        "k_route": {"sha": "b4c6debdfdee", "bytes": 566923872},
-        "k_attend": {"sha": "487bdd8c2df1", "bytes": 1637786029},
+        "k_scan": {"sha": "a346aed743a7", "bytes": 1096263841},
+        "k_route": {"sha": "8bee36898bbb", "bytes": 565775337},
+        "k_attend": {"sha": "02b6d3f8d2b7", "bytes": 1637795103},
     },
 }
 

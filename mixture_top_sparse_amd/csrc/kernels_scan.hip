@@ -755,9 +755,10 @@ __global__ __launch_bounds__(256) void k_theta_fine(const typename T::elem* __re
 // merge of the per-split partials
 // ---------------------------------------------------------------------------
 
-// grid (m, BH, P), 256 threads.  Block (lm, bh, p) combines the splits
-// s = p, p + P, p + 2P, ...; wave w takes the w-th, (w+4)-th, ... of them in
-// batches of 8 (loads first, then the arithmetic).  A split's top list only
+// 256 threads per block; a merge block handles landmark (block) lm of head
+// bh for part p of P and combines the splits s = p, p + P, p + 2P, ...; wave
+// w takes the w-th, (w+4)-th, ... of them in batches of 8 (loads first, then
+// the arithmetic; only a split's stored entries are loaded).  A split's top list only
 // enters the merge network when its best key beats the wave's current k-th
 // best.  FINAL (P = 1): writes idx_out (ascending) and Vl.  Otherwise the
 // block's combined top list and softmax state go to the out_* arrays in the
@@ -822,13 +823,11 @@ __global__ __launch_bounds__(256) void k_merge(
     }
     uint64_t lst[kBatch];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {  // issued with the loads above; masked once cnt is in
+    for (int u = 0; u < kBatch; ++u) {  // only the split's cnt stored entries
       const int i = i0 + NWM * u;
       const int64_t r = row0 + static_cast<int64_t>(i < nmine ? p + P * i : p) * mrows;
-      lst[u] = part_keys[r * kTopCap + l];
+      lst[u] = l < cnt[u] ? part_keys[r * kTopCap + l] : 0ull;
     }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) lst[u] = (l < cnt[u]) ? lst[u] : 0ull;
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       if (i0 + NWM * u >= nmine) break;

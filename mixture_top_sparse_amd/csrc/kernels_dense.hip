@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 
   const uint32_t soff0 = stage_src_off(w, 0, l), soff1 = stage_src_off(w, 1, l);
   const uint32_t a0 = lds_address(b0), a1 = lds_address(b1);
-  stage_tile_bf16(Kh, Vh, 0, N, a0, a0 + 8192, w, soff0, soff1);
+  stage_tile_bf16<false>(Kh, Vh, 0, N, a0, a0 + 8192, w, soff0, soff1);
 
   float M = -INFINITY, Lsum = 0.f;
   f32x4 acc[4];
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
     const int64_t t0 = static_cast<int64_t>(it) * kTileKeys;
-    if (it + 1 < ntiles) stage_tile_bf16(Kh, Vh, t0 + kTileKeys, N, nxt, nxt + 8192, w, soff0, soff1);
+    if (it + 1 < ntiles) stage_tile_bf16<false>(Kh, Vh, t0 + kTileKeys, N, nxt, nxt + 8192, w, soff0, soff1);
     compute_tile(cur, cur + 8192, t0);
   };
   for (int it = 0; it < ntiles; it += 2) {

@@ -13,6 +13,7 @@ constexpr int kMaxK = 64;        // keys per expert
 constexpr int kTopCap = 64;      // per-split top list length (one key per lane)
 constexpr int kCandCap = 8;      // candidate buffer per landmark (bf16 landmark scan)
 constexpr int kTileKeys = 64;    // keys per landmark-scan tile
+constexpr int64_t kLastLevelCacheBytes = int64_t{256} << 20;  // MI355X Infinity Cache
 constexpr int kRouteSeg = 1024;  // queries per routing/bucketing segment
 constexpr int kAttendTile = 64;  // queries per expert-attention tile
 constexpr int kAttendMaxTpb = 16;  // tiles per expert-attention work item, at most

@@ -60,11 +60,21 @@ __device__ __forceinline__ void lds_store_u64(uint32_t addr, uint64_t v) {
 // LDS address lds_base + 16 * lane (lds_base wave-uniform, in M0).  Written
 // as assembly so that the compiler inserts no waits of its own for it: the
 // scan orders every tile with explicit vmcnt waits and block barriers.
+// NT: the non-temporal cache policy, for data read exactly once (the
+// landmark scan's pass over K and V): the stream then does not displace
+// what the last-level cache holds for later kernels.
+template <bool NT>
 __device__ __forceinline__ void dma16_to_lds(const void* gaddr, uint32_t lds_base) {
-  __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                   :
-                   : "v"(gaddr), "s"(lds_base)
-                   : "memory", "m0");
+  if constexpr (NT)
+    __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+                     :
+                     : "v"(gaddr), "s"(lds_base)
+                     : "memory", "m0");
+  else
+    __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                     :
+                     : "v"(gaddr), "s"(lds_base)
+                     : "memory", "m0");
 }
 
 // Wave `w` (wave-uniform) requests its two 1 KiB pieces (rows 16w..16w+15)
@@ -72,6 +82,7 @@ __device__ __forceinline__ void dma16_to_lds(const void* gaddr, uint32_t lds_bas
 // Full tiles use the tile base plus the lane's 32-bit offset; a tile that
 // runs past the head's last key re-reads key N-1 for the missing rows (their
 // scores are masked and their probabilities are 0).
+template <bool NT>
 __device__ __forceinline__ void stage_tile_bf16(const uint16_t* __restrict__ Kh,
                                                 const uint16_t* __restrict__ Vh, int64_t t0,
                                                 int64_t N, uint32_t kbuf, uint32_t vbuf, int w,
@@ -86,10 +97,10 @@ __device__ __forceinline__ void stage_tile_bf16(const uint16_t* __restrict__ Kh,
     if ((o1 & ~127u) > last) o1 = last + (o1 & 127u);
   }
   const uint32_t p0 = 2048u * static_cast<uint32_t>(w), p1 = p0 + 1024u;
-  dma16_to_lds(kt + o0, kbuf + p0);
-  dma16_to_lds(vt + o0, vbuf + p0);
-  dma16_to_lds(kt + o1, kbuf + p1);
-  dma16_to_lds(vt + o1, vbuf + p1);
+  dma16_to_lds<NT>(kt + o0, kbuf + p0);
+  dma16_to_lds<NT>(vt + o0, vbuf + p0);
+  dma16_to_lds<NT>(kt + o1, kbuf + p1);
+  dma16_to_lds<NT>(vt + o1, vbuf + p1);
 }
 
 }  // namespace mita

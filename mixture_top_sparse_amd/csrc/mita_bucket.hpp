@@ -68,7 +68,7 @@ __device__ __forceinline__ void bucket_prefix(const int32_t* __restrict__ counts
 struct ScatterLds {
   int lbase[kMaxM];   // next local slot of each expert
   int gshift[kMaxM];  // global position minus local slot, per expert
-  int32_t sq[kRouteSeg];
+  uint16_t sq[kRouteSeg];  // query index within the segment
   uint8_t se[kRouteSeg];
 };
 
@@ -144,7 +144,7 @@ __device__ __forceinline__ void scatter_segment(
     const int total = __popcll(same);
     const int pos = ok ? L.lbase[r] + rank : -1;
     if (pos >= 0 && pos < kRouteSeg) {
-      L.sq[pos] = static_cast<int32_t>(q0 + 64 * it + l);
+      L.sq[pos] = static_cast<uint16_t>(64 * it + l);
       L.se[pos] = static_cast<uint8_t>(r);
     }
     if (ok && rank == total - 1) L.lbase[r] += total;  // after every lane's read of lbase[r]
@@ -155,8 +155,9 @@ __device__ __forceinline__ void scatter_segment(
     const int e = L.se[i];
     const int pos = e < m ? L.gshift[e] + i : -1;
     if (pos >= 0 && pos < N) {
-      perm[bh * N + pos] = L.sq[i];
-      if (perm_copy) perm_copy[bh * N + pos] = L.sq[i];
+      const int32_t q = static_cast<int32_t>(q0 + L.sq[i]);
+      perm[bh * N + pos] = q;
+      if (perm_copy) perm_copy[bh * N + pos] = q;
     }
   }
 }

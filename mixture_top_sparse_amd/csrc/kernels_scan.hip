@@ -9,7 +9,8 @@
 // FlashAttention-style pass (same page, implementation remark).  Here one
 // kernel streams K and V once:
 //
-//   k_scan_bf16 / k_scan_f32  (split, head) blocks; wave w owns landmarks
+//   k_scan_bf16 / k_scan_f32  1D grid of (split, head) blocks, then the
+//     blocks of step 4's prefix (mita_bucket.hpp); wave w owns landmarks
 //     16w..16w+15.  Per 64-key tile: S^T = K_tile Ql^T on MFMA (key rows x
 //     landmark columns), online softmax of scale*S with P.V on MFMA (bf16: P
 //     split into bf16 hi + lo parts), and an exact streaming top-k: scores
@@ -19,8 +20,11 @@
 //     = i-th best).  The bf16 kernel stages K and V tiles straight into LDS
 //     with the global-load-to-LDS DMA (no register staging, no transposing
 //     stores) and reads V^T operands with the LDS transpose read.
-//   k_merge (landmark, head) blocks: merges the per-split top lists and the
-//     per-split softmax states (log-sum-exp) into idx_out and Vl.
+//   k_merge (landmark, head) blocks, in one or two passes: merges the
+//     per-split top lists and the per-split softmax states (log-sum-exp)
+//     into idx_out and Vl; its first pass also carries step 4's scatter.
+//   k_theta_fine / k_theta_sample: the top-k pre-threshold's group maxima
+//     for fp32 inputs (the bf16 ones are in kernels_route.hip).
 //
 // Selection keys are 64-bit (order-preserving score bits, inverted index),
 // so "higher score, then lower index" is a plain unsigned comparison.

@@ -242,20 +242,22 @@ __global__ __launch_bounds__(256) void k_route(const typename T::elem* __restric
 // every key its own group; 16: 16-key blocks; 64: the tile).  Rows past N
 // read row N - 1: every load is unconditional; those scores are dropped.
 // The scores use the scan's operand layout and accumulation order, so they
-// are bitwise the scores the scan computes.
-template <int GS, bool SAMPLED>
-__device__ __forceinline__ void theta_tile_wave(const uint16_t* __restrict__ K,
-                                                const uint16_t* qls, int64_t N, int m,
-                                                int groups, int ti, int64_t bh,
-                                                uint32_t* __restrict__ gmax) {
-  static_assert(GS == 1 || GS == 16 || GS == 64, "groups of 1, 16 or 64 keys");
-  static_assert(!SAMPLED || GS == 64, "samples are whole tiles");
-  const int l = lane_id(), g = l >> 4, c16 = l & 15;
+// are bitwise the scores the scan computes.  The tile's key operands (ko)
+// come from theta_tile_load, issued by the caller before it waits for the
+// landmark staging.
+template <bool SAMPLED>
+__device__ __forceinline__ int64_t theta_tile_start(int64_t N, int groups, int ti) {
   const int64_t ntiles = (N + kTileKeys - 1) / kTileKeys;
-  const int64_t t0 = SAMPLED ? ((static_cast<int64_t>(ti) * ntiles) / groups) * kTileKeys
-                             : static_cast<int64_t>(ti) * kTileKeys;
+  return SAMPLED ? ((static_cast<int64_t>(ti) * ntiles) / groups) * kTileKeys
+                 : static_cast<int64_t>(ti) * kTileKeys;
+}
+
+template <bool SAMPLED>
+__device__ __forceinline__ void theta_tile_load(const uint16_t* __restrict__ K, int64_t N,
+                                                int groups, int ti, int64_t bh, u32x4 (&ko)[4][2]) {
+  const int l = lane_id(), g = l >> 4, c16 = l & 15;
+  const int64_t t0 = theta_tile_start<SAMPLED>(N, groups, ti);
   const uint16_t* Kh = K + bh * N * kD;
-  u32x4 ko[4][2];
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     const int64_t row = t0 + 16 * kb + c16;
@@ -264,6 +266,16 @@ __device__ __forceinline__ void theta_tile_wave(const uint16_t* __restrict__ K,
     for (int s = 0; s < 2; ++s)
       ko[kb][s] = *reinterpret_cast<const u32x4*>(Kh + rr * kD + 32 * s + 8 * g);
   }
+}
+
+template <int GS, bool SAMPLED>
+__device__ __forceinline__ void theta_tile_wave(const u32x4 (&ko)[4][2], const uint16_t* qls,
+                                                int64_t N, int m, int groups, int ti, int64_t bh,
+                                                uint32_t* __restrict__ gmax) {
+  static_assert(GS == 1 || GS == 16 || GS == 64, "groups of 1, 16 or 64 keys");
+  static_assert(!SAMPLED || GS == 64, "samples are whole tiles");
+  const int l = lane_id(), g = l >> 4, c16 = l & 15;
+  const int64_t t0 = theta_tile_start<SAMPLED>(N, groups, ti);
 #pragma unroll
   for (int lb = 0; lb < 4; ++lb) {
     if (16 * lb >= m) break;  // uniform
@@ -312,7 +324,9 @@ __device__ __forceinline__ void theta_tile_wave(const uint16_t* __restrict__ K,
 // landmark queries.  Its own launch before routing: inside the routing
 // launch, the selection would have to wait across blocks for every tile of
 // the head, and the device-scope fences and polls that takes cost routing
-// more than this launch does.
+// more than this launch does.  The key tile is requested before the
+// landmark staging, so the two memory latencies overlap.  Rows are clamped,
+// so a wave past the last tile loads in bounds and stores nothing.
 template <int GS, bool SAMPLED>
 __global__ __launch_bounds__(256) void k_theta_groups(const uint16_t* __restrict__ K,
                                                      const uint16_t* __restrict__ Ql, int64_t N,
@@ -322,10 +336,12 @@ __global__ __launch_bounds__(256) void k_theta_groups(const uint16_t* __restrict
   const int64_t bh = blockIdx.y;
   const int ti = static_cast<int>(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(wave_id());
   const int64_t ntiles = (N + kTileKeys - 1) / kTileKeys;
+  u32x4 ko[4][2];
+  theta_tile_load<SAMPLED>(K, N, groups, ti, bh, ko);
   stage_landmarks(Ql, m, bh, qls);
   __syncthreads();
   if (ti < (SAMPLED ? groups : ntiles))
-    theta_tile_wave<GS, SAMPLED>(K, qls, N, m, groups, ti, bh, gmax);
+    theta_tile_wave<GS, SAMPLED>(ko, qls, N, m, groups, ti, bh, gmax);
 }
 
 template <class T>

@@ -40,9 +40,14 @@
  * device), allocated stream-ordered on `stream` (hipMallocAsync) by the
  * first call that needs it and kept for later calls on that stream, which
  * are ordered after it by the stream itself.  A block that is too small for
- * a call is released with hipFreeAsync on its stream and replaced; a new
- * stream beyond the eighth takes over the least recently used block.  At
- * 2^20 tokens x 4 heads the block is about 54 MB.  Every kernel of a call
+ * a call is released with hipFreeAsync on its stream and replaced.  A new
+ * stream beyond the eighth takes over the least recently used block: that
+ * call first waits for the whole device (hipDeviceSynchronize), so the old
+ * block is idle even if its stream has been destroyed, and frees it on the
+ * new stream.  mita_release_workspace(stream) frees a stream's block early;
+ * call it before destroying a stream that made calls, or after the last
+ * call, to return the memory.  At 2^20 tokens x 4 heads the block is about
+ * 54 MB.  Every kernel of a call
  * runs on `stream`; there is no host synchronisation and no global state
  * besides the cached work-space blocks, the per-device attribute cache and
  * the optional stage profiler.  A per-device mutex serialises the enqueue
@@ -155,6 +160,18 @@ int mita_forward_ex(const void* Q, const void* K, const void* V, int dtype, int6
  */
 int mita_dense_attention(const void* Q, const void* K, const void* V, int dtype, int64_t B,
                          int64_t H, int64_t N, int64_t d, float scale, float* out, void* stream);
+
+/*
+ * mita_release_workspace — free the work-space block cached for `stream` (a
+ * hipStream_t; NULL = the default stream) on the current device.  For
+ * callers that destroy streams or want the memory back; no step of the
+ * method.  The block is freed in stream order (hipFreeAsync on `stream`),
+ * after the calls already enqueued there, so `stream` must still exist.  A
+ * stream with no cached block is not an error.  The next mita_forward call
+ * on `stream` allocates a new block.  Returns MITA_OK, or MITA_ERR_HIP when
+ * no device is current or the free fails.
+ */
+int mita_release_workspace(void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* mita_status_string(int status);

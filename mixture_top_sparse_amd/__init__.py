@@ -16,6 +16,7 @@ __all__ = [
     "mita_forward",
     "mita_forward_ex",
     "mita_dense_attention",
+    "mita_release_workspace",
     "mita_status_string",
     "mita_last_error",
     "mita_version",
@@ -87,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.mita_profile_stage_name.restype = ctypes.c_char_p
         L.mita_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(ctypes.c_int64), ctypes.c_int]
+        L.mita_release_workspace.argtypes = [ctypes.c_void_p]
+        L.mita_release_workspace.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -198,6 +201,17 @@ def mita_dense_attention(Q, K, V, *, scale=None):
                                           float(scale), out.data_ptr(), stream),
                "mita_dense_attention")
     return out
+
+
+def mita_release_workspace(stream=None, device=None) -> None:
+    """Free the library's cached work space of a torch stream (default: the
+    current stream of `device`), in that stream's order."""
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    with torch.cuda.device(stream.device):
+        _raise(lib().mita_release_workspace(stream.cuda_stream), "mita_release_workspace")
 
 
 def mita_profile_enable(enabled: bool) -> None:

@@ -170,8 +170,18 @@ hipError_t workspace_for(DeviceState& ds, hipStream_t st, size_t bytes, void** o
         if (w.used < e->used) e = &w;
     }
   }
-  if (e->p != nullptr && (e->st != st || e->bytes < bytes)) {
-    const hipError_t ef = hipFreeAsync(e->p, e->st);
+  if (e->p != nullptr && e->st != st) {
+    // another stream's block: that stream may since have been destroyed, so
+    // its handle is not used.  Once the device is idle no call is using the
+    // block, and it can be freed in the order of the calling stream.
+    hipError_t ef = hipDeviceSynchronize();
+    if (ef == hipSuccess) ef = hipFreeAsync(e->p, st);
+    e->p = nullptr;
+    e->bytes = 0;
+    if (ef != hipSuccess) return ef;
+  } else if (e->p != nullptr && e->bytes < bytes) {
+    // too small: freed after this stream's earlier calls, replaced below
+    const hipError_t ef = hipFreeAsync(e->p, st);
     e->p = nullptr;
     e->bytes = 0;
     if (ef != hipSuccess) return ef;
@@ -514,6 +524,25 @@ int mita_dense_attention(const void* Q, const void* K, const void* V, int dtype,
   } catch (...) {
     return fail(MITA_ERR_INTERNAL, "unexpected exception inside mita_dense_attention");
   }
+}
+
+int mita_release_workspace(void* stream) {
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  DeviceState* ds = device_state();
+  if (ds == nullptr) return fail(MITA_ERR_HIP, "no current HIP device");
+  std::lock_guard<std::mutex> lk(ds->mu);
+  for (auto& w : ds->ws) {
+    if (w.p == nullptr || w.st != st) continue;
+    const hipError_t e = hipFreeAsync(w.p, st);
+    w.p = nullptr;
+    w.bytes = 0;
+    w.st = nullptr;
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(MITA_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(e));
+    }
+  }
+  return MITA_OK;
 }
 
 int mita_profile_enable(int enabled) {

@@ -207,3 +207,49 @@ def test_streams_and_workspace_growth():
     for got, want in zip([host(r) for r in seq], [ref[0], ref[1], ref[0]]):
         for a, b in zip(got, want):
             assert np.array_equal(a, b)
+
+
+def test_workspace_eviction_and_release():
+    """Ten streams (two more than the library caches blocks for, so later
+    calls take over least recently used blocks), then early release of some
+    streams' blocks and calls on them again: every result is bitwise the
+    result of the same call on the default stream."""
+    import mixture_top_sparse_amd as mts
+
+    w = WORKLOADS["seg_32x32"].with_(B=2, H=2)
+    Qt, Kt, Vt = to_torch(generate(w), w.dtype, "cuda")
+
+    def fwd():
+        return mts.mita_forward(Qt, Kt, Vt, m=w.m, k=w.k, grid=w.grid, scale=w.scale)
+
+    def host(res):
+        torch.cuda.synchronize()
+        return [t.cpu().numpy() for t in res]
+
+    _say("case eviction: reference on the default stream")
+    ref = host(fwd())
+    streams = [torch.cuda.Stream() for _ in range(10)]
+    assert len({s.cuda_stream for s in streams}) == 10
+    for rnd in range(2):
+        _say(f"case eviction: round {rnd}, one call on each of 10 streams")
+        got = []
+        for s in streams:
+            with torch.cuda.stream(s):
+                got.append(fwd())
+        for r in got:
+            for a, b in zip(host(r), ref):
+                assert np.array_equal(a, b)
+    _say("case eviction: release three streams' blocks, call again")
+    for s in streams[:3]:
+        mts.mita_release_workspace(s)
+        mts.mita_release_workspace(s)  # nothing cached any more: not an error
+    got = []
+    for s in streams[:4]:
+        with torch.cuda.stream(s):
+            got.append(fwd())
+    for r in got:
+        for a, b in zip(host(r), ref):
+            assert np.array_equal(a, b)
+    for s in streams:
+        mts.mita_release_workspace(s)
+    torch.cuda.synchronize()

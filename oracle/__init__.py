@@ -21,6 +21,9 @@ from .oracle import (  # noqa: F401
     route,
     bucket,
     output,
+    route_s,
+    bucket_s,
+    output_s,
     forward,
     dense,
 )

@@ -355,6 +355,139 @@ int mita_oracle_output(const double* Q, const double* K, const double* V, const 
 }
 
 /* ------------------------------------------------------------------------ */
+/* Steps 3-5 with s experts per query (reading in mita_oracle.h)             */
+/* ------------------------------------------------------------------------ */
+
+int mita_oracle_route_s(const double* Q, const double* Ql, int64_t N, int64_t d, int64_t m,
+                        int64_t s, const int64_t* qsel, int64_t nq, int32_t* routes) {
+  if (!Q || !Ql || !routes || N < 1 || d < 1 || m < 1 || s < 1 || s > m) return -1;
+  if (!qsel && nq != N) return -1;
+  if (nq < 0) return -1;
+  int bad = 0;
+#pragma omp parallel
+  {
+    double* R = (double*)malloc((size_t)m * sizeof(double));
+    char* taken = (char*)malloc((size_t)m);
+    if (!R || !taken) {
+#pragma omp atomic write
+      bad = 2;
+    }
+#pragma omp for schedule(static)
+    for (int64_t p = 0; p < nq; ++p) {
+      if (!R || !taken) continue;
+      const int64_t q = qsel ? qsel[p] : p;
+      if (q < 0 || q >= N) {
+#pragma omp atomic write
+        bad = 1;
+        continue;
+      }
+      for (int64_t i = 0; i < m; ++i) {
+        R[i] = dot(Q + q * d, Ql + i * d, d);
+        taken[i] = 0;
+      }
+      /* s rounds of the single-expert rule over the landmarks left */
+      for (int64_t j = 0; j < s; ++j) {
+        int64_t best = -1;
+        for (int64_t i = 0; i < m; ++i) {
+          if (taken[i]) continue;
+          if (best < 0 || R[i] > R[best]) best = i; /* strict: first maximum */
+        }
+        taken[best] = 1;
+        routes[p * s + j] = (int32_t)best;
+      }
+    }
+    free(R);
+    free(taken);
+  }
+  return bad == 2 ? -2 : (bad ? -1 : 0);
+}
+
+int mita_oracle_bucket_s(const int32_t* routes, int64_t N, int64_t m, int64_t s,
+                         int32_t* offsets, int32_t* perm) {
+  if (!routes || !offsets || !perm || N < 1 || m < 1 || s < 1 || s > m) return -1;
+  for (int64_t e = 0; e <= m; ++e) offsets[e] = 0;
+  for (int64_t q = 0; q < N; ++q)
+    for (int64_t j = 0; j < s; ++j) {
+      const int32_t e = routes[q * s + j];
+      if (e < 0 || e >= m) return -1;
+      for (int64_t i = 0; i < j; ++i)
+        if (routes[q * s + i] == e) return -1; /* experts of a query are distinct */
+      offsets[e + 1] += 1;
+    }
+  for (int64_t e = 0; e < m; ++e) offsets[e + 1] += offsets[e];
+  int32_t* fill = (int32_t*)malloc((size_t)m * sizeof(int32_t));
+  if (!fill) return -2;
+  for (int64_t e = 0; e < m; ++e) fill[e] = offsets[e];
+  /* queries in increasing index: each expert's group stays in index order */
+  for (int64_t q = 0; q < N; ++q)
+    for (int64_t j = 0; j < s; ++j) perm[fill[routes[q * s + j]]++] = (int32_t)q;
+  free(fill);
+  return 0;
+}
+
+int mita_oracle_output_s(const double* Q, const double* K, const double* V, const double* Ql,
+                         const double* Vl, const int32_t* idx, const int32_t* routes, int64_t N,
+                         int64_t d, int64_t m, int64_t k, int64_t s, double scale,
+                         const int64_t* qsel, int64_t nq, double* out) {
+  if (!Q || !K || !V || !Ql || !Vl || !idx || !routes || !out) return -1;
+  if (N < 1 || d < 1 || m < 1 || k < 1 || k > N || s < 1 || s > m) return -1;
+  if (!(scale > 0.0) || isinf(scale)) return -1;
+  if (!qsel && nq != N) return -1;
+  if (nq < 0) return -1;
+  int bad = 0;
+#pragma omp parallel
+  {
+    const int64_t np = m + s * k; /* pairs one query attends over */
+    double* w = (double*)malloc((size_t)np * sizeof(double));
+    int32_t* key = (int32_t*)malloc((size_t)(s * k) * sizeof(int32_t));
+    if (!w || !key) {
+#pragma omp atomic write
+      bad = 2;
+    }
+#pragma omp for schedule(static)
+    for (int64_t p = 0; p < nq; ++p) {
+      if (!w || !key) continue;
+      const int64_t q = qsel ? qsel[p] : p;
+      int ok = q >= 0 && q < N;
+      for (int64_t j = 0; ok && j < s; ++j)
+        ok = routes[q * s + j] >= 0 && routes[q * s + j] < m;
+      if (!ok) {
+#pragma omp atomic write
+        bad = 1;
+        continue;
+      }
+      /* the raw keys: expert routes[q][0]'s k keys, then the next expert's */
+      for (int64_t j = 0; j < s; ++j)
+        for (int64_t t = 0; t < k; ++t)
+          key[j * k + t] = idx[(int64_t)routes[q * s + j] * k + t];
+      double mx = -INFINITY;
+      for (int64_t i = 0; i < m; ++i) {
+        w[i] = scale * dot(Q + q * d, Ql + i * d, d);
+        if (w[i] > mx) mx = w[i];
+      }
+      for (int64_t t = 0; t < s * k; ++t) {
+        w[m + t] = scale * dot(Q + q * d, K + (int64_t)key[t] * d, d);
+        if (w[m + t] > mx) mx = w[m + t];
+      }
+      double z = 0.0;
+      for (int64_t i = 0; i < np; ++i) {
+        w[i] = exp(w[i] - mx);
+        z += w[i];
+      }
+      for (int64_t c = 0; c < d; ++c) {
+        double acc = 0.0;
+        for (int64_t i = 0; i < m; ++i) acc += w[i] * Vl[i * d + c];
+        for (int64_t t = 0; t < s * k; ++t) acc += w[m + t] * V[(int64_t)key[t] * d + c];
+        out[p * d + c] = acc / z;
+      }
+    }
+    free(w);
+    free(key);
+  }
+  return bad == 2 ? -2 : (bad ? -1 : 0);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Dense attention (the baseline)                                           */
 /* ------------------------------------------------------------------------ */
 

@@ -119,6 +119,43 @@ int mita_oracle_forward(const double* Q, const double* K, const double* V, int64
                         int32_t* idx, int32_t* route, double* Ql, double* Vl,
                         int32_t* offsets, int32_t* perm);
 
+/* ---- several experts per query (s >= 1) --------------------------------
+ * The pages name the number s of experts a query is routed to and run only
+ * s = 1 ([P2], the remark that each query goes to one expert in the
+ * experiments; [P3], the configuration named before the concatenation).
+ * For s > 1 they state neither how a query picks its experts nor how the
+ * pairs of several experts meet.  Reading taken here:
+ *   - a query's experts are the s landmarks with the largest logits
+ *     Q[q] . Ql[i], ties to the lower landmark index, listed in that order
+ *     (the s = 1 rule, repeated over the landmarks not yet taken);
+ *   - the query attends over the m compressed pairs followed by the k raw
+ *     pairs of each of its s experts, in list order, with one softmax over
+ *     all m + s*k scaled logits.  Experts may share keys ([P2]: experts may
+ *     pick overlapping pairs); a key held by two of the query's experts is
+ *     counted once per expert.  This is what [P3] Algorithm 1 computes when
+ *     each expert's query subset is attended separately and the partial
+ *     results are combined by online softmax.
+ * With s = 1 each function below equals its single-expert counterpart. */
+
+/* Step 3 with s experts: routes is [nq][s] (positions in qsel when qsel is
+ * non-NULL), each row the query's s experts in order; 1 <= s <= m. */
+int mita_oracle_route_s(const double* Q, const double* Ql, int64_t N, int64_t d, int64_t m,
+                        int64_t s, const int64_t* qsel, int64_t nq, int32_t* routes);
+
+/* Step 4 with s experts: offsets [m+1] over all N*s (query, expert)
+ * assignments; perm [N*s] = the query of each assignment, ordered by
+ * (expert, query index).  The s experts of a query must be distinct. */
+int mita_oracle_bucket_s(const int32_t* routes, int64_t N, int64_t m, int64_t s,
+                         int32_t* offsets, int32_t* perm);
+
+/* Step 5 with s experts: one softmax over the m compressed pairs and the k
+ * raw pairs of each of the query's s experts (routes [N][s], indexed by
+ * query regardless of qsel); out is [nq][d] (or [N][d]). */
+int mita_oracle_output_s(const double* Q, const double* K, const double* V, const double* Ql,
+                         const double* Vl, const int32_t* idx, const int32_t* routes, int64_t N,
+                         int64_t d, int64_t m, int64_t k, int64_t s, double scale,
+                         const int64_t* qsel, int64_t nq, double* out);
+
 /* Dense attention, the baseline the pages time MiTA against (page 2,
  * section on wall-clock time in long-sequence modelling; page 1, section on
  * long-sequence training time): query q attends over all N key/value pairs

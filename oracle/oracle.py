@@ -60,6 +60,11 @@ def _load(path: str) -> ctypes.CDLL:
                                       _i32p, _i32p, _f64p, _f64p, _i32p, _i32p]
     L.mita_oracle_dense.argtypes = [_f64p, _f64p, _f64p, _i64, _i64, ctypes.c_double, _i64p,
                                     _i64, _f64p]
+    L.mita_oracle_route_s.argtypes = [_f64p, _f64p, _i64, _i64, _i64, _i64, _i64p, _i64, _i32p]
+    L.mita_oracle_bucket_s.argtypes = [_i32p, _i64, _i64, _i64, _i32p, _i32p]
+    L.mita_oracle_output_s.argtypes = [_f64p, _f64p, _f64p, _f64p, _f64p, _i32p, _i32p, _i64,
+                                       _i64, _i64, _i64, _i64, ctypes.c_double, _i64p, _i64,
+                                       _f64p]
     L.mita_oracle_threads.restype = ctypes.c_int
     return L
 
@@ -185,6 +190,46 @@ def output(Q, K, V, Ql, Vl, idx, route_, scale: float, qsel=None) -> np.ndarray:
     _check(lib().mita_oracle_output(_p(Q, _f64p), _p(K, _f64p), _p(V, _f64p), _p(Ql, _f64p),
                                     _p(Vl, _f64p), _p(idx, _i32p), _p(r, _i32p), N, d, m, k,
                                     float(scale), _p(sel, _i64p), nq, _p(out, _f64p)), "output")
+    return out
+
+
+def route_s(Q, Ql, s: int, qsel=None) -> np.ndarray:
+    """[nq, s] int32: each query's s experts, best first."""
+    Q, Ql = _f64(Q), _f64(Ql)
+    N, d = Q.shape
+    m = Ql.shape[0]
+    sel = None if qsel is None else np.ascontiguousarray(np.asarray(qsel, dtype=np.int64))
+    nq = N if sel is None else sel.shape[0]
+    r = np.empty((nq, s), np.int32)
+    _check(lib().mita_oracle_route_s(_p(Q, _f64p), _p(Ql, _f64p), N, d, m, s, _p(sel, _i64p), nq,
+                                     _p(r, _i32p)), "route_s")
+    return r
+
+
+def bucket_s(routes, m: int):
+    """offsets [m+1] and perm [N*s] over every (query, expert) assignment."""
+    r = _i32(routes)
+    N, s = r.shape
+    offsets = np.empty(m + 1, np.int32)
+    perm = np.empty(N * s, np.int32)
+    _check(lib().mita_oracle_bucket_s(_p(r, _i32p), N, m, s, _p(offsets, _i32p),
+                                      _p(perm, _i32p)), "bucket_s")
+    return offsets, perm
+
+
+def output_s(Q, K, V, Ql, Vl, idx, routes, scale: float, qsel=None) -> np.ndarray:
+    Q, K, V, Ql, Vl = _f64(Q), _f64(K), _f64(V), _f64(Ql), _f64(Vl)
+    idx, r = _i32(idx), _i32(routes)
+    N, d = Q.shape
+    m, k = idx.shape
+    s = r.shape[1]
+    sel = None if qsel is None else np.ascontiguousarray(np.asarray(qsel, dtype=np.int64))
+    nq = N if sel is None else sel.shape[0]
+    out = np.empty((nq, d), np.float64)
+    _check(lib().mita_oracle_output_s(_p(Q, _f64p), _p(K, _f64p), _p(V, _f64p), _p(Ql, _f64p),
+                                      _p(Vl, _f64p), _p(idx, _i32p), _p(r, _i32p), N, d, m, k,
+                                      s, float(scale), _p(sel, _i64p), nq, _p(out, _f64p)),
+           "output_s")
     return out
 
 

@@ -403,6 +403,134 @@ def check_output_invariants():
 
 
 # ---------------------------------------------------------------------------
+# several experts per query (s > 1): the pages name s and run only s = 1
+# ([P2], the remark on the experiments' routing; [P3], the configuration named
+# before the concatenation).  Reading: the s best landmarks (ties to the lower
+# index, best first), and one softmax over the m compressed pairs and the k
+# pairs of every routed expert, a key shared by two experts counted once per
+# expert, which is what [P3] Algorithm 1's per-expert attention combined by
+# online softmax gives.
+# ---------------------------------------------------------------------------
+
+
+def check_route_s_vs_lexsort_with_ties():
+    """The s experts are the first s landmarks in the order (larger logit,
+    then lower index), from numpy's lexsort over exact integer logits with
+    many ties; s = 1 is the single-expert routing; s = m lists every
+    landmark once."""
+    rng = _rng(81)
+    Q = _int_data(rng, (300, 4), -2, 2)
+    Ql = _int_data(rng, (7, 4), -1, 1)
+    R = Q @ Ql.T
+    order = np.stack([np.lexsort((np.arange(7), -R[q])) for q in range(300)])
+    for s in (1, 2, 3, 7):
+        assert np.array_equal(O.route_s(Q, Ql, s), order[:, :s])
+    assert np.array_equal(O.route_s(Q, Ql, 1)[:, 0], O.route(Q, Ql))
+    sel = rng.choice(300, 23, replace=False)
+    assert np.array_equal(O.route_s(Q, Ql, 3, qsel=sel), order[sel, :3])
+
+
+def check_bucket_s_vs_stable_argsort():
+    """Every (query, expert) assignment, grouped by expert with queries in
+    index order: a stable argsort of the flattened routes, each entry mapped
+    back to its query."""
+    rng = _rng(82)
+    for N, m, s in [(500, 9, 3), (40, 4, 4), (7, 5, 1)]:
+        routes = np.stack([rng.permutation(m)[:s] for _ in range(N)]).astype(np.int32)
+        off, perm = O.bucket_s(routes, m)
+        flat = routes.reshape(-1)
+        assert np.array_equal(perm, np.argsort(flat, kind="stable") // s)
+        assert np.array_equal(off, np.concatenate([[0], np.cumsum(np.bincount(flat, minlength=m))]))
+    # one query listing the same expert twice is rejected
+    try:
+        O.bucket_s(np.array([[1, 1]], np.int32), 3)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("repeated expert accepted")
+
+
+def _s_case(rng, N=70, d=8, m=6, k=9, s=3):
+    Q, K, V = (rng.standard_normal((N, d)) for _ in range(3))
+    Ql, Vl = rng.standard_normal((m, d)), rng.standard_normal((m, d))
+    # overlapping experts: keys drawn from the first half of the sequence
+    idx = np.sort(np.stack([rng.choice(N // 2, k, replace=False) for _ in range(m)]), 1)
+    routes = np.stack([rng.permutation(m)[:s] for _ in range(N)])
+    return Q, K, V, Ql, Vl, idx.astype(np.int32), routes.astype(np.int32)
+
+
+def check_output_s_vs_concatenated_attention():
+    """Per query, torch's softmax attention over the stacked keys
+    [Ql; K[idx[e1]]; ...; K[idx[es]]] and values [Vl; V[...]; ...]."""
+    rng = _rng(83)
+    Q, K, V, Ql, Vl, idx, routes = _s_case(rng)
+    scale = 0.37
+    got = O.output_s(Q, K, V, Ql, Vl, idx, routes, scale)
+    for q in range(Q.shape[0]):
+        kk = torch.from_numpy(np.vstack([Ql] + [K[idx[e]] for e in routes[q]]))
+        vv = torch.from_numpy(np.vstack([Vl] + [V[idx[e]] for e in routes[q]]))
+        w = torch.softmax(scale * (kk @ torch.from_numpy(Q[q])), 0)
+        np.testing.assert_allclose(got[q], (w @ vv).numpy(), rtol=1e-11, atol=1e-13)
+    sel = np.array([5, 0, 69])
+    np.testing.assert_array_equal(O.output_s(Q, K, V, Ql, Vl, idx, routes, scale, qsel=sel),
+                                  got[sel])
+
+
+def check_output_s_is_online_softmax_of_expert_partials():
+    """[P3] Algorithm 1: attend each routed expert's pairs separately, keep
+    (max, sum, weighted sum) per part, and combine the parts (the compressed
+    pairs and the s experts) by rescaling to a common maximum."""
+    rng = _rng(84)
+    Q, K, V, Ql, Vl, idx, routes = _s_case(rng, N=40, s=4)
+    scale = 0.5
+    got = O.output_s(Q, K, V, Ql, Vl, idx, routes, scale)
+    for q in range(Q.shape[0]):
+        parts = [(Ql, Vl)] + [(K[idx[e]], V[idx[e]]) for e in routes[q]]
+        mx, tot, acc = -np.inf, 0.0, np.zeros(Q.shape[1])
+        for kp, vp in parts:
+            lg = scale * (kp @ Q[q])
+            pm = lg.max()
+            pe = np.exp(lg - pm)
+            nm = max(mx, pm)
+            tot = tot * np.exp(mx - nm) + pe.sum() * np.exp(pm - nm)
+            acc = acc * np.exp(mx - nm) + (pe @ vp) * np.exp(pm - nm)
+            mx = nm
+        np.testing.assert_allclose(got[q], acc / tot, rtol=1e-11, atol=1e-13)
+
+
+def check_output_s_shared_keys_count_per_expert():
+    """With k = N every expert holds every key, so the s experts repeat all N
+    pairs s times: closed form softmax over the compressed logits and the raw
+    logits raised by log(s).  A union that merged repeated keys, or a drop of
+    any expert, fails this."""
+    rng = _rng(85)
+    N, d, m, s, scale = 50, 8, 5, 3, 0.3
+    Q, K, V = (rng.standard_normal((N, d)) for _ in range(3))
+    Ql, Vl = rng.standard_normal((m, d)), rng.standard_normal((m, d))
+    idx = np.tile(np.arange(N, dtype=np.int32), (m, 1))
+    routes = np.stack([rng.permutation(m)[:s] for _ in range(N)]).astype(np.int32)
+    got = O.output_s(Q, K, V, Ql, Vl, idx, routes, scale)
+    lc = scale * (Q @ Ql.T)
+    lr = scale * (Q @ K.T) + np.log(s)
+    lg = np.hstack([lc, lr])
+    w = np.exp(lg - lg.max(1, keepdims=True))
+    want = (w[:, :m] @ Vl + w[:, m:] @ V) / w.sum(1, keepdims=True)
+    np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-13)
+
+
+def check_output_s_reduces_and_is_order_free():
+    """s = 1 is the single-expert output bit for bit; reordering a query's
+    experts changes only the summation order."""
+    rng = _rng(86)
+    Q, K, V, Ql, Vl, idx, routes = _s_case(rng, s=3)
+    one = O.output_s(Q, K, V, Ql, Vl, idx, routes[:, :1], 0.4)
+    np.testing.assert_array_equal(one, O.output(Q, K, V, Ql, Vl, idx, routes[:, 0], 0.4))
+    a = O.output_s(Q, K, V, Ql, Vl, idx, routes, 0.4)
+    b = O.output_s(Q, K, V, Ql, Vl, idx, routes[:, ::-1], 0.4)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
 # the dense-attention baseline (the full attention the pages time MiTA
 # against: "NeurIPS 2026 | Mixture-of-Top-k 注意力…", section
 # "长序列建模：实际运行时间也能明显缩短")

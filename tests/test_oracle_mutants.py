@@ -33,15 +33,30 @@ MUTANTS = {
     "route_argmin": ("if (v > best_v) { /* strict", "if (v < best_v) { /* strict"),
     "bucket_unstable": ("for (int64_t q = 0; q < N; ++q) perm[fill[route[q]]++] = (int32_t)q;",
                         "for (int64_t q = N - 1; q >= 0; --q) perm[fill[route[q]]++] = (int32_t)q;"),
-    "output_drops_compressed_values": ("for (int64_t i = 0; i < m; ++i) acc += w[i] * Vl[i * d + c];",
-                                       "for (int64_t i = 0; i < m; ++i) acc += 0.0 * Vl[i * d + c];"),
+    "output_drops_compressed_values": (
+        "for (int64_t i = 0; i < m; ++i) acc += w[i] * Vl[i * d + c];\n        for (int64_t j = 0;",
+        "for (int64_t i = 0; i < m; ++i) acc += 0.0 * Vl[i * d + c];\n        for (int64_t j = 0;"),
     "output_raw_logits_unscaled": ("w[m + j] = scale * dot(", "w[m + j] = dot("),
     "output_wrong_expert": ("const int32_t* ex = idx + (int64_t)route[q] * k;",
                             "const int32_t* ex = idx + (int64_t)((route[q] + 1) % m) * k;"),
     "output_keys_as_values": ("acc += w[m + j] * V[(int64_t)ex[j] * d + c];",
                               "acc += w[m + j] * K[(int64_t)ex[j] * d + c];"),
-    "output_compressed_keys_from_k": ("w[i] = scale * dot(Q + q * d, Ql + i * d, d);",
-                                      "w[i] = scale * dot(Q + q * d, K + i * d, d);"),
+    "output_compressed_keys_from_k": (
+        "w[i] = scale * dot(Q + q * d, Ql + i * d, d);\n        if (w[i] > mx) mx = w[i];\n      }\n      for (int64_t j = 0;",
+        "w[i] = scale * dot(Q + q * d, K + i * d, d);\n        if (w[i] > mx) mx = w[i];\n      }\n      for (int64_t j = 0;"),
+    "route_s_ties_to_high_index": ("if (best < 0 || R[i] > R[best]) best = i;",
+                                   "if (best < 0 || R[i] >= R[best]) best = i;"),
+    "route_s_smallest_logits": ("if (best < 0 || R[i] > R[best]) best = i;",
+                                "if (best < 0 || R[i] < R[best]) best = i;"),
+    "route_s_repeats_best": ("if (taken[i]) continue;", "if (0) continue;"),
+    "bucket_s_unstable": ("for (int64_t q = 0; q < N; ++q)\n    for (int64_t j = 0; j < s; ++j) perm[",
+                          "for (int64_t q = N - 1; q >= 0; --q)\n    for (int64_t j = 0; j < s; ++j) perm["),
+    "output_s_repeats_first_expert": ("key[j * k + t] = idx[(int64_t)routes[q * s + j] * k + t];",
+                                      "key[j * k + t] = idx[(int64_t)routes[q * s] * k + t];"),
+    "output_s_raw_logits_unscaled": ("w[m + t] = scale * dot(", "w[m + t] = dot("),
+    "output_s_drops_compressed_values": (
+        "for (int64_t i = 0; i < m; ++i) acc += w[i] * Vl[i * d + c];\n        for (int64_t t = 0;",
+        "for (int64_t i = 0; i < m; ++i) acc += 0.0 * Vl[i * d + c];\n        for (int64_t t = 0;"),
     "dense_unscaled": ("w[t] = scale * dot(Q + q * d, K + t * d, d);",
                        "w[t] = dot(Q + q * d, K + t * d, d);"),
     "dense_unnormalised": ("out[p * d + c] = sum / total;", "out[p * d + c] = sum;"),

@@ -120,6 +120,31 @@ def test_edge_case(name):
     _check(w, g, exact)
 
 
+# each pre-threshold path of the top-k scan at least once per input type:
+# sampled tiles (from 32K keys), 16-key groups (4097-32767 keys), every key
+# (up to 4096 keys, the edge cases above)
+THRESHOLD_PATHS = {
+    "f32_sampled_40000": _edge("f32_sampled_40000", 1, 2, 40000, (1, 40000, 1, 37), 5,
+                               dtype="f32", values="mixture", centres=64),
+    "f32_groups16_6000": _edge("f32_groups16_6000", 2, 1, 6000, (1, 6000, 1, 20), 40,
+                               dtype="f32"),
+    "bf16_sampled_k3_50001": _edge("bf16_sampled_k3_50001", 1, 2, 50001, (1, 50001, 1, 37), 3,
+                                   values="mixture", centres=128),
+}
+
+
+@pytest.mark.parametrize("name", sorted(THRESHOLD_PATHS))
+def test_threshold_paths(name):
+    w = THRESHOLD_PATHS[name]
+    _say(f"case {name} B={w.B} H={w.H} N={w.N} m={w.m} k={w.k} {w.dtype}")
+    Q, K, V = generate(w)
+    g, exact = _run(w, Q, K, V)
+    rng = np.random.default_rng(321)
+    qsel = np.unique(np.concatenate([np.arange(64), np.arange(w.N - 64, w.N),
+                                     rng.choice(w.N, 1000, replace=False)]))
+    _check(w, g, exact, qsel=qsel)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_exact_ties_resolve_to_lowest_index(dtype):
     """Small-integer inputs: every dot product is exact in fp32 and fp64, so

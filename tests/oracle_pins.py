@@ -359,6 +359,40 @@ def check_output_pair_count_closed_form():
     np.testing.assert_allclose(got, np.tile(want, (N, 1)), rtol=1e-12, atol=1e-14)
 
 
+def check_golden_pair_count_m25_k25():
+    """The pages' worked count (tests/golden/pair_count_m25_k25.json): at
+    m = k = 25 a query attends over 25 compressed and 25 raw pairs, 50 in
+    all.  One-hot values (a column per landmark and per key) make each
+    pair's softmax weight appear in its own output column, so the pairs a
+    query attends over can be counted; with equal logits each weighs 1/50."""
+    import json
+    import os
+
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "pair_count_m25_k25.json")))
+    m, k = g["m"], g["k"]
+    gh, gw, mh, mw = g["grid"]
+    N = gh * gw
+    assert mh * mw == m and g["compressed_pairs"] + g["raw_pairs"] == g["total_pairs"]
+    rng = _rng(65)
+    d = m + N
+    Q = np.zeros((N, d))  # equal logits for every pair
+    K = rng.standard_normal((N, d))
+    Vl = np.eye(m, d)
+    V = np.eye(N, d, k=m)
+    Ql = rng.standard_normal((m, d))
+    idx = np.sort(np.stack([rng.choice(N, k, replace=False) for _ in range(m)]), 1).astype(
+        np.int32)
+    r = rng.integers(0, m, N).astype(np.int32)
+    out = O.output(Q, K, V, Ql, Vl, idx, r, 0.125)
+    for q in range(N):
+        used = np.flatnonzero(out[q] > 0)
+        assert used.size == g["total_pairs"]
+        assert np.count_nonzero(used < m) == g["compressed_pairs"]
+        assert np.array_equal(used[used >= m] - m, idx[r[q]])
+        np.testing.assert_allclose(out[q, used], 1.0 / g["total_pairs"], rtol=1e-14)
+
+
 def check_output_uses_routed_expert():
     """Each query reads exactly the expert it is routed to: compare against
     dense attention over [Ql; K[idx[route[q]]]] computed per query with

@@ -40,8 +40,12 @@ struct AttendLds<BF16, MPAD, KPAD, NW> {
   alignas(16) uint16_t pk[(MPAD + KPAD) * PKST];
   alignas(16) uint16_t vc[kD * VCST];  // fp16 2^-s * Vl^T
   alignas(16) uint16_t vr[kD * VRST];  // fp16 2^-s * V^T of the expert's rows
+  // 2-wave blocks (short items) store output rows straight from registers:
+  // without the stage they need 22 KiB of LDS instead of 31 KiB, so 7 blocks
+  // fit a CU instead of 5, and their latency-bound items overlap more
+  static constexpr bool kStageOut = NW > 2;
   alignas(16) int32_t perm[kAttendTile * kAttendMaxTpb];  // the work item's query indices
-  alignas(16) float ostage[NW][16 * kOStageStride];  // per-wave output rows
+  alignas(16) float ostage[kStageOut ? NW : 1][kStageOut ? 16 * kOStageStride : 4];
   uint32_t vmax;            // bits of the largest |value| staged (>= 0)
 };
 
@@ -283,11 +287,22 @@ __device__ __forceinline__ void attend_queries_bf16(AttendLds<BF16, MPAD, KPAD, 
                                     *reinterpret_cast<const u32x2*>(rv + 16)), pf, acc[dt]);
     }
   }
+  const float f = oscale * __builtin_amdgcn_rcpf(lsum);  // lsum >= 1
+  if constexpr (!L::kStageOut) {
+    // straight from registers: lane (query c16, g) holds features
+    // 16dt + 4g .. +3, so the 4 lanes of a query store 64 contiguous bytes
+    // per instruction.  Slots past the item repeat its last query (same
+    // operands, identical bits).
+    const int64_t q = S.perm[min(sl0 + c16, nq - 1)];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+      *reinterpret_cast<f32x4*>(out_h + q * kD + 16 * dt + 4 * g) = acc[dt] * f;
+    return;
+  }
   // Output rows go through this wave's LDS stage: lane (query c16, g) holds
   // features 16dt + 4g .. +3; read back, 16 lanes cover one 256-byte row, so
   // each store instruction writes four complete rows.
   float* st = S.ostage[wave_id()];
-  const float f = oscale * __builtin_amdgcn_rcpf(lsum);  // lsum >= 1
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
     *reinterpret_cast<f32x4*>(st + c16 * kOStageStride + 16 * dt + 4 * g) = acc[dt] * f;

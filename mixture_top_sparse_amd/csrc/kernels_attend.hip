@@ -40,11 +40,12 @@ struct AttendLds<BF16, MPAD, KPAD, NW> {
   alignas(16) uint16_t pk[(MPAD + KPAD) * PKST];
   alignas(16) uint16_t vc[kD * VCST];  // fp16 2^-s * Vl^T
   alignas(16) uint16_t vr[kD * VRST];  // fp16 2^-s * V^T of the expert's rows
-  // 2-wave blocks (short items) store output rows straight from registers:
-  // without the stage they need 22 KiB of LDS instead of 31 KiB, so 7 blocks
-  // fit a CU instead of 5, and their latency-bound items overlap more
+  // 2-wave blocks (short items) keep each lane's query index in registers
+  // and store output rows straight from them: without the index copy and the
+  // output stage they need 18 KiB of LDS instead of 31 KiB at m = k = 25, so
+  // 8 blocks fit a CU instead of 5, and their latency-bound items overlap more
   static constexpr bool kStageOut = NW > 2;
-  alignas(16) int32_t perm[kAttendTile * kAttendMaxTpb];  // the work item's query indices
+  alignas(16) int32_t perm[kStageOut ? kAttendTile * kAttendMaxTpb : 4];  // item's queries
   alignas(16) float ostage[kStageOut ? NW : 1][kStageOut ? 16 * kOStageStride : 4];
   uint32_t vmax;            // bits of the largest |value| staged (>= 0)
 };
@@ -212,11 +213,13 @@ __device__ int stage_bf16(AttendLds<BF16, MPAD, KPAD, NW>& S, const uint16_t* __
 // 16 queries of one wave (lane column c16 = query) against the staged expert
 // `after_scores` runs once the logits have been formed (the Q operand is then
 // free, so the caller can refill it while the rest of the sub-tile runs).
+// qcol: the query row of this lane's column (used when rows are stored
+// straight from registers).
 template <int MPAD, int KPAD, int NW, bool FULL, class AfterScores>
 __device__ __forceinline__ void attend_queries_bf16(AttendLds<BF16, MPAD, KPAD, NW>& S,
                                                     bf16x8 (&qb)[2], int sl0, int nq, int m,
                                                     int k, float c2, float oscale,
-                                                    float* __restrict__ out_h,
+                                                    float* __restrict__ out_h, int64_t qcol,
                                                     AfterScores&& after_scores) {
   using L = AttendLds<BF16, MPAD, KPAD, NW>;
   constexpr int NPB = (MPAD + KPAD) / 16;
@@ -293,10 +296,9 @@ __device__ __forceinline__ void attend_queries_bf16(AttendLds<BF16, MPAD, KPAD, 
     // 16dt + 4g .. +3, so the 4 lanes of a query store 64 contiguous bytes
     // per instruction.  Slots past the item repeat its last query (same
     // operands, identical bits).
-    const int64_t q = S.perm[min(sl0 + c16, nq - 1)];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
-      *reinterpret_cast<f32x4*>(out_h + q * kD + 16 * dt + 4 * g) = acc[dt] * f;
+      *reinterpret_cast<f32x4*>(out_h + qcol * kD + 16 * dt + 4 * g) = acc[dt] * f;
     return;
   }
   // Output rows go through this wave's LDS stage: lane (query c16, g) holds
@@ -346,14 +348,16 @@ __device__ void attend_bf16(AttendLds<BF16, MPAD, KPAD, NW>& S, const uint16_t* 
       qb[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(Qh + q * kD + 32 * s + 8 * g));
   };
   // the first D sub-tiles' rows are requested before staging (perm from global)
-  int32_t p0[D];
+  using L = AttendLds<BF16, MPAD, KPAD, NW>;
+  int64_t pq[D];  // each ring slot's query row (this lane's column)
 #pragma unroll
-  for (int j = 0; j < D; ++j) p0[j] = ph[ti.qb + slot(j)];
+  for (int j = 0; j < D; ++j) pq[j] = clamp_index(ph[ti.qb + slot(j)], N);
   bf16x8 ring[D][2];
 #pragma unroll
-  for (int j = 0; j < D; ++j) load_q(clamp_index(p0[j], N), ring[j]);
-  for (int c = tid; c < nq; c += 64 * NW)
-    S.perm[c] = static_cast<int32_t>(clamp_index(ph[ti.qb + c], N));
+  for (int j = 0; j < D; ++j) load_q(pq[j], ring[j]);
+  if constexpr (L::kStageOut)
+    for (int c = tid; c < nq; c += 64 * NW)
+      S.perm[c] = static_cast<int32_t>(clamp_index(ph[ti.qb + c], N));
   const int sh = stage_bf16<MPAD, KPAD, NW>(S, K, V, Ql, vl, idx + (bh * m + ti.e) * k, N, m, k, bh);
   const float oscale = exp2i(sh);
   __syncthreads();
@@ -373,8 +377,15 @@ __device__ void attend_bf16(AttendLds<BF16, MPAD, KPAD, NW>& S, const uint16_t* 
         __asm__ volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         attend_queries_bf16<MPAD, KPAD, NW, FULL>(
-            S, ring[j], 16 * (w + W * i), nq, m, k, c2, oscale, out_h,
-            [&](bf16x8(&qb)[2]) { load_q(S.perm[slot(i + D)], qb); });  // sub-tile i + D
+            S, ring[j], 16 * (w + W * i), nq, m, k, c2, oscale, out_h, pq[j],
+            [&](bf16x8(&qb)[2]) {  // sub-tile i + D into this slot
+              if constexpr (L::kStageOut) {
+                load_q(S.perm[slot(i + D)], qb);
+              } else {
+                pq[j] = clamp_index(ph[ti.qb + slot(i + D)], N);
+                load_q(pq[j], qb);
+              }
+            });
       }
     }
   } else {
@@ -383,7 +394,7 @@ __device__ void attend_bf16(AttendLds<BF16, MPAD, KPAD, NW>& S, const uint16_t* 
     for (int j = 0; j < D; ++j)
       if (j < nw)
         attend_queries_bf16<MPAD, KPAD, NW, FULL>(S, ring[j], 16 * (w + W * j), nq, m, k, c2,
-                                                  oscale, out_h, [](bf16x8(&)[2]) {});
+                                                  oscale, out_h, pq[j], [](bf16x8(&)[2]) {});
   }
 }
 

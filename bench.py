@@ -28,24 +28,42 @@ KERNEL_SOURCES = {"k_scan": "kernels_scan.hip", "k_route": "kernels_route.hip",
                   "k_attend": "kernels_attend.hip"}
 # HBM bytes per launch on the 1M-token workload from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE (scaled by 2.0 and 1.0, the factors a 1 GiB copy kernel gives),
-# with the sha1 of the kernel's sources when the counters were taken: a
-# kernel whose sources changed since reports traffic null.
+# with the sha1 of the kernel's sources (kernel_sha) when the counters were
+# taken: a kernel whose sources changed since reports traffic null.
 COUNTED_TRAFFIC = {
     "len_1m": {
-        "k_scan": {"sha": "beef060d23c7", "bytes": 1093188941},
-        "k_route": {"sha": "dda1f9df2419", "bytes": 565872902},
-        "k_attend": {"sha": "b50440838347", "bytes": 1637937507},
+        "k_scan": {"sha": "d7a4cc6d07c6", "bytes": 1093188941},
+        "k_route": {"sha": "6a9a7ba53373", "bytes": 565872902},
+        "k_attend": {"sha": "bc852b89d59c", "bytes": 1637937507},
     },
 }
 
 
+def kernel_sources(symbol: str) -> list[str]:
+    """A kernel's source file, then every local header it includes, directly
+    or through other local headers, in name order."""
+    import re
+
+    csrc = os.path.join(ROOT, "mixture_top_sparse_amd", "csrc")
+    seen, todo = set(), [KERNEL_SOURCES[symbol]]
+    while todo:
+        f = todo.pop()
+        if f in seen:
+            continue
+        seen.add(f)
+        with open(os.path.join(csrc, f)) as fh:
+            todo += [h for h in re.findall(r'^#include "([^"]+)"', fh.read(), flags=re.M)
+                     if os.path.exists(os.path.join(csrc, h))]
+    return [KERNEL_SOURCES[symbol]] + sorted(seen - {KERNEL_SOURCES[symbol]})
+
+
 def kernel_sha(symbol: str) -> str:
-    """sha1 (12 hex digits) of a kernel's source file and the shared headers."""
+    """sha1 (12 hex digits) of a kernel's source file and its local headers."""
     import hashlib
 
     h = hashlib.sha1()
     csrc = os.path.join(ROOT, "mixture_top_sparse_amd", "csrc")
-    for f in (KERNEL_SOURCES[symbol], "mita_device.hpp", "mita_internal.hpp", "tile_dma.hpp"):
+    for f in kernel_sources(symbol):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:12]

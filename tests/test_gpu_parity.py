@@ -278,3 +278,37 @@ def test_workspace_eviction_and_release():
     for s in streams:
         mts.mita_release_workspace(s)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_golden_pair_count_closed_form(dtype):
+    """The pages' count at m = k = 25 (tests/golden/pair_count_m25_k25.json:
+    25 compressed + 25 raw pairs) on the GPU path, independent of the oracle.
+    With Q = 0 every logit ties: every query goes to landmark 0, every expert
+    holds keys 0..k-1 (ties to the lower index), V_l is the mean of V, and
+    every output row is (m * mean(V) + sum of V[0..k-1]) / total_pairs."""
+    import json
+    import os
+
+    from parity import TOL
+
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "pair_count_m25_k25.json")))
+    gh, gw, mh, mw = g["grid"]
+    m, k, N = g["m"], g["k"], gh * gw
+    w = _edge(f"golden_pairs_{dtype}", 1, 2, N, tuple(g["grid"]), k, dtype=dtype)
+    rng = np.random.default_rng(11)
+    Q = np.zeros((1, 2, N, 64), np.float32)
+    K = rng.standard_normal((1, 2, N, 64)).astype(np.float32)
+    V = rng.standard_normal((1, 2, N, 64)).astype(np.float32)
+    _say(f"case golden pair count m={m} k={k} {dtype}")
+    res, exact = _run(w, Q, K, V)
+    Vd = exact[2]
+    assert np.all(res["route"] == 0)
+    assert np.array_equal(res["idx"], np.broadcast_to(np.arange(k, dtype=np.int32),
+                                                      res["idx"].shape))
+    for h in range(2):
+        want = (g["compressed_pairs"] * Vd[0, h].mean(0) + Vd[0, h, :g["raw_pairs"]].sum(0)) \
+            / g["total_pairs"]
+        err = np.abs(res["out"][0, h] - want[None, :]).max()
+        assert err <= TOL[dtype], err

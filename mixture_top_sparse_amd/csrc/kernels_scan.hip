@@ -375,10 +375,11 @@ __global__ __launch_bounds__(256) void k_scan_f32(
 // With three blocks per CU (at most 168 VGPRs) that keeps 48 KiB of tile
 // requests in flight per CU; deeper rings (96 KiB per CU) measured slower,
 // the DMA path losing bandwidth when that many requests queue up.
-// CAP: candidate buffer entries per landmark.  8 in general; 64 where the
-// pre-threshold is the exact k-th score (N <= 4096 keys): then about k keys
-// per landmark pass it, and a 64-entry buffer takes them all without a
-// sort-and-merge per 8 candidates (the end-of-block flush sorts each once).
+// CAP: candidate buffer entries per landmark.  8 in general; 64 (32 when
+// k <= 32) where the pre-threshold is the exact k-th score (N <= 4096 keys):
+// then about k keys per landmark pass it, and the buffer takes them all
+// without a sort-and-merge per 8 candidates (the end-of-block flush sorts
+// each once).  A full buffer is merged mid-scan, so any CAP is exact.
 // NT: K and V tiles are loaded with the non-temporal cache policy (see
 // launch_scan_nw for when).
 template <int NW, int CAP, bool NT>
@@ -943,7 +944,11 @@ static hipError_t launch_scan_nw(const Shape& s, const void* K, const void* V, c
     const uint16_t* Kp = static_cast<const uint16_t*>(K);
     const uint16_t* Vp = static_cast<const uint16_t*>(V);
     const uint16_t* Qlp = static_cast<const uint16_t*>(ws.ql);
-    if (exact)
+    if (exact && s.k <= 32)  // about k candidates per landmark: a 32-entry buffer holds them
+      hipLaunchKernelGGL((k_scan_bf16<NW, 32, false>), grid, dim3(256), 0, st, Kp, Vp, Qlp,
+                         ws.theta, s.N, s.m, s.k, s.scan_splits, c2, ws.part_keys, ws.part_cnt,
+                         ws.part_stats, ws.part_acc, static_cast<int>(s.BH), ba);
+    else if (exact)
       hipLaunchKernelGGL((k_scan_bf16<NW, 64, false>), grid, dim3(256), 0, st, Kp, Vp, Qlp,
                          ws.theta, s.N, s.m, s.k, s.scan_splits, c2, ws.part_keys, ws.part_cnt,
                          ws.part_stats, ws.part_acc, static_cast<int>(s.BH), ba);

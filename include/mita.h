@@ -41,10 +41,12 @@
  * first call that needs it and kept for later calls on that stream, which
  * are ordered after it by the stream itself.  A block that is too small for
  * a call is released with hipFreeAsync on its stream and replaced.  A new
- * stream beyond the eighth takes over the least recently used block: that
- * call first waits for the whole device (hipDeviceSynchronize), so the old
- * block is idle even if its stream has been destroyed, and frees it on the
- * new stream.  mita_release_workspace(stream) frees a stream's block early;
+ * stream beyond the eighth takes over the least recently used block: every
+ * call records an event after its last kernel, and the new stream waits for
+ * the old block's event on the GPU (hipStreamWaitEvent) before freeing it in
+ * its own order, so the old stream's handle is never used again (it may have
+ * been destroyed) and the host never waits.  mita_release_workspace(stream)
+ * frees a stream's block early;
  * call it before destroying a stream that made calls, or after the last
  * call, to return the memory.  At 2^20 tokens x 4 heads the block is about
  * 54 MB.  Every kernel of a call
@@ -189,7 +191,7 @@ int mita_version(void);
  * mita_profile_read): pool, landmark_threshold (the top-k pre-threshold's
  * group maxima), route (with the pre-threshold's selection as leading
  * blocks), landmark_scan (with step 4's prefix over the routing counts as
- * leading blocks), landmark_merge (its first pass carries step 4's
+ * trailing blocks), landmark_merge (its first pass carries step 4's
  * scatter), expert_attend; each of route, landmark_scan and expert_attend
  * is a single kernel launch.  mita_profile_read() waits for the recorded events and
  * returns, per stage, the summed milliseconds and the number of calls since

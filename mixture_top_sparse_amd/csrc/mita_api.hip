@@ -125,10 +125,14 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // calls and reused while it is large enough.  Calls on one stream are
 // ordered by that stream, so a call's kernels never overlap the previous
 // call's use of the block.  A block that is too small is released with
-// hipFreeAsync on its stream and replaced by a larger hipMallocAsync block;
-// the least recently used entry makes room for a new stream.  The device
-// mutex is held for the whole enqueue sequence of a call, so calls from
-// several host threads on one stream do not interleave their kernels.
+// hipFreeAsync on its stream and replaced by a larger hipMallocAsync block.
+// Each call records the entry's event on its stream after its last kernel;
+// when a new stream takes over the least recently used entry, it waits for
+// that event on the GPU (hipStreamWaitEvent) and frees the old block in its
+// own order.  The old stream's handle is never used again (it may have been
+// destroyed), and the host never waits.  The device mutex is held for the
+// whole enqueue sequence of a call, so calls from several host threads on
+// one stream do not interleave their kernels.
 // ---------------------------------------------------------------------------
 
 constexpr int kWsStreams = 8;
@@ -140,6 +144,7 @@ struct DeviceState {
     void* p = nullptr;
     size_t bytes = 0;
     uint64_t used = 0;
+    hipEvent_t done = nullptr;  // recorded on st after each call that used p
   } ws[kWsStreams];
   uint64_t clock = 0;
 };
@@ -152,8 +157,12 @@ DeviceState* device_state() {
   return &g_dev[dev];
 }
 
-// a work-space block of at least `bytes` for calls on stream st
-hipError_t workspace_for(DeviceState& ds, hipStream_t st, size_t bytes, void** out) {
+// A work-space block of at least `bytes` for calls on stream st, and its
+// entry (the caller records entry->done on st after enqueueing the call).
+// Returns MITA_OK, MITA_ERR_OOM (allocation failed) or MITA_ERR_HIP (a wait
+// or free failed; the old block is then kept, not leaked).
+int workspace_for(DeviceState& ds, hipStream_t st, size_t bytes, void** out,
+                  DeviceState::Ws** entry) {
   ++ds.clock;
   DeviceState::Ws* e = nullptr;
   for (auto& w : ds.ws)
@@ -170,34 +179,41 @@ hipError_t workspace_for(DeviceState& ds, hipStream_t st, size_t bytes, void** o
         if (w.used < e->used) e = &w;
     }
   }
-  if (e->p != nullptr && e->st != st) {
-    // another stream's block: that stream may since have been destroyed, so
-    // its handle is not used.  Once the device is idle no call is using the
-    // block, and it can be freed in the order of the calling stream.
-    hipError_t ef = hipDeviceSynchronize();
+  if (e->done == nullptr) {
+    const hipError_t ec = hipEventCreateWithFlags(&e->done, hipEventDisableTiming);
+    if (ec != hipSuccess) {
+      e->done = nullptr;
+      return fail(MITA_ERR_HIP, std::string("hipEventCreateWithFlags: ") + hipGetErrorString(ec));
+    }
+  }
+  if (e->p != nullptr && (e->st != st || e->bytes < bytes)) {
+    // Another stream's block (taken over), or this stream's block grown too
+    // small.  The calls that used it end with e->done; st waits for that on
+    // the GPU and frees the block in its own order.
+    hipError_t ef = hipStreamWaitEvent(st, e->done, 0);
     if (ef == hipSuccess) ef = hipFreeAsync(e->p, st);
+    if (ef != hipSuccess)
+      return fail(MITA_ERR_HIP, std::string("releasing a cached work space: ") +
+                                    hipGetErrorString(ef));
     e->p = nullptr;
     e->bytes = 0;
-    if (ef != hipSuccess) return ef;
-  } else if (e->p != nullptr && e->bytes < bytes) {
-    // too small: freed after this stream's earlier calls, replaced below
-    const hipError_t ef = hipFreeAsync(e->p, st);
-    e->p = nullptr;
-    e->bytes = 0;
-    if (ef != hipSuccess) return ef;
   }
   if (e->p == nullptr) {
     const size_t want = bytes + bytes / 4;  // room for somewhat larger calls
     void* p = nullptr;
     const hipError_t ea = hipMallocAsync(&p, want, st);
-    if (ea != hipSuccess || p == nullptr) return ea != hipSuccess ? ea : hipErrorOutOfMemory;
+    if (ea != hipSuccess || p == nullptr)
+      return fail(MITA_ERR_OOM, std::string("work-space allocation failed: ") +
+                                    hipGetErrorString(ea != hipSuccess ? ea
+                                                                       : hipErrorOutOfMemory));
     e->p = p;
     e->bytes = want;
   }
   e->st = st;
   e->used = ds.clock;
   *out = e->p;
-  return hipSuccess;
+  *entry = e;
+  return MITA_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -427,13 +443,14 @@ int mita_forward_ex(const void* Q, const void* K, const void* V, int dtype, int6
     Workspace ws;
     const size_t bytes = plan_workspace(s, &ws, nullptr);
     void* base = nullptr;
-    hipError_t e = workspace_for(*ds, st, bytes, &base);
-    if (e != hipSuccess || base == nullptr) {
+    DeviceState::Ws* entry = nullptr;
+    rc = workspace_for(*ds, st, bytes, &base, &entry);
+    if (rc != MITA_OK) {
       (void)hipGetLastError();
-      return fail(MITA_ERR_OOM, std::string("work-space allocation failed: ") +
-                                    hipGetErrorString(e));
+      return rc;
     }
     plan_workspace(s, &ws, static_cast<char*>(base));
+    hipError_t e = hipSuccess;
 
     void* ql_copy = dbg ? dbg->ql : nullptr;
     float* vl_copy = dbg ? dbg->vl : nullptr;
@@ -450,7 +467,7 @@ int mita_forward_ex(const void* Q, const void* K, const void* V, int dtype, int6
     // All on the caller's stream, in this order: pool; the top-k
     // pre-threshold's group maxima; routing (the pre-threshold's selection as
     // its leading blocks); the landmark scan (step 4's prefix over the
-    // routing counts as its leading blocks); the merge (step 4's scatter as
+    // routing counts as its trailing blocks); the merge (step 4's scatter as
     // leading blocks of its first pass); the expert attention.  Bucketing
     // rides in launches that follow routing anyway, so the call needs no
     // second stream and no events.
@@ -480,6 +497,12 @@ int mita_forward_ex(const void* Q, const void* K, const void* V, int dtype, int6
       e = launch_attend(s, Q, K, V, idx_out, ws, out, st);
     }
     if (g_prof.enabled && e == hipSuccess) g_prof.calls += 1;
+    // the block is in use until here on st (see workspace_for)
+    const hipError_t er = hipEventRecord(entry->done, st);
+    if (e == hipSuccess && er != hipSuccess) {
+      where = "work-space event";
+      e = er;
+    }
     if (e != hipSuccess)
       return fail(MITA_ERR_HIP, std::string("launch of stage ") + where +
                                     " failed: " + hipGetErrorString(e));
@@ -533,14 +556,14 @@ int mita_release_workspace(void* stream) {
   std::lock_guard<std::mutex> lk(ds->mu);
   for (auto& w : ds->ws) {
     if (w.p == nullptr || w.st != st) continue;
-    const hipError_t e = hipFreeAsync(w.p, st);
-    w.p = nullptr;
-    w.bytes = 0;
-    w.st = nullptr;
+    const hipError_t e = hipFreeAsync(w.p, st);  // after the calls already on st
     if (e != hipSuccess) {
       (void)hipGetLastError();
       return fail(MITA_ERR_HIP, std::string("hipFreeAsync: ") + hipGetErrorString(e));
     }
+    w.p = nullptr;
+    w.bytes = 0;
+    w.st = nullptr;
   }
   return MITA_OK;
 }

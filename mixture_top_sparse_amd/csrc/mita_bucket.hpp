@@ -9,7 +9,7 @@
 // has a launch of its own:
 //   bucket_prefix   (one 256-thread block per expert and head): exclusive
 //                   prefix of the expert's counts over the segments, and the
-//                   expert's total.  Leading blocks of the landmark-scan
+//                   expert's total.  Trailing blocks of the landmark-scan
 //                   launch, which follows routing on the same stream.
 //   scatter_segment (one wave per segment): expert offsets from the totals,
 //                   then a stable sort of the segment in LDS (a query's rank

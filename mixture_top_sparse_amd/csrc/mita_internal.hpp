@@ -80,7 +80,7 @@ hipError_t launch_pool(const Shape& s, const void* Q, const Workspace& ws, void*
 hipError_t launch_threshold(const Shape& s, const void* K, const Workspace& ws,
                             hipStream_t st);
 hipError_t launch_groups_bf16(const Shape& s, const void* K, const Workspace& ws, hipStream_t st);
-// landmark scan, with step 4's prefix over the routing counts as leading
+// landmark scan, with step 4's prefix over the routing counts as trailing
 // blocks (needs the routes' counts: after launch_route)
 hipError_t launch_scan(const Shape& s, const void* K, const void* V, const Workspace& ws,
                        const int32_t* route, hipStream_t st);

@@ -224,16 +224,41 @@ def check_topk_permutation_equivariance():
         assert set(p[b[i]].tolist()) == set(a[i].tolist())
 
 
+def _abs_product_sum(a, b):
+    """Sum over coordinates of |a_j * b_j|, written out term by term."""
+    return float(sum(abs(float(x) * float(y)) for x, y in zip(a, b)))
+
+
 def check_topk_gap_report():
+    """The near-tie report of the top-k step: the k-th and (k+1)-th scores in
+    the order (larger score, then lower key) and, for those two keys, the sum
+    of |products| of their dot products (the bound the comparison protocol
+    scales its fp32 band by).  Computed here from a lexicographic sort and
+    term-by-term sums; integer data make some scores tie exactly, so the tie
+    rule decides which key sits at each of the two places."""
     rng = _rng(25)
-    Ql = rng.standard_normal((5, 8))
-    K = rng.standard_normal((90, 8))
-    _, gap = O.topk(Ql, K, 10, with_gap=True)
+    cases = [(rng.standard_normal((5, 8)), rng.standard_normal((90, 8)), 10),
+             (_int_data(rng, (7, 6), -2, 2), _int_data(rng, (80, 6), -2, 2), 13),
+             (_int_data(rng, (4, 5), -1, 1), _int_data(rng, (40, 5), -3, 3), 1)]
+    for Ql, K, k in cases:
+        _, gap = O.topk(Ql, K, k, with_gap=True)
+        S = Ql @ K.T
+        for i in range(Ql.shape[0]):
+            order = np.lexsort((np.arange(K.shape[0]), -S[i]))  # score desc, index asc
+            tk, tn = order[k - 1], order[k]
+            assert np.isclose(gap[i, 0], S[i, tk], rtol=1e-12, atol=1e-12)
+            assert np.isclose(gap[i, 1], S[i, tn], rtol=1e-12, atol=1e-12)
+            assert np.isclose(gap[i, 2], _abs_product_sum(Ql[i], K[tk]), rtol=1e-13, atol=0)
+            assert np.isclose(gap[i, 3], _abs_product_sum(Ql[i], K[tn]), rtol=1e-13, atol=0)
+            assert gap[i, 2] >= abs(gap[i, 0]) and gap[i, 3] >= abs(gap[i, 1])
+    # k = N: no (k+1)-th key, so no near-tie is possible
+    Ql, K = rng.standard_normal((3, 4)), rng.standard_normal((12, 4))
+    _, gap = O.topk(Ql, K, 12, with_gap=True)
     S = Ql @ K.T
-    srt = -np.sort(-S, axis=1)
-    np.testing.assert_allclose(gap[:, 0], srt[:, 9], rtol=1e-12)
-    np.testing.assert_allclose(gap[:, 1], srt[:, 10], rtol=1e-12)
-    assert np.all(gap[:, 2] >= np.abs(gap[:, 0]) - 1e-12)
+    assert np.all(gap[:, 1] == -np.inf) and np.all(gap[:, 3] == 0.0)
+    for i in range(3):
+        last = np.lexsort((np.arange(12), -S[i]))[11]
+        assert np.isclose(gap[i, 2], _abs_product_sum(Ql[i], K[last]), rtol=1e-13, atol=0)
 
 
 # ---------------------------------------------------------------------------
@@ -292,14 +317,35 @@ def check_route_vs_argmax_with_ties():
 
 
 def check_route_top2_report():
+    """The near-tie report of routing: the best and second-best logits (each
+    the first occurrence in landmark order, the best one excluded from the
+    search for the second) and the sums of |products| of those two dot
+    products, from an independent sort and term-by-term sums."""
     rng = _rng(42)
-    Q = rng.standard_normal((50, 8))
-    Ql = rng.standard_normal((6, 8))
+    cases = [(rng.standard_normal((50, 8)), rng.standard_normal((6, 8))),
+             (_int_data(rng, (120, 4), -2, 2), _int_data(rng, (9, 4), -1, 1))]
+    for Q, Ql in cases:
+        sel = np.arange(Q.shape[0])[::3]
+        for qsel in (None, sel):
+            r, top2 = O.route(Q, Ql, qsel=qsel, with_top2=True)
+            qs = np.arange(Q.shape[0]) if qsel is None else sel
+            R = Q[qs] @ Ql.T
+            for p, q in enumerate(qs):
+                order = np.lexsort((np.arange(Ql.shape[0]), -R[p]))
+                best, second = order[0], order[1]
+                assert r[p] == best
+                assert np.isclose(top2[p, 0], R[p, best], rtol=1e-12, atol=1e-12)
+                assert np.isclose(top2[p, 1], R[p, second], rtol=1e-12, atol=1e-12)
+                assert np.isclose(top2[p, 2], _abs_product_sum(Q[q], Ql[best]), rtol=1e-13,
+                                  atol=0)
+                assert np.isclose(top2[p, 3], _abs_product_sum(Q[q], Ql[second]), rtol=1e-13,
+                                  atol=0)
+    # a single landmark: no runner-up
+    Q, Ql = rng.standard_normal((10, 4)), rng.standard_normal((1, 4))
     r, top2 = O.route(Q, Ql, with_top2=True)
-    R = Q @ Ql.T
-    srt = -np.sort(-R, axis=1)
-    np.testing.assert_allclose(top2[:, 0], srt[:, 0], rtol=1e-12)
-    np.testing.assert_allclose(top2[:, 1], srt[:, 1], rtol=1e-12)
+    assert np.all(r == 0) and np.all(top2[:, 1] == -np.inf) and np.all(top2[:, 3] == 0.0)
+    for q in range(10):
+        assert np.isclose(top2[q, 2], _abs_product_sum(Q[q], Ql[0]), rtol=1e-13, atol=0)
 
 
 # ---------------------------------------------------------------------------

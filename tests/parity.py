@@ -15,6 +15,10 @@ Per (batch, head):
 Near-tie (top-k and routing alike): gap between the two fp64 scores below
 max(1e-4 * max(|a|, |b|), 2 * d * 2^-24 * max(A_a, A_b)), where A is the sum
 of |products| of the dot product (the fp32 accumulation error bound).
+Near-ties are rare for continuous inputs, so their counts are capped: at
+most max(1, 1% of the experts checked) top-k near-ties and max(1, 0.1% of
+the queries checked) routing near-ties per comparison.  A band that grew too
+wide (and so excused real selection or routing errors) would break a cap.
 Tolerance: 1e-5 absolute for fp32 inputs, 5e-3 for bf16 inputs (fp32
 accumulation).
 """
@@ -42,17 +46,37 @@ class Report:
     vl_max_err: float = 0.0
     out_max_err: float = 0.0
     queries_checked: int = 0
+    experts_checked: int = 0
     failures: list = field(default_factory=list)
 
     def fail(self, msg):
         if len(self.failures) < 20:
             self.failures.append(msg)
 
+    def caps(self):
+        """(top-k cap, routing cap) on the near-tie counts."""
+        return max(1, self.experts_checked // 100), max(1, self.queries_checked // 1000)
+
+    def cap_failures(self):
+        tcap, rcap = self.caps()
+        msgs = []
+        if self.topk_near_ties > tcap:
+            msgs.append(f"{self.topk_near_ties} top-k near-ties over {self.experts_checked} "
+                        f"experts exceed the cap {tcap}")
+        if self.route_near_ties > rcap:
+            msgs.append(f"{self.route_near_ties} routing near-ties over {self.queries_checked} "
+                        f"queries exceed the cap {rcap}")
+        return msgs
+
     def ok(self):
-        return not self.failures
+        return not self.failures and not self.cap_failures()
+
+    def problems(self):
+        return self.failures + self.cap_failures()
 
     def summary(self):
-        return (f"heads={self.heads} queries={self.queries_checked} ql_mismatch={self.ql_mismatch} "
+        return (f"heads={self.heads} queries={self.queries_checked} experts={self.experts_checked} "
+                f"ql_mismatch={self.ql_mismatch} "
                 f"topk_near_ties={self.topk_near_ties} route_near_ties={self.route_near_ties} "
                 f"vl_max_err={self.vl_max_err:.3e} out_max_err={self.out_max_err:.3e}")
 
@@ -78,7 +102,9 @@ def check_head(w, Qh, Kh, Vh, g, rep: Report, qsel=None, exact_ties=False):
     """Compare one head.  Qh, Kh, Vh: [N, d] exact fp64 inputs; g: dict of this
     head's GPU results; qsel: optional query sample; exact_ties: demand
     identical sets/routes even at near-ties (for inputs whose scores are
-    exact in fp32, where ties must resolve by index on both sides)."""
+    exact in fp32, where ties must resolve by index on both sides).  Adds
+    this head's counts to rep (near-ties, experts and queries checked) and
+    returns it."""
     tol = TOL[w.dtype]
     N, d = Qh.shape
     m, k = w.m, w.k
@@ -92,6 +118,7 @@ def check_head(w, Qh, Kh, Vh, g, rep: Report, qsel=None, exact_ties=False):
         rep.fail(f"landmark queries differ in {bad} elements")
 
     idx_o, gap = O.topk(ql, Kh, k, with_gap=True)
+    rep.experts_checked += m
     for i in range(m):
         if np.array_equal(idx_o[i], g["idx"][i]):
             continue
@@ -125,7 +152,7 @@ def check_head(w, Qh, Kh, Vh, g, rep: Report, qsel=None, exact_ties=False):
     r_g = g["route"][qs]
     if np.any((g["route"] < 0) | (g["route"] >= m)):
         rep.fail("route out of range")
-        return
+        return rep
     for j in np.nonzero(r_o != r_g)[0]:
         q = qs[j]
         if exact_ties:
@@ -151,3 +178,4 @@ def check_head(w, Qh, Kh, Vh, g, rep: Report, qsel=None, exact_ties=False):
     rep.queries_checked += len(qs)
     if not err <= tol:
         rep.fail(f"output max err {err:.3e} > {tol}")
+    return rep

@@ -49,8 +49,9 @@ def _check(w, g, exact, heads=None, qsel=None, exact_ties=False):
     for b, h in pairs:
         gh = {key: val[b, h] for key, val in g.items()}
         check_head(w, Qd[b, h], Kd[b, h], Vd[b, h], gh, rep, qsel=qsel, exact_ties=exact_ties)
-    _say(f"{w.name}: {rep.summary()}")
-    assert rep.ok(), rep.failures
+    _say(f"{w.name}: {rep.summary()} near-tie caps (top-k, route)={rep.caps()}")
+    assert rep.ok(), rep.problems()
+    return rep
 
 
 # ---------------------------------------------------------------------------

@@ -57,6 +57,19 @@ MUTANTS = {
     "output_s_drops_compressed_values": (
         "for (int64_t i = 0; i < m; ++i) acc += w[i] * Vl[i * d + c];\n        for (int64_t t = 0;",
         "for (int64_t i = 0; i < m; ++i) acc += 0.0 * Vl[i * d + c];\n        for (int64_t t = 0;"),
+    # the near-tie report that the comparison protocol's band is built from
+    "abs_dot_inflated": ("s += fabs(a[j] * b[j]);", "s += 100.0 * fabs(a[j] * b[j]);"),
+    "abs_dot_signed": ("s += fabs(a[j] * b[j]);", "s += a[j] * b[j];"),
+    "gap_bound_of_best_key": ("g[2] = abs_dot(Ql + i * d, K + row[k - 1].t * d, d);",
+                              "g[2] = abs_dot(Ql + i * d, K + row[0].t * d, d);"),
+    "gap_next_bound_of_kth_key": ("g[3] = abs_dot(Ql + i * d, K + row[k].t * d, d);",
+                                  "g[3] = abs_dot(Ql + i * d, K + row[k - 1].t * d, d);"),
+    "route_runner_up_bound_zero": (
+        "g[3] = second_i >= 0 ? abs_dot(Q + q * d, Ql + second_i * d, d) : 0.0;",
+        "g[3] = 0.0;"),
+    "route_best_bound_of_landmark0": ("g[2] = abs_dot(Q + q * d, Ql + best * d, d);",
+                                      "g[2] = abs_dot(Q + q * d, Ql, d);"),
+    "route_runner_up_ties_to_last": ("if (v > second) {", "if (v >= second) {"),
     "dense_unscaled": ("w[t] = scale * dot(Q + q * d, K + t * d, d);",
                        "w[t] = dot(Q + q * d, K + t * d, d);"),
     "dense_unnormalised": ("out[p * d + c] = sum / total;", "out[p * d + c] = sum;"),

@@ -142,6 +142,30 @@ int mita_forward_ex(const void* Q, const void* K, const void* V, int dtype, int6
                     void* stream, const mita_intermediates* dbg);
 
 /*
+ * mita_forward_noalloc — mita_forward for callers that cannot allocate
+ * device memory: code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid hipMalloc.  It computes exactly what mita_forward
+ * computes with the same kernels, but its work space is a static device
+ * array of 64 MiB (one per device, allocated when the library's code object
+ * loads and held until the process ends) instead of a cached
+ * hipMallocAsync block: the call makes no hipMalloc, hipMallocAsync,
+ * hipFree, hipFreeAsync or other allocating call, and records no event (the
+ * stage profiler skips it).  Every call on a device shares that device's
+ * array, so calls that overlap on one GPU race: issue them on one stream, or
+ * order them.  Nothing in the array needs to start at zero; each call writes
+ * every part it later reads.
+ *
+ * Same arguments, pointer rules and errors as mita_forward, plus
+ * MITA_ERR_UNSUPPORTED (with the byte counts in mita_last_error()) when the
+ * call's work space would exceed the 64 MiB array; nothing is enqueued then.
+ * The 2^20-token 4-head workload (m = k = 64) needs about 60 MB.
+ */
+int mita_forward_noalloc(const void* Q, const void* K, const void* V, int dtype, int64_t B,
+                         int64_t H, int64_t N, int64_t d, const mita_grid* grid, int64_t m,
+                         int64_t k, float scale, float* out, int32_t* idx_out,
+                         int32_t* route_out, void* stream);
+
+/*
  * mita_dense_attention — dense (full) attention, the baseline the pages time
  * MiTA against ["NeurIPS 2026 | Mixture-of-Top-k 注意力…", section
  * "长序列建模：实际运行时间也能明显缩短"; P1, section "长序列建模：训练时间从

@@ -15,6 +15,7 @@ import os
 __all__ = [
     "mita_forward",
     "mita_forward_ex",
+    "mita_forward_noalloc",
     "mita_dense_attention",
     "mita_release_workspace",
     "mita_status_string",
@@ -72,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.mita_forward.restype = ctypes.c_int
         L.mita_forward_ex.argtypes = _FWD_ARGS + [ctypes.POINTER(MitaIntermediates)]
         L.mita_forward_ex.restype = ctypes.c_int
+        L.mita_forward_noalloc.argtypes = _FWD_ARGS
+        L.mita_forward_noalloc.restype = ctypes.c_int
         L.mita_dense_attention.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
                                            ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
@@ -138,7 +141,7 @@ def _check_inputs(Q, K, V):
     return dt
 
 
-def _call(Q, K, V, m: int, k: int, grid, scale, want_dbg: bool):
+def _call(Q, K, V, m: int, k: int, grid, scale, want_dbg: bool, noalloc: bool = False):
     import torch
 
     dt = _check_inputs(Q, K, V)
@@ -154,6 +157,9 @@ def _call(Q, K, V, m: int, k: int, grid, scale, want_dbg: bool):
         stream = torch.cuda.current_stream(dev).cuda_stream
         args = [Q.data_ptr(), K.data_ptr(), V.data_ptr(), dt, B, H, N, d, g, int(m), int(k),
                 float(scale), out.data_ptr(), idx.data_ptr(), route.data_ptr(), stream]
+        if noalloc:
+            _raise(lib().mita_forward_noalloc(*args), "mita_forward_noalloc")
+            return out, idx, route
         if not want_dbg:
             _raise(lib().mita_forward(*args), "mita_forward")
             return out, idx, route
@@ -182,6 +188,14 @@ def mita_forward_ex(Q, K, V, *, m: int, k: int, grid=None, scale=None):
     """Like mita_forward, plus a dict of intermediates: ql (landmark queries),
     vl (landmark values, fp32), perm (queries grouped by expert) and offsets."""
     return _call(Q, K, V, m, k, grid, scale, want_dbg=True)
+
+
+def mita_forward_noalloc(Q, K, V, *, m: int, k: int, grid=None, scale=None):
+    """mita_forward without any device allocation by the library: its work
+    space is the library's static 64 MiB scratch array (calls that overlap on
+    one GPU race; larger problems raise).  The outputs are still allocated
+    here, by torch, before the call."""
+    return _call(Q, K, V, m, k, grid, scale, want_dbg=False, noalloc=True)
 
 
 def mita_dense_attention(Q, K, V, *, scale=None):

@@ -83,8 +83,9 @@ struct StageTimer {
   int stage;
   hipStream_t st;
   hipEvent_t a = nullptr, b = nullptr;
-  StageTimer(int s, hipStream_t stream) : stage(s), st(stream) {
-    if (g_prof.enabled) {
+  // on: false for the no-allocation entry point (the profiler creates events)
+  StageTimer(int s, hipStream_t stream, bool on) : stage(s), st(stream) {
+    if (on && g_prof.enabled) {
       a = g_prof.get();
       b = g_prof.get();
       if (a && b) hipEventRecord(a, st);
@@ -137,8 +138,17 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 constexpr int kWsStreams = 8;
 
+// The no-allocation entry point's work space: one array per device, sized
+// for every workload of this build's limits up to kScratchBytes (64 MiB: the
+// 2^20-token, 4-head workload needs about 60 MB).  In host code `scratch`
+// names a host-side stand-in, never a device address: host code only ever
+// uses the address hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = size_t{64} << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
 struct DeviceState {
   std::mutex mu;
+  void* scratch_ptr = nullptr;  // this device's copy of `scratch` (device address)
   struct Ws {
     hipStream_t st = nullptr;
     void* p = nullptr;
@@ -213,6 +223,23 @@ int workspace_for(DeviceState& ds, hipStream_t st, size_t bytes, void** out,
   e->used = ds.clock;
   *out = e->p;
   *entry = e;
+  return MITA_OK;
+}
+
+// This device's address of the static scratch array, looked up once per
+// device (the caller holds the device mutex, with that device current).
+int scratch_for(DeviceState& ds, void** out) {
+  if (ds.scratch_ptr == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return fail(MITA_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") +
+                                    hipGetErrorString(e != hipSuccess ? e : hipErrorInvalidSymbol));
+    }
+    ds.scratch_ptr = p;
+  }
+  *out = ds.scratch_ptr;
   return MITA_OK;
 }
 
@@ -421,10 +448,17 @@ const char* mita_status_string(int status) {
 
 const char* mita_last_error(void) { return g_last_error.c_str(); }
 
-int mita_forward_ex(const void* Q, const void* K, const void* V, int dtype, int64_t B, int64_t H,
-                    int64_t N, int64_t d, const mita_grid* grid, int64_t m, int64_t k,
-                    float scale, float* out, int32_t* idx_out, int32_t* route_out, void* stream,
-                    const mita_intermediates* dbg) {
+}  // extern "C"
+
+namespace {
+
+// The forward pass: validation, work space, then every launch on `stream`.
+// use_scratch: take the device's static scratch array instead of a cached
+// stream-ordered block (no allocation of any kind).
+int forward_impl(const void* Q, const void* K, const void* V, int dtype, int64_t B, int64_t H,
+                 int64_t N, int64_t d, const mita_grid* grid, int64_t m, int64_t k, float scale,
+                 float* out, int32_t* idx_out, int32_t* route_out, void* stream,
+                 const mita_intermediates* dbg, bool use_scratch) {
   try {
     g_last_error.clear();
     Shape s;
@@ -437,14 +471,23 @@ int mita_forward_ex(const void* Q, const void* K, const void* V, int dtype, int6
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     derive(s, device_cus());
+    Workspace ws;
+    const size_t bytes = plan_workspace(s, &ws, nullptr);
+    if (use_scratch && bytes > kScratchBytes)
+      return fail(MITA_ERR_UNSUPPORTED,
+                  "mita_forward_noalloc: this call needs " + std::to_string(bytes) +
+                      " bytes of work space, more than the static scratch array's " +
+                      std::to_string(kScratchBytes) + " bytes (use mita_forward)");
     DeviceState* ds = device_state();
     if (ds == nullptr) return fail(MITA_ERR_HIP, "no current HIP device");
     std::lock_guard<std::mutex> lk(ds->mu);  // the whole enqueue sequence
-    Workspace ws;
-    const size_t bytes = plan_workspace(s, &ws, nullptr);
     void* base = nullptr;
     DeviceState::Ws* entry = nullptr;
-    rc = workspace_for(*ds, st, bytes, &base, &entry);
+    if (use_scratch) {
+      rc = scratch_for(*ds, &base);
+    } else {
+      rc = workspace_for(*ds, st, bytes, &base, &entry);
+    }
     if (rc != MITA_OK) {
       (void)hipGetLastError();
       return rc;
@@ -461,7 +504,7 @@ int mita_forward_ex(const void* Q, const void* K, const void* V, int dtype, int6
     const char* where = "pool";
     if (inject_launch) e = hipErrorLaunchFailure;
     if (e == hipSuccess) {
-      StageTimer t(kStagePool, st);
+      StageTimer t(kStagePool, st, !use_scratch);
       e = launch_pool(s, Q, ws, ql_copy, 0, s.BH, st);
     }
     // All on the caller's stream, in this order: pool; the top-k
@@ -473,35 +516,37 @@ int mita_forward_ex(const void* Q, const void* K, const void* V, int dtype, int6
     // second stream and no events.
     if (e == hipSuccess && s.theta_groups > 0) {
       where = "landmark_threshold";
-      StageTimer t(kStageThreshold, st);
+      StageTimer t(kStageThreshold, st, !use_scratch);
       e = launch_threshold(s, K, ws, st);
     }
     if (e == hipSuccess) {
       where = "route";
-      StageTimer t(kStageRoute, st);
+      StageTimer t(kStageRoute, st, !use_scratch);
       e = launch_route(s, Q, ws, route_out, st);
     }
     if (e == hipSuccess) {
       where = "landmark_scan";
-      StageTimer t(kStageScan, st);
+      StageTimer t(kStageScan, st, !use_scratch);
       e = launch_scan(s, K, V, ws, route_out, st);
     }
     if (e == hipSuccess) {
       where = "landmark_merge";
-      StageTimer t(kStageMerge, st);
+      StageTimer t(kStageMerge, st, !use_scratch);
       e = launch_merge(s, ws, idx_out, vl_copy, route_out, off_copy, perm_copy, st);
     }
     if (e == hipSuccess) {
       where = "expert_attend";
-      StageTimer t(kStageAttend, st);
+      StageTimer t(kStageAttend, st, !use_scratch);
       e = launch_attend(s, Q, K, V, idx_out, ws, out, st);
     }
-    if (g_prof.enabled && e == hipSuccess) g_prof.calls += 1;
-    // the block is in use until here on st (see workspace_for)
-    const hipError_t er = hipEventRecord(entry->done, st);
-    if (e == hipSuccess && er != hipSuccess) {
-      where = "work-space event";
-      e = er;
+    if (!use_scratch && g_prof.enabled && e == hipSuccess) g_prof.calls += 1;
+    if (entry != nullptr) {
+      // the block is in use until here on st (see workspace_for)
+      const hipError_t er = hipEventRecord(entry->done, st);
+      if (e == hipSuccess && er != hipSuccess) {
+        where = "work-space event";
+        e = er;
+      }
     }
     if (e != hipSuccess)
       return fail(MITA_ERR_HIP, std::string("launch of stage ") + where +
@@ -510,6 +555,26 @@ int mita_forward_ex(const void* Q, const void* K, const void* V, int dtype, int6
   } catch (...) {
     return fail(MITA_ERR_INTERNAL, "unexpected exception inside mita_forward");
   }
+}
+
+}  // namespace
+
+extern "C" {
+
+int mita_forward_ex(const void* Q, const void* K, const void* V, int dtype, int64_t B, int64_t H,
+                    int64_t N, int64_t d, const mita_grid* grid, int64_t m, int64_t k,
+                    float scale, float* out, int32_t* idx_out, int32_t* route_out, void* stream,
+                    const mita_intermediates* dbg) {
+  return forward_impl(Q, K, V, dtype, B, H, N, d, grid, m, k, scale, out, idx_out, route_out,
+                      stream, dbg, false);
+}
+
+int mita_forward_noalloc(const void* Q, const void* K, const void* V, int dtype, int64_t B,
+                         int64_t H, int64_t N, int64_t d, const mita_grid* grid, int64_t m,
+                         int64_t k, float scale, float* out, int32_t* idx_out,
+                         int32_t* route_out, void* stream) {
+  return forward_impl(Q, K, V, dtype, B, H, N, d, grid, m, k, scale, out, idx_out, route_out,
+                      stream, nullptr, true);
 }
 
 int mita_forward(const void* Q, const void* K, const void* V, int dtype, int64_t B, int64_t H,

@@ -106,6 +106,32 @@ def test_unsupported(L, case):
     assert mts.mita_last_error() != ""
 
 
+def call_noalloc(L, **over):
+    a = dict(Q=A, K=A, V=A, dtype=1, B=2, H=3, N=4096, d=64, grid=None, m=64, k=64, scale=0.125,
+             out=A, idx=A, route=A, stream=None)
+    a.update(over)
+    g = None if a["grid"] is None else ctypes.byref(mts.MitaGrid(*a["grid"]))
+    return L.mita_forward_noalloc(a["Q"], a["K"], a["V"], a["dtype"], a["B"], a["H"], a["N"],
+                                  a["d"], g, a["m"], a["k"], a["scale"], a["out"], a["idx"],
+                                  a["route"], a["stream"])
+
+
+@pytest.mark.parametrize("case", sorted(set(INVALID) - {"misaligned_dbg"}))
+def test_noalloc_invalid_arguments(L, case):
+    """The no-allocation entry point validates exactly like mita_forward."""
+    assert call_noalloc(L, **INVALID[case]) == mts.MITA_ERR_INVALID_ARG
+    assert mts.mita_last_error() != ""
+
+
+def test_noalloc_rejects_work_space_beyond_scratch(L):
+    """2^23 tokens x 2 heads needs more than the 64 MiB static array (the
+    query permutation alone is 64 MiB): rejected on the host, with the byte
+    counts, before any launch."""
+    assert call_noalloc(L, B=1, H=2, N=1 << 23) == mts.MITA_ERR_UNSUPPORTED
+    msg = mts.mita_last_error()
+    assert "scratch" in msg and str(64 << 20) in msg
+
+
 def test_injected_allocation_failure(L, monkeypatch):
     monkeypatch.setenv("MITA_FAULT_INJECT", "alloc")
     assert call(L) == mts.MITA_ERR_OOM

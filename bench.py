@@ -165,8 +165,11 @@ def cpu_baseline(w, Qt, Kt, Vt, g_out, g_idx, g_route):
     sl = [t[0:1, 0:1].contiguous() for t in (Qt, Kt, Vt)]
     g = gpu_results_to_numpy(mts.mita_forward_ex(*sl, m=w.m, k=w.k, grid=w.grid, scale=w.scale))
     g = {key: val[0, 0] for key, val in g.items()}
-    same_as_full = (np.array_equal(g["idx"], idx_g) and np.array_equal(g["route"], route_g)
-                    and np.array_equal(g["out"], g_out[0, 0].cpu().numpy()))
+    # the one-slice call splits the key scan differently (more splits per
+    # head), so its landmark values may differ from the full call's in the
+    # last bits; experts and routes must not
+    same_as_full = np.array_equal(g["idx"], idx_g) and np.array_equal(g["route"], route_g)
+    slice_vs_full = float(np.max(np.abs(g["out"] - g_out[0, 0].cpu().numpy())))
     rep = check_head(w, Q[0, 0], K[0, 0], V[0, 0], g, Report(), qsel=sel)
     same_idx = int(sum(np.array_equal(a, b) for a, b in zip(res["idx"][0, 0], idx_g)))
     log(f"cpu baseline slice parity: {rep.summary()}")
@@ -190,7 +193,8 @@ def cpu_baseline(w, Qt, Kt, Vt, g_out, g_idx, g_route):
             "vl_max_err": rep.vl_max_err,
             "out_max_err_sampled": rep.out_max_err,
             "tolerance": TOL_BY_DTYPE[w.dtype],
-            "slice_call_matches_full_call": bool(same_as_full),
+            "slice_call_experts_routes_match_full_call": bool(same_as_full),
+            "slice_call_out_max_diff_vs_full_call": slice_vs_full,
             "pass": rep.ok(),
         },
     }
@@ -217,10 +221,39 @@ def copy_probe(nbytes: int = 1 << 30, reps: int = 10) -> dict:
             "GBs": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
-def dense_baseline(w, Qt, Kt, Vt, mita_ms: float) -> dict:
+def device_warmup(ms: float) -> dict | None:
+    """A plain 256 MiB fp32 copy kernel (torch.neg) repeated for about `ms`
+    milliseconds of GPU time: brings the memory clocks out of their idle
+    state before the timed MiTA steps (no MiTA work, nothing timed)."""
+    import torch
+
+    if ms <= 0:
+        return None
+    x = torch.ones((64 << 20,), dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    launches, spent = 0, 0.0
+    while spent < ms:
+        e0.record()
+        for _ in range(10):
+            torch.neg(x, out=y)
+        e1.record()
+        torch.cuda.synchronize()
+        spent += e0.elapsed_time(e1)
+        launches += 10
+    del x, y
+    log(f"device warm-up: {launches} copy launches of 256 MiB in {spent:.1f} ms")
+    return {"kind": "fp32 copy kernel (torch.neg), 256 MiB per launch", "launches": launches,
+            "ms": round(spent, 2)}
+
+
+def dense_baseline(w, Qt, Kt, Vt) -> dict:
     """Dense (full) attention on the same inputs with the library's own
-    flash-attention kernel: time per forward, MFMA throughput, and MiTA's
-    speedup over it (the ratio the pages report against full attention)."""
+    flash-attention kernel: time per forward and MFMA throughput (MiTA's
+    speedup over it, the ratio the pages report against full attention, is
+    added once the MiTA step is timed)."""
     import torch
 
     import mixture_top_sparse_amd as mts
@@ -241,11 +274,10 @@ def dense_baseline(w, Qt, Kt, Vt, mita_ms: float) -> dict:
     ms = e0.elapsed_time(e1) / reps
     flops = 4.0 * w.B * w.H * float(w.N) ** 2 * w.d
     tflops = flops / (ms * 1e-3) / 1e12
-    log(f"dense attention: {ms:.3f} ms/forward ({reps} timed), {tflops:.0f} TFLOP/s, "
-        f"MiTA speedup {ms / mita_ms:.1f}x")
+    log(f"dense attention: {ms:.3f} ms/forward ({reps} timed), {tflops:.0f} TFLOP/s")
     return {"kernel": "k_dense_bf16", "ms_per_step": round(ms, 4), "steps": reps,
             "flops": flops, "achieved": round(tflops, 1), "peak": 2500.0, "unit": "TFLOP/s",
-            "frac": round(tflops / 2500.0, 4), "speedup": round(ms / mita_ms, 2)}
+            "frac": round(tflops / 2500.0, 4)}
 
 
 def main() -> int:
@@ -258,6 +290,11 @@ def main() -> int:
     ap.add_argument("--dense", choices=["auto", "on", "off"], default="auto",
                     help="also time the hand-written dense (full) attention kernel on the same "
                          "inputs and report the speedup (auto: bf16 workloads with N >= 65536)")
+    ap.add_argument("--device-warmup-ms", type=float, default=60.0,
+                    help="before MiTA's own warm-up steps, run a plain memory-bound copy kernel "
+                         "for this long: HBM and fabric clocks ramp over the first 10-15 ms of "
+                         "memory-bound work after idling, which a few warm-up steps do not "
+                         "cover (0 disables)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also time a plain 1 GiB device copy kernel (bandwidth context and the "
                          "calibration kernel for HBM byte counters)")
@@ -285,6 +322,13 @@ def main() -> int:
 
     def step():
         return mts.mita_forward(Qt, Kt, Vt, m=w.m, k=w.k, grid=w.grid, scale=w.scale)
+
+    warm = device_warmup(args.device_warmup_ms)
+    # The dense-attention baseline runs first (it is part of the report, and
+    # it takes the GPU out of its idle clock state before MiTA's warm-up).
+    dense = None
+    if args.dense == "on" or (args.dense == "auto" and w.dtype == "bf16" and w.N >= 65536):
+        dense = dense_baseline(w, Qt, Kt, Vt)
 
     for _ in range(args.warmup):
         res = step()
@@ -383,8 +427,12 @@ def main() -> int:
                       "bucket_size_min_med_max": [int(sizes.min()), float(np.median(sizes)),
                                                   int(sizes.max())]},
     }
-    if args.dense == "on" or (args.dense == "auto" and w.dtype == "bf16" and w.N >= 65536):
-        line["dense_baseline"] = dense_baseline(w, Qt, Kt, Vt, ms_per_step)
+    if warm is not None:
+        line["device_warmup"] = warm
+    if dense is not None:
+        dense["speedup"] = round(dense["ms_per_step"] / ms_per_step, 2)
+        log(f"MiTA speedup over dense attention: {dense['speedup']:.1f}x")
+        line["dense_baseline"] = dense
     if args.copy_probe:
         line["copy_probe"] = copy_probe()
     if not args.no_cpu_baseline:

@@ -13,7 +13,7 @@
 // 64 queries reuse it.  Queries are gathered in expert order (perm) straight
 // into MFMA operand registers; output rows are scattered back.
 //   logits^T = [Ql; K_e] Q_tile^T   (pair rows x query columns, MFMA)
-//   out^T    = [Vl; V_e]^T P^T       (fp16 MFMA on 2^-s scaled values)
+//   out^T    = [Vl; V_e]^T P^T       (bf16 MFMA; P and Vl as hi + lo pairs)
 // Every per-query quantity (max, sum, rescale) stays in the 4 lanes that hold
 // that query's column.
 //
@@ -26,7 +26,6 @@ namespace mita {
 
 constexpr int kAttendWaves = 8;       // bf16 expert attention: waves per block
 constexpr int kAttendShortItems = 256;  // below this many queries per expert (mean): 2 waves
-constexpr int kOStageStride = 68;     // floats per staged output row (bank spread)
 
 template <class T, int MPAD, int KPAD, int NW = kAttendWaves>
 struct AttendLds;
@@ -35,19 +34,20 @@ struct AttendLds;
 template <int MPAD, int KPAD, int NW>
 struct AttendLds<BF16, MPAD, KPAD, NW> {
   static constexpr int PKST = 72;        // pair-key rows (bf16 elements)
-  static constexpr int VCST = MPAD + 4;  // compressed Vl^T rows (fp16)
-  static constexpr int VRST = KPAD + 4;  // raw V^T rows (fp16)
+  static constexpr int VCST = MPAD + 4;  // compressed Vl^T rows (bf16)
+  static constexpr int VRST = KPAD + 4;  // raw V^T rows (bf16)
   alignas(16) uint16_t pk[(MPAD + KPAD) * PKST];
-  alignas(16) uint16_t vc[kD * VCST];  // fp16 2^-s * Vl^T
-  alignas(16) uint16_t vr[kD * VRST];  // fp16 2^-s * V^T of the expert's rows
+  alignas(16) uint16_t vch[kD * VCST];  // Vl^T, bf16 hi part
+  alignas(16) uint16_t vcl[kD * VCST];  // Vl^T, bf16 lo part (Vl - hi, rounded)
+  alignas(16) uint16_t vr[kD * VRST];   // V^T of the expert's rows (exact bf16)
   // 2-wave blocks (short items) keep each lane's query index in registers
   // and store output rows straight from them: without the index copy and the
-  // output stage they need 18 KiB of LDS instead of 31 KiB at m = k = 25, so
-  // 8 blocks fit a CU instead of 5, and their latency-bound items overlap more
+  // output stage they need far less LDS, so several fit a CU and their
+  // latency-bound items overlap more
   static constexpr bool kStageOut = NW > 2;
   alignas(16) int32_t perm[kStageOut ? kAttendTile * kAttendMaxTpb : 4];  // item's queries
-  alignas(16) float ostage[kStageOut ? NW : 1][kStageOut ? 16 * kOStageStride : 4];
-  uint32_t vmax;            // bits of the largest |value| staged (>= 0)
+  // per wave: 16 output rows of 64 floats, 16-byte chunks XOR-swizzled by row
+  alignas(16) float ostage[kStageOut ? NW : 1][kStageOut ? 16 * kD : 4];
 };
 
 template <int MPAD, int KPAD, int NW>
@@ -90,17 +90,20 @@ __device__ __forceinline__ int64_t clamp_index(int64_t v, int64_t n) {
 
 // ---- bf16 ----------------------------------------------------------------
 //
-// Logits run on bf16 MFMA (Q, Ql and K are exact bf16).  P.V runs on fp16
-// MFMA: P in [0, 1] rounds to fp16 with relative error <= 2^-11; the values
-// are scaled by 2^-s (s >= 0 chosen from the largest |value| of the item, so
-// that every scaled value stays below 2^15) and then convert to fp16 — exactly
-// for the raw bf16 values, with relative error <= 2^-11 for the fp32 landmark
-// values (convex combinations of V rows, so that error is <= 2^-11 max|V|).
-// The output multiplies the 2^s back.
+// Logits run on bf16 MFMA (Q, Ql and K are exact bf16).  P.V runs on bf16
+// MFMA too, with the computed operands split into hi + lo bf16 pairs
+// (hi = rne(x), lo = rne(x - hi): about 16 significant bits): the softmax
+// weights P always, the landmark values Vl for the compressed pairs.  Raw
+// values are exact bf16.  Per 32 pairs: raw  acc += V^T P_hi + V^T P_lo;
+// compressed  acc += Vl_hi^T P_hi + Vl_hi^T P_lo + Vl_lo^T P_hi (the
+// dropped Vl_lo P_lo term is below 2^-16 of the product).  Each operand
+// carries relative error <= 2^-16 (two roundings at unit 2^-8), so an output
+// differs from the exact combination of its weights by at most about
+// 3 * 2^-16 * max|value| plus fp32 accumulation, whatever the values' range.
 
-// Stage the expert of this work item; returns the value scale exponent s.
+// Stage the expert of this work item.
 template <int MPAD, int KPAD, int NW>
-__device__ int stage_bf16(AttendLds<BF16, MPAD, KPAD, NW>& S, const uint16_t* __restrict__ K,
+__device__ void stage_bf16(AttendLds<BF16, MPAD, KPAD, NW>& S, const uint16_t* __restrict__ K,
                           const uint16_t* __restrict__ V, const uint16_t* __restrict__ Ql,
                           const float* __restrict__ vl, const int32_t* __restrict__ ex, int64_t N,
                           int m, int k, int64_t bh) {
@@ -109,62 +112,67 @@ __device__ int stage_bf16(AttendLds<BF16, MPAD, KPAD, NW>& S, const uint16_t* __
   constexpr int NT = 64 * NW;
   const int tid = threadIdx.x;
   const u32x4 z = {0, 0, 0, 0};
-  if (tid == 0) S.vmax = 0u;
-  __syncthreads();
 
-  // raw values: unit u = rows 2rp, 2rp+1 of the expert, 8 features from 8*col
-  constexpr int RU = (KPAD / 2) * 8, RN = (RU + NT - 1) / NT;
-  u32x4 va[RN], vb[RN];
-  uint32_t mbits = 0;  // largest |bf16| bit pattern seen
+  // raw values: unit u = rows 2rp, 2rp+1 of the expert, 8 features from
+  // 8*col, stored transposed as bf16 pairs (row 2rp low, 2rp+1 high)
+  constexpr int RU = (KPAD / 2) * 8;
+  for (int u = tid; u < RU; u += NT) {
+    const int rp = u >> 3, col = u & 7;
+    u32x4 va = z, vb = z;
+    if (2 * rp < k)
+      va = *reinterpret_cast<const u32x4*>(V + (bh * N + clamp_index(ex[2 * rp], N)) * kD +
+                                           col * 8);
+    if (2 * rp + 1 < k)
+      vb = *reinterpret_cast<const u32x4*>(V + (bh * N + clamp_index(ex[2 * rp + 1], N)) * kD +
+                                           col * 8);
 #pragma unroll
-  for (int j = 0; j < RN; ++j) {
-    const int u = tid + NT * j, rp = u >> 3, col = u & 7;
-    va[j] = z;
-    vb[j] = z;
-    if (u < RU) {
-      if (2 * rp < k)
-        va[j] = *reinterpret_cast<const u32x4*>(V + (bh * N + clamp_index(ex[2 * rp], N)) * kD +
-                                                col * 8);
-      if (2 * rp + 1 < k)
-        vb[j] = *reinterpret_cast<const u32x4*>(V + (bh * N + clamp_index(ex[2 * rp + 1], N)) * kD +
-                                                col * 8);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        mbits = max(mbits, max(va[j][i] & 0x7FFFu, (va[j][i] >> 16) & 0x7FFFu));
-        mbits = max(mbits, max(vb[j][i] & 0x7FFFu, (vb[j][i] >> 16) & 0x7FFFu));
-      }
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t a = (i & 1) ? (va[i >> 1] >> 16) : (va[i >> 1] & 0xFFFFu);
+      const uint32_t b = (i & 1) ? (vb[i >> 1] >> 16) : (vb[i >> 1] & 0xFFFFu);
+      *reinterpret_cast<uint32_t*>(S.vr + (col * 8 + i) * L::VRST + 2 * rp) = a | (b << 16);
     }
   }
-  float vmax = __uint_as_float(mbits << 16);
-  // landmark values: unit u = rows 2lp, 2lp+1, 8 features from 8*dc
+  // landmark values: unit u = rows 2lp, 2lp+1, 8 features from 8*dc, split
+  // into bf16 hi + lo and stored transposed
   constexpr int LP = MPAD / 2;
-  constexpr int LU = LP * 8, LN = (LU + NT - 1) / NT;
-  float la[LN][8], lb[LN][8];
+  constexpr int LU = LP * 8;
+  for (int u = tid; u < LU; u += NT) {
+    const int lp = u % LP, dc = u / LP;
+    float la[8], lb[8];
 #pragma unroll
-  for (int j = 0; j < LN; ++j) {
-    const int u = tid + NT * j, lp = u % LP, dc = u / LP;
+    for (int i = 0; i < 8; ++i) la[i] = lb[i] = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) la[j][i] = lb[j][i] = 0.f;
-    if (u < LU) {
+    for (int h = 0; h < 2; ++h) {
+      const int row = 2 * lp + h;
+      if (row < m) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(vl + (bh * m + row) * kD + dc * 8);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(vl + (bh * m + row) * kD + dc * 8 + 4);
+        float* dst = h ? lb : la;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int row = 2 * lp + h;
-        if (row < m) {
-          const f32x4 a = *reinterpret_cast<const f32x4*>(vl + (bh * m + row) * kD + dc * 8);
-          const f32x4 b = *reinterpret_cast<const f32x4*>(vl + (bh * m + row) * kD + dc * 8 + 4);
-          float* dst = h ? lb[j] : la[j];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            dst[i] = a[i];
-            dst[4 + i] = b[i];
-          }
+        for (int i = 0; i < 4; ++i) {
+          dst[i] = a[i];
+          dst[4 + i] = b[i];
         }
       }
+    }
+    bf16x8 ah, al, bh8, bl8;
+    split_hi_lo_pk(la, ah, al);
+    split_hi_lo_pk(lb, bh8, bl8);
+    // the halves are taken from the raw bits (element i of a bf16x8 is the
+    // low (even i) or high (odd i) half of dword i/2)
+    const u32x4 wah = __builtin_bit_cast(u32x4, ah), wal = __builtin_bit_cast(u32x4, al);
+    const u32x4 wbh = __builtin_bit_cast(u32x4, bh8), wbl = __builtin_bit_cast(u32x4, bl8);
+    auto half = [](const u32x4& v, int i) {
+      return (i & 1) ? (v[i >> 1] >> 16) : (v[i >> 1] & 0xFFFFu);
+    };
 #pragma unroll
-      for (int i = 0; i < 8; ++i) vmax = fmaxf(vmax, fmaxf(fabsf(la[j][i]), fabsf(lb[j][i])));
+    for (int i = 0; i < 8; ++i) {
+      *reinterpret_cast<uint32_t*>(S.vch + (dc * 8 + i) * L::VCST + 2 * lp) =
+          half(wah, i) | (half(wbh, i) << 16);
+      *reinterpret_cast<uint32_t*>(S.vcl + (dc * 8 + i) * L::VCST + 2 * lp) =
+          half(wal, i) | (half(wbl, i) << 16);
     }
   }
-  atomicMax(&S.vmax, __float_as_uint(vmax));
 
   // pair keys: Ql rows then the expert's K rows (zero rows for padding)
   for (int c = tid; c < NP * 8; c += NT) {
@@ -178,36 +186,6 @@ __device__ int stage_bf16(AttendLds<BF16, MPAD, KPAD, NW>& S, const uint16_t* __
     }
     *reinterpret_cast<u32x4*>(S.pk + row * L::PKST + cc * 8) = v;
   }
-  __syncthreads();
-
-  const int e = static_cast<int>((S.vmax >> 23) & 0xFF) - 127;
-  const int sh = e > 14 ? e - 14 : 0;  // 2^-sh * max|value| < 2^15
-  const float sc = exp2i(-sh);
-#pragma unroll
-  for (int j = 0; j < RN; ++j) {
-    const int u = tid + NT * j, rp = u >> 3, col = u & 7;
-    if (u < RU) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t wa = va[j][i >> 1], wb = vb[j][i >> 1];
-        const float a = __uint_as_float((i & 1) ? (wa & 0xFFFF0000u) : (wa << 16));
-        const float b = __uint_as_float((i & 1) ? (wb & 0xFFFF0000u) : (wb << 16));
-        *reinterpret_cast<uint32_t*>(S.vr + (col * 8 + i) * L::VRST + 2 * rp) =
-            pack_f16(a * sc, b * sc);
-      }
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < LN; ++j) {
-    const int u = tid + NT * j, lp = u % LP, dc = u / LP;
-    if (u < LU) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<uint32_t*>(S.vc + (dc * 8 + i) * L::VCST + 2 * lp) =
-            pack_f16(la[j][i] * sc, lb[j][i] * sc);
-    }
-  }
-  return sh;
 }
 
 // 16 queries of one wave (lane column c16 = query) against the staged expert
@@ -218,8 +196,8 @@ __device__ int stage_bf16(AttendLds<BF16, MPAD, KPAD, NW>& S, const uint16_t* __
 template <int MPAD, int KPAD, int NW, bool FULL, class AfterScores>
 __device__ __forceinline__ void attend_queries_bf16(AttendLds<BF16, MPAD, KPAD, NW>& S,
                                                     bf16x8 (&qb)[2], int sl0, int nq, int m,
-                                                    int k, float c2, float oscale,
-                                                    float* __restrict__ out_h, int64_t qcol,
+                                                    int k, float c2, float* __restrict__ out_h,
+                                                    int64_t qcol,
                                                     AfterScores&& after_scores) {
   using L = AttendLds<BF16, MPAD, KPAD, NW>;
   constexpr int NPB = (MPAD + KPAD) / 16;
@@ -264,33 +242,42 @@ __device__ __forceinline__ void attend_queries_bf16(AttendLds<BF16, MPAD, KPAD, 
   f32x4 acc[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x4{0, 0, 0, 0};
-  // 32 pairs per step: pair blocks 2*s2 and 2*s2+1 give this lane's 8 P values
-  auto p_f16 = [&](int pb0) {
-    u32x4 w = {pack_f16(x[pb0][0], x[pb0][1]), pack_f16(x[pb0][2], x[pb0][3]),
-               pack_f16(x[pb0 + 1][0], x[pb0 + 1][1]), pack_f16(x[pb0 + 1][2], x[pb0 + 1][3])};
-    return __builtin_bit_cast(f16x8, w);
+  // 32 pairs per step: pair blocks 2*s2 and 2*s2+1 give this lane's 8 P
+  // values, split into bf16 hi + lo
+  auto p_split = [&](int pb0, bf16x8& hi, bf16x8& lo) {
+    const float p[8] = {x[pb0][0],     x[pb0][1],     x[pb0][2],     x[pb0][3],
+                        x[pb0 + 1][0], x[pb0 + 1][1], x[pb0 + 1][2], x[pb0 + 1][3]};
+    split_hi_lo_pk(p, hi, lo);
+  };
+  auto vt = [&](const uint16_t* row) {
+    return join_bf16x8(*reinterpret_cast<const u32x2*>(row),
+                       *reinterpret_cast<const u32x2*>(row + 16));
   };
 #pragma unroll
   for (int s2 = 0; s2 < MPAD / 32; ++s2) {
-    const f16x8 pf = p_f16(2 * s2);
+    bf16x8 ph, pl;
+    p_split(2 * s2, ph, pl);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      const uint16_t* rc = S.vc + (16 * dt + c16) * L::VCST + 32 * s2 + 4 * g;
-      acc[dt] = mfma_f16(join_f16x8(*reinterpret_cast<const u32x2*>(rc),
-                                    *reinterpret_cast<const u32x2*>(rc + 16)), pf, acc[dt]);
+      const int off = (16 * dt + c16) * L::VCST + 32 * s2 + 4 * g;
+      const bf16x8 vh = vt(S.vch + off), vlo = vt(S.vcl + off);
+      acc[dt] = mfma_bf16(vlo, ph, acc[dt]);
+      acc[dt] = mfma_bf16(vh, pl, acc[dt]);
+      acc[dt] = mfma_bf16(vh, ph, acc[dt]);
     }
   }
 #pragma unroll
   for (int s2 = 0; s2 < KPAD / 32; ++s2) {
-    const f16x8 pf = p_f16(MPAD / 16 + 2 * s2);
+    bf16x8 ph, pl;
+    p_split(MPAD / 16 + 2 * s2, ph, pl);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      const uint16_t* rv = S.vr + (16 * dt + c16) * L::VRST + 32 * s2 + 4 * g;
-      acc[dt] = mfma_f16(join_f16x8(*reinterpret_cast<const u32x2*>(rv),
-                                    *reinterpret_cast<const u32x2*>(rv + 16)), pf, acc[dt]);
+      const bf16x8 vv = vt(S.vr + (16 * dt + c16) * L::VRST + 32 * s2 + 4 * g);
+      acc[dt] = mfma_bf16(vv, pl, acc[dt]);
+      acc[dt] = mfma_bf16(vv, ph, acc[dt]);
     }
   }
-  const float f = oscale * __builtin_amdgcn_rcpf(lsum);  // lsum >= 1
+  const float f = __builtin_amdgcn_rcpf(lsum);  // lsum >= 1
   if constexpr (!L::kStageOut) {
     // straight from registers: lane (query c16, g) holds features
     // 16dt + 4g .. +3, so the 4 lanes of a query store 64 contiguous bytes
@@ -302,19 +289,21 @@ __device__ __forceinline__ void attend_queries_bf16(AttendLds<BF16, MPAD, KPAD, 
     return;
   }
   // Output rows go through this wave's LDS stage: lane (query c16, g) holds
-  // features 16dt + 4g .. +3; read back, 16 lanes cover one 256-byte row, so
-  // each store instruction writes four complete rows.
+  // features 16dt + 4g .. +3 (16-byte chunk 4dt + g of row c16); read back,
+  // 16 lanes cover one 256-byte row, so each store instruction writes four
+  // complete rows.  Chunks are XOR-swizzled by row (no bank conflicts either
+  // way).
   float* st = S.ostage[wave_id()];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
-    *reinterpret_cast<f32x4*>(st + c16 * kOStageStride + 16 * dt + 4 * g) = acc[dt] * f;
+    *reinterpret_cast<f32x4*>(st + c16 * kD + (((4 * dt + g) ^ c16) & 15) * 4) = acc[dt] * f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = 4 * j + (l >> 4);
     // slots past the item repeat its last query: those lanes computed that
     // query's row from the same operands, so they store identical bits
     const int sl = min(sl0 + row, nq - 1);
-    const f32x4 v = *reinterpret_cast<const f32x4*>(st + row * kOStageStride + 4 * (l & 15));
+    const f32x4 v = *reinterpret_cast<const f32x4*>(st + row * kD + (((l & 15) ^ row) & 15) * 4);
     const int64_t q = S.perm[sl];
     // non-temporal: the rows are not read again here, and written-through
     // lines do not leave dirty cache lines for the next kernel to flush
@@ -358,8 +347,7 @@ __device__ void attend_bf16(AttendLds<BF16, MPAD, KPAD, NW>& S, const uint16_t* 
   if constexpr (L::kStageOut)
     for (int c = tid; c < nq; c += 64 * NW)
       S.perm[c] = static_cast<int32_t>(clamp_index(ph[ti.qb + c], N));
-  const int sh = stage_bf16<MPAD, KPAD, NW>(S, K, V, Ql, vl, idx + (bh * m + ti.e) * k, N, m, k, bh);
-  const float oscale = exp2i(sh);
+  stage_bf16<MPAD, KPAD, NW>(S, K, V, Ql, vl, idx + (bh * m + ti.e) * k, N, m, k, bh);
   __syncthreads();
 
   const int nw = nsub > w ? (nsub - w + W - 1) / W : 0;  // this wave's sub-tiles
@@ -377,7 +365,7 @@ __device__ void attend_bf16(AttendLds<BF16, MPAD, KPAD, NW>& S, const uint16_t* 
         __asm__ volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         attend_queries_bf16<MPAD, KPAD, NW, FULL>(
-            S, ring[j], 16 * (w + W * i), nq, m, k, c2, oscale, out_h, pq[j],
+            S, ring[j], 16 * (w + W * i), nq, m, k, c2, out_h, pq[j],
             [&](bf16x8(&qb)[2]) {  // sub-tile i + D into this slot
               if constexpr (L::kStageOut) {
                 load_q(S.perm[slot(i + D)], qb);
@@ -394,7 +382,7 @@ __device__ void attend_bf16(AttendLds<BF16, MPAD, KPAD, NW>& S, const uint16_t* 
     for (int j = 0; j < D; ++j)
       if (j < nw)
         attend_queries_bf16<MPAD, KPAD, NW, FULL>(S, ring[j], 16 * (w + W * j), nq, m, k, c2,
-                                                  oscale, out_h, pq[j], [](bf16x8(&)[2]) {});
+                                                  out_h, pq[j], [](bf16x8(&)[2]) {});
   }
 }
 

@@ -89,6 +89,25 @@ def test_workload_sampled(name):
     _check(w, g, exact, heads=heads, qsel=qsel)
 
 
+@pytest.mark.parametrize("name", ["deit_s_14x14", "len_64k"])
+def test_values_scaled_by_8(name):
+    """Values 8x larger (a power of two, so bf16 rounding commutes with it):
+    the attention's P.V error bound scales with max|V|, and the hi + lo
+    operands must keep it inside the 5e-3 tolerance at max|V| near 45."""
+    w = WORKLOADS[name]
+    _say(f"case {name} with V scaled by 8")
+    Q, K, V = generate(w)
+    g, exact = _run(w, Q, K, 8.0 * V)
+    assert np.abs(exact[2]).max() > 30.0
+    if w.N <= 4096:
+        rep = _check(w, g, exact)
+    else:
+        rng = np.random.default_rng(5)
+        qsel = np.unique(np.concatenate([np.arange(64), rng.choice(w.N, 2000, replace=False)]))
+        rep = _check(w, g, exact, heads=[(0, 0), (w.B - 1, w.H - 1)], qsel=qsel)
+    _say(f"{name} x8: out_max_err={rep.out_max_err:.3e}")
+
+
 # ---------------------------------------------------------------------------
 # edge cases
 # ---------------------------------------------------------------------------

@@ -24,9 +24,9 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 TOL_BY_DTYPE = {"f32": 1e-5, "bf16": 5e-3}  # the parity tolerance of each input type
 # profiler stages that are exactly one kernel launch, with that kernel's name
 SINGLE_KERNEL_STAGES = {"landmark_scan": "k_scan", "route": "k_route",
-                        "expert_attend": "k_attend"}
+                        "expert_attend": "k_attend", "single_launch": "k_small"}
 KERNEL_SOURCES = {"k_scan": "kernels_scan.hip", "k_route": "kernels_route.hip",
-                  "k_attend": "kernels_attend.hip"}
+                  "k_attend": "kernels_attend.hip", "k_small": "kernels_small.hip"}
 # HBM bytes per launch on the 1M-token workload from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE (scaled by 2.0 and 1.0, the factors a 1 GiB copy kernel gives),
 # with the sha1 of the kernel's sources (kernel_sha) when the counters were
@@ -111,6 +111,8 @@ def stage_bytes(w) -> dict[str, float]:
         "landmark_scan": BH * (2 * N * d * e),
         "landmark_merge": BH * (4 * m * k + 4 * m * d + 4 * N + 4 * N),
         "expert_attend": BH * (N * d * e + 4 * N * d + 4 * N + rows * 2 * d * e),
+        # the one-launch path of short sequences runs all five steps
+        "single_launch": path_bytes(w),
     }
 
 
@@ -369,7 +371,7 @@ def main() -> int:
     avg_stage = {k: v / max(calls, 1) for k, v in stage_ms.items()}
     sbytes = stage_bytes(w)
     # the dominant kernel: the slowest of the single-launch stages
-    dominant = max(SINGLE_KERNEL_STAGES, key=lambda st: avg_stage[st])
+    dominant = max(SINGLE_KERNEL_STAGES, key=lambda st: avg_stage.get(st, 0.0))
     ach = sbytes[dominant] / (avg_stage[dominant] * 1e-3) / 1e9
     pbytes = path_bytes(w)
     path_gbs = pbytes / (ms_per_step * 1e-3) / 1e9

@@ -49,7 +49,9 @@
  * frees a stream's block early;
  * call it before destroying a stream that made calls, or after the last
  * call, to return the memory.  At 2^20 tokens x 4 heads the block is about
- * 54 MB.  Every kernel of a call
+ * 54 MB.  bf16 calls with N <= 256 tokens take a one-launch path instead
+ * (one workgroup per head holds the head's keys and values in LDS and runs
+ * all five steps): they use no work space at all.  Every kernel of a call
  * runs on `stream`; there is no host synchronisation and no global state
  * besides the cached work-space blocks, the per-device attribute cache and
  * the optional stage profiler.  A per-device mutex serialises the enqueue
@@ -216,8 +218,10 @@ int mita_version(void);
  * group maxima), route (with the pre-threshold's selection as leading
  * blocks), landmark_scan (with step 4's prefix over the routing counts as
  * trailing blocks), landmark_merge (its first pass carries step 4's
- * scatter), expert_attend; each of route, landmark_scan and expert_attend
- * is a single kernel launch.  mita_profile_read() waits for the recorded events and
+ * scatter), expert_attend, and single_launch (bf16 heads of at most 256
+ * tokens run all five steps in one launch, one workgroup per head, with no
+ * work space; the other stages then record nothing); each of route,
+ * landmark_scan, expert_attend and single_launch is a single kernel launch.  mita_profile_read() waits for the recorded events and
  * returns, per stage, the summed milliseconds and the number of calls since
  * the last mita_profile_enable().  Not thread-safe: profile from one thread.
  *   mita_profile_enable(1) clears the sums and starts recording;

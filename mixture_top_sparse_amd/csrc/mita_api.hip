@@ -40,10 +40,12 @@ enum Stage {
   kStageScan,
   kStageMerge,
   kStageAttend,
+  kStageSmall,  // the one-launch path for short sequences (all five steps)
   kStageCount
 };
 const char* kStageNames[kStageCount] = {"pool",          "landmark_threshold", "route",
-                                        "landmark_scan", "landmark_merge",     "expert_attend"};
+                                        "landmark_scan", "landmark_merge",     "expert_attend",
+                                        "single_launch"};
 
 struct Profiler {
   bool enabled = false;
@@ -382,13 +384,17 @@ void derive(Shape& s, int cus) {
   // the t_e add up to at most tiles + m - 1, and each ceil adds at most
   // (tpb - 1) / tpb, so tiles / tpb + m bounds them
   s.attend_items = static_cast<int>(cdiv(tiles, tpb) + s.m);
-
+  s.small = small_path_fits(s);
 }
 
 }  // namespace
 
 size_t plan_workspace(const Shape& s, Workspace* ws, char* base) {
   size_t off = 0;
+  if (s.small) {  // the one-launch path keeps everything in LDS
+    *ws = Workspace{};
+    return 0;
+  }
   auto take = [&](size_t bytes) -> char* {
     char* p = base ? base + off : nullptr;
     off += (bytes + 255) / 256 * 256;
@@ -481,25 +487,42 @@ int forward_impl(const void* Q, const void* K, const void* V, int dtype, int64_t
     DeviceState* ds = device_state();
     if (ds == nullptr) return fail(MITA_ERR_HIP, "no current HIP device");
     std::lock_guard<std::mutex> lk(ds->mu);  // the whole enqueue sequence
-    void* base = nullptr;
-    DeviceState::Ws* entry = nullptr;
-    if (use_scratch) {
-      rc = scratch_for(*ds, &base);
-    } else {
-      rc = workspace_for(*ds, st, bytes, &base, &entry);
-    }
-    if (rc != MITA_OK) {
-      (void)hipGetLastError();
-      return rc;
-    }
-    plan_workspace(s, &ws, static_cast<char*>(base));
-    hipError_t e = hipSuccess;
-
     void* ql_copy = dbg ? dbg->ql : nullptr;
     float* vl_copy = dbg ? dbg->vl : nullptr;
     int32_t* perm_copy = dbg ? dbg->perm : nullptr;
     int32_t* off_copy = dbg ? dbg->offsets : nullptr;
     const bool inject_launch = inject && std::strcmp(inject, "launch") == 0;
+    void* base = nullptr;
+    DeviceState::Ws* entry = nullptr;
+    if (use_scratch) {
+      // looked up on the entry point's first call on this device, whichever
+      // path the call takes
+      rc = scratch_for(*ds, &base);
+      if (rc != MITA_OK) return rc;
+    }
+    if (s.small) {
+      // one launch, no work space (nothing to allocate, no event to record)
+      hipError_t e = inject_launch ? hipErrorLaunchFailure : hipSuccess;
+      if (e == hipSuccess) {
+        StageTimer t(kStageSmall, st, !use_scratch);
+        e = launch_small(s, Q, K, V, out, idx_out, route_out, ql_copy, vl_copy, perm_copy,
+                         off_copy, st);
+      }
+      if (!use_scratch && g_prof.enabled && e == hipSuccess) g_prof.calls += 1;
+      if (e != hipSuccess)
+        return fail(MITA_ERR_HIP, std::string("launch of stage single_launch failed: ") +
+                                      hipGetErrorString(e));
+      return MITA_OK;
+    }
+    if (!use_scratch) {
+      rc = workspace_for(*ds, st, bytes, &base, &entry);
+      if (rc != MITA_OK) {
+        (void)hipGetLastError();
+        return rc;
+      }
+    }
+    plan_workspace(s, &ws, static_cast<char*>(base));
+    hipError_t e = hipSuccess;
 
     const char* where = "pool";
     if (inject_launch) e = hipErrorLaunchFailure;

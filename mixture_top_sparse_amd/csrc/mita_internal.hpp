@@ -21,6 +21,7 @@ constexpr int kPoolChunk = 4096; // tokens per pooling partial sum (fewer, longe
 constexpr int kPoolDirectMax = 128;  // windows up to this many tokens: one-launch pooling
 constexpr int kThetaTilesPerBlock = 1;  // sample tiles per top-k pre-threshold block
 constexpr int kThetaMaxGroups = 4096;  // group maxima the pre-threshold selection holds (64 per lane)
+constexpr int kSmallMaxN = 256;  // bf16 heads up to this many tokens: one-launch path
 
 struct Shape {
   int64_t B = 0, H = 0, BH = 0, N = 0;
@@ -44,6 +45,7 @@ struct Shape {
   int nseg = 0;        // routing segments per head
   int attend_tpb = 0;   // 64-query tiles per expert-attention work item
   int attend_items = 0; // upper bound of work items per head
+  bool small = false;   // one launch, one workgroup per head, no work space
 };
 
 // Work space carved from one stream-ordered allocation.
@@ -94,6 +96,12 @@ hipError_t launch_route(const Shape& s, const void* Q, const Workspace& ws, int3
                         hipStream_t st);
 hipError_t launch_attend(const Shape& s, const void* Q, const void* K, const void* V,
                          const int32_t* idx, const Workspace& ws, float* out, hipStream_t st);
+// the whole forward pass in one launch for short bf16 sequences (one
+// workgroup per head, no work space); small_path_fits says when it applies
+bool small_path_fits(const Shape& s);
+hipError_t launch_small(const Shape& s, const void* Q, const void* K, const void* V, float* out,
+                        int32_t* idx_out, int32_t* route_out, void* ql_copy, float* vl_copy,
+                        int32_t* perm_copy, int32_t* off_copy, hipStream_t st);
 // dense attention over all N pairs (the baseline); bf16 only
 hipError_t launch_dense(int dtype, const void* Q, const void* K, const void* V, int64_t BH,
                         int64_t N, float scale, float* out, hipStream_t st);

@@ -150,7 +150,7 @@ def test_profiler_without_calls(L):
     mts.mita_profile_enable(True)
     ms, calls = mts.mita_profile_read()
     assert calls == 0 and list(ms) == ["pool", "landmark_threshold", "route", "landmark_scan",
-                                       "landmark_merge", "expert_attend"]
+                                       "landmark_merge", "expert_attend", "single_launch"]
     mts.mita_profile_enable(False)
 
 

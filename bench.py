@@ -288,6 +288,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="len_1m")
+    ap.add_argument("--experts-per-query", type=int, default=1, metavar="S",
+                    help="route each query to its S best landmarks (mita_forward_s; S > 1 is "
+                         "the several-experts reading, timed for context, not the metric)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dense", choices=["auto", "on", "off"], default="auto",
                     help="also time the hand-written dense (full) attention kernel on the same "
@@ -322,8 +325,15 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
 
-    def step():
-        return mts.mita_forward(Qt, Kt, Vt, m=w.m, k=w.k, grid=w.grid, scale=w.scale)
+    S = args.experts_per_query
+    if S == 1:
+        def step():
+            return mts.mita_forward(Qt, Kt, Vt, m=w.m, k=w.k, grid=w.grid, scale=w.scale)
+    else:
+        def step():
+            out, idx, routes = mts.mita_forward_s(Qt, Kt, Vt, m=w.m, k=w.k, s=S, grid=w.grid,
+                                                  scale=w.scale)
+            return out, idx, routes[..., 0]
 
     warm = device_warmup(args.device_warmup_ms)
     # The dense-attention baseline runs first (it is part of the report, and
@@ -397,7 +407,7 @@ def main() -> int:
         "dtype": w.dtype,
         "data": "synthetic (seeded Gaussian-mixture tokens; no dataset, no weights)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "m": w.m,
-                   "k": w.k, "grid": list(w.grid), "values": w.values, "centres": w.centres,
+                   "k": w.k, "s": S, "grid": list(w.grid), "values": w.values, "centres": w.centres,
                    "noise": w.noise, "seed": w.seed},
         # the metric's own fraction: algorithmic bytes of the whole step over
         # the step time, against the 8 TB/s peak
@@ -437,7 +447,7 @@ def main() -> int:
         line["dense_baseline"] = dense
     if args.copy_probe:
         line["copy_probe"] = copy_probe()
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and S == 1:
         line["cpu_baseline"] = cpu_baseline(w, Qt, Kt, Vt, out, idx, route)
     print(json.dumps(line), flush=True)
     return 0

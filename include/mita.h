@@ -144,6 +144,32 @@ int mita_forward_ex(const void* Q, const void* K, const void* V, int dtype, int6
                     void* stream, const mita_intermediates* dbg);
 
 /*
+ * mita_forward_s — MiTA with s experts per query.  The pages name the number
+ * s of experts a query is routed to and run their experiments with s = 1
+ * ["NeurIPS 2026 | Mixture-of-Top-k 注意力…", section "MiTA：用少量地标查询，
+ * 同时完成压缩与专家构造"]; for s > 1 they leave open how the experts are
+ * picked and combined.  Reading taken here: query q's experts are the s
+ * landmarks with the largest q.Ql[i], best first (ties: lower landmark
+ * index), and q attends with one softmax over the m compressed pairs and the
+ * k raw pairs of each of its experts — m + s*k pairs, a key held by two of
+ * its experts counted once per expert — which is what the Algorithm 1
+ * caption of "And attention is also FFN? …" computes (each expert attends
+ * its query subset, the parts combined by online softmax).
+ *
+ *   s          1 <= s <= m, s <= 8 in this build; s > 1 needs MITA_BF16
+ *              inputs and N*s < 2^31 (else MITA_ERR_UNSUPPORTED)
+ *   routes_out [B][H][N][s] int32: each query's experts, best first
+ *   the other arguments, pointer rules and errors as in mita_forward.
+ *
+ * s = 1 computes exactly what mita_forward computes.  For s > 1 the work
+ * space also holds one softmax partial per (query, expert): 264 bytes per
+ * token, head and expert.
+ */
+int mita_forward_s(const void* Q, const void* K, const void* V, int dtype, int64_t B, int64_t H,
+                   int64_t N, int64_t d, const mita_grid* grid, int64_t m, int64_t k, int64_t s,
+                   float scale, float* out, int32_t* idx_out, int32_t* routes_out, void* stream);
+
+/*
  * mita_forward_noalloc — mita_forward for callers that cannot allocate
  * device memory: code being captured into a HIP graph, tight serving loops,
  * harnesses that forbid hipMalloc.  It computes exactly what mita_forward

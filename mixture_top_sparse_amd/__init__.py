@@ -16,6 +16,7 @@ __all__ = [
     "mita_forward",
     "mita_forward_ex",
     "mita_forward_noalloc",
+    "mita_forward_s",
     "mita_dense_attention",
     "mita_release_workspace",
     "mita_status_string",
@@ -75,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.mita_forward_ex.restype = ctypes.c_int
         L.mita_forward_noalloc.argtypes = _FWD_ARGS
         L.mita_forward_noalloc.restype = ctypes.c_int
+        L.mita_forward_s.argtypes = _FWD_ARGS[:11] + [ctypes.c_int64] + _FWD_ARGS[11:]
+        L.mita_forward_s.restype = ctypes.c_int
         L.mita_dense_attention.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
                                            ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
@@ -196,6 +199,29 @@ def mita_forward_noalloc(Q, K, V, *, m: int, k: int, grid=None, scale=None):
     one GPU race; larger problems raise).  The outputs are still allocated
     here, by torch, before the call."""
     return _call(Q, K, V, m, k, grid, scale, want_dbg=False, noalloc=True)
+
+
+def mita_forward_s(Q, K, V, *, m: int, k: int, s: int, grid=None, scale=None):
+    """MiTA with s experts per query (bf16 inputs for s > 1).  Returns (out
+    [B,H,N,d] fp32, idx [B,H,m,k] int32, routes [B,H,N,s] int32, best first)."""
+    import torch
+
+    dt = _check_inputs(Q, K, V)
+    B, H, N, d = Q.shape
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    dev = Q.device
+    out = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, H, m, k), dtype=torch.int32, device=dev)
+    routes = torch.empty((B, H, N, s), dtype=torch.int32, device=dev)
+    g = None if grid is None else ctypes.byref(MitaGrid(*[int(x) for x in grid]))
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        _raise(lib().mita_forward_s(Q.data_ptr(), K.data_ptr(), V.data_ptr(), dt, B, H, N, d, g,
+                                    int(m), int(k), int(s), float(scale), out.data_ptr(),
+                                    idx.data_ptr(), routes.data_ptr(), stream),
+               "mita_forward_s")
+    return out, idx, routes
 
 
 def mita_dense_attention(Q, K, V, *, scale=None):

@@ -511,6 +511,183 @@ __global__ __launch_bounds__(256) void k_attend_f32(
   attend_f32<MPAD, KPAD>(S, Q, K, V, Ql, vl, idx, perm, N, m, k, c2, out, bh, ti);
 }
 
+// ---- several experts per query (s > 1, bf16) -------------------------------
+//
+// The work items run over the N*s (query, expert) assignments grouped by
+// expert (perm holds assignment indices a = q*s + j, j = the rank of the
+// expert among the query's s).  Each assignment gets one softmax partial
+// over its expert's k raw pairs, and over the m compressed pairs too when
+// j = 0 (the query's best expert), so that every query sees the compressed
+// pairs once and each of its experts' raw pairs once: m + s*k pairs in all,
+// a key shared by two of its experts counted once per expert — the
+// oracle's reading, which the Algorithm 1 caption of "And attention is also
+// FFN? …" gives (each expert's query subset attended separately, the parts
+// combined by online softmax).  Partials: the unnormalised P.V row, the
+// maximum logit (times log2 e * scale) and the weight sum; k_combine_s
+// merges a query's s partials.
+template <int MPAD, int KPAD>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k_attend_multi(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ Ql, const float* __restrict__ vl,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ perm,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ item_start, int tpb,
+    int64_t N, int s, int m, int k, float c2, float* __restrict__ pacc,
+    float* __restrict__ pstat) {
+  constexpr int NW = 2;
+  using L = AttendLds<BF16, MPAD, KPAD, NW>;
+  __shared__ L S;
+  const int64_t bh = blockIdx.y;
+  const int64_t NA = N * s;
+  TileInfo ti;
+  if (!find_item(item_start + bh * (m + 1), offsets + bh * (m + 1), m, tpb, blockIdx.x, ti))
+    return;
+  const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
+  const int nq = ti.qe - ti.qb;
+  if (nq <= 0) return;
+  stage_bf16<MPAD, KPAD, NW>(S, K, V, Ql, vl, idx + (bh * m + ti.e) * k, N, m, k, bh);
+  __syncthreads();
+  const uint16_t* Qh = Q + bh * N * kD;
+  constexpr int NPB = (MPAD + KPAD) / 16;
+  const int nsub = (nq + 15) / 16;
+  for (int sub = w; sub < nsub; sub += NW) {
+    const int slot = min(16 * sub + c16, nq - 1);  // slots past the item repeat its last
+    const int64_t a = perm[bh * NA + ti.qb + slot];
+    const int64_t q = a / s;
+    const bool with_compressed = (a % s) == 0;
+    bf16x8 qb[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      qb[t] = as_bf16x8(*reinterpret_cast<const u32x4*>(Qh + q * kD + 32 * t + 8 * g));
+    float x[NPB][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int pb = 0; pb < NPB; ++pb) {
+      f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8 kk = as_bf16x8(
+            *reinterpret_cast<const u32x4*>(S.pk + (16 * pb + c16) * L::PKST + 32 * t + 8 * g));
+        acc = mfma_bf16(kk, qb[t], acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int p = 16 * pb + 4 * g + r;
+        const bool valid = (p < MPAD) ? (p < m && with_compressed) : (p - MPAD < k);
+        x[pb][r] = valid ? acc[r] : -INFINITY;
+        mx = fmaxf(mx, x[pb][r]);
+      }
+    }
+    mx = xor_max(mx, 16);
+    mx = xor_max(mx, 32) * c2;
+    float lsum = 0.f;
+#pragma unroll
+    for (int pb = 0; pb < NPB; ++pb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        x[pb][r] = fast_exp2(fmaf(x[pb][r], c2, -mx));
+        lsum += x[pb][r];
+      }
+    lsum = xor_sum(lsum, 16);
+    lsum = xor_sum(lsum, 32);
+    f32x4 o[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[dt] = f32x4{0, 0, 0, 0};
+    auto p_split = [&](int pb0, bf16x8& hi, bf16x8& lo) {
+      const float p8[8] = {x[pb0][0],     x[pb0][1],     x[pb0][2],     x[pb0][3],
+                           x[pb0 + 1][0], x[pb0 + 1][1], x[pb0 + 1][2], x[pb0 + 1][3]};
+      split_hi_lo_pk(p8, hi, lo);
+    };
+    auto vt = [&](const uint16_t* row) {
+      return join_bf16x8(*reinterpret_cast<const u32x2*>(row),
+                         *reinterpret_cast<const u32x2*>(row + 16));
+    };
+#pragma unroll
+    for (int s2 = 0; s2 < MPAD / 32; ++s2) {
+      bf16x8 ph, pl;
+      p_split(2 * s2, ph, pl);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int off = (16 * dt + c16) * L::VCST + 32 * s2 + 4 * g;
+        const bf16x8 vh = vt(S.vch + off), vlo = vt(S.vcl + off);
+        o[dt] = mfma_bf16(vlo, ph, o[dt]);
+        o[dt] = mfma_bf16(vh, pl, o[dt]);
+        o[dt] = mfma_bf16(vh, ph, o[dt]);
+      }
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < KPAD / 32; ++s2) {
+      bf16x8 ph, pl;
+      p_split(MPAD / 16 + 2 * s2, ph, pl);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const bf16x8 vv = vt(S.vr + (16 * dt + c16) * L::VRST + 32 * s2 + 4 * g);
+        o[dt] = mfma_bf16(vv, pl, o[dt]);
+        o[dt] = mfma_bf16(vv, ph, o[dt]);
+      }
+    }
+    if (16 * sub + c16 < nq) {  // the assignment's partial (unnormalised)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        *reinterpret_cast<f32x4*>(pacc + (bh * NA + a) * kD + 16 * dt + 4 * g) = o[dt];
+      if (g == 0) {
+        pstat[(bh * NA + a) * 2] = mx;
+        pstat[(bh * NA + a) * 2 + 1] = lsum;
+      }
+    }
+  }
+}
+
+// Merge each query's s partials: with M the largest partial maximum,
+// out = sum_j 2^(m_j - M) acc_j / sum_j 2^(m_j - M) l_j.  Grid (ceil(N/16),
+// BH), 256 threads: 16 lanes per query, four features each.
+__global__ __launch_bounds__(256) void k_combine_s(const float* __restrict__ pacc,
+                                                  const float* __restrict__ pstat, int64_t N,
+                                                  int s, float* __restrict__ out) {
+  const int64_t bh = blockIdx.y;
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  const int f = (threadIdx.x & 15) * 4;
+  if (q >= N) return;
+  const int64_t NA = N * s;
+  float M = -INFINITY;
+  for (int j = 0; j < s; ++j) M = fmaxf(M, pstat[(bh * NA + q * s + j) * 2]);
+  float z = 0.f;
+  f32x4 acc = {0, 0, 0, 0};
+  for (int j = 0; j < s; ++j) {
+    const int64_t a = bh * NA + q * s + j;
+    const float wj = fast_exp2(pstat[a * 2] - M);
+    z += wj * pstat[a * 2 + 1];
+    acc += wj * *reinterpret_cast<const f32x4*>(pacc + a * kD + f);
+  }
+  *reinterpret_cast<f32x4*>(out + (bh * N + q) * kD + f) = acc * (1.0f / z);
+}
+
+template <int MPAD, int KPAD>
+static hipError_t launch_attend_multi_t(const Shape& s, const void* Q, const void* K,
+                                        const void* V, const int32_t* idx, const Workspace& ws,
+                                        float* out, hipStream_t st) {
+  auto kern = k_attend_multi<MPAD, KPAD>;
+  hipLaunchKernelGGL(kern, dim3(s.attend_items, s.BH), dim3(128), 0, st,
+                     static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
+                     static_cast<const uint16_t*>(V), static_cast<const uint16_t*>(ws.ql), ws.vl,
+                     idx, ws.perm, ws.offsets, ws.item_start, s.attend_tpb, s.N, s.s, s.m, s.k,
+                     s.scale * kLog2e, ws.pacc, ws.pstat);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_combine_s, dim3((s.N + 15) / 16, s.BH), dim3(256), 0, st, ws.pacc,
+                     ws.pstat, s.N, s.s, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_attend_multi(const Shape& s, const void* Q, const void* K, const void* V,
+                               const int32_t* idx, const Workspace& ws, float* out,
+                               hipStream_t st) {
+  if (s.dtype != 1) return hipErrorInvalidValue;
+  if (s.mpad == 32 && s.kpad == 32) return launch_attend_multi_t<32, 32>(s, Q, K, V, idx, ws, out, st);
+  if (s.mpad == 32) return launch_attend_multi_t<32, 64>(s, Q, K, V, idx, ws, out, st);
+  if (s.kpad == 32) return launch_attend_multi_t<64, 32>(s, Q, K, V, idx, ws, out, st);
+  return launch_attend_multi_t<64, 64>(s, Q, K, V, idx, ws, out, st);
+}
+
 template <class T, int MPAD, int KPAD, bool FULL, int NW>
 struct AttendKernel;
 template <int MPAD, int KPAD, bool FULL, int NW>

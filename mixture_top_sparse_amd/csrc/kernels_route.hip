@@ -234,6 +234,90 @@ __global__ __launch_bounds__(256) void k_route(const typename T::elem* __restric
                    qls);
 }
 
+// Several experts per query (s > 1, bf16): block (segment, head) covers
+// assignments seg * kRouteSeg + [0, kRouteSeg) of the head's flattened
+// [N][s] expert list, i.e. the queries whose assignments fall there.  A
+// query's s experts are its s largest logits q . Ql[i], best first, ties to
+// the lower landmark (s rounds of argmax, each dropping the landmark it took)
+// — the reading of the pages' several-experts-per-query routing that the
+// oracle's route_s follows ("Mixture-of-Top-k 注意力…", section "MiTA：用少量
+// 地标查询，同时完成压缩与专家构造", s experts per query; the experiments use
+// s = 1).  Only the assignments inside the segment are stored and counted
+// (expert-major counts per segment, as k_route's), so the counting sort of
+// step 4 runs over the N*s assignments unchanged.  Leading blocks: the
+// pre-threshold selection, as in k_route.
+template <int KPL>
+__global__ __launch_bounds__(256) void k_route_s(const uint16_t* __restrict__ Q,
+                                                const uint16_t* __restrict__ Ql, int64_t N, int m,
+                                                int s, int nseg, int32_t* __restrict__ routes,
+                                                int32_t* __restrict__ counts, int nsel,
+                                                const uint32_t* __restrict__ gmax, int k,
+                                                int groups, int mrows,
+                                                float* __restrict__ theta) {
+  using TR = RouteTraits<BF16>;
+  __shared__ int cnt[kMaxM];
+  __shared__ __attribute__((aligned(16))) uint16_t qls[kMaxM * kQlStride];
+  if constexpr (KPL > 0) {
+    if (static_cast<int>(blockIdx.x) < nsel) {  // whole block
+      const int lm = static_cast<int>(blockIdx.x) * 4 +
+                     __builtin_amdgcn_readfirstlane(wave_id());
+      if (lm < m) theta_select_wave<KPL>(gmax, m, k, groups, mrows, lm, blockIdx.y, theta);
+      return;
+    }
+  }
+  const int seg = static_cast<int>(blockIdx.x) - (KPL > 0 ? nsel : 0);
+  const int64_t bh = blockIdx.y;
+  const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
+  if (threadIdx.x < kMaxM) cnt[threadIdx.x] = 0;
+  stage_landmarks(Ql, m, bh, qls);
+  __syncthreads();
+  const int64_t NA = N * s;
+  const int64_t a0 = static_cast<int64_t>(seg) * kRouteSeg;
+  const int64_t a1 = a0 + kRouteSeg < NA ? a0 + kRouteSeg : NA;
+  const int64_t q0 = a0 / s, q1 = (a1 - 1) / s + 1;  // queries with an assignment here
+  const int mtiles = (m + 15) >> 4;
+  const uint16_t* Qh = Q + bh * N * kD;
+  for (int64_t qg = q0 + 16 * w; qg < q1; qg += 64) {  // 16 queries per wave and step
+    const int64_t q = qg + c16;
+    TR::QReg b;
+    TR::load_q(b, Qh + (q < N ? q : N - 1) * kD, true, g);
+    float v[4][4];  // logits of landmarks 16 mt + 4g + r
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x4 r4 = {0, 0, 0, 0};
+      if (mt < mtiles) r4 = TR::logits_lds(qls, mt, b, c16, g);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[mt][r] = (mt < mtiles && 16 * mt + 4 * g + r < m) ? r4[r] : -INFINITY;
+    }
+    for (int j = 0; j < s; ++j) {
+      float best = -INFINITY;
+      int bi = 0;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool better = v[mt][r] > best;  // increasing landmark order in the lane
+          best = better ? v[mt][r] : best;
+          bi = better ? 16 * mt + 4 * g + r : bi;
+        }
+      xor_argmax(best, bi, 16);
+      xor_argmax(best, bi, 32);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (16 * mt + 4 * g + r == bi) v[mt][r] = -INFINITY;  // taken
+      const int64_t a = q * s + j;
+      if (g == 0 && q < q1 && a >= a0 && a < a1) {
+        routes[bh * NA + a] = bi;
+        atomicAdd(&cnt[bi], 1);
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < m) counts[(bh * m + threadIdx.x) * nseg + seg] = cnt[threadIdx.x];
+}
+
 // The pre-threshold's group maxima of one 64-key tile of head bh (bf16), one
 // wave: the tile is scored against every landmark (operands from the LDS
 // copy of the landmark queries), and the maximum key of each group of GS
@@ -395,6 +479,31 @@ hipError_t launch_groups_bf16(const Shape& s, const void* K, const Workspace& ws
     launch_groups_gs<16, false>(s, K, ws, nth, st);
   else
     launch_groups_gs<64, false>(s, K, ws, nth, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_s(const Shape& s, const void* Q, const Workspace& ws, int32_t* routes,
+                          hipStream_t st) {
+  const uint16_t* Qp = static_cast<const uint16_t*>(Q);
+  const uint16_t* Qlp = static_cast<const uint16_t*>(ws.ql);
+  if (s.dtype != 1 || s.theta_groups > 64 * 64) return hipErrorInvalidValue;
+  const int nsel = s.theta_groups > 0 ? (s.m + 3) / 4 : 0;
+  const dim3 grid(nsel + s.nseg, s.BH);
+  if (nsel == 0)
+    hipLaunchKernelGGL((k_route_s<0>), grid, dim3(256), 0, st, Qp, Qlp, s.N, s.m, s.s, s.nseg,
+                       routes, ws.counts, 0, nullptr, s.k, 0, s.mrows, nullptr);
+  else if (s.theta_groups <= 64 * 4)
+    hipLaunchKernelGGL((k_route_s<4>), grid, dim3(256), 0, st, Qp, Qlp, s.N, s.m, s.s, s.nseg,
+                       routes, ws.counts, nsel, ws.gmax, s.k, s.theta_groups, s.mrows, ws.theta);
+  else if (s.theta_groups <= 64 * 16)
+    hipLaunchKernelGGL((k_route_s<16>), grid, dim3(256), 0, st, Qp, Qlp, s.N, s.m, s.s, s.nseg,
+                       routes, ws.counts, nsel, ws.gmax, s.k, s.theta_groups, s.mrows, ws.theta);
+  else if (s.theta_groups <= 64 * 32)
+    hipLaunchKernelGGL((k_route_s<32>), grid, dim3(256), 0, st, Qp, Qlp, s.N, s.m, s.s, s.nseg,
+                       routes, ws.counts, nsel, ws.gmax, s.k, s.theta_groups, s.mrows, ws.theta);
+  else
+    hipLaunchKernelGGL((k_route_s<64>), grid, dim3(256), 0, st, Qp, Qlp, s.N, s.m, s.s, s.nseg,
+                       routes, ws.counts, nsel, ws.gmax, s.k, s.theta_groups, s.mrows, ws.theta);
   return hipGetLastError();
 }
 

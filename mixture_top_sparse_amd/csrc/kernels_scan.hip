@@ -919,7 +919,7 @@ static BucketArgs bucket_args(const Shape& s, const int32_t* route, const Worksp
   a.nseg = s.nseg;
   a.tile = kAttendTile;
   a.tpb = s.attend_tpb;
-  a.N = s.N;
+  a.N = s.NA;  // the items sorted: queries, or (query, expert) assignments when s > 1
   return a;
 }
 

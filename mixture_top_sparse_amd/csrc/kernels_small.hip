@@ -573,7 +573,7 @@ static hipError_t launch_small_n(const Shape& s, const void* Q, const void* K, c
 }
 
 bool small_path_fits(const Shape& s) {
-  return s.dtype == 1 && s.N <= kSmallMaxN && s.m <= kMaxM && s.k <= kMaxK;
+  return s.dtype == 1 && s.s == 1 && s.N <= kSmallMaxN && s.m <= kMaxM && s.k <= kMaxK;
 }
 
 hipError_t launch_small(const Shape& s, const void* Q, const void* K, const void* V, float* out,

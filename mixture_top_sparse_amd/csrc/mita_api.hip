@@ -372,11 +372,12 @@ void derive(Shape& s, int cus) {
       s.theta_groups = static_cast<int>(ktiles);
     }
   }
-  s.nseg = static_cast<int>(cdiv(s.N, kRouteSeg));
+  s.NA = s.N * s.s;
+  s.nseg = static_cast<int>(cdiv(s.NA, kRouteSeg));
   // expert attention: work items of up to 16 tiles, keeping >= 2 items per CU
   // (fewer, larger items stage each expert less often: -4% to -7% per step
   // at long1d_16k and seg_32x32 against >= 4 items per CU; 8 was slower)
-  const int64_t tiles = cdiv(s.N, kAttendTile);
+  const int64_t tiles = cdiv(s.NA, kAttendTile);
   int64_t tpb = (tiles * s.BH) / (2 * static_cast<int64_t>(cus));
   tpb = tpb < 1 ? 1 : (tpb > kAttendMaxTpb ? kAttendMaxTpb : tpb);
   s.attend_tpb = static_cast<int>(tpb);
@@ -428,7 +429,11 @@ size_t plan_workspace(const Shape& s, Workspace* ws, char* base) {
   ws->totals = reinterpret_cast<int32_t*>(take(BH * s.m * 4));
   ws->offsets = reinterpret_cast<int32_t*>(take(BH * (s.m + 1) * 4));
   ws->item_start = reinterpret_cast<int32_t*>(take(BH * (s.m + 1) * 4));
-  ws->perm = reinterpret_cast<int32_t*>(take(BH * s.N * 4));
+  ws->perm = reinterpret_cast<int32_t*>(take(BH * s.NA * 4));
+  if (s.s > 1) {
+    ws->pacc = reinterpret_cast<float*>(take(BH * s.NA * kD * sizeof(float)));
+    ws->pstat = reinterpret_cast<float*>(take(BH * s.NA * 2 * sizeof(float)));
+  }
   return off;
 }
 
@@ -462,8 +467,8 @@ namespace {
 // use_scratch: take the device's static scratch array instead of a cached
 // stream-ordered block (no allocation of any kind).
 int forward_impl(const void* Q, const void* K, const void* V, int dtype, int64_t B, int64_t H,
-                 int64_t N, int64_t d, const mita_grid* grid, int64_t m, int64_t k, float scale,
-                 float* out, int32_t* idx_out, int32_t* route_out, void* stream,
+                 int64_t N, int64_t d, const mita_grid* grid, int64_t m, int64_t k, int64_t sx,
+                 float scale, float* out, int32_t* idx_out, int32_t* route_out, void* stream,
                  const mita_intermediates* dbg, bool use_scratch) {
   try {
     g_last_error.clear();
@@ -471,6 +476,13 @@ int forward_impl(const void* Q, const void* K, const void* V, int dtype, int64_t
     int rc = validate(Q, K, V, dtype, B, H, N, d, grid, m, k, scale, out, idx_out, route_out, dbg,
                       &s);
     if (rc != MITA_OK) return rc;
+    if (sx < 1 || sx > m) return fail(MITA_ERR_INVALID_ARG, "s must satisfy 1 <= s <= m");
+    if (sx > kMaxS) return fail(MITA_ERR_UNSUPPORTED, "s must be <= 8 in this build");
+    if (sx > 1 && dtype != MITA_BF16)
+      return fail(MITA_ERR_UNSUPPORTED, "s > 1 needs bfloat16 inputs in this build");
+    if (sx > 1 && N * sx >= (int64_t(1) << 31))
+      return fail(MITA_ERR_UNSUPPORTED, "N * s must be < 2^31");
+    s.s = static_cast<int>(sx);
     const char* inject = std::getenv("MITA_FAULT_INJECT");
     if (inject && std::strcmp(inject, "alloc") == 0)
       return fail(MITA_ERR_OOM, "work-space allocation failed (injected by MITA_FAULT_INJECT)");
@@ -545,7 +557,7 @@ int forward_impl(const void* Q, const void* K, const void* V, int dtype, int64_t
     if (e == hipSuccess) {
       where = "route";
       StageTimer t(kStageRoute, st, !use_scratch);
-      e = launch_route(s, Q, ws, route_out, st);
+      e = s.s > 1 ? launch_route_s(s, Q, ws, route_out, st) : launch_route(s, Q, ws, route_out, st);
     }
     if (e == hipSuccess) {
       where = "landmark_scan";
@@ -560,7 +572,8 @@ int forward_impl(const void* Q, const void* K, const void* V, int dtype, int64_t
     if (e == hipSuccess) {
       where = "expert_attend";
       StageTimer t(kStageAttend, st, !use_scratch);
-      e = launch_attend(s, Q, K, V, idx_out, ws, out, st);
+      e = s.s > 1 ? launch_attend_multi(s, Q, K, V, idx_out, ws, out, st)
+                  : launch_attend(s, Q, K, V, idx_out, ws, out, st);
     }
     if (!use_scratch && g_prof.enabled && e == hipSuccess) g_prof.calls += 1;
     if (entry != nullptr) {
@@ -588,15 +601,23 @@ int mita_forward_ex(const void* Q, const void* K, const void* V, int dtype, int6
                     int64_t N, int64_t d, const mita_grid* grid, int64_t m, int64_t k,
                     float scale, float* out, int32_t* idx_out, int32_t* route_out, void* stream,
                     const mita_intermediates* dbg) {
-  return forward_impl(Q, K, V, dtype, B, H, N, d, grid, m, k, scale, out, idx_out, route_out,
+  return forward_impl(Q, K, V, dtype, B, H, N, d, grid, m, k, 1, scale, out, idx_out, route_out,
                       stream, dbg, false);
+}
+
+int mita_forward_s(const void* Q, const void* K, const void* V, int dtype, int64_t B, int64_t H,
+                   int64_t N, int64_t d, const mita_grid* grid, int64_t m, int64_t k, int64_t s,
+                   float scale, float* out, int32_t* idx_out, int32_t* routes_out,
+                   void* stream) {
+  return forward_impl(Q, K, V, dtype, B, H, N, d, grid, m, k, s, scale, out, idx_out, routes_out,
+                      stream, nullptr, false);
 }
 
 int mita_forward_noalloc(const void* Q, const void* K, const void* V, int dtype, int64_t B,
                          int64_t H, int64_t N, int64_t d, const mita_grid* grid, int64_t m,
                          int64_t k, float scale, float* out, int32_t* idx_out,
                          int32_t* route_out, void* stream) {
-  return forward_impl(Q, K, V, dtype, B, H, N, d, grid, m, k, scale, out, idx_out, route_out,
+  return forward_impl(Q, K, V, dtype, B, H, N, d, grid, m, k, 1, scale, out, idx_out, route_out,
                       stream, nullptr, true);
 }
 

@@ -22,6 +22,7 @@ constexpr int kPoolDirectMax = 128;  // windows up to this many tokens: one-laun
 constexpr int kThetaTilesPerBlock = 1;  // sample tiles per top-k pre-threshold block
 constexpr int kThetaMaxGroups = 4096;  // group maxima the pre-threshold selection holds (64 per lane)
 constexpr int kSmallMaxN = 256;  // bf16 heads up to this many tokens: one-launch path
+constexpr int kMaxS = 8;         // experts per query, at most
 
 struct Shape {
   int64_t B = 0, H = 0, BH = 0, N = 0;
@@ -46,6 +47,8 @@ struct Shape {
   int attend_tpb = 0;   // 64-query tiles per expert-attention work item
   int attend_items = 0; // upper bound of work items per head
   bool small = false;   // one launch, one workgroup per head, no work space
+  int s = 1;            // experts per query
+  int64_t NA = 0;       // (query, expert) assignments per head: N * s
 };
 
 // Work space carved from one stream-ordered allocation.
@@ -69,7 +72,9 @@ struct Workspace {
   int32_t* totals = nullptr;     // [BH][m] routed queries per expert
   int32_t* offsets = nullptr;    // [BH][m+1]
   int32_t* item_start = nullptr; // [BH][m+1] first attention work item of each expert
-  int32_t* perm = nullptr;       // [BH][N]
+  int32_t* perm = nullptr;       // [BH][NA] queries (s > 1: assignments q*s + j) by expert
+  float* pacc = nullptr;         // s > 1: [BH][NA][64] unnormalised P.V per assignment
+  float* pstat = nullptr;        // s > 1: [BH][NA][2] (maximum logit in log2 units, weight sum)
 };
 
 size_t plan_workspace(const Shape& s, Workspace* ws, char* base);
@@ -96,6 +101,14 @@ hipError_t launch_route(const Shape& s, const void* Q, const Workspace& ws, int3
                         hipStream_t st);
 hipError_t launch_attend(const Shape& s, const void* Q, const void* K, const void* V,
                          const int32_t* idx, const Workspace& ws, float* out, hipStream_t st);
+// several experts per query (s > 1, bf16): top-s routing over the flattened
+// [N][s] assignments (with the pre-threshold's selection as leading blocks),
+// and the attention's per-assignment partials merged per query
+hipError_t launch_route_s(const Shape& s, const void* Q, const Workspace& ws, int32_t* routes,
+                          hipStream_t st);
+hipError_t launch_attend_multi(const Shape& s, const void* Q, const void* K, const void* V,
+                               const int32_t* idx, const Workspace& ws, float* out,
+                               hipStream_t st);
 // the whole forward pass in one launch for short bf16 sequences (one
 // workgroup per head, no work space); small_path_fits says when it applies
 bool small_path_fits(const Shape& s);

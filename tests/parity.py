@@ -179,3 +179,68 @@ def check_head(w, Qh, Kh, Vh, g, rep: Report, qsel=None, exact_ties=False):
     if not err <= tol:
         rep.fail(f"output max err {err:.3e} > {tol}")
     return rep
+
+
+def check_head_s(w, Qh, Kh, Vh, g, s, rep: Report, qsel=None):
+    """One head of a forward with s experts per query (g: out [N, d], idx
+    [m, k], routes [N, s] of the GPU).  Experts as in check_head.  Routes:
+    each query's list equals the oracle's (route_s), or differs only where
+    the oracle's sorted logits are near-tied: the GPU's j-th choice must then
+    score within the band of the oracle's j-th best (counted as a routing
+    near-tie).  Outputs: the oracle's output_s re-run with the GPU's experts
+    and routes, within the tolerance."""
+    tol = TOL[w.dtype]
+    N, d = Qh.shape
+    m, k = w.m, w.k
+    rmode = O.ROUND_BF16 if w.dtype == "bf16" else O.ROUND_F32
+    rep.heads += 1
+    ql = O.pool(Qh, *w.grid, rmode)
+    idx_o, gap = O.topk(ql, Kh, k, with_gap=True)
+    rep.experts_checked += m
+    for i in range(m):
+        if np.array_equal(idx_o[i], g["idx"][i]):
+            continue
+        thr = near_tie_threshold(gap[i, 0], gap[i, 1], gap[i, 2], gap[i, 3], d)
+        if not (gap[i, 0] - gap[i, 1] < thr):
+            rep.fail(f"expert {i}: index set differs without a near-tie")
+            continue
+        if np.min(Kh[g["idx"][i]] @ ql[i]) < gap[i, 0] - thr:
+            rep.fail(f"expert {i}: GPU picked a key below the near-tie band")
+            continue
+        rep.topk_near_ties += 1
+    vl = O.landmark_values(ql, Kh, Vh, w.scale)
+    qs = np.arange(N) if qsel is None else np.asarray(qsel)
+    r_o = O.route_s(Qh, ql, s, qsel=qs)
+    r_g = g["routes"][qs]
+    if np.any((r_g < 0) | (r_g >= m)):
+        rep.fail("route out of range")
+        return rep
+    for jq in np.nonzero(np.any(r_o != r_g, axis=1))[0]:
+        q = qs[jq]
+        if len(set(r_g[jq].tolist())) != s:
+            rep.fail(f"query {q}: repeated expert in {r_g[jq]}")
+            continue
+        R = Qh[q] @ ql.T
+        A = np.abs(Qh[q][None, :] * ql).sum(1)
+        order = r_o[jq]
+        ok = True
+        for j in range(s):
+            if r_g[jq, j] == order[j]:
+                continue
+            # the oracle's j-th and the next best logit must be near-tied,
+            # and the GPU's choice must score within that band
+            nxt = np.sort(R)[::-1][j + 1] if j + 1 < m else -np.inf
+            thr = near_tie_threshold(R[order[j]], nxt, A[order[j]], A.max(), d)
+            if not (R[order[j]] - nxt < thr and R[r_g[jq, j]] >= R[order[j]] - thr):
+                ok = False
+        if ok:
+            rep.route_near_ties += 1
+        else:
+            rep.fail(f"query {q}: routes {r_g[jq]} vs oracle {order} without a near-tie")
+    out_o = O.output_s(Qh, Kh, Vh, ql, vl, g["idx"], g["routes"], w.scale, qsel=qs)
+    err = float(np.max(np.abs(out_o - g["out"][qs])))
+    rep.out_max_err = max(rep.out_max_err, err)
+    rep.queries_checked += len(qs)
+    if not err <= tol:
+        rep.fail(f"output max err {err:.3e} > {tol}")
+    return rep

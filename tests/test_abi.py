@@ -132,6 +132,27 @@ def test_noalloc_rejects_work_space_beyond_scratch(L):
     assert "scratch" in msg and str(64 << 20) in msg
 
 
+def call_s(L, s, **over):
+    a = dict(Q=A, K=A, V=A, dtype=1, B=2, H=3, N=4096, d=64, grid=None, m=64, k=64, scale=0.125,
+             out=A, idx=A, route=A, stream=None)
+    a.update(over)
+    return L.mita_forward_s(a["Q"], a["K"], a["V"], a["dtype"], a["B"], a["H"], a["N"], a["d"],
+                            None, a["m"], a["k"], s, a["scale"], a["out"], a["idx"], a["route"],
+                            a["stream"])
+
+
+@pytest.mark.parametrize("s, over, want", [
+    (0, {}, "invalid"), (65, {}, "invalid"), (3, dict(m=2), "invalid"),
+    (9, {}, "unsupported"), (2, dict(dtype=0), "unsupported"),
+    (2, dict(Q=None), "invalid"), (2, dict(scale=-1.0), "invalid")])
+def test_forward_s_argument_checks(L, s, over, want):
+    """mita_forward_s validates s (1 <= s <= m, s <= 8, bf16 for s > 1) and
+    every other argument as mita_forward does, before any HIP call."""
+    code = mts.MITA_ERR_INVALID_ARG if want == "invalid" else mts.MITA_ERR_UNSUPPORTED
+    assert call_s(L, s, **over) == code
+    assert mts.mita_last_error() != ""
+
+
 def test_injected_allocation_failure(L, monkeypatch):
     monkeypatch.setenv("MITA_FAULT_INJECT", "alloc")
     assert call(L) == mts.MITA_ERR_OOM

@@ -206,7 +206,7 @@ int mita_forward_noalloc(const void* Q, const void* K, const void* V, int dtype,
  *   Q, K, V    [B][H][N][d] bfloat16 (MITA_BF16 only in this build;
  *              MITA_F32 gives MITA_ERR_UNSUPPORTED)
  *   B, H, N    >= 1, N < 2^31, B*H <= 65535, B*H*N*d < 2^40
- *   d          64 only in this build
+ *   d          64 or 128 in this build (others: MITA_ERR_UNSUPPORTED)
  *   scale      finite and > 0
  *   out        [B][H][N][d] fp32, fully overwritten
  *

@@ -171,9 +171,187 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   }
 }
 
+// ---- head dimension 128 ------------------------------------------------
+//
+// The same kernel for d = 128 (the embedding width of the pages' long-sequence
+// throughput model, "Mixture-of-Top-k 注意力…", section "长序列建模：实际运行
+// 时间也能明显缩短"): each 64-key tile is staged as two halves of 64 features
+// (four 8 KiB pieces: K and V, features 0-63 and 64-127, each in the scan's
+// swizzled 128-byte-row layout), scores take four 32-wide MFMA steps and
+// P.V eight 16-feature output blocks.  Twice the MFMA work per exp of the
+// d = 64 kernel.
+constexpr int kD2 = 128;
+
+// wave w's pieces of the K and V tile halves at key t0 (rows of 256 bytes in
+// HBM; half h = features 64h..64h+63); rows past N re-read row N - 1
+__device__ __forceinline__ void stage_tile_bf16_d128(const uint16_t* __restrict__ Kh,
+                                                     const uint16_t* __restrict__ Vh, int64_t t0,
+                                                     int64_t N, uint32_t buf, int w, int l) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    int r = 16 * w + 8 * j + (l >> 3);
+    const int c = (l & 7) ^ ((r >> 1) & 7);
+    if (t0 + r >= N) r = static_cast<int>(N - 1 - t0);  // ragged last tile
+    const uint32_t p = 2048u * static_cast<uint32_t>(w) + 1024u * j;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint16_t* src = Kh + (t0 + r) * kD2 + 64 * h + 8 * c;
+      dma16_to_lds<false>(src, buf + 8192u * h + p);                 // K half h
+      dma16_to_lds<false>(Vh + (t0 + r) * kD2 + 64 * h + 8 * c, buf + 16384u + 8192u * h + p);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_dense_bf16_d128(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, int64_t N, float c2, float* __restrict__ out) {
+  // per stage: K half 0, K half 1, V half 0, V half 1 (8 KiB each)
+  __shared__ __attribute__((aligned(16))) uint8_t b0[32768];
+  __shared__ __attribute__((aligned(16))) uint8_t b1[32768];
+  const int l = lane_id(), g = l >> 4, c16 = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(wave_id());
+  const int64_t bh = blockIdx.y;
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * 64 + 16 * w + c16;
+  const uint16_t* Kh = K + bh * N * kD2;
+  const uint16_t* Vh = V + bh * N * kD2;
+  const int ntiles = static_cast<int>((N + kTileKeys - 1) / kTileKeys);
+  bf16x8 qv[4];  // features 32s + 8g .. +7
+  {
+    const uint16_t* qr = Q + (bh * N + (q < N ? q : N - 1)) * kD2;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      qv[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qr + 32 * s + 8 * g));
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __asm__ volatile("" ::: "memory");
+  const uint32_t a0 = lds_address(b0), a1 = lds_address(b1);
+  stage_tile_bf16_d128(Kh, Vh, 0, N, a0, w, l);
+
+  float M = -INFINITY, Lsum = 0.f;
+  f32x4 acc[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4{0, 0, 0, 0};
+  const int kq0 = tile_off(c16, g), kq1 = tile_off(c16, 4 + g);
+  int voff[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+    voff[dt] = tile_off(4 * g + (c16 >> 2), 2 * dt + ((c16 & 3) >> 1)) + ((c16 & 1) << 3);
+
+  auto compute_tile = [&](const uint8_t* buf, int64_t t0) __attribute__((always_inline)) {
+    float sc[4][4];
+    {
+      f32x4 a[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) a[kb] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint8_t* kl = buf + 8192 * h;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          a[kb] = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(kl + kq0 + 2048 * kb)),
+                            qv[2 * h], a[kb]);
+          a[kb] = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(kl + kq1 + 2048 * kb)),
+                            qv[2 * h + 1], a[kb]);
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[kb][r] = a[kb][r];
+    }
+    if (t0 + kTileKeys > N) {
+      __asm__ volatile("" ::: "memory");
+      const int rel = static_cast<int>(N - t0) - 4 * g;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (16 * kb + r >= rel) sc[kb][r] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      mx = fmax_nc(mx, fmax_nc(fmax_nc(sc[kb][0], sc[kb][1]), fmax_nc(sc[kb][2], sc[kb][3])));
+    mx = xor_max(mx, 16);
+    mx = xor_max(mx, 32) * c2;
+    if (ballot(mx > M)) {
+      const float Mn = fmaxf(M, mx);
+      const float alpha = fast_exp2(M - Mn);
+      Lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) acc[dt] *= alpha;
+      M = Mn;
+    }
+    float p[4][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[kb][r] = fast_exp2(fmaf(sc[kb][r], c2, -M));
+        Lsum += p[kb][r];
+      }
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      float pp[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pp[r] = p[2 * s2][r];
+        pp[4 + r] = p[2 * s2 + 1][r];
+      }
+      bf16x8 hi, lo;
+      split_hi_lo_pk(pp, hi, lo);  // P in bf16 (the residual is not used)
+      (void)lo;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint8_t* vl = buf + 16384 + 8192 * h;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16*)(vl + voff[dt] + 4096 * s2));
+          const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16*)(vl + voff[dt] + 4096 * s2 + 2048));
+          const bf16x8 va =
+              __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[4 * h + dt] = mfma_bf16(va, hi, acc[4 * h + dt]);
+        }
+      }
+    }
+  };
+
+  auto step = [&](int it, const uint8_t* cur, uint32_t nxt) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    const int64_t t0 = static_cast<int64_t>(it) * kTileKeys;
+    if (it + 1 < ntiles) stage_tile_bf16_d128(Kh, Vh, t0 + kTileKeys, N, nxt, w, l);
+    compute_tile(cur, t0);
+  };
+  for (int it = 0; it < ntiles; it += 2) {
+    step(it, b0, a1);
+    if (it + 1 >= ntiles) break;
+    step(it + 1, b1, a0);
+  }
+  Lsum = xor_sum(Lsum, 16);
+  Lsum = xor_sum(Lsum, 32);
+  if (q < N) {
+    const float f = 1.0f / Lsum;
+    float* o = out + (bh * N + q) * kD2;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      *reinterpret_cast<f32x4*>(o + 16 * dt + 4 * g) = acc[dt] * f;
+  }
+}
+
 hipError_t launch_dense(int dtype, const void* Q, const void* K, const void* V, int64_t BH,
-                        int64_t N, float scale, float* out, hipStream_t st) {
+                        int64_t N, int64_t d, float scale, float* out, hipStream_t st) {
   if (dtype != 1) return hipErrorInvalidValue;  // bf16 only
+  if (d == kD2) {
+    hipLaunchKernelGGL(k_dense_bf16_d128, dim3((N + 63) / 64, BH), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
+                       static_cast<const uint16_t*>(V), N, scale * kLog2e, out);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_dense_bf16, dim3((N + 63) / 64, BH), dim3(256), 0, st,
                      static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
                      static_cast<const uint16_t*>(V), N, scale * kLog2e, out);

@@ -640,14 +640,15 @@ int mita_dense_attention(const void* Q, const void* K, const void* V, int dtype,
     if (B * H > 65535) return fail(MITA_ERR_UNSUPPORTED, "B*H must be <= 65535 in this build");
     if (dtype != MITA_BF16)
       return fail(MITA_ERR_UNSUPPORTED, "the dense baseline supports bf16 inputs only");
-    if (d != kD) return fail(MITA_ERR_UNSUPPORTED, "only d == 64 is supported in this build");
-    if (B * H * N > (int64_t(1) << 40) / kD)
+    if (d != kD && d != 2 * kD)
+      return fail(MITA_ERR_UNSUPPORTED, "the dense baseline supports d == 64 and d == 128");
+    if (B * H * N > (int64_t(1) << 40) / d)
       return fail(MITA_ERR_INVALID_ARG, "B*H*N*d must be < 2^40");
     if (!(scale > 0.0f) || !std::isfinite(scale))
       return fail(MITA_ERR_INVALID_ARG, "scale must be finite and > 0");
     for (const void* p : {Q, K, V, static_cast<const void*>(out)})
       if (!aligned16(p)) return fail(MITA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
-    const hipError_t e = launch_dense(dtype, Q, K, V, B * H, N, scale, out,
+    const hipError_t e = launch_dense(dtype, Q, K, V, B * H, N, d, scale, out,
                                       static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
       return fail(MITA_ERR_HIP, std::string("launch of the dense kernel failed: ") +

@@ -117,6 +117,6 @@ hipError_t launch_small(const Shape& s, const void* Q, const void* K, const void
                         int32_t* perm_copy, int32_t* off_copy, hipStream_t st);
 // dense attention over all N pairs (the baseline); bf16 only
 hipError_t launch_dense(int dtype, const void* Q, const void* K, const void* V, int64_t BH,
-                        int64_t N, float scale, float* out, hipStream_t st);
+                        int64_t N, int64_t d, float scale, float* out, hipStream_t st);
 
 }  // namespace mita

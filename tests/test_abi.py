@@ -198,7 +198,7 @@ DENSE_INVALID = {
 
 DENSE_UNSUPPORTED = {
     "f32": dict(dtype=0),
-    "d_128": dict(d=128),
+    "d_96": dict(d=96),
     "too_many_heads": dict(B=300, H=300),
 }
 

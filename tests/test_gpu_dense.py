@@ -36,12 +36,17 @@ def _gpu():
 
 
 CASES = {
-    # name: (workload the inputs are drawn from, B, H, N, queries checked or None = all)
-    "one_key": ("long1d_16k", 1, 1, 1, None),
-    "ragged_300": ("seg_40x40", 1, 2, 300, None),
-    "mixture_4096": ("long1d_16k", 1, 2, 4096, None),
-    "iid_196_batch": ("deit_s_14x14", 2, 3, 196, None),
-    "len_64k_sampled": ("len_64k", 1, 1, 65536, 256),
+    # name: (workload the inputs are drawn from, B, H, N, queries checked or None = all, d)
+    "one_key": ("long1d_16k", 1, 1, 1, None, 64),
+    "ragged_300": ("seg_40x40", 1, 2, 300, None, 64),
+    "mixture_4096": ("long1d_16k", 1, 2, 4096, None, 64),
+    "iid_196_batch": ("deit_s_14x14", 2, 3, 196, None, 64),
+    "len_64k_sampled": ("len_64k", 1, 1, 65536, 256, 64),
+    # head dimension 128 (the pages' long-sequence throughput model width)
+    "d128_one_key": ("long1d_16k", 1, 1, 1, None, 128),
+    "d128_ragged_300": ("seg_40x40", 1, 2, 300, None, 128),
+    "d128_mixture_4096": ("long1d_16k", 1, 2, 4096, None, 128),
+    "d128_len_64k_sampled": ("len_64k", 1, 1, 65536, 256, 128),
 }
 
 
@@ -51,9 +56,9 @@ def test_dense_matches_oracle(name):
 
     import mixture_top_sparse_amd as mts
 
-    wname, B, H, N, nsample = CASES[name]
-    w = WORKLOADS[wname].with_(B=B, H=H, N=N, grid=(1, N, 1, 1), k=1)
-    _say(f"case {name}: inputs of {wname}, B={B} H={H} N={N} bf16")
+    wname, B, H, N, nsample, d = CASES[name]
+    w = WORKLOADS[wname].with_(B=B, H=H, N=N, d=d, grid=(1, N, 1, 1), k=1)
+    _say(f"case {name}: inputs of {wname}, B={B} H={H} N={N} d={d} bf16")
     Q, K, V = generate(w)
     Qt, Kt, Vt = to_torch((Q, K, V), "bf16", "cuda")
     out = mts.mita_dense_attention(Qt, Kt, Vt, scale=w.scale)

@@ -26,4 +26,5 @@ from .oracle import (  # noqa: F401
     output_s,
     forward,
     dense,
+    backward,
 )

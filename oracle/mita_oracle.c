@@ -580,3 +580,132 @@ int mita_oracle_forward(const double* Q, const double* K, const double* V, int64
   free(pm);
   return rc;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Backward pass (training): gradients of sum(dout * out) with respect to    */
+/* Q, K and V, the experts and routes held fixed                              */
+/* ------------------------------------------------------------------------ */
+
+int mita_oracle_backward(const double* Q, const double* K, const double* V, int64_t N,
+                         int64_t d, int64_t gh, int64_t gw, int64_t mh, int64_t mw, int64_t k,
+                         double scale, int round_mode, const int32_t* idx, const int32_t* route,
+                         const double* dout, double* dQ, double* dK, double* dV) {
+  const int64_t m = mh * mw;
+  if (!Q || !K || !V || !idx || !route || !dout || !dQ || !dK || !dV) return -1;
+  if (N < 1 || d < 1 || m < 1 || m > N || k < 1 || k > N) return -1;
+  if (!(scale > 0.0) || isinf(scale)) return -1;
+  double* Ql = (double*)calloc((size_t)(m * d), sizeof(double));
+  double* Vl = (double*)calloc((size_t)(m * d), sizeof(double));
+  double* dQl = (double*)calloc((size_t)(m * d), sizeof(double));
+  double* dVl = (double*)calloc((size_t)(m * d), sizeof(double));
+  double* w = (double*)malloc((size_t)((m + k > N ? m + k : N) * 2) * sizeof(double));
+  int rc = (Ql && Vl && dQl && dVl && w) ? 0 : -2;
+  /* the forward's landmark queries and values (the same functions as the
+   * forward pass; the rounding of Ql is taken as the identity below) */
+  if (rc == 0) rc = mita_oracle_pool(Q, N, d, gh, gw, mh, mw, round_mode, Ql);
+  if (rc == 0) rc = mita_oracle_landmark_values(Ql, K, V, N, d, m, scale, Vl);
+  if (rc == 0) {
+    for (int64_t i = 0; i < N * d; ++i) dQ[i] = dK[i] = dV[i] = 0.0;
+    double* dw = w + (m + k > N ? m + k : N);
+    /* 1. the output softmax of each query over its m + k pairs */
+    for (int64_t q = 0; q < N && rc == 0; ++q) {
+      const int64_t e = route[q];
+      if (e < 0 || e >= m) {
+        rc = -1;
+        break;
+      }
+      const int32_t* ex = idx + e * k;
+      const double* qq = Q + q * d;
+      const double* G = dout + q * d;
+      double mx = -INFINITY;
+      for (int64_t i = 0; i < m; ++i) {
+        w[i] = scale * dot(qq, Ql + i * d, d);
+        if (w[i] > mx) mx = w[i];
+      }
+      for (int64_t j = 0; j < k; ++j) {
+        w[m + j] = scale * dot(qq, K + (int64_t)ex[j] * d, d);
+        if (w[m + j] > mx) mx = w[m + j];
+      }
+      double z = 0.0;
+      for (int64_t i = 0; i < m + k; ++i) {
+        w[i] = exp(w[i] - mx);
+        z += w[i];
+      }
+      for (int64_t i = 0; i < m + k; ++i) w[i] /= z; /* the softmax weights */
+      /* dw: the gradient of each weight (dout . its value) */
+      double c = 0.0;
+      for (int64_t i = 0; i < m; ++i) {
+        dw[i] = dot(G, Vl + i * d, d);
+        c += w[i] * dw[i];
+      }
+      for (int64_t j = 0; j < k; ++j) {
+        dw[m + j] = dot(G, V + (int64_t)ex[j] * d, d);
+        c += w[m + j] * dw[m + j];
+      }
+      /* through the softmax to the logits, then to the dot products */
+      for (int64_t i = 0; i < m; ++i) {
+        const double g = scale * w[i] * (dw[i] - c);
+        for (int64_t a = 0; a < d; ++a) {
+          dQ[q * d + a] += g * Ql[i * d + a];
+          dQl[i * d + a] += g * qq[a];
+          dVl[i * d + a] += w[i] * G[a];
+        }
+      }
+      for (int64_t j = 0; j < k; ++j) {
+        const int64_t t = ex[j];
+        const double g = scale * w[m + j] * (dw[m + j] - c);
+        for (int64_t a = 0; a < d; ++a) {
+          dQ[q * d + a] += g * K[t * d + a];
+          dK[t * d + a] += g * qq[a];
+          dV[t * d + a] += w[m + j] * G[a];
+        }
+      }
+    }
+    /* 2. the landmarks' cross-attention over all N keys (Vl = softmax(scale
+     *    Ql K^T) V) */
+    for (int64_t i = 0; i < m && rc == 0; ++i) {
+      double mx = -INFINITY;
+      for (int64_t t = 0; t < N; ++t) {
+        w[t] = scale * dot(Ql + i * d, K + t * d, d);
+        if (w[t] > mx) mx = w[t];
+      }
+      double z = 0.0;
+      for (int64_t t = 0; t < N; ++t) {
+        w[t] = exp(w[t] - mx);
+        z += w[t];
+      }
+      double c = 0.0;
+      for (int64_t t = 0; t < N; ++t) {
+        w[t] /= z;
+        dw[t] = dot(dVl + i * d, V + t * d, d);
+        c += w[t] * dw[t];
+      }
+      for (int64_t t = 0; t < N; ++t) {
+        const double g = scale * w[t] * (dw[t] - c);
+        for (int64_t a = 0; a < d; ++a) {
+          dQl[i * d + a] += g * K[t * d + a];
+          dK[t * d + a] += g * Ql[i * d + a];
+          dV[t * d + a] += w[t] * dVl[i * d + a];
+        }
+      }
+    }
+    /* 3. the pooling: Ql[i] is the mean of Q over window i */
+    for (int64_t i = 0; i < m && rc == 0; ++i) {
+      int64_t r0, r1, c0, c1;
+      rc = mita_oracle_window(gh, gw, mh, mw, i, &r0, &r1, &c0, &c1);
+      if (rc != 0) break;
+      const double cnt = (double)((r1 - r0) * (c1 - c0));
+      for (int64_t r = r0; r < r1; ++r)
+        for (int64_t cc = c0; cc < c1; ++cc) {
+          const int64_t t = r * gw + cc;
+          for (int64_t a = 0; a < d; ++a) dQ[t * d + a] += dQl[i * d + a] / cnt;
+        }
+    }
+  }
+  free(Ql);
+  free(Vl);
+  free(dQl);
+  free(dVl);
+  free(w);
+  return rc;
+}

@@ -164,6 +164,22 @@ int mita_oracle_output_s(const double* Q, const double* K, const double* V, cons
 int mita_oracle_dense(const double* Q, const double* K, const double* V, int64_t N, int64_t d,
                       double scale, const int64_t* qsel, int64_t nq, double* out);
 
+/* Backward pass (training; the pages' wall-clock results are training times:
+ * [P1] section "长序列建模：训练时间从10.6小时降至2.4小时"): given dout [N][d],
+ * the gradients dQ, dK, dV [N][d] of sum(dout * out) for one (batch, head),
+ * out being the forward output with the experts idx [m][k] and routes [N]
+ * held fixed (selections carry no gradient) and the rounding of the landmark
+ * queries into the input type taken as the identity.  Three parts, in the
+ * forward's reverse order: the output softmax of every query over its m + k
+ * pairs (into dQ, dK, dV and the landmarks' dQl, dVl), the landmarks'
+ * cross-attention over all N keys (into dQl, dK, dV), and the pooling (dQl
+ * spread back over each window, divided by its size, into dQ).  Straight
+ * loops, fp64. */
+int mita_oracle_backward(const double* Q, const double* K, const double* V, int64_t N,
+                         int64_t d, int64_t gh, int64_t gw, int64_t mh, int64_t mw, int64_t k,
+                         double scale, int round_mode, const int32_t* idx, const int32_t* route,
+                         const double* dout, double* dQ, double* dK, double* dV);
+
 /* Number of OpenMP threads the oracle uses (for reporting). */
 int mita_oracle_threads(void);
 

@@ -65,6 +65,9 @@ def _load(path: str) -> ctypes.CDLL:
     L.mita_oracle_output_s.argtypes = [_f64p, _f64p, _f64p, _f64p, _f64p, _i32p, _i32p, _i64,
                                        _i64, _i64, _i64, _i64, ctypes.c_double, _i64p, _i64,
                                        _f64p]
+    L.mita_oracle_backward.argtypes = [_f64p, _f64p, _f64p, _i64, _i64, _i64, _i64, _i64, _i64,
+                                       _i64, ctypes.c_double, ctypes.c_int, _i32p, _i32p, _f64p,
+                                       _f64p, _f64p, _f64p]
     L.mita_oracle_threads.restype = ctypes.c_int
     return L
 
@@ -267,3 +270,20 @@ def forward(Q, K, V, grid: tuple[int, int, int, int], k: int, scale: float,
         _p(res["ql"], _f64p), _p(res["vl"], _f64p), _p(res["offsets"], _i32p),
         _p(res["perm"], _i32p)), "forward")
     return res
+
+
+def backward(Q, K, V, grid, k: int, scale: float, round_mode, idx, route_, dout):
+    """Gradients (dQ, dK, dV) of sum(dout * out) for one head, the experts
+    and routes held fixed (mita_oracle_backward)."""
+    Q, K, V, dout = _f64(Q), _f64(K), _f64(V), _f64(dout)
+    idx, r = _i32(idx), _i32(route_)
+    N, d = Q.shape
+    gh, gw, mh, mw = grid
+    dQ = np.empty((N, d), np.float64)
+    dK = np.empty((N, d), np.float64)
+    dV = np.empty((N, d), np.float64)
+    _check(lib().mita_oracle_backward(_p(Q, _f64p), _p(K, _f64p), _p(V, _f64p), N, d, gh, gw, mh,
+                                      mw, k, float(scale), int(round_mode), _p(idx, _i32p),
+                                      _p(r, _i32p), _p(dout, _f64p), _p(dQ, _f64p),
+                                      _p(dK, _f64p), _p(dV, _f64p)), "backward")
+    return dQ, dK, dV

@@ -692,4 +692,118 @@ def check_forward_composes_steps():
             np.testing.assert_array_equal(res["out"][b, h], out)
 
 
+# ---------------------------------------------------------------------------
+# backward pass (training): the experts and routes held fixed [P1 section
+# "长序列建模：训练时间从10.6小时降至2.4小时" — the pages' wall-clock results are
+# training times]
+# ---------------------------------------------------------------------------
+
+
+def _bw_case(rng, N, d, grid, k, scale):
+    Q, K, V = (rng.standard_normal((N, d)) for _ in range(3))
+    ql = O.pool(Q, *grid, O.ROUND_NONE)
+    idx = O.topk(ql, K, k)
+    r = O.route(Q, ql)
+    G = rng.standard_normal((N, d))
+    return Q, K, V, idx, r, G
+
+
+def _torch_forward_fixed(Q, K, V, grid, idx, r, scale):
+    """The forward written with torch's own operators (adaptive average
+    pooling, softmax, matmul) for autograd, with the experts and routes
+    given (not re-selected)."""
+    gh, gw, mh, mw = grid
+    N, d = Q.shape
+    ql = F.adaptive_avg_pool2d(Q.T.reshape(d, gh, gw), (mh, mw)).reshape(d, mh * mw).T
+    A = torch.softmax(scale * (ql @ K.T), dim=-1)
+    vl = A @ V
+    outs = []
+    for q in range(N):
+        ex = torch.as_tensor(idx[r[q]].astype(np.int64))
+        logits = scale * torch.cat([ql @ Q[q], K[ex] @ Q[q]])
+        w = torch.softmax(logits, dim=0)
+        outs.append(w[:ql.shape[0]] @ vl + w[ql.shape[0]:] @ V[ex])
+    return torch.stack(outs)
+
+
+def check_backward_vs_autograd():
+    """The hand-derived backward against torch autograd of the same forward
+    (fp64), on a 1D grid and an overlapping 2D grid (14x14 -> 5x5 bins)."""
+    rng = _rng(81)
+    for N, d, grid, k, scale in [(30, 8, (1, 30, 1, 5), 4, 0.35),
+                                 (196, 4, (14, 14, 5, 5), 6, 0.5)]:
+        Q, K, V, idx, r, G = _bw_case(rng, N, d, grid, k, scale)
+        dQ, dK, dV = O.backward(Q, K, V, grid, k, scale, O.ROUND_NONE, idx, r, G)
+        Qt, Kt, Vt = (torch.tensor(x, requires_grad=True) for x in (Q, K, V))
+        out = _torch_forward_fixed(Qt, Kt, Vt, grid, idx, r, scale)
+        # the torch forward is the oracle's forward (pinned elsewhere)
+        vl = O.landmark_values(O.pool(Q, *grid, O.ROUND_NONE), K, V, scale)
+        ref_out = O.output(Q, K, V, O.pool(Q, *grid, O.ROUND_NONE), vl, idx, r, scale)
+        np.testing.assert_allclose(out.detach().numpy(), ref_out, rtol=1e-11, atol=1e-12)
+        (out * torch.from_numpy(G)).sum().backward()
+        for got, t in ((dQ, Qt), (dK, Kt), (dV, Vt)):
+            np.testing.assert_allclose(got, t.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def check_backward_finite_differences():
+    """Central differences of sum(dout * out) through the oracle's own
+    forward steps (fixed experts and routes) on every entry of Q, K, V."""
+    rng = _rng(82)
+    N, d, grid, k, scale = 12, 3, (3, 4, 2, 2), 3, 0.7
+    Q, K, V, idx, r, G = _bw_case(rng, N, d, grid, k, scale)
+    dQ, dK, dV = O.backward(Q, K, V, grid, k, scale, O.ROUND_NONE, idx, r, G)
+
+    def loss(Q, K, V):
+        ql = O.pool(Q, *grid, O.ROUND_NONE)
+        vl = O.landmark_values(ql, K, V, scale)
+        return float((O.output(Q, K, V, ql, vl, idx, r, scale) * G).sum())
+
+    eps = 1e-6
+    for which, grad in ((0, dQ), (1, dK), (2, dV)):
+        for t in range(N):
+            for a in range(d):
+                args = [Q.copy(), K.copy(), V.copy()]
+                args[which][t, a] += eps
+                up = loss(*args)
+                args[which][t, a] -= 2 * eps
+                down = loss(*args)
+                fd = (up - down) / (2 * eps)
+                assert abs(fd - grad[t, a]) <= 1e-6 * (1 + abs(fd)), (which, t, a, fd, grad[t, a])
+
+
+def check_backward_invariants():
+    """Each output row is a convex combination of value rows (the landmark
+    values being convex combinations of V), so the value gradients sum to the
+    output gradients; the gradients are linear in dout; the rounding of the
+    landmark queries changes the point of evaluation, not the rule."""
+    rng = _rng(83)
+    N, d, grid, k, scale = 40, 6, (1, 40, 1, 6), 5, 0.4
+    Q, K, V, idx, r, G = _bw_case(rng, N, d, grid, k, scale)
+    dQ, dK, dV = O.backward(Q, K, V, grid, k, scale, O.ROUND_NONE, idx, r, G)
+    np.testing.assert_allclose(dV.sum(0), G.sum(0), rtol=1e-12, atol=1e-12)
+    d2 = O.backward(Q, K, V, grid, k, scale, O.ROUND_NONE, idx, r, -2.5 * G)
+    for a, b in zip((dQ, dK, dV), d2):
+        np.testing.assert_allclose(b, -2.5 * a, rtol=1e-12, atol=1e-13)
+    z = O.backward(Q, K, V, grid, k, scale, O.ROUND_NONE, idx, r, 0 * G)
+    assert all(np.all(t == 0) for t in z)
+    # bf16 rounding of Ql: the gradients are those at the rounded landmarks
+    Qb = np.vectorize(O.round_bf16)(Q)
+    b16 = O.backward(Qb, K, V, grid, k, scale, O.ROUND_BF16, idx, r, G)
+    Qt, Kt, Vt = (torch.tensor(x, requires_grad=True) for x in (Qb, K, V))
+    gh, gw, mh, mw = grid
+    ql = F.adaptive_avg_pool2d(Qt.T.reshape(d, gh, gw), (mh, mw)).reshape(d, mh * mw).T
+    qlr = torch.from_numpy(O.pool(Qb, *grid, O.ROUND_BF16))
+    ql = ql + (qlr - ql).detach()  # rounded values, identity derivative
+    A = torch.softmax(scale * (ql @ Kt.T), dim=-1)
+    vl = A @ Vt
+    outs = []
+    for q in range(N):
+        ex = torch.as_tensor(idx[r[q]].astype(np.int64))
+        w = torch.softmax(scale * torch.cat([ql @ Qt[q], Kt[ex] @ Qt[q]]), dim=0)
+        outs.append(w[:ql.shape[0]] @ vl + w[ql.shape[0]:] @ Vt[ex])
+    (torch.stack(outs) * torch.from_numpy(G)).sum().backward()
+    for got, t in zip(b16, (Qt, Kt, Vt)):
+        np.testing.assert_allclose(got, t.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
 ALL_CHECKS = [v for k_, v in sorted(globals().items()) if k_.startswith("check_")]

@@ -102,6 +102,19 @@ static int one_case(int64_t N, int64_t d, int64_t gh, int64_t gw, int64_t mh, in
     free(offs);
     free(perms);
   }
+  /* the backward pass with these experts and routes */
+  {
+    double* G = randn(N * d);
+    double* dQ = (double*)malloc((size_t)(N * d) * sizeof(double));
+    double* dK = (double*)malloc((size_t)(N * d) * sizeof(double));
+    double* dV = (double*)malloc((size_t)(N * d) * sizeof(double));
+    CHECK(mita_oracle_backward(Q, K, V, N, d, gh, gw, mh, mw, k, 0.125, round_mode, idx, route,
+                               G, dQ, dK, dV));
+    free(G);
+    free(dQ);
+    free(dK);
+    free(dV);
+  }
   (void)mita_oracle_round_bf16(3.14159);
   (void)mita_oracle_round_bf16(-1e-40);
   (void)mita_oracle_round_bf16(1e39);
@@ -125,6 +138,9 @@ int main(void) {
   /* argument errors are reported, not acted on */
   if (mita_oracle_topk(NULL, NULL, 0, 0, 0, 0, NULL, NULL) == 0) return 1;
   if (mita_oracle_pool(NULL, 1, 1, 1, 1, 2, 1, 0, NULL) == 0) return 1;
+  if (mita_oracle_backward(NULL, NULL, NULL, 1, 1, 1, 1, 1, 1, 1, 1.0, 0, NULL, NULL, NULL, NULL,
+                           NULL, NULL) == 0)
+    return 1;
   printf("oracle sanitize driver: ok (%d threads)\n", mita_oracle_threads());
   return 0;
 }

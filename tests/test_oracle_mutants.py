@@ -15,8 +15,8 @@ SRC = os.path.join(os.path.dirname(O.oracle.__file__), "mita_oracle.c")
 
 MUTANTS = {
     "pool_bin_end_floor": ("*r1 = ceil_div((a + 1) * gh, mh);", "*r1 = floor_div((a + 1) * gh, mh);"),
-    "pool_count_off_by_one": ("(double)((r1 - r0) * (c1 - c0));",
-                              "(double)((r1 - r0) * (c1 - c0) + 1);"),
+    "pool_count_off_by_one": ("count = (double)((r1 - r0) * (c1 - c0));",
+                              "count = (double)((r1 - r0) * (c1 - c0) + 1);"),
     "bf16_double_rounding": ("ldexp(nearbyint(ldexp(x, -q)), q);",
                              "ldexp(nearbyint(ldexp((double)(float)x, -q)), q);"),
     "bf16_ties_away": ("ldexp(nearbyint(ldexp(x, -q)), q);", "ldexp(round(ldexp(x, -q)), q);"),
@@ -36,7 +36,7 @@ MUTANTS = {
     "output_drops_compressed_values": (
         "for (int64_t i = 0; i < m; ++i) acc += w[i] * Vl[i * d + c];\n        for (int64_t j = 0;",
         "for (int64_t i = 0; i < m; ++i) acc += 0.0 * Vl[i * d + c];\n        for (int64_t j = 0;"),
-    "output_raw_logits_unscaled": ("w[m + j] = scale * dot(", "w[m + j] = dot("),
+    "output_raw_logits_unscaled": ("w[m + j] = scale * dot(Q + q * d,", "w[m + j] = dot(Q + q * d,"),
     "output_wrong_expert": ("const int32_t* ex = idx + (int64_t)route[q] * k;",
                             "const int32_t* ex = idx + (int64_t)((route[q] + 1) % m) * k;"),
     "output_keys_as_values": ("acc += w[m + j] * V[(int64_t)ex[j] * d + c];",
@@ -75,6 +75,24 @@ MUTANTS = {
     "dense_unnormalised": ("out[p * d + c] = sum / total;", "out[p * d + c] = sum;"),
     "dense_keys_as_values": ("sum += w[t] * V[t * d + c];", "sum += w[t] * K[t * d + c];"),
     "dense_drops_last_key": ("        total += w[t];\n", "        total += (t + 1 < N) ? w[t] : 0.0;\n"),
+    # backward pass with the experts and routes held fixed
+    "backward_drops_softmax_correction": (
+        "const double g = scale * w[m + j] * (dw[m + j] - c);",
+        "const double g = scale * w[m + j] * dw[m + j];"),
+    "backward_landmark_logit_unscaled": ("const double g = scale * w[i] * (dw[i] - c);",
+                                         "const double g = w[i] * (dw[i] - c);"),
+    "backward_pool_not_averaged": ("dQ[t * d + a] += dQl[i * d + a] / cnt;",
+                                   "dQ[t * d + a] += dQl[i * d + a];"),
+    "backward_drops_landmark_value_path": ("dV[t * d + a] += w[t] * dVl[i * d + a];",
+                                           "dV[t * d + a] += 0.0 * dVl[i * d + a];"),
+    "backward_cross_attention_keys_get_query": ("dK[t * d + a] += g * Ql[i * d + a];",
+                                                "dK[t * d + a] += g * Q[i * d + a];"),
+    "backward_dq_uses_values": ("dQ[q * d + a] += g * K[t * d + a];",
+                                "dQ[q * d + a] += g * V[t * d + a];"),
+    "backward_landmark_grad_not_fed_back": ("dQl[i * d + a] += g * K[t * d + a];",
+                                            "dQl[i * d + a] += 0.0 * K[t * d + a];"),
+    "backward_compressed_value_grad_unweighted": ("dVl[i * d + a] += w[i] * G[a];",
+                                                  "dVl[i * d + a] += G[a];"),
 }
 
 

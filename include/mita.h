@@ -216,6 +216,44 @@ int mita_dense_attention(const void* Q, const void* K, const void* V, int dtype,
                          int64_t H, int64_t N, int64_t d, float scale, float* out, void* stream);
 
 /*
+ * mita_backward — the gradients of MiTA attention for training.  The pages'
+ * wall-clock results are training times ["NeurIPS'26：注意力也是FFN？…",
+ * section "长序列建模：训练时间从10.6小时降至2.4小时"; "NeurIPS 2026 |
+ * Mixture-of-Top-k 注意力…", section "实验结果：接近完整注意力，长序列训练时间
+ * 减少约 77%"] but give no backward rule; reading taken here: the experts
+ * idx and the routes are constants (selections carry no gradient), and the
+ * rounding of the landmark queries into the input type passes gradients
+ * unchanged.  Given dout = dL/d out, the call computes dQ, dK, dV of
+ * L = sum(dout * out) through the output softmax (step 5), the landmark
+ * cross-attention that gives Vl (step 2b) and the pooling (step 1): the
+ * landmark queries and values are recomputed from Q, K, V, then every
+ * contraction runs on fp32 MFMA with fp32 accumulation.
+ *
+ *   Q, K, V    [B][H][N][d] in `dtype`, the forward's inputs
+ *   dtype, B, H, N, d, grid, m, k, scale   as in mita_forward (d == 64)
+ *   idx        [B][H][m][k] int32, the experts (mita_forward's idx_out);
+ *              entries outside [0, N) are clamped into it
+ *   routes     [B][H][N] int32, one expert per query (mita_forward's
+ *              route_out); entries outside [0, m) are clamped into it
+ *   dout       [B][H][N][d] fp32
+ *   dQ, dK, dV [B][H][N][d] fp32, fully overwritten; must not overlap the
+ *              inputs or each other
+ *   stream     a hipStream_t (NULL = the default stream)
+ *
+ * Work space: a cached stream-ordered block as in mita_forward (grown to
+ * the larger call's need): the query grouping (4 bytes per token and head)
+ * and fp32 partial sums of the landmark gradients (up to 32 KiB per expert
+ * work item and 64 KiB per key block of a head).  dK and dV receive the expert
+ * step's sums by fp32 atomic adds, so their last bits may differ between
+ * runs; dQ is deterministic.  Same pointer rules (16-byte alignment) and
+ * error behaviour as mita_forward.
+ */
+int mita_backward(const void* Q, const void* K, const void* V, int dtype, int64_t B, int64_t H,
+                  int64_t N, int64_t d, const mita_grid* grid, int64_t m, int64_t k,
+                  float scale, const int32_t* idx, const int32_t* routes, const float* dout,
+                  float* dQ, float* dK, float* dV, void* stream);
+
+/*
  * mita_release_workspace — free the work-space block cached for `stream` (a
  * hipStream_t; NULL = the default stream) on the current device.  For
  * callers that destroy streams or want the memory back; no step of the
@@ -247,7 +285,11 @@ int mita_version(void);
  * scatter), expert_attend, and single_launch (bf16 heads of at most 256
  * tokens run all five steps in one launch, one workgroup per head, with no
  * work space; the other stages then record nothing); each of route,
- * landmark_scan, expert_attend and single_launch is a single kernel launch.  mita_profile_read() waits for the recorded events and
+ * landmark_scan, expert_attend and single_launch is a single kernel launch.
+ * Backward calls record bw_zero, bw_pool, bw_landmark_fwd (partials and
+ * merge), bw_bucket (count, prefix, scatter), bw_attend (with its
+ * reduction), bw_cross (one launch) and bw_pool_grad (reduction and spread);
+ * a backward call counts as a call too.  mita_profile_read() waits for the recorded events and
  * returns, per stage, the summed milliseconds and the number of calls since
  * the last mita_profile_enable().  Not thread-safe: profile from one thread.
  *   mita_profile_enable(1) clears the sums and starts recording;

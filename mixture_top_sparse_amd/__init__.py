@@ -1,4 +1,5 @@
-"""MiTA (Mixture-of-Top-k Attention) forward pass on AMD MI355X (gfx950).
+"""MiTA (Mixture-of-Top-k Attention) on AMD MI355X (gfx950): the forward
+pass and its backward with the selections held fixed.
 
 Thin ctypes binding over ``libmita.so`` (declared in ``include/mita.h``).
 This module only marshals arguments: it checks tensor shapes, types and
@@ -18,6 +19,7 @@ __all__ = [
     "mita_forward_noalloc",
     "mita_forward_s",
     "mita_dense_attention",
+    "mita_backward",
     "mita_release_workspace",
     "mita_status_string",
     "mita_last_error",
@@ -83,6 +85,13 @@ def lib() -> ctypes.CDLL:
                                            ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
                                            ctypes.c_void_p, ctypes.c_void_p]
         L.mita_dense_attention.restype = ctypes.c_int
+        L.mita_backward.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                    ctypes.c_int64, ctypes.POINTER(MitaGrid), ctypes.c_int64,
+                                    ctypes.c_int64, ctypes.c_float, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.mita_backward.restype = ctypes.c_int
         L.mita_status_string.argtypes = [ctypes.c_int]
         L.mita_status_string.restype = ctypes.c_char_p
         L.mita_last_error.argtypes = []
@@ -241,6 +250,38 @@ def mita_dense_attention(Q, K, V, *, scale=None):
                                           float(scale), out.data_ptr(), stream),
                "mita_dense_attention")
     return out
+
+
+def mita_backward(Q, K, V, idx, route, dout, *, m: int, k: int, grid=None, scale=None):
+    """Gradients (dQ, dK, dV) [B,H,N,d] fp32 of sum(dout * out), out being
+    mita_forward's output for the same Q, K, V, with the experts idx
+    [B,H,m,k] and the routes [B,H,N] (int32) held fixed.  dout: [B,H,N,d]
+    fp32.  Enqueued on torch's current stream."""
+    import torch
+
+    dt = _check_inputs(Q, K, V)
+    B, H, N, d = Q.shape
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    for name, t, shape, dtype in (("idx", idx, (B, H, m, k), torch.int32),
+                                  ("route", route, (B, H, N), torch.int32),
+                                  ("dout", dout, (B, H, N, d), torch.float32)):
+        if not isinstance(t, torch.Tensor) or t.device != Q.device:
+            raise ValueError(f"{name} must be a tensor on Q's device")
+        if tuple(t.shape) != shape or t.dtype != dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {shape}")
+    dev = Q.device
+    dQ = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    dK = torch.empty_like(dQ)
+    dV = torch.empty_like(dQ)
+    g = None if grid is None else ctypes.byref(MitaGrid(*[int(x) for x in grid]))
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        _raise(lib().mita_backward(Q.data_ptr(), K.data_ptr(), V.data_ptr(), dt, B, H, N, d, g,
+                                   int(m), int(k), float(scale), idx.data_ptr(), route.data_ptr(),
+                                   dout.data_ptr(), dQ.data_ptr(), dK.data_ptr(), dV.data_ptr(),
+                                   stream), "mita_backward")
+    return dQ, dK, dV
 
 
 def mita_release_workspace(stream=None, device=None) -> None:

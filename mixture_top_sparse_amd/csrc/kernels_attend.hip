@@ -19,6 +19,7 @@
 //
 // Roofline: HBM-bound per query: d*e bytes of Q gathered (one full row) and
 // 4d bytes of fp32 output written; the staged expert (~40 KiB) comes from L2.
+#include "mita_bucket.hpp"
 #include "mita_device.hpp"
 #include "mita_internal.hpp"
 
@@ -57,32 +58,6 @@ struct AttendLds<F32, MPAD, KPAD, NW> {
   alignas(16) float pk[(MPAD + KPAD) * PKST];
   alignas(16) float val[(MPAD + KPAD) * VST];
 };
-
-struct TileInfo {
-  int e;      // expert
-  int qb;     // first perm slot of this work item
-  int qe;     // one past its last perm slot
-};
-
-// Work item t of a head covers up to `tpb` consecutive 64-query tiles of one
-// expert; item_start[e] is the first item of expert e (exclusive scan of
-// ceil(tiles_e / tpb)).  item_start is non-decreasing, so t's expert is the
-// number of experts e < m - 1 whose successor starts at or before t: one
-// load per lane (m <= 64) and a ballot, instead of a chain of m dependent
-// loads.
-__device__ __forceinline__ bool find_item(const int32_t* __restrict__ item_start,
-                                          const int32_t* __restrict__ offsets, int m, int tpb,
-                                          int t, TileInfo& ti) {
-  const int l = lane_id();
-  const int next = l < m - 1 ? item_start[l + 1] : INT32_MAX;
-  if (t >= item_start[m]) return false;
-  const int e = __popcll(ballot(next <= t));
-  const int j0 = (t - item_start[e]) * tpb;
-  ti.e = e;
-  ti.qb = offsets[e] + kAttendTile * j0;
-  ti.qe = min(ti.qb + kAttendTile * tpb, static_cast<int>(offsets[e + 1]));
-  return true;
-}
 
 __device__ __forceinline__ int64_t clamp_index(int64_t v, int64_t n) {
   return v < 0 ? 0 : (v >= n ? n - 1 : v);

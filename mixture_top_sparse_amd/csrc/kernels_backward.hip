@@ -1,0 +1,913 @@
+// kernels_backward.hip — the backward pass (training) of MiTA attention: the
+// gradients dQ, dK, dV of sum(dout * out) with the experts idx and the routes
+// held fixed (the selections carry no gradient) and the rounding of the
+// landmark queries into the input type taken as the identity.  The pages'
+// wall-clock results are training times ("NeurIPS'26：注意力也是FFN？…",
+// section "长序列建模：训练时间从10.6小时降至2.4小时"; "Mixture-of-Top-k
+// 注意力…", section "实验结果：接近完整注意力，长序列训练时间减少约 77%").
+//
+// The forward, per head (Ql[i] the mean of Q over window i, scale s):
+//   A  = softmax_rows(s Ql K^T)           (m x N)    Vl = A V
+//   out[q] = sum_p w_qp val_p,  w_q = softmax(s q . key_p) over the m + k
+//   pairs p of q (keys [Ql; K[idx[route[q]]]], values [Vl; V[idx[...]]]).
+// Its reverse, in launch order (all on the caller's stream):
+//   zero      dK = dV = 0 (filled by a kernel: the expert step adds atomically)
+//   pool      Ql exactly as the forward computes it (the pooling kernel)
+//   lmfwd     per key chunk: online-softmax partials of A V   (fp32 MFMA)
+//   lmmerge   Vl and the log-sum-exp of each landmark row
+//   count / prefix / scatter   the queries grouped by their given routes
+//   attend    per expert work item (one expert, <= tpb * 64 queries):
+//               g_qp = s w_qp (dout_q . val_p - dout_q . out_q)
+//               dQ[q] = sum_p g_qp key_p          (stored: complete but for
+//                                                   the pooling term)
+//               dK/dV of the expert's raw keys += g^T Q, w^T dout (atomics)
+//               dQl/dVl partials of the item     (summed by reduce1)
+//   reduce1   dVl, the expert step's dQl, and D_i = dVl_i . Vl_i
+//   cross     per key chunk: h_it = s A_it (dVl_i . V_t - D_i);
+//               dK[t] += sum_i h_it Ql_i,  dV[t] += sum_i A_it dVl_i
+//               (read-modify-write: one block owns each key), and partials
+//               of dQl += h K
+//   reduce2   dQl in full, divided by each window's size
+//   poolbw    dQ[t] += sum over the windows i containing t of dQl_i / |W_i|
+// Every contraction runs on v_mfma_f32_16x16x4_f32 (fp32 operands, fp32
+// accumulation), so the gradients carry fp32 rounding only.
+//
+// Roofline: per (token, head) the pass reads Q, K, V (3 d e bytes, e the
+// input element size) and dout (4d), and writes dQ, dK, dV (12d) plus their
+// read-modify-writes (8d each for dQ in poolbw and for dK, dV in cross):
+// about 3de + 40d bytes.  The contractions cost about 2 d (5 (m + k) + 7 m)
+// flops per (token, head) at fp32 MFMA rate, which exceeds the bytes' time
+// at 157 TFLOP/s for m = k = 64: the pass is MFMA-bound (fp32).
+#include "mita.h"
+#include "mita_bucket.hpp"
+#include "mita_device.hpp"
+#include "mita_internal.hpp"
+
+namespace mita {
+namespace {
+
+constexpr int kBwSt = 68;         // fp32 LDS row stride (64 + 4)
+constexpr int kBwPairs = 128;     // m + k rounded up to 16 each, at most
+constexpr int kBwGsSt = kBwPairs + 4;
+
+// eight consecutive elements of a row, as fp32
+__device__ __forceinline__ void load8(const uint16_t* __restrict__ p, float (&v)[8]) {
+  const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* __restrict__ p, float (&v)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = a[i];
+    v[4 + i] = b[i];
+  }
+}
+__device__ __forceinline__ void zero8(float (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = 0.f;
+}
+__device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+  *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+}
+
+__device__ __forceinline__ int64_t clamp64(int64_t v, int64_t n) {
+  return v < 0 ? 0 : (v >= n ? n - 1 : v);
+}
+
+// Adaptive-pooling bin a of n bins over g cells: [floor(a g / n), ceil((a + 1) g / n)).
+__device__ __forceinline__ void bin_range(int64_t a, int64_t g, int64_t n, int64_t& b0,
+                                          int64_t& b1) {
+  b0 = (a * g) / n;
+  b1 = ((a + 1) * g + n - 1) / n;
+}
+
+// ---------------------------------------------------------------------------
+// zero fill (dK, dV) — a kernel, not a memset, so the sequence stays
+// capturable in a graph
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_bw_zero(f32x4* __restrict__ a, f32x4* __restrict__ b,
+                                                 int64_t n4) {
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n4;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    a[i] = z;
+    b[i] = z;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// landmark cross-attention, forward (Vl and its row log-sum-exp)
+// ---------------------------------------------------------------------------
+
+// Block (chunk, head): keys [chunk * csize, ...) in 16-key groups, wave w
+// taking groups w, w + 4, ...  Per group: S^T = K_g Ql^T (keys on rows,
+// landmarks on columns), the running column maximum and sum, and
+// acc^T (dims x landmarks) += V_g^T P^T — the landmark on the output column
+// keeps each landmark's rescale inside its own lanes.  Partial p = 4 chunk +
+// w: stats [BH][P][64][2] (max in log2 units, sum), acc [BH][P][64][64].
+template <class T, int MB>
+__global__ __launch_bounds__(256) void k_bw_lmfwd(const typename T::elem* __restrict__ K,
+                                                  const typename T::elem* __restrict__ V,
+                                                  const typename T::elem* __restrict__ ql,
+                                                  int64_t N, int m, int csize, float c2,
+                                                  float* __restrict__ part_stats,
+                                                  float* __restrict__ part_acc) {
+  constexpr int MP = 16 * MB;
+  __shared__ __attribute__((aligned(16))) float sQl[MP * kBwSt];
+  __shared__ __attribute__((aligned(16))) float sKV[4][2][16 * kBwSt];
+  const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
+  const int64_t bh = blockIdx.y;
+  const int P = static_cast<int>(gridDim.x) * 4;
+  for (int u = threadIdx.x; u < MP * 8; u += 256) {
+    const int row = u >> 3, j = u & 7;
+    float v[8];
+    if (row < m)
+      load8(ql + (bh * m + row) * kD + 8 * j, v);
+    else
+      zero8(v);
+    store8(sQl + row * kBwSt + 8 * j, v);
+  }
+  __syncthreads();
+  const int64_t k0 = static_cast<int64_t>(blockIdx.x) * csize;
+  const int64_t k1 = k0 + csize < N ? k0 + csize : N;
+  float M[MB], L[MB];
+  f32x4 acc[MB][4];
+#pragma unroll
+  for (int lb = 0; lb < MB; ++lb) {
+    M[lb] = -INFINITY;
+    L[lb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) acc[lb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float* sK = sKV[w][0];
+  float* sV = sKV[w][1];
+  for (int64_t t0 = k0 + 16 * w; t0 < k1; t0 += 64) {
+    // this wave's 16 keys (its LDS accesses complete in program order)
+#pragma unroll
+    for (int u = l; u < 128; u += 64) {
+      const int row = u >> 3, j = u & 7;
+      const int64_t t = t0 + row;
+      float kv[8], vv[8];
+      if (t < k1) {
+        load8(K + (bh * N + t) * kD + 8 * j, kv);
+        load8(V + (bh * N + t) * kD + 8 * j, vv);
+      } else {
+        zero8(kv);
+        zero8(vv);
+      }
+      store8(sK + row * kBwSt + 8 * j, kv);
+      store8(sV + row * kBwSt + 8 * j, vv);
+    }
+    float a[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) a[s] = sK[c16 * kBwSt + 4 * s + g];
+#pragma unroll
+    for (int lb = 0; lb < MB; ++lb) {
+      f32x4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 16; ++s) S = mfma_f32(a[s], sQl[(16 * lb + c16) * kBwSt + 4 * s + g], S);
+      // S[r]: key t0 + 4g + r, landmark 16 lb + c16
+      float x[4];
+      float cm = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        x[r] = (t0 + 4 * g + r < k1) ? S[r] * c2 : -INFINITY;
+        cm = fmaxf(cm, x[r]);
+      }
+      cm = xor_max(cm, 16);
+      cm = xor_max(cm, 32);
+      const float Mn = fmaxf(M[lb], cm);  // finite: key t0 is in range
+      const float f = fast_exp2(M[lb] - Mn);
+      float p[4], ps = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[r] = fast_exp2(x[r] - Mn);
+        ps += p[r];
+      }
+      ps = xor_sum(ps, 16);
+      ps = xor_sum(ps, 32);
+      L[lb] = L[lb] * f + ps;
+      M[lb] = Mn;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        acc[lb][db] *= f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          acc[lb][db] = mfma_f32(sV[(4 * g + r) * kBwSt + 16 * db + c16], p[r], acc[lb][db]);
+      }
+    }
+  }
+  const int64_t pbase = (bh * P + static_cast<int64_t>(blockIdx.x) * 4 + w) * kMaxM;
+#pragma unroll
+  for (int lb = 0; lb < MB; ++lb) {
+    const int64_t row = pbase + 16 * lb + c16;
+    if (g == 0) {
+      part_stats[row * 2] = M[lb];
+      part_stats[row * 2 + 1] = L[lb];
+    }
+    // acc[lb][db][r]: dim 16 db + 4 g + r of landmark 16 lb + c16
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+      *reinterpret_cast<f32x4*>(part_acc + row * kD + 16 * db + 4 * g) = acc[lb][db];
+  }
+}
+
+// One wave per landmark (four per block): Vl = acc / sum over the partials,
+// lse2 = max + log2(sum) (log2 units of the scaled logits).
+__global__ __launch_bounds__(256) void k_bw_lmmerge(const float* __restrict__ part_stats,
+                                                    const float* __restrict__ part_acc, int m,
+                                                    int P, float* __restrict__ vl,
+                                                    float* __restrict__ lse2) {
+  const int l = lane_id(), w = wave_id();
+  const int64_t bh = blockIdx.y;
+  const int i = static_cast<int>(blockIdx.x) * 4 + w;
+  if (i >= m) return;
+  float M = -INFINITY, L = 0.f, a = 0.f;
+  for (int p = 0; p < P; ++p) {
+    const int64_t row = (bh * P + p) * kMaxM + i;
+    const float Mp = part_stats[row * 2];
+    if (Mp == -INFINITY) continue;  // a wave that had no keys
+    const float Lp = part_stats[row * 2 + 1];
+    const float ap = part_acc[row * kD + l];
+    const float Mn = fmaxf(M, Mp);
+    const float f0 = fast_exp2(M - Mn), f1 = fast_exp2(Mp - Mn);
+    L = L * f0 + Lp * f1;
+    a = a * f0 + ap * f1;
+    M = Mn;
+  }
+  vl[(bh * m + i) * kD + l] = a / L;
+  if (l == 0) lse2[bh * m + i] = M + __log2f(L);
+}
+
+// ---------------------------------------------------------------------------
+// grouping of the queries by their given routes (stable counting sort)
+// ---------------------------------------------------------------------------
+
+// Block (segment, head): per-expert counts of the segment's routes (routes
+// outside [0, m) count as the nearest expert, as the scatter places them).
+__global__ __launch_bounds__(256) void k_bw_count(const int32_t* __restrict__ route, int64_t N,
+                                                  int m, int nseg, int32_t* __restrict__ counts) {
+  __shared__ int cnt[kMaxM];
+  if (threadIdx.x < kMaxM) cnt[threadIdx.x] = 0;
+  __syncthreads();
+  const int64_t bh = blockIdx.y;
+  const int seg = blockIdx.x;
+  const int64_t q0 = static_cast<int64_t>(seg) * kRouteSeg;
+  for (int i = threadIdx.x; i < kRouteSeg; i += 256) {
+    const int64_t q = q0 + i;
+    if (q < N) {
+      int r = route[bh * N + q];
+      r = r < 0 ? 0 : (r >= m ? m - 1 : r);
+      atomicAdd(&cnt[r], 1);
+    }
+  }
+  __syncthreads();
+  if (static_cast<int>(threadIdx.x) < m) counts[(bh * m + threadIdx.x) * nseg + seg] = cnt[threadIdx.x];
+}
+
+__global__ __launch_bounds__(256) void k_bw_prefix(const int32_t* __restrict__ counts, int m,
+                                                   int nseg, int32_t* __restrict__ colpre,
+                                                   int32_t* __restrict__ totals) {
+  __shared__ int wsum[4];
+  bucket_prefix(counts, m, nseg, blockIdx.x, blockIdx.y, colpre, totals, wsum);
+}
+
+__global__ __launch_bounds__(256) void k_bw_scatter(const int32_t* __restrict__ route,
+                                                    const int32_t* __restrict__ counts, int m,
+                                                    int nseg, int64_t N, int tpb,
+                                                    const int32_t* __restrict__ totals,
+                                                    const int32_t* __restrict__ colpre,
+                                                    int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ item_start,
+                                                    int32_t* __restrict__ perm) {
+  __shared__ ScatterLds L[4];
+  const int w = __builtin_amdgcn_readfirstlane(wave_id());
+  const int seg = static_cast<int>(blockIdx.x) * 4 + w;
+  if (seg < nseg)
+    scatter_segment(route, counts, m, nseg, N, kAttendTile, tpb, totals, colpre, offsets, nullptr,
+                    item_start, perm, nullptr, seg, blockIdx.y, L[w]);
+}
+
+// ---------------------------------------------------------------------------
+// the output softmax, per expert work item
+// ---------------------------------------------------------------------------
+
+// Block (work item, head), four waves.  The item's expert is staged once as
+// fp32 pair rows: keys [Ql; 0; K_e; 0] and values [Vl; 0; V_e; 0] with the
+// landmarks padded to MP = 16 ceil(m / 16) rows and the raw keys to KP rows
+// (PP = MP + KP <= 128, NB = PP / 16 column blocks).  Queries go 16 at a
+// time: wave w computes the logits and dout . value of column blocks w and
+// w + 4 (queries on rows, pairs on columns), the row max and the sums over
+// the pairs meet in LDS, and then
+//   dKey[p] += sum_q g_qp q,  dVal[p] += sum_q w_qp dout_q
+// run with the wave's own columns as the MFMA A operand straight from the
+// accumulator layout (pairs on the output rows), while dQ = g [keys] takes
+// g through LDS, wave w producing dims 16 w .. 16 w + 15 of the 16 queries.
+template <class T>
+__global__ __launch_bounds__(256) void k_bw_attend(
+    const typename T::elem* __restrict__ Q, const typename T::elem* __restrict__ K,
+    const typename T::elem* __restrict__ V, const typename T::elem* __restrict__ ql,
+    const float* __restrict__ vl, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ item_start, int tpb, int64_t N, int m, int k, float scale,
+    const float* __restrict__ dout, float* __restrict__ dQ, float* __restrict__ dK,
+    float* __restrict__ dV, float* __restrict__ part, int items) {
+  __shared__ __attribute__((aligned(16))) float sPk[kBwPairs * kBwSt];
+  __shared__ __attribute__((aligned(16))) float sPv[kBwPairs * kBwSt];
+  __shared__ __attribute__((aligned(16))) float sQ[16 * kBwSt];
+  __shared__ __attribute__((aligned(16))) float sG[16 * kBwSt];
+  __shared__ __attribute__((aligned(16))) float sGs[16 * kBwGsSt];
+  __shared__ float sRed[3][4][16];
+  __shared__ int sQid[16];
+  const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
+  const int tid = threadIdx.x;
+  const int64_t bh = blockIdx.y;
+  TileInfo ti;
+  if (!find_item(item_start + bh * (m + 1), offsets + bh * (m + 1), m, tpb, blockIdx.x, ti))
+    return;  // whole block: past the head's last item
+  const int MP = (m + 15) & ~15, KP = (k + 15) & ~15;
+  const int PP = MP + KP, NB = PP / 16;
+  const int32_t* ex = idx + (bh * m + ti.e) * k;
+  for (int u = tid; u < PP * 8; u += 256) {
+    const int row = u >> 3, j = u & 7;
+    float kv[8], vv[8];
+    if (row < m) {
+      load8(ql + (bh * m + row) * kD + 8 * j, kv);
+      load8(vl + (bh * m + row) * kD + 8 * j, vv);
+    } else if (row >= MP && row < MP + k) {
+      const int64_t t = clamp64(ex[row - MP], N);
+      load8(K + (bh * N + t) * kD + 8 * j, kv);
+      load8(V + (bh * N + t) * kD + 8 * j, vv);
+    } else {
+      zero8(kv);
+      zero8(vv);
+    }
+    store8(sPk + row * kBwSt + 8 * j, kv);
+    store8(sPv + row * kBwSt + 8 * j, vv);
+  }
+  const float c2 = scale * kLog2e;
+  f32x4 aK[2][4], aV[2][4];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      aK[cb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      aV[cb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  for (int q0 = ti.qb; q0 < ti.qe; q0 += 16) {
+    const int nv = ti.qe - q0 < 16 ? ti.qe - q0 : 16;
+    __syncthreads();  // the expert staged; the previous group's LDS reads done
+    if (tid < 128) {
+      const int row = tid >> 3, j = tid & 7;
+      float qv[8], gv[8];
+      if (row < nv) {
+        const int64_t q = clamp64(perm[bh * N + q0 + row], N);
+        load8(Q + (bh * N + q) * kD + 8 * j, qv);
+        load8(dout + (bh * N + q) * kD + 8 * j, gv);
+        if (j == 0) sQid[row] = static_cast<int>(q);
+      } else {
+        zero8(qv);
+        zero8(gv);
+      }
+      store8(sQ + row * kBwSt + 8 * j, qv);
+      store8(sG + row * kBwSt + 8 * j, gv);
+    }
+    __syncthreads();
+    float aq[16], ag[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      aq[s] = sQ[c16 * kBwSt + 4 * s + g];
+      ag[s] = sG[c16 * kBwSt + 4 * s + g];
+    }
+    f32x4 S[2], dW[2];
+    float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const int pb = w + 4 * cb;
+      S[cb] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      dW[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (pb < NB) {  // wave-uniform
+        f32x4 s4 = {0.f, 0.f, 0.f, 0.f}, d4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+          s4 = mfma_f32(aq[s], sPk[(16 * pb + c16) * kBwSt + 4 * s + g], s4);
+          d4 = mfma_f32(ag[s], sPv[(16 * pb + c16) * kBwSt + 4 * s + g], d4);
+        }
+        const int p = 16 * pb + c16;
+        const bool pv = p < m || (p >= MP && p < MP + k);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          S[cb][r] = pv ? s4[r] * c2 : -INFINITY;  // log2 units
+          mx[r] = fmaxf(mx[r], S[cb][r]);
+        }
+        dW[cb] = d4;
+      }
+    }
+    // row (query) statistics over all pairs: within 16 lanes, then across waves
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      mx[r] = xor_max(mx[r], 1);
+      mx[r] = xor_max(mx[r], 2);
+      mx[r] = xor_max(mx[r], 4);
+      mx[r] = xor_max(mx[r], 8);
+      if (c16 == 0) sRed[0][w][4 * g + r] = mx[r];
+    }
+    __syncthreads();
+    float Mr[4], z[4], y[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * g + r;
+      Mr[r] = fmaxf(fmaxf(sRed[0][0][row], sRed[0][1][row]), fmaxf(sRed[0][2][row], sRed[0][3][row]));
+      z[r] = 0.f;
+      y[r] = 0.f;
+    }
+    float E[2][4];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        E[cb][r] = fast_exp2(S[cb][r] - Mr[r]);  // 0 for masked pairs
+        z[r] += E[cb][r];
+        y[r] += E[cb][r] * dW[cb][r];
+      }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+      for (int mk = 1; mk < 16; mk <<= 1) {
+        z[r] = xor_sum(z[r], mk);
+        y[r] = xor_sum(y[r], mk);
+      }
+      if (c16 == 0) {
+        sRed[1][w][4 * g + r] = z[r];
+        sRed[2][w][4 * g + r] = y[r];
+      }
+    }
+    __syncthreads();
+    float Wt[2][4], Gs[2][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * g + r;
+      const float Z = sRed[1][0][row] + sRed[1][1][row] + sRed[1][2][row] + sRed[1][3][row];
+      const float Y = sRed[2][0][row] + sRed[2][1][row] + sRed[2][2][row] + sRed[2][3][row];
+      const float inv = row < nv ? 1.f / Z : 0.f;  // padding rows contribute nothing
+      const float c = Y / Z;                       // dout . out of this query
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        Wt[cb][r] = E[cb][r] * inv;
+        Gs[cb][r] = scale * Wt[cb][r] * (dW[cb][r] - c);
+      }
+    }
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const int pb = w + 4 * cb;
+      if (pb >= NB) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sGs[(4 * g + r) * kBwGsSt + 16 * pb + c16] = Gs[cb][r];
+      // pairs on the output rows: A = g^T (pair c16, query 4g + r), B = Q / dout rows
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          aK[cb][db] = mfma_f32(Gs[cb][r], sQ[(4 * g + r) * kBwSt + 16 * db + c16], aK[cb][db]);
+          aV[cb][db] = mfma_f32(Wt[cb][r], sG[(4 * g + r) * kBwSt + 16 * db + c16], aV[cb][db]);
+        }
+    }
+    __syncthreads();
+    // dQ (16 queries x dims 16w .. 16w + 15) = g [keys]
+    f32x4 dq = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < 4 * NB; ++s)
+      dq = mfma_f32(sGs[c16 * kBwGsSt + 4 * s + g], sPk[(4 * s + g) * kBwSt + 16 * w + c16], dq);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * g + r;
+      if (row < nv) dQ[(bh * N + sQid[row]) * kD + 16 * w + c16] = dq[r];
+    }
+  }
+  // the item's sums: landmark rows to its partial, raw-key rows to dK / dV
+  float* pq = part + ((bh * items + blockIdx.x) * 2) * static_cast<int64_t>(m) * kD;
+  float* pv = pq + static_cast<int64_t>(m) * kD;
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int pb = w + 4 * cb;
+    if (pb >= NB) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int p = 16 * pb + 4 * g + r;
+      if (p < m) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          pq[p * kD + 16 * db + c16] = aK[cb][db][r];
+          pv[p * kD + 16 * db + c16] = aV[cb][db][r];
+        }
+      } else if (p >= MP && p < MP + k) {
+        const int64_t t = clamp64(ex[p - MP], N);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          unsafeAtomicAdd(dK + (bh * N + t) * kD + 16 * db + c16, aK[cb][db][r]);
+          unsafeAtomicAdd(dV + (bh * N + t) * kD + 16 * db + c16, aV[cb][db][r]);
+        }
+      }
+    }
+  }
+}
+
+// Block (landmark, head): dVl and the expert step's dQl summed over the
+// head's work items, and D = dVl . Vl.
+__global__ __launch_bounds__(256) void k_bw_reduce1(const float* __restrict__ part,
+                                                    const int32_t* __restrict__ item_start,
+                                                    const float* __restrict__ vl, int m, int items,
+                                                    float* __restrict__ dql, float* __restrict__ dvl,
+                                                    float* __restrict__ dd) {
+  __shared__ float red[2][4][64];
+  const int l = lane_id(), w = wave_id();
+  const int64_t bh = blockIdx.y;
+  const int i = blockIdx.x;
+  const int n = item_start[bh * (m + 1) + m];
+  const int64_t stride = static_cast<int64_t>(m) * kD;
+  float sq = 0.f, sv = 0.f;
+  for (int t = w; t < n; t += 4) {
+    const float* pq = part + (bh * items + t) * 2 * stride + i * kD;
+    sq += pq[l];
+    sv += pq[stride + l];
+  }
+  red[0][w][l] = sq;
+  red[1][w][l] = sv;
+  __syncthreads();
+  if (w != 0) return;
+  sq = red[0][0][l] + red[0][1][l] + red[0][2][l] + red[0][3][l];
+  sv = red[1][0][l] + red[1][1][l] + red[1][2][l] + red[1][3][l];
+  const int64_t o = (bh * m + i) * kD + l;
+  dql[o] = sq;
+  dvl[o] = sv;
+  float dv = sv * vl[o];
+#pragma unroll
+  for (int mk = 1; mk < 64; mk <<= 1) dv = xor_sum(dv, mk);
+  if (l == 0) dd[bh * m + i] = dv;
+}
+
+// ---------------------------------------------------------------------------
+// the landmark cross-attention, backward
+// ---------------------------------------------------------------------------
+
+// Block (chunk, head), wave w taking 16-key groups w, w + 4, ... of the chunk.
+// Per group, keys on rows and landmarks on columns:
+//   S^T = K_g Ql^T, dP^T = V_g dVl^T,  A = 2^(c2 S - lse2),  h = s A (dP - D)
+//   dQl += h K_g            (A operand = h straight from the accumulators)
+//   dK_g += h^T Ql, dV_g += A^T dVl   (h, A through the wave's LDS)
+// dK, dV rows of the group are read, added to and written back (each key
+// belongs to one group).  The wave's dQl sums go to partial 4 chunk + w.
+template <class T, int MB>
+__global__ __launch_bounds__(256) void k_bw_cross(const typename T::elem* __restrict__ K,
+                                                  const typename T::elem* __restrict__ V,
+                                                  const typename T::elem* __restrict__ ql,
+                                                  const float* __restrict__ dvl,
+                                                  const float* __restrict__ lse2,
+                                                  const float* __restrict__ dd, int64_t N, int m,
+                                                  int csize, float scale,
+                                                  float* __restrict__ dK, float* __restrict__ dV,
+                                                  float* __restrict__ part2) {
+  constexpr int MP = 16 * MB;
+  __shared__ __attribute__((aligned(16))) float sQl[MP * kBwSt];
+  __shared__ __attribute__((aligned(16))) float sdVl[MP * kBwSt];
+  __shared__ float sLse[MP], sD[MP];
+  __shared__ __attribute__((aligned(16))) float sKV[4][2][16 * kBwSt];
+  const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
+  const int64_t bh = blockIdx.y;
+  const int P = static_cast<int>(gridDim.x) * 4;
+  for (int u = threadIdx.x; u < MP * 8; u += 256) {
+    const int row = u >> 3, j = u & 7;
+    float a[8], b[8];
+    if (row < m) {
+      load8(ql + (bh * m + row) * kD + 8 * j, a);
+      load8(dvl + (bh * m + row) * kD + 8 * j, b);
+    } else {
+      zero8(a);
+      zero8(b);
+    }
+    store8(sQl + row * kBwSt + 8 * j, a);
+    store8(sdVl + row * kBwSt + 8 * j, b);
+  }
+  if (threadIdx.x < MP) {
+    const int i = threadIdx.x;
+    sLse[i] = i < m ? lse2[bh * m + i] : INFINITY;  // padding landmarks: weight 0
+    sD[i] = i < m ? dd[bh * m + i] : 0.f;
+  }
+  __syncthreads();
+  const float c2 = scale * kLog2e;
+  const int64_t k0 = static_cast<int64_t>(blockIdx.x) * csize;
+  const int64_t k1 = k0 + csize < N ? k0 + csize : N;
+  f32x4 aQ[MB][4];
+#pragma unroll
+  for (int lb = 0; lb < MB; ++lb)
+#pragma unroll
+    for (int db = 0; db < 4; ++db) aQ[lb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float* sK = sKV[w][0];  // K rows; then A^T
+  float* sV = sKV[w][1];  // V rows; then h^T
+  for (int64_t t0 = k0 + 16 * w; t0 < k1; t0 += 64) {
+#pragma unroll
+    for (int u = l; u < 128; u += 64) {
+      const int row = u >> 3, j = u & 7;
+      const int64_t t = t0 + row;
+      float kv[8], vv[8];
+      if (t < k1) {
+        load8(K + (bh * N + t) * kD + 8 * j, kv);
+        load8(V + (bh * N + t) * kD + 8 * j, vv);
+      } else {
+        zero8(kv);
+        zero8(vv);
+      }
+      store8(sK + row * kBwSt + 8 * j, kv);
+      store8(sV + row * kBwSt + 8 * j, vv);
+    }
+    float ak[16], av[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      ak[s] = sK[c16 * kBwSt + 4 * s + g];
+      av[s] = sV[c16 * kBwSt + 4 * s + g];
+    }
+    float A[MB][4], Hh[MB][4];
+#pragma unroll
+    for (int lb = 0; lb < MB; ++lb) {
+      f32x4 S = {0.f, 0.f, 0.f, 0.f}, dP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        S = mfma_f32(ak[s], sQl[(16 * lb + c16) * kBwSt + 4 * s + g], S);
+        dP = mfma_f32(av[s], sdVl[(16 * lb + c16) * kBwSt + 4 * s + g], dP);
+      }
+      const int i = 16 * lb + c16;
+      const float ls = sLse[i], Di = sD[i];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool kv = t0 + 4 * g + r < k1;
+        A[lb][r] = kv ? fast_exp2(S[r] * c2 - ls) : 0.f;
+        Hh[lb][r] = scale * A[lb][r] * (dP[r] - Di);
+      }
+    }
+    // dQl += h K_g: landmarks on the output rows
+#pragma unroll
+    for (int lb = 0; lb < MB; ++lb)
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          aQ[lb][db] = mfma_f32(Hh[lb][r], sK[(4 * g + r) * kBwSt + 16 * db + c16], aQ[lb][db]);
+    // A and h transposed through the wave's LDS (after its reads of K and V)
+#pragma unroll
+    for (int lb = 0; lb < MB; ++lb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sK[(4 * g + r) * kBwSt + 16 * lb + c16] = A[lb][r];
+        sV[(4 * g + r) * kBwSt + 16 * lb + c16] = Hh[lb][r];
+      }
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      f32x4 dk = {0.f, 0.f, 0.f, 0.f}, dv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4 * MB; ++s) {
+        dk = mfma_f32(sV[c16 * kBwSt + 4 * s + g], sQl[(4 * s + g) * kBwSt + 16 * db + c16], dk);
+        dv = mfma_f32(sK[c16 * kBwSt + 4 * s + g], sdVl[(4 * s + g) * kBwSt + 16 * db + c16], dv);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t t = t0 + 4 * g + r;
+        if (t < k1) {
+          float* pk = dK + (bh * N + t) * kD + 16 * db + c16;
+          float* pvv = dV + (bh * N + t) * kD + 16 * db + c16;
+          *pk += dk[r];
+          *pvv += dv[r];
+        }
+      }
+    }
+  }
+  const int64_t pbase = (bh * P + static_cast<int64_t>(blockIdx.x) * 4 + w) * kMaxM;
+#pragma unroll
+  for (int lb = 0; lb < MB; ++lb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * lb + 4 * g + r;
+      if (i < m) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) part2[(pbase + i) * kD + 16 * db + c16] = aQ[lb][db][r];
+      }
+    }
+}
+
+// Block (landmark, head): dQl = the expert step's part + the cross partials,
+// divided by the window's size.
+__global__ __launch_bounds__(256) void k_bw_reduce2(const float* __restrict__ part2, int P,
+                                                    const float* __restrict__ dql1, int m, int gh,
+                                                    int gw, int mh, int mw,
+                                                    float* __restrict__ dqlw) {
+  __shared__ float red[4][64];
+  const int l = lane_id(), w = wave_id();
+  const int64_t bh = blockIdx.y;
+  const int i = blockIdx.x;
+  float s = 0.f;
+  for (int p = w; p < P; p += 4) s += part2[((bh * P + p) * kMaxM + i) * kD + l];
+  red[w][l] = s;
+  __syncthreads();
+  if (w != 0) return;
+  s = red[0][l] + red[1][l] + red[2][l] + red[3][l] + dql1[(bh * m + i) * kD + l];
+  int64_t r0, r1, c0, c1;
+  bin_range(i / mw, gh, mh, r0, r1);
+  bin_range(i % mw, gw, mw, c0, c1);
+  dqlw[(bh * m + i) * kD + l] = s / static_cast<float>((r1 - r0) * (c1 - c0));
+}
+
+// Block (16 tokens, head), sixteen threads per token with 4 dims each.  A
+// grid cell lies only in bins of floor(r mh / gh) and its two neighbours per
+// axis (mh <= gh).
+__global__ __launch_bounds__(256) void k_bw_poolbw(const float* __restrict__ dqlw, int64_t N,
+                                                   int m, int gh, int gw, int mh, int mw,
+                                                   float* __restrict__ dQ) {
+  const int64_t bh = blockIdx.y;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  const int dq4 = threadIdx.x & 15;
+  if (t >= N) return;
+  const int64_t row = t / gw, col = t % gw;
+  const int64_t a0 = row * mh / gh, b0 = col * mw / gw;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t a = a0 > 0 ? a0 - 1 : 0; a <= a0 + 1 && a < mh; ++a) {
+    int64_t r0, r1;
+    bin_range(a, gh, mh, r0, r1);
+    if (row < r0 || row >= r1) continue;
+    for (int64_t b = b0 > 0 ? b0 - 1 : 0; b <= b0 + 1 && b < mw; ++b) {
+      int64_t c0, c1;
+      bin_range(b, gw, mw, c0, c1);
+      if (col < c0 || col >= c1) continue;
+      acc += *reinterpret_cast<const f32x4*>(dqlw + (bh * m + a * mw + b) * kD + 4 * dq4);
+    }
+  }
+  f32x4* p = reinterpret_cast<f32x4*>(dQ + (bh * N + t) * kD + 4 * dq4);
+  *p += acc;
+}
+
+template <class T>
+hipError_t launch_backward_t(const Shape& s, const BwPlan& bp, const BwWorkspace& ws,
+                             const void* Qv, const void* Kv, const void* Vv, const int32_t* idx,
+                             const int32_t* route, const float* dout, float* dQ, float* dK,
+                             float* dV, hipStream_t st, int first, int last) {
+  using E = typename T::elem;
+  const E* Q = static_cast<const E*>(Qv);
+  const E* K = static_cast<const E*>(Kv);
+  const E* V = static_cast<const E*>(Vv);
+  const E* ql = static_cast<const E*>(ws.fw.ql);
+  const int BH = static_cast<int>(s.BH);
+  const int mb = (s.m + 15) / 16;
+  const float c2 = s.scale * kLog2e;
+  hipError_t e = hipSuccess;
+  auto step = [&](int i) { return e == hipSuccess && i >= first && i <= last; };
+  if (step(kBwZero)) {
+    const int64_t n4 = s.BH * s.N * kD / 4;
+    int64_t blocks = (n4 + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(k_bw_zero, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
+                       reinterpret_cast<f32x4*>(dK), reinterpret_cast<f32x4*>(dV), n4);
+    e = hipGetLastError();
+  }
+  if (step(kBwPool)) e = launch_pool(s, Qv, ws.fw, nullptr, 0, s.BH, st);
+  if (step(kBwLandmarkFwd)) {
+    const dim3 grid(bp.lm_chunks, BH);
+    switch (mb) {
+      case 1: hipLaunchKernelGGL((k_bw_lmfwd<T, 1>), grid, dim3(256), 0, st, K, V, ql, s.N, s.m, bp.lm_chunk, c2, ws.lm_stats, ws.lm_acc); break;
+      case 2: hipLaunchKernelGGL((k_bw_lmfwd<T, 2>), grid, dim3(256), 0, st, K, V, ql, s.N, s.m, bp.lm_chunk, c2, ws.lm_stats, ws.lm_acc); break;
+      case 3: hipLaunchKernelGGL((k_bw_lmfwd<T, 3>), grid, dim3(256), 0, st, K, V, ql, s.N, s.m, bp.lm_chunk, c2, ws.lm_stats, ws.lm_acc); break;
+      default: hipLaunchKernelGGL((k_bw_lmfwd<T, 4>), grid, dim3(256), 0, st, K, V, ql, s.N, s.m, bp.lm_chunk, c2, ws.lm_stats, ws.lm_acc); break;
+    }
+    e = hipGetLastError();
+    if (e == hipSuccess) {
+      hipLaunchKernelGGL(k_bw_lmmerge, dim3((s.m + 3) / 4, BH), dim3(256), 0, st, ws.lm_stats,
+                         ws.lm_acc, s.m, 4 * bp.lm_chunks, ws.vl, ws.lse2);
+      e = hipGetLastError();
+    }
+  }
+  if (step(kBwBucket)) {
+    hipLaunchKernelGGL(k_bw_count, dim3(bp.nseg, BH), dim3(256), 0, st, route, s.N, s.m, bp.nseg,
+                       ws.counts);
+    e = hipGetLastError();
+    if (e == hipSuccess) {
+      hipLaunchKernelGGL(k_bw_prefix, dim3(s.m, BH), dim3(256), 0, st, ws.counts, s.m, bp.nseg,
+                         ws.colpre, ws.totals);
+      e = hipGetLastError();
+    }
+    if (e == hipSuccess) {
+      hipLaunchKernelGGL(k_bw_scatter, dim3((bp.nseg + 3) / 4, BH), dim3(256), 0, st, route,
+                         ws.counts, s.m, bp.nseg, s.N, bp.tpb, ws.totals, ws.colpre, ws.offsets,
+                         ws.item_start, ws.perm);
+      e = hipGetLastError();
+    }
+  }
+  if (step(kBwAttend)) {
+    hipLaunchKernelGGL(k_bw_attend<T>, dim3(bp.items, BH), dim3(256), 0, st, Q, K, V, ql, ws.vl,
+                       idx, ws.perm, ws.offsets, ws.item_start, bp.tpb, s.N, s.m, s.k, s.scale,
+                       dout, dQ, dK, dV, ws.part1, bp.items);
+    e = hipGetLastError();
+    if (e == hipSuccess) {
+      hipLaunchKernelGGL(k_bw_reduce1, dim3(s.m, BH), dim3(256), 0, st, ws.part1, ws.item_start,
+                         ws.vl, s.m, bp.items, ws.dql1, ws.dvl, ws.dd);
+      e = hipGetLastError();
+    }
+  }
+  if (step(kBwCross)) {
+    const dim3 grid(bp.cross_chunks, BH);
+    switch (mb) {
+      case 1: hipLaunchKernelGGL((k_bw_cross<T, 1>), grid, dim3(256), 0, st, K, V, ql, ws.dvl, ws.lse2, ws.dd, s.N, s.m, bp.cross_chunk, s.scale, dK, dV, ws.part2); break;
+      case 2: hipLaunchKernelGGL((k_bw_cross<T, 2>), grid, dim3(256), 0, st, K, V, ql, ws.dvl, ws.lse2, ws.dd, s.N, s.m, bp.cross_chunk, s.scale, dK, dV, ws.part2); break;
+      case 3: hipLaunchKernelGGL((k_bw_cross<T, 3>), grid, dim3(256), 0, st, K, V, ql, ws.dvl, ws.lse2, ws.dd, s.N, s.m, bp.cross_chunk, s.scale, dK, dV, ws.part2); break;
+      default: hipLaunchKernelGGL((k_bw_cross<T, 4>), grid, dim3(256), 0, st, K, V, ql, ws.dvl, ws.lse2, ws.dd, s.N, s.m, bp.cross_chunk, s.scale, dK, dV, ws.part2); break;
+    }
+    e = hipGetLastError();
+  }
+  if (step(kBwPoolBw)) {
+    hipLaunchKernelGGL(k_bw_reduce2, dim3(s.m, BH), dim3(256), 0, st, ws.part2,
+                       4 * bp.cross_chunks, ws.dql1, s.m, s.gh, s.gw, s.mh, s.mw, ws.dqlw);
+    e = hipGetLastError();
+    if (e == hipSuccess) {
+      hipLaunchKernelGGL(k_bw_poolbw, dim3(static_cast<unsigned>((s.N + 15) / 16), BH), dim3(256),
+                         0, st, ws.dqlw, s.N, s.m, s.gh, s.gw, s.mh, s.mw, dQ);
+      e = hipGetLastError();
+    }
+  }
+  return e;
+}
+
+}  // namespace
+
+BwPlan plan_backward(const Shape& s, int cus) {
+  BwPlan p;
+  // key chunks: about two blocks per CU over all heads, whole 64-key groups
+  auto chunk_for = [&](int64_t min_keys) {
+    int64_t c = (s.N * s.BH + 2 * cus - 1) / (2 * cus);
+    c = (c + 63) / 64 * 64;
+    if (c < min_keys) c = min_keys;
+    const int64_t whole = (s.N + 63) / 64 * 64;
+    if (c > whole) c = whole;
+    return c;
+  };
+  const int64_t lc = chunk_for(256);
+  p.lm_chunk = static_cast<int>(lc);
+  p.lm_chunks = static_cast<int>((s.N + lc - 1) / lc);
+  const int64_t cc = chunk_for(256);
+  p.cross_chunk = static_cast<int>(cc);
+  p.cross_chunks = static_cast<int>((s.N + cc - 1) / cc);
+  p.nseg = static_cast<int>((s.N + kRouteSeg - 1) / kRouteSeg);
+  // expert work items of up to tpb 64-query tiles, about two per CU
+  const int64_t tiles = (s.N + kAttendTile - 1) / kAttendTile;
+  int64_t tpb = (tiles * s.BH) / (2 * static_cast<int64_t>(cus));
+  tpb = tpb < 1 ? 1 : (tpb > 16 ? 16 : tpb);
+  p.tpb = static_cast<int>(tpb);
+  p.items = static_cast<int>((tiles + tpb - 1) / tpb + s.m);
+  return p;
+}
+
+size_t plan_bw_workspace(const Shape& s, const BwPlan& bp, BwWorkspace* ws, char* base) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char* {
+    char* p = base ? base + off : nullptr;
+    off += (bytes + 255) / 256 * 256;
+    return p;
+  };
+  const size_t BH = static_cast<size_t>(s.BH), es = s.dtype == MITA_BF16 ? 2 : 4;
+  const size_t m = static_cast<size_t>(s.m);
+  *ws = BwWorkspace{};
+  ws->fw.pool_part = reinterpret_cast<double*>(take(BH * m * s.pool_splits * kD * sizeof(double)));
+  ws->fw.ql = take(BH * m * kD * es);
+  const size_t p1 = BH * 4 * bp.lm_chunks * kMaxM;
+  ws->lm_stats = reinterpret_cast<float*>(take(p1 * 2 * sizeof(float)));
+  ws->lm_acc = reinterpret_cast<float*>(take(p1 * kD * sizeof(float)));
+  ws->vl = reinterpret_cast<float*>(take(BH * m * kD * sizeof(float)));
+  ws->lse2 = reinterpret_cast<float*>(take(BH * m * sizeof(float)));
+  ws->counts = reinterpret_cast<int32_t*>(take(BH * m * bp.nseg * 4));
+  ws->colpre = reinterpret_cast<int32_t*>(take(BH * m * bp.nseg * 4));
+  ws->totals = reinterpret_cast<int32_t*>(take(BH * m * 4));
+  ws->offsets = reinterpret_cast<int32_t*>(take(BH * (m + 1) * 4));
+  ws->item_start = reinterpret_cast<int32_t*>(take(BH * (m + 1) * 4));
+  ws->perm = reinterpret_cast<int32_t*>(take(BH * s.N * 4));
+  ws->part1 = reinterpret_cast<float*>(take(BH * bp.items * 2 * m * kD * sizeof(float)));
+  ws->dql1 = reinterpret_cast<float*>(take(BH * m * kD * sizeof(float)));
+  ws->dvl = reinterpret_cast<float*>(take(BH * m * kD * sizeof(float)));
+  ws->dd = reinterpret_cast<float*>(take(BH * m * sizeof(float)));
+  ws->part2 = reinterpret_cast<float*>(take(BH * 4 * bp.cross_chunks * kMaxM * kD * sizeof(float)));
+  ws->dqlw = reinterpret_cast<float*>(take(BH * m * kD * sizeof(float)));
+  return off;
+}
+
+hipError_t launch_backward(const Shape& s, const BwPlan& bp, const BwWorkspace& ws,
+                           const void* Q, const void* K, const void* V, const int32_t* idx,
+                           const int32_t* route, const float* dout, float* dQ, float* dK,
+                           float* dV, hipStream_t st, int first, int last) {
+  return s.dtype == MITA_BF16
+             ? launch_backward_t<BF16>(s, bp, ws, Q, K, V, idx, route, dout, dQ, dK, dV, st,
+                                       first, last)
+             : launch_backward_t<F32>(s, bp, ws, Q, K, V, idx, route, dout, dQ, dK, dV, st, first,
+                                      last);
+}
+
+}  // namespace mita

@@ -41,11 +41,14 @@ enum Stage {
   kStageMerge,
   kStageAttend,
   kStageSmall,  // the one-launch path for short sequences (all five steps)
-  kStageCount
+  kStageBw0,    // the backward pass's steps (BwStep order) follow
+  kStageCount = kStageBw0 + kBwStepCount
 };
-const char* kStageNames[kStageCount] = {"pool",          "landmark_threshold", "route",
-                                        "landmark_scan", "landmark_merge",     "expert_attend",
-                                        "single_launch"};
+const char* kStageNames[kStageCount] = {
+    "pool",         "landmark_threshold", "route",           "landmark_scan",
+    "landmark_merge", "expert_attend",    "single_launch",   "bw_zero",
+    "bw_pool",      "bw_landmark_fwd",    "bw_bucket",       "bw_attend",
+    "bw_cross",     "bw_pool_grad"};
 
 struct Profiler {
   bool enabled = false;
@@ -593,9 +596,75 @@ int forward_impl(const void* Q, const void* K, const void* V, int dtype, int64_t
   }
 }
 
+// The backward pass: validation, work space, then its steps on `stream`.
+int backward_impl(const void* Q, const void* K, const void* V, int dtype, int64_t B, int64_t H,
+                  int64_t N, int64_t d, const mita_grid* grid, int64_t m, int64_t k, float scale,
+                  const int32_t* idx, const int32_t* routes, const float* dout, float* dQ,
+                  float* dK, float* dV, void* stream) {
+  try {
+    g_last_error.clear();
+    if (!idx || !routes || !dout || !dQ || !dK || !dV)
+      return fail(MITA_ERR_INVALID_ARG, "idx, routes, dout, dQ, dK and dV must be non-null");
+    Shape s;
+    int rc = validate(Q, K, V, dtype, B, H, N, d, grid, m, k, scale, dQ, idx, routes, nullptr, &s);
+    if (rc != MITA_OK) return rc;
+    for (const void* p : {static_cast<const void*>(dout), static_cast<const void*>(dK),
+                          static_cast<const void*>(dV)})
+      if (!aligned16(p)) return fail(MITA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    if (dQ == dK || dQ == dV || dK == dV)
+      return fail(MITA_ERR_INVALID_ARG, "dQ, dK and dV must be distinct buffers");
+    const char* inject = std::getenv("MITA_FAULT_INJECT");
+    if (inject && std::strcmp(inject, "alloc") == 0)
+      return fail(MITA_ERR_OOM, "work-space allocation failed (injected by MITA_FAULT_INJECT)");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    derive(s, device_cus());  // the pooling geometry (pool_splits, pool_direct)
+    const BwPlan bp = plan_backward(s, device_cus());
+    BwWorkspace ws;
+    const size_t bytes = plan_bw_workspace(s, bp, &ws, nullptr);
+    DeviceState* ds = device_state();
+    if (ds == nullptr) return fail(MITA_ERR_HIP, "no current HIP device");
+    std::lock_guard<std::mutex> lk(ds->mu);
+    void* base = nullptr;
+    DeviceState::Ws* entry = nullptr;
+    rc = workspace_for(*ds, st, bytes, &base, &entry);
+    if (rc != MITA_OK) {
+      (void)hipGetLastError();
+      return rc;
+    }
+    plan_bw_workspace(s, bp, &ws, static_cast<char*>(base));
+    hipError_t e = (inject && std::strcmp(inject, "launch") == 0) ? hipErrorLaunchFailure
+                                                                  : hipSuccess;
+    int where = 0;
+    for (int i = 0; i < kBwStepCount && e == hipSuccess; ++i) {
+      where = i;
+      StageTimer t(kStageBw0 + i, st, true);
+      e = launch_backward(s, bp, ws, Q, K, V, idx, routes, dout, dQ, dK, dV, st, i, i);
+    }
+    if (g_prof.enabled && e == hipSuccess) g_prof.calls += 1;
+    const hipError_t er = hipEventRecord(entry->done, st);  // the block is in use until here
+    if (e != hipSuccess)
+      return fail(MITA_ERR_HIP, std::string("launch of backward stage ") +
+                                    kStageNames[kStageBw0 + where] + " failed: " +
+                                    hipGetErrorString(e));
+    if (er != hipSuccess)
+      return fail(MITA_ERR_HIP, std::string("work-space event: ") + hipGetErrorString(er));
+    return MITA_OK;
+  } catch (...) {
+    return fail(MITA_ERR_INTERNAL, "unexpected exception inside mita_backward");
+  }
+}
+
 }  // namespace
 
 extern "C" {
+
+int mita_backward(const void* Q, const void* K, const void* V, int dtype, int64_t B, int64_t H,
+                  int64_t N, int64_t d, const mita_grid* grid, int64_t m, int64_t k,
+                  float scale, const int32_t* idx, const int32_t* routes, const float* dout,
+                  float* dQ, float* dK, float* dV, void* stream) {
+  return backward_impl(Q, K, V, dtype, B, H, N, d, grid, m, k, scale, idx, routes, dout, dQ, dK,
+                       dV, stream);
+}
 
 int mita_forward_ex(const void* Q, const void* K, const void* V, int dtype, int64_t B, int64_t H,
                     int64_t N, int64_t d, const mita_grid* grid, int64_t m, int64_t k,

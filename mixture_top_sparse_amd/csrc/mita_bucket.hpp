@@ -162,6 +162,33 @@ __device__ __forceinline__ void scatter_segment(
   }
 }
 
+// A work item of the expert-grouped attention kernels (forward and backward).
+struct TileInfo {
+  int e;      // expert
+  int qb;     // first perm slot of this work item
+  int qe;     // one past its last perm slot
+};
+
+// Work item t of a head covers up to `tpb` consecutive 64-query tiles of one
+// expert; item_start[e] is the first item of expert e (exclusive scan of
+// ceil(tiles_e / tpb)).  item_start is non-decreasing, so t's expert is the
+// number of experts e < m - 1 whose successor starts at or before t: one
+// load per lane (m <= 64) and a ballot, instead of a chain of m dependent
+// loads.
+__device__ __forceinline__ bool find_item(const int32_t* __restrict__ item_start,
+                                          const int32_t* __restrict__ offsets, int m, int tpb,
+                                          int t, TileInfo& ti) {
+  const int l = lane_id();
+  const int next = l < m - 1 ? item_start[l + 1] : INT32_MAX;
+  if (t >= item_start[m]) return false;
+  const int e = __popcll(ballot(next <= t));
+  const int j0 = (t - item_start[e]) * tpb;
+  ti.e = e;
+  ti.qb = offsets[e] + kAttendTile * j0;
+  ti.qe = min(ti.qb + kAttendTile * tpb, static_cast<int>(offsets[e + 1]));
+  return true;
+}
+
 // Arguments of the bucket bodies, passed through the scan and merge launches.
 struct BucketArgs {
   const int32_t* route;

@@ -119,4 +119,55 @@ hipError_t launch_small(const Shape& s, const void* Q, const void* K, const void
 hipError_t launch_dense(int dtype, const void* Q, const void* K, const void* V, int64_t BH,
                         int64_t N, int64_t d, float scale, float* out, hipStream_t st);
 
+// ---------------------------------------------------------------------------
+// backward pass (experts and routes given)
+// ---------------------------------------------------------------------------
+
+// its steps, in launch order (launch_backward runs steps first..last)
+enum BwStep {
+  kBwZero = 0,     // dK = dV = 0
+  kBwPool,         // Ql, as the forward computes it
+  kBwLandmarkFwd,  // Vl and the landmarks' log-sum-exp (partials, merge)
+  kBwBucket,       // queries grouped by the given routes
+  kBwAttend,       // the output softmax per expert item, then dVl, dQl part, D
+  kBwCross,        // the landmark cross-attention's backward
+  kBwPoolBw,       // dQl in full, spread back over the windows into dQ
+  kBwStepCount
+};
+
+struct BwPlan {
+  int lm_chunk = 0, lm_chunks = 0;        // keys per landmark-forward block, blocks per head
+  int cross_chunk = 0, cross_chunks = 0;  // the same for the cross-attention backward
+  int nseg = 0;                           // routing segments per head (kRouteSeg queries)
+  int tpb = 1;                            // 64-query tiles per expert work item
+  int items = 0;                          // upper bound of work items per head
+};
+
+struct BwWorkspace {
+  Workspace fw;                 // pool_part and ql only
+  float* lm_stats = nullptr;    // [BH][4 lm_chunks][64][2] (max in log2 units, sum)
+  float* lm_acc = nullptr;      // [BH][4 lm_chunks][64][64] unnormalised A.V
+  float* vl = nullptr;          // [BH][m][64]
+  float* lse2 = nullptr;        // [BH][m] log2-sum-exp2 of the scaled logits (log2 units)
+  int32_t* counts = nullptr;    // [BH][m][nseg]
+  int32_t* colpre = nullptr;    // [BH][m][nseg]
+  int32_t* totals = nullptr;    // [BH][m]
+  int32_t* offsets = nullptr;   // [BH][m+1]
+  int32_t* item_start = nullptr;// [BH][m+1]
+  int32_t* perm = nullptr;      // [BH][N]
+  float* part1 = nullptr;       // [BH][items][2][m][64] per-item dQl, dVl
+  float* dql1 = nullptr;        // [BH][m][64] the expert step's dQl
+  float* dvl = nullptr;         // [BH][m][64]
+  float* dd = nullptr;          // [BH][m] dVl . Vl
+  float* part2 = nullptr;       // [BH][4 cross_chunks][64][64] the cross step's dQl
+  float* dqlw = nullptr;        // [BH][m][64] dQl / |window|
+};
+
+BwPlan plan_backward(const Shape& s, int cus);
+size_t plan_bw_workspace(const Shape& s, const BwPlan& bp, BwWorkspace* ws, char* base);
+hipError_t launch_backward(const Shape& s, const BwPlan& bp, const BwWorkspace& ws,
+                           const void* Q, const void* K, const void* V, const int32_t* idx,
+                           const int32_t* route, const float* dout, float* dQ, float* dK,
+                           float* dV, hipStream_t st, int first, int last);
+
 }  // namespace mita

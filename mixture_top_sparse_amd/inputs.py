@@ -107,6 +107,29 @@ def generate(w: Workload) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
     return Q, K, V
 
 
+def generate_dout(w: Workload) -> np.ndarray:
+    """The gradient of a loss with respect to the output, for the backward
+    pass: [B, H, N, d] fp32, i.i.d. N(0, 1) from seed 1000 + w.seed."""
+    rng = np.random.Generator(np.random.PCG64(1000 + w.seed))
+    return rng.standard_normal((w.B, w.H, w.N, w.d), dtype=np.float32)
+
+
+def generate_selection(w: Workload, seed: int) -> tuple[np.ndarray, np.ndarray]:
+    """Arbitrary experts and routes (not the ones the method would select):
+    idx [B, H, m, k] with keys drawn uniformly, repeats across experts
+    allowed, and routes [B, H, N] drawn so that a few experts get most of the
+    queries and some none.  For the backward pass, which takes both as
+    given."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    idx = rng.integers(0, w.N, size=(w.B, w.H, w.m, w.k)).astype(np.int32)
+    p = rng.dirichlet(np.full(w.m, 0.3), size=(w.B, w.H))
+    routes = np.empty((w.B, w.H, w.N), np.int32)
+    for b in range(w.B):
+        for h in range(w.H):
+            routes[b, h] = rng.choice(w.m, size=w.N, p=p[b, h])
+    return idx, routes
+
+
 def to_torch(arrs, dtype: str, device: str = "cpu"):
     """Convert fp32 numpy arrays to torch tensors of the workload's storage
     type (bf16 by round-to-nearest-even)."""

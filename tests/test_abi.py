@@ -171,8 +171,51 @@ def test_profiler_without_calls(L):
     mts.mita_profile_enable(True)
     ms, calls = mts.mita_profile_read()
     assert calls == 0 and list(ms) == ["pool", "landmark_threshold", "route", "landmark_scan",
-                                       "landmark_merge", "expert_attend", "single_launch"]
+                                       "landmark_merge", "expert_attend", "single_launch",
+                                       "bw_zero", "bw_pool", "bw_landmark_fwd", "bw_bucket",
+                                       "bw_attend", "bw_cross", "bw_pool_grad"]
     mts.mita_profile_enable(False)
+
+
+# ---- mita_backward ---------------------------------------------------------
+
+
+def bw_call(L, **over):
+    a = dict(Q=A, K=A, V=A, dtype=1, B=2, H=3, N=4096, d=64, grid=None, m=64, k=64, scale=0.125,
+             idx=A, route=A, dout=A, dQ=A, dK=A + 0x100, dV=A + 0x200, stream=None)
+    a.update(over)
+    g = None if a["grid"] is None else ctypes.byref(mts.MitaGrid(*a["grid"]))
+    return L.mita_backward(a["Q"], a["K"], a["V"], a["dtype"], a["B"], a["H"], a["N"], a["d"], g,
+                           a["m"], a["k"], a["scale"], a["idx"], a["route"], a["dout"], a["dQ"],
+                           a["dK"], a["dV"], a["stream"])
+
+
+BW_INVALID = dict(
+    {k_: v for k_, v in INVALID.items()
+     if k_ not in ("null_out", "misaligned_out", "misaligned_dbg")},
+    null_dout=dict(dout=None), null_dq=dict(dQ=None), null_dk=dict(dK=None),
+    null_dv=dict(dV=None), misaligned_dout=dict(dout=A + 4), misaligned_dk=dict(dK=A + 8),
+    same_dk_dv=dict(dV=A + 0x100), same_dq_dk=dict(dK=A),
+)
+
+
+@pytest.mark.parametrize("case", sorted(BW_INVALID))
+def test_backward_invalid_arguments(L, case):
+    """mita_backward validates on the host like mita_forward, plus its own
+    gradient buffers, before any HIP call."""
+    assert bw_call(L, **BW_INVALID[case]) == mts.MITA_ERR_INVALID_ARG
+    assert mts.mita_last_error() != ""
+
+
+@pytest.mark.parametrize("case", sorted(UNSUPPORTED))
+def test_backward_unsupported(L, case):
+    assert bw_call(L, **UNSUPPORTED[case]) == mts.MITA_ERR_UNSUPPORTED
+
+
+def test_backward_injected_allocation_failure(L, monkeypatch):
+    monkeypatch.setenv("MITA_FAULT_INJECT", "alloc")
+    assert bw_call(L) == mts.MITA_ERR_OOM
+    assert "injected" in mts.mita_last_error()
 
 
 # ---- mita_dense_attention (the full-attention baseline) ------------------

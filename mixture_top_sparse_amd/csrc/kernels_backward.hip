@@ -11,7 +11,7 @@
 //   out[q] = sum_p w_qp val_p,  w_q = softmax(s q . key_p) over the m + k
 //   pairs p of q (keys [Ql; K[idx[route[q]]]], values [Vl; V[idx[...]]]).
 // Its reverse, in launch order (all on the caller's stream):
-//   zero      dK = dV = 0 (filled by a kernel: the expert step adds atomically)
+//   zero      the expert step's per-(expert, key) sums = 0 (a fill kernel)
 //   pool      Ql exactly as the forward computes it (the pooling kernel)
 //   lmfwd     per key chunk: online-softmax partials of A V   (fp32 MFMA)
 //   lmmerge   Vl and the log-sum-exp of each landmark row
@@ -20,22 +20,23 @@
 //               g_qp = s w_qp (dout_q . val_p - dout_q . out_q)
 //               dQ[q] = sum_p g_qp key_p          (stored: complete but for
 //                                                   the pooling term)
-//               dK/dV of the expert's raw keys += g^T Q, w^T dout (atomics)
+//               sums per (expert, key) += g^T Q, w^T dout (atomics)
 //               dQl/dVl partials of the item     (summed by reduce1)
 //   reduce1   dVl, the expert step's dQl, and D_i = dVl_i . Vl_i
 //   cross     per key chunk: h_it = s A_it (dVl_i . V_t - D_i);
-//               dK[t] += sum_i h_it Ql_i,  dV[t] += sum_i A_it dVl_i
-//               (read-modify-write: one block owns each key), and partials
-//               of dQl += h K
+//               dK[t] = sum_i h_it Ql_i,  dV[t] = sum_i A_it dVl_i
+//               (stored: one block owns each key), and partials of
+//               dQl += h K
+//   keyadd    dK, dV at each expert key += the expert step's sums (atomics)
 //   reduce2   dQl in full, divided by each window's size
 //   poolbw    dQ[t] += sum over the windows i containing t of dQl_i / |W_i|
 // Every contraction runs on v_mfma_f32_16x16x4_f32 (fp32 operands, fp32
 // accumulation), so the gradients carry fp32 rounding only.
 //
 // Roofline: per (token, head) the pass reads Q, K, V (3 d e bytes, e the
-// input element size) and dout (4d), and writes dQ, dK, dV (12d) plus their
-// read-modify-writes (8d each for dQ in poolbw and for dK, dV in cross):
-// about 3de + 40d bytes.  The contractions cost about 2 d (5 (m + k) + 7 m)
+// input element size; K and V twice, in the landmark forward and the cross
+// step) and dout (4d), and writes dQ, dK, dV (12d) plus dQ's
+// read-modify-write in poolbw (8d): about 5de + 24d bytes.  The contractions cost about 2 d (5 (m + k) + 7 m)
 // flops per (token, head) at fp32 MFMA rate, which exceeds the bytes' time
 // at 157 TFLOP/s for m = k = 64: the pass is MFMA-bound (fp32).
 #include "mita.h"
@@ -68,6 +69,55 @@ __device__ __forceinline__ void load8(const float* __restrict__ p, float (&v)[8]
     v[4 + i] = b[i];
   }
 }
+// eight consecutive elements held in their storage type (a load in flight
+// while the wave computes), converted to fp32 when stored to LDS
+template <class T>
+struct Raw8;
+template <>
+struct Raw8<BF16> {
+  u32x4 w;
+  __device__ void load(const uint16_t* __restrict__ p) { w = *reinterpret_cast<const u32x4*>(p); }
+  __device__ void zero() { w = u32x4{0u, 0u, 0u, 0u}; }
+  __device__ void store(float* dst) const {
+    *reinterpret_cast<f32x4*>(dst) = f32x4{__uint_as_float(w[0] << 16),
+                                           __uint_as_float(w[0] & 0xFFFF0000u),
+                                           __uint_as_float(w[1] << 16),
+                                           __uint_as_float(w[1] & 0xFFFF0000u)};
+    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{__uint_as_float(w[2] << 16),
+                                               __uint_as_float(w[2] & 0xFFFF0000u),
+                                               __uint_as_float(w[3] << 16),
+                                               __uint_as_float(w[3] & 0xFFFF0000u)};
+  }
+};
+template <>
+struct Raw8<F32> {
+  f32x4 a, b;
+  __device__ void load(const float* __restrict__ p) {
+    a = *reinterpret_cast<const f32x4*>(p);
+    b = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  __device__ void zero() { a = b = f32x4{0.f, 0.f, 0.f, 0.f}; }
+  __device__ void store(float* dst) const {
+    *reinterpret_cast<f32x4*>(dst) = a;
+    *reinterpret_cast<f32x4*>(dst + 4) = b;
+  }
+};
+
+// four consecutive elements, as fp32
+__device__ __forceinline__ void load4(const uint16_t* __restrict__ p, float (&v)[4]) {
+  const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+  v[0] = __uint_as_float(w[0] << 16);
+  v[1] = __uint_as_float(w[0] & 0xFFFF0000u);
+  v[2] = __uint_as_float(w[1] << 16);
+  v[3] = __uint_as_float(w[1] & 0xFFFF0000u);
+}
+__device__ __forceinline__ void load4(const float* __restrict__ p, float (&v)[4]) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  v[0] = a[0];
+  v[1] = a[1];
+  v[2] = a[2];
+  v[3] = a[3];
+}
 __device__ __forceinline__ void zero8(float (&v)[8]) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = 0.f;
@@ -89,8 +139,8 @@ __device__ __forceinline__ void bin_range(int64_t a, int64_t g, int64_t n, int64
 }
 
 // ---------------------------------------------------------------------------
-// zero fill (dK, dV) — a kernel, not a memset, so the sequence stays
-// capturable in a graph
+// zero fill (the expert step's per-(expert, key) sums) — a kernel, not a
+// memset, so the sequence stays capturable in a graph
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_bw_zero(f32x4* __restrict__ a, f32x4* __restrict__ b,
                                                  int64_t n4) {
@@ -113,7 +163,7 @@ __global__ __launch_bounds__(256) void k_bw_zero(f32x4* __restrict__ a, f32x4* _
 // keeps each landmark's rescale inside its own lanes.  Partial p = 4 chunk +
 // w: stats [BH][P][64][2] (max in log2 units, sum), acc [BH][P][64][64].
 template <class T, int MB>
-__global__ __launch_bounds__(256) void k_bw_lmfwd(const typename T::elem* __restrict__ K,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_bw_lmfwd(const typename T::elem* __restrict__ K,
                                                   const typename T::elem* __restrict__ V,
                                                   const typename T::elem* __restrict__ ql,
                                                   int64_t N, int m, int csize, float c2,
@@ -148,23 +198,33 @@ __global__ __launch_bounds__(256) void k_bw_lmfwd(const typename T::elem* __rest
   }
   float* sK = sKV[w][0];
   float* sV = sKV[w][1];
-  for (int64_t t0 = k0 + 16 * w; t0 < k1; t0 += 64) {
-    // this wave's 16 keys (its LDS accesses complete in program order)
+  // this wave's 16 keys, one group ahead: lane l holds chunks l and l + 64
+  // (row u / 8, elements 8 (u % 8) ..) of K and V
+  Raw8<T> rk[2], rv[2];
+  auto fetch = [&](int64_t t0) {
 #pragma unroll
-    for (int u = l; u < 128; u += 64) {
-      const int row = u >> 3, j = u & 7;
-      const int64_t t = t0 + row;
-      float kv[8], vv[8];
+    for (int h = 0; h < 2; ++h) {
+      const int u = l + 64 * h;
+      const int64_t t = t0 + (u >> 3);
       if (t < k1) {
-        load8(K + (bh * N + t) * kD + 8 * j, kv);
-        load8(V + (bh * N + t) * kD + 8 * j, vv);
+        rk[h].load(K + (bh * N + t) * kD + 8 * (u & 7));
+        rv[h].load(V + (bh * N + t) * kD + 8 * (u & 7));
       } else {
-        zero8(kv);
-        zero8(vv);
+        rk[h].zero();
+        rv[h].zero();
       }
-      store8(sK + row * kBwSt + 8 * j, kv);
-      store8(sV + row * kBwSt + 8 * j, vv);
     }
+  };
+  fetch(k0 + 16 * w);
+  for (int64_t t0 = k0 + 16 * w; t0 < k1; t0 += 64) {
+    // (the wave's LDS accesses complete in program order)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int u = l + 64 * h;
+      rk[h].store(sK + (u >> 3) * kBwSt + 8 * (u & 7));
+      rv[h].store(sV + (u >> 3) * kBwSt + 8 * (u & 7));
+    }
+    fetch(t0 + 64);
     float a[16];
 #pragma unroll
     for (int s = 0; s < 16; ++s) a[s] = sK[c16 * kBwSt + 4 * s + g];
@@ -299,34 +359,38 @@ __global__ __launch_bounds__(256) void k_bw_scatter(const int32_t* __restrict__ 
 // the output softmax, per expert work item
 // ---------------------------------------------------------------------------
 
-// Block (work item, head), four waves.  The item's expert is staged once as
-// fp32 pair rows: keys [Ql; 0; K_e; 0] and values [Vl; 0; V_e; 0] with the
-// landmarks padded to MP = 16 ceil(m / 16) rows and the raw keys to KP rows
-// (PP = MP + KP <= 128, NB = PP / 16 column blocks).  Queries go 16 at a
-// time: wave w computes the logits and dout . value of column blocks w and
-// w + 4 (queries on rows, pairs on columns), the row max and the sums over
-// the pairs meet in LDS, and then
+// Block (work item, head), eight waves in two halves.  The item's expert
+// is staged once as fp32 pair rows: keys [Ql; 0; K_e; 0] and values
+// [Vl; 0; V_e; 0] with the landmarks padded to MP = 16 ceil(m / 16) rows and
+// the raw keys to KP rows (PP = MP + KP <= 128, NB = PP / 16 column
+// blocks).  Each half takes every other group of 16 queries (its next
+// group's rows are loaded while it computes the current one); within a
+// half, wave wl computes the logits and dout . value of column blocks wl
+// and wl + 4 (queries on rows, pairs on columns), the row max and the sums
+// over the pairs meet in LDS, and then
 //   dKey[p] += sum_q g_qp q,  dVal[p] += sum_q w_qp dout_q
 // run with the wave's own columns as the MFMA A operand straight from the
 // accumulator layout (pairs on the output rows), while dQ = g [keys] takes
-// g through LDS, wave w producing dims 16 w .. 16 w + 15 of the 16 queries.
+// g through LDS, wave wl producing dims 16 wl .. 16 wl + 15 of the 16
+// queries.  At the end the second half's sums are added to the first's.
 template <class T>
-__global__ __launch_bounds__(256) void k_bw_attend(
+__global__ __launch_bounds__(512) void k_bw_attend(
     const typename T::elem* __restrict__ Q, const typename T::elem* __restrict__ K,
     const typename T::elem* __restrict__ V, const typename T::elem* __restrict__ ql,
     const float* __restrict__ vl, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ item_start, int tpb, int64_t N, int m, int k, float scale,
-    const float* __restrict__ dout, float* __restrict__ dQ, float* __restrict__ dK,
-    float* __restrict__ dV, float* __restrict__ part, int items) {
+    const float* __restrict__ dout, float* __restrict__ dQ, float* __restrict__ dke,
+    float* __restrict__ dve, float* __restrict__ part, int items) {
   __shared__ __attribute__((aligned(16))) float sPk[kBwPairs * kBwSt];
   __shared__ __attribute__((aligned(16))) float sPv[kBwPairs * kBwSt];
-  __shared__ __attribute__((aligned(16))) float sQ[16 * kBwSt];
-  __shared__ __attribute__((aligned(16))) float sG[16 * kBwSt];
-  __shared__ __attribute__((aligned(16))) float sGs[16 * kBwGsSt];
-  __shared__ float sRed[3][4][16];
-  __shared__ int sQid[16];
+  __shared__ __attribute__((aligned(16))) float sQ[2][16 * kBwSt];
+  __shared__ __attribute__((aligned(16))) float sG[2][16 * kBwSt];
+  __shared__ __attribute__((aligned(16))) float sGs[2][16 * kBwGsSt];
+  __shared__ float sRed[2][3][4][16];
+  __shared__ int sQid[2][16];
   const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
+  const int hf = w >> 2, wl = w & 3;
   const int tid = threadIdx.x;
   const int64_t bh = blockIdx.y;
   TileInfo ti;
@@ -335,7 +399,7 @@ __global__ __launch_bounds__(256) void k_bw_attend(
   const int MP = (m + 15) & ~15, KP = (k + 15) & ~15;
   const int PP = MP + KP, NB = PP / 16;
   const int32_t* ex = idx + (bh * m + ti.e) * k;
-  for (int u = tid; u < PP * 8; u += 256) {
+  for (int u = tid; u < PP * 8; u += 512) {
     const int row = u >> 3, j = u & 7;
     float kv[8], vv[8];
     if (row < m) {
@@ -361,36 +425,45 @@ __global__ __launch_bounds__(256) void k_bw_attend(
       aK[cb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
       aV[cb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-  for (int q0 = ti.qb; q0 < ti.qe; q0 += 16) {
-    const int nv = ti.qe - q0 < 16 ? ti.qe - q0 : 16;
-    __syncthreads();  // the expert staged; the previous group's LDS reads done
-    if (tid < 128) {
-      const int row = tid >> 3, j = tid & 7;
-      float qv[8], gv[8];
-      if (row < nv) {
-        const int64_t q = clamp64(perm[bh * N + q0 + row], N);
-        load8(Q + (bh * N + q) * kD + 8 * j, qv);
-        load8(dout + (bh * N + q) * kD + 8 * j, gv);
-        if (j == 0) sQid[row] = static_cast<int>(q);
-      } else {
-        zero8(qv);
-        zero8(gv);
-      }
-      store8(sQ + row * kBwSt + 8 * j, qv);
-      store8(sG + row * kBwSt + 8 * j, gv);
+  // the half's query rows: thread (row, 4 dims), one group ahead
+  const int srow = (tid & 255) >> 4, sc4 = tid & 15;
+  float pq[4], pg[4];
+  int pid = 0;
+  auto fetch = [&](int q0h) {
+    if (q0h + srow < ti.qe) {
+      const int64_t q = clamp64(perm[bh * N + q0h + srow], N);
+      load4(Q + (bh * N + q) * kD + 4 * sc4, pq);
+      load4(dout + (bh * N + q) * kD + 4 * sc4, pg);
+      pid = static_cast<int>(q);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pq[i] = pg[i] = 0.f;
     }
+  };
+  fetch(ti.qb + 16 * hf);
+  float* const hQ = sQ[hf];
+  float* const hG = sG[hf];
+  float* const hGs = sGs[hf];
+  for (int qq = ti.qb; qq < ti.qe; qq += 32) {
+    const int q0 = qq + 16 * hf;
+    const int nv = ti.qe - q0 < 0 ? 0 : (ti.qe - q0 < 16 ? ti.qe - q0 : 16);
+    __syncthreads();  // the expert staged; the previous groups' LDS reads done
+    *reinterpret_cast<f32x4*>(hQ + srow * kBwSt + 4 * sc4) = f32x4{pq[0], pq[1], pq[2], pq[3]};
+    *reinterpret_cast<f32x4*>(hG + srow * kBwSt + 4 * sc4) = f32x4{pg[0], pg[1], pg[2], pg[3]};
+    if (sc4 == 0) sQid[hf][srow] = pid;
+    fetch(q0 + 32);
     __syncthreads();
     float aq[16], ag[16];
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
-      aq[s] = sQ[c16 * kBwSt + 4 * s + g];
-      ag[s] = sG[c16 * kBwSt + 4 * s + g];
+      aq[s] = hQ[c16 * kBwSt + 4 * s + g];
+      ag[s] = hG[c16 * kBwSt + 4 * s + g];
     }
     f32x4 S[2], dW[2];
     float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      const int pb = w + 4 * cb;
+      const int pb = wl + 4 * cb;
       S[cb] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
       dW[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (pb < NB) {  // wave-uniform
@@ -410,21 +483,23 @@ __global__ __launch_bounds__(256) void k_bw_attend(
         dW[cb] = d4;
       }
     }
-    // row (query) statistics over all pairs: within 16 lanes, then across waves
+    // row (query) statistics over all pairs: within 16 lanes, then across
+    // the half's four waves
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       mx[r] = xor_max(mx[r], 1);
       mx[r] = xor_max(mx[r], 2);
       mx[r] = xor_max(mx[r], 4);
       mx[r] = xor_max(mx[r], 8);
-      if (c16 == 0) sRed[0][w][4 * g + r] = mx[r];
+      if (c16 == 0) sRed[hf][0][wl][4 * g + r] = mx[r];
     }
     __syncthreads();
     float Mr[4], z[4], y[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 4 * g + r;
-      Mr[r] = fmaxf(fmaxf(sRed[0][0][row], sRed[0][1][row]), fmaxf(sRed[0][2][row], sRed[0][3][row]));
+      Mr[r] = fmaxf(fmaxf(sRed[hf][0][0][row], sRed[hf][0][1][row]),
+                    fmaxf(sRed[hf][0][2][row], sRed[hf][0][3][row]));
       z[r] = 0.f;
       y[r] = 0.f;
     }
@@ -445,8 +520,8 @@ __global__ __launch_bounds__(256) void k_bw_attend(
         y[r] = xor_sum(y[r], mk);
       }
       if (c16 == 0) {
-        sRed[1][w][4 * g + r] = z[r];
-        sRed[2][w][4 * g + r] = y[r];
+        sRed[hf][1][wl][4 * g + r] = z[r];
+        sRed[hf][2][wl][4 * g + r] = y[r];
       }
     }
     __syncthreads();
@@ -454,8 +529,10 @@ __global__ __launch_bounds__(256) void k_bw_attend(
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 4 * g + r;
-      const float Z = sRed[1][0][row] + sRed[1][1][row] + sRed[1][2][row] + sRed[1][3][row];
-      const float Y = sRed[2][0][row] + sRed[2][1][row] + sRed[2][2][row] + sRed[2][3][row];
+      const float Z = sRed[hf][1][0][row] + sRed[hf][1][1][row] + sRed[hf][1][2][row] +
+                      sRed[hf][1][3][row];
+      const float Y = sRed[hf][2][0][row] + sRed[hf][2][1][row] + sRed[hf][2][2][row] +
+                      sRed[hf][2][3][row];
       const float inv = row < nv ? 1.f / Z : 0.f;  // padding rows contribute nothing
       const float c = Y / Z;                       // dout . out of this query
 #pragma unroll
@@ -466,52 +543,77 @@ __global__ __launch_bounds__(256) void k_bw_attend(
     }
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      const int pb = w + 4 * cb;
+      const int pb = wl + 4 * cb;
       if (pb >= NB) continue;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sGs[(4 * g + r) * kBwGsSt + 16 * pb + c16] = Gs[cb][r];
+      for (int r = 0; r < 4; ++r) hGs[(4 * g + r) * kBwGsSt + 16 * pb + c16] = Gs[cb][r];
       // pairs on the output rows: A = g^T (pair c16, query 4g + r), B = Q / dout rows
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          aK[cb][db] = mfma_f32(Gs[cb][r], sQ[(4 * g + r) * kBwSt + 16 * db + c16], aK[cb][db]);
-          aV[cb][db] = mfma_f32(Wt[cb][r], sG[(4 * g + r) * kBwSt + 16 * db + c16], aV[cb][db]);
+          aK[cb][db] = mfma_f32(Gs[cb][r], hQ[(4 * g + r) * kBwSt + 16 * db + c16], aK[cb][db]);
+          aV[cb][db] = mfma_f32(Wt[cb][r], hG[(4 * g + r) * kBwSt + 16 * db + c16], aV[cb][db]);
         }
     }
     __syncthreads();
-    // dQ (16 queries x dims 16w .. 16w + 15) = g [keys]
+    // dQ (16 queries x dims 16 wl .. 16 wl + 15) = g [keys]
     f32x4 dq = {0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < 4 * NB; ++s)
-      dq = mfma_f32(sGs[c16 * kBwGsSt + 4 * s + g], sPk[(4 * s + g) * kBwSt + 16 * w + c16], dq);
+      dq = mfma_f32(hGs[c16 * kBwGsSt + 4 * s + g], sPk[(4 * s + g) * kBwSt + 16 * wl + c16], dq);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 4 * g + r;
-      if (row < nv) dQ[(bh * N + sQid[row]) * kD + 16 * w + c16] = dq[r];
+      if (row < nv) dQ[(bh * N + sQid[hf][row]) * kD + 16 * wl + c16] = dq[r];
     }
   }
-  // the item's sums: landmark rows to its partial, raw-key rows to dK / dV
-  float* pq = part + ((bh * items + blockIdx.x) * 2) * static_cast<int64_t>(m) * kD;
-  float* pv = pq + static_cast<int64_t>(m) * kD;
+  // the second half's sums into the first's (through the staged expert's LDS)
+  __syncthreads();
+  if (hf == 1) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const int pb = wl + 4 * cb;
+      if (pb >= NB) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          sPk[(16 * pb + 4 * g + r) * kBwSt + 16 * db + c16] = aK[cb][db][r];
+          sPv[(16 * pb + 4 * g + r) * kBwSt + 16 * db + c16] = aV[cb][db][r];
+        }
+    }
+  }
+  __syncthreads();
+  if (hf == 1) return;
+  // the item's sums: landmark rows to its partial, raw-key rows to the
+  // expert's key sums
+  float* pq_ = part + ((bh * items + blockIdx.x) * 2) * static_cast<int64_t>(m) * kD;
+  float* pv_ = pq_ + static_cast<int64_t>(m) * kD;
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
-    const int pb = w + 4 * cb;
+    const int pb = wl + 4 * cb;
     if (pb >= NB) continue;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int p = 16 * pb + 4 * g + r;
+      float sk[4], sv[4];
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        sk[db] = aK[cb][db][r] + sPk[p * kBwSt + 16 * db + c16];
+        sv[db] = aV[cb][db][r] + sPv[p * kBwSt + 16 * db + c16];
+      }
       if (p < m) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          pq[p * kD + 16 * db + c16] = aK[cb][db][r];
-          pv[p * kD + 16 * db + c16] = aV[cb][db][r];
+          pq_[p * kD + 16 * db + c16] = sk[db];
+          pv_[p * kD + 16 * db + c16] = sv[db];
         }
       } else if (p >= MP && p < MP + k) {
-        const int64_t t = clamp64(ex[p - MP], N);
+        const int64_t row = (bh * m + ti.e) * k + (p - MP);  // expert e's j-th key
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          unsafeAtomicAdd(dK + (bh * N + t) * kD + 16 * db + c16, aK[cb][db][r]);
-          unsafeAtomicAdd(dV + (bh * N + t) * kD + 16 * db + c16, aV[cb][db][r]);
+          unsafeAtomicAdd(dke + row * kD + 16 * db + c16, sk[db]);
+          unsafeAtomicAdd(dve + row * kD + 16 * db + c16, sv[db]);
         }
       }
     }
@@ -561,10 +663,10 @@ __global__ __launch_bounds__(256) void k_bw_reduce1(const float* __restrict__ pa
 //   S^T = K_g Ql^T, dP^T = V_g dVl^T,  A = 2^(c2 S - lse2),  h = s A (dP - D)
 //   dQl += h K_g            (A operand = h straight from the accumulators)
 //   dK_g += h^T Ql, dV_g += A^T dVl   (h, A through the wave's LDS)
-// dK, dV rows of the group are read, added to and written back (each key
-// belongs to one group).  The wave's dQl sums go to partial 4 chunk + w.
+// The group's dK, dV rows are stored (each key belongs to one group); the
+// wave's dQl sums go to partial 4 chunk + w.
 template <class T, int MB>
-__global__ __launch_bounds__(256) void k_bw_cross(const typename T::elem* __restrict__ K,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_bw_cross(const typename T::elem* __restrict__ K,
                                                   const typename T::elem* __restrict__ V,
                                                   const typename T::elem* __restrict__ ql,
                                                   const float* __restrict__ dvl,
@@ -610,22 +712,30 @@ __global__ __launch_bounds__(256) void k_bw_cross(const typename T::elem* __rest
     for (int db = 0; db < 4; ++db) aQ[lb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   float* sK = sKV[w][0];  // K rows; then A^T
   float* sV = sKV[w][1];  // V rows; then h^T
+  Raw8<T> rk[2], rv[2];   // the next group's rows (as in k_bw_lmfwd)
+  auto fetch = [&](int64_t t0) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int u = l + 64 * h;
+      const int64_t t = t0 + (u >> 3);
+      if (t < k1) {
+        rk[h].load(K + (bh * N + t) * kD + 8 * (u & 7));
+        rv[h].load(V + (bh * N + t) * kD + 8 * (u & 7));
+      } else {
+        rk[h].zero();
+        rv[h].zero();
+      }
+    }
+  };
+  fetch(k0 + 16 * w);
   for (int64_t t0 = k0 + 16 * w; t0 < k1; t0 += 64) {
 #pragma unroll
-    for (int u = l; u < 128; u += 64) {
-      const int row = u >> 3, j = u & 7;
-      const int64_t t = t0 + row;
-      float kv[8], vv[8];
-      if (t < k1) {
-        load8(K + (bh * N + t) * kD + 8 * j, kv);
-        load8(V + (bh * N + t) * kD + 8 * j, vv);
-      } else {
-        zero8(kv);
-        zero8(vv);
-      }
-      store8(sK + row * kBwSt + 8 * j, kv);
-      store8(sV + row * kBwSt + 8 * j, vv);
+    for (int h = 0; h < 2; ++h) {
+      const int u = l + 64 * h;
+      rk[h].store(sK + (u >> 3) * kBwSt + 8 * (u & 7));
+      rv[h].store(sV + (u >> 3) * kBwSt + 8 * (u & 7));
     }
+    fetch(t0 + 64);
     float ak[16], av[16];
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
@@ -677,11 +787,9 @@ __global__ __launch_bounds__(256) void k_bw_cross(const typename T::elem* __rest
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t t = t0 + 4 * g + r;
-        if (t < k1) {
-          float* pk = dK + (bh * N + t) * kD + 16 * db + c16;
-          float* pvv = dV + (bh * N + t) * kD + 16 * db + c16;
-          *pk += dk[r];
-          *pvv += dv[r];
+        if (t < k1) {  // the expert step's sums are added afterwards (k_bw_keyadd)
+          dK[(bh * N + t) * kD + 16 * db + c16] = dk[r];
+          dV[(bh * N + t) * kD + 16 * db + c16] = dv[r];
         }
       }
     }
@@ -697,6 +805,25 @@ __global__ __launch_bounds__(256) void k_bw_cross(const typename T::elem* __rest
         for (int db = 0; db < 4; ++db) part2[(pbase + i) * kD + 16 * db + c16] = aQ[lb][db][r];
       }
     }
+}
+
+// Block (expert, head), wave w taking the expert's keys j = w, w + 4, ...,
+// lane = dim: the expert step's sums of each (expert, key) added into dK, dV
+// at the key (atomically: a key may belong to several experts).
+__global__ __launch_bounds__(256) void k_bw_keyadd(const float* __restrict__ dke,
+                                                   const float* __restrict__ dve,
+                                                   const int32_t* __restrict__ idx, int64_t N,
+                                                   int m, int k, float* __restrict__ dK,
+                                                   float* __restrict__ dV) {
+  const int64_t bh = blockIdx.y;
+  const int e = blockIdx.x;
+  const int c = threadIdx.x & 63;
+  for (int j = threadIdx.x >> 6; j < k; j += 4) {
+    const int64_t row = (bh * m + e) * k + j;
+    const int64_t t = clamp64(idx[row], N);
+    unsafeAtomicAdd(dK + (bh * N + t) * kD + c, dke[row * kD + c]);
+    unsafeAtomicAdd(dV + (bh * N + t) * kD + c, dve[row * kD + c]);
+  }
 }
 
 // Block (landmark, head): dQl = the expert step's part + the cross partials,
@@ -765,11 +892,11 @@ hipError_t launch_backward_t(const Shape& s, const BwPlan& bp, const BwWorkspace
   hipError_t e = hipSuccess;
   auto step = [&](int i) { return e == hipSuccess && i >= first && i <= last; };
   if (step(kBwZero)) {
-    const int64_t n4 = s.BH * s.N * kD / 4;
+    const int64_t n4 = s.BH * s.m * s.k * kD / 4;
     int64_t blocks = (n4 + 255) / 256;
     if (blocks > 8192) blocks = 8192;
     hipLaunchKernelGGL(k_bw_zero, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
-                       reinterpret_cast<f32x4*>(dK), reinterpret_cast<f32x4*>(dV), n4);
+                       reinterpret_cast<f32x4*>(ws.dke), reinterpret_cast<f32x4*>(ws.dve), n4);
     e = hipGetLastError();
   }
   if (step(kBwPool)) e = launch_pool(s, Qv, ws.fw, nullptr, 0, s.BH, st);
@@ -805,9 +932,9 @@ hipError_t launch_backward_t(const Shape& s, const BwPlan& bp, const BwWorkspace
     }
   }
   if (step(kBwAttend)) {
-    hipLaunchKernelGGL(k_bw_attend<T>, dim3(bp.items, BH), dim3(256), 0, st, Q, K, V, ql, ws.vl,
+    hipLaunchKernelGGL(k_bw_attend<T>, dim3(bp.items, BH), dim3(512), 0, st, Q, K, V, ql, ws.vl,
                        idx, ws.perm, ws.offsets, ws.item_start, bp.tpb, s.N, s.m, s.k, s.scale,
-                       dout, dQ, dK, dV, ws.part1, bp.items);
+                       dout, dQ, ws.dke, ws.dve, ws.part1, bp.items);
     e = hipGetLastError();
     if (e == hipSuccess) {
       hipLaunchKernelGGL(k_bw_reduce1, dim3(s.m, BH), dim3(256), 0, st, ws.part1, ws.item_start,
@@ -824,6 +951,11 @@ hipError_t launch_backward_t(const Shape& s, const BwPlan& bp, const BwWorkspace
       default: hipLaunchKernelGGL((k_bw_cross<T, 4>), grid, dim3(256), 0, st, K, V, ql, ws.dvl, ws.lse2, ws.dd, s.N, s.m, bp.cross_chunk, s.scale, dK, dV, ws.part2); break;
     }
     e = hipGetLastError();
+    if (e == hipSuccess) {
+      hipLaunchKernelGGL(k_bw_keyadd, dim3(s.m, BH), dim3(256), 0, st, ws.dke, ws.dve, idx, s.N,
+                         s.m, s.k, dK, dV);
+      e = hipGetLastError();
+    }
   }
   if (step(kBwPoolBw)) {
     hipLaunchKernelGGL(k_bw_reduce2, dim3(s.m, BH), dim3(256), 0, st, ws.part2,
@@ -896,6 +1028,8 @@ size_t plan_bw_workspace(const Shape& s, const BwPlan& bp, BwWorkspace* ws, char
   ws->dd = reinterpret_cast<float*>(take(BH * m * sizeof(float)));
   ws->part2 = reinterpret_cast<float*>(take(BH * 4 * bp.cross_chunks * kMaxM * kD * sizeof(float)));
   ws->dqlw = reinterpret_cast<float*>(take(BH * m * kD * sizeof(float)));
+  ws->dke = reinterpret_cast<float*>(take(BH * m * s.k * kD * sizeof(float)));
+  ws->dve = reinterpret_cast<float*>(take(BH * m * s.k * kD * sizeof(float)));
   return off;
 }
 

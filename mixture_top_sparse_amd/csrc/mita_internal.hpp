@@ -125,12 +125,13 @@ hipError_t launch_dense(int dtype, const void* Q, const void* K, const void* V, 
 
 // its steps, in launch order (launch_backward runs steps first..last)
 enum BwStep {
-  kBwZero = 0,     // dK = dV = 0
+  kBwZero = 0,     // the expert step's per-(expert, key) sums = 0
   kBwPool,         // Ql, as the forward computes it
   kBwLandmarkFwd,  // Vl and the landmarks' log-sum-exp (partials, merge)
   kBwBucket,       // queries grouped by the given routes
   kBwAttend,       // the output softmax per expert item, then dVl, dQl part, D
-  kBwCross,        // the landmark cross-attention's backward
+  kBwCross,        // the landmark cross-attention's backward (stores dK, dV), then
+                   // the expert step's key sums added in
   kBwPoolBw,       // dQl in full, spread back over the windows into dQ
   kBwStepCount
 };
@@ -161,6 +162,8 @@ struct BwWorkspace {
   float* dd = nullptr;          // [BH][m] dVl . Vl
   float* part2 = nullptr;       // [BH][4 cross_chunks][64][64] the cross step's dQl
   float* dqlw = nullptr;        // [BH][m][64] dQl / |window|
+  float* dke = nullptr;         // [BH][m][k][64] the expert step's dK sums per (expert, key)
+  float* dve = nullptr;         // [BH][m][k][64] the same for dV
 };
 
 BwPlan plan_backward(const Shape& s, int cus);

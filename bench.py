@@ -1,5 +1,6 @@
 #!/usr/bin/env python3
-"""Throughput of the MiTA forward pass on one MI355X.
+"""Throughput of the MiTA forward pass on one MI355X (and, beside it, of the
+backward pass used in training).
 
 One step = one complete forward (all five stages: pool, landmark scan +
 merge, route, bucket, expert attention) over one batch of synthetic inputs
@@ -282,6 +283,73 @@ def dense_baseline(w, Qt, Kt, Vt) -> dict:
             "frac": round(tflops / 2500.0, 4)}
 
 
+FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix rate, published
+
+
+def backward_flops(w) -> dict[str, float]:
+    """Algorithmic fp32 MFMA flops per launch of the backward's contraction
+    kernels: the expert step does five (m + k) x d products per query (logits,
+    dout . values, dQ, and the pair-side sums for keys and values), the
+    cross-attention step five m x d products per key, the recomputed
+    landmark forward two per key."""
+    BH, N, d, m, k = w.B * w.H, w.N, w.d, w.m, w.k
+    return {"bw_attend": BH * N * 10.0 * (m + k) * d,
+            "bw_cross": BH * N * 10.0 * m * d,
+            "bw_landmark_fwd": BH * N * 4.0 * m * d}
+
+
+def backward_bench(w, Qt, Kt, Vt, idx, route) -> dict:
+    """The backward pass (mita_backward, experts and routes from the forward
+    just timed) on the same inputs: time per call, per-step times from the
+    stage profiler, and its dominant kernel against the fp32 MFMA peak."""
+    import torch
+
+    import mixture_top_sparse_amd as mts
+    from mixture_top_sparse_amd.inputs import generate_dout
+
+    dout = torch.from_numpy(generate_dout(w)).cuda()
+    call = lambda: mts.mita_backward(Qt, Kt, Vt, idx, route, dout, m=w.m, k=w.k, grid=w.grid,
+                                     scale=w.scale)
+    call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    call()
+    torch.cuda.synchronize()
+    once = time.perf_counter() - t0
+    reps = max(3, min(20, int(1.0 / max(once, 1e-4))))
+    for _ in range(2):
+        call()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    mts.mita_profile_enable(True)
+    for _ in range(reps):
+        call()
+    torch.cuda.synchronize()
+    mts.mita_profile_enable(False)
+    stage_ms, calls = mts.mita_profile_read()
+    st = {k_: v / max(calls, 1) for k_, v in stage_ms.items() if k_.startswith("bw_")}
+    fl = backward_flops(w)
+    tf = {k_: fl[k_] / (st[k_] * 1e-3) / 1e12 for k_ in fl if st.get(k_, 0) > 0}
+    dom = max(fl, key=lambda k_: st.get(k_, 0.0))
+    value = w.B * w.H * w.N / (ms * 1e-3) / 1e6
+    log(f"backward: {ms:.3f} ms/call ({reps} timed), {value:.1f} Mtokens.heads/s; "
+        f"{dom} {st[dom]:.3f} ms at {tf[dom]:.1f} TFLOP/s fp32")
+    return {"ms_per_call": round(ms, 4), "calls": reps, "value": round(value, 2),
+            "unit": "Mtokens·heads/s", "stages_ms": {k_: round(v, 4) for k_, v in st.items()},
+            "stages_TFLOPs": {k_: round(v, 1) for k_, v in tf.items()},
+            "roofline": {"scope": "dominant backward kernel", "bound": "mfma", "kernel": dom,
+                         "flops": fl[dom], "launch_ms": round(st[dom], 4),
+                         "achieved": round(tf[dom], 1), "peak": FP32_MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf[dom] / FP32_MFMA_PEAK_TFLOPS, 4),
+                         "traffic": None}}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -300,6 +368,9 @@ def main() -> int:
                          "for this long: HBM and fabric clocks ramp over the first 10-15 ms of "
                          "memory-bound work after idling, which a few warm-up steps do not "
                          "cover (0 disables)")
+    ap.add_argument("--backward", choices=["on", "off"], default="on",
+                    help="after the forward, time mita_backward (the training pass, with the "
+                         "forward's experts and routes) and report it beside the metric")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also time a plain 1 GiB device copy kernel (bandwidth context and the "
                          "calibration kernel for HBM byte counters)")
@@ -445,6 +516,10 @@ def main() -> int:
         dense["speedup"] = round(dense["ms_per_step"] / ms_per_step, 2)
         log(f"MiTA speedup over dense attention: {dense['speedup']:.1f}x")
         line["dense_baseline"] = dense
+    if args.backward == "on" and S == 1:
+        bw = backward_bench(w, Qt, Kt, Vt, idx, route)
+        bw["vs_forward"] = round(bw["ms_per_call"] / ms_per_step, 2)
+        line["backward"] = bw
     if args.copy_probe:
         line["copy_probe"] = copy_probe()
     if not args.no_cpu_baseline and S == 1:

@@ -160,8 +160,9 @@ __global__ __launch_bounds__(256) void k_bw_zero(f32x4* __restrict__ a, f32x4* _
 // taking groups w, w + 4, ...  Per group: S^T = K_g Ql^T (keys on rows,
 // landmarks on columns), the running column maximum and sum, and
 // acc^T (dims x landmarks) += V_g^T P^T — the landmark on the output column
-// keeps each landmark's rescale inside its own lanes.  Partial p = 4 chunk +
-// w: stats [BH][P][64][2] (max in log2 units, sum), acc [BH][P][64][64].
+// keeps each landmark's rescale inside its own lanes.  The four waves'
+// states are combined into the block's partial: stats [BH][P][64][2] (max
+// in log2 units, sum), acc [BH][P][64][64], P = chunks.
 template <class T, int MB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_bw_lmfwd(const typename T::elem* __restrict__ K,
                                                   const typename T::elem* __restrict__ V,
@@ -170,11 +171,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                                                   float* __restrict__ part_stats,
                                                   float* __restrict__ part_acc) {
   constexpr int MP = 16 * MB;
-  __shared__ __attribute__((aligned(16))) float sQl[MP * kBwSt];
-  __shared__ __attribute__((aligned(16))) float sKV[4][2][16 * kBwSt];
+  // Ql, then each wave's 16 staged K and V rows; at the end the area holds
+  // waves 1..3's states for wave 0 to combine
+  constexpr int kWords = MP * kBwSt + 8 * 16 * kBwSt;
+  static_assert(3 * MP * (kD + 2) <= kWords, "combine area");
+  __shared__ __attribute__((aligned(16))) float smem[kWords];
+  float* const sQl = smem;
   const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
   const int64_t bh = blockIdx.y;
-  const int P = static_cast<int>(gridDim.x) * 4;
+  const int P = static_cast<int>(gridDim.x);
   for (int u = threadIdx.x; u < MP * 8; u += 256) {
     const int row = u >> 3, j = u & 7;
     float v[8];
@@ -196,8 +201,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
     for (int db = 0; db < 4; ++db) acc[lb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  float* sK = sKV[w][0];
-  float* sV = sKV[w][1];
+  float* sK = smem + MP * kBwSt + (2 * w) * 16 * kBwSt;
+  float* sV = sK + 16 * kBwSt;
   // this wave's 16 keys, one group ahead: lane l holds chunks l and l + 64
   // (row u / 8, elements 8 (u % 8) ..) of K and V
   Raw8<T> rk[2], rv[2];
@@ -264,36 +269,74 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       }
     }
   }
-  const int64_t pbase = (bh * P + static_cast<int64_t>(blockIdx.x) * 4 + w) * kMaxM;
+  // the four waves' states combined by wave 0 (acc[lb][db][r]: dim
+  // 16 db + 4 g + r of landmark 16 lb + c16)
+  float* const xacc = smem;                // [3][MP][64]
+  float* const xst = smem + 3 * MP * kD;   // [3][MP][2]
+  __syncthreads();  // every wave done with its staging rows
+  if (w > 0) {
+#pragma unroll
+    for (int lb = 0; lb < MB; ++lb) {
+      const int row = (w - 1) * MP + 16 * lb + c16;
+      if (g == 0) {
+        xst[row * 2] = M[lb];
+        xst[row * 2 + 1] = L[lb];
+      }
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        *reinterpret_cast<f32x4*>(xacc + row * kD + 16 * db + 4 * g) = acc[lb][db];
+    }
+  }
+  __syncthreads();
+  if (w > 0) return;
+  const int64_t pbase = (bh * P + blockIdx.x) * kMaxM;
 #pragma unroll
   for (int lb = 0; lb < MB; ++lb) {
-    const int64_t row = pbase + 16 * lb + c16;
-    if (g == 0) {
-      part_stats[row * 2] = M[lb];
-      part_stats[row * 2 + 1] = L[lb];
+    const int i = 16 * lb + c16;
+    // wave 0 had keys (the chunk's first group), so Mt is finite
+    float Mt = M[lb];
+#pragma unroll
+    for (int v = 0; v < 3; ++v) Mt = fmaxf(Mt, xst[(v * MP + i) * 2]);
+    const float f0 = fast_exp2(M[lb] - Mt);
+    float Lt = L[lb] * f0;
+    f32x4 at[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) at[db] = acc[lb][db] * f0;
+#pragma unroll
+    for (int v = 0; v < 3; ++v) {
+      const float fv = fast_exp2(xst[(v * MP + i) * 2] - Mt);  // 0 for a wave without keys
+      Lt += xst[(v * MP + i) * 2 + 1] * fv;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        at[db] += *reinterpret_cast<const f32x4*>(xacc + (v * MP + i) * kD + 16 * db + 4 * g) * fv;
     }
-    // acc[lb][db][r]: dim 16 db + 4 g + r of landmark 16 lb + c16
+    const int64_t row = pbase + i;
+    if (g == 0) {
+      part_stats[row * 2] = Mt;
+      part_stats[row * 2 + 1] = Lt;
+    }
 #pragma unroll
     for (int db = 0; db < 4; ++db)
-      *reinterpret_cast<f32x4*>(part_acc + row * kD + 16 * db + 4 * g) = acc[lb][db];
+      *reinterpret_cast<f32x4*>(part_acc + row * kD + 16 * db + 4 * g) = at[db];
   }
 }
 
-// One wave per landmark (four per block): Vl = acc / sum over the partials,
-// lse2 = max + log2(sum) (log2 units of the scaled logits).
+// Block (landmark, head), lane = dim: wave w merges partials w, w + 4, ...
+// (online), then wave 0 the four results: Vl = acc / sum, lse2 = max +
+// log2(sum) (log2 units of the scaled logits).  Every partial has keys.
 __global__ __launch_bounds__(256) void k_bw_lmmerge(const float* __restrict__ part_stats,
                                                     const float* __restrict__ part_acc, int m,
                                                     int P, float* __restrict__ vl,
                                                     float* __restrict__ lse2) {
+  __shared__ float sM[4], sL[4], sA[4][64];
   const int l = lane_id(), w = wave_id();
   const int64_t bh = blockIdx.y;
-  const int i = static_cast<int>(blockIdx.x) * 4 + w;
-  if (i >= m) return;
+  const int i = blockIdx.x;
   float M = -INFINITY, L = 0.f, a = 0.f;
-  for (int p = 0; p < P; ++p) {
+#pragma unroll 4
+  for (int p = w; p < P; p += 4) {
     const int64_t row = (bh * P + p) * kMaxM + i;
     const float Mp = part_stats[row * 2];
-    if (Mp == -INFINITY) continue;  // a wave that had no keys
     const float Lp = part_stats[row * 2 + 1];
     const float ap = part_acc[row * kD + l];
     const float Mn = fmaxf(M, Mp);
@@ -302,8 +345,23 @@ __global__ __launch_bounds__(256) void k_bw_lmmerge(const float* __restrict__ pa
     a = a * f0 + ap * f1;
     M = Mn;
   }
-  vl[(bh * m + i) * kD + l] = a / L;
-  if (l == 0) lse2[bh * m + i] = M + __log2f(L);
+  if (l == 0) {
+    sM[w] = M;
+    sL[w] = L;
+  }
+  sA[w][l] = a;
+  __syncthreads();
+  if (w != 0) return;
+  const float Mt = fmaxf(fmaxf(sM[0], sM[1]), fmaxf(sM[2], sM[3]));  // wave 0 had a partial
+  float Lt = 0.f, at = 0.f;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const float f = fast_exp2(sM[v] - Mt);  // 0 for a wave without partials
+    Lt += sL[v] * f;
+    at += sA[v][l] * f;
+  }
+  vl[(bh * m + i) * kD + l] = at / Lt;
+  if (l == 0) lse2[bh * m + i] = Mt + __log2f(Lt);
 }
 
 // ---------------------------------------------------------------------------
@@ -910,8 +968,8 @@ hipError_t launch_backward_t(const Shape& s, const BwPlan& bp, const BwWorkspace
     }
     e = hipGetLastError();
     if (e == hipSuccess) {
-      hipLaunchKernelGGL(k_bw_lmmerge, dim3((s.m + 3) / 4, BH), dim3(256), 0, st, ws.lm_stats,
-                         ws.lm_acc, s.m, 4 * bp.lm_chunks, ws.vl, ws.lse2);
+      hipLaunchKernelGGL(k_bw_lmmerge, dim3(s.m, BH), dim3(256), 0, st, ws.lm_stats,
+                         ws.lm_acc, s.m, bp.lm_chunks, ws.vl, ws.lse2);
       e = hipGetLastError();
     }
   }
@@ -1011,7 +1069,7 @@ size_t plan_bw_workspace(const Shape& s, const BwPlan& bp, BwWorkspace* ws, char
   *ws = BwWorkspace{};
   ws->fw.pool_part = reinterpret_cast<double*>(take(BH * m * s.pool_splits * kD * sizeof(double)));
   ws->fw.ql = take(BH * m * kD * es);
-  const size_t p1 = BH * 4 * bp.lm_chunks * kMaxM;
+  const size_t p1 = BH * bp.lm_chunks * kMaxM;
   ws->lm_stats = reinterpret_cast<float*>(take(p1 * 2 * sizeof(float)));
   ws->lm_acc = reinterpret_cast<float*>(take(p1 * kD * sizeof(float)));
   ws->vl = reinterpret_cast<float*>(take(BH * m * kD * sizeof(float)));

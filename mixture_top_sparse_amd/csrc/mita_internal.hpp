@@ -146,8 +146,8 @@ struct BwPlan {
 
 struct BwWorkspace {
   Workspace fw;                 // pool_part and ql only
-  float* lm_stats = nullptr;    // [BH][4 lm_chunks][64][2] (max in log2 units, sum)
-  float* lm_acc = nullptr;      // [BH][4 lm_chunks][64][64] unnormalised A.V
+  float* lm_stats = nullptr;    // [BH][lm_chunks][64][2] (max in log2 units, sum)
+  float* lm_acc = nullptr;      // [BH][lm_chunks][64][64] unnormalised A.V
   float* vl = nullptr;          // [BH][m][64]
   float* lse2 = nullptr;        // [BH][m] log2-sum-exp2 of the scaled logits (log2 units)
   int32_t* counts = nullptr;    // [BH][m][nseg]

@@ -39,6 +39,8 @@
 // read-modify-write in poolbw (8d): about 5de + 24d bytes.  The contractions cost about 2 d (5 (m + k) + 7 m)
 // flops per (token, head) at fp32 MFMA rate, which exceeds the bytes' time
 // at 157 TFLOP/s for m = k = 64: the pass is MFMA-bound (fp32).
+#include <type_traits>
+
 #include "mita.h"
 #include "mita_bucket.hpp"
 #include "mita_device.hpp"
@@ -50,6 +52,7 @@ namespace {
 constexpr int kBwSt = 68;         // fp32 LDS row stride (64 + 4)
 constexpr int kBwPairs = 128;     // m + k rounded up to 16 each, at most
 constexpr int kBwGsSt = kBwPairs + 4;
+constexpr int kBf16St = 72;       // bf16 LDS row stride (64 + 8: 144 B, 16-byte aligned)
 
 // eight consecutive elements of a row, as fp32
 __device__ __forceinline__ void load8(const uint16_t* __restrict__ p, float (&v)[8]) {
@@ -78,6 +81,8 @@ struct Raw8<BF16> {
   u32x4 w;
   __device__ void load(const uint16_t* __restrict__ p) { w = *reinterpret_cast<const u32x4*>(p); }
   __device__ void zero() { w = u32x4{0u, 0u, 0u, 0u}; }
+  // the 8 bf16 values as they are (a bf16 LDS row)
+  __device__ void store_raw(uint16_t* dst) const { *reinterpret_cast<u32x4*>(dst) = w; }
   __device__ void store(float* dst) const {
     *reinterpret_cast<f32x4*>(dst) = f32x4{__uint_as_float(w[0] << 16),
                                            __uint_as_float(w[0] & 0xFFFF0000u),
@@ -91,6 +96,7 @@ struct Raw8<BF16> {
 };
 template <>
 struct Raw8<F32> {
+  __device__ void store_raw(float* dst) const { store(dst); }
   f32x4 a, b;
   __device__ void load(const float* __restrict__ p) {
     a = *reinterpret_cast<const f32x4*>(p);
@@ -100,6 +106,44 @@ struct Raw8<F32> {
   __device__ void store(float* dst) const {
     *reinterpret_cast<f32x4*>(dst) = a;
     *reinterpret_cast<f32x4*>(dst + 4) = b;
+  }
+};
+
+// One 16 x 16 block of scores X Y^T over the 64 dims, X's row c16 held by
+// the lane as the MFMA A operand (loaded once, used against several Y
+// blocks), Y's rows from LDS.  bf16 inputs: two v_mfma_f32_16x16x32_bf16
+// from bf16 rows (stride kBf16St elements), exact products; fp32 inputs:
+// sixteen v_mfma_f32_16x16x4f32 from fp32 rows (stride kBwSt).  Output
+// D[4g + r][c16], as every MFMA here.
+template <class T>
+struct ScoreA;
+template <>
+struct ScoreA<BF16> {
+  bf16x8 a0, a1;
+  __device__ void load(const float* base, int row, int g) {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(base) + row * kBf16St + 8 * g;
+    a0 = as_bf16x8(*reinterpret_cast<const u32x4*>(p));
+    a1 = as_bf16x8(*reinterpret_cast<const u32x4*>(p + 32));
+  }
+  __device__ f32x4 score(const float* ybase, int yrow, int g) const {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(ybase) + yrow * kBf16St + 8 * g;
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+    c = mfma_bf16(a0, as_bf16x8(*reinterpret_cast<const u32x4*>(p)), c);
+    return mfma_bf16(a1, as_bf16x8(*reinterpret_cast<const u32x4*>(p + 32)), c);
+  }
+};
+template <>
+struct ScoreA<F32> {
+  float a[16];
+  __device__ void load(const float* base, int row, int g) {
+#pragma unroll
+    for (int s = 0; s < 16; ++s) a[s] = base[row * kBwSt + 4 * s + g];
+  }
+  __device__ f32x4 score(const float* ybase, int yrow, int g) const {
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 16; ++s) c = mfma_f32(a[s], ybase[yrow * kBwSt + 4 * s + g], c);
+    return c;
   }
 };
 
@@ -171,23 +215,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                                                   float* __restrict__ part_stats,
                                                   float* __restrict__ part_acc) {
   constexpr int MP = 16 * MB;
-  // Ql, then each wave's 16 staged K and V rows; at the end the area holds
-  // waves 1..3's states for wave 0 to combine
-  constexpr int kWords = MP * kBwSt + 8 * 16 * kBwSt;
-  static_assert(3 * MP * (kD + 2) <= kWords, "combine area");
+  constexpr bool kBf = std::is_same<T, BF16>::value;
+  // bf16: the scores run on bf16 MFMA from bf16 copies of Ql and K (exact);
+  // fp32: on fp32 MFMA from fp32 copies.  V is staged in fp32 for P.V.
+  constexpr int kQlWords = kBf ? MP * kBf16St / 2 : MP * kBwSt;
+  constexpr int kKWords = kBf ? 16 * kBf16St / 2 : 16 * kBwSt;
+  constexpr int kStage = kQlWords + 4 * (kKWords + 16 * kBwSt);
+  constexpr int kComb = 3 * MP * (kD + 2);  // waves 1..3's states at the end
+  constexpr int kWords = kStage > kComb ? kStage : kComb;
   __shared__ __attribute__((aligned(16))) float smem[kWords];
-  float* const sQl = smem;
   const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
   const int64_t bh = blockIdx.y;
   const int P = static_cast<int>(gridDim.x);
   for (int u = threadIdx.x; u < MP * 8; u += 256) {
     const int row = u >> 3, j = u & 7;
-    float v[8];
+    Raw8<T> v;
     if (row < m)
-      load8(ql + (bh * m + row) * kD + 8 * j, v);
+      v.load(ql + (bh * m + row) * kD + 8 * j);
     else
-      zero8(v);
-    store8(sQl + row * kBwSt + 8 * j, v);
+      v.zero();
+    if constexpr (kBf)
+      v.store_raw(reinterpret_cast<uint16_t*>(smem) + row * kBf16St + 8 * j);
+    else
+      v.store(smem + row * kBwSt + 8 * j);
   }
   __syncthreads();
   const int64_t k0 = static_cast<int64_t>(blockIdx.x) * csize;
@@ -201,8 +251,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
     for (int db = 0; db < 4; ++db) acc[lb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  float* sK = smem + MP * kBwSt + (2 * w) * 16 * kBwSt;
-  float* sV = sK + 16 * kBwSt;
+  float* const sKw = smem + kQlWords + w * (kKWords + 16 * kBwSt);  // this wave's K rows
+  float* const sV = sKw + kKWords;                                   // and V rows (fp32)
   // this wave's 16 keys, one group ahead: lane l holds chunks l and l + 64
   // (row u / 8, elements 8 (u % 8) ..) of K and V
   Raw8<T> rk[2], rv[2];
@@ -226,18 +276,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int u = l + 64 * h;
-      rk[h].store(sK + (u >> 3) * kBwSt + 8 * (u & 7));
+      if constexpr (kBf)
+        rk[h].store_raw(reinterpret_cast<uint16_t*>(sKw) + (u >> 3) * kBf16St + 8 * (u & 7));
+      else
+        rk[h].store(sKw + (u >> 3) * kBwSt + 8 * (u & 7));
       rv[h].store(sV + (u >> 3) * kBwSt + 8 * (u & 7));
     }
     fetch(t0 + 64);
-    float a[16];
-#pragma unroll
-    for (int s = 0; s < 16; ++s) a[s] = sK[c16 * kBwSt + 4 * s + g];
+    ScoreA<T> a;
+    a.load(sKw, c16, g);
 #pragma unroll
     for (int lb = 0; lb < MB; ++lb) {
-      f32x4 S = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 16; ++s) S = mfma_f32(a[s], sQl[(16 * lb + c16) * kBwSt + 4 * s + g], S);
+      const f32x4 S = a.score(smem, 16 * lb + c16, g);
       // S[r]: key t0 + 4g + r, landmark 16 lb + c16
       float x[4];
       float cm = -INFINITY;
@@ -447,6 +497,11 @@ __global__ __launch_bounds__(512) void k_bw_attend(
   __shared__ __attribute__((aligned(16))) float sGs[2][16 * kBwGsSt];
   __shared__ float sRed[2][3][4][16];
   __shared__ int sQid[2][16];
+  // bf16: the pair keys and the query rows also as bf16 rows (exact), for
+  // the logits on bf16 MFMA
+  constexpr bool kBf = std::is_same<T, BF16>::value;
+  __shared__ __attribute__((aligned(16))) float sPk16[kBf ? kBwPairs * kBf16St / 2 : 1];
+  __shared__ __attribute__((aligned(16))) float sQ16[2][kBf ? 16 * kBf16St / 2 : 1];
   const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
   const int hf = w >> 2, wl = w & 3;
   const int tid = threadIdx.x;
@@ -459,21 +514,24 @@ __global__ __launch_bounds__(512) void k_bw_attend(
   const int32_t* ex = idx + (bh * m + ti.e) * k;
   for (int u = tid; u < PP * 8; u += 512) {
     const int row = u >> 3, j = u & 7;
-    float kv[8], vv[8];
+    Raw8<T> kv;
+    float vv[8];
     if (row < m) {
-      load8(ql + (bh * m + row) * kD + 8 * j, kv);
+      kv.load(ql + (bh * m + row) * kD + 8 * j);
       load8(vl + (bh * m + row) * kD + 8 * j, vv);
     } else if (row >= MP && row < MP + k) {
       const int64_t t = clamp64(ex[row - MP], N);
-      load8(K + (bh * N + t) * kD + 8 * j, kv);
+      kv.load(K + (bh * N + t) * kD + 8 * j);
       load8(V + (bh * N + t) * kD + 8 * j, vv);
     } else {
-      zero8(kv);
+      kv.zero();
       zero8(vv);
     }
-    store8(sPk + row * kBwSt + 8 * j, kv);
+    kv.store(sPk + row * kBwSt + 8 * j);
+    if constexpr (kBf) kv.store_raw(reinterpret_cast<uint16_t*>(sPk16) + row * kBf16St + 8 * j);
     store8(sPv + row * kBwSt + 8 * j, vv);
   }
+  const float* const sPks = kBf ? sPk16 : sPk;  // the rows the logits read
   const float c2 = scale * kLog2e;
   f32x4 aK[2][4], aV[2][4];
 #pragma unroll
@@ -507,16 +565,19 @@ __global__ __launch_bounds__(512) void k_bw_attend(
     const int nv = ti.qe - q0 < 0 ? 0 : (ti.qe - q0 < 16 ? ti.qe - q0 : 16);
     __syncthreads();  // the expert staged; the previous groups' LDS reads done
     *reinterpret_cast<f32x4*>(hQ + srow * kBwSt + 4 * sc4) = f32x4{pq[0], pq[1], pq[2], pq[3]};
+    if constexpr (kBf)  // the bf16 values, back from their exact fp32 form
+      *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(sQ16[hf]) + srow * kBf16St + 4 * sc4) =
+          u32x2{(__float_as_uint(pq[0]) >> 16) | (__float_as_uint(pq[1]) & 0xFFFF0000u),
+                (__float_as_uint(pq[2]) >> 16) | (__float_as_uint(pq[3]) & 0xFFFF0000u)};
     *reinterpret_cast<f32x4*>(hG + srow * kBwSt + 4 * sc4) = f32x4{pg[0], pg[1], pg[2], pg[3]};
     if (sc4 == 0) sQid[hf][srow] = pid;
     fetch(q0 + 32);
     __syncthreads();
-    float aq[16], ag[16];
+    ScoreA<T> aq;
+    aq.load(kBf ? sQ16[hf] : hQ, c16, g);
+    float ag[16];
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      aq[s] = hQ[c16 * kBwSt + 4 * s + g];
-      ag[s] = hG[c16 * kBwSt + 4 * s + g];
-    }
+    for (int s = 0; s < 16; ++s) ag[s] = hG[c16 * kBwSt + 4 * s + g];
     f32x4 S[2], dW[2];
     float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
@@ -525,12 +586,10 @@ __global__ __launch_bounds__(512) void k_bw_attend(
       S[cb] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
       dW[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (pb < NB) {  // wave-uniform
-        f32x4 s4 = {0.f, 0.f, 0.f, 0.f}, d4 = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 s4 = aq.score(sPks, 16 * pb + c16, g);
+        f32x4 d4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 16; ++s) {
-          s4 = mfma_f32(aq[s], sPk[(16 * pb + c16) * kBwSt + 4 * s + g], s4);
-          d4 = mfma_f32(ag[s], sPv[(16 * pb + c16) * kBwSt + 4 * s + g], d4);
-        }
+        for (int s = 0; s < 16; ++s) d4 = mfma_f32(ag[s], sPv[(16 * pb + c16) * kBwSt + 4 * s + g], d4);
         const int p = 16 * pb + c16;
         const bool pv = p < m || (p >= MP && p < MP + k);
 #pragma unroll
@@ -678,31 +737,52 @@ __global__ __launch_bounds__(512) void k_bw_attend(
   }
 }
 
-// Block (landmark, head): dVl and the expert step's dQl summed over the
-// head's work items, and D = dVl . Vl.
-__global__ __launch_bounds__(256) void k_bw_reduce1(const float* __restrict__ part,
-                                                    const int32_t* __restrict__ item_start,
-                                                    const float* __restrict__ vl, int m, int items,
-                                                    float* __restrict__ dql, float* __restrict__ dvl,
-                                                    float* __restrict__ dd) {
-  __shared__ float red[2][4][64];
+// Block (landmark, head), 16 waves, lane = dim: dVl and the expert step's
+// dQl summed over the head's work items (wave w takes items w, w + 16, ...,
+// four at a time), and D = dVl . Vl.
+__global__ __launch_bounds__(1024) void k_bw_reduce1(const float* __restrict__ part,
+                                                     const int32_t* __restrict__ item_start,
+                                                     const float* __restrict__ vl, int m,
+                                                     int items, float* __restrict__ dql,
+                                                     float* __restrict__ dvl,
+                                                     float* __restrict__ dd) {
+  __shared__ float red[2][16][64];
   const int l = lane_id(), w = wave_id();
   const int64_t bh = blockIdx.y;
   const int i = blockIdx.x;
   const int n = item_start[bh * (m + 1) + m];
   const int64_t stride = static_cast<int64_t>(m) * kD;
+  const float* base = part + bh * items * 2 * stride + i * kD + l;
   float sq = 0.f, sv = 0.f;
-  for (int t = w; t < n; t += 4) {
-    const float* pq = part + (bh * items + t) * 2 * stride + i * kD;
-    sq += pq[l];
-    sv += pq[stride + l];
+  int t = w;
+  for (; t + 48 < n; t += 64) {
+    float a[4], b[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      a[u] = base[(t + 16 * u) * 2 * stride];
+      b[u] = base[(t + 16 * u) * 2 * stride + stride];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      sq += a[u];
+      sv += b[u];
+    }
+  }
+  for (; t < n; t += 16) {
+    sq += base[t * 2 * stride];
+    sv += base[t * 2 * stride + stride];
   }
   red[0][w][l] = sq;
   red[1][w][l] = sv;
   __syncthreads();
   if (w != 0) return;
-  sq = red[0][0][l] + red[0][1][l] + red[0][2][l] + red[0][3][l];
-  sv = red[1][0][l] + red[1][1][l] + red[1][2][l] + red[1][3][l];
+  sq = 0.f;
+  sv = 0.f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    sq += red[0][v][l];
+    sv += red[1][v][l];
+  }
   const int64_t o = (bh * m + i) * kD + l;
   dql[o] = sq;
   dvl[o] = sv;
@@ -734,24 +814,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                                                   float* __restrict__ dK, float* __restrict__ dV,
                                                   float* __restrict__ part2) {
   constexpr int MP = 16 * MB;
-  __shared__ __attribute__((aligned(16))) float sQl[MP * kBwSt];
+  constexpr bool kBf = std::is_same<T, BF16>::value;
+  // bf16: Ql and each wave's K rows as bf16 rows (exact; the scores on bf16
+  // MFMA, the fp32 operands read from them); fp32: fp32 rows
+  __shared__ __attribute__((aligned(16))) float sQl[kBf ? MP * kBf16St / 2 : MP * kBwSt];
   __shared__ __attribute__((aligned(16))) float sdVl[MP * kBwSt];
   __shared__ float sLse[MP], sD[MP];
   __shared__ __attribute__((aligned(16))) float sKV[4][2][16 * kBwSt];
+  __shared__ __attribute__((aligned(16))) float sK16[kBf ? 4 : 1][kBf ? 16 * kBf16St / 2 : 1];
   const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
   const int64_t bh = blockIdx.y;
   const int P = static_cast<int>(gridDim.x) * 4;
   for (int u = threadIdx.x; u < MP * 8; u += 256) {
     const int row = u >> 3, j = u & 7;
-    float a[8], b[8];
+    Raw8<T> a;
+    float b[8];
     if (row < m) {
-      load8(ql + (bh * m + row) * kD + 8 * j, a);
+      a.load(ql + (bh * m + row) * kD + 8 * j);
       load8(dvl + (bh * m + row) * kD + 8 * j, b);
     } else {
-      zero8(a);
+      a.zero();
       zero8(b);
     }
-    store8(sQl + row * kBwSt + 8 * j, a);
+    if constexpr (kBf)
+      a.store_raw(reinterpret_cast<uint16_t*>(sQl) + row * kBf16St + 8 * j);
+    else
+      a.store(sQl + row * kBwSt + 8 * j);
     store8(sdVl + row * kBwSt + 8 * j, b);
   }
   if (threadIdx.x < MP) {
@@ -768,8 +856,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   for (int lb = 0; lb < MB; ++lb)
 #pragma unroll
     for (int db = 0; db < 4; ++db) aQ[lb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float* sK = sKV[w][0];  // K rows; then A^T
+  float* sK = sKV[w][0];  // fp32: K rows; then A^T (bf16: A^T only)
   float* sV = sKV[w][1];  // V rows; then h^T
+  float* const sKs = kBf ? sK16[kBf ? w : 0] : sK;  // the rows the scores read
+  // element (row, col) of K_g and of Ql as fp32
+  auto kval = [&](int row, int col) -> float {
+    if constexpr (kBf)
+      return bf16_to_f32(reinterpret_cast<const uint16_t*>(sKs)[row * kBf16St + col]);
+    else
+      return sK[row * kBwSt + col];
+  };
+  auto qlval = [&](int row, int col) -> float {
+    if constexpr (kBf)
+      return bf16_to_f32(reinterpret_cast<const uint16_t*>(sQl)[row * kBf16St + col]);
+    else
+      return sQl[row * kBwSt + col];
+  };
   Raw8<T> rk[2], rv[2];   // the next group's rows (as in k_bw_lmfwd)
   auto fetch = [&](int64_t t0) {
 #pragma unroll
@@ -790,25 +892,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int u = l + 64 * h;
-      rk[h].store(sK + (u >> 3) * kBwSt + 8 * (u & 7));
+      if constexpr (kBf)
+        rk[h].store_raw(reinterpret_cast<uint16_t*>(sKs) + (u >> 3) * kBf16St + 8 * (u & 7));
+      else
+        rk[h].store(sK + (u >> 3) * kBwSt + 8 * (u & 7));
       rv[h].store(sV + (u >> 3) * kBwSt + 8 * (u & 7));
     }
     fetch(t0 + 64);
-    float ak[16], av[16];
+    ScoreA<T> ak;
+    ak.load(sKs, c16, g);
+    float av[16];
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      ak[s] = sK[c16 * kBwSt + 4 * s + g];
-      av[s] = sV[c16 * kBwSt + 4 * s + g];
-    }
+    for (int s = 0; s < 16; ++s) av[s] = sV[c16 * kBwSt + 4 * s + g];
     float A[MB][4], Hh[MB][4];
 #pragma unroll
     for (int lb = 0; lb < MB; ++lb) {
-      f32x4 S = {0.f, 0.f, 0.f, 0.f}, dP = {0.f, 0.f, 0.f, 0.f};
+      const f32x4 S = ak.score(sQl, 16 * lb + c16, g);
+      f32x4 dP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        S = mfma_f32(ak[s], sQl[(16 * lb + c16) * kBwSt + 4 * s + g], S);
+      for (int s = 0; s < 16; ++s)
         dP = mfma_f32(av[s], sdVl[(16 * lb + c16) * kBwSt + 4 * s + g], dP);
-      }
       const int i = 16 * lb + c16;
       const float ls = sLse[i], Di = sD[i];
 #pragma unroll
@@ -820,12 +923,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
     // dQl += h K_g: landmarks on the output rows
 #pragma unroll
-    for (int lb = 0; lb < MB; ++lb)
+    for (int db = 0; db < 4; ++db) {
+      float kb[4];
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int r = 0; r < 4; ++r) kb[r] = kval(4 * g + r, 16 * db + c16);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          aQ[lb][db] = mfma_f32(Hh[lb][r], sK[(4 * g + r) * kBwSt + 16 * db + c16], aQ[lb][db]);
+      for (int lb = 0; lb < MB; ++lb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) aQ[lb][db] = mfma_f32(Hh[lb][r], kb[r], aQ[lb][db]);
+    }
     // A and h transposed through the wave's LDS (after its reads of K and V)
 #pragma unroll
     for (int lb = 0; lb < MB; ++lb)
@@ -839,7 +945,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       f32x4 dk = {0.f, 0.f, 0.f, 0.f}, dv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4 * MB; ++s) {
-        dk = mfma_f32(sV[c16 * kBwSt + 4 * s + g], sQl[(4 * s + g) * kBwSt + 16 * db + c16], dk);
+        dk = mfma_f32(sV[c16 * kBwSt + 4 * s + g], qlval(4 * s + g, 16 * db + c16), dk);
         dv = mfma_f32(sK[c16 * kBwSt + 4 * s + g], sdVl[(4 * s + g) * kBwSt + 16 * db + c16], dv);
       }
 #pragma unroll
@@ -906,32 +1012,41 @@ __global__ __launch_bounds__(256) void k_bw_reduce2(const float* __restrict__ pa
   dqlw[(bh * m + i) * kD + l] = s / static_cast<float>((r1 - r0) * (c1 - c0));
 }
 
-// Block (16 tokens, head), sixteen threads per token with 4 dims each.  A
-// grid cell lies only in bins of floor(r mh / gh) and its two neighbours per
-// axis (mh <= gh).
+// Block (64 tokens, head), four threads per token with 16 dims each.  Grid
+// cell r lies in bin a of n bins over g cells iff a g < (r + 1) n and
+// r n < (a + 1) g (the bin rule [floor(a g / n), ceil((a + 1) g / n)) with
+// the divisions multiplied out); only bins within two of floor(r n / g)
+// qualify (n <= g), and that estimate comes from one fp64 division.
 __global__ __launch_bounds__(256) void k_bw_poolbw(const float* __restrict__ dqlw, int64_t N,
                                                    int m, int gh, int gw, int mh, int mw,
                                                    float* __restrict__ dQ) {
   const int64_t bh = blockIdx.y;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
-  const int dq4 = threadIdx.x & 15;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 64 + (threadIdx.x >> 2);
+  const int part = threadIdx.x & 3;
   if (t >= N) return;
-  const int64_t row = t / gw, col = t % gw;
-  const int64_t a0 = row * mh / gh, b0 = col * mw / gw;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int64_t a = a0 > 0 ? a0 - 1 : 0; a <= a0 + 1 && a < mh; ++a) {
-    int64_t r0, r1;
-    bin_range(a, gh, mh, r0, r1);
-    if (row < r0 || row >= r1) continue;
-    for (int64_t b = b0 > 0 ? b0 - 1 : 0; b <= b0 + 1 && b < mw; ++b) {
-      int64_t c0, c1;
-      bin_range(b, gw, mw, c0, c1);
-      if (col < c0 || col >= c1) continue;
-      acc += *reinterpret_cast<const f32x4*>(dqlw + (bh * m + a * mw + b) * kD + 4 * dq4);
+  float* p = dQ + (bh * N + t) * kD + 16 * part;
+  f32x4 cur[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) cur[j] = *reinterpret_cast<const f32x4*>(p + 4 * j);
+  const int row = static_cast<int>(t) / gw, col = static_cast<int>(t) - row * gw;
+  const int a0 = static_cast<int>(static_cast<double>(row) * mh / gh);
+  const int b0 = static_cast<int>(static_cast<double>(col) * mw / gw);
+  const int a_lo = a0 - 2 > 0 ? a0 - 2 : 0, a_hi = a0 + 2 < mh - 1 ? a0 + 2 : mh - 1;
+  const int b_lo = b0 - 2 > 0 ? b0 - 2 : 0, b_hi = b0 + 2 < mw - 1 ? b0 + 2 : mw - 1;
+  for (int a = a_lo; a <= a_hi; ++a) {
+    if (!(int64_t{a} * gh < (int64_t{row} + 1) * mh && int64_t{row} * mh < (int64_t{a} + 1) * gh))
+      continue;
+    for (int b = b_lo; b <= b_hi; ++b) {
+      if (!(int64_t{b} * gw < (int64_t{col} + 1) * mw && int64_t{col} * mw < (int64_t{b} + 1) * gw))
+        continue;
+      const float* src = dqlw + (bh * m + a * mw + b) * kD + 16 * part;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cur[j] += *reinterpret_cast<const f32x4*>(src + 4 * j);
     }
   }
-  f32x4* p = reinterpret_cast<f32x4*>(dQ + (bh * N + t) * kD + 4 * dq4);
-  *p += acc;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    __builtin_nontemporal_store(cur[j], reinterpret_cast<f32x4*>(p + 4 * j));
 }
 
 template <class T>
@@ -995,7 +1110,7 @@ hipError_t launch_backward_t(const Shape& s, const BwPlan& bp, const BwWorkspace
                        dout, dQ, ws.dke, ws.dve, ws.part1, bp.items);
     e = hipGetLastError();
     if (e == hipSuccess) {
-      hipLaunchKernelGGL(k_bw_reduce1, dim3(s.m, BH), dim3(256), 0, st, ws.part1, ws.item_start,
+      hipLaunchKernelGGL(k_bw_reduce1, dim3(s.m, BH), dim3(1024), 0, st, ws.part1, ws.item_start,
                          ws.vl, s.m, bp.items, ws.dql1, ws.dvl, ws.dd);
       e = hipGetLastError();
     }
@@ -1020,7 +1135,7 @@ hipError_t launch_backward_t(const Shape& s, const BwPlan& bp, const BwWorkspace
                        4 * bp.cross_chunks, ws.dql1, s.m, s.gh, s.gw, s.mh, s.mw, ws.dqlw);
     e = hipGetLastError();
     if (e == hipSuccess) {
-      hipLaunchKernelGGL(k_bw_poolbw, dim3(static_cast<unsigned>((s.N + 15) / 16), BH), dim3(256),
+      hipLaunchKernelGGL(k_bw_poolbw, dim3(static_cast<unsigned>((s.N + 63) / 64), BH), dim3(256),
                          0, st, ws.dqlw, s.N, s.m, s.gh, s.gw, s.mh, s.mw, dQ);
       e = hipGetLastError();
     }

@@ -600,32 +600,24 @@ __global__ __launch_bounds__(512) void k_bw_attend(
         dW[cb] = d4;
       }
     }
-    // row (query) statistics over all pairs: within 16 lanes, then across
-    // the half's four waves
+    // row (query) statistics over all pairs in one exchange: each wave's max
+    // and sums over its own columns (within 16 lanes), then rescaled to the
+    // half's maximum.  A wave without columns (NB <= 3) reports -inf and 0.
+    float E[2][4], z[4], y[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       mx[r] = xor_max(mx[r], 1);
       mx[r] = xor_max(mx[r], 2);
       mx[r] = xor_max(mx[r], 4);
       mx[r] = xor_max(mx[r], 8);
-      if (c16 == 0) sRed[hf][0][wl][4 * g + r] = mx[r];
-    }
-    __syncthreads();
-    float Mr[4], z[4], y[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 4 * g + r;
-      Mr[r] = fmaxf(fmaxf(sRed[hf][0][0][row], sRed[hf][0][1][row]),
-                    fmaxf(sRed[hf][0][2][row], sRed[hf][0][3][row]));
       z[r] = 0.f;
       y[r] = 0.f;
     }
-    float E[2][4];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        E[cb][r] = fast_exp2(S[cb][r] - Mr[r]);  // 0 for masked pairs
+        E[cb][r] = mx[r] == -INFINITY ? 0.f : fast_exp2(S[cb][r] - mx[r]);  // 0 when masked
         z[r] += E[cb][r];
         y[r] += E[cb][r] * dW[cb][r];
       }
@@ -637,6 +629,7 @@ __global__ __launch_bounds__(512) void k_bw_attend(
         y[r] = xor_sum(y[r], mk);
       }
       if (c16 == 0) {
+        sRed[hf][0][wl][4 * g + r] = mx[r];
         sRed[hf][1][wl][4 * g + r] = z[r];
         sRed[hf][2][wl][4 * g + r] = y[r];
       }
@@ -646,11 +639,21 @@ __global__ __launch_bounds__(512) void k_bw_attend(
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 4 * g + r;
-      const float Z = sRed[hf][1][0][row] + sRed[hf][1][1][row] + sRed[hf][1][2][row] +
-                      sRed[hf][1][3][row];
-      const float Y = sRed[hf][2][0][row] + sRed[hf][2][1][row] + sRed[hf][2][2][row] +
-                      sRed[hf][2][3][row];
-      const float inv = row < nv ? 1.f / Z : 0.f;  // padding rows contribute nothing
+      float mv[4], M = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        mv[v] = sRed[hf][0][v][row];
+        M = fmaxf(M, mv[v]);
+      }
+      float Z = 0.f, Y = 0.f;  // M is finite: some wave holds a valid pair
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float f = mv[v] == -INFINITY ? 0.f : fast_exp2(mv[v] - M);
+        Z += sRed[hf][1][v][row] * f;
+        Y += sRed[hf][2][v][row] * f;
+      }
+      const float own = mx[r] == -INFINITY ? 0.f : fast_exp2(mx[r] - M);
+      const float inv = row < nv ? own / Z : 0.f;  // padding rows contribute nothing
       const float c = Y / Z;                       // dout . out of this query
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {

@@ -216,9 +216,16 @@ __global__ __launch_bounds__(kSmallThreads) void k_small_bf16(
       for (int r = 0; r < 4; ++r)
         ob[kt][r] = (16 * kt + 4 * g + r < N) ? score_order_bits(sc[kt][r]) : 0u;
     // expert: T = the k-th largest order bits (the largest t with at least
-    // k keys >= t), found bit by bit; then ties at T by lower key
+    // k keys >= t), found bit by bit; then ties at T by lower key.  A
+    // landmark whose count reaches exactly k at some candidate stops there:
+    // the keys >= that candidate are then exactly its top k (the tie step
+    // below takes every key equal to it, if any), so the rest of the search
+    // would not change the set.  The wave stops once all 16 have (lanes of
+    // landmarks past m from the start).
     uint32_t T = 0;
+    bool done = i >= m;
     for (int bit = 31; bit >= 0; --bit) {
+      if (ballot(!done) == 0ull) break;  // wave-uniform
       const uint32_t cand = T | (1u << bit);
       int c = 0;
 #pragma unroll
@@ -227,7 +234,10 @@ __global__ __launch_bounds__(kSmallThreads) void k_small_bf16(
         for (int r = 0; r < 4; ++r) c += ob[kt][r] >= cand ? 1 : 0;
       c = xor_sum_i(c, 16);
       c = xor_sum_i(c, 32);
-      if (c >= k) T = cand;
+      if (!done && c >= k) {
+        T = cand;
+        done = c == k;
+      }
     }
     int gt = 0;
 #pragma unroll

@@ -147,6 +147,33 @@ struct ScoreA<F32> {
   }
 };
 
+// Max and sum over the 16 lanes of a row (lanes 16j .. 16j + 15), every
+// lane getting the result, on the VALU with DPP lane moves: two quad
+// swaps, then the half-row mirror (quads 0 <-> 1, 2 <-> 3 of each 8) and
+// the row mirror (the two halves), so that each step combines two partial
+// results that cover disjoint lanes.
+__device__ __forceinline__ float dpp_f(float v, int ctrl_sel) {
+  const int x = __float_as_int(v);
+  int y;
+  switch (ctrl_sel) {  // the control must be a constant
+    case 0: y = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false); break;   // quad_perm [1,0,3,2]
+    case 1: y = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false); break;   // quad_perm [2,3,0,1]
+    case 2: y = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false); break;  // row_half_mirror
+    default: y = __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, false); break; // row_mirror
+  }
+  return __int_as_float(y);
+}
+__device__ __forceinline__ float row16_max(float v) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) v = fmaxf(v, dpp_f(v, c));
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) v += dpp_f(v, c);
+  return v;
+}
+
 // four consecutive elements, as fp32
 __device__ __forceinline__ void load4(const uint16_t* __restrict__ p, float (&v)[4]) {
   const u32x2 w = *reinterpret_cast<const u32x2*>(p);
@@ -587,9 +614,13 @@ __global__ __launch_bounds__(512) void k_bw_attend(
       dW[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (pb < NB) {  // wave-uniform
         const f32x4 s4 = aq.score(sPks, 16 * pb + c16, g);
-        f32x4 d4 = {0.f, 0.f, 0.f, 0.f};
+        f32x4 d4 = {0.f, 0.f, 0.f, 0.f}, d4b = d4;  // two chains of 8
 #pragma unroll
-        for (int s = 0; s < 16; ++s) d4 = mfma_f32(ag[s], sPv[(16 * pb + c16) * kBwSt + 4 * s + g], d4);
+        for (int s = 0; s < 16; s += 2) {
+          d4 = mfma_f32(ag[s], sPv[(16 * pb + c16) * kBwSt + 4 * s + g], d4);
+          d4b = mfma_f32(ag[s + 1], sPv[(16 * pb + c16) * kBwSt + 4 * (s + 1) + g], d4b);
+        }
+        d4 += d4b;
         const int p = 16 * pb + c16;
         const bool pv = p < m || (p >= MP && p < MP + k);
 #pragma unroll
@@ -606,10 +637,7 @@ __global__ __launch_bounds__(512) void k_bw_attend(
     float E[2][4], z[4], y[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      mx[r] = xor_max(mx[r], 1);
-      mx[r] = xor_max(mx[r], 2);
-      mx[r] = xor_max(mx[r], 4);
-      mx[r] = xor_max(mx[r], 8);
+      mx[r] = row16_max(mx[r]);
       z[r] = 0.f;
       y[r] = 0.f;
     }
@@ -623,11 +651,8 @@ __global__ __launch_bounds__(512) void k_bw_attend(
       }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-#pragma unroll
-      for (int mk = 1; mk < 16; mk <<= 1) {
-        z[r] = xor_sum(z[r], mk);
-        y[r] = xor_sum(y[r], mk);
-      }
+      z[r] = row16_sum(z[r]);
+      y[r] = row16_sum(y[r]);
       if (c16 == 0) {
         sRed[hf][0][wl][4 * g + r] = mx[r];
         sRed[hf][1][wl][4 * g + r] = z[r];
@@ -678,13 +703,19 @@ __global__ __launch_bounds__(512) void k_bw_attend(
     }
     __syncthreads();
     // dQ (16 queries x dims 16 wl .. 16 wl + 15) = g [keys]
-    f32x4 dq = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < 4 * NB; ++s)
-      dq = mfma_f32(hGs[c16 * kBwGsSt + 4 * s + g], sPk[(4 * s + g) * kBwSt + 16 * wl + c16], dq);
+    f32x4 dq[4];  // four independent chains over the pair steps
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dq[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < 4 * NB; s += 4)  // 4 NB is a multiple of 4
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        dq[j] = mfma_f32(hGs[c16 * kBwGsSt + 4 * (s + j) + g],
+                         sPk[(4 * (s + j) + g) * kBwSt + 16 * wl + c16], dq[j]);
+    dq[0] += dq[1] + dq[2] + dq[3];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 4 * g + r;
-      if (row < nv) dQ[(bh * N + sQid[hf][row]) * kD + 16 * wl + c16] = dq[r];
+      if (row < nv) dQ[(bh * N + sQid[hf][row]) * kD + 16 * wl + c16] = dq[0][r];
     }
   }
   // the second half's sums into the first's (through the staged expert's LDS)

@@ -29,6 +29,7 @@
 // Roofline: per head, Q is read from global three times (pooling, routing,
 // the attention's gather; the second and third hit L2), K and V once, the
 // fp32 output and routes written once.  No work space.
+#include "mita_bucket.hpp"
 #include "mita_device.hpp"
 #include "mita_internal.hpp"
 
@@ -289,8 +290,9 @@ __global__ __launch_bounds__(kSmallThreads) void k_small_bf16(
       sel_before += st[kt];
     }
   }
-  if (LT == 4 || (w >= LT && w < 2 * LT)) {
-    const int lt = LT == 4 ? w : w - LT;
+  // LT == 1, 2: wave LT computes every tile's landmark values in turn while
+  // wave 3 routes and buckets; LT == 4: each wave its own tile
+  for (int lt = LT == 4 ? w : 0; (LT == 4 || w == LT) && lt < LT; lt += (LT == 4 ? LT : 1)) {
     const int i = 16 * lt + c16;
     float sc[NTMAX][4];
     tile_scores(lt, sc);
@@ -351,23 +353,12 @@ __global__ __launch_bounds__(kSmallThreads) void k_small_bf16(
     }
   }
 
-  // ---- 3. routing: one 16-query tile per wave and step -------------------
-  // (needs only Ql, which step 1 left in LDS before the barrier)
-  constexpr int RT = (NTMAX + 3) / 4;  // query tiles per wave, at most
-  bf16x8 rq[RT][2];                     // all of them requested up front
-#pragma unroll
-  for (int j = 0; j < RT; ++j) {
-    const int q = min(16 * (w + 4 * j) + c16, N - 1);
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-      rq[j][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(Qh + q * kD + 32 * s + 8 * g));
-  }
-#pragma unroll
-  for (int j = 0; j < RT; ++j) {
-    const int qt = w + 4 * j;
-    if (qt >= nt) continue;
+  // ---- 3. routing (and 4. bucketing) -------------------------------------
+  // (needs only Ql, which step 1 left in LDS before the barrier).  A query's
+  // route: the largest q . Ql[i] over the MFMA logits, ties to the lower
+  // landmark.
+  auto route_tile = [&](int qt, const bf16x8 (&qb)[2]) {
     const int q = min(16 * qt + c16, N - 1);
-    bf16x8(&qb)[2] = rq[j];
     float best = -INFINITY;
     int bi = 0;
 #pragma unroll
@@ -395,8 +386,77 @@ __global__ __launch_bounds__(kSmallThreads) void k_small_bf16(
       route_out[bh * N + q] = bi;
       atomicAdd(&S.cnt[bi], 1);
     }
-  }
-  __syncthreads();
+  };
+  auto load_tile = [&](int qt, bf16x8 (&qb)[2]) {
+    const int q = min(16 * qt + c16, N - 1);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      qb[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(Qh + q * kD + 32 * s + 8 * g));
+  };
+  if (LT < 4) {
+    // One wave routes every query tile (two tiles' rows in flight) and then
+    // sorts the queries by expert on its own, while waves 0 .. LT-1 select
+    // the experts and wave LT computes the landmark values: routing and
+    // bucketing leave the critical path.  A single wave's LDS accesses
+    // complete in program order, so it needs no barrier of its own.
+    if (w == 3) {
+      bf16x8 qa[2], qn[2];
+      load_tile(0, qa);
+      for (int qt = 0; qt < nt; ++qt) {
+        if (qt + 1 < nt) load_tile(qt + 1, qn);
+        route_tile(qt, qa);
+        qa[0] = qn[0];
+        qa[1] = qn[1];
+      }
+      // offsets and first sub-tile of each expert: lane e holds expert e
+      const int c = l < m ? S.cnt[l] : 0;
+      const int incl = wave_inclusive_sum(c);
+      const int u = (c + 15) / 16;
+      const int incl_u = wave_inclusive_sum(u);
+      if (l < m) {
+        S.off[l] = incl - c;
+        S.sub[l] = incl_u - u;
+      }
+      if (l == m - 1) {
+        S.off[m] = incl;
+        S.sub[m] = incl_u;
+      }
+      if (off_copy && l < m) off_copy[bh * (m + 1) + l] = incl - c;
+      if (off_copy && l == m - 1) off_copy[bh * (m + 1) + m] = incl;
+      // stable ranks: queries 64 G + l in groups; lane e carries how many
+      // queries of expert e the earlier groups placed
+      int placed = 0;
+      const int base = l < m ? incl - c : 0;
+      for (int G = 0; 64 * G < N; ++G) {
+        const int q = 64 * G + l;
+        const int r = q < N ? S.route[q] : -1;
+        int below = 0, mine = 0;
+        for (int e = 0; e < m; ++e) {
+          const uint64_t b = ballot(r == e);
+          if (r == e) below = static_cast<int>(count_below(b));
+          if (l == e) mine = static_cast<int>(__popcll(b));
+        }
+        const int start = static_cast<int>(lane_read(static_cast<uint32_t>(base + placed), r < 0 ? 0 : r));
+        if (q < N) {
+          const int pos = start + below;
+          S.perm[pos] = static_cast<int16_t>(q);
+          if (perm_copy) perm_copy[bh * N + pos] = q;
+        }
+        placed += mine;
+      }
+    }
+    __syncthreads();
+  } else {
+    // LT == 4: every wave routes its own query tiles (all requested up
+    // front), then the four sort together
+    constexpr int RT = (NTMAX + 3) / 4;  // query tiles per wave, at most
+    bf16x8 rq[RT][2];
+#pragma unroll
+    for (int j = 0; j < RT; ++j) load_tile(w + 4 * j, rq[j]);
+#pragma unroll
+    for (int j = 0; j < RT; ++j)
+      if (w + 4 * j < nt) route_tile(w + 4 * j, rq[j]);
+    __syncthreads();
 
   // ---- 4. bucketing: counting sort by expert, stable ---------------------
   if (tid == 0) {
@@ -433,6 +493,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_small_bf16(
   }
   if (off_copy && tid <= m) off_copy[bh * (m + 1) + tid] = S.off[tid];
   __syncthreads();
+  }
 
   // ---- 5. expert attention: one 16-query sub-tile of one expert per wave --
   const int nsub = S.sub[m];

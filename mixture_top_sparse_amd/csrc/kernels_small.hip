@@ -80,6 +80,18 @@ __device__ __forceinline__ void prefix_over_g(int v, int c16, int g, int& before
   total = v0 + v1 + v2 + v3;
 }
 
+typedef unsigned short us16x2 __attribute__((ext_vector_type(2)));
+
+// per 16-bit half: 1 where x < c, else 0 (saturating c - x, then min with
+// 1; written out so that the compiler keeps the two packed instructions
+// instead of turning them into compares through VCC)
+__device__ __forceinline__ uint32_t lt16x2(uint32_t c2x, uint32_t x) {
+  uint32_t d, r;
+  asm("v_pk_sub_u16 %0, %1, %2 clamp" : "=v"(d) : "v"(c2x), "v"(x));
+  asm("v_pk_min_u16 %0, %1, %2" : "=v"(r) : "v"(d), "v"(0x00010001u));
+  return r;
+}
+
 // 8 bf16 values (K-positions of a 16x16x32 MFMA operand) from lane-chosen
 // rows of a row-major bf16 matrix: element j is row rows[j], column col
 __device__ __forceinline__ bf16x8 gather_column8(const uint16_t* base, const int (&rows)[8],
@@ -98,7 +110,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_small_bf16(
     const uint16_t* __restrict__ V, int N, int gh, int gw, int mh, int mw, int k, float c2,
     float* __restrict__ out, int32_t* __restrict__ idx_out, int32_t* __restrict__ route_out,
     uint16_t* __restrict__ ql_copy, float* __restrict__ vl_copy, int32_t* __restrict__ perm_copy,
-    int32_t* __restrict__ off_copy) {
+    int32_t* __restrict__ off_copy, int role_period) {
   using L = SmallLds<NMAX, MPAD, KPAD>;
   constexpr int NTMAX = NMAX / 16;  // key (and query) tiles of 16
   __shared__ L S;
@@ -106,6 +118,12 @@ __global__ __launch_bounds__(kSmallThreads) void k_small_bf16(
   const int64_t bh = blockIdx.x;
   const int tid = threadIdx.x, l = lane_id(), g = l >> 4, c16 = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(wave_id());
+  // the waves' roles in the middle phases (selection, landmark values,
+  // routing): swapped between wave pairs (0, 2) and (1, 3) in every other
+  // group of role_period blocks (the CU count), so that two blocks sharing
+  // a CU - one from each group - run their selection waves on different
+  // SIMDs
+  const int rw = ((static_cast<int>(blockIdx.x) / role_period) & 1) ? (w ^ 2) : w;
   const int nt = (N + 15) / 16;
   const int ntp = (nt + 1) & ~1;  // whole 32-key MFMA steps
   const uint16_t* Qh = Q + bh * N * kD;
@@ -204,10 +222,10 @@ __global__ __launch_bounds__(kSmallThreads) void k_small_bf16(
       for (int r = 0; r < 4; ++r) sc[kt][r] = (16 * kt + 4 * g + r < N) ? a[r] : -INFINITY;
     }
   };
-  if (w < LT) {
-    const int i = 16 * w + c16;  // this lane's landmark (>= m: nothing is kept)
+  if (rw < LT) {
+    const int i = 16 * rw + c16;  // this lane's landmark (>= m: nothing is kept)
     float sc[NTMAX][4];
-    tile_scores(w, sc);
+    tile_scores(rw, sc);
     // 32-bit order bits of the scores of keys 16 kt + 4g + r (0, below
     // every real score, for the keys past N)
     uint32_t ob[NTMAX][4];
@@ -223,21 +241,65 @@ __global__ __launch_bounds__(kSmallThreads) void k_small_bf16(
     // below takes every key equal to it, if any), so the rest of the search
     // would not change the set.  The wave stops once all 16 have (lanes of
     // landmarks past m from the start).
+    //   Counting runs on packed 16-bit halves, two keys per register: while
+    // the candidate's low half is zero (bits 31 .. 16) a key reaches it iff
+    // its high half does; after that only keys whose high half equals T's
+    // can still differ, and they compare on their low halves (the others
+    // keep a fixed count).  Keys past N have order bits 0 and never count.
+    constexpr int NV = NTMAX * 4, NP = NV / 2;
+    uint32_t hp[NP];
+#pragma unroll
+    for (int p2 = 0; p2 < NP; ++p2) {
+      const uint32_t a = ob[(2 * p2) >> 2][(2 * p2) & 3], b = ob[(2 * p2 + 1) >> 2][(2 * p2 + 1) & 3];
+      hp[p2] = (a >> 16) | (b & 0xFFFF0000u);
+    }
+    // keys below the candidate c (16 bits, >= 1) among the packed halves
+    auto below16 = [&](const uint32_t (&v)[NP], uint32_t c) -> int {
+      const uint32_t c2x = c * 0x10001u;
+      us16x2 a0 = {0, 0}, a1 = {0, 0};
+#pragma unroll
+      for (int p2 = 0; p2 < NP; p2 += 2) {
+        a0 += __builtin_bit_cast(us16x2, lt16x2(c2x, v[p2]));
+        if (p2 + 1 < NP) a1 += __builtin_bit_cast(us16x2, lt16x2(c2x, v[p2 + 1]));
+      }
+      a0 += a1;
+      return static_cast<int>(a0[0]) + static_cast<int>(a0[1]);
+    };
     uint32_t T = 0;
     bool done = i >= m;
-    for (int bit = 31; bit >= 0; --bit) {
+    for (int bit = 31; bit >= 16; --bit) {
       if (ballot(!done) == 0ull) break;  // wave-uniform
       const uint32_t cand = T | (1u << bit);
-      int c = 0;
-#pragma unroll
-      for (int kt = 0; kt < NTMAX; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) c += ob[kt][r] >= cand ? 1 : 0;
+      int c = NV - below16(hp, cand >> 16);
       c = xor_sum_i(c, 16);
       c = xor_sum_i(c, 32);
       if (!done && c >= k) {
         T = cand;
         done = c == k;
+      }
+    }
+    if (ballot(!done) != 0ull) {
+      // low halves: keys whose high half is T's take their low half, the
+      // others 0 (below every low candidate); those above T's high half
+      // count for every low candidate
+      const uint32_t hiT = T >> 16;
+      const int above = hiT == 0xFFFFu ? 0 : NV - below16(hp, hiT + 1);
+      uint32_t lp[NP];
+#pragma unroll
+      for (int p2 = 0; p2 < NP; ++p2) {
+        const uint32_t a = ob[(2 * p2) >> 2][(2 * p2) & 3], b = ob[(2 * p2 + 1) >> 2][(2 * p2 + 1) & 3];
+        lp[p2] = ((a >> 16) == hiT ? (a & 0xFFFFu) : 0u) | ((b >> 16) == hiT ? (b << 16) : 0u);
+      }
+      for (int bit = 15; bit >= 0; --bit) {
+        if (ballot(!done) == 0ull) break;  // wave-uniform
+        const uint32_t cand = T | (1u << bit);
+        int c = above + NV - below16(lp, cand & 0xFFFFu);
+        c = xor_sum_i(c, 16);
+        c = xor_sum_i(c, 32);
+        if (!done && c >= k) {
+          T = cand;
+          done = c == k;
+        }
       }
     }
     int gt = 0;
@@ -292,7 +354,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_small_bf16(
   }
   // LT == 1, 2: wave LT computes every tile's landmark values in turn while
   // wave 3 routes and buckets; LT == 4: each wave its own tile
-  for (int lt = LT == 4 ? w : 0; (LT == 4 || w == LT) && lt < LT; lt += (LT == 4 ? LT : 1)) {
+  for (int lt = LT == 4 ? w : 0; (LT == 4 || rw == LT) && lt < LT; lt += (LT == 4 ? LT : 1)) {
     const int i = 16 * lt + c16;
     float sc[NTMAX][4];
     tile_scores(lt, sc);
@@ -399,7 +461,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_small_bf16(
     // the experts and wave LT computes the landmark values: routing and
     // bucketing leave the critical path.  A single wave's LDS accesses
     // complete in program order, so it needs no barrier of its own.
-    if (w == 3) {
+    if (rw == 3) {
       bf16x8 qa[2], qn[2];
       load_tile(0, qa);
       for (int qt = 0; qt < nt; ++qt) {
@@ -621,7 +683,8 @@ static hipError_t launch_small_t(const Shape& s, const void* Q, const void* K, c
                      static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
                      static_cast<const uint16_t*>(V), static_cast<int>(s.N), s.gh, s.gw, s.mh,
                      s.mw, s.k, s.scale * kLog2e, out, idx_out, route_out,
-                     static_cast<uint16_t*>(ql_copy), vl_copy, perm_copy, off_copy);
+                     static_cast<uint16_t*>(ql_copy), vl_copy, perm_copy, off_copy,
+                     s.cus > 0 ? s.cus : 256);
   return hipGetLastError();
 }
 

@@ -320,6 +320,7 @@ int64_t max_window(const Shape& s) {
 }
 
 void derive(Shape& s, int cus) {
+  s.cus = cus;
   s.mpad = static_cast<int>(round_up(s.m, 32));
   s.kpad = static_cast<int>(round_up(s.k, 32));
   s.scan_waves = s.m <= 16 ? 1 : (s.m <= 32 ? 2 : 4);

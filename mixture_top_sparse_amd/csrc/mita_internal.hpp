@@ -49,6 +49,7 @@ struct Shape {
   bool small = false;   // one launch, one workgroup per head, no work space
   int s = 1;            // experts per query
   int64_t NA = 0;       // (query, expert) assignments per head: N * s
+  int cus = 0;          // compute units of the device
 };
 
 // Work space carved from one stream-ordered allocation.

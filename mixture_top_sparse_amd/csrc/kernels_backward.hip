@@ -771,6 +771,257 @@ __global__ __launch_bounds__(512) void k_bw_attend(
   }
 }
 
+// The same step for bf16 inputs in four-wave blocks whose LDS fits two
+// blocks per CU (about 61 KiB), so that one block's barriers overlap the
+// other's work: every operand that is exact in bf16 stays bf16 in LDS (the
+// pair keys [Ql; K_e], the raw values V_e, the query rows) and is widened
+// when read; the landmark values Vl, dout and g stay fp32.  One group of 16
+// queries at a time (the next group's rows in registers meanwhile); wave w
+// owns column blocks w and w + 4 and dims 16 w .. 16 w + 15 of dQ, as in
+// k_bw_attend.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_bw_attend_bf16(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ ql,
+    const float* __restrict__ vl, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ item_start, int tpb, int64_t N, int m, int k, float scale,
+    const float* __restrict__ dout, float* __restrict__ dQ, float* __restrict__ dke,
+    float* __restrict__ dve, float* __restrict__ part, int items) {
+  __shared__ __attribute__((aligned(16))) uint16_t sPk[kBwPairs * kBf16St];  // [Ql; 0; K_e; 0]
+  __shared__ __attribute__((aligned(16))) float sVl[kMaxM * kBwSt];          // Vl rows (fp32)
+  __shared__ __attribute__((aligned(16))) uint16_t sV[kMaxK * kBf16St];     // V_e rows
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[16 * kBf16St];
+  __shared__ __attribute__((aligned(16))) float sG[16 * kBwSt];
+  __shared__ __attribute__((aligned(16))) float sGs[16 * kBwGsSt];
+  __shared__ float sRed[3][4][16];
+  __shared__ int sQid[16];
+  const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
+  const int tid = threadIdx.x;
+  const int64_t bh = blockIdx.y;
+  TileInfo ti;
+  if (!find_item(item_start + bh * (m + 1), offsets + bh * (m + 1), m, tpb, blockIdx.x, ti))
+    return;  // whole block: past the head's last item
+  const int MP = (m + 15) & ~15, KP = (k + 15) & ~15;
+  const int PP = MP + KP, NB = PP / 16;
+  const int32_t* ex = idx + (bh * m + ti.e) * k;
+  for (int u = tid; u < PP * 8; u += 256) {
+    const int row = u >> 3, j = u & 7;
+    Raw8<BF16> kv;
+    if (row < m) {
+      kv.load(ql + (bh * m + row) * kD + 8 * j);
+      float vv[8];
+      load8(vl + (bh * m + row) * kD + 8 * j, vv);
+      store8(sVl + row * kBwSt + 8 * j, vv);
+    } else if (row >= MP && row < MP + k) {
+      const int64_t t = clamp64(ex[row - MP], N);
+      kv.load(K + (bh * N + t) * kD + 8 * j);
+      Raw8<BF16> v8;
+      v8.load(V + (bh * N + t) * kD + 8 * j);
+      v8.store_raw(sV + (row - MP) * kBf16St + 8 * j);
+    } else {
+      kv.zero();
+      if (row < MP) {
+        float z[8];
+        zero8(z);
+        store8(sVl + row * kBwSt + 8 * j, z);
+      } else {
+        Raw8<BF16> z;
+        z.zero();
+        z.store_raw(sV + (row - MP) * kBf16St + 8 * j);
+      }
+    }
+    kv.store_raw(sPk + row * kBf16St + 8 * j);
+  }
+  const float c2 = scale * kLog2e;
+  f32x4 aK[2][4], aV[2][4];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      aK[cb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      aV[cb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  // one group ahead: thread (row, 4 dims) of Q (8 bytes) and of dout
+  const int srow = tid >> 4, sc4 = tid & 15;
+  u32x2 pq = {0u, 0u};
+  f32x4 pg = {0.f, 0.f, 0.f, 0.f};
+  int pid = 0;
+  auto fetch = [&](int q0) {
+    if (q0 + srow < ti.qe) {
+      const int64_t q = clamp64(perm[bh * N + q0 + srow], N);
+      pq = *reinterpret_cast<const u32x2*>(Q + (bh * N + q) * kD + 4 * sc4);
+      pg = *reinterpret_cast<const f32x4*>(dout + (bh * N + q) * kD + 4 * sc4);
+      pid = static_cast<int>(q);
+    } else {
+      pq = u32x2{0u, 0u};
+      pg = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  // element (row, col) of a bf16 LDS array, widened
+  auto bf = [](const uint16_t* a, int i) { return bf16_to_f32(a[i]); };
+  fetch(ti.qb);
+  for (int q0 = ti.qb; q0 < ti.qe; q0 += 16) {
+    const int nv = ti.qe - q0 < 16 ? ti.qe - q0 : 16;
+    __syncthreads();  // the expert staged; the previous group's LDS reads done
+    *reinterpret_cast<u32x2*>(sQ + srow * kBf16St + 4 * sc4) = pq;
+    *reinterpret_cast<f32x4*>(sG + srow * kBwSt + 4 * sc4) = pg;
+    if (sc4 == 0) sQid[srow] = pid;
+    fetch(q0 + 16);
+    __syncthreads();
+    ScoreA<BF16> aq;
+    aq.load(reinterpret_cast<const float*>(sQ), c16, g);
+    float ag[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) ag[s] = sG[c16 * kBwSt + 4 * s + g];
+    f32x4 S[2], dW[2];
+    float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const int pb = w + 4 * cb;
+      S[cb] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      dW[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (pb < NB) {  // wave-uniform
+        const f32x4 s4 = aq.score(reinterpret_cast<const float*>(sPk), 16 * pb + c16, g);
+        f32x4 d4 = {0.f, 0.f, 0.f, 0.f}, d4b = d4;  // two chains of 8
+        const int p = 16 * pb + c16;
+        if (16 * pb < MP) {  // landmark values (fp32)
+#pragma unroll
+          for (int s = 0; s < 16; s += 2) {
+            d4 = mfma_f32(ag[s], sVl[p * kBwSt + 4 * s + g], d4);
+            d4b = mfma_f32(ag[s + 1], sVl[p * kBwSt + 4 * (s + 1) + g], d4b);
+          }
+        } else {  // raw values (bf16)
+#pragma unroll
+          for (int s = 0; s < 16; s += 2) {
+            d4 = mfma_f32(ag[s], bf(sV, (p - MP) * kBf16St + 4 * s + g), d4);
+            d4b = mfma_f32(ag[s + 1], bf(sV, (p - MP) * kBf16St + 4 * (s + 1) + g), d4b);
+          }
+        }
+        d4 += d4b;
+        const bool pv = p < m || (p >= MP && p < MP + k);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          S[cb][r] = pv ? s4[r] * c2 : -INFINITY;  // log2 units
+          mx[r] = fmaxf(mx[r], S[cb][r]);
+        }
+        dW[cb] = d4;
+      }
+    }
+    // row statistics in one exchange (each wave's own max and sums over its
+    // columns, rescaled to the block's maximum; a wave without columns
+    // reports -inf and 0)
+    float E[2][4], z[4], y[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      mx[r] = row16_max(mx[r]);
+      z[r] = 0.f;
+      y[r] = 0.f;
+    }
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        E[cb][r] = mx[r] == -INFINITY ? 0.f : fast_exp2(S[cb][r] - mx[r]);
+        z[r] += E[cb][r];
+        y[r] += E[cb][r] * dW[cb][r];
+      }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      z[r] = row16_sum(z[r]);
+      y[r] = row16_sum(y[r]);
+      if (c16 == 0) {
+        sRed[0][w][4 * g + r] = mx[r];
+        sRed[1][w][4 * g + r] = z[r];
+        sRed[2][w][4 * g + r] = y[r];
+      }
+    }
+    __syncthreads();
+    float Wt[2][4], Gs[2][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * g + r;
+      float mv[4], M = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        mv[v] = sRed[0][v][row];
+        M = fmaxf(M, mv[v]);
+      }
+      float Z = 0.f, Y = 0.f;  // M is finite: some wave holds a valid pair
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float f = mv[v] == -INFINITY ? 0.f : fast_exp2(mv[v] - M);
+        Z += sRed[1][v][row] * f;
+        Y += sRed[2][v][row] * f;
+      }
+      const float own = mx[r] == -INFINITY ? 0.f : fast_exp2(mx[r] - M);
+      const float inv = row < nv ? own / Z : 0.f;  // padding rows contribute nothing
+      const float c = Y / Z;                       // dout . out of this query
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        Wt[cb][r] = E[cb][r] * inv;
+        Gs[cb][r] = scale * Wt[cb][r] * (dW[cb][r] - c);
+      }
+    }
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const int pb = w + 4 * cb;
+      if (pb >= NB) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sGs[(4 * g + r) * kBwGsSt + 16 * pb + c16] = Gs[cb][r];
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          aK[cb][db] = mfma_f32(Gs[cb][r], bf(sQ, (4 * g + r) * kBf16St + 16 * db + c16), aK[cb][db]);
+          aV[cb][db] = mfma_f32(Wt[cb][r], sG[(4 * g + r) * kBwSt + 16 * db + c16], aV[cb][db]);
+        }
+    }
+    __syncthreads();
+    // dQ (16 queries x dims 16 w .. 16 w + 15) = g [keys], four chains
+    f32x4 dq[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dq[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < 4 * NB; s += 4)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        dq[j] = mfma_f32(sGs[c16 * kBwGsSt + 4 * (s + j) + g],
+                         bf(sPk, (4 * (s + j) + g) * kBf16St + 16 * w + c16), dq[j]);
+    dq[0] += dq[1] + dq[2] + dq[3];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * g + r;
+      if (row < nv) dQ[(bh * N + sQid[row]) * kD + 16 * w + c16] = dq[0][r];
+    }
+  }
+  // the item's sums: landmark rows to its partial, raw-key rows to the
+  // expert's key sums
+  float* pq_ = part + ((bh * items + blockIdx.x) * 2) * static_cast<int64_t>(m) * kD;
+  float* pv_ = pq_ + static_cast<int64_t>(m) * kD;
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int pb = w + 4 * cb;
+    if (pb >= NB) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int p = 16 * pb + 4 * g + r;
+      if (p < m) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          pq_[p * kD + 16 * db + c16] = aK[cb][db][r];
+          pv_[p * kD + 16 * db + c16] = aV[cb][db][r];
+        }
+      } else if (p >= MP && p < MP + k) {
+        const int64_t row = (bh * m + ti.e) * k + (p - MP);  // expert e's j-th key
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          unsafeAtomicAdd(dke + row * kD + 16 * db + c16, aK[cb][db][r]);
+          unsafeAtomicAdd(dve + row * kD + 16 * db + c16, aV[cb][db][r]);
+        }
+      }
+    }
+  }
+}
+
 // Block (landmark, head), 16 waves, lane = dim: dVl and the expert step's
 // dQl summed over the head's work items (wave w takes items w, w + 16, ...,
 // four at a time), and D = dVl . Vl.
@@ -1139,9 +1390,14 @@ hipError_t launch_backward_t(const Shape& s, const BwPlan& bp, const BwWorkspace
     }
   }
   if (step(kBwAttend)) {
-    hipLaunchKernelGGL(k_bw_attend<T>, dim3(bp.items, BH), dim3(512), 0, st, Q, K, V, ql, ws.vl,
-                       idx, ws.perm, ws.offsets, ws.item_start, bp.tpb, s.N, s.m, s.k, s.scale,
-                       dout, dQ, ws.dke, ws.dve, ws.part1, bp.items);
+    if constexpr (std::is_same<T, BF16>::value)
+      hipLaunchKernelGGL(k_bw_attend_bf16, dim3(bp.items, BH), dim3(256), 0, st, Q, K, V, ql,
+                         ws.vl, idx, ws.perm, ws.offsets, ws.item_start, bp.tpb, s.N, s.m, s.k,
+                         s.scale, dout, dQ, ws.dke, ws.dve, ws.part1, bp.items);
+    else
+      hipLaunchKernelGGL(k_bw_attend<T>, dim3(bp.items, BH), dim3(512), 0, st, Q, K, V, ql,
+                         ws.vl, idx, ws.perm, ws.offsets, ws.item_start, bp.tpb, s.N, s.m, s.k,
+                         s.scale, dout, dQ, ws.dke, ws.dve, ws.part1, bp.items);
     e = hipGetLastError();
     if (e == hipSuccess) {
       hipLaunchKernelGGL(k_bw_reduce1, dim3(s.m, BH), dim3(1024), 0, st, ws.part1, ws.item_start,

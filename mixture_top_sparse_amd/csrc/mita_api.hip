@@ -390,6 +390,11 @@ void derive(Shape& s, int cus) {
   // (tpb - 1) / tpb, so tiles / tpb + m bounds them
   s.attend_items = static_cast<int>(cdiv(tiles, tpb) + s.m);
   s.small = small_path_fits(s);
+  s.medium = !s.small && medium_path_fits(s);
+  if (s.medium) {  // exact selection inside the one launch: no pre-threshold
+    s.theta_groups = 0;
+    s.theta_sampled = false;
+  }
 }
 
 }  // namespace
@@ -414,6 +419,13 @@ size_t plan_workspace(const Shape& s, Workspace* ws, char* base) {
   } else {
     ws->gmax = nullptr;
     ws->theta = nullptr;
+  }
+  if (s.medium) {  // no split partials
+    ws->vl = reinterpret_cast<float*>(take(BH * s.m * kD * sizeof(float)));
+    ws->offsets = reinterpret_cast<int32_t*>(take(BH * (s.m + 1) * 4));
+    ws->item_start = reinterpret_cast<int32_t*>(take(BH * (s.m + 1) * 4));
+    ws->perm = reinterpret_cast<int32_t*>(take(BH * s.NA * 4));
+    return off;
   }
   const size_t parts = BH * s.scan_splits * s.mrows;
   ws->part_keys = reinterpret_cast<uint64_t*>(take(parts * kTopCap * sizeof(uint64_t)));
@@ -546,32 +558,43 @@ int forward_impl(const void* Q, const void* K, const void* V, int dtype, int64_t
       StageTimer t(kStagePool, st, !use_scratch);
       e = launch_pool(s, Q, ws, ql_copy, 0, s.BH, st);
     }
-    // All on the caller's stream, in this order: pool; the top-k
+    // All on the caller's stream, in this order.  Mid-length bf16 heads:
+    // pool; the landmark scan and exact selection, routing and bucketing in
+    // one launch; the expert attention.  Otherwise: pool; the top-k
     // pre-threshold's group maxima; routing (the pre-threshold's selection as
     // its leading blocks); the landmark scan (step 4's prefix over the
     // routing counts as its trailing blocks); the merge (step 4's scatter as
     // leading blocks of its first pass); the expert attention.  Bucketing
     // rides in launches that follow routing anyway, so the call needs no
     // second stream and no events.
-    if (e == hipSuccess && s.theta_groups > 0) {
-      where = "landmark_threshold";
-      StageTimer t(kStageThreshold, st, !use_scratch);
-      e = launch_threshold(s, K, ws, st);
-    }
-    if (e == hipSuccess) {
-      where = "route";
-      StageTimer t(kStageRoute, st, !use_scratch);
-      e = s.s > 1 ? launch_route_s(s, Q, ws, route_out, st) : launch_route(s, Q, ws, route_out, st);
-    }
-    if (e == hipSuccess) {
-      where = "landmark_scan";
-      StageTimer t(kStageScan, st, !use_scratch);
-      e = launch_scan(s, K, V, ws, route_out, st);
-    }
-    if (e == hipSuccess) {
-      where = "landmark_merge";
-      StageTimer t(kStageMerge, st, !use_scratch);
-      e = launch_merge(s, ws, idx_out, vl_copy, route_out, off_copy, perm_copy, st);
+    if (s.medium) {
+      if (e == hipSuccess) {
+        where = "landmark_scan";
+        StageTimer t(kStageScan, st, !use_scratch);
+        e = launch_medium(s, Q, K, V, ws, idx_out, route_out, vl_copy, off_copy, perm_copy, st);
+      }
+    } else {
+      if (e == hipSuccess && s.theta_groups > 0) {
+        where = "landmark_threshold";
+        StageTimer t(kStageThreshold, st, !use_scratch);
+        e = launch_threshold(s, K, ws, st);
+      }
+      if (e == hipSuccess) {
+        where = "route";
+        StageTimer t(kStageRoute, st, !use_scratch);
+        e = s.s > 1 ? launch_route_s(s, Q, ws, route_out, st)
+                    : launch_route(s, Q, ws, route_out, st);
+      }
+      if (e == hipSuccess) {
+        where = "landmark_scan";
+        StageTimer t(kStageScan, st, !use_scratch);
+        e = launch_scan(s, K, V, ws, route_out, st);
+      }
+      if (e == hipSuccess) {
+        where = "landmark_merge";
+        StageTimer t(kStageMerge, st, !use_scratch);
+        e = launch_merge(s, ws, idx_out, vl_copy, route_out, off_copy, perm_copy, st);
+      }
     }
     if (e == hipSuccess) {
       where = "expert_attend";

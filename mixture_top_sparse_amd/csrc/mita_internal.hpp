@@ -22,6 +22,7 @@ constexpr int kPoolDirectMax = 128;  // windows up to this many tokens: one-laun
 constexpr int kThetaTilesPerBlock = 1;  // sample tiles per top-k pre-threshold block
 constexpr int kThetaMaxGroups = 4096;  // group maxima the pre-threshold selection holds (64 per lane)
 constexpr int kSmallMaxN = 256;  // bf16 heads up to this many tokens: one-launch path
+constexpr int kMediumMaxN = 1600;  // bf16 heads up to this many tokens: steps 2-4 in one launch
 constexpr int kMaxS = 8;         // experts per query, at most
 
 struct Shape {
@@ -47,6 +48,7 @@ struct Shape {
   int attend_tpb = 0;   // 64-query tiles per expert-attention work item
   int attend_items = 0; // upper bound of work items per head
   bool small = false;   // one launch, one workgroup per head, no work space
+  bool medium = false;  // scan, selection, routing and bucketing in one launch
   int s = 1;            // experts per query
   int64_t NA = 0;       // (query, expert) assignments per head: N * s
   int cus = 0;          // compute units of the device
@@ -116,6 +118,14 @@ bool small_path_fits(const Shape& s);
 hipError_t launch_small(const Shape& s, const void* Q, const void* K, const void* V, float* out,
                         int32_t* idx_out, int32_t* route_out, void* ql_copy, float* vl_copy,
                         int32_t* perm_copy, int32_t* off_copy, hipStream_t st);
+// steps 2 to 4 in one launch for mid-length bf16 sequences (after pooling,
+// before the expert attention): each landmark's exact top k and V_l from
+// scores kept in registers, and per head the routes and the bucket order;
+// medium_path_fits says when it applies
+bool medium_path_fits(const Shape& s);
+hipError_t launch_medium(const Shape& s, const void* Q, const void* K, const void* V,
+                         const Workspace& ws, int32_t* idx_out, int32_t* route_out,
+                         float* vl_copy, int32_t* off_copy, int32_t* perm_copy, hipStream_t st);
 // dense attention over all N pairs (the baseline); bf16 only
 hipError_t launch_dense(int dtype, const void* Q, const void* K, const void* V, int64_t BH,
                         int64_t N, int64_t d, float scale, float* out, hipStream_t st);

@@ -76,7 +76,10 @@ __device__ __forceinline__ int64_t clamp_index(int64_t v, int64_t n) {
 // differs from the exact combination of its weights by at most about
 // 3 * 2^-16 * max|value| plus fp32 accumulation, whatever the values' range.
 
-// Stage the expert of this work item.
+// Stage the expert of this work item.  Every global load is issued before
+// any LDS write (the expert's key indices first, then the rows they name,
+// the landmark values and the landmark queries), so the item pays one
+// index-then-row latency instead of one per operand.
 template <int MPAD, int KPAD, int NW>
 __device__ void stage_bf16(AttendLds<BF16, MPAD, KPAD, NW>& S, const uint16_t* __restrict__ K,
                           const uint16_t* __restrict__ V, const uint16_t* __restrict__ Ql,
@@ -87,79 +90,113 @@ __device__ void stage_bf16(AttendLds<BF16, MPAD, KPAD, NW>& S, const uint16_t* _
   constexpr int NT = 64 * NW;
   const int tid = threadIdx.x;
   const u32x4 z = {0, 0, 0, 0};
-
   // raw values: unit u = rows 2rp, 2rp+1 of the expert, 8 features from
   // 8*col, stored transposed as bf16 pairs (row 2rp low, 2rp+1 high)
-  constexpr int RU = (KPAD / 2) * 8;
-  for (int u = tid; u < RU; u += NT) {
-    const int rp = u >> 3, col = u & 7;
-    u32x4 va = z, vb = z;
-    if (2 * rp < k)
-      va = *reinterpret_cast<const u32x4*>(V + (bh * N + clamp_index(ex[2 * rp], N)) * kD +
-                                           col * 8);
-    if (2 * rp + 1 < k)
-      vb = *reinterpret_cast<const u32x4*>(V + (bh * N + clamp_index(ex[2 * rp + 1], N)) * kD +
-                                           col * 8);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t a = (i & 1) ? (va[i >> 1] >> 16) : (va[i >> 1] & 0xFFFFu);
-      const uint32_t b = (i & 1) ? (vb[i >> 1] >> 16) : (vb[i >> 1] & 0xFFFFu);
-      *reinterpret_cast<uint32_t*>(S.vr + (col * 8 + i) * L::VRST + 2 * rp) = a | (b << 16);
-    }
-  }
+  constexpr int RU = (KPAD / 2) * 8, RPT = (RU + NT - 1) / NT;
   // landmark values: unit u = rows 2lp, 2lp+1, 8 features from 8*dc, split
   // into bf16 hi + lo and stored transposed
   constexpr int LP = MPAD / 2;
-  constexpr int LU = LP * 8;
-  for (int u = tid; u < LU; u += NT) {
-    const int lp = u % LP, dc = u / LP;
-    float la[8], lb[8];
+  constexpr int LU = LP * 8, LPT = (LU + NT - 1) / NT;
+  // pair keys: Ql rows then the expert's K rows (zero rows for padding)
+  constexpr int PU = NP * 8, PPT = (PU + NT - 1) / NT;
+
+  int64_t rra[RPT], rrb[RPT];  // raw rows of each raw unit (-1: none)
+  int64_t prow[PPT];           // source row of each pair-key chunk (-1: zero)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) la[i] = lb[i] = 0.f;
+  for (int j = 0; j < RPT; ++j) {
+    const int u = tid + NT * j, rp = u >> 3;
+    rra[j] = (u < RU && 2 * rp < k) ? clamp_index(ex[2 * rp], N) : -1;
+    rrb[j] = (u < RU && 2 * rp + 1 < k) ? clamp_index(ex[2 * rp + 1], N) : -1;
+  }
+#pragma unroll
+  for (int j = 0; j < PPT; ++j) {
+    const int c = tid + NT * j, row = c >> 3;
+    prow[j] = (c >= PU || row >= NP) ? -1
+              : row < MPAD           ? (row < m ? row : -1)
+              : (row - MPAD < k ? clamp_index(ex[row - MPAD], N) : -1);
+  }
+  u32x4 va[RPT], vb[RPT];
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    const int col = (tid + NT * j) & 7;
+    va[j] = rra[j] >= 0 ? *reinterpret_cast<const u32x4*>(V + (bh * N + rra[j]) * kD + col * 8) : z;
+    vb[j] = rrb[j] >= 0 ? *reinterpret_cast<const u32x4*>(V + (bh * N + rrb[j]) * kD + col * 8) : z;
+  }
+  f32x4 lv[LPT][2][2];
+#pragma unroll
+  for (int j = 0; j < LPT; ++j) {
+    const int u = tid + NT * j, lp = u % LP, dc = u / LP;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int row = 2 * lp + h;
-      if (row < m) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(vl + (bh * m + row) * kD + dc * 8);
-        const f32x4 b = *reinterpret_cast<const f32x4*>(vl + (bh * m + row) * kD + dc * 8 + 4);
-        float* dst = h ? lb : la;
+      const bool ok = u < LU && row < m;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          dst[i] = a[i];
-          dst[4 + i] = b[i];
-        }
-      }
-    }
-    bf16x8 ah, al, bh8, bl8;
-    split_hi_lo_pk(la, ah, al);
-    split_hi_lo_pk(lb, bh8, bl8);
-    // the halves are taken from the raw bits (element i of a bf16x8 is the
-    // low (even i) or high (odd i) half of dword i/2)
-    const u32x4 wah = __builtin_bit_cast(u32x4, ah), wal = __builtin_bit_cast(u32x4, al);
-    const u32x4 wbh = __builtin_bit_cast(u32x4, bh8), wbl = __builtin_bit_cast(u32x4, bl8);
-    auto half = [](const u32x4& v, int i) {
-      return (i & 1) ? (v[i >> 1] >> 16) : (v[i >> 1] & 0xFFFFu);
-    };
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      *reinterpret_cast<uint32_t*>(S.vch + (dc * 8 + i) * L::VCST + 2 * lp) =
-          half(wah, i) | (half(wbh, i) << 16);
-      *reinterpret_cast<uint32_t*>(S.vcl + (dc * 8 + i) * L::VCST + 2 * lp) =
-          half(wal, i) | (half(wbl, i) << 16);
+      for (int q = 0; q < 2; ++q)
+        lv[j][h][q] = ok ? *reinterpret_cast<const f32x4*>(vl + (bh * m + row) * kD + dc * 8 + 4 * q)
+                         : f32x4{0, 0, 0, 0};
     }
   }
-
-  // pair keys: Ql rows then the expert's K rows (zero rows for padding)
-  for (int c = tid; c < NP * 8; c += NT) {
-    const int row = c >> 3, cc = c & 7;
-    u32x4 v = z;
-    if (row < MPAD) {
-      if (row < m) v = *reinterpret_cast<const u32x4*>(Ql + (bh * m + row) * kD + cc * 8);
-    } else if (row - MPAD < k) {
-      const int64_t t = clamp_index(ex[row - MPAD], N);
-      v = *reinterpret_cast<const u32x4*>(K + (bh * N + t) * kD + cc * 8);
+  u32x4 pv[PPT];
+#pragma unroll
+  for (int j = 0; j < PPT; ++j) {
+    const int c = tid + NT * j, row = c >> 3, cc = c & 7;
+    pv[j] = prow[j] < 0 ? z
+            : row < MPAD ? *reinterpret_cast<const u32x4*>(Ql + (bh * m + prow[j]) * kD + cc * 8)
+                         : *reinterpret_cast<const u32x4*>(K + (bh * N + prow[j]) * kD + cc * 8);
+  }
+  // LDS writes
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    const int u = tid + NT * j;
+    if (u < RU) {
+      const int rp = u >> 3, col = u & 7;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t a = (i & 1) ? (va[j][i >> 1] >> 16) : (va[j][i >> 1] & 0xFFFFu);
+        const uint32_t b = (i & 1) ? (vb[j][i >> 1] >> 16) : (vb[j][i >> 1] & 0xFFFFu);
+        *reinterpret_cast<uint32_t*>(S.vr + (col * 8 + i) * L::VRST + 2 * rp) = a | (b << 16);
+      }
     }
-    *reinterpret_cast<u32x4*>(S.pk + row * L::PKST + cc * 8) = v;
+  }
+#pragma unroll
+  for (int j = 0; j < LPT; ++j) {
+    const int u = tid + NT * j;
+    if (u < LU) {
+      const int lp = u % LP, dc = u / LP;
+      float la[8], lb[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        la[i] = lv[j][0][0][i];
+        la[4 + i] = lv[j][0][1][i];
+        lb[i] = lv[j][1][0][i];
+        lb[4 + i] = lv[j][1][1][i];
+      }
+      bf16x8 ah, al, bh8, bl8;
+      split_hi_lo_pk(la, ah, al);
+      split_hi_lo_pk(lb, bh8, bl8);
+      // the halves are taken from the raw bits (element i of a bf16x8 is
+      // the low (even i) or high (odd i) half of dword i/2)
+      const u32x4 wah = __builtin_bit_cast(u32x4, ah), wal = __builtin_bit_cast(u32x4, al);
+      const u32x4 wbh = __builtin_bit_cast(u32x4, bh8), wbl = __builtin_bit_cast(u32x4, bl8);
+      auto half = [](const u32x4& v, int i) {
+        return (i & 1) ? (v[i >> 1] >> 16) : (v[i >> 1] & 0xFFFFu);
+      };
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        *reinterpret_cast<uint32_t*>(S.vch + (dc * 8 + i) * L::VCST + 2 * lp) =
+            half(wah, i) | (half(wbh, i) << 16);
+        *reinterpret_cast<uint32_t*>(S.vcl + (dc * 8 + i) * L::VCST + 2 * lp) =
+            half(wal, i) | (half(wbl, i) << 16);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < PPT; ++j) {
+    const int c = tid + NT * j;
+    if (c < PU) {
+      const int row = c >> 3, cc = c & 7;
+      *reinterpret_cast<u32x4*>(S.pk + row * L::PKST + cc * 8) = pv[j];
+    }
   }
 }
 
@@ -471,6 +508,281 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 8
   attend_bf16<MPAD, KPAD, FULL, NW>(S, Q, K, V, Ql, vl, idx, perm, N, m, k, c2, out, bh, ti);
 }
 
+// ---- short items: several work items per block ---------------------------
+//
+// When experts hold few queries (the image-shaped workloads: 20-35 per
+// expert), a block that stages one expert spends most of its life waiting on
+// a chain of dependent loads: the work-item table, the expert's key list,
+// the key and value rows it names.  Here each 2-wave block takes
+// kAttendIpb consecutive work items of one head: the compressed pairs (Ql
+// rows, Vl as hi + lo) are staged once, the items' key lists are read once,
+// and while the block computes one item the next item's key and value rows
+// and its first query rows are already loading into registers (their
+// positions in the bucket order were read one item earlier still).
+constexpr int kAttendIpbMax = 8;  // work items per block, at most
+
+template <int MPAD, int KPAD>
+struct RawRows {  // one item's raw pairs in flight, 128 threads
+  static constexpr int RU = (KPAD / 2) * 8, RPT = (RU + 127) / 128;  // value-row units
+  static constexpr int KU = KPAD * 8, KPT = (KU + 127) / 128;        // key-row chunks
+  u32x4 va[RPT], vb[RPT], kv[KPT];
+};
+
+template <int MPAD, int KPAD>
+__device__ __forceinline__ void raw_load(RawRows<MPAD, KPAD>& R, const int32_t* ex /* LDS */,
+                                         const uint16_t* __restrict__ K,
+                                         const uint16_t* __restrict__ V, int64_t N, int k,
+                                         int64_t bh) {
+  using RR = RawRows<MPAD, KPAD>;
+  const int tid = threadIdx.x;
+  const u32x4 z = {0, 0, 0, 0};
+#pragma unroll
+  for (int j = 0; j < RR::RPT; ++j) {
+    const int u = tid + 128 * j, rp = u >> 3, col = u & 7;
+    const bool ok = u < RR::RU;
+    R.va[j] = (ok && 2 * rp < k) ? *reinterpret_cast<const u32x4*>(V + (bh * N + ex[2 * rp]) * kD + col * 8) : z;
+    R.vb[j] = (ok && 2 * rp + 1 < k)
+                  ? *reinterpret_cast<const u32x4*>(V + (bh * N + ex[2 * rp + 1]) * kD + col * 8)
+                  : z;
+  }
+#pragma unroll
+  for (int j = 0; j < RR::KPT; ++j) {
+    const int c = tid + 128 * j, row = c >> 3, cc = c & 7;
+    R.kv[j] = (c < RR::KU && row < k)
+                  ? *reinterpret_cast<const u32x4*>(K + (bh * N + ex[row]) * kD + cc * 8)
+                  : z;
+  }
+}
+
+template <int MPAD, int KPAD>
+__device__ __forceinline__ void raw_store(AttendLds<BF16, MPAD, KPAD, 2>& S,
+                                          const RawRows<MPAD, KPAD>& R) {
+  using L = AttendLds<BF16, MPAD, KPAD, 2>;
+  using RR = RawRows<MPAD, KPAD>;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < RR::RPT; ++j) {
+    const int u = tid + 128 * j;
+    if (u < RR::RU) {
+      const int rp = u >> 3, col = u & 7;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t a = (i & 1) ? (R.va[j][i >> 1] >> 16) : (R.va[j][i >> 1] & 0xFFFFu);
+        const uint32_t b = (i & 1) ? (R.vb[j][i >> 1] >> 16) : (R.vb[j][i >> 1] & 0xFFFFu);
+        *reinterpret_cast<uint32_t*>(S.vr + (col * 8 + i) * L::VRST + 2 * rp) = a | (b << 16);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < RR::KPT; ++j) {
+    const int c = tid + 128 * j;
+    if (c < RR::KU)
+      *reinterpret_cast<u32x4*>(S.pk + (MPAD + (c >> 3)) * L::PKST + (c & 7) * 8) = R.kv[j];
+  }
+}
+
+// the compressed pairs of head bh: Ql rows (pair-key rows 0 .. MPAD-1) and
+// Vl^T as bf16 hi + lo, every load issued before any LDS write
+template <int MPAD, int KPAD>
+__device__ __forceinline__ void stage_compressed(AttendLds<BF16, MPAD, KPAD, 2>& S,
+                                                 const uint16_t* __restrict__ Ql,
+                                                 const float* __restrict__ vl, int m, int64_t bh) {
+  using L = AttendLds<BF16, MPAD, KPAD, 2>;
+  constexpr int LP = MPAD / 2, LU = LP * 8, LPT = (LU + 127) / 128;
+  constexpr int QU = MPAD * 8, QPT = (QU + 127) / 128;
+  const int tid = threadIdx.x;
+  const u32x4 z = {0, 0, 0, 0};
+  f32x4 lv[LPT][2][2];
+#pragma unroll
+  for (int j = 0; j < LPT; ++j) {
+    const int u = tid + 128 * j, lp = u % LP, dc = u / LP;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 2 * lp + h;
+      const bool ok = u < LU && row < m;
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        lv[j][h][q] = ok ? *reinterpret_cast<const f32x4*>(vl + (bh * m + row) * kD + dc * 8 + 4 * q)
+                         : f32x4{0, 0, 0, 0};
+    }
+  }
+  u32x4 qv[QPT];
+#pragma unroll
+  for (int j = 0; j < QPT; ++j) {
+    const int c = tid + 128 * j, row = c >> 3;
+    qv[j] = (c < QU && row < m) ? *reinterpret_cast<const u32x4*>(Ql + (bh * m + row) * kD + (c & 7) * 8) : z;
+  }
+#pragma unroll
+  for (int j = 0; j < LPT; ++j) {
+    const int u = tid + 128 * j;
+    if (u < LU) {
+      const int lp = u % LP, dc = u / LP;
+      float la[8], lb[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        la[i] = lv[j][0][0][i];
+        la[4 + i] = lv[j][0][1][i];
+        lb[i] = lv[j][1][0][i];
+        lb[4 + i] = lv[j][1][1][i];
+      }
+      bf16x8 ah, al, bh8, bl8;
+      split_hi_lo_pk(la, ah, al);
+      split_hi_lo_pk(lb, bh8, bl8);
+      const u32x4 wah = __builtin_bit_cast(u32x4, ah), wal = __builtin_bit_cast(u32x4, al);
+      const u32x4 wbh = __builtin_bit_cast(u32x4, bh8), wbl = __builtin_bit_cast(u32x4, bl8);
+      auto half = [](const u32x4& v, int i) {
+        return (i & 1) ? (v[i >> 1] >> 16) : (v[i >> 1] & 0xFFFFu);
+      };
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        *reinterpret_cast<uint32_t*>(S.vch + (dc * 8 + i) * L::VCST + 2 * lp) =
+            half(wah, i) | (half(wbh, i) << 16);
+        *reinterpret_cast<uint32_t*>(S.vcl + (dc * 8 + i) * L::VCST + 2 * lp) =
+            half(wal, i) | (half(wbl, i) << 16);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < QPT; ++j) {
+    const int c = tid + 128 * j;
+    if (c < QU) *reinterpret_cast<u32x4*>(S.pk + (c >> 3) * L::PKST + (c & 7) * 8) = qv[j];
+  }
+}
+
+// grid (ceil(items / kAttendIpb), BH), 128 threads
+template <int MPAD, int KPAD, bool FULL>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k_attend_items_bf16(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ Ql, const float* __restrict__ vl, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ item_start, int tpb, int64_t N, int m, int k, float c2,
+    float* __restrict__ out, int ipb) {
+  constexpr int NW = 2, D = 2;  // waves; query rows in flight per wave (sub-tiles)
+  using L = AttendLds<BF16, MPAD, KPAD, NW>;
+  __shared__ L S;
+  __shared__ int32_t sex[kAttendIpbMax][KPAD];  // the items' key lists (clamped)
+  const int64_t bh = blockIdx.y;
+  const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
+  const int t0 = static_cast<int>(blockIdx.x) * ipb;
+  const int32_t* IS = item_start + bh * (m + 1);
+  const int32_t* OF = offsets + bh * (m + 1);
+  // work items t0 .. t0 + nit - 1 (item t: expert e = the number of experts
+  // e' < m - 1 whose successor starts at or before t; item_start is
+  // non-decreasing); lane j keeps item j's expert and query range
+  const int nitems = IS[m];
+  if (t0 >= nitems) return;  // whole block
+  const int nit = min(ipb, nitems - t0);
+  const int nextst = l < m - 1 ? IS[l + 1] : INT32_MAX;
+  const int ist = l < m ? IS[l] : 0;
+  const int ofl = l <= m && l < 64 ? OF[l] : 0;
+  const int ofm = OF[m];
+  int my_e = 0, my_qb = 0, my_qe = 0;
+#pragma unroll
+  for (int j = 0; j < kAttendIpbMax; ++j) {
+    const int t = t0 + j;
+    const int e = __popcll(ballot(nextst <= t));  // wave-uniform
+    const int qb = __builtin_amdgcn_readlane(ofl, e) +
+                   kAttendTile * tpb * (t - __builtin_amdgcn_readlane(ist, e));
+    const int oe = e + 1 < 64 ? __builtin_amdgcn_readlane(ofl, e + 1) : ofm;  // offsets[e + 1]
+    if (l == j) {
+      my_e = e;
+      my_qb = qb;
+      my_qe = min(qb + kAttendTile * tpb, oe);
+    }
+  }
+  // key lists of the block's items, then the compressed pairs
+  for (int c = tid; c < kAttendIpbMax * KPAD; c += 128) {
+    const int j = c / KPAD, r = c % KPAD;
+    const int e = static_cast<int>(lane_read(static_cast<uint32_t>(my_e), j));
+    sex[j][r] = (j < nit && r < k) ? static_cast<int32_t>(clamp_index(idx[(bh * m + e) * k + r], N)) : 0;
+  }
+  stage_compressed<MPAD, KPAD>(S, Ql, vl, m, bh);
+  __syncthreads();
+
+  const uint16_t* Qh = Q + bh * N * kD;
+  const int32_t* ph = perm + bh * N;
+  float* out_h = out + bh * N * kD;
+  auto load_q = [&](int64_t q, bf16x8 (&qb)[2]) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      qb[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(Qh + q * kD + 32 * s + 8 * g));
+  };
+  // this wave's sub-tiles of item j: w, w + NW, ...; slots clamped to the
+  // item's last query (every gather reads a valid row, so the ring needs no
+  // branch and its waits stay exact)
+  auto slot = [&](int nq, int i) { return min(16 * (w + NW * i) + c16, nq - 1); };
+  RawRows<MPAD, KPAD> R;
+  // pq: this item's ring rows; pqn: the next item's first rows (read one
+  // item ahead); pqnn: the item after that
+  int64_t pq[D], pqn[D], pqnn[D];
+  bf16x8 ring[D][2], ringn[D][2];
+  auto first_rows = [&](int j, int64_t (&dst)[D]) {
+    const int qbj = __builtin_amdgcn_readlane(my_qb, j);
+    const int nqj = __builtin_amdgcn_readlane(my_qe, j) - qbj;
+#pragma unroll
+    for (int d = 0; d < D; ++d) dst[d] = clamp_index(ph[qbj + slot(nqj, d)], N);
+  };
+  {  // item 0: raw rows and first query rows; item 1's row positions
+    first_rows(0, pq);
+#pragma unroll
+    for (int d = 0; d < D; ++d) load_q(pq[d], ring[d]);
+    if (nit > 1) first_rows(1, pqn);
+    raw_load<MPAD, KPAD>(R, sex[0], K, V, N, k, bh);
+    raw_store<MPAD, KPAD>(S, R);
+  }
+  __syncthreads();
+  for (int j = 0; j < nit; ++j) {  // nit is block-uniform
+    const int qb = __builtin_amdgcn_readlane(my_qb, j), nq = __builtin_amdgcn_readlane(my_qe, j) - qb;
+    const bool has_next = j + 1 < nit;
+    if (has_next) {  // the next item's rows start loading now
+#pragma unroll
+      for (int d = 0; d < D; ++d) load_q(pqn[d], ringn[d]);
+      raw_load<MPAD, KPAD>(R, sex[j + 1], K, V, N, k, bh);
+      if (j + 2 < nit) first_rows(j + 2, pqnn);
+    }
+    const int nsub = (nq + 15) / 16;
+    const int nw = nsub > w ? (nsub - w + NW - 1) / NW : 0;  // this wave's sub-tiles
+    if (nw >= D) {
+      // whole ring rounds: the last round's extra slots repeat the item's
+      // last query (same values stored again); refills past the end re-read it
+      const int rounds = (nw + D - 1) / D;
+      for (int r = 0; r < rounds; ++r) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+          const int i = r * D + d;
+          __asm__ volatile("" ::: "memory");
+          __builtin_amdgcn_sched_barrier(0);
+          attend_queries_bf16<MPAD, KPAD, NW, FULL>(
+              S, ring[d], 16 * (w + NW * i), nq, m, k, c2, out_h, pq[d],
+              [&](bf16x8(&q)[2]) {
+                pq[d] = clamp_index(ph[qb + slot(nq, i + D)], N);
+                load_q(pq[d], q);
+              });
+        }
+      }
+    } else {
+      // fewer sub-tiles than ring slots: all of them are in the ring already
+#pragma unroll
+      for (int d = 0; d < D; ++d)
+        if (d < nw)
+          attend_queries_bf16<MPAD, KPAD, NW, FULL>(S, ring[d], 16 * (w + NW * d), nq, m, k, c2,
+                                                    out_h, pq[d], [](bf16x8(&)[2]) {});
+    }
+    __syncthreads();  // every wave is done with item j's raw pairs
+    if (has_next) {
+      raw_store<MPAD, KPAD>(S, R);
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        pq[d] = pqn[d];
+        pqn[d] = pqnn[d];
+        ring[d][0] = ringn[d][0];
+        ring[d][1] = ringn[d][1];
+      }
+      __syncthreads();
+    }
+  }
+}
+
 template <int MPAD, int KPAD, bool FULL>
 __global__ __launch_bounds__(256) void k_attend_f32(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
@@ -680,6 +992,22 @@ template <class T, int MPAD, int KPAD, int NW>
 static hipError_t launch_attend_w(const Shape& s, const void* Q, const void* K, const void* V,
                                   const int32_t* idx, const Workspace& ws, float* out,
                                   hipStream_t st) {
+  if constexpr (std::is_same<T, BF16>::value && NW == 2) {
+    auto kern = (s.m == MPAD && s.k == KPAD) ? k_attend_items_bf16<MPAD, KPAD, true>
+                                             : k_attend_items_bf16<MPAD, KPAD, false>;
+    // items per block: enough that every block of the launch is resident
+    // at once (about three 2-wave blocks per CU), so no second round of
+    // blocks runs on a half-empty GPU
+    const int64_t per_head = std::max<int64_t>(1, 3 * static_cast<int64_t>(s.cus > 0 ? s.cus : 256) / s.BH);
+    const int ipb = static_cast<int>(
+        std::min<int64_t>(kAttendIpbMax, std::max<int64_t>(1, (s.attend_items + per_head - 1) / per_head)));
+    hipLaunchKernelGGL(kern, dim3((s.attend_items + ipb - 1) / ipb, s.BH), dim3(128), 0, st,
+                       static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
+                       static_cast<const uint16_t*>(V), static_cast<const uint16_t*>(ws.ql),
+                       ws.vl, idx, ws.perm, ws.offsets, ws.item_start, s.attend_tpb, s.N, s.m,
+                       s.k, s.scale * kLog2e, out, ipb);
+    return hipGetLastError();
+  }
   using E = typename T::elem;
   auto kern = (s.m == MPAD && s.k == KPAD) ? AttendKernel<T, MPAD, KPAD, true, NW>::fn
                                            : AttendKernel<T, MPAD, KPAD, false, NW>::fn;

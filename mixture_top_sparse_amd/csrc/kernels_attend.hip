@@ -521,48 +521,51 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 8
 // positions in the bucket order were read one item earlier still).
 constexpr int kAttendIpbMax = 8;  // work items per block, at most
 
-template <int MPAD, int KPAD>
-struct RawRows {  // one item's raw pairs in flight, 128 threads
-  static constexpr int RU = (KPAD / 2) * 8, RPT = (RU + 127) / 128;  // value-row units
-  static constexpr int KU = KPAD * 8, KPT = (KU + 127) / 128;        // key-row chunks
+template <int MPAD, int KPAD, int NT>
+struct RawRows {  // one item's raw pairs in flight, NT threads
+  static constexpr int RU = (KPAD / 2) * 8, RPT = (RU + NT - 1) / NT;  // value-row units
+  static constexpr int KU = KPAD * 8, KPT = (KU + NT - 1) / NT;        // key-row chunks
   u32x4 va[RPT], vb[RPT], kv[KPT];
 };
 
-template <int MPAD, int KPAD>
-__device__ __forceinline__ void raw_load(RawRows<MPAD, KPAD>& R, const int32_t* ex /* LDS */,
+template <int MPAD, int KPAD, int NT>
+__device__ __forceinline__ void raw_load(RawRows<MPAD, KPAD, NT>& R, const int32_t* ex,
                                          const uint16_t* __restrict__ K,
                                          const uint16_t* __restrict__ V, int64_t N, int k,
                                          int64_t bh) {
-  using RR = RawRows<MPAD, KPAD>;
+  using RR = RawRows<MPAD, KPAD, NT>;
   const int tid = threadIdx.x;
   const u32x4 z = {0, 0, 0, 0};
 #pragma unroll
   for (int j = 0; j < RR::RPT; ++j) {
-    const int u = tid + 128 * j, rp = u >> 3, col = u & 7;
+    const int u = tid + NT * j, rp = u >> 3, col = u & 7;
     const bool ok = u < RR::RU;
-    R.va[j] = (ok && 2 * rp < k) ? *reinterpret_cast<const u32x4*>(V + (bh * N + ex[2 * rp]) * kD + col * 8) : z;
+    R.va[j] = (ok && 2 * rp < k)
+                  ? *reinterpret_cast<const u32x4*>(V + (bh * N + clamp_index(ex[2 * rp], N)) * kD + col * 8)
+                  : z;
     R.vb[j] = (ok && 2 * rp + 1 < k)
-                  ? *reinterpret_cast<const u32x4*>(V + (bh * N + ex[2 * rp + 1]) * kD + col * 8)
+                  ? *reinterpret_cast<const u32x4*>(V + (bh * N + clamp_index(ex[2 * rp + 1], N)) * kD + col * 8)
                   : z;
   }
 #pragma unroll
   for (int j = 0; j < RR::KPT; ++j) {
-    const int c = tid + 128 * j, row = c >> 3, cc = c & 7;
+    const int c = tid + NT * j, row = c >> 3, cc = c & 7;
     R.kv[j] = (c < RR::KU && row < k)
-                  ? *reinterpret_cast<const u32x4*>(K + (bh * N + ex[row]) * kD + cc * 8)
+                  ? *reinterpret_cast<const u32x4*>(K + (bh * N + clamp_index(ex[row], N)) * kD + cc * 8)
                   : z;
   }
 }
 
-template <int MPAD, int KPAD>
-__device__ __forceinline__ void raw_store(AttendLds<BF16, MPAD, KPAD, 2>& S,
-                                          const RawRows<MPAD, KPAD>& R) {
-  using L = AttendLds<BF16, MPAD, KPAD, 2>;
-  using RR = RawRows<MPAD, KPAD>;
+template <int MPAD, int KPAD, int NW>
+__device__ __forceinline__ void raw_store(AttendLds<BF16, MPAD, KPAD, NW>& S,
+                                          const RawRows<MPAD, KPAD, 64 * NW>& R) {
+  constexpr int NT = 64 * NW;
+  using L = AttendLds<BF16, MPAD, KPAD, NW>;
+  using RR = RawRows<MPAD, KPAD, NT>;
   const int tid = threadIdx.x;
 #pragma unroll
   for (int j = 0; j < RR::RPT; ++j) {
-    const int u = tid + 128 * j;
+    const int u = tid + NT * j;
     if (u < RR::RU) {
       const int rp = u >> 3, col = u & 7;
 #pragma unroll
@@ -575,7 +578,7 @@ __device__ __forceinline__ void raw_store(AttendLds<BF16, MPAD, KPAD, 2>& S,
   }
 #pragma unroll
   for (int j = 0; j < RR::KPT; ++j) {
-    const int c = tid + 128 * j;
+    const int c = tid + NT * j;
     if (c < RR::KU)
       *reinterpret_cast<u32x4*>(S.pk + (MPAD + (c >> 3)) * L::PKST + (c & 7) * 8) = R.kv[j];
   }
@@ -583,19 +586,20 @@ __device__ __forceinline__ void raw_store(AttendLds<BF16, MPAD, KPAD, 2>& S,
 
 // the compressed pairs of head bh: Ql rows (pair-key rows 0 .. MPAD-1) and
 // Vl^T as bf16 hi + lo, every load issued before any LDS write
-template <int MPAD, int KPAD>
-__device__ __forceinline__ void stage_compressed(AttendLds<BF16, MPAD, KPAD, 2>& S,
+template <int MPAD, int KPAD, int NW>
+__device__ __forceinline__ void stage_compressed(AttendLds<BF16, MPAD, KPAD, NW>& S,
                                                  const uint16_t* __restrict__ Ql,
                                                  const float* __restrict__ vl, int m, int64_t bh) {
-  using L = AttendLds<BF16, MPAD, KPAD, 2>;
-  constexpr int LP = MPAD / 2, LU = LP * 8, LPT = (LU + 127) / 128;
-  constexpr int QU = MPAD * 8, QPT = (QU + 127) / 128;
+  constexpr int NT = 64 * NW;
+  using L = AttendLds<BF16, MPAD, KPAD, NW>;
+  constexpr int LP = MPAD / 2, LU = LP * 8, LPT = (LU + NT - 1) / NT;
+  constexpr int QU = MPAD * 8, QPT = (QU + NT - 1) / NT;
   const int tid = threadIdx.x;
   const u32x4 z = {0, 0, 0, 0};
   f32x4 lv[LPT][2][2];
 #pragma unroll
   for (int j = 0; j < LPT; ++j) {
-    const int u = tid + 128 * j, lp = u % LP, dc = u / LP;
+    const int u = tid + NT * j, lp = u % LP, dc = u / LP;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int row = 2 * lp + h;
@@ -609,12 +613,12 @@ __device__ __forceinline__ void stage_compressed(AttendLds<BF16, MPAD, KPAD, 2>&
   u32x4 qv[QPT];
 #pragma unroll
   for (int j = 0; j < QPT; ++j) {
-    const int c = tid + 128 * j, row = c >> 3;
+    const int c = tid + NT * j, row = c >> 3;
     qv[j] = (c < QU && row < m) ? *reinterpret_cast<const u32x4*>(Ql + (bh * m + row) * kD + (c & 7) * 8) : z;
   }
 #pragma unroll
   for (int j = 0; j < LPT; ++j) {
-    const int u = tid + 128 * j;
+    const int u = tid + NT * j;
     if (u < LU) {
       const int lp = u % LP, dc = u / LP;
       float la[8], lb[8];
@@ -644,7 +648,7 @@ __device__ __forceinline__ void stage_compressed(AttendLds<BF16, MPAD, KPAD, 2>&
   }
 #pragma unroll
   for (int j = 0; j < QPT; ++j) {
-    const int c = tid + 128 * j;
+    const int c = tid + NT * j;
     if (c < QU) *reinterpret_cast<u32x4*>(S.pk + (c >> 3) * L::PKST + (c & 7) * 8) = qv[j];
   }
 }
@@ -696,7 +700,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
     const int e = static_cast<int>(lane_read(static_cast<uint32_t>(my_e), j));
     sex[j][r] = (j < nit && r < k) ? static_cast<int32_t>(clamp_index(idx[(bh * m + e) * k + r], N)) : 0;
   }
-  stage_compressed<MPAD, KPAD>(S, Ql, vl, m, bh);
+  stage_compressed<MPAD, KPAD, NW>(S, Ql, vl, m, bh);
   __syncthreads();
 
   const uint16_t* Qh = Q + bh * N * kD;
@@ -711,7 +715,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
   // item's last query (every gather reads a valid row, so the ring needs no
   // branch and its waits stay exact)
   auto slot = [&](int nq, int i) { return min(16 * (w + NW * i) + c16, nq - 1); };
-  RawRows<MPAD, KPAD> R;
+  RawRows<MPAD, KPAD, 64 * NW> R;
   // pq: this item's ring rows; pqn: the next item's first rows (read one
   // item ahead); pqnn: the item after that
   int64_t pq[D], pqn[D], pqnn[D];
@@ -727,8 +731,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
     for (int d = 0; d < D; ++d) load_q(pq[d], ring[d]);
     if (nit > 1) first_rows(1, pqn);
-    raw_load<MPAD, KPAD>(R, sex[0], K, V, N, k, bh);
-    raw_store<MPAD, KPAD>(S, R);
+    raw_load<MPAD, KPAD, 64 * NW>(R, sex[0], K, V, N, k, bh);
+    raw_store<MPAD, KPAD, NW>(S, R);
   }
   __syncthreads();
   for (int j = 0; j < nit; ++j) {  // nit is block-uniform
@@ -737,7 +741,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
     if (has_next) {  // the next item's rows start loading now
 #pragma unroll
       for (int d = 0; d < D; ++d) load_q(pqn[d], ringn[d]);
-      raw_load<MPAD, KPAD>(R, sex[j + 1], K, V, N, k, bh);
+      raw_load<MPAD, KPAD, 64 * NW>(R, sex[j + 1], K, V, N, k, bh);
       if (j + 2 < nit) first_rows(j + 2, pqnn);
     }
     const int nsub = (nq + 15) / 16;
@@ -770,7 +774,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
     __syncthreads();  // every wave is done with item j's raw pairs
     if (has_next) {
-      raw_store<MPAD, KPAD>(S, R);
+      raw_store<MPAD, KPAD, NW>(S, R);
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         pq[d] = pqn[d];

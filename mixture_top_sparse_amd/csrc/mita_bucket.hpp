@@ -172,20 +172,27 @@ struct TileInfo {
 // Work item t of a head covers up to `tpb` consecutive 64-query tiles of one
 // expert; item_start[e] is the first item of expert e (exclusive scan of
 // ceil(tiles_e / tpb)).  item_start is non-decreasing, so t's expert is the
-// number of experts e < m - 1 whose successor starts at or before t: one
-// load per lane (m <= 64) and a ballot, instead of a chain of m dependent
-// loads.
+// number of experts e < m - 1 whose successor starts at or before t.  Every
+// lane loads its own expert's entries in one round (item_start[l],
+// item_start[l + 1], offsets[l]; offsets[m]); the ballot then names the
+// expert and the other values come from lane reads, so a work item costs
+// one round of dependent loads instead of a chain of them.
 __device__ __forceinline__ bool find_item(const int32_t* __restrict__ item_start,
                                           const int32_t* __restrict__ offsets, int m, int tpb,
                                           int t, TileInfo& ti) {
   const int l = lane_id();
   const int next = l < m - 1 ? item_start[l + 1] : INT32_MAX;
-  if (t >= item_start[m]) return false;
-  const int e = __popcll(ballot(next <= t));
-  const int j0 = (t - item_start[e]) * tpb;
+  const int ist = l < m ? item_start[l] : 0;
+  const int ofl = l <= m && l < 64 ? offsets[l] : 0;
+  const int total = item_start[m];
+  const int ofm = offsets[m];
+  if (t >= total) return false;
+  const int e = __popcll(ballot(next <= t));  // wave-uniform
+  const int j0 = (t - __builtin_amdgcn_readlane(ist, e)) * tpb;
+  const int oe = e + 1 < 64 ? __builtin_amdgcn_readlane(ofl, e + 1) : ofm;  // offsets[e + 1]
   ti.e = e;
-  ti.qb = offsets[e] + kAttendTile * j0;
-  ti.qe = min(ti.qb + kAttendTile * tpb, static_cast<int>(offsets[e + 1]));
+  ti.qb = __builtin_amdgcn_readlane(ofl, e) + kAttendTile * j0;
+  ti.qe = min(ti.qb + kAttendTile * tpb, oe);
   return true;
 }
 

@@ -27,7 +27,22 @@ TOL_BY_DTYPE = {"f32": 1e-5, "bf16": 5e-3}  # the parity tolerance of each input
 SINGLE_KERNEL_STAGES = {"landmark_scan": "k_scan", "route": "k_route",
                         "expert_attend": "k_attend", "single_launch": "k_small"}
 KERNEL_SOURCES = {"k_scan": "kernels_scan.hip", "k_route": "kernels_route.hip",
-                  "k_attend": "kernels_attend.hip", "k_small": "kernels_small.hip"}
+                  "k_attend": "kernels_attend.hip", "k_small": "kernels_small.hip",
+                  "k_medium": "kernels_medium.hip"}
+# bf16 heads of 257 .. MEDIUM_MAX_N tokens (one expert per query) run steps 2
+# to 4 in one launch, which the stage profiler books as landmark_scan
+MEDIUM_MAX_N = 1600
+
+
+def medium_path(w, s: int = 1) -> bool:
+    return w.dtype == "bf16" and s == 1 and 256 < w.N <= MEDIUM_MAX_N and w.m <= 64 and w.k <= 64
+
+
+def stage_kernel(stage: str, w, s: int = 1) -> str:
+    """The kernel that makes up a single-launch stage on this workload."""
+    if stage == "landmark_scan" and medium_path(w, s):
+        return "k_medium"
+    return SINGLE_KERNEL_STAGES[stage]
 # HBM bytes per launch on the 1M-token workload from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE (scaled by 2.0 and 1.0, the factors a 1 GiB copy kernel gives),
 # with the sha1 of the kernel's sources (kernel_sha) when the counters were
@@ -95,13 +110,17 @@ def threshold_tiles(w) -> int:
     return ktiles // 2 if ktiles // 2 >= 256 else ktiles
 
 
-def stage_bytes(w) -> dict[str, float]:
+def stage_bytes(w, s: int = 1) -> dict[str, float]:
     """Algorithmic HBM bytes per launch of each stage: what the stage must
     read and write at minimum (inputs once, outputs once), not what the
     implementation happens to move."""
     e = 2 if w.dtype == "bf16" else 4
     BH, N, d, m, k = w.B * w.H, w.N, w.d, w.m, w.k
     rows = min(m * k, N)
+    # the mid-length launch: K, V and Q read, experts, landmark values,
+    # routes and the bucket order written
+    scan = (BH * (3 * N * d * e + 4 * m * k + 4 * m * d + 4 * N + 4 * N) if medium_path(w, s)
+            else BH * (2 * N * d * e))
     # step 4 (bucketing: read the routes, write perm) rides in the merge
     # launch; its prefix over the routing counts in the scan launch moves
     # no per-token bytes
@@ -109,7 +128,7 @@ def stage_bytes(w) -> dict[str, float]:
         "pool": BH * (N * d * e + m * d * e),
         "landmark_threshold": BH * (threshold_tiles(w) * 64 * d * e + m * d * e),
         "route": BH * (N * d * e + 4 * N),
-        "landmark_scan": BH * (2 * N * d * e),
+        "landmark_scan": scan,
         "landmark_merge": BH * (4 * m * k + 4 * m * d + 4 * N + 4 * N),
         "expert_attend": BH * (N * d * e + 4 * N * d + 4 * N + rows * 2 * d * e),
         # the one-launch path of short sequences runs all five steps
@@ -450,7 +469,7 @@ def main() -> int:
         f"({ms_profiled:.3f} ms/step with the stage profiler on)")
 
     avg_stage = {k: v / max(calls, 1) for k, v in stage_ms.items() if not k.startswith("bw_")}
-    sbytes = stage_bytes(w)
+    sbytes = stage_bytes(w, S)
     # the dominant kernel: the slowest of the single-launch stages
     dominant = max(SINGLE_KERNEL_STAGES, key=lambda st: avg_stage.get(st, 0.0))
     ach = sbytes[dominant] / (avg_stage[dominant] * 1e-3) / 1e9
@@ -490,13 +509,13 @@ def main() -> int:
             "scope": "dominant kernel",
             "bound": "hbm",
             "kernel": dominant,
-            "symbol": SINGLE_KERNEL_STAGES[dominant],
+            "symbol": stage_kernel(dominant, w, S),
             "launch_ms": round(avg_stage[dominant], 4),
             "achieved": round(ach, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBS, 4),
-            "traffic": counted_traffic(w.name, SINGLE_KERNEL_STAGES[dominant]),
+            "traffic": counted_traffic(w.name, stage_kernel(dominant, w, S)),
             "traffic_source": "rocprofv3 FETCH_SIZE + WRITE_SIZE of this kernel from an earlier "
                               "profiler run (profiles/), carried while the kernel's sources "
                               "hash the same; null once they change",

@@ -487,7 +487,7 @@ __global__ __launch_bounds__(256) void k_bw_scatter(const int32_t* __restrict__ 
   const int seg = static_cast<int>(blockIdx.x) * 4 + w;
   if (seg < nseg)
     scatter_segment(route, counts, m, nseg, N, kAttendTile, tpb, totals, colpre, offsets, nullptr,
-                    item_start, perm, nullptr, seg, blockIdx.y, L[w]);
+                    item_start, perm, nullptr, seg, kRouteSeg, blockIdx.y, L[w]);
 }
 
 // ---------------------------------------------------------------------------

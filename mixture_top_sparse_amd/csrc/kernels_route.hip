@@ -128,11 +128,11 @@ __device__ __forceinline__ void stage_landmarks(const E* __restrict__ Ql, int m,
   }
 }
 
-// One routing block (256 threads) routes queries seg*1024 + [0, 1024) of
-// head bh in 64 groups of 16; wave w takes groups w, w + 4, w + 8, ... (so a
-// short head keeps all four waves busy), four groups of Q rows in flight,
-// and the block stores the segment's per-expert counts.
-template <class T>
+// One routing block (256 threads) routes queries seg*SEG + [0, SEG) of head
+// bh (SEG = 1024 or 256) in groups of 16; wave w takes groups w, w + 4,
+// w + 8, ... (so a short head keeps all four waves busy), four groups of Q
+// rows in flight, and the block stores the segment's per-expert counts.
+template <class T, int SEG>
 __device__ __forceinline__ void route_segment(const typename T::elem* __restrict__ Q,
                                               const typename T::elem* __restrict__ Ql,
                                               int64_t N, int m, int nseg, int seg, int64_t bh,
@@ -146,10 +146,10 @@ __device__ __forceinline__ void route_segment(const typename T::elem* __restrict
   stage_landmarks(Ql, m, bh, qls);
   const E* Qh = Q + bh * N * kD;
   // group G of this wave: queries qw + 64 G + [0, 16)
-  const int64_t qw = static_cast<int64_t>(seg) * kRouteSeg + 16 * w;
+  const int64_t qw = static_cast<int64_t>(seg) * SEG + 16 * w;
   // a ring of D groups of 16 queries in flight; the landmark operands are
   // read from LDS for every group (not pinned in registers: occupancy)
-  constexpr int D = 4, NG = 16;
+  constexpr int D = 4, NG = SEG / 64;
   // unconditional loads of a clamped row (results past N are never used):
   // branch-free, so the compiler's wait counts stay exact
   auto load_group = [&](int G, typename TR::QReg& dst) {
@@ -210,7 +210,7 @@ __device__ __forceinline__ void route_segment(const typename T::elem* __restrict
 //    pooling has just read Q front to back, so the first rows routed are
 //    the ones most recently read (measured: about 1% faster than front to
 //    back at 2^18 and 2^20 tokens; the last-level cache returns little of Q).
-template <class T, int KPL>
+template <class T, int KPL, int SEG>
 __global__ __launch_bounds__(256) void k_route(const typename T::elem* __restrict__ Q,
                                               const typename T::elem* __restrict__ Ql, int64_t N,
                                               int m, int nseg, int32_t* __restrict__ route_out,
@@ -230,8 +230,8 @@ __global__ __launch_bounds__(256) void k_route(const typename T::elem* __restric
     }
   }
   const int seg = nseg - 1 - (static_cast<int>(blockIdx.x) - (KPL > 0 ? nsel : 0));
-  route_segment<T>(Q, Ql, N, m, nseg, seg, gridDim.y - 1 - blockIdx.y, route_out, counts, cnt,
-                   qls);
+  route_segment<T, SEG>(Q, Ql, N, m, nseg, seg, gridDim.y - 1 - blockIdx.y, route_out, counts,
+                        cnt, qls);
 }
 
 // Several experts per query (s > 1, bf16): block (segment, head) covers
@@ -428,8 +428,8 @@ __global__ __launch_bounds__(256) void k_theta_groups(const uint16_t* __restrict
     theta_tile_wave<GS, SAMPLED>(ko, qls, N, m, groups, ti, bh, gmax);
 }
 
-template <class T>
-static hipError_t launch_route_t(const Shape& s, const void* Q, const Workspace& ws,
+template <class T, int SEG>
+static hipError_t launch_route_seg(const Shape& s, const void* Q, const Workspace& ws,
                                  int32_t* route_out, hipStream_t st) {
   using E = typename T::elem;
   const E* Qp = static_cast<const E*>(Q);
@@ -439,25 +439,32 @@ static hipError_t launch_route_t(const Shape& s, const void* Q, const Workspace&
   const dim3 grid(nsel + s.nseg, s.BH);
   // maxima per lane in the selection: the fewest that hold every group
   if (nsel == 0)
-    hipLaunchKernelGGL((k_route<T, 0>), grid, dim3(256), 0, st, Qp, Qlp, s.N, s.m, s.nseg,
+    hipLaunchKernelGGL((k_route<T, 0, SEG>), grid, dim3(256), 0, st, Qp, Qlp, s.N, s.m, s.nseg,
                        route_out, ws.counts, 0, nullptr, s.k, 0, s.mrows, nullptr);
   else if (s.theta_groups <= 64 * 4)
-    hipLaunchKernelGGL((k_route<T, 4>), grid, dim3(256), 0, st, Qp, Qlp, s.N, s.m, s.nseg,
+    hipLaunchKernelGGL((k_route<T, 4, SEG>), grid, dim3(256), 0, st, Qp, Qlp, s.N, s.m, s.nseg,
                        route_out, ws.counts, nsel, ws.gmax, s.k, s.theta_groups, s.mrows,
                        ws.theta);
   else if (s.theta_groups <= 64 * 16)
-    hipLaunchKernelGGL((k_route<T, 16>), grid, dim3(256), 0, st, Qp, Qlp, s.N, s.m, s.nseg,
+    hipLaunchKernelGGL((k_route<T, 16, SEG>), grid, dim3(256), 0, st, Qp, Qlp, s.N, s.m, s.nseg,
                        route_out, ws.counts, nsel, ws.gmax, s.k, s.theta_groups, s.mrows,
                        ws.theta);
   else if (s.theta_groups <= 64 * 32)
-    hipLaunchKernelGGL((k_route<T, 32>), grid, dim3(256), 0, st, Qp, Qlp, s.N, s.m, s.nseg,
+    hipLaunchKernelGGL((k_route<T, 32, SEG>), grid, dim3(256), 0, st, Qp, Qlp, s.N, s.m, s.nseg,
                        route_out, ws.counts, nsel, ws.gmax, s.k, s.theta_groups, s.mrows,
                        ws.theta);
   else
-    hipLaunchKernelGGL((k_route<T, 64>), grid, dim3(256), 0, st, Qp, Qlp, s.N, s.m, s.nseg,
+    hipLaunchKernelGGL((k_route<T, 64, SEG>), grid, dim3(256), 0, st, Qp, Qlp, s.N, s.m, s.nseg,
                        route_out, ws.counts, nsel, ws.gmax, s.k, s.theta_groups, s.mrows,
                        ws.theta);
   return hipGetLastError();
+}
+
+template <class T>
+static hipError_t launch_route_t(const Shape& s, const void* Q, const Workspace& ws,
+                                 int32_t* route_out, hipStream_t st) {
+  return s.rseg == kRouteSegSmall ? launch_route_seg<T, kRouteSegSmall>(s, Q, ws, route_out, st)
+                                  : launch_route_seg<T, kRouteSeg>(s, Q, ws, route_out, st);
 }
 
 template <int GS, bool SAMPLED>

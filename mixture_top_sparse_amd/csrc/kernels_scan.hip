@@ -796,7 +796,7 @@ __global__ __launch_bounds__(256) void k_merge(
     if (seg < ba.nseg)
       scatter_segment(ba.route, ba.counts, ba.m, ba.nseg, ba.N, ba.tile, ba.tpb, ba.totals,
                       ba.colpre, ba.offsets, ba.offsets_copy, ba.item_start, ba.perm,
-                      ba.perm_copy, seg, bh, reinterpret_cast<ScatterLds*>(smem)[w]);
+                      ba.perm_copy, seg, ba.seglen, bh, reinterpret_cast<ScatterLds*>(smem)[w]);
     return;
   }
   auto tops = reinterpret_cast<uint64_t(*)[64]>(smem);                   // [NWM][64]
@@ -917,6 +917,7 @@ static BucketArgs bucket_args(const Shape& s, const int32_t* route, const Worksp
   a.perm_copy = perm_copy;
   a.m = s.m;
   a.nseg = s.nseg;
+  a.seglen = s.rseg;
   a.tile = kAttendTile;
   a.tpb = s.attend_tpb;
   a.N = s.NA;  // the items sorted: queries, or (query, expert) assignments when s > 1

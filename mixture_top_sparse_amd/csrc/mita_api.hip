@@ -377,7 +377,14 @@ void derive(Shape& s, int cus) {
     }
   }
   s.NA = s.N * s.s;
-  s.nseg = static_cast<int>(cdiv(s.NA, kRouteSeg));
+  // routing and bucketing segments: 1024 queries, or 256 when 1024-query
+  // segments would give fewer than four routing blocks per CU (a routing
+  // block is latency-bound: at 2^16 tokens x 4 heads, one 1024-query block
+  // per CU took 15 us)
+  s.rseg = (s.s == 1 && cdiv(s.NA, kRouteSeg) * s.BH < 4 * static_cast<int64_t>(cus))
+               ? kRouteSegSmall
+               : kRouteSeg;
+  s.nseg = static_cast<int>(cdiv(s.NA, s.rseg));
   // expert attention: work items of up to 16 tiles, keeping >= 2 items per CU
   // (fewer, larger items stage each expert less often: -4% to -7% per step
   // at long1d_16k and seg_32x32 against >= 4 items per CU; 8 was slower)

@@ -86,7 +86,7 @@ __device__ __forceinline__ void scatter_segment(
     int64_t N, int tile, int tpb, const int32_t* __restrict__ totals,
     const int32_t* __restrict__ colpre, int32_t* __restrict__ offsets,
     int32_t* __restrict__ offsets_copy, int32_t* __restrict__ item_start,
-    int32_t* __restrict__ perm, int32_t* __restrict__ perm_copy, int seg, int64_t bh,
+    int32_t* __restrict__ perm, int32_t* __restrict__ perm_copy, int seg, int seglen, int64_t bh,
     ScatterLds& L) {
   const int l = lane_id();
   const int c = l < m ? totals[bh * m + l] : 0;
@@ -107,16 +107,14 @@ __device__ __forceinline__ void scatter_segment(
       if (offsets_copy) offsets_copy[bh * (m + 1) + m] = incl;
     }
   }
-  // all of the segment's routes in flight at once
+  // all of the segment's routes in flight at once (seglen <= kRouteSeg)
   constexpr int NG = kRouteSeg / 64;
-  const int64_t q0 = static_cast<int64_t>(seg) * kRouteSeg;
-  const int nq = static_cast<int>(N - q0 < kRouteSeg ? N - q0 : kRouteSeg);
+  const int64_t q0 = static_cast<int64_t>(seg) * seglen;
+  const int nq = static_cast<int>(N - q0 < seglen ? N - q0 : seglen);
   int rr[NG];
 #pragma unroll
-  for (int it = 0; it < NG; ++it) {
-    const int64_t q = q0 + 64 * it + l;
-    rr[it] = q < N ? route[bh * N + q] : 0;
-  }
+  for (int it = 0; it < NG; ++it)
+    rr[it] = 64 * it + l < nq ? route[bh * N + q0 + 64 * it + l] : 0;
   {
     const int cl = l < m ? counts[(bh * m + l) * nseg + seg] : 0;
     const int lex = wave_inclusive_sum(cl) - cl;  // local start of expert l
@@ -207,7 +205,7 @@ struct BucketArgs {
   int32_t* item_start;
   int32_t* perm;
   int32_t* perm_copy;
-  int m, nseg, tile, tpb;
+  int m, nseg, seglen, tile, tpb;
   int64_t N;
 };
 

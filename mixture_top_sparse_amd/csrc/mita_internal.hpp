@@ -15,6 +15,7 @@ constexpr int kCandCap = 8;      // candidate buffer per landmark (bf16 landmark
 constexpr int kTileKeys = 64;    // keys per landmark-scan tile
 constexpr int64_t kLastLevelCacheBytes = int64_t{256} << 20;  // MI355X Infinity Cache
 constexpr int kRouteSeg = 1024;  // queries per routing/bucketing segment
+constexpr int kRouteSegSmall = 256;  // the same for short heads (few segments)
 constexpr int kAttendTile = 64;  // queries per expert-attention tile
 constexpr int kAttendMaxTpb = 16;  // tiles per expert-attention work item, at most
 constexpr int kPoolChunk = 4096; // tokens per pooling partial sum (fewer, longer blocks stream faster)
@@ -44,6 +45,7 @@ struct Shape {
   int theta_groups = 0;// sample groups for the top-k pre-threshold (0: off)
   int theta_gs = 64;    // keys per pre-threshold group: 1, 16 or 64
   bool theta_sampled = false;  // groups are a sample of the 64-key tiles
+  int rseg = kRouteSeg;  // queries (assignments) per routing/bucketing segment: 1024, or 256
   int nseg = 0;        // routing segments per head
   int attend_tpb = 0;   // 64-query tiles per expert-attention work item
   int attend_items = 0; // upper bound of work items per head

@@ -452,6 +452,7 @@ size_t plan_workspace(const Shape& s, Workspace* ws, char* base) {
   ws->totals = reinterpret_cast<int32_t*>(take(BH * s.m * 4));
   ws->offsets = reinterpret_cast<int32_t*>(take(BH * (s.m + 1) * 4));
   ws->item_start = reinterpret_cast<int32_t*>(take(BH * (s.m + 1) * 4));
+  ws->item_order = reinterpret_cast<int32_t*>(take(BH * (2 * s.m + 1) * 4));
   ws->perm = reinterpret_cast<int32_t*>(take(BH * s.NA * 4));
   if (s.s > 1) {
     ws->pacc = reinterpret_cast<float*>(take(BH * s.NA * kD * sizeof(float)));

@@ -20,6 +20,10 @@
 //                   first landmark-merge launch, four segments per block.
 // Both depend only on the routes and the counts; the expert attention that
 // reads their results is the next launch after the merge.
+//
+// Work items: an expert's queries in runs of up to tpb 64-query tiles
+// (item_start[e] = its first item).  write_item_order gives the order in
+// which the long-item attention dispatches them.
 #pragma once
 
 #include "mita_device.hpp"
@@ -160,6 +164,34 @@ __device__ __forceinline__ void scatter_segment(
   }
 }
 
+// One wave: the long-item attention's dispatch order for head bh (item_order,
+// [2m+1] per head): each expert's full items (tpb tiles) in expert order,
+// then each expert's last, partly filled item, largest first (ties: lower
+// expert), so that the short items fill the tail of the launch instead of a
+// full item starting there (at 2^16 tokens x 4 heads the attention went 41
+// -> 34 us).  Stored as the exclusive prefix of the experts' full items
+// ([m+1]) and the experts by the size of their last item ([m]).  Needs only
+// the experts' totals.
+__device__ __forceinline__ void write_item_order(const int32_t* __restrict__ totals, int m,
+                                                 int tile, int tpb, int64_t bh,
+                                                 int32_t* __restrict__ item_order) {
+  const int l = lane_id();
+  const int c = l < m ? totals[bh * m + l] : 0;
+  const int items = ((c + tile - 1) / tile + tpb - 1) / tpb;
+  const int full = items > 0 ? items - 1 : 0;
+  const int last = items > 0 ? c - full * tpb * tile : 0;  // queries in the last item
+  const int full_incl = wave_inclusive_sum(full);
+  int rank = 0;
+  for (int j = 0; j < m; ++j) {
+    const int lj = __builtin_amdgcn_readlane(last, j);
+    rank += (lj > last || (lj == last && j < l)) ? 1 : 0;
+  }
+  int32_t* F = item_order + bh * (2 * m + 1);
+  if (l < m) F[l] = full_incl - full;
+  if (l == m - 1) F[m] = full_incl;
+  if (items > 0) F[m + 1 + rank] = l;
+}
+
 // A work item of the expert-grouped attention kernels (forward and backward).
 struct TileInfo {
   int e;      // expert
@@ -194,6 +226,39 @@ __device__ __forceinline__ bool find_item(const int32_t* __restrict__ item_start
   return true;
 }
 
+// Work item t in the long-item dispatch order (item_order above, the head's
+// slice): t < F (= the full items) is full item t - fs[e] of expert e, the
+// number of experts whose successor's full items start at or before t; past
+// them, t names the last item of expert last[t - F].  One round of loads
+// (per lane: fs[l + 1], fs[l], offsets[l]) and one more for a last item.
+__device__ __forceinline__ void find_item_ordered(const int32_t* __restrict__ order,
+                                                  const int32_t* __restrict__ offsets, int m,
+                                                  int tpb, int t, TileInfo& ti) {
+  const int l = lane_id();
+  const int next = l < m - 1 ? order[l + 1] : INT32_MAX;
+  const int fsl = l <= m && l < 64 ? order[l] : 0;
+  const int ofl = l <= m && l < 64 ? offsets[l] : 0;
+  const int nfull = order[m];
+  const int ofm = offsets[m];
+  int e, j0;
+  bool partial;
+  if (t < nfull) {
+    e = __popcll(ballot(next <= t));  // wave-uniform
+    j0 = (t - __builtin_amdgcn_readlane(fsl, e)) * tpb;
+    partial = false;
+  } else {
+    e = __builtin_amdgcn_readfirstlane(order[m + 1 + (t - nfull)]);
+    const int full = (e + 1 < 64 ? __builtin_amdgcn_readlane(fsl, e + 1) : nfull) -
+                     __builtin_amdgcn_readlane(fsl, e);
+    j0 = full * tpb;
+    partial = true;
+  }
+  const int oe = e + 1 < 64 ? __builtin_amdgcn_readlane(ofl, e + 1) : ofm;  // offsets[e + 1]
+  ti.e = e;
+  ti.qb = __builtin_amdgcn_readlane(ofl, e) + kAttendTile * j0;
+  ti.qe = partial ? oe : min(ti.qb + kAttendTile * tpb, oe);
+}
+
 // Arguments of the bucket bodies, passed through the scan and merge launches.
 struct BucketArgs {
   const int32_t* route;
@@ -203,6 +268,7 @@ struct BucketArgs {
   int32_t* offsets;
   int32_t* offsets_copy;
   int32_t* item_start;
+  int32_t* item_order;
   int32_t* perm;
   int32_t* perm_copy;
   int m, nseg, seglen, tile, tpb;

@@ -77,6 +77,9 @@ struct Workspace {
   int32_t* totals = nullptr;     // [BH][m] routed queries per expert
   int32_t* offsets = nullptr;    // [BH][m+1]
   int32_t* item_start = nullptr; // [BH][m+1] first attention work item of each expert
+  int32_t* item_order = nullptr; // [BH][2m+1] long-item dispatch order: each expert's first
+                                 //   full item ([m+1], exclusive prefix), then the experts
+                                 //   by the size of their last item ([m], largest first)
   int32_t* perm = nullptr;       // [BH][NA] queries (s > 1: assignments q*s + j) by expert
   float* pacc = nullptr;         // s > 1: [BH][NA][64] unnormalised P.V per assignment
   float* pstat = nullptr;        // s > 1: [BH][NA][2] (maximum logit in log2 units, weight sum)

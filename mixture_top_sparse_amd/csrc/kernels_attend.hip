@@ -26,7 +26,6 @@
 namespace mita {
 
 constexpr int kAttendWaves = 8;       // bf16 expert attention: waves per block
-constexpr int kAttendShortItems = 256;  // below this many queries per expert (mean): 2 waves
 
 template <class T, int MPAD, int KPAD, int NW = kAttendWaves>
 struct AttendLds;
@@ -531,13 +530,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 8
 // When experts hold few queries (the image-shaped workloads: 20-35 per
 // expert), a block that stages one expert spends most of its life waiting on
 // a chain of dependent loads: the work-item table, the expert's key list,
-// the key and value rows it names.  Here each 2-wave block takes
-// kAttendIpb consecutive work items of one head: the compressed pairs (Ql
-// rows, Vl as hi + lo) are staged once, the items' key lists are read once,
-// and while the block computes one item the next item's key and value rows
-// and its first query rows are already loading into registers (their
-// positions in the bucket order were read one item earlier still).
-constexpr int kAttendIpbMax = 8;  // work items per block, at most
+// the key and value rows it names.  Here each 2-wave block takes up to ipb
+// work items of one head (consecutive ones, or, with at most 64 items per
+// head, those that write_item_blocks assigned it by size): the compressed
+// pairs (Ql rows, Vl as hi + lo) are staged once, the items' key lists are
+// read once, and while the block computes one item the next item's key and
+// value rows and its first query rows are already loading into registers
+// (their positions in the bucket order were read one item earlier still).
 
 template <int MPAD, int KPAD, int NT>
 struct RawRows {  // one item's raw pairs in flight, NT threads
@@ -677,8 +676,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ Ql, const float* __restrict__ vl, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ item_start, int tpb, int64_t N, int m, int k, float c2,
-    float* __restrict__ out, int ipb) {
+    const int32_t* __restrict__ item_start, const int32_t* __restrict__ item_blocks, int tpb,
+    int64_t N, int m, int k, float c2, float* __restrict__ out, int ipb) {
   constexpr int NW = 2, D = 2;  // waves; query rows in flight per wave (sub-tiles)
   using L = AttendLds<BF16, MPAD, KPAD, NW>;
   __shared__ L S;
@@ -691,9 +690,17 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
   // work items t0 .. t0 + nit - 1 (item t: expert e = the number of experts
   // e' < m - 1 whose successor starts at or before t; item_start is
   // non-decreasing); lane j keeps item j's expert and query range
-  const int nitems = IS[m];
-  if (t0 >= nitems) return;  // whole block
-  const int nit = min(ipb, nitems - t0);
+  // the block's items: ipb consecutive ones, or its slots of item_blocks
+  // (items assigned to blocks by size, empty slots last)
+  int tl = 0, nit = 0;
+  if (item_blocks != nullptr) {
+    tl = l < ipb ? item_blocks[(bh * gridDim.x + blockIdx.x) * ipb + l] : -1;
+    nit = __popcll(ballot(tl >= 0));
+  } else {
+    tl = t0 + l;
+    nit = min(ipb, IS[m] - t0);
+  }
+  if (nit <= 0) return;  // whole block
   const int nextst = l < m - 1 ? IS[l + 1] : INT32_MAX;
   const int ist = l < m ? IS[l] : 0;
   const int ofl = l <= m && l < 64 ? OF[l] : 0;
@@ -701,7 +708,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void k
   int my_e = 0, my_qb = 0, my_qe = 0;
 #pragma unroll
   for (int j = 0; j < kAttendIpbMax; ++j) {
-    const int t = t0 + j;
+    const int t = __builtin_amdgcn_readlane(tl, j);
     const int e = __popcll(ballot(nextst <= t));  // wave-uniform
     const int qb = __builtin_amdgcn_readlane(ofl, e) +
                    kAttendTile * tpb * (t - __builtin_amdgcn_readlane(ist, e));
@@ -1016,17 +1023,15 @@ static hipError_t launch_attend_w(const Shape& s, const void* Q, const void* K, 
   if constexpr (std::is_same<T, BF16>::value && NW == 2) {
     auto kern = (s.m == MPAD && s.k == KPAD) ? k_attend_items_bf16<MPAD, KPAD, true>
                                              : k_attend_items_bf16<MPAD, KPAD, false>;
-    // items per block: enough that every block of the launch is resident
-    // at once (about three 2-wave blocks per CU), so no second round of
-    // blocks runs on a half-empty GPU
-    const int64_t per_head = std::max<int64_t>(1, 3 * static_cast<int64_t>(s.cus > 0 ? s.cus : 256) / s.BH);
-    const int ipb = static_cast<int>(
-        std::min<int64_t>(kAttendIpbMax, std::max<int64_t>(1, (s.attend_items + per_head - 1) / per_head)));
-    hipLaunchKernelGGL(kern, dim3((s.attend_items + ipb - 1) / ipb, s.BH), dim3(128), 0, st,
+    // ipb items per block and nbx blocks per head, chosen when the call is
+    // planned so that every block of the launch is resident at once (about
+    // three 2-wave blocks per CU): no second round of blocks runs on a
+    // half-empty GPU
+    hipLaunchKernelGGL(kern, dim3(s.attend_nbx, s.BH), dim3(128), 0, st,
                        static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
                        static_cast<const uint16_t*>(V), static_cast<const uint16_t*>(ws.ql),
-                       ws.vl, idx, ws.perm, ws.offsets, ws.item_start, s.attend_tpb, s.N, s.m,
-                       s.k, s.scale * kLog2e, out, ipb);
+                       ws.vl, idx, ws.perm, ws.offsets, ws.item_start, ws.item_blocks,
+                       s.attend_tpb, s.N, s.m, s.k, s.scale * kLog2e, out, s.attend_ipb);
     return hipGetLastError();
   }
   using E = typename T::elem;

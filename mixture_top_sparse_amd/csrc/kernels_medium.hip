@@ -91,7 +91,7 @@ struct MedRouteLds {
   uint8_t route[kMediumMaxN];
   int cnt[kMaxM];
   int base[kMaxM];
-  int wcnt[8][kMaxM];
+  alignas(16) int wcnt[8][kMaxM];  // (also the block assignment's scratch, read as int4)
 };
 
 template <int NTMAX>
@@ -658,7 +658,8 @@ __device__ __forceinline__ void med_route_bucket(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Ql, int N, int m, int64_t bh,
     int tpb, int32_t* __restrict__ route_out, int32_t* __restrict__ offsets,
     int32_t* __restrict__ item_start, int32_t* __restrict__ perm, int32_t* __restrict__ off_copy,
-    int32_t* __restrict__ perm_copy, MedRouteLds& S) {
+    int32_t* __restrict__ perm_copy, int32_t* __restrict__ item_blocks, int ipb, int nbx,
+    MedRouteLds& S) {
   const int tid = threadIdx.x, l = lane_id(), g = l >> 4, c16 = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(wave_id());
   const uint16_t* Qh = Q + bh * N * kD;
@@ -773,6 +774,11 @@ __device__ __forceinline__ void med_route_bucket(
     }
     __syncthreads();  // bases read and counters summed before the next chunk
   }
+  // the short-item attention's block assignment, after the scatter (the
+  // scatter's waves need not wait for it)
+  if (w == 0 && item_blocks != nullptr)  // (the counters' LDS is free now)
+    write_item_blocks(l < m ? S.cnt[l] : 0, m, tpb, ipb, nbx, bh, item_blocks,
+                      &S.wcnt[0][0]);
 }
 
 // grid: nsel select blocks, then BH route blocks.  Select block b: XCD
@@ -785,7 +791,8 @@ __global__ __launch_bounds__(kMedThreads) void k_medium_bf16(
     float c2, int BH, int nblk, int nsel, int tpb, float* __restrict__ vl,
     float* __restrict__ vl_copy, int32_t* __restrict__ idx_out, int32_t* __restrict__ route_out,
     int32_t* __restrict__ offsets, int32_t* __restrict__ item_start, int32_t* __restrict__ perm,
-    int32_t* __restrict__ off_copy, int32_t* __restrict__ perm_copy) {
+    int32_t* __restrict__ off_copy, int32_t* __restrict__ perm_copy,
+    int32_t* __restrict__ item_blocks, int ipb, int nbx) {
   __shared__ MedLds<NTMAX> S;
   const int b = static_cast<int>(blockIdx.x);
   if (b < nsel) {
@@ -795,7 +802,7 @@ __global__ __launch_bounds__(kMedThreads) void k_medium_bf16(
     med_select<NTMAX>(K, V, Ql, N, m, k, c2, bh, tb, vl, vl_copy, idx_out, S.sel);
   } else {
     med_route_bucket(Q, Ql, N, m, b - nsel, tpb, route_out, offsets, item_start, perm, off_copy,
-                     perm_copy, S.rt);
+                     perm_copy, item_blocks, ipb, nbx, S.rt);
   }
 }
 
@@ -813,7 +820,7 @@ hipError_t launch_medium_t(const Shape& s, const void* Q, const void* K, const v
                      static_cast<const uint16_t*>(ws.ql), static_cast<int>(s.N), s.m, s.k,
                      s.scale * kLog2e, static_cast<int>(s.BH), nblk, nsel, s.attend_tpb, ws.vl,
                      vl_copy, idx_out, route_out, ws.offsets, ws.item_start, ws.perm, off_copy,
-                     perm_copy);
+                     perm_copy, ws.item_blocks, s.attend_ipb, s.attend_nbx);
   return hipGetLastError();
 }
 

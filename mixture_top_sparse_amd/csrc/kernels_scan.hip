@@ -775,8 +775,9 @@ __global__ __launch_bounds__(256) void k_theta_fine(const typename T::elem* __re
 // of block x sorts segment 4x + w (mita_bucket.hpp).  The merge blocks
 // follow: block nsb + j is landmark block j % mx of part j / mx (P parts).
 // The final pass has one trailing block per head that writes the expert
-// attention's dispatch order (write_item_order: it needs only the experts'
-// totals, which the scan launch's prefix blocks left).
+// attention's dispatch order (write_item_order) and its short-item blocks'
+// items (write_item_blocks): both need only the experts' totals, which the
+// scan launch's prefix blocks left.
 template <bool FINAL, int NWM>
 __global__ __launch_bounds__(256) void k_merge(
     const uint64_t* __restrict__ part_keys, const int32_t* __restrict__ part_cnt,
@@ -794,8 +795,13 @@ __global__ __launch_bounds__(256) void k_merge(
   const int l = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(wave_id());
   const int64_t bh = blockIdx.y;
-  if (FINAL && ba.item_order != nullptr && blockIdx.x == gridDim.x - 1) {  // trailing block
-    if (wave_id() == 0) write_item_order(ba.totals, ba.m, ba.tile, ba.tpb, bh, ba.item_order);
+  if (FINAL && (ba.item_order != nullptr || ba.item_blocks != nullptr) &&
+      blockIdx.x == gridDim.x - 1) {  // trailing block
+    if (w == 0 && ba.item_order != nullptr)
+      write_item_order(ba.totals, ba.m, ba.tile, ba.tpb, bh, ba.item_order);
+    if (w == 1 && ba.item_blocks != nullptr)
+      write_item_blocks(l < ba.m ? ba.totals[bh * ba.m + l] : 0, ba.m, ba.tpb, ba.ipb, ba.nbx, bh,
+                        ba.item_blocks, reinterpret_cast<int*>(smem));
     return;
   }
   if (static_cast<int>(blockIdx.x) < nsb) {  // whole block: step 4's scatter
@@ -921,6 +927,9 @@ static BucketArgs bucket_args(const Shape& s, const int32_t* route, const Worksp
   a.offsets_copy = offsets_copy;
   a.item_start = ws.item_start;
   a.item_order = ws.item_order;
+  a.item_blocks = ws.item_blocks;
+  a.ipb = s.attend_ipb;
+  a.nbx = s.attend_nbx;
   a.perm = ws.perm;
   a.perm_copy = perm_copy;
   a.m = s.m;
@@ -1029,7 +1038,7 @@ static void merge_pass(const Shape& s, const uint64_t* keys, const int32_t* cnt,
                        hipStream_t st) {
   const int mx = NWM == 4 ? s.m : (s.m + 3) / 4;
   // the final pass has one more block per head: the attention's dispatch order
-  const int order = FINAL && ba.item_order != nullptr ? 1 : 0;
+  const int order = FINAL && (ba.item_order != nullptr || ba.item_blocks != nullptr) ? 1 : 0;
   hipLaunchKernelGGL((k_merge<FINAL, NWM>), dim3(nsb + mx * P + order, s.BH), dim3(256), 0, st, keys, cnt,
                      stats, acc, s.m, s.k, s.mrows, splits, idx_out, vl, vl_copy, out_keys,
                      out_cnt, out_stats, out_acc, nsb, mx, P, ba);

@@ -396,6 +396,18 @@ void derive(Shape& s, int cus) {
   // the t_e add up to at most tiles + m - 1, and each ceil adds at most
   // (tpb - 1) / tpb, so tiles / tpb + m bounds them
   s.attend_items = static_cast<int>(cdiv(tiles, tpb) + s.m);
+  // short items (bf16, s = 1, under 256 queries per expert on average):
+  // 2-wave blocks of ipb consecutive work items, ipb chosen so that every
+  // block of the launch is resident at once (about three per CU); with at
+  // most 64 items per head they are assigned to the blocks by size instead
+  s.attend_short = s.dtype == MITA_BF16 && s.s == 1 && s.N < kAttendShortItems * static_cast<int64_t>(s.m);
+  {
+    const int64_t per_head = std::max<int64_t>(1, 3 * static_cast<int64_t>(cus) / s.BH);
+    s.attend_ipb = static_cast<int>(std::min<int64_t>(
+        kAttendIpbMax, std::max<int64_t>(1, cdiv(s.attend_items, per_head))));
+    s.attend_nbx = static_cast<int>(cdiv(s.attend_items, s.attend_ipb));
+  }
+  s.attend_balanced = s.attend_short && s.attend_items <= 64;
   s.small = small_path_fits(s);
   s.medium = !s.small && medium_path_fits(s);
   if (s.medium) {  // exact selection inside the one launch: no pre-threshold
@@ -432,6 +444,9 @@ size_t plan_workspace(const Shape& s, Workspace* ws, char* base) {
     ws->offsets = reinterpret_cast<int32_t*>(take(BH * (s.m + 1) * 4));
     ws->item_start = reinterpret_cast<int32_t*>(take(BH * (s.m + 1) * 4));
     ws->perm = reinterpret_cast<int32_t*>(take(BH * s.NA * 4));
+    if (s.attend_balanced)
+      ws->item_blocks =
+          reinterpret_cast<int32_t*>(take(BH * s.attend_nbx * s.attend_ipb * 4));
     return off;
   }
   const size_t parts = BH * s.scan_splits * s.mrows;
@@ -453,6 +468,8 @@ size_t plan_workspace(const Shape& s, Workspace* ws, char* base) {
   ws->offsets = reinterpret_cast<int32_t*>(take(BH * (s.m + 1) * 4));
   ws->item_start = reinterpret_cast<int32_t*>(take(BH * (s.m + 1) * 4));
   ws->item_order = reinterpret_cast<int32_t*>(take(BH * (2 * s.m + 1) * 4));
+  if (s.attend_balanced)
+    ws->item_blocks = reinterpret_cast<int32_t*>(take(BH * s.attend_nbx * s.attend_ipb * 4));
   ws->perm = reinterpret_cast<int32_t*>(take(BH * s.NA * 4));
   if (s.s > 1) {
     ws->pacc = reinterpret_cast<float*>(take(BH * s.NA * kD * sizeof(float)));

@@ -192,6 +192,57 @@ __device__ __forceinline__ void write_item_order(const int32_t* __restrict__ tot
   if (items > 0) F[m + 1 + rank] = l;
 }
 
+// One wave: head bh's work items assigned to the short-item attention's nbx
+// blocks of ipb slots (table [nbx * ipb] per head, -1 = empty slot).  A
+// block of consecutive items costs what its items add up to, and at the
+// segmentation shapes (20-70 queries per expert) the costliest block held
+// twice the median's 16-query sub-tiles.  Here the items are ranked by cost
+// (16-query sub-tiles plus two for the item's own staging, largest first)
+// and dealt out in a snake: rank r goes to slot r / nbx of block r % nbx,
+// or of block nbx - 1 - r % nbx on odd rounds.  Every lane places its own
+// item; no block gets more than ceil(total / nbx) <= ipb items.  c: this
+// lane's expert total (lanes < m); at most 64 items per head (one per
+// lane).  lds: 128 ints of this wave's own (the comparisons read it as
+// broadcasts, four values per read).
+__device__ __forceinline__ void write_item_blocks(int c, int m, int tpb, int ipb, int nbx,
+                                                  int64_t bh, int32_t* __restrict__ table,
+                                                  int* lds) {
+  const int l = lane_id();
+  const int items = l < m ? ((c + kAttendTile - 1) / kAttendTile + tpb - 1) / tpb : 0;
+  const int incl = wave_inclusive_sum(items);
+  const int total = __builtin_amdgcn_readlane(incl, 63);
+  int32_t* T = table + bh * (nbx * ipb);
+  for (int i = l; i < nbx * ipb; i += 64) T[i] = -1;
+  // lane t: work item t's expert (the experts whose items end at or before
+  // t) and its queries
+  lds[l] = incl;
+  int e = 0;
+#pragma unroll
+  for (int j = 0; j < 64; j += 4) {
+    const int4 v = *reinterpret_cast<const int4*>(lds + j);
+    e += (j < m && v.x <= l) + (j + 1 < m && v.y <= l) + (j + 2 < m && v.z <= l) +
+         (j + 3 < m && v.w <= l);
+  }
+  const int es = e < 64 ? e : 63;
+  const int ce = static_cast<int>(lane_read(static_cast<uint32_t>(c), es));
+  const int fe = static_cast<int>(lane_read(static_cast<uint32_t>(incl - items), es));
+  const int q = l < total ? min(ce - (l - fe) * tpb * kAttendTile, tpb * kAttendTile) : 0;
+  // sort key: cost (sub-tiles plus two), then the lower item first
+  const int key = l < total ? (((q + 15) / 16 + 2) << 6) | (63 - l) : -1;
+  lds[64 + l] = key;
+  int rank = 0;
+#pragma unroll
+  for (int j = 0; j < 64; j += 4) {
+    const int4 v = *reinterpret_cast<const int4*>(lds + 64 + j);
+    rank += (v.x > key) + (v.y > key) + (v.z > key) + (v.w > key);
+  }
+  if (l < total) {
+    const int round = rank / nbx, pos = rank % nbx;
+    const int blk = (round & 1) ? nbx - 1 - pos : pos;
+    if (round < ipb) T[blk * ipb + round] = l;  // (round < ipb: total <= nbx * ipb)
+  }
+}
+
 // A work item of the expert-grouped attention kernels (forward and backward).
 struct TileInfo {
   int e;      // expert
@@ -269,6 +320,8 @@ struct BucketArgs {
   int32_t* offsets_copy;
   int32_t* item_start;
   int32_t* item_order;
+  int32_t* item_blocks;  // the short-item attention's table (or nullptr)
+  int ipb, nbx;
   int32_t* perm;
   int32_t* perm_copy;
   int m, nseg, seglen, tile, tpb;

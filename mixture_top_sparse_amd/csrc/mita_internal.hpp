@@ -17,7 +17,9 @@ constexpr int64_t kLastLevelCacheBytes = int64_t{256} << 20;  // MI355X Infinity
 constexpr int kRouteSeg = 1024;  // queries per routing/bucketing segment
 constexpr int kRouteSegSmall = 256;  // the same for short heads (few segments)
 constexpr int kAttendTile = 64;  // queries per expert-attention tile
-constexpr int kAttendMaxTpb = 16;  // tiles per expert-attention work item, at most
+constexpr int kAttendMaxTpb = 16;
+constexpr int kAttendShortItems = 256;  // below this many queries per expert (mean): 2-wave blocks
+constexpr int kAttendIpbMax = 8;        // 2-wave blocks: work items per block, at most  // tiles per expert-attention work item, at most
 constexpr int kPoolChunk = 4096; // tokens per pooling partial sum (fewer, longer blocks stream faster)
 constexpr int kPoolDirectMax = 128;  // windows up to this many tokens: one-launch pooling
 constexpr int kThetaTilesPerBlock = 1;  // sample tiles per top-k pre-threshold block
@@ -49,6 +51,10 @@ struct Shape {
   int nseg = 0;        // routing segments per head
   int attend_tpb = 0;   // 64-query tiles per expert-attention work item
   int attend_items = 0; // upper bound of work items per head
+  bool attend_short = false;    // bf16 with few queries per expert: the 2-wave items kernel
+  int attend_ipb = 1;           // its work items per block
+  int attend_nbx = 1;           // its blocks per head
+  bool attend_balanced = false; // its items assigned to blocks by size (at most 64 per head)
   bool small = false;   // one launch, one workgroup per head, no work space
   bool medium = false;  // scan, selection, routing and bucketing in one launch
   int s = 1;            // experts per query
@@ -77,6 +83,8 @@ struct Workspace {
   int32_t* totals = nullptr;     // [BH][m] routed queries per expert
   int32_t* offsets = nullptr;    // [BH][m+1]
   int32_t* item_start = nullptr; // [BH][m+1] first attention work item of each expert
+  int32_t* item_blocks = nullptr; // [BH][attend_nbx * attend_ipb] short-item blocks' items (-1:
+                                  //   empty slot), when attend_balanced
   int32_t* item_order = nullptr; // [BH][2m+1] long-item dispatch order: each expert's first
                                  //   full item ([m+1], exclusive prefix), then the experts
                                  //   by the size of their last item ([m], largest first)

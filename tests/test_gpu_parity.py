@@ -128,6 +128,10 @@ EDGES = {
     "grid_12x20": _edge("grid_12x20", 2, 1, 240, (12, 20, 3, 5), 33, values="mixture", centres=16),
     "f32_ragged": _edge("f32_ragged", 1, 3, 777, (1, 777, 1, 40), 50, dtype="f32"),
     "m17_k63": _edge("m17_k63", 1, 2, 5000, (1, 5000, 1, 17), 63, values="mixture", centres=32),
+    # the multi-launch path with short work items (64 queries per expert on
+    # average) assigned to the attention's blocks by size
+    "short_items_2048": _edge("short_items_2048", 2, 2, 2048, (1, 2048, 1, 32), 24,
+                              values="mixture", centres=16),
 }
 
 

@@ -137,10 +137,13 @@ __global__ __launch_bounds__(64) void k_pool_final(const double* __restrict__ pa
 // Small windows (at most kPoolDirectMax tokens, the 2D image grids): grid
 // (ceil(m / 8), BH), 256 threads; 32 lanes per landmark = 8 groups of 8
 // columns x 4 token phases.  Each lane sums every fourth token of its
-// landmark's window for its 8 columns in fp64 (loads unrolled by 4), the
-// four phases combine by lane swaps, and phase 0 divides once and rounds:
-// one launch instead of a partial-sum and a final launch.  The fp64 sums are
-// exact for bf16 inputs, so the order of the additions does not matter.
+// landmark's window for its 8 columns in fp64, the four phases combine by
+// lane swaps, and phase 0 divides once and rounds: one launch instead of a
+// partial-sum and a final launch.  A lane's loads go out 16 at a time (rows
+// past the window read the window's first token and are not added), and
+// the tokens' window positions are stepped, not divided out per token
+// (pooling at the 40x40 grid: 15.0 -> 13.7 us).  The fp64 sums are exact
+// for bf16 inputs, so the order of the additions does not matter.
 template <class T>
 __global__ __launch_bounds__(256) void k_pool_direct(const typename T::elem* __restrict__ Q,
                                                     int64_t N, int gh, int gw, int mh, int mw,
@@ -155,22 +158,32 @@ __global__ __launch_bounds__(256) void k_pool_direct(const typename T::elem* __r
   const int64_t wc = c1 - c0, W = (r1 - r0) * wc;
   const typename T::elem* Qh = Q + bh * N * kD + col * 8;
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  auto tok = [&](int64_t t) { return (r0 + t / wc) * gw + (c0 + t % wc); };
-  int64_t t = ph;
-  for (; t + 12 < W; t += 16) {  // four tokens of this phase in flight
-    float v[4][8];
+  // the phase's tokens ph, ph + 4, ... as (row, column) in the window,
+  // stepped without a division per token (wc <= W <= kPoolDirectMax)
+  const int wc32 = static_cast<int>(wc), W32 = static_cast<int>(W);
+  const int dr = 4 / wc32, dc = 4 % wc32;
+  int rr = ph / wc32, cc = ph % wc32;
+  constexpr int U = 16;  // tokens of this phase in flight
+  for (int t0 = ph; t0 < W32; t0 += 4 * U) {
+    float v[U][8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) load8(Qh + tok(t + 4 * j) * kD, v[j]);
+    for (int j = 0; j < U; ++j) {
+      // past the window: any of its rows (the window's first), not added
+      const int64_t tk = t0 + 4 * j < W32 ? (r0 + rr) * gw + (c0 + cc) : r0 * gw + c0;
+      load8(Qh + tk * kD, v[j]);
+      rr += dr;
+      cc += dc;
+      if (cc >= wc32) {
+        cc -= wc32;
+        ++rr;
+      }
+    }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < U; ++j)
+      if (t0 + 4 * j < W32) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += static_cast<double>(v[j][e]);
-  }
-  for (; t < W; t += 4) {
-    float v[8];
-    load8(Qh + tok(t) * kD, v);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += static_cast<double>(v[e]);
+        for (int e = 0; e < 8; ++e) acc[e] += static_cast<double>(v[j][e]);
+      }
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {

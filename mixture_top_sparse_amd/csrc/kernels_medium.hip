@@ -22,7 +22,7 @@
 //             LDS at the end.
 //     select  expert i = the k best keys, ties at the k-th score to the lower
 //             keys (the reading the oracle follows).  theta = the k-th
-//             largest 16-key slice maximum is a lower bound of the k-th
+//             largest 8-key group maximum is a lower bound of the k-th
 //             score; the keys at or above it (about k to 2k) are collected
 //             in LDS, and a bisection over their 32-bit order bits gives the
 //             k-th score T.  The keys above T and the lowest-index ties
@@ -67,7 +67,7 @@ template <int NTMAX>
 struct MedSelectLds {
   alignas(16) uint8_t vslot[8][2][2048];  // per wave: two 16-row V slices (tile_dma layout)
   union {  // used one after the other
-    uint32_t smax[32][NTMAX * 4 + 1];  // per landmark slot: order bits of each 16-key slice's
+    uint32_t smax[32][NTMAX * 8 + 1];  // per landmark slot: order bits of each 8-key group's
                                        // maximum (rows padded against bank conflicts)
     uint64_t cand[32][kMedCap + 1];  // candidate keys: order bits << 32 | ~key index (rows
                                      // padded: the 16 lanes of a store hit 16 banks)
@@ -269,13 +269,12 @@ __device__ __forceinline__ void med_select(const uint16_t* __restrict__ K,
         o[r] = valid[r] ? score_order_bits(a[r]) : 0u;
         tm = valid[r] ? fmax_nc(tm, a[r]) : tm;
       }
-      // the slice's largest score for this lane's landmark (order bits)
+      // the largest score of each 8-key half of the slice for this lane's
+      // landmark (order bits): keys 4g..4g+3 of lanes g = 0, 1 and of 2, 3
       uint32_t sm = max(max(o[0], o[1]), max(o[2], o[3]));
       auto r16 = __builtin_amdgcn_permlane16_swap(sm, sm, false, false);
       sm = max(r16[0], r16[1]);
-      auto r32 = __builtin_amdgcn_permlane32_swap(sm, sm, false, false);
-      sm = max(r32[0], r32[1]);
-      if (g == 0) S.u.smax[li][4 * t + kq] = sm;
+      if ((g & 1) == 0) S.u.smax[li][8 * t + 2 * kq + (g >> 1)] = sm;
       // online softmax
       tm = xor_max(tm, 16);
       tm = xor_max(tm, 32);
@@ -330,10 +329,12 @@ __device__ __forceinline__ void med_select(const uint16_t* __restrict__ K,
   }
 
   // ---- selection ------------------------------------------------------------
-  // Candidates: theta = the k-th largest of the landmark's 16-key slice
+  // Candidates: theta = the k-th largest of the landmark's 8-key group
   // maxima (k distinct keys reach it, so the k-th best key does too; 0 when
-  // there are fewer than k slices); the keys at or above theta (about k to
-  // 2k of them for scores without many ties) go to a list in LDS.  The
+  // there are fewer than k groups); the keys at or above theta (about k to
+  // 2k of them for scores without many ties) go to a list in LDS.  With
+  // 16-key groups the bound was loose at 1024 keys (the 49th of 64 maxima),
+  // lists overflowed, and the exact bisection below ran for 18 us.  The
   // expert is then the first k of the list by (score, lower key).  A list
   // longer than kMedCap (heavy ties) sends the whole block to the exact
   // bisection over every key below instead.  Both searches handle a wave's
@@ -343,13 +344,13 @@ __device__ __forceinline__ void med_select(const uint16_t* __restrict__ K,
   const bool lok = 32 * tb + ls < m;
   lds_barrier();  // slice maxima
   {
-    constexpr int QN = (NTMAX * 4 + 15) / 16;  // slice maxima per lane
-    const int ns = 4 * NT;
+    constexpr int QN = (NTMAX * 8 + 15) / 16;  // group maxima per lane
+    const int ns = 8 * NT;
     uint32_t v[QN];
 #pragma unroll
     for (int q = 0; q < QN; ++q) v[q] = (lok && p + 16 * q < ns) ? S.u.smax[ls][p + 16 * q] : 0u;
     uint32_t th = 0;
-    bool dn = !lok || ns < k;  // fewer slices than k: every key is a candidate
+    bool dn = !lok || ns < k;  // fewer groups than k: every key is a candidate
     for (int bit = 31; bit >= 0; --bit) {
       if (ballot(!dn) == 0ull) break;  // wave-uniform
       const uint32_t cand = th | (1u << bit);

@@ -492,25 +492,6 @@ __device__ void attend_f32(AttendLds<F32, MPAD, KPAD>& S, const float* __restric
 // blocks fit several to a CU: budget for 2 waves per SIMD (LDS allows no
 // more at m, k > 32; staging holds twice the values per thread).  fp32
 // (small problems): 256 threads, default budget.
-// One block per work item, grid (items per head, heads), the heads
-// interleaved in dispatch order (linear block L: head L % heads, position
-// L / heads).  With item_order the positions follow its order (full items,
-// then the last items, largest first); without it (the mid-length path),
-// item order.  False past the head's items.
-__device__ __forceinline__ bool dispatch_item(const int32_t* __restrict__ item_start,
-                                              const int32_t* __restrict__ item_order,
-                                              const int32_t* __restrict__ offsets, int m, int tpb,
-                                              int64_t& bh, TileInfo& ti) {
-  const int64_t L = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
-  bh = L % gridDim.y;
-  const int p = static_cast<int>(L / gridDim.y);
-  if (item_order == nullptr)
-    return find_item(item_start + bh * (m + 1), offsets + bh * (m + 1), m, tpb, p, ti);
-  if (p >= item_start[bh * (m + 1) + m]) return false;
-  find_item_ordered(item_order + bh * (2 * m + 1), offsets + bh * (m + 1), m, tpb, p, ti);
-  return true;
-}
-
 template <int MPAD, int KPAD, bool FULL, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 8 ? 4 : 2))) void k_attend_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -521,7 +502,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 8
   __shared__ AttendLds<BF16, MPAD, KPAD, NW> S;
   int64_t bh;
   TileInfo ti;
-  if (!dispatch_item(item_start, item_order, offsets, m, tpb, bh, ti)) return;
+  int p;
+  if (!dispatch_item(item_start, item_order, offsets, m, tpb, bh, p, ti)) return;
   attend_bf16<MPAD, KPAD, FULL, NW>(S, Q, K, V, Ql, vl, idx, perm, N, m, k, c2, out, bh, ti);
 }
 
@@ -822,7 +804,8 @@ __global__ __launch_bounds__(256) void k_attend_f32(
   __shared__ AttendLds<F32, MPAD, KPAD> S;
   int64_t bh;
   TileInfo ti;
-  if (!dispatch_item(item_start, item_order, offsets, m, tpb, bh, ti)) return;
+  int p;
+  if (!dispatch_item(item_start, item_order, offsets, m, tpb, bh, p, ti)) return;
   attend_f32<MPAD, KPAD>(S, Q, K, V, Ql, vl, idx, perm, N, m, k, c2, out, bh, ti);
 }
 

@@ -481,9 +481,14 @@ __global__ __launch_bounds__(256) void k_bw_scatter(const int32_t* __restrict__ 
                                                     const int32_t* __restrict__ colpre,
                                                     int32_t* __restrict__ offsets,
                                                     int32_t* __restrict__ item_start,
-                                                    int32_t* __restrict__ perm) {
+                                                    int32_t* __restrict__ perm,
+                                                    int32_t* __restrict__ item_order) {
   __shared__ ScatterLds L[4];
   const int w = __builtin_amdgcn_readfirstlane(wave_id());
+  if (blockIdx.x == gridDim.x - 1) {  // trailing block: the expert step's dispatch order
+    if (w == 0) write_item_order(totals, m, kAttendTile, tpb, blockIdx.y, item_order);
+    return;
+  }
   const int seg = static_cast<int>(blockIdx.x) * 4 + w;
   if (seg < nseg)
     scatter_segment(route, counts, m, nseg, N, kAttendTile, tpb, totals, colpre, offsets, nullptr,
@@ -514,7 +519,8 @@ __global__ __launch_bounds__(512) void k_bw_attend(
     const typename T::elem* __restrict__ V, const typename T::elem* __restrict__ ql,
     const float* __restrict__ vl, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ item_start, int tpb, int64_t N, int m, int k, float scale,
+    const int32_t* __restrict__ item_start, const int32_t* __restrict__ item_order, int tpb,
+    int64_t N, int m, int k, float scale,
     const float* __restrict__ dout, float* __restrict__ dQ, float* __restrict__ dke,
     float* __restrict__ dve, float* __restrict__ part, int items) {
   __shared__ __attribute__((aligned(16))) float sPk[kBwPairs * kBwSt];
@@ -532,9 +538,10 @@ __global__ __launch_bounds__(512) void k_bw_attend(
   const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
   const int hf = w >> 2, wl = w & 3;
   const int tid = threadIdx.x;
-  const int64_t bh = blockIdx.y;
+  int64_t bh;
+  int p;  // the block's position: its partial's slot
   TileInfo ti;
-  if (!find_item(item_start + bh * (m + 1), offsets + bh * (m + 1), m, tpb, blockIdx.x, ti))
+  if (!dispatch_item(item_start, item_order, offsets, m, tpb, bh, p, ti))
     return;  // whole block: past the head's last item
   const int MP = (m + 15) & ~15, KP = (k + 15) & ~15;
   const int PP = MP + KP, NB = PP / 16;
@@ -738,7 +745,7 @@ __global__ __launch_bounds__(512) void k_bw_attend(
   if (hf == 1) return;
   // the item's sums: landmark rows to its partial, raw-key rows to the
   // expert's key sums
-  float* pq_ = part + ((bh * items + blockIdx.x) * 2) * static_cast<int64_t>(m) * kD;
+  float* pq_ = part + ((bh * items + p) * 2) * static_cast<int64_t>(m) * kD;
   float* pv_ = pq_ + static_cast<int64_t>(m) * kD;
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
@@ -784,7 +791,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ ql,
     const float* __restrict__ vl, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ item_start, int tpb, int64_t N, int m, int k, float scale,
+    const int32_t* __restrict__ item_start, const int32_t* __restrict__ item_order, int tpb,
+    int64_t N, int m, int k, float scale,
     const float* __restrict__ dout, float* __restrict__ dQ, float* __restrict__ dke,
     float* __restrict__ dve, float* __restrict__ part, int items) {
   __shared__ __attribute__((aligned(16))) uint16_t sPk[kBwPairs * kBf16St];  // [Ql; 0; K_e; 0]
@@ -797,9 +805,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   __shared__ int sQid[16];
   const int l = lane_id(), w = wave_id(), g = l >> 4, c16 = l & 15;
   const int tid = threadIdx.x;
-  const int64_t bh = blockIdx.y;
+  int64_t bh;
+  int p;  // the block's position: its partial's slot
   TileInfo ti;
-  if (!find_item(item_start + bh * (m + 1), offsets + bh * (m + 1), m, tpb, blockIdx.x, ti))
+  if (!dispatch_item(item_start, item_order, offsets, m, tpb, bh, p, ti))
     return;  // whole block: past the head's last item
   const int MP = (m + 15) & ~15, KP = (k + 15) & ~15;
   const int PP = MP + KP, NB = PP / 16;
@@ -995,7 +1004,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   }
   // the item's sums: landmark rows to its partial, raw-key rows to the
   // expert's key sums
-  float* pq_ = part + ((bh * items + blockIdx.x) * 2) * static_cast<int64_t>(m) * kD;
+  float* pq_ = part + ((bh * items + p) * 2) * static_cast<int64_t>(m) * kD;
   float* pv_ = pq_ + static_cast<int64_t>(m) * kD;
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
@@ -1383,21 +1392,21 @@ hipError_t launch_backward_t(const Shape& s, const BwPlan& bp, const BwWorkspace
       e = hipGetLastError();
     }
     if (e == hipSuccess) {
-      hipLaunchKernelGGL(k_bw_scatter, dim3((bp.nseg + 3) / 4, BH), dim3(256), 0, st, route,
+      hipLaunchKernelGGL(k_bw_scatter, dim3((bp.nseg + 3) / 4 + 1, BH), dim3(256), 0, st, route,
                          ws.counts, s.m, bp.nseg, s.N, bp.tpb, ws.totals, ws.colpre, ws.offsets,
-                         ws.item_start, ws.perm);
+                         ws.item_start, ws.perm, ws.item_order);
       e = hipGetLastError();
     }
   }
   if (step(kBwAttend)) {
     if constexpr (std::is_same<T, BF16>::value)
       hipLaunchKernelGGL(k_bw_attend_bf16, dim3(bp.items, BH), dim3(256), 0, st, Q, K, V, ql,
-                         ws.vl, idx, ws.perm, ws.offsets, ws.item_start, bp.tpb, s.N, s.m, s.k,
-                         s.scale, dout, dQ, ws.dke, ws.dve, ws.part1, bp.items);
+                         ws.vl, idx, ws.perm, ws.offsets, ws.item_start, ws.item_order, bp.tpb,
+                         s.N, s.m, s.k, s.scale, dout, dQ, ws.dke, ws.dve, ws.part1, bp.items);
     else
       hipLaunchKernelGGL(k_bw_attend<T>, dim3(bp.items, BH), dim3(512), 0, st, Q, K, V, ql,
-                         ws.vl, idx, ws.perm, ws.offsets, ws.item_start, bp.tpb, s.N, s.m, s.k,
-                         s.scale, dout, dQ, ws.dke, ws.dve, ws.part1, bp.items);
+                         ws.vl, idx, ws.perm, ws.offsets, ws.item_start, ws.item_order, bp.tpb,
+                         s.N, s.m, s.k, s.scale, dout, dQ, ws.dke, ws.dve, ws.part1, bp.items);
     e = hipGetLastError();
     if (e == hipSuccess) {
       hipLaunchKernelGGL(k_bw_reduce1, dim3(s.m, BH), dim3(1024), 0, st, ws.part1, ws.item_start,
@@ -1484,6 +1493,7 @@ size_t plan_bw_workspace(const Shape& s, const BwPlan& bp, BwWorkspace* ws, char
   ws->totals = reinterpret_cast<int32_t*>(take(BH * m * 4));
   ws->offsets = reinterpret_cast<int32_t*>(take(BH * (m + 1) * 4));
   ws->item_start = reinterpret_cast<int32_t*>(take(BH * (m + 1) * 4));
+  ws->item_order = reinterpret_cast<int32_t*>(take(BH * (2 * m + 1) * 4));
   ws->perm = reinterpret_cast<int32_t*>(take(BH * s.N * 4));
   ws->part1 = reinterpret_cast<float*>(take(BH * bp.items * 2 * m * kD * sizeof(float)));
   ws->dql1 = reinterpret_cast<float*>(take(BH * m * kD * sizeof(float)));

@@ -310,6 +310,25 @@ __device__ __forceinline__ void find_item_ordered(const int32_t* __restrict__ or
   ti.qe = partial ? oe : min(ti.qb + kAttendTile * tpb, oe);
 }
 
+// One block per work item, grid (items per head, heads), the heads
+// interleaved in dispatch order (linear block L: head L % heads, position p =
+// L / heads).  With item_order the positions follow its order (full items,
+// then the last items, largest first); without it (the mid-length path),
+// item order.  False past the head's items.
+__device__ __forceinline__ bool dispatch_item(const int32_t* __restrict__ item_start,
+                                              const int32_t* __restrict__ item_order,
+                                              const int32_t* __restrict__ offsets, int m, int tpb,
+                                              int64_t& bh, int& p, TileInfo& ti) {
+  const int64_t L = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
+  bh = L % gridDim.y;
+  p = static_cast<int>(L / gridDim.y);
+  if (item_order == nullptr)
+    return find_item(item_start + bh * (m + 1), offsets + bh * (m + 1), m, tpb, p, ti);
+  if (p >= item_start[bh * (m + 1) + m]) return false;
+  find_item_ordered(item_order + bh * (2 * m + 1), offsets + bh * (m + 1), m, tpb, p, ti);
+  return true;
+}
+
 // Arguments of the bucket bodies, passed through the scan and merge launches.
 struct BucketArgs {
   const int32_t* route;

@@ -179,6 +179,7 @@ struct BwWorkspace {
   int32_t* totals = nullptr;    // [BH][m]
   int32_t* offsets = nullptr;   // [BH][m+1]
   int32_t* item_start = nullptr;// [BH][m+1]
+  int32_t* item_order = nullptr;// [BH][2m+1] the expert step's dispatch order (write_item_order)
   int32_t* perm = nullptr;      // [BH][N]
   float* part1 = nullptr;       // [BH][items][2][m][64] per-item dQl, dVl
   float* dql1 = nullptr;        // [BH][m][64] the expert step's dQl

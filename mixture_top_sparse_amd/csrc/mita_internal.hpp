@@ -17,9 +17,9 @@ constexpr int64_t kLastLevelCacheBytes = int64_t{256} << 20;  // MI355X Infinity
 constexpr int kRouteSeg = 1024;  // queries per routing/bucketing segment
 constexpr int kRouteSegSmall = 256;  // the same for short heads (few segments)
 constexpr int kAttendTile = 64;  // queries per expert-attention tile
-constexpr int kAttendMaxTpb = 16;
+constexpr int kAttendMaxTpb = 16;  // tiles per expert-attention work item, at most
 constexpr int kAttendShortItems = 256;  // below this many queries per expert (mean): 2-wave blocks
-constexpr int kAttendIpbMax = 8;        // 2-wave blocks: work items per block, at most  // tiles per expert-attention work item, at most
+constexpr int kAttendIpbMax = 8;        // 2-wave blocks: work items per block, at most
 constexpr int kPoolChunk = 4096; // tokens per pooling partial sum (fewer, longer blocks stream faster)
 constexpr int kPoolDirectMax = 128;  // windows up to this many tokens: one-launch pooling
 constexpr int kThetaTilesPerBlock = 1;  // sample tiles per top-k pre-threshold block

@@ -7,10 +7,12 @@
 // section "长序列建模：训练时间从10.6小时降至2.4小时").  This kernel gives
 // that ratio on the same GPU, with no library attention underneath.
 //
-// A flash-attention forward for bf16 inputs: grid (query tiles of 64, B*H),
-// 4 waves per block, wave w owning queries 16w..16w+15 of the tile.  Every
+// A flash-attention forward for bf16 inputs: grid (query tiles of 64 QB,
+// B*H), 4 waves per block, wave w owning QB blocks of 16 queries.  Every
 // 64-key tile of the head streams through a two-slot LDS ring by the same
-// global-load-to-LDS staging as the landmark scan.  Per tile and wave:
+// global-load-to-LDS staging as the landmark scan; each K and V operand
+// read from it feeds QB MFMAs (with one 16-query block per wave, the LDS
+// reads bounded the kernel).  Per tile and 16-query block:
 // Sᵀ = K·Qᵀ on bf16 MFMA, an online softmax in the log2 domain (lazy rescale),
 // and Oᵀ += Vᵀ·Pᵀ on bf16 MFMA with P rounded to bf16 once, as
 // flash-attention kernels do; fp32 output.
@@ -24,7 +26,17 @@
 
 namespace mita {
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_dense_bf16(
+// 16-query row blocks per wave.  Measured at 2^16 tokens x 8 heads: d = 64
+// 821 (one block), 962 (two), 915 (three), 1000 TFLOP/s (four); d = 128 856
+// (one), 1126 (two), 812 TFLOP/s (four, one wave per SIMD).
+constexpr int kDenseQB64 = 4;
+constexpr int kDenseQB128 = 2;
+
+// QB: 16-query row blocks per wave (wave w owns rows 16 (QB w + j), j < QB,
+// of the block's 64 QB queries).  Every K and V operand read from LDS feeds
+// QB MFMAs, so QB = 2 halves the LDS traffic per flop.
+template <int QB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QB <= 2 ? 3 : 2))) void k_dense_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, int64_t N, float c2, float* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) uint8_t b0[16384];  // K tile (8 KiB), then V tile
@@ -32,19 +44,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   const int l = lane_id(), g = l >> 4, c16 = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(wave_id());
   const int64_t bh = blockIdx.y;
-  const int64_t q = static_cast<int64_t>(blockIdx.x) * 64 + 16 * w + c16;  // this lane's query
+  int64_t q[QB];  // this lane's query in each row block
+#pragma unroll
+  for (int j = 0; j < QB; ++j)
+    q[j] = static_cast<int64_t>(blockIdx.x) * (64 * QB) + 16 * (QB * w + j) + c16;
   const uint16_t* Kh = K + bh * N * kD;
   const uint16_t* Vh = V + bh * N * kD;
   const int ntiles = static_cast<int>((N + kTileKeys - 1) / kTileKeys);
 
-  // the wave's 16 queries as the B operand (rows past N read row N - 1 and
-  // are not stored); complete before the first tile request, so that inside
-  // the loop the only outstanding requests are tiles
-  bf16x8 qv[2];
-  {
-    const uint16_t* qr = Q + (bh * N + (q < N ? q : N - 1)) * kD;
+  // the wave's queries as B operands (rows past N read row N - 1 and are not
+  // stored); complete before the first tile request, so that inside the
+  // loop the only outstanding requests are tiles
+  bf16x8 qv[QB][2];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) qv[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qr + 32 * s + 8 * g));
+  for (int j = 0; j < QB; ++j) {
+    const uint16_t* qr = Q + (bh * N + (q[j] < N ? q[j] : N - 1)) * kD;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      qv[j][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qr + 32 * s + 8 * g));
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __asm__ volatile("" ::: "memory");
@@ -53,10 +70,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   const uint32_t a0 = lds_address(b0), a1 = lds_address(b1);
   stage_tile_bf16<false>(Kh, Vh, 0, N, a0, a0 + 8192, w, soff0, soff1);
 
-  float M = -INFINITY, Lsum = 0.f;
-  f32x4 acc[4];
+  float M[QB], Lsum[QB];
+  f32x4 acc[QB][4];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x4{0, 0, 0, 0};
+  for (int j = 0; j < QB; ++j) {
+    M[j] = -INFINITY;
+    Lsum[j] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) acc[j][dt] = f32x4{0, 0, 0, 0};
+  }
   const int kq0 = tile_off(c16, g), kq1 = tile_off(c16, 4 + g);  // + 2048 kb
   int voff[4];  // + 4096 s2 + 2048 h
 #pragma unroll
@@ -65,7 +87,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 
   auto compute_tile = [&](const uint8_t* kl, const uint8_t* vl, int64_t t0)
       __attribute__((always_inline)) {
-    float sc[4][4];
+    float sc[QB][4][4];
     {
       u32x4 ko[4][2];
 #pragma unroll
@@ -73,47 +95,60 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         ko[kb][0] = *reinterpret_cast<const u32x4*>(kl + kq0 + 2048 * kb);
         ko[kb][1] = *reinterpret_cast<const u32x4*>(kl + kq1 + 2048 * kb);
       }
-      f32x4 a[4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) a[kb] = mfma_bf16(as_bf16x8(ko[kb][0]), qv[0], f32x4{0, 0, 0, 0});
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) a[kb] = mfma_bf16(as_bf16x8(ko[kb][1]), qv[1], a[kb]);
+      f32x4 a[QB][4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sc[kb][r] = a[kb][r];
+        for (int j = 0; j < QB; ++j)
+          a[j][kb] = mfma_bf16(as_bf16x8(ko[kb][0]), qv[j][0], f32x4{0, 0, 0, 0});
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int j = 0; j < QB; ++j) a[j][kb] = mfma_bf16(as_bf16x8(ko[kb][1]), qv[j][1], a[j][kb]);
+#pragma unroll
+      for (int j = 0; j < QB; ++j)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sc[j][kb][r] = a[j][kb][r];
     }
     if (t0 + kTileKeys > N) {  // ragged last tile: drop keys past N
       __asm__ volatile("" ::: "memory");  // keep this a branch
       const int rel = static_cast<int>(N - t0) - 4 * g;  // key 16kb+4g+r valid iff 16kb+r < rel
 #pragma unroll
+      for (int j = 0; j < QB; ++j)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (16 * kb + r >= rel) sc[j][kb][r] = -INFINITY;
+    }
+    float p[QB][4][4];
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        mx = fmax_nc(mx, fmax_nc(fmax_nc(sc[j][kb][0], sc[j][kb][1]),
+                                 fmax_nc(sc[j][kb][2], sc[j][kb][3])));
+      mx = xor_max(mx, 16);
+      mx = xor_max(mx, 32) * c2;
+      if (ballot(mx > M[j])) {
+        const float Mn = fmaxf(M[j], mx);
+        const float alpha = fast_exp2(M[j] - Mn);
+        Lsum[j] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) acc[j][dt] *= alpha;
+        M[j] = Mn;
+      }
+#pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (16 * kb + r >= rel) sc[kb][r] = -INFINITY;
+        for (int r = 0; r < 4; ++r) {
+          p[j][kb][r] = fast_exp2(fmaf(sc[j][kb][r], c2, -M[j]));
+          Lsum[j] += p[j][kb][r];
+        }
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      mx = fmax_nc(mx, fmax_nc(fmax_nc(sc[kb][0], sc[kb][1]), fmax_nc(sc[kb][2], sc[kb][3])));
-    mx = xor_max(mx, 16);
-    mx = xor_max(mx, 32) * c2;
-    if (ballot(mx > M)) {
-      const float Mn = fmaxf(M, mx);
-      const float alpha = fast_exp2(M - Mn);
-      Lsum *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
-      M = Mn;
-    }
-    float p[4][4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[kb][r] = fast_exp2(fmaf(sc[kb][r], c2, -M));
-        Lsum += p[kb][r];
-      }
     // Oᵀ[d][q] += Vᵀ[d][keys] Pᵀ[keys][q]; K-position 8g + j is key
     // 32 s2 + 4g + j (j < 4) or 32 s2 + 16 + 4g + (j - 4)
 #pragma unroll
@@ -127,17 +162,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
             (lds_v4i16*)(vl + voff[dt] + 4096 * s2 + 2048));
         va[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
       }
-      float pp[8];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pp[r] = p[2 * s2][r];
-        pp[4 + r] = p[2 * s2 + 1][r];
+      for (int j = 0; j < QB; ++j) {
+        float pp[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pp[r] = p[j][2 * s2][r];
+          pp[4 + r] = p[j][2 * s2 + 1][r];
+        }
+        bf16x8 hi, lo;
+        split_hi_lo_pk(pp, hi, lo);  // P in bf16 (the residual is not used)
+        (void)lo;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) acc[j][dt] = mfma_bf16(va[dt], hi, acc[j][dt]);
       }
-      bf16x8 hi, lo;
-      split_hi_lo_pk(pp, hi, lo);  // P in bf16 (the residual is not used)
-      (void)lo;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma_bf16(va[dt], hi, acc[dt]);
     }
   };
 
@@ -161,13 +199,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   }
 
   // normalise: the query's weight sum is spread over its 4 lane groups
-  Lsum = xor_sum(Lsum, 16);
-  Lsum = xor_sum(Lsum, 32);
-  if (q < N) {
-    const float f = 1.0f / Lsum;  // Lsum >= 1 (the maximum's weight)
-    float* o = out + (bh * N + q) * kD;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) *reinterpret_cast<f32x4*>(o + 16 * dt + 4 * g) = acc[dt] * f;
+  for (int j = 0; j < QB; ++j) {
+    float ls = xor_sum(Lsum[j], 16);
+    ls = xor_sum(ls, 32);
+    if (q[j] < N) {
+      const float f = 1.0f / ls;  // ls >= 1 (the maximum's weight)
+      float* o = out + (bh * N + q[j]) * kD;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) *reinterpret_cast<f32x4*>(o + 16 * dt + 4 * g) = acc[j][dt] * f;
+    }
   }
 }
 
@@ -202,6 +243,8 @@ __device__ __forceinline__ void stage_tile_bf16_d128(const uint16_t* __restrict_
   }
 }
 
+// QB: 16-query row blocks per wave, as in k_dense_bf16.
+template <int QB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_dense_bf16_d128(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, int64_t N, float c2, float* __restrict__ out) {
@@ -211,26 +254,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int l = lane_id(), g = l >> 4, c16 = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(wave_id());
   const int64_t bh = blockIdx.y;
-  const int64_t q = static_cast<int64_t>(blockIdx.x) * 64 + 16 * w + c16;
+  int64_t q[QB];
+#pragma unroll
+  for (int j = 0; j < QB; ++j)
+    q[j] = static_cast<int64_t>(blockIdx.x) * (64 * QB) + 16 * (QB * w + j) + c16;
   const uint16_t* Kh = K + bh * N * kD2;
   const uint16_t* Vh = V + bh * N * kD2;
   const int ntiles = static_cast<int>((N + kTileKeys - 1) / kTileKeys);
-  bf16x8 qv[4];  // features 32s + 8g .. +7
-  {
-    const uint16_t* qr = Q + (bh * N + (q < N ? q : N - 1)) * kD2;
+  bf16x8 qv[QB][4];  // features 32s + 8g .. +7
+#pragma unroll
+  for (int j = 0; j < QB; ++j) {
+    const uint16_t* qr = Q + (bh * N + (q[j] < N ? q[j] : N - 1)) * kD2;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      qv[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qr + 32 * s + 8 * g));
+      qv[j][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qr + 32 * s + 8 * g));
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __asm__ volatile("" ::: "memory");
   const uint32_t a0 = lds_address(b0), a1 = lds_address(b1);
   stage_tile_bf16_d128(Kh, Vh, 0, N, a0, w, l);
 
-  float M = -INFINITY, Lsum = 0.f;
-  f32x4 acc[8];
+  float M[QB], Lsum[QB];
+  f32x4 acc[QB][8];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4{0, 0, 0, 0};
+  for (int j = 0; j < QB; ++j) {
+    M[j] = -INFINITY;
+    Lsum[j] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[j][dt] = f32x4{0, 0, 0, 0};
+  }
   const int kq0 = tile_off(c16, g), kq1 = tile_off(c16, 4 + g);
   int voff[4];
 #pragma unroll
@@ -238,69 +290,86 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     voff[dt] = tile_off(4 * g + (c16 >> 2), 2 * dt + ((c16 & 3) >> 1)) + ((c16 & 1) << 3);
 
   auto compute_tile = [&](const uint8_t* buf, int64_t t0) __attribute__((always_inline)) {
-    float sc[4][4];
+    float sc[QB][4][4];
     {
-      f32x4 a[4];
+      f32x4 a[QB][4];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) a[kb] = f32x4{0, 0, 0, 0};
+      for (int j = 0; j < QB; ++j)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) a[j][kb] = f32x4{0, 0, 0, 0};
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const uint8_t* kl = buf + 8192 * h;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-          a[kb] = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(kl + kq0 + 2048 * kb)),
-                            qv[2 * h], a[kb]);
-          a[kb] = mfma_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(kl + kq1 + 2048 * kb)),
-                            qv[2 * h + 1], a[kb]);
+          const bf16x8 k0 = as_bf16x8(*reinterpret_cast<const u32x4*>(kl + kq0 + 2048 * kb));
+          const bf16x8 k1 = as_bf16x8(*reinterpret_cast<const u32x4*>(kl + kq1 + 2048 * kb));
+#pragma unroll
+          for (int j = 0; j < QB; ++j) {
+            a[j][kb] = mfma_bf16(k0, qv[j][2 * h], a[j][kb]);
+            a[j][kb] = mfma_bf16(k1, qv[j][2 * h + 1], a[j][kb]);
+          }
         }
       }
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int j = 0; j < QB; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sc[kb][r] = a[kb][r];
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sc[j][kb][r] = a[j][kb][r];
     }
     if (t0 + kTileKeys > N) {
       __asm__ volatile("" ::: "memory");
       const int rel = static_cast<int>(N - t0) - 4 * g;
 #pragma unroll
+      for (int j = 0; j < QB; ++j)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (16 * kb + r >= rel) sc[j][kb][r] = -INFINITY;
+    }
+    float p[QB][4][4];
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        mx = fmax_nc(mx, fmax_nc(fmax_nc(sc[j][kb][0], sc[j][kb][1]),
+                                 fmax_nc(sc[j][kb][2], sc[j][kb][3])));
+      mx = xor_max(mx, 16);
+      mx = xor_max(mx, 32) * c2;
+      if (ballot(mx > M[j])) {
+        const float Mn = fmaxf(M[j], mx);
+        const float alpha = fast_exp2(M[j] - Mn);
+        Lsum[j] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) acc[j][dt] *= alpha;
+        M[j] = Mn;
+      }
+#pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (16 * kb + r >= rel) sc[kb][r] = -INFINITY;
+        for (int r = 0; r < 4; ++r) {
+          p[j][kb][r] = fast_exp2(fmaf(sc[j][kb][r], c2, -M[j]));
+          Lsum[j] += p[j][kb][r];
+        }
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      mx = fmax_nc(mx, fmax_nc(fmax_nc(sc[kb][0], sc[kb][1]), fmax_nc(sc[kb][2], sc[kb][3])));
-    mx = xor_max(mx, 16);
-    mx = xor_max(mx, 32) * c2;
-    if (ballot(mx > M)) {
-      const float Mn = fmaxf(M, mx);
-      const float alpha = fast_exp2(M - Mn);
-      Lsum *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) acc[dt] *= alpha;
-      M = Mn;
-    }
-    float p[4][4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[kb][r] = fast_exp2(fmaf(sc[kb][r], c2, -M));
-        Lsum += p[kb][r];
-      }
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
-      float pp[8];
+      bf16x8 hi[QB];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pp[r] = p[2 * s2][r];
-        pp[4 + r] = p[2 * s2 + 1][r];
+      for (int j = 0; j < QB; ++j) {
+        float pp[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pp[r] = p[j][2 * s2][r];
+          pp[4 + r] = p[j][2 * s2 + 1][r];
+        }
+        bf16x8 lo;
+        split_hi_lo_pk(pp, hi[j], lo);  // P in bf16 (the residual is not used)
+        (void)lo;
       }
-      bf16x8 hi, lo;
-      split_hi_lo_pk(pp, hi, lo);  // P in bf16 (the residual is not used)
-      (void)lo;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const uint8_t* vl = buf + 16384 + 8192 * h;
@@ -312,7 +381,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
               (lds_v4i16*)(vl + voff[dt] + 4096 * s2 + 2048));
           const bf16x8 va =
               __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
-          acc[4 * h + dt] = mfma_bf16(va, hi, acc[4 * h + dt]);
+#pragma unroll
+          for (int j = 0; j < QB; ++j) acc[j][4 * h + dt] = mfma_bf16(va, hi[j], acc[j][4 * h + dt]);
         }
       }
     }
@@ -332,14 +402,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     if (it + 1 >= ntiles) break;
     step(it + 1, b1, a0);
   }
-  Lsum = xor_sum(Lsum, 16);
-  Lsum = xor_sum(Lsum, 32);
-  if (q < N) {
-    const float f = 1.0f / Lsum;
-    float* o = out + (bh * N + q) * kD2;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-      *reinterpret_cast<f32x4*>(o + 16 * dt + 4 * g) = acc[dt] * f;
+  for (int j = 0; j < QB; ++j) {
+    float ls = xor_sum(Lsum[j], 16);
+    ls = xor_sum(ls, 32);
+    if (q[j] < N) {
+      const float f = 1.0f / ls;
+      float* o = out + (bh * N + q[j]) * kD2;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        *reinterpret_cast<f32x4*>(o + 16 * dt + 4 * g) = acc[j][dt] * f;
+    }
   }
 }
 
@@ -347,12 +420,14 @@ hipError_t launch_dense(int dtype, const void* Q, const void* K, const void* V, 
                         int64_t N, int64_t d, float scale, float* out, hipStream_t st) {
   if (dtype != 1) return hipErrorInvalidValue;  // bf16 only
   if (d == kD2) {
-    hipLaunchKernelGGL(k_dense_bf16_d128, dim3((N + 63) / 64, BH), dim3(256), 0, st,
-                       static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
+    constexpr int QB = kDenseQB128;
+    hipLaunchKernelGGL(k_dense_bf16_d128<QB>, dim3((N + 64 * QB - 1) / (64 * QB), BH), dim3(256),
+                       0, st, static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
                        static_cast<const uint16_t*>(V), N, scale * kLog2e, out);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(k_dense_bf16, dim3((N + 63) / 64, BH), dim3(256), 0, st,
+  constexpr int QB = kDenseQB64;
+  hipLaunchKernelGGL(k_dense_bf16<QB>, dim3((N + 64 * QB - 1) / (64 * QB), BH), dim3(256), 0, st,
                      static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
                      static_cast<const uint16_t*>(V), N, scale * kLog2e, out);
   return hipGetLastError();

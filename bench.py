@@ -303,10 +303,21 @@ def dense_baseline(w, Qt, Kt, Vt) -> dict:
 
 
 FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix rate, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix rate, published
+
+
+def backward_peaks(w) -> dict[str, float]:
+    """The matrix rate each backward contraction kernel runs on: for bf16
+    inputs the expert step issues bf16 MFMAs (its fp32 operands split into
+    bf16 hi + lo parts), every other kernel fp32 MFMAs."""
+    bf16 = w.dtype == "bf16"
+    return {"bw_attend": BF16_MFMA_PEAK_TFLOPS if bf16 else FP32_MFMA_PEAK_TFLOPS,
+            "bw_cross": FP32_MFMA_PEAK_TFLOPS,
+            "bw_landmark_fwd": FP32_MFMA_PEAK_TFLOPS}
 
 
 def backward_flops(w) -> dict[str, float]:
-    """Algorithmic fp32 MFMA flops per launch of the backward's contraction
+    """Algorithmic flops per launch of the backward's contraction
     kernels: the expert step does five (m + k) x d products per query (logits,
     dout . values, dQ, and the pair-side sums for keys and values), the
     cross-attention step five m x d products per key, the recomputed
@@ -320,7 +331,8 @@ def backward_flops(w) -> dict[str, float]:
 def backward_bench(w, Qt, Kt, Vt, idx, route) -> dict:
     """The backward pass (mita_backward, experts and routes from the forward
     just timed) on the same inputs: time per call, per-step times from the
-    stage profiler, and its dominant kernel against the fp32 MFMA peak."""
+    stage profiler, and its dominant kernel against the peak of the matrix
+    instructions it issues (backward_peaks)."""
     import torch
 
     import mixture_top_sparse_amd as mts
@@ -357,15 +369,16 @@ def backward_bench(w, Qt, Kt, Vt, idx, route) -> dict:
     tf = {k_: fl[k_] / (st[k_] * 1e-3) / 1e12 for k_ in fl if st.get(k_, 0) > 0}
     dom = max(fl, key=lambda k_: st.get(k_, 0.0))
     value = w.B * w.H * w.N / (ms * 1e-3) / 1e6
+    peak = backward_peaks(w)[dom]
     log(f"backward: {ms:.3f} ms/call ({reps} timed), {value:.1f} Mtokens.heads/s; "
-        f"{dom} {st[dom]:.3f} ms at {tf[dom]:.1f} TFLOP/s fp32")
+        f"{dom} {st[dom]:.3f} ms at {tf[dom]:.1f} TFLOP/s (peak {peak:.1f})")
     return {"ms_per_call": round(ms, 4), "calls": reps, "value": round(value, 2),
             "unit": "Mtokens·heads/s", "stages_ms": {k_: round(v, 4) for k_, v in st.items()},
             "stages_TFLOPs": {k_: round(v, 1) for k_, v in tf.items()},
             "roofline": {"scope": "dominant backward kernel", "bound": "mfma", "kernel": dom,
                          "flops": fl[dom], "launch_ms": round(st[dom], 4),
-                         "achieved": round(tf[dom], 1), "peak": FP32_MFMA_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tf[dom] / FP32_MFMA_PEAK_TFLOPS, 4),
+                         "achieved": round(tf[dom], 1), "peak": peak,
+                         "unit": "TFLOP/s", "frac": round(tf[dom] / peak, 4),
                          "traffic": None}}
 
 

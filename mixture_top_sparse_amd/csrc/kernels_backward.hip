@@ -30,15 +30,23 @@
 //   keyadd    dK, dV at each expert key += the expert step's sums (atomics)
 //   reduce2   dQl in full, divided by each window's size
 //   poolbw    dQ[t] += sum over the windows i containing t of dQl_i / |W_i|
-// Every contraction runs on v_mfma_f32_16x16x4_f32 (fp32 operands, fp32
-// accumulation), so the gradients carry fp32 rounding only.
+// With fp32 inputs every contraction runs on v_mfma_f32_16x16x4_f32 (fp32
+// operands, fp32 accumulation).  With bf16 inputs the score products run on
+// bf16 MFMA from the exact bf16 rows, and the expert step's other products
+// on bf16 MFMA too: operands exact in bf16 (Q, K, V rows) as they are, the
+// computed ones (dout, Vl, g, the weights w) split into bf16 hi + lo parts
+// (hi = rne(x), lo = rne(x - hi)), the lo x lo term dropped, so that each
+// product is within about 2^-16 of the exact one, relative; fp32
+// accumulation throughout.
 //
 // Roofline: per (token, head) the pass reads Q, K, V (3 d e bytes, e the
 // input element size; K and V twice, in the landmark forward and the cross
 // step) and dout (4d), and writes dQ, dK, dV (12d) plus dQ's
 // read-modify-write in poolbw (8d): about 5de + 24d bytes.  The contractions cost about 2 d (5 (m + k) + 7 m)
 // flops per (token, head) at fp32 MFMA rate, which exceeds the bytes' time
-// at 157 TFLOP/s for m = k = 64: the pass is MFMA-bound (fp32).
+// at 157 TFLOP/s for m = k = 64: with fp32 operands the pass is MFMA-bound.
+// On bf16 MFMA the expert step is bound by the latency of its dependent
+// phases instead.
 #include <type_traits>
 
 #include "mita.h"
@@ -778,14 +786,39 @@ __global__ __launch_bounds__(512) void k_bw_attend(
   }
 }
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// v_mfma_f32_16x16x16_bf16: A[16][16], B[16][16], lane l holds row (A) or
+// column (B) l % 16 and the 4 consecutive K-elements 4 (l / 16) .. + 3
+__device__ __forceinline__ f32x4 mfma_bf16_k16(v4i16 a, v4i16 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+// 4 fp32 values as bf16 hi = rne(x) and lo = rne(x - hi)
+__device__ __forceinline__ void split4(const float (&x)[4], v4i16& hi, v4i16& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const __bf16 h = static_cast<__bf16>(x[i]);
+    hi[i] = __builtin_bit_cast(short, h);
+    lo[i] = __builtin_bit_cast(short, static_cast<__bf16>(x[i] - static_cast<float>(h)));
+  }
+}
+__device__ __forceinline__ void split4(const f32x4& x, v4i16& hi, v4i16& lo) {
+  const float v[4] = {x[0], x[1], x[2], x[3]};
+  split4(v, hi, lo);
+}
+
 // The same step for bf16 inputs in four-wave blocks whose LDS fits two
-// blocks per CU (about 61 KiB), so that one block's barriers overlap the
+// blocks per CU (about 62 KiB), so that one block's barriers overlap the
 // other's work: every operand that is exact in bf16 stays bf16 in LDS (the
-// pair keys [Ql; K_e], the raw values V_e, the query rows) and is widened
-// when read; the landmark values Vl, dout and g stay fp32.  One group of 16
-// queries at a time (the next group's rows in registers meanwhile); wave w
-// owns column blocks w and w + 4 and dims 16 w .. 16 w + 15 of dQ, as in
-// k_bw_attend.
+// pair keys [Ql; K_e], the raw values V_e, the query rows), the landmark
+// values as bf16 hi + lo, dout and g as fp32.  Every product runs on bf16
+// MFMA: dout . [Vl; V_e]^T and g . [Ql; K_e] on v_mfma_f32_16x16x32_bf16,
+// the pair-side sums g^T Q and w^T dout on v_mfma_f32_16x16x16_bf16 (its
+// A operand is the lane's own four weights), computed operands as hi + lo
+// (expert step at 2^20 tokens x 4 heads: 3.84 -> 2.45 ms against fp32
+// MFMA).  One group of 16 queries at a time (the next group's rows in
+// registers meanwhile); wave w owns column blocks w and w + 4 and dims
+// 16 w .. 16 w + 15 of dQ, as in k_bw_attend.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_bw_attend_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ ql,
@@ -796,7 +829,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     const float* __restrict__ dout, float* __restrict__ dQ, float* __restrict__ dke,
     float* __restrict__ dve, float* __restrict__ part, int items) {
   __shared__ __attribute__((aligned(16))) uint16_t sPk[kBwPairs * kBf16St];  // [Ql; 0; K_e; 0]
-  __shared__ __attribute__((aligned(16))) float sVl[kMaxM * kBwSt];          // Vl rows (fp32)
+  __shared__ __attribute__((aligned(16))) uint16_t sVlh[kMaxM * kBf16St];   // Vl rows, bf16 hi
+  __shared__ __attribute__((aligned(16))) uint16_t sVll[kMaxM * kBf16St];   // Vl rows, bf16 lo
   __shared__ __attribute__((aligned(16))) uint16_t sV[kMaxK * kBf16St];     // V_e rows
   __shared__ __attribute__((aligned(16))) uint16_t sQ[16 * kBf16St];
   __shared__ __attribute__((aligned(16))) float sG[16 * kBwSt];
@@ -820,7 +854,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       kv.load(ql + (bh * m + row) * kD + 8 * j);
       float vv[8];
       load8(vl + (bh * m + row) * kD + 8 * j, vv);
-      store8(sVl + row * kBwSt + 8 * j, vv);
+      bf16x8 hi, lo;
+      split_hi_lo_pk(vv, hi, lo);
+      *reinterpret_cast<bf16x8*>(sVlh + row * kBf16St + 8 * j) = hi;
+      *reinterpret_cast<bf16x8*>(sVll + row * kBf16St + 8 * j) = lo;
     } else if (row >= MP && row < MP + k) {
       const int64_t t = clamp64(ex[row - MP], N);
       kv.load(K + (bh * N + t) * kD + 8 * j);
@@ -830,9 +867,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     } else {
       kv.zero();
       if (row < MP) {
-        float z[8];
-        zero8(z);
-        store8(sVl + row * kBwSt + 8 * j, z);
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(sVlh + row * kBf16St + 8 * j) = z;
+        *reinterpret_cast<u32x4*>(sVll + row * kBf16St + 8 * j) = z;
       } else {
         Raw8<BF16> z;
         z.zero();
@@ -879,9 +916,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     __syncthreads();
     ScoreA<BF16> aq;
     aq.load(reinterpret_cast<const float*>(sQ), c16, g);
-    float ag[16];
+    // dout of query c16, features 32 s + 8 g .. + 7, as bf16 hi + lo (the
+    // A operand of dout . [Vl; V_e]^T)
+    bf16x8 agh[2], agl[2];
 #pragma unroll
-    for (int s = 0; s < 16; ++s) ag[s] = sG[c16 * kBwSt + 4 * s + g];
+    for (int s = 0; s < 2; ++s) {
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(sG + c16 * kBwSt + 32 * s + 8 * g);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(sG + c16 * kBwSt + 32 * s + 8 * g + 4);
+      const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      split_hi_lo_pk(x, agh[s], agl[s]);
+    }
+    // queries 4 g .. 4 g + 3 at feature 16 db + c16: Q (exact bf16) and dout
+    // (hi + lo), the B operands of the key and value sums
+    v4i16 bq[4], bgh[4], bgl[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      float x[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bq[db][j] = static_cast<short>(sQ[(4 * g + j) * kBf16St + 16 * db + c16]);
+        x[j] = sG[(4 * g + j) * kBwSt + 16 * db + c16];
+      }
+      split4(x, bgh[db], bgl[db]);
+    }
     f32x4 S[2], dW[2];
     float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
@@ -893,17 +950,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         const f32x4 s4 = aq.score(reinterpret_cast<const float*>(sPk), 16 * pb + c16, g);
         f32x4 d4 = {0.f, 0.f, 0.f, 0.f}, d4b = d4;  // two chains of 8
         const int p = 16 * pb + c16;
-        if (16 * pb < MP) {  // landmark values (fp32)
+        if (16 * pb < MP) {  // landmark values: hi + lo by hi + lo, lo x lo dropped
 #pragma unroll
-          for (int s = 0; s < 16; s += 2) {
-            d4 = mfma_f32(ag[s], sVl[p * kBwSt + 4 * s + g], d4);
-            d4b = mfma_f32(ag[s + 1], sVl[p * kBwSt + 4 * (s + 1) + g], d4b);
+          for (int s = 0; s < 2; ++s) {
+            const bf16x8 vh = as_bf16x8(*reinterpret_cast<const u32x4*>(sVlh + p * kBf16St + 32 * s + 8 * g));
+            const bf16x8 vo = as_bf16x8(*reinterpret_cast<const u32x4*>(sVll + p * kBf16St + 32 * s + 8 * g));
+            d4 = mfma_bf16(agh[s], vh, d4);
+            d4b = mfma_bf16(agl[s], vh, d4b);
+            d4 = mfma_bf16(agh[s], vo, d4);
           }
-        } else {  // raw values (bf16)
+        } else {  // raw values (exact bf16)
 #pragma unroll
-          for (int s = 0; s < 16; s += 2) {
-            d4 = mfma_f32(ag[s], bf(sV, (p - MP) * kBf16St + 4 * s + g), d4);
-            d4b = mfma_f32(ag[s + 1], bf(sV, (p - MP) * kBf16St + 4 * (s + 1) + g), d4b);
+          for (int s = 0; s < 2; ++s) {
+            const bf16x8 vr = as_bf16x8(*reinterpret_cast<const u32x4*>(sV + (p - MP) * kBf16St + 32 * s + 8 * g));
+            d4 = mfma_bf16(agh[s], vr, d4);
+            d4b = mfma_bf16(agl[s], vr, d4b);
           }
         }
         d4 += d4b;
@@ -977,24 +1038,58 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       if (pb >= NB) continue;
 #pragma unroll
       for (int r = 0; r < 4; ++r) sGs[(4 * g + r) * kBwGsSt + 16 * pb + c16] = Gs[cb][r];
+      // sums over the 16 queries on v_mfma_f32_16x16x16_bf16: A = the lane's
+      // own 4 weights (queries 4 g .. 4 g + 3 of pair column c16) as hi + lo
+      v4i16 gh, gl, wh, wl;
+      split4(Gs[cb], gh, gl);
+      split4(Wt[cb], wh, wl);
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          aK[cb][db] = mfma_f32(Gs[cb][r], bf(sQ, (4 * g + r) * kBf16St + 16 * db + c16), aK[cb][db]);
-          aV[cb][db] = mfma_f32(Wt[cb][r], sG[(4 * g + r) * kBwSt + 16 * db + c16], aV[cb][db]);
-        }
+      for (int db = 0; db < 4; ++db) {
+        aK[cb][db] = mfma_bf16_k16(gh, bq[db], aK[cb][db]);
+        aK[cb][db] = mfma_bf16_k16(gl, bq[db], aK[cb][db]);
+        aV[cb][db] = mfma_bf16_k16(wh, bgh[db], aV[cb][db]);
+        aV[cb][db] = mfma_bf16_k16(wl, bgh[db], aV[cb][db]);
+        aV[cb][db] = mfma_bf16_k16(wh, bgl[db], aV[cb][db]);
+      }
     }
     __syncthreads();
     // dQ (16 queries x dims 16 w .. 16 w + 15) = g [keys], four chains
+    // bf16 MFMA over pairs in steps of 32 (g as hi + lo, the keys exact),
+    // then 16 when NB is odd
     f32x4 dq[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) dq[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < 4 * NB; s += 4)
+#pragma unroll
+    for (int t = 0; t < kBwPairs / 32; ++t) {
+      if (32 * t + 32 > 16 * NB) break;  // wave-uniform
+      const float* gr = sGs + c16 * kBwGsSt + 32 * t + 8 * g;
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(gr);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(gr + 4);
+      const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      bf16x8 ah, al;
+      split_hi_lo_pk(x, ah, al);
+      u32x4 kw;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        dq[j] = mfma_f32(sGs[c16 * kBwGsSt + 4 * (s + j) + g],
-                         bf(sPk, (4 * (s + j) + g) * kBf16St + 16 * w + c16), dq[j]);
+        kw[j] = static_cast<uint32_t>(sPk[(32 * t + 8 * g + 2 * j) * kBf16St + 16 * w + c16]) |
+                (static_cast<uint32_t>(sPk[(32 * t + 8 * g + 2 * j + 1) * kBf16St + 16 * w + c16]) << 16);
+      dq[t & 1] = mfma_bf16(ah, as_bf16x8(kw), dq[t & 1]);
+      dq[2 + (t & 1)] = mfma_bf16(al, as_bf16x8(kw), dq[2 + (t & 1)]);
+    }
+    if (NB & 1) {
+      const int p0 = 16 * (NB - 1);
+      float x[4];
+      v4i16 kq;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[j] = sGs[c16 * kBwGsSt + p0 + 4 * g + j];
+        kq[j] = static_cast<short>(sPk[(p0 + 4 * g + j) * kBf16St + 16 * w + c16]);
+      }
+      v4i16 ah, al;
+      split4(x, ah, al);
+      dq[0] = mfma_bf16_k16(ah, kq, dq[0]);
+      dq[1] = mfma_bf16_k16(al, kq, dq[1]);
+    }
     dq[0] += dq[1] + dq[2] + dq[3];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {

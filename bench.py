@@ -308,11 +308,11 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix rate, published
 
 def backward_peaks(w) -> dict[str, float]:
     """The matrix rate each backward contraction kernel runs on: for bf16
-    inputs the expert step issues bf16 MFMAs (its fp32 operands split into
-    bf16 hi + lo parts), every other kernel fp32 MFMAs."""
+    inputs the expert and cross steps issue bf16 MFMAs (their fp32 operands
+    split into bf16 hi + lo parts), the landmark forward fp32 MFMAs."""
     bf16 = w.dtype == "bf16"
     return {"bw_attend": BF16_MFMA_PEAK_TFLOPS if bf16 else FP32_MFMA_PEAK_TFLOPS,
-            "bw_cross": FP32_MFMA_PEAK_TFLOPS,
+            "bw_cross": BF16_MFMA_PEAK_TFLOPS if bf16 else FP32_MFMA_PEAK_TFLOPS,
             "bw_landmark_fwd": FP32_MFMA_PEAK_TFLOPS}
 
 

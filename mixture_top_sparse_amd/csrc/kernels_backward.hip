@@ -32,8 +32,8 @@
 //   poolbw    dQ[t] += sum over the windows i containing t of dQl_i / |W_i|
 // With fp32 inputs every contraction runs on v_mfma_f32_16x16x4_f32 (fp32
 // operands, fp32 accumulation).  With bf16 inputs the score products run on
-// bf16 MFMA from the exact bf16 rows, and the expert step's other products
-// on bf16 MFMA too: operands exact in bf16 (Q, K, V rows) as they are, the
+// bf16 MFMA from the exact bf16 rows, and the expert step's and the cross
+// step's other products on bf16 MFMA too: operands exact in bf16 (Q, K, V rows) as they are, the
 // computed ones (dout, Vl, g, the weights w) split into bf16 hi + lo parts
 // (hi = rne(x), lo = rne(x - hi)), the lo x lo term dropped, so that each
 // product is within about 2^-16 of the exact one, relative; fp32
@@ -1191,7 +1191,10 @@ __global__ __launch_bounds__(1024) void k_bw_reduce1(const float* __restrict__ p
 //   dQl += h K_g            (A operand = h straight from the accumulators)
 //   dK_g += h^T Ql, dV_g += A^T dVl   (h, A through the wave's LDS)
 // The group's dK, dV rows are stored (each key belongs to one group); the
-// wave's dQl sums go to partial 4 chunk + w.
+// wave's dQl sums go to partial 4 chunk + w.  bf16 inputs: every product on
+// bf16 MFMA, V rows (exact) straight from global memory as the dP A
+// operand, dVl as bf16 hi + lo in LDS, h and A as hi + lo (cross step at
+// 2^20 tokens x 4 heads: 1.28 -> 0.72 ms against fp32 MFMA).
 template <class T, int MB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_bw_cross(const typename T::elem* __restrict__ K,
                                                   const typename T::elem* __restrict__ V,
@@ -1207,7 +1210,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   // bf16: Ql and each wave's K rows as bf16 rows (exact; the scores on bf16
   // MFMA, the fp32 operands read from them); fp32: fp32 rows
   __shared__ __attribute__((aligned(16))) float sQl[kBf ? MP * kBf16St / 2 : MP * kBwSt];
-  __shared__ __attribute__((aligned(16))) float sdVl[MP * kBwSt];
+  __shared__ __attribute__((aligned(16))) float sdVl[kBf ? 1 : MP * kBwSt];
+  // bf16: dVl rows as bf16 hi + lo (MFMA operands)
+  __shared__ __attribute__((aligned(16))) uint16_t sdVlh[kBf ? MP * kBf16St : 1];
+  __shared__ __attribute__((aligned(16))) uint16_t sdVll[kBf ? MP * kBf16St : 1];
   __shared__ float sLse[MP], sD[MP];
   __shared__ __attribute__((aligned(16))) float sKV[4][2][16 * kBwSt];
   __shared__ __attribute__((aligned(16))) float sK16[kBf ? 4 : 1][kBf ? 16 * kBf16St / 2 : 1];
@@ -1225,11 +1231,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       a.zero();
       zero8(b);
     }
-    if constexpr (kBf)
+    if constexpr (kBf) {
       a.store_raw(reinterpret_cast<uint16_t*>(sQl) + row * kBf16St + 8 * j);
-    else
+      bf16x8 hi, lo;
+      split_hi_lo_pk(b, hi, lo);
+      *reinterpret_cast<bf16x8*>(sdVlh + row * kBf16St + 8 * j) = hi;
+      *reinterpret_cast<bf16x8*>(sdVll + row * kBf16St + 8 * j) = lo;
+    } else {
       a.store(sQl + row * kBwSt + 8 * j);
-    store8(sdVl + row * kBwSt + 8 * j, b);
+      store8(sdVl + row * kBwSt + 8 * j, b);
+    }
   }
   if (threadIdx.x < MP) {
     const int i = threadIdx.x;
@@ -1262,6 +1273,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       return sQl[row * kBwSt + col];
   };
   Raw8<T> rk[2], rv[2];   // the next group's rows (as in k_bw_lmfwd)
+  // bf16: the next group's V rows as the MFMA A operand (lane (c16, g): key
+  // c16, features 32 s + 8 g .. + 7), straight from global memory
+  u32x4 vq[2];
   auto fetch = [&](int64_t t0) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -1269,11 +1283,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       const int64_t t = t0 + (u >> 3);
       if (t < k1) {
         rk[h].load(K + (bh * N + t) * kD + 8 * (u & 7));
-        rv[h].load(V + (bh * N + t) * kD + 8 * (u & 7));
+        if constexpr (!kBf) rv[h].load(V + (bh * N + t) * kD + 8 * (u & 7));
       } else {
         rk[h].zero();
-        rv[h].zero();
+        if constexpr (!kBf) rv[h].zero();
       }
+    }
+    if constexpr (kBf) {
+      const int64_t t = t0 + c16;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        vq[s] = t < k1 ? *reinterpret_cast<const u32x4*>(
+                             reinterpret_cast<const uint16_t*>(V) + (bh * N + t) * kD + 32 * s + 8 * g)
+                       : z;
     }
   };
   fetch(k0 + 16 * w);
@@ -1281,26 +1304,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int u = l + 64 * h;
-      if constexpr (kBf)
+      if constexpr (kBf) {
         rk[h].store_raw(reinterpret_cast<uint16_t*>(sKs) + (u >> 3) * kBf16St + 8 * (u & 7));
-      else
+      } else {
         rk[h].store(sK + (u >> 3) * kBwSt + 8 * (u & 7));
-      rv[h].store(sV + (u >> 3) * kBwSt + 8 * (u & 7));
+        rv[h].store(sV + (u >> 3) * kBwSt + 8 * (u & 7));
+      }
+    }
+    bf16x8 va[2];  // bf16: this group's V rows (exact)
+    if constexpr (kBf) {
+      va[0] = as_bf16x8(vq[0]);
+      va[1] = as_bf16x8(vq[1]);
     }
     fetch(t0 + 64);
     ScoreA<T> ak;
     ak.load(sKs, c16, g);
     float av[16];
+    if constexpr (!kBf) {
 #pragma unroll
-    for (int s = 0; s < 16; ++s) av[s] = sV[c16 * kBwSt + 4 * s + g];
+      for (int s = 0; s < 16; ++s) av[s] = sV[c16 * kBwSt + 4 * s + g];
+    }
     float A[MB][4], Hh[MB][4];
 #pragma unroll
     for (int lb = 0; lb < MB; ++lb) {
       const f32x4 S = ak.score(sQl, 16 * lb + c16, g);
       f32x4 dP = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (kBf) {  // V exact, dVl as hi + lo
+        f32x4 dPb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 16; ++s)
-        dP = mfma_f32(av[s], sdVl[(16 * lb + c16) * kBwSt + 4 * s + g], dP);
+        for (int s = 0; s < 2; ++s) {
+          const int o = (16 * lb + c16) * kBf16St + 32 * s + 8 * g;
+          dP = mfma_bf16(va[s], as_bf16x8(*reinterpret_cast<const u32x4*>(sdVlh + o)), dP);
+          dPb = mfma_bf16(va[s], as_bf16x8(*reinterpret_cast<const u32x4*>(sdVll + o)), dPb);
+        }
+        dP += dPb;
+      } else {
+#pragma unroll
+        for (int s = 0; s < 16; ++s)
+          dP = mfma_f32(av[s], sdVl[(16 * lb + c16) * kBwSt + 4 * s + g], dP);
+      }
       const int i = 16 * lb + c16;
       const float ls = sLse[i], Di = sD[i];
 #pragma unroll
@@ -1311,15 +1353,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       }
     }
     // dQl += h K_g: landmarks on the output rows
+    if constexpr (kBf) {  // v_mfma_f32_16x16x16_bf16: A = the lane's own h (hi + lo)
+      v4i16 hh[MB], hl[MB];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      float kb[4];
+      for (int lb = 0; lb < MB; ++lb) split4(Hh[lb], hh[lb], hl[lb]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) kb[r] = kval(4 * g + r, 16 * db + c16);
+      for (int db = 0; db < 4; ++db) {
+        v4i16 kq;
 #pragma unroll
-      for (int lb = 0; lb < MB; ++lb)
+        for (int r = 0; r < 4; ++r)
+          kq[r] = static_cast<short>(
+              reinterpret_cast<const uint16_t*>(sKs)[(4 * g + r) * kBf16St + 16 * db + c16]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) aQ[lb][db] = mfma_f32(Hh[lb][r], kb[r], aQ[lb][db]);
+        for (int lb = 0; lb < MB; ++lb) {
+          aQ[lb][db] = mfma_bf16_k16(hh[lb], kq, aQ[lb][db]);
+          aQ[lb][db] = mfma_bf16_k16(hl[lb], kq, aQ[lb][db]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        float kb[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) kb[r] = kval(4 * g + r, 16 * db + c16);
+#pragma unroll
+        for (int lb = 0; lb < MB; ++lb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) aQ[lb][db] = mfma_f32(Hh[lb][r], kb[r], aQ[lb][db]);
+      }
     }
     // A and h transposed through the wave's LDS (after its reads of K and V)
 #pragma unroll
@@ -1329,13 +1390,81 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         sK[(4 * g + r) * kBwSt + 16 * lb + c16] = A[lb][r];
         sV[(4 * g + r) * kBwSt + 16 * lb + c16] = Hh[lb][r];
       }
+    // bf16: A operands h^T and A^T (key c16, landmarks 32 s + 8 g .. + 7)
+    // as hi + lo, once for all four feature blocks; an odd landmark block
+    // count ends with a 16-landmark step on v_mfma_f32_16x16x16_bf16
+    constexpr int S32 = kBf ? MP / 32 : 1;
+    constexpr int S32A = S32 > 0 ? S32 : 1;  // (array extent)
+    bf16x8 hth[S32A], htl[S32A], ath[S32A], atl[S32A];
+    v4i16 hth4, htl4, ath4, atl4;
+    if constexpr (kBf) {
+#pragma unroll
+      for (int s = 0; s < S32; ++s) {
+        float x[8], y[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          x[j] = sV[c16 * kBwSt + 32 * s + 8 * g + j];
+          y[j] = sK[c16 * kBwSt + 32 * s + 8 * g + j];
+        }
+        split_hi_lo_pk(x, hth[s], htl[s]);
+        split_hi_lo_pk(y, ath[s], atl[s]);
+      }
+      if constexpr ((MB & 1) != 0) {
+        float x[4], y[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[j] = sV[c16 * kBwSt + 32 * S32 + 4 * g + j];
+          y[j] = sK[c16 * kBwSt + 32 * S32 + 4 * g + j];
+        }
+        split4(x, hth4, htl4);
+        split4(y, ath4, atl4);
+      }
+    }
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       f32x4 dk = {0.f, 0.f, 0.f, 0.f}, dv = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (kBf) {
+        const uint16_t* q16 = reinterpret_cast<const uint16_t*>(sQl);
+        f32x4 dk2 = {0.f, 0.f, 0.f, 0.f}, dv2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 4 * MB; ++s) {
-        dk = mfma_f32(sV[c16 * kBwSt + 4 * s + g], qlval(4 * s + g, 16 * db + c16), dk);
-        dv = mfma_f32(sK[c16 * kBwSt + 4 * s + g], sdVl[(4 * s + g) * kBwSt + 16 * db + c16], dv);
+        for (int s = 0; s < S32; ++s) {
+          u32x4 bq, bh, bl;  // landmarks 32 s + 8 g + j at feature 16 db + c16
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r0 = (32 * s + 8 * g + 2 * j) * kBf16St + 16 * db + c16, r1 = r0 + kBf16St;
+            bq[j] = static_cast<uint32_t>(q16[r0]) | (static_cast<uint32_t>(q16[r1]) << 16);
+            bh[j] = static_cast<uint32_t>(sdVlh[r0]) | (static_cast<uint32_t>(sdVlh[r1]) << 16);
+            bl[j] = static_cast<uint32_t>(sdVll[r0]) | (static_cast<uint32_t>(sdVll[r1]) << 16);
+          }
+          dk = mfma_bf16(hth[s], as_bf16x8(bq), dk);
+          dk2 = mfma_bf16(htl[s], as_bf16x8(bq), dk2);
+          dv = mfma_bf16(ath[s], as_bf16x8(bh), dv);
+          dv2 = mfma_bf16(atl[s], as_bf16x8(bh), dv2);
+          dv = mfma_bf16(ath[s], as_bf16x8(bl), dv);
+        }
+        if constexpr ((MB & 1) != 0) {
+          v4i16 bq4, bh4, bl4;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r = (32 * S32 + 4 * g + j) * kBf16St + 16 * db + c16;
+            bq4[j] = static_cast<short>(q16[r]);
+            bh4[j] = static_cast<short>(sdVlh[r]);
+            bl4[j] = static_cast<short>(sdVll[r]);
+          }
+          dk = mfma_bf16_k16(hth4, bq4, dk);
+          dk2 = mfma_bf16_k16(htl4, bq4, dk2);
+          dv = mfma_bf16_k16(ath4, bh4, dv);
+          dv2 = mfma_bf16_k16(atl4, bh4, dv2);
+          dv = mfma_bf16_k16(ath4, bl4, dv);
+        }
+        dk += dk2;
+        dv += dv2;
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4 * MB; ++s) {
+          dk = mfma_f32(sV[c16 * kBwSt + 4 * s + g], qlval(4 * s + g, 16 * db + c16), dk);
+          dv = mfma_f32(sK[c16 * kBwSt + 4 * s + g], sdVl[(4 * s + g) * kBwSt + 16 * db + c16], dv);
+        }
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {

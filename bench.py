@@ -307,13 +307,11 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix rate, published
 
 
 def backward_peaks(w) -> dict[str, float]:
-    """The matrix rate each backward contraction kernel runs on: for bf16
-    inputs the expert and cross steps issue bf16 MFMAs (their fp32 operands
-    split into bf16 hi + lo parts), the landmark forward fp32 MFMAs."""
-    bf16 = w.dtype == "bf16"
-    return {"bw_attend": BF16_MFMA_PEAK_TFLOPS if bf16 else FP32_MFMA_PEAK_TFLOPS,
-            "bw_cross": BF16_MFMA_PEAK_TFLOPS if bf16 else FP32_MFMA_PEAK_TFLOPS,
-            "bw_landmark_fwd": FP32_MFMA_PEAK_TFLOPS}
+    """The matrix rate each backward contraction kernel runs on: bf16 MFMAs
+    for bf16 inputs (their fp32 operands split into bf16 hi + lo parts),
+    fp32 MFMAs for fp32 inputs."""
+    peak = BF16_MFMA_PEAK_TFLOPS if w.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
+    return {"bw_attend": peak, "bw_cross": peak, "bw_landmark_fwd": peak}
 
 
 def backward_flops(w) -> dict[str, float]:

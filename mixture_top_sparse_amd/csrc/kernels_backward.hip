@@ -32,8 +32,8 @@
 //   poolbw    dQ[t] += sum over the windows i containing t of dQl_i / |W_i|
 // With fp32 inputs every contraction runs on v_mfma_f32_16x16x4_f32 (fp32
 // operands, fp32 accumulation).  With bf16 inputs the score products run on
-// bf16 MFMA from the exact bf16 rows, and the expert step's and the cross
-// step's other products on bf16 MFMA too: operands exact in bf16 (Q, K, V rows) as they are, the
+// bf16 MFMA from the exact bf16 rows, and every other product of the
+// landmark forward, the expert step and the cross step on bf16 MFMA too: operands exact in bf16 (Q, K, V rows) as they are, the
 // computed ones (dout, Vl, g, the weights w) split into bf16 hi + lo parts
 // (hi = rne(x), lo = rne(x - hi)), the lo x lo term dropped, so that each
 // product is within about 2^-16 of the exact one, relative; fp32
@@ -231,6 +231,27 @@ __global__ __launch_bounds__(256) void k_bw_zero(f32x4* __restrict__ a, f32x4* _
   }
 }
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// v_mfma_f32_16x16x16_bf16: A[16][16], B[16][16], lane l holds row (A) or
+// column (B) l % 16 and the 4 consecutive K-elements 4 (l / 16) .. + 3
+__device__ __forceinline__ f32x4 mfma_bf16_k16(v4i16 a, v4i16 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+// 4 fp32 values as bf16 hi = rne(x) and lo = rne(x - hi)
+__device__ __forceinline__ void split4(const float (&x)[4], v4i16& hi, v4i16& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const __bf16 h = static_cast<__bf16>(x[i]);
+    hi[i] = __builtin_bit_cast(short, h);
+    lo[i] = __builtin_bit_cast(short, static_cast<__bf16>(x[i] - static_cast<float>(h)));
+  }
+}
+__device__ __forceinline__ void split4(const f32x4& x, v4i16& hi, v4i16& lo) {
+  const float v[4] = {x[0], x[1], x[2], x[3]};
+  split4(v, hi, lo);
+}
+
 // ---------------------------------------------------------------------------
 // landmark cross-attention, forward (Vl and its row log-sum-exp)
 // ---------------------------------------------------------------------------
@@ -311,15 +332,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int u = l + 64 * h;
-      if constexpr (kBf)
+      if constexpr (kBf) {
         rk[h].store_raw(reinterpret_cast<uint16_t*>(sKw) + (u >> 3) * kBf16St + 8 * (u & 7));
-      else
+        rv[h].store_raw(reinterpret_cast<uint16_t*>(sV) + (u >> 3) * kBf16St + 8 * (u & 7));
+      } else {
         rk[h].store(sKw + (u >> 3) * kBwSt + 8 * (u & 7));
-      rv[h].store(sV + (u >> 3) * kBwSt + 8 * (u & 7));
+        rv[h].store(sV + (u >> 3) * kBwSt + 8 * (u & 7));
+      }
     }
     fetch(t0 + 64);
     ScoreA<T> a;
     a.load(sKw, c16, g);
+    // bf16: V^T (feature 16 db + c16, keys 4 g .. 4 g + 3; exact) as the A
+    // operand of v_mfma_f32_16x16x16_bf16, P as hi + lo the B operand
+    v4i16 vt[4];
+    if constexpr (kBf) {
+      const uint16_t* v16 = reinterpret_cast<const uint16_t*>(sV);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vt[db][j] = static_cast<short>(v16[(4 * g + j) * kBf16St + 16 * db + c16]);
+    }
 #pragma unroll
     for (int lb = 0; lb < MB; ++lb) {
       const f32x4 S = a.score(smem, 16 * lb + c16, g);
@@ -345,12 +378,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       ps = xor_sum(ps, 32);
       L[lb] = L[lb] * f + ps;
       M[lb] = Mn;
+      if constexpr (kBf) {
+        v4i16 ph, pl;
+        split4(p, ph, pl);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        acc[lb][db] *= f;
+        for (int db = 0; db < 4; ++db) {
+          acc[lb][db] *= f;
+          acc[lb][db] = mfma_bf16_k16(vt[db], ph, acc[lb][db]);
+          acc[lb][db] = mfma_bf16_k16(vt[db], pl, acc[lb][db]);
+        }
+      } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          acc[lb][db] = mfma_f32(sV[(4 * g + r) * kBwSt + 16 * db + c16], p[r], acc[lb][db]);
+        for (int db = 0; db < 4; ++db) {
+          acc[lb][db] *= f;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[lb][db] = mfma_f32(sV[(4 * g + r) * kBwSt + 16 * db + c16], p[r], acc[lb][db]);
+        }
       }
     }
   }
@@ -784,27 +828,6 @@ __global__ __launch_bounds__(512) void k_bw_attend(
       }
     }
   }
-}
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-
-// v_mfma_f32_16x16x16_bf16: A[16][16], B[16][16], lane l holds row (A) or
-// column (B) l % 16 and the 4 consecutive K-elements 4 (l / 16) .. + 3
-__device__ __forceinline__ f32x4 mfma_bf16_k16(v4i16 a, v4i16 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-// 4 fp32 values as bf16 hi = rne(x) and lo = rne(x - hi)
-__device__ __forceinline__ void split4(const float (&x)[4], v4i16& hi, v4i16& lo) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const __bf16 h = static_cast<__bf16>(x[i]);
-    hi[i] = __builtin_bit_cast(short, h);
-    lo[i] = __builtin_bit_cast(short, static_cast<__bf16>(x[i] - static_cast<float>(h)));
-  }
-}
-__device__ __forceinline__ void split4(const f32x4& x, v4i16& hi, v4i16& lo) {
-  const float v[4] = {x[0], x[1], x[2], x[3]};
-  split4(v, hi, lo);
 }
 
 // The same step for bf16 inputs in four-wave blocks whose LDS fits two

@@ -1666,7 +1666,13 @@ hipError_t launch_backward_t(const Shape& s, const BwPlan& bp, const BwWorkspace
     switch (mb) {
       case 1: hipLaunchKernelGGL((k_bw_cross<T, 1>), grid, dim3(256), 0, st, K, V, ql, ws.dvl, ws.lse2, ws.dd, s.N, s.m, bp.cross_chunk, s.scale, dK, dV, ws.part2); break;
       case 2: hipLaunchKernelGGL((k_bw_cross<T, 2>), grid, dim3(256), 0, st, K, V, ql, ws.dvl, ws.lse2, ws.dd, s.N, s.m, bp.cross_chunk, s.scale, dK, dV, ws.part2); break;
-      case 3: hipLaunchKernelGGL((k_bw_cross<T, 3>), grid, dim3(256), 0, st, K, V, ql, ws.dvl, ws.lse2, ws.dd, s.N, s.m, bp.cross_chunk, s.scale, dK, dV, ws.part2); break;
+      case 3:
+        if constexpr (std::is_same<T, BF16>::value)  // bf16: the three-block instance spills
+          // registers; the four-block one gives the padding landmarks zero weight
+          hipLaunchKernelGGL((k_bw_cross<T, 4>), grid, dim3(256), 0, st, K, V, ql, ws.dvl, ws.lse2, ws.dd, s.N, s.m, bp.cross_chunk, s.scale, dK, dV, ws.part2);
+        else
+          hipLaunchKernelGGL((k_bw_cross<T, 3>), grid, dim3(256), 0, st, K, V, ql, ws.dvl, ws.lse2, ws.dd, s.N, s.m, bp.cross_chunk, s.scale, dK, dV, ws.part2);
+        break;
       default: hipLaunchKernelGGL((k_bw_cross<T, 4>), grid, dim3(256), 0, st, K, V, ql, ws.dvl, ws.lse2, ws.dd, s.N, s.m, bp.cross_chunk, s.scale, dK, dV, ws.part2); break;
     }
     e = hipGetLastError();
